@@ -1,0 +1,174 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them."""
+
+import numpy as np
+import pytest
+
+import oracle.csa_oracle as O
+import oracle_pins as P
+
+
+def _fails(monkeypatch, **patches):
+    for name, fn in patches.items():
+        monkeypatch.setattr(O, name, fn)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(O)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except Exception:  # a crash also counts as caught
+            failed.append(pin.__name__)
+    return failed
+
+
+orig_scale = O.scale_exponent
+orig_mag = O.e2m1_magnitude_code
+orig_quant = O.quantize_rows
+orig_deq = O.dequantize_rows
+orig_pool = O.pool_blocks
+orig_scores = O.index_scores
+orig_select = O.select_topk
+orig_attend = O.attend
+orig_win = O.window_positions
+orig_nvis = O.n_visible
+orig_gather = O.gather_rows
+
+
+def m_scale_off_by_one(a):
+    return orig_scale(a) + 1
+
+
+def m_no_clamp(a):
+    a = np.asarray(a, dtype=np.float64)
+    _, ex = np.frexp(a)
+    return np.where(a == 0, -127, ex.astype(np.int64) - 3)
+
+
+def m_ties_up(a):
+    a = np.asarray(a, dtype=np.float64)
+    return ((a >= 0.25).astype(np.int64) + (a >= 0.75) + (a >= 1.25) + (a >= 1.75)
+            + (a >= 2.5) + (a >= 3.5) + (a >= 5.0))
+
+
+def m_nibbles_swapped(p):
+    c, s = orig_quant(p)
+    return ((c >> 4) | (c << 4)).astype(np.uint8), s
+
+
+def m_drop_negative_zero(p):
+    c, s = orig_quant(p)
+    lo, hi = c & 0xF, c >> 4
+    lo = np.where(lo == 8, 0, lo)
+    hi = np.where(hi == 8, 0, hi)
+    return (lo | (hi << 4)).astype(np.uint8), s
+
+
+def m_deq_bias(c, s):
+    return orig_deq(c, s) * 2.0
+
+
+def m_pool_mean(kv, g, m):
+    return orig_pool(kv, np.zeros_like(g), m)
+
+
+def m_pool_drop_last(kv, g, m):
+    kv = np.array(kv, copy=True)
+    n = len(kv)
+    for b in range(0, n, m):
+        if min(b + m, n) - b > 1:
+            kv[min(b + m, n) - 1] = kv[b]
+    return orig_pool(kv, g, m)
+
+
+def m_no_relu(q, w, keys):
+    return (np.asarray(keys, np.int64) @ np.asarray(q, np.int64).T) @ np.asarray(w, np.int64)
+
+
+def m_relu_after_sum(q, w, keys):
+    d = np.asarray(keys, np.int64) @ np.asarray(q, np.int64).T
+    return np.maximum(d @ np.asarray(w, np.int64), 0)
+
+
+def m_ties_high(blocks, scores, k):
+    blocks = np.asarray(blocks, np.int64)
+    return orig_select(blocks[::-1], np.asarray(scores)[::-1], k) if blocks.size else orig_select(blocks, scores, k)
+
+
+def m_ties_high2(blocks, scores, k):
+    blocks = np.asarray(blocks, np.int64)
+    scores = np.asarray(scores, np.int64)
+    order = np.lexsort((-blocks, -scores))
+    keep = np.sort(blocks[order[:min(k, blocks.size)]])
+    idx = np.full(k, -1, np.int32)
+    idx[:keep.size] = keep
+    sc = np.full(k, -1, np.int32)
+    return idx, sc
+
+
+def m_score_order(blocks, scores, k):
+    blocks = np.asarray(blocks, np.int64)
+    scores = np.asarray(scores, np.int64)
+    order = np.lexsort((blocks, -scores))[:min(k, blocks.size)]
+    idx = np.full(k, -1, np.int32)
+    idx[:order.size] = blocks[order]
+    sc = np.full(k, -1, np.int32)
+    sc[:order.size] = scores[order]
+    return idx, sc
+
+
+def m_visible_early(t, m):
+    return (t + 2) // m
+
+
+def m_window_off_by_one(t, W):
+    return np.arange(max(0, t - W), t + 1)
+
+
+def m_window_excludes_self(t, W):
+    return np.arange(max(0, t - W + 1), t)
+
+
+def m_attend_no_scale(q, rows, s):
+    return orig_attend(q, rows, 1.0)
+
+
+def m_attend_softmax_heads(q, rows, s):
+    logits = s * (q @ rows.T)
+    e = np.exp(logits - logits.max(axis=0, keepdims=True))
+    e = e / e.sum(axis=0, keepdims=True)
+    return e @ rows, np.zeros(q.shape[0])
+
+
+def m_gather_no_window(codes, scales, blocks, win, Wcap, t, W):
+    rows = orig_gather(codes, scales, blocks, win, Wcap, t, W)
+    nwin = len(orig_win(t, W))
+    return rows[:-nwin] if rows.shape[0] > nwin else rows
+
+
+MUTANTS = {
+    "scale exponent off by one": {"scale_exponent": m_scale_off_by_one},
+    "scale exponent not clamped": {"scale_exponent": m_no_clamp},
+    "ties rounded up": {"e2m1_magnitude_code": m_ties_up},
+    "nibbles swapped": {"quantize_rows": m_nibbles_swapped},
+    "negative zero dropped": {"quantize_rows": m_drop_negative_zero},
+    "dequant scale doubled": {"dequantize_rows": m_deq_bias},
+    "pooling ignores gates": {"pool_blocks": m_pool_mean},
+    "pooling drops last token": {"pool_blocks": m_pool_drop_last},
+    "indexer without relu": {"index_scores": m_no_relu},
+    "relu after head sum": {"index_scores": m_relu_after_sum},
+    "ties to higher index": {"select_topk": m_ties_high2},
+    "output in score order": {"select_topk": m_score_order},
+    "block visible one token early": {"n_visible": m_visible_early},
+    "window one too long": {"window_positions": m_window_off_by_one},
+    "window excludes the query token": {"window_positions": m_window_excludes_self},
+    "softmax scale ignored": {"attend": m_attend_no_scale},
+    "softmax over heads": {"attend": m_attend_softmax_heads},
+    "window dropped": {"gather_rows": m_gather_no_window},
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    failed = _fails(monkeypatch, **MUTANTS[name])
+    assert failed, f"no pin caught the planted mistake: {name}"
