@@ -1,0 +1,280 @@
+"""Python binding of libcsa (compressed sparse attention for MI355X / gfx950).
+
+Argument marshalling only: every function checks dtypes, devices, shapes and
+contiguity of torch tensors, then calls the C symbol of the same name in
+libcsa.so on torch's current HIP stream. No computation happens here, and
+there is no fallback: if libcsa.so is missing or a call fails, an exception
+is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "CSAError", "lib", "cache_bytes", "compress_quantize", "dequantize", "index_topk",
+    "index_scan", "index_select", "index_topk_workspace", "workspace_clear", "sparse_attn",
+    "hca_dense_attn", "attn_workspace", "Workspace", "BF16", "F32", "F16", "EXPORTED",
+]
+
+BF16, F32, F16 = 0, 1, 2
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa.so")
+
+# every symbol declared in include/csa.h
+EXPORTED = [
+    "csa_status_string", "csa_version", "csa_cache_bytes", "csa_compress_quantize",
+    "csa_dequantize", "csa_index_topk_workspace", "csa_index_topk", "csa_index_scan",
+    "csa_index_select", "csa_workspace_clear", "csa_attn_workspace", "csa_sparse_attn",
+    "hca_dense_attn",
+]
+
+
+class CSAError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcsa.so (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CSAError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        sig = {
+            "csa_status_string": (ctypes.c_char_p, [I]),
+            "csa_version": (I, []),
+            "csa_cache_bytes": (I64, [I64, I, I]),
+            "csa_compress_quantize": (I, [P, I64, P, I, I64, I64, I, I, P, P, I64, P]),
+            "csa_dequantize": (I, [P, P, I64, I, I64, I64, I, P, I, P]),
+            "csa_index_topk_workspace": (I64, [I, I, I64, I, I]),
+            "csa_index_topk": (I, [P, P, P, I64, I, I, I, I, I, I64, P, I, I, P, P, P, I64, P]),
+            "csa_index_scan": (I, [P, P, P, I64, I, I, I, I, I, I64, P, I, I, P, P, P, I64, P]),
+            "csa_index_select": (I, [P, P, P, I64, I, I, I, I, I, I64, P, I, I, P, P, P, I64, P]),
+            "csa_workspace_clear": (I, [P, I64, P]),
+            "csa_attn_workspace": (I64, [I, I, I, I, I64]),
+            "csa_sparse_attn": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, I64, F, P, I, P,
+                                    P, I64, P]),
+            "hca_dense_attn": (I, [P, P, P, I64, I, P, I, I, I, I, I, I, I64, F, P, I, P, P,
+                                   I64, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().csa_status_string(status).decode()
+        raise CSAError(f"{what}: {msg} ({status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+
+
+def cache_bytes(n_tokens: int, d: int, m: int) -> int:
+    return lib().csa_cache_bytes(n_tokens, d, m)
+
+
+class Workspace:
+    """Zero-initialised device workspace that grows on demand."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+        self.key = None
+
+    def get(self, nbytes: int, key=None):
+        """A buffer of at least nbytes. `key` names the layout of the
+        workspace head (B*T for the indexer); the buffer is zero-filled
+        again whenever it changes."""
+        if nbytes <= 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device or "cuda")
+        elif key is not None and key != self.key:
+            self.buf.zero_()
+        self.key = key
+        return self.buf
+
+
+_DEFAULT_WS = {}
+
+
+def _default_ws(device):
+    """Per-device index workspace used when the caller passes none (calls on
+    one device must then be ordered, e.g. issued on one stream)."""
+    key = str(device)
+    if key not in _DEFAULT_WS:
+        _DEFAULT_WS[key] = Workspace(device)
+    return _DEFAULT_WS[key]
+
+
+def compress_quantize(kv, gate, tok0: int, m: int, codes, scales):
+    """kv float32 [B][n_tok][kv_ld] (d = codes.shape[2]*2 columns used),
+    gate float32 [B][n_tok], codes uint8 [B][blk_cap][d/2], scales uint8
+    [B][blk_cap][d/32]."""
+    _need(kv, torch.float32, "kv", 3)
+    _need(gate, torch.float32, "gate", 2)
+    _need(codes, torch.uint8, "codes", 3)
+    _need(scales, torch.uint8, "scales", 3)
+    B, n_tok, ld = kv.shape
+    d = codes.shape[2] * 2
+    if gate.shape != (B, n_tok) or codes.shape[0] != B or scales.shape[:2] != codes.shape[:2]:
+        raise ValueError("compress_quantize: inconsistent shapes")
+    if scales.shape[2] * 32 != d:
+        raise ValueError("compress_quantize: scales width must be d/32")
+    _check(lib().csa_compress_quantize(_ptr(kv), ld, _ptr(gate), B, tok0, n_tok, d, m,
+                                       _ptr(codes), _ptr(scales), codes.shape[1], _stream()),
+           "csa_compress_quantize")
+
+
+def dequantize(codes, scales, blk0: int, n_blk: int, out):
+    _need(codes, torch.uint8, "codes", 3)
+    _need(scales, torch.uint8, "scales", 3)
+    B, cap, half = codes.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32, torch.float16: F16}[out.dtype]
+    _need(out, out.dtype, "out", 3)
+    if out.shape != (B, n_blk, 2 * half):
+        raise ValueError("dequantize: out must be [B][n_blk][d]")
+    _check(lib().csa_dequantize(_ptr(codes), _ptr(scales), cap, B, blk0, n_blk, 2 * half,
+                                _ptr(out), dt, _stream()), "csa_dequantize")
+
+
+def index_topk_workspace(B, T, n_max, k, cand_given=False) -> int:
+    return lib().csa_index_topk_workspace(B, T, n_max, k, int(bool(cand_given)))
+
+
+def _index_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, out_score=None, cand=None,
+                workspace=None):
+    _need(q_idx, torch.int8, "q_idx", 4)
+    _need(w, torch.int8, "w", 3)
+    _need(keys, torch.int8, "keys", 3)
+    _need(out_idx, torch.int32, "out_idx", 3)
+    _need(out_score, torch.int32, "out_score", 3)
+    _need(cand, torch.int32, "cand", 3)
+    B, T, Hi, Di = q_idx.shape
+    if w.shape != (B, T, Hi) or keys.shape[0] != B or keys.shape[2] != Di:
+        raise ValueError("index_topk: inconsistent shapes")
+    if out_idx.shape != (B, T, k) or (out_score is not None and out_score.shape != (B, T, k)):
+        raise ValueError("index_topk: out_idx / out_score must be [B][T][k]")
+    C = 0
+    if cand is not None:
+        if cand.shape[:2] != (B, T):
+            raise ValueError("index_topk: cand must be [B][T][C]")
+        C = cand.shape[2]
+    blk_cap = keys.shape[1]
+    n_max = C if cand is not None else min(blk_cap, (pos0 + T) // m)
+    need = index_topk_workspace(B, T, n_max, k, cand is not None)
+    if workspace is None:
+        workspace = _default_ws(q_idx.device)
+    ws = workspace.get(need, key=B * T) if isinstance(workspace, Workspace) else workspace
+    ws_bytes = 0 if ws is None else ws.numel()
+    _check(getattr(lib(), fn_name)(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di, m,
+                                   pos0, _ptr(cand), C, k, _ptr(out_idx), _ptr(out_score),
+                                   _ptr(ws), ws_bytes, _stream()), fn_name)
+
+
+def index_topk(*args, **kw):
+    """Indexer scores + top-k; see csa_index_topk in include/csa.h."""
+    _index_call("csa_index_topk", *args, **kw)
+
+
+def index_scan(*args, **kw):
+    _index_call("csa_index_scan", *args, **kw)
+
+
+def index_select(*args, **kw):
+    _index_call("csa_index_select", *args, **kw)
+
+
+def workspace_clear(ws):
+    _need(ws, torch.uint8, "ws")
+    _check(lib().csa_workspace_clear(_ptr(ws), ws.numel() // 4 * 4, _stream()),
+           "csa_workspace_clear")
+
+
+def attn_workspace(B, T, H, d, n_slots) -> int:
+    return lib().csa_attn_workspace(B, T, H, d, n_slots)
+
+
+def _attn_common(q, codes, scales, win, out, lse):
+    _need(q, torch.bfloat16, "q", 4)
+    _need(codes, torch.uint8, "codes", 3)
+    _need(scales, torch.uint8, "scales", 3)
+    _need(win, torch.bfloat16, "win", 3)
+    _need(lse, torch.float32, "lse", 3)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _need(out, out.dtype, "out", 4)
+    B, T, H, d = q.shape
+    if out.shape != q.shape or win.shape[0] != B or win.shape[2] != d:
+        raise ValueError("attention: inconsistent shapes")
+    if codes.shape[0] != B or codes.shape[2] * 2 != d or scales.shape[:2] != codes.shape[:2]:
+        raise ValueError("attention: cache shape mismatch")
+    if lse is not None and lse.shape != (B, T, H):
+        raise ValueError("lse must be [B][T][H]")
+    return B, T, H, d, (BF16 if out.dtype == torch.bfloat16 else F32)
+
+
+def sparse_attn(q, codes, scales, idx, win, W, pos0, softmax_scale, out, lse=None,
+                workspace=None):
+    """Attention over the idx-selected entries plus the window; see csa_sparse_attn."""
+    B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse)
+    _need(idx, torch.int32, "idx", 3)
+    k = idx.shape[2]
+    if idx.shape[:2] != (B, T):
+        raise ValueError("idx must be [B][T][k]")
+    need = attn_workspace(B, T, H, d, k + W)
+    ws = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if ws is None else ws.numel()
+    _check(lib().csa_sparse_attn(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1], _ptr(idx), k,
+                                 _ptr(win), win.shape[1], W, B, T, H, d, pos0,
+                                 float(softmax_scale), _ptr(out), dt, _ptr(lse), _ptr(ws),
+                                 ws_bytes, _stream()), "csa_sparse_attn")
+
+
+def hca_dense_attn(q, codes, scales, m, win, W, pos0, softmax_scale, out, lse=None,
+                   workspace=None):
+    """Attention over every visible entry of an m-token cache plus the window."""
+    B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse)
+    n_slots = min(codes.shape[1], (pos0 + T) // m) + W
+    need = attn_workspace(B, T, H, d, n_slots)
+    ws = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if ws is None else ws.numel()
+    _check(lib().hca_dense_attn(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1], m, _ptr(win),
+                                win.shape[1], W, B, T, H, d, pos0, float(softmax_scale),
+                                _ptr(out), dt, _ptr(lse), _ptr(ws), ws_bytes, _stream()),
+           "hca_dense_attn")

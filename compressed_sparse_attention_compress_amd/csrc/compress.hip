@@ -1,0 +1,193 @@
+// Block compression + MXFP4 quantisation, and MXFP4 dequantisation.
+//
+// Method: "Frontier Architecture Decoding Notes (4): DeepSeek V4", section 1
+// (the KV is summarised per 4-token block for CSA, up to 128 tokens for HCA)
+// and the podcast transcript "DeepSeek-V4.1-Flash: Pushing the Limits of KV
+// Cache Compression", cue 16 (MXFP4 main cache). Pooling rule: softmax over
+// the block's gate logits, weighted sum of the token latents. Quantisation:
+// OCP MX v1.0 MXFP4 (E8M0 per 32, exponent floor(log2 amax) - 2, RNE on the
+// E2M1 grid with saturation, sign kept on zero).
+//
+// The pooled value is computed in float64 with the multiply and the add
+// rounded separately, tokens in order, so the decision of every code is taken
+// on the same float64 value a plain float64 evaluation produces (the only
+// difference left is the last bit of exp()). HBM-bound: one wave reads a
+// block's m x d float32 latents with 32-byte loads per lane.
+#include "csa_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+// One lane owns 8 consecutive channels of one block; D/8 lanes cover a block
+// row, so a wave holds 64/(D/8) blocks.
+template <int D>
+__global__ __launch_bounds__(256) void k_compress_quantize(
+    const float* __restrict__ kv, int64_t kv_ld, const float* __restrict__ gate,
+    int64_t n_tok, int m, int64_t nblk, int64_t total, int64_t blk_first,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t blk_cap) {
+  constexpr int LPB = D / 8;
+  constexpr int BPW = 64 / LPB;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t gb = ((int64_t)blockIdx.x * 4 + wave) * BPW + lane / LPB;
+  if (gb >= total) return;  // whole 4-lane groups leave together
+  const int64_t b = gb / nblk;
+  const int64_t bi = gb - b * nblk;
+  const int64_t j0 = bi * m;
+  const int n = (int)((n_tok - j0) < m ? (n_tok - j0) : m);
+  const int seg = lane % LPB;
+  const float* g = gate + b * n_tok + j0;
+  const float* x = kv + (b * n_tok + j0) * kv_ld + seg * 8;
+
+  double gmax = (double)g[0];
+  for (int j = 1; j < n; ++j) gmax = fmax(gmax, (double)g[j]);
+  double den = exp((double)g[0] - gmax);
+  for (int j = 1; j < n; ++j) den = den + exp((double)g[j] - gmax);
+
+  double p[8];
+  {
+    const double w0 = exp((double)g[0] - gmax) / den;
+    const float4 a = *reinterpret_cast<const float4*>(x);
+    const float4 c = *reinterpret_cast<const float4*>(x + 4);
+    p[0] = w0 * (double)a.x; p[1] = w0 * (double)a.y;
+    p[2] = w0 * (double)a.z; p[3] = w0 * (double)a.w;
+    p[4] = w0 * (double)c.x; p[5] = w0 * (double)c.y;
+    p[6] = w0 * (double)c.z; p[7] = w0 * (double)c.w;
+  }
+  for (int j = 1; j < n; ++j) {
+    const double wj = exp((double)g[j] - gmax) / den;
+    const float* xj = x + (int64_t)j * kv_ld;
+    const float4 a = *reinterpret_cast<const float4*>(xj);
+    const float4 c = *reinterpret_cast<const float4*>(xj + 4);
+    p[0] = p[0] + wj * (double)a.x; p[1] = p[1] + wj * (double)a.y;
+    p[2] = p[2] + wj * (double)a.z; p[3] = p[3] + wj * (double)a.w;
+    p[4] = p[4] + wj * (double)c.x; p[5] = p[5] + wj * (double)c.y;
+    p[6] = p[6] + wj * (double)c.z; p[7] = p[7] + wj * (double)c.w;
+  }
+
+  // group amax over the 4 lanes (32 channels) of a scale group
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(p[i]));
+  amax = fmax(amax, __shfl_xor(amax, 1, 64));
+  amax = fmax(amax, __shfl_xor(amax, 2, 64));
+
+  int e = -127;
+  if (amax > 0.0) {
+    int ex;
+    (void)frexp(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+    e = ex - 1 - 2;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double y = ldexp(p[i], -e);
+    const double a = fabs(y);
+    uint32_t mag = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) +
+                   (a >= 3.5) + (a > 5.0);
+    uint32_t code = (signbit(y) ? 8u : 0u) | mag;
+    word |= code << (4 * i);
+  }
+  const int64_t row = b * blk_cap + blk_first + bi;
+  *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + seg * 4) = word;
+  if ((seg & 3) == 0) scales[row * (D / 32) + seg / 4] = (uint8_t)(e + 127);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256) void k_dequantize(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t blk_cap,
+    int64_t blk0, int64_t n_blk, int d, int64_t total, void* __restrict__ out) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= total) return;
+  const int segs = d / 8;
+  const int64_t row = u / segs;
+  const int seg = (int)(u - row * segs);
+  const int64_t b = row / n_blk;
+  const int64_t bi = row - b * n_blk;
+  const int64_t src = b * blk_cap + blk0 + bi;
+  const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + src * (d / 2) + seg * 4);
+  const float sc = e8m0_to_f32(scales[src * (d / 32) + seg / 4]);
+  if (OUT == CSA_BF16) {
+    v8bf v = fp4x8_to_bf16(word, sc);
+    *reinterpret_cast<v8bf*>(reinterpret_cast<__bf16*>(out) + u * 8) = v;
+  } else if (OUT == CSA_F16) {
+    v8h v = fp4x8_to_f16(word, sc);
+    *reinterpret_cast<v8h*>(reinterpret_cast<_Float16*>(out) + u * 8) = v;
+  } else {
+    v8bf v = fp4x8_to_bf16(word, sc);
+    float* o = reinterpret_cast<float*>(out) + u * 8;
+    float4 a, c;
+    a.x = (float)v[0]; a.y = (float)v[1]; a.z = (float)v[2]; a.w = (float)v[3];
+    c.x = (float)v[4]; c.y = (float)v[5]; c.z = (float)v[6]; c.w = (float)v[7];
+    reinterpret_cast<float4*>(o)[0] = a;
+    reinterpret_cast<float4*>(o)[1] = c;
+  }
+}
+
+}  // namespace
+
+extern "C" int64_t csa_cache_bytes(int64_t n_tokens, int d, int m) {
+  if (n_tokens < 0 || m < 1 || d <= 0 || d % 32) return -1;
+  return ((n_tokens + m - 1) / m) * (int64_t)(d / 2 + d / 32);
+}
+
+extern "C" int csa_compress_quantize(const float* kv, int64_t kv_ld, const float* gate, int B,
+                                     int64_t tok0, int64_t n_tok, int d, int m, uint8_t* codes,
+                                     uint8_t* scales, int64_t blk_cap, hipStream_t stream) {
+  if (B < 0 || n_tok < 0 || tok0 < 0 || blk_cap < 0) return CSA_ERR_SHAPE;
+  if (m < 1 || m > 128) return CSA_ERR_SHAPE;
+  if (d != 32 && d != 64 && d != 128 && d != 256 && d != 512) return CSA_ERR_SHAPE;
+  if (kv_ld < d || kv_ld % 4) return CSA_ERR_ALIGN;
+  if (tok0 % m) return CSA_ERR_RANGE;
+  if (B == 0 || n_tok == 0) return CSA_OK;
+  if (!kv || !gate || !codes || !scales) return CSA_ERR_NULL;
+  if (!csa_aligned(kv, 16) || !csa_aligned(codes, 4)) return CSA_ERR_ALIGN;
+  const int64_t blk_first = tok0 / m;
+  const int64_t nblk = (n_tok + m - 1) / m;
+  if (blk_first + nblk > blk_cap) return CSA_ERR_RANGE;
+  const int64_t total = (int64_t)B * nblk;
+  const int bpwg = 4 * (64 / (d / 8));
+  const int64_t grid = (total + bpwg - 1) / bpwg;
+  if (grid > 0x7fffffff) return CSA_ERR_SHAPE;
+#define CSA_LAUNCH_COMPRESS(DD)                                                            \
+  hipLaunchKernelGGL(k_compress_quantize<DD>, dim3((unsigned)grid), dim3(256), 0, stream, kv, \
+                     kv_ld, gate, n_tok, m, nblk, total, blk_first, codes, scales, blk_cap)
+  switch (d) {
+    case 32: CSA_LAUNCH_COMPRESS(32); break;
+    case 64: CSA_LAUNCH_COMPRESS(64); break;
+    case 128: CSA_LAUNCH_COMPRESS(128); break;
+    case 256: CSA_LAUNCH_COMPRESS(256); break;
+    default: CSA_LAUNCH_COMPRESS(512); break;
+  }
+#undef CSA_LAUNCH_COMPRESS
+  CSA_TRY_LAUNCH();
+  return CSA_OK;
+}
+
+extern "C" int csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t blk_cap, int B,
+                              int64_t blk0, int64_t n_blk, int d, void* out, int out_dtype,
+                              hipStream_t stream) {
+  if (B < 0 || blk0 < 0 || n_blk < 0 || blk_cap < 0) return CSA_ERR_SHAPE;
+  if (d <= 0 || d % 32 || d > 4096) return CSA_ERR_SHAPE;
+  if (out_dtype != CSA_BF16 && out_dtype != CSA_F16 && out_dtype != CSA_F32) return CSA_ERR_DTYPE;
+  if (blk0 + n_blk > blk_cap) return CSA_ERR_RANGE;
+  if (B == 0 || n_blk == 0) return CSA_OK;
+  if (!codes || !scales || !out) return CSA_ERR_NULL;
+  if (!csa_aligned(codes, 4) || !csa_aligned(out, 16)) return CSA_ERR_ALIGN;
+  const int64_t total = (int64_t)B * n_blk * (d / 8);
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7fffffff) return CSA_ERR_SHAPE;
+  if (out_dtype == CSA_BF16)
+    hipLaunchKernelGGL(k_dequantize<CSA_BF16>, dim3((unsigned)grid), dim3(256), 0, stream, codes,
+                       scales, blk_cap, blk0, n_blk, d, total, out);
+  else if (out_dtype == CSA_F16)
+    hipLaunchKernelGGL(k_dequantize<CSA_F16>, dim3((unsigned)grid), dim3(256), 0, stream, codes,
+                       scales, blk_cap, blk0, n_blk, d, total, out);
+  else
+    hipLaunchKernelGGL(k_dequantize<CSA_F32>, dim3((unsigned)grid), dim3(256), 0, stream, codes,
+                       scales, blk_cap, blk0, n_blk, d, total, out);
+  CSA_TRY_LAUNCH();
+  return CSA_OK;
+}

@@ -1,0 +1,116 @@
+// Internal helpers shared by the HIP translation units of libcsa (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned short v8us __attribute__((ext_vector_type(8)));
+
+#define CSA_TRY_LAUNCH()                                   \
+  do {                                                     \
+    if (hipGetLastError() != hipSuccess) return CSA_ERR_HIP; \
+  } while (0)
+
+static inline bool csa_aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// ---------------------------------------------------------------- scans ----
+
+// Inclusive prefix sum over the NT threads of a workgroup (NT multiple of
+// 64). `tmp` must hold NT/64 ints of LDS. Returns the inclusive prefix and
+// writes the workgroup total to *total. Contains two barriers.
+template <int NT>
+__device__ inline int wg_scan_incl(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int wv = 0; wv < NT / 64; ++wv) {
+    int s = tmp[wv];
+    pre += (wv < wave) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return x + pre;
+}
+
+// Inclusive prefix sum across the 64 lanes of one wave.
+__device__ inline int wave_scan_incl(int v) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// ------------------------------------------------------------ MXFP4 -----
+
+// E8M0 byte -> float32 scale 2^(s-127). Byte 0 is 2^-127, a float32
+// subnormal.
+__device__ inline float e8m0_to_f32(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+
+// Eight E2M1 codes (a 32-bit word, channel 2i in the low nibble of byte i)
+// times 2^(s-127) -> eight bfloat16 values, using the gfx950 scaled FP4
+// conversion (exact: every result is representable in bfloat16).
+__device__ inline v8bf fp4x8_to_bf16(uint32_t word, float scale) {
+  v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
+  v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
+  v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
+  v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
+  v8bf r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// Same to float16 (exact while the scaled values stay in float16 range).
+__device__ inline v8h fp4x8_to_f16(uint32_t word, float scale) {
+  v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, scale, 0);
+  v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, scale, 1);
+  v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, scale, 2);
+  v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, scale, 3);
+  v8h r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// ----------------------------------------------------------- indexer ----
+
+// Monotone (non-decreasing) map of a non-negative int32 score to one of 512
+// histogram bins: 0 for 0, otherwise the float32 exponent and top 4 mantissa
+// bits (16 bins per octave).
+__device__ inline int score_bin512(int s) {
+  if (s <= 0) return 0;
+  return (int)(__float_as_uint((float)s) >> 19) - 2031;
+}
+
+// 256 bins, 8 per octave.
+__device__ inline int score_bin256(int s) {
+  if (s <= 0) return 0;
+  return (int)(__float_as_uint((float)s) >> 20) - 1015;
+}

@@ -1,0 +1,948 @@
+// Indexer scores + exact top-k over compressed blocks.
+//
+// Method: podcast transcript "DeepSeek-V4.1-Flash: Pushing the Limits of KV
+// Cache Compression", cue 12 (Full layers run their own indexer and keep
+// their own top-k; Reindex layers rescore a shared pool) and cue 14 (the
+// indexer scores every causally visible position; the pool makes later
+// layers' cost independent of the context length); "Frontier Architecture
+// Decoding Notes (4)", section 1 (top-k over 4-token blocks).
+// Score of block b: s = sum_h w[h] * max(0, q[h] . key[b]), int8 inputs, exact
+// int32 accumulation on the int8 matrix cores (v_mfma_i32_16x16x64_i8).
+// Selection order: score descending, then lower block index; output ascending.
+//
+// Two execution plans, both exact (hence bit-identical results):
+//  * split scan (few queries per sequence, or a candidate pool): the entry
+//    range of every query is cut into 2048-entry tiles, one workgroup each.
+//    k_idx_scan streams the int8 keys once (HBM-bound), writes every score to
+//    a slab and adds a 512-bin monotone histogram of its scores into a
+//    per-query global histogram; the last tile to finish derives the
+//    threshold bin. k_idx_select re-reads each tile's slab (same grid, so the
+//    same XCD and its L2), keeps the entries at or above the threshold bin in
+//    index order, and the last tile of each query resolves the exact k-th
+//    score among those few candidates by radix refinement and writes the
+//    ascending index list.
+//  * multi-pass (long query runs sharing a sequence's keys, i.e. prefill
+//    chunks): one workgroup per group of consecutive queries streams the
+//    L2-resident keys once per pass, recomputing the scores on the matrix
+//    cores: pass 1 builds per-query histograms, refinement passes narrow the
+//    threshold to one exact score, and the final pass emits the selected
+//    blocks in ascending order directly.
+#include "csa_internal.h"
+
+namespace {
+
+constexpr int TILE = 2048;       // entries per split-scan workgroup
+constexpr int NB1 = 512;         // split-scan histogram bins
+constexpr int MAX_TILES = 2048;  // split-scan limit: n_max <= TILE * MAX_TILES
+constexpr int PREFILL_MIN_T = 16;
+
+// One 16-entry column tile: A = indexer queries (rows = heads), B = keys
+// (columns = entries). Lane (j + 16g) holds D[head 4g + r][entry j] in
+// acc[r]; after the weighted ReLU and the sum over the four lane groups every
+// lane j + 16g returns the score of entry j.
+template <int KS>
+__device__ inline int score_tile(const v4i (&A)[KS], const v4i (&Bk)[KS], const int (&wr)[4]) {
+  v4i acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[ks], Bk[ks], acc, 0, 0, 0);
+  int p = wr[0] * max(acc[0], 0) + wr[1] * max(acc[1], 0) + wr[2] * max(acc[2], 0) +
+          wr[3] * max(acc[3], 0);
+  p += __shfl_xor(p, 16, 64);
+  p += __shfl_xor(p, 32, 64);
+  return p;
+}
+
+// Coherent (agent-scope) stores/loads for data handed between workgroups of
+// one kernel; together with wait_vmem() before the hand-off counter they need
+// no L2 write-back or invalidate.
+__device__ inline uint64_t pack_cand(int score, int entry) {
+  return (uint64_t)(uint32_t)score | ((uint64_t)(uint32_t)entry << 32);
+}
+__device__ inline void st_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_coherent32(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int ld_coherent32(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int2 ld_cand(const int2* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<int2*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return int2{(int)(uint32_t)v, (int)(uint32_t)(v >> 32)};
+}
+// s_waitcnt vmcnt(0): every vector memory access of this wave has completed
+// (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15).
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Exclusive prefix sum, in place, of an LDS array of n <= 2048 ints, by a
+// 256-thread workgroup. Ends with a barrier.
+__device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
+  const int base = threadIdx.x * 8;
+  int loc[8];
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    loc[j] = (base + j < n) ? a[base + j] : 0;
+    s += loc[j];
+  }
+  int tot;
+  int run = wg_scan_incl<256>(s, tmp, &tot) - s;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (base + j < n) a[base + j] = run;
+    run += loc[j];
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------
+// split scan, phase 1: scores -> slab, per-query score histogram
+// ------------------------------------------------------------------------
+// Every load is unconditional (addresses clamped into the buffers, invalid
+// entries masked after the product) so that a wave keeps 8 x 1 KB of keys in
+// flight; the scores of 4 column tiles are stored by all 64 lanes at once.
+template <int DI, bool CAND>
+__global__ __launch_bounds__(256) void k_idx_scan(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
+    const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
+    const int32_t* __restrict__ cand, int C, int64_t npad, int32_t* __restrict__ slab,
+    uint32_t* __restrict__ hist) {
+  constexpr int KS = (DI + 63) / 64;
+  constexpr int BATCH = 8;
+  __shared__ uint32_t lh[NB1];
+  const int tile = blockIdx.x;
+  const int qi = blockIdx.y;
+  const int b = qi / T;
+  const int64_t t = pos0 + (qi - b * T);
+  int64_t nv = (t + 1) / m;
+  nv = nv < blk_cap ? nv : blk_cap;
+  const int64_t N = CAND ? (int64_t)C : nv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+
+  for (int i = threadIdx.x; i < NB1; i += 256) lh[i] = 0;
+
+  v4i A[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c0 = ks * 64 + 16 * g;
+    if (i16 < Hi && c0 < DI)
+      A[ks] = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)qi * Hi + i16) * DI + c0);
+    else
+      A[ks] = v4i{0, 0, 0, 0};
+  }
+  int wr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g + r;
+    wr[r] = h < Hi ? (int)w[(int64_t)qi * Hi + h] : 0;
+  }
+  __syncthreads();
+
+  const int64_t e_wave = (int64_t)tile * TILE + wave * (TILE / 4);
+  const int8_t* kb = keys + (int64_t)b * blk_cap * DI;
+  const int32_t* cq = CAND ? cand + (int64_t)qi * C : nullptr;
+  int32_t* sq = slab + (int64_t)qi * npad;
+  // lanes with c0 >= DI (only when DI == 32) load a duplicate in-bounds chunk;
+  // their A operand is zero, so the product does not see it
+  int coff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) coff[ks] = (ks * 64 + 16 * g) % DI;
+  const bool loads_ok = nv > 0;  // some key row exists to clamp to
+  if (e_wave < N) {
+#pragma unroll 1
+    for (int bt = 0; bt < TILE / 4 / 16; bt += BATCH) {
+      const int64_t ebase = e_wave + (int64_t)bt * 16;
+      int64_t blk[BATCH];
+      bool valid[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t e = ebase + u * 16 + i16;
+        if (CAND) {
+          const int64_t c = cq[e < N ? e : N - 1];
+          valid[u] = e < N && c >= 0 && c < nv;
+          blk[u] = valid[u] ? c : 0;
+        } else {
+          valid[u] = e < nv;
+          blk[u] = valid[u] ? e : nv - 1;
+        }
+      }
+      v4i Bk[BATCH][KS];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          Bk[u][ks] = loads_ok ? __builtin_nontemporal_load(
+                                     reinterpret_cast<const v4i*>(kb + blk[u] * DI + coff[ks]))
+                               : v4i{0, 0, 0, 0};
+      int sc[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int s = score_tile<KS>(A, Bk[u], wr);
+        sc[u] = valid[u] ? s : -1;
+      }
+      // lane (j + 16g) stores tile 4h+g, entry j: 64 consecutive entries
+#pragma unroll
+      for (int h = 0; h < BATCH / 4; ++h) {
+        const int v = g == 0 ? sc[4 * h] : (g == 1 ? sc[4 * h + 1] : (g == 2 ? sc[4 * h + 2] : sc[4 * h + 3]));
+        const int64_t e = ebase + 64 * h + lane;
+        if (e < N) {
+          sq[e] = v;
+          if (v >= 0) atomicAdd(&lh[score_bin512(v)], 1u);
+        }
+      }
+      if (ebase + BATCH * 16 >= N) break;
+    }
+  }
+  __syncthreads();
+  uint32_t* hq = hist + (int64_t)qi * NB1;
+  for (int i = threadIdx.x; i < NB1; i += 256)
+    if (lh[i]) atomicAdd(&hq[i], lh[i]);
+}
+
+// ------------------------------------------------------------------------
+// split scan, phase 2: candidates at or above the threshold bin, then the
+// exact resolution by the last tile of each query
+// ------------------------------------------------------------------------
+// Dynamic LDS: t_off[MAX_TILES] ints, then a candidate area of cap_lds
+// (score, entry) pairs. The last tile of a query copies the candidates of all
+// tiles into that area in one parallel pass (index order kept) and resolves
+// everything there; a query with more candidates than cap_lds (massive ties)
+// takes the slower path that walks the per-tile lists in global memory.
+__global__ __launch_bounds__(256) void k_idx_select(
+    int T, int m, int64_t pos0, int64_t blk_cap, const int32_t* __restrict__ cand, int C, int k,
+    int n_tiles, int64_t npad, const int32_t* __restrict__ slab, int2* __restrict__ cbuf,
+    int32_t* __restrict__ cnt, uint32_t* __restrict__ hist, uint32_t* __restrict__ done2,
+    int32_t* __restrict__ out_idx, int32_t* __restrict__ out_score, int cap_lds) {
+  extern __shared__ __attribute__((aligned(16))) int smem[];
+  __shared__ int tmp[4];
+  __shared__ int s_last;
+  __shared__ uint32_t bh[256];
+  __shared__ int s_red[8];
+  int* t_off = smem;                    // [MAX_TILES]
+  int* area = smem + MAX_TILES;         // [2 * cap_lds]
+  const int tile = blockIdx.x;
+  const int qi = blockIdx.y;
+  const int b = qi / T;
+  const int64_t t = pos0 + (qi - b * T);
+  int64_t nv = (t + 1) / m;
+  nv = nv < blk_cap ? nv : blk_cap;
+  const int64_t N = cand ? (int64_t)C : nv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int2* cq = cbuf + (int64_t)qi * npad;
+
+  // Threshold bin T1 from the finished histogram (same result in every
+  // workgroup of the query): the bin where the count from the top first
+  // reaches k_eff; A1 = entries in higher bins. Thread j owns bins 511-2j and
+  // 510-2j, so the prefix runs from the top bin down.
+  uint32_t* hq = hist + (int64_t)qi * NB1;
+  const int hb = NB1 - 1 - 2 * (int)threadIdx.x;
+  const int c_hi = (int)hq[hb];
+  const int c_lo = (int)hq[hb - 1];
+  int total_valid;
+  const int incl = wg_scan_incl<256>(c_hi + c_lo, tmp, &total_valid);
+  const int excl = incl - c_hi - c_lo;
+  const int keff = k < total_valid ? k : total_valid;
+  if (keff > 0) {
+    if (excl + c_hi >= keff && excl < keff) {
+      s_red[0] = hb;
+      s_red[1] = excl;
+    }
+    if (incl >= keff && excl + c_hi < keff) {
+      s_red[0] = hb - 1;
+      s_red[1] = excl + c_hi;
+    }
+  }
+  __syncthreads();
+  const int T1 = s_red[0], A1 = s_red[1];
+  __syncthreads();
+
+  if (keff > 0) {
+    const int64_t e0 = (int64_t)tile * TILE + threadIdx.x * 8;
+    const int32_t* sq = slab + (int64_t)qi * npad;
+    int s[8];
+    if (e0 + 8 <= N) {
+      const int4 a = *reinterpret_cast<const int4*>(sq + e0);
+      const int4 c = *reinterpret_cast<const int4*>(sq + e0 + 4);
+      s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
+      s[4] = c.x; s[5] = c.y; s[6] = c.z; s[7] = c.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[j] = (e0 + j < N) ? sq[e0 + j] : -1;
+    }
+    int f = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f += (s[j] >= 0 && score_bin512(s[j]) >= T1);
+    int total;
+    int pos = wg_scan_incl<256>(f, tmp, &total) - f;
+    // candidates and counts are read by another workgroup of this kernel:
+    // agent-scope atomic stores keep them coherent across XCDs without
+    // writing back or invalidating any L2
+    uint64_t* dst = reinterpret_cast<uint64_t*>(cq + (int64_t)tile * TILE);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s[j] >= 0 && score_bin512(s[j]) >= T1)
+        st_coherent(dst + pos++, pack_cand(s[j], (int)(e0 + j)));
+    if (threadIdx.x == 0) st_coherent32(cnt + (int64_t)qi * n_tiles + tile, total);
+  }
+  wait_vmem();  // this thread's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(&done2[qi], 1u) == (uint32_t)(n_tiles - 1));
+  __syncthreads();
+  if (!s_last) return;
+  // every workgroup of this query has read the histogram: clear it (and the
+  // counter) for the next call
+  __hip_atomic_store(&hq[hb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&hq[hb - 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&done2[qi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  int32_t* oi = out_idx + (int64_t)qi * k;
+  int32_t* os = out_score ? out_score + (int64_t)qi * k : nullptr;
+  const int32_t* cqq = cand ? cand + (int64_t)qi * C : nullptr;
+  for (int i = keff + threadIdx.x; i < k; i += 256) {
+    oi[i] = -1;
+    if (os) os[i] = -1;
+  }
+  if (keff == 0) return;
+
+  const int32_t* cntq = cnt + (int64_t)qi * n_tiles;
+  for (int i = threadIdx.x; i < n_tiles; i += 256) t_off[i] = ld_coherent32(cntq + i);
+  __syncthreads();
+  const int last_cnt = t_off[n_tiles - 1];
+  __syncthreads();
+  lds_excl_scan(t_off, n_tiles, tmp);
+  const int M = t_off[n_tiles - 1] + last_cnt;
+
+  int need = keff - A1;  // threshold-bin candidates still to take
+  if (M <= cap_lds) {
+    // ---- fast path: all candidates in LDS, index order kept
+    int* cs = area;
+    int* ce = area + cap_lds;
+    for (int i = threadIdx.x; i < M; i += 256) {
+      int lo = 0, hi = n_tiles - 1;  // last tile with t_off <= i
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t_off[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      const int2 v = ld_cand(cq + (int64_t)lo * TILE + (i - t_off[lo]));
+      cs[i] = v.x;
+      ce[i] = v.y;
+    }
+    __syncthreads();
+    int vmin = 0x7fffffff, vmax = -1;
+    for (int i = threadIdx.x; i < M; i += 256) {
+      const int sv = cs[i];
+      if (score_bin512(sv) == T1) {
+        vmin = min(vmin, sv);
+        vmax = max(vmax, sv);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      vmin = min(vmin, __shfl_xor(vmin, off, 64));
+      vmax = max(vmax, __shfl_xor(vmax, off, 64));
+    }
+    if (lane == 0) {
+      s_red[wave] = vmin;
+      s_red[4 + wave] = vmax;
+    }
+    __syncthreads();
+    int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
+    const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
+    __syncthreads();
+    int R = hi - lo;
+    while (R > 0) {
+      const int bits = 32 - __clz(R);
+      const int shift = bits > 8 ? bits - 8 : 0;
+      bh[threadIdx.x] = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < M; i += 256) {
+        const int sv = cs[i];
+        if (score_bin512(sv) == T1 && sv >= lo && sv - lo <= R)
+          atomicAdd(&bh[(sv - lo) >> shift], 1u);
+      }
+      __syncthreads();
+      const int v = (int)bh[255 - threadIdx.x];
+      int tot;
+      const int inc = wg_scan_incl<256>(v, tmp, &tot);
+      if (inc >= need && inc - v < need) {
+        s_red[0] = 255 - (int)threadIdx.x;
+        s_red[1] = need - (inc - v);
+      }
+      __syncthreads();
+      const int beta = s_red[0];
+      need = s_red[1];
+      __syncthreads();
+      lo += beta << shift;
+      R = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
+    }
+    const int tau = lo;
+    const int take_eq = need;
+    int eq_run = 0, out_run = 0;
+    for (int base = 0; base < M; base += 256) {
+      const int i = base + threadIdx.x;
+      const bool in = i < M;
+      const int sv = in ? cs[i] : -1;
+      const int is_eq = (in && sv == tau) ? 1 : 0;
+      int eq_tot;
+      const int eq_rank = eq_run + wg_scan_incl<256>(is_eq, tmp, &eq_tot) - is_eq;
+      const int take = (in && (sv > tau || (is_eq && eq_rank < take_eq))) ? 1 : 0;
+      int tk_tot;
+      const int pos = out_run + wg_scan_incl<256>(take, tmp, &tk_tot) - take;
+      if (take && pos < keff) {
+        const int e = ce[i];
+        oi[pos] = cqq ? cqq[e] : e;
+        if (os) os[pos] = sv;
+      }
+      eq_run += eq_tot;
+      out_run += tk_tot;
+    }
+    return;
+  }
+
+  // ---- slow path: per-tile lists in global memory (arrays alias the area)
+  int* t_cnt = area;
+  int* t_gt = area + MAX_TILES;
+  int* t_eq = area + 2 * MAX_TILES;
+  int* t_eqb = area + 3 * MAX_TILES;
+  for (int i = threadIdx.x; i < n_tiles; i += 256) t_cnt[i] = ld_coherent32(cntq + i);
+  __syncthreads();
+  int vmin = 0x7fffffff, vmax = -1;
+  for (int tl = wave; tl < n_tiles; tl += 4) {
+    const int c = t_cnt[tl];
+    for (int j = lane; j < c; j += 64) {
+      const int sv = ld_cand(cq + (int64_t)tl * TILE + j).x;
+      if (score_bin512(sv) == T1) {
+        vmin = min(vmin, sv);
+        vmax = max(vmax, sv);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    vmin = min(vmin, __shfl_xor(vmin, off, 64));
+    vmax = max(vmax, __shfl_xor(vmax, off, 64));
+  }
+  if (lane == 0) {
+    s_red[wave] = vmin;
+    s_red[4 + wave] = vmax;
+  }
+  __syncthreads();
+  int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
+  const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
+  __syncthreads();
+  int R = hi - lo;
+  while (R > 0) {
+    const int bits = 32 - __clz(R);
+    const int shift = bits > 8 ? bits - 8 : 0;
+    bh[threadIdx.x] = 0;
+    __syncthreads();
+    for (int tl = wave; tl < n_tiles; tl += 4) {
+      const int c = t_cnt[tl];
+      for (int j = lane; j < c; j += 64) {
+        const int sv = ld_cand(cq + (int64_t)tl * TILE + j).x;
+        if (score_bin512(sv) == T1 && sv >= lo && sv - lo <= R)
+          atomicAdd(&bh[(sv - lo) >> shift], 1u);
+      }
+    }
+    __syncthreads();
+    const int v = (int)bh[255 - threadIdx.x];
+    int tot;
+    const int inc = wg_scan_incl<256>(v, tmp, &tot);
+    if (inc >= need && inc - v < need) {
+      s_red[0] = 255 - (int)threadIdx.x;
+      s_red[1] = need - (inc - v);
+    }
+    __syncthreads();
+    const int beta = s_red[0];
+    need = s_red[1];
+    __syncthreads();
+    lo += beta << shift;
+    R = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
+  }
+  const int tau = lo;
+  const int take_eq = need;
+  for (int tl = wave; tl < n_tiles; tl += 4) {
+    const int c = t_cnt[tl];
+    int gt = 0, eq = 0;
+    for (int j = lane; j < c; j += 64) {
+      const int sv = ld_cand(cq + (int64_t)tl * TILE + j).x;
+      gt += sv > tau;
+      eq += sv == tau;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      gt += __shfl_xor(gt, off, 64);
+      eq += __shfl_xor(eq, off, 64);
+    }
+    if (lane == 0) {
+      t_gt[tl] = gt;
+      t_eq[tl] = eq;
+      t_eqb[tl] = eq;
+    }
+  }
+  __syncthreads();
+  lds_excl_scan(t_eqb, n_tiles, tmp);
+  for (int tl = threadIdx.x; tl < n_tiles; tl += 256) {
+    int take = take_eq - t_eqb[tl];
+    take = take < 0 ? 0 : (take > t_eq[tl] ? t_eq[tl] : take);
+    t_gt[tl] += take;  // selected count of the tile
+  }
+  __syncthreads();
+  lds_excl_scan(t_gt, n_tiles, tmp);  // -> output offset of each tile
+  for (int tl = wave; tl < n_tiles; tl += 4) {
+    const int c = t_cnt[tl];
+    int eq_run = t_eqb[tl];
+    int out_run = t_gt[tl];
+    for (int j0 = 0; j0 < c; j0 += 64) {
+      const int j = j0 + lane;
+      int2 v = int2{-1, -1};
+      if (j < c) v = ld_cand(cq + (int64_t)tl * TILE + j);
+      const bool is_eq = j < c && v.x == tau;
+      const uint64_t meq = __ballot(is_eq);
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      const int eq_rank = eq_run + __popcll(meq & below);
+      const bool take = j < c && (v.x > tau || (is_eq && eq_rank < take_eq));
+      const uint64_t mt = __ballot(take);
+      if (take) {
+        const int pos = out_run + __popcll(mt & below);
+        if (pos < keff) {
+          oi[pos] = cqq ? cqq[v.y] : v.y;
+          if (os) os[pos] = v.x;
+        }
+      }
+      eq_run += __popcll(meq);
+      out_run += __popcll(mt);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// multi-pass plan for long query runs (prefill chunks)
+// ------------------------------------------------------------------------
+// HP = padded head count (4, 8 or 16); rows of an MFMA tile are
+// (query, head) pairs, QPT = 16 / HP queries per row tile; RT row tiles per
+// wave; QG queries per workgroup.
+template <int DI, int HP, int RT>
+__global__ __launch_bounds__(256) void k_idx_prefill(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
+    const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0, int k,
+    int32_t* __restrict__ out_idx, int32_t* __restrict__ out_score) {
+  constexpr int KS = (DI + 63) / 64;
+  constexpr int QPT = 16 / HP;
+  constexpr int QW = QPT * RT;
+  constexpr int QG = 4 * QW;
+  constexpr int NB = 256;
+  constexpr int GPQ = HP / 4;  // lane groups per query in the score layout
+  __shared__ uint32_t hist[QG][NB];
+  __shared__ int st_keff[QG], st_T1[QG], st_need[QG], st_lo[QG], st_R[QG];
+  __shared__ int s_any;
+
+  const int b = blockIdx.y;
+  const int q0 = blockIdx.x * QG;  // first query (index within T) of the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+
+  // A operands and weights for the RT row tiles of this wave
+  v4i A[RT][KS];
+  int wr[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int ql = wave * QW + rt * QPT + i16 / HP;
+    const int h = i16 % HP;
+    const int ti = q0 + ql;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = ks * 64 + 16 * g;
+      if (ti < T && h < Hi && c0 < DI)
+        A[rt][ks] = *reinterpret_cast<const v4i*>(
+            q_idx + (((int64_t)b * T + ti) * Hi + h) * DI + c0);
+      else
+        A[rt][ks] = v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      const int qq = q0 + wave * QW + rt * QPT + row / HP;
+      const int hh = row % HP;
+      wr[rt][r] = (qq < T && hh < Hi) ? (int)w[((int64_t)b * T + qq) * Hi + hh] : 0;
+    }
+  }
+  // the score lanes: lane group g holds query (g / GPQ) of each row tile;
+  // the first lane group of each query "owns" it
+  const bool owner = (g % GPQ) == 0;
+  int my_ti[RT];
+  int64_t my_nv[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    my_ti[rt] = q0 + wave * QW + rt * QPT + g / GPQ;
+    int64_t nv = (pos0 + my_ti[rt] + 1) / m;
+    nv = nv < blk_cap ? nv : blk_cap;
+    my_nv[rt] = my_ti[rt] < T ? nv : 0;
+  }
+  const int t_last = (q0 + QG < T ? q0 + QG : T) - 1;
+  int64_t n_end = (pos0 + t_last + 1) / m;
+  n_end = n_end < blk_cap ? n_end : blk_cap;
+  const int8_t* kb = keys + (int64_t)b * blk_cap * DI;
+
+  // Streams every key tile once and hands the scores to `f(rt, entry, s)`
+  // on owner lanes for visible entries.
+  auto sweep = [&](auto&& f) {
+#pragma unroll 1
+    for (int64_t e0 = 0; e0 < n_end; e0 += 64) {
+      v4i Bk[4][KS];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int64_t e = e0 + u * 16 + i16;
+        e = e < n_end ? e : n_end - 1;  // clamped; entries past n_end are masked
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          Bk[u][ks] = *reinterpret_cast<const v4i*>(kb + e * DI + (ks * 64 + 16 * g) % DI);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t e = e0 + u * 16 + i16;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          v4i acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[rt][ks], Bk[u][ks], acc, 0, 0, 0);
+          int p = wr[rt][0] * max(acc[0], 0) + wr[rt][1] * max(acc[1], 0) +
+                  wr[rt][2] * max(acc[2], 0) + wr[rt][3] * max(acc[3], 0);
+          if (GPQ >= 2) p += __shfl_xor(p, 16, 64);
+          if (GPQ >= 4) p += __shfl_xor(p, 32, 64);
+          f(rt, e, p, owner && e < my_nv[rt]);
+        }
+      }
+    }
+  };
+
+  for (int i = threadIdx.x; i < QG * NB; i += 256) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  // pass 1: level-1 histogram (8 bins per octave)
+  sweep([&](int rt, int64_t e, int s, bool ok) {
+    if (ok) atomicAdd(&hist[wave * QW + rt * QPT + g / GPQ][score_bin256(s)], 1u);
+  });
+  __syncthreads();
+  // threshold bin per query (one thread per query scans from the top)
+  if (threadIdx.x < QG) {
+    const int ql = threadIdx.x;
+    const int ti = q0 + ql;
+    int64_t nv = (pos0 + ti + 1) / m;
+    nv = nv < blk_cap ? nv : blk_cap;
+    const int nvalid = ti < T ? (int)nv : 0;
+    const int keff = k < nvalid ? k : nvalid;
+    int acc = 0, T1 = 0, A1 = 0;
+    if (keff > 0) {
+      for (int bin = NB - 1; bin >= 0; --bin) {
+        const int c = (int)hist[ql][bin];
+        if (acc + c >= keff) {
+          T1 = bin;
+          A1 = acc;
+          break;
+        }
+        acc += c;
+      }
+    }
+    st_keff[ql] = keff;
+    st_T1[ql] = T1;
+    st_need[ql] = keff - A1;
+    // integer range of scores mapped to bin T1 (a little wider than exact
+    // above 2^24, where int->float rounds; the bin test keeps it exact)
+    int lo = 0, R = 0;
+    if (T1 > 0) {
+      const uint32_t fb = (uint32_t)(T1 + 1015) << 20;
+      const double flo = (double)__uint_as_float(fb);
+      const double fhi = (double)__uint_as_float(fb + (1u << 20));
+      const double ulp = flo >= 16777216.0 ? flo / 8388608.0 : 0.0;
+      double dlo = flo - ulp, dhi = fhi + ulp;
+      if (dlo < 0) dlo = 0;
+      if (dhi > 2147483647.0) dhi = 2147483647.0;
+      lo = (int)dlo;
+      R = (int)dhi - lo;
+    }
+    st_lo[ql] = lo;
+    st_R[ql] = (keff > 0) ? R : 0;
+  }
+  __syncthreads();
+
+  // refinement passes until every query has one exact threshold score
+  while (true) {
+    if (threadIdx.x == 0) s_any = 0;
+    __syncthreads();
+    if (threadIdx.x < QG && st_R[threadIdx.x] > 0) s_any = 1;
+    for (int i = threadIdx.x; i < QG * NB; i += 256) (&hist[0][0])[i] = 0;
+    __syncthreads();
+    if (!s_any) break;
+    sweep([&](int rt, int64_t e, int s, bool ok) {
+      const int ql = wave * QW + rt * QPT + g / GPQ;
+      const int R = st_R[ql];
+      if (ok && R > 0 && score_bin256(s) == st_T1[ql]) {
+        const int lo = st_lo[ql];
+        const int bits = 32 - __clz(R);
+        const int shift = bits > 8 ? bits - 8 : 0;
+        if (s >= lo && s - lo <= R) atomicAdd(&hist[ql][(s - lo) >> shift], 1u);
+      }
+    });
+    __syncthreads();
+    if (threadIdx.x < QG) {
+      const int ql = threadIdx.x;
+      const int R = st_R[ql];
+      if (R > 0) {
+        const int bits = 32 - __clz(R);
+        const int shift = bits > 8 ? bits - 8 : 0;
+        int need = st_need[ql], acc = 0, beta = 0;
+        for (int bk = NB - 1; bk >= 0; --bk) {
+          const int c = (int)hist[ql][bk];
+          if (acc + c >= need) {
+            beta = bk;
+            break;
+          }
+          acc += c;
+        }
+        st_need[ql] = need - acc;
+        st_lo[ql] += beta << shift;
+        st_R[ql] = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
+      }
+    }
+    __syncthreads();
+  }
+
+  // emission pass: wave-local, in ascending entry order per query
+  int tau[RT], take_eq[RT], eq_run[RT], out_run[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int ql = wave * QW + rt * QPT + g / GPQ;
+    tau[rt] = st_keff[ql] > 0 ? st_lo[ql] : 0x7fffffff;
+    take_eq[rt] = st_need[ql];
+    eq_run[rt] = 0;
+    out_run[rt] = 0;
+  }
+  const uint64_t below16 = (i16 == 0) ? 0ull : (~0ull >> (64 - i16));
+  sweep([&](int rt, int64_t e, int s, bool ok) {
+    const bool is_eq = ok && s == tau[rt];
+    const uint64_t meq = (__ballot(is_eq) >> (16 * g)) & 0xffffull;
+    const int eq_rank = eq_run[rt] + __popcll(meq & below16);
+    const bool take = ok && (s > tau[rt] || (is_eq && eq_rank < take_eq[rt]));
+    const uint64_t mt = (__ballot(take) >> (16 * g)) & 0xffffull;
+    if (take) {
+      const int64_t row = (int64_t)b * T + my_ti[rt];
+      const int pos = out_run[rt] + __popcll(mt & below16);
+      if (pos < k) {
+        out_idx[row * k + pos] = (int32_t)e;
+        if (out_score) out_score[row * k + pos] = s;
+      }
+    }
+    eq_run[rt] += __popcll(meq);
+    out_run[rt] += __popcll(mt);
+  });
+  // -1 padding after the k_eff selected entries
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (owner && my_ti[rt] < T) {
+      const int64_t row = (int64_t)b * T + my_ti[rt];
+      for (int i = out_run[rt] + i16; i < k; i += 16) {
+        out_idx[row * k + i] = -1;
+        if (out_score) out_score[row * k + i] = -1;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// host side
+// ------------------------------------------------------------------------
+struct IdxLayout {
+  int n_tiles;
+  int64_t npad;
+  int64_t off_slab, off_cbuf, off_hist, off_cnt, off_done2, bytes;
+};
+
+static inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+static IdxLayout idx_layout(int64_t BT, int64_t n_max) {
+  IdxLayout L;
+  int64_t nt = (n_max + TILE - 1) / TILE;
+  L.n_tiles = (int)(nt < 1 ? 1 : nt);
+  L.npad = (int64_t)L.n_tiles * TILE;
+  int64_t o = 0;
+  // header: depends on B*T only, kept zero between calls
+  L.off_done2 = o; o = align_up(o + BT * 4, 256);
+  L.off_hist = o; o = align_up(o + BT * NB1 * 4, 256);
+  // body: rewritten by every call
+  L.off_cnt = o; o = align_up(o + BT * L.n_tiles * 4, 256);
+  L.off_slab = o; o = align_up(o + BT * L.npad * 4, 256);
+  L.off_cbuf = o; o = align_up(o + BT * L.npad * 8, 256);
+  L.bytes = o;
+  return L;
+}
+
+// Candidates the select kernel keeps in LDS: about twice k (the entries above
+// the threshold bin plus that bin), at least enough for the slow-path arrays.
+static int select_cap(int k) {
+  int c = 4096;
+  while (c < 2 * k && c < 16384) c *= 2;
+  return c;
+}
+
+static bool split_plan(int T, const int32_t* cand, int cand_given) {
+  return cand != nullptr || cand_given || T < PREFILL_MIN_T;
+}
+
+struct IdxArgs {
+  const int8_t* q_idx; const int8_t* w; const int8_t* keys; int64_t blk_cap;
+  int B, T, Hi, Di, m; int64_t pos0; const int32_t* cand; int C, k;
+  int32_t* out_idx; int32_t* out_score; void* ws; int64_t ws_bytes; hipStream_t stream;
+};
+
+static int idx_check(const IdxArgs& a, int64_t* n_max) {
+  if (a.B < 0 || a.T < 0 || a.blk_cap < 0 || a.pos0 < 0) return CSA_ERR_SHAPE;
+  if (a.Hi < 1 || a.Hi > 16) return CSA_ERR_SHAPE;
+  if (a.Di != 32 && a.Di != 64 && a.Di != 128) return CSA_ERR_SHAPE;
+  if (a.Hi * a.Di > 1024) return CSA_ERR_SHAPE;
+  if (a.m < 1 || a.k < 1) return CSA_ERR_SHAPE;
+  if (a.cand && a.C < 0) return CSA_ERR_SHAPE;
+  if ((int64_t)a.B * a.T > 65535 * 32768LL) return CSA_ERR_SHAPE;
+  if (a.pos0 + a.T > (int64_t)1 << 40) return CSA_ERR_RANGE;
+  if (a.B == 0 || a.T == 0) return CSA_OK;
+  if (!a.q_idx || !a.w || !a.keys || !a.out_idx) return CSA_ERR_NULL;
+  if (!csa_aligned(a.q_idx, 16) || !csa_aligned(a.keys, 16)) return CSA_ERR_ALIGN;
+  int64_t nv = (a.pos0 + a.T) / a.m;
+  nv = nv < a.blk_cap ? nv : a.blk_cap;
+  *n_max = a.cand ? (int64_t)a.C : nv;
+  if (*n_max > (int64_t)TILE * MAX_TILES) return CSA_ERR_SHAPE;
+  if (nv > 0x7fffffff) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+
+static int idx_phase(const IdxArgs& a, int phase) {
+  int64_t n_max = 0;
+  int st = idx_check(a, &n_max);
+  if (st != CSA_OK || a.B == 0 || a.T == 0) return st;
+  const int BT = a.B * a.T;
+  if (split_plan(a.T, a.cand, 0)) {
+    IdxLayout L = idx_layout(BT, n_max);
+    if (!a.ws) return CSA_ERR_WORKSPACE;
+    if (a.ws_bytes < L.bytes) return CSA_ERR_WORKSPACE;
+    if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
+    char* ws = reinterpret_cast<char*>(a.ws);
+    int32_t* slab = reinterpret_cast<int32_t*>(ws + L.off_slab);
+    int2* cbuf = reinterpret_cast<int2*>(ws + L.off_cbuf);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.off_hist);
+    int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.off_cnt);
+    uint32_t* done2 = reinterpret_cast<uint32_t*>(ws + L.off_done2);
+    const int C = a.cand ? a.C : 0;
+    dim3 grid(L.n_tiles, BT);
+    if (phase == 0) {
+#define CSA_LAUNCH_SCAN(DD, CC)                                                              \
+  hipLaunchKernelGGL((k_idx_scan<DD, CC>), grid, dim3(256), 0, a.stream, a.q_idx, a.w, a.keys, \
+                     a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.cand, C, L.npad, slab, hist)
+      if (a.cand) {
+        if (a.Di == 32) CSA_LAUNCH_SCAN(32, true);
+        else if (a.Di == 64) CSA_LAUNCH_SCAN(64, true);
+        else CSA_LAUNCH_SCAN(128, true);
+      } else {
+        if (a.Di == 32) CSA_LAUNCH_SCAN(32, false);
+        else if (a.Di == 64) CSA_LAUNCH_SCAN(64, false);
+        else CSA_LAUNCH_SCAN(128, false);
+      }
+#undef CSA_LAUNCH_SCAN
+    } else {
+      const int cap_lds = select_cap(a.k);
+      const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int);
+      if (lds > 65536 &&
+          hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_select),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return CSA_ERR_HIP;
+      hipLaunchKernelGGL(k_idx_select, grid, dim3(256), lds, a.stream, a.T, a.m, a.pos0,
+                         a.blk_cap, a.cand, C, a.k, L.n_tiles, L.npad, slab, cbuf, cnt, hist,
+                         done2, a.out_idx, a.out_score, cap_lds);
+    }
+    CSA_TRY_LAUNCH();
+    return CSA_OK;
+  }
+  if (phase != 0) return CSA_OK;
+  const int HP = a.Hi <= 4 ? 4 : (a.Hi <= 8 ? 8 : 16);
+  constexpr int RT = 2;
+  const int QG = 4 * RT * (16 / HP);
+  dim3 grid((a.T + QG - 1) / QG, a.B);
+#define CSA_LAUNCH_PRE(DD, HH)                                                              \
+  hipLaunchKernelGGL((k_idx_prefill<DD, HH, RT>), grid, dim3(256), 0, a.stream, a.q_idx, a.w, \
+                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.k, a.out_idx, a.out_score)
+#define CSA_LAUNCH_PRE_H(DD) \
+  if (HP == 4) CSA_LAUNCH_PRE(DD, 4); else if (HP == 8) CSA_LAUNCH_PRE(DD, 8); else CSA_LAUNCH_PRE(DD, 16)
+  if (a.Di == 32) { CSA_LAUNCH_PRE_H(32); }
+  else if (a.Di == 64) { CSA_LAUNCH_PRE_H(64); }
+  else { CSA_LAUNCH_PRE_H(128); }
+#undef CSA_LAUNCH_PRE_H
+#undef CSA_LAUNCH_PRE
+  CSA_TRY_LAUNCH();
+  return CSA_OK;
+}
+
+__global__ void k_fill_zero(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t j = i; j < n; j += stride) p[j] = 0u;
+}
+
+}  // namespace
+
+extern "C" int64_t csa_index_topk_workspace(int B, int T, int64_t n_max, int k, int cand_given) {
+  (void)k;
+  if (B < 0 || T < 0 || n_max < 0) return -1;
+  if (!split_plan(T, nullptr, cand_given)) return 0;
+  return idx_layout((int64_t)B * T, n_max).bytes;
+}
+
+#define CSA_IDX_ARGS                                                                      \
+  IdxArgs a{q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos0, cand, C, k, out_idx, out_score, \
+            workspace, ws_bytes, stream}
+
+extern "C" int csa_index_scan(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                              int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                              const int32_t* cand, int C, int k, int32_t* out_idx,
+                              int32_t* out_score, void* workspace, int64_t ws_bytes,
+                              hipStream_t stream) {
+  CSA_IDX_ARGS;
+  return idx_phase(a, 0);
+}
+
+extern "C" int csa_index_select(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                                int64_t blk_cap, int B, int T, int Hi, int Di, int m,
+                                int64_t pos0, const int32_t* cand, int C, int k,
+                                int32_t* out_idx, int32_t* out_score, void* workspace,
+                                int64_t ws_bytes, hipStream_t stream) {
+  CSA_IDX_ARGS;
+  return idx_phase(a, 1);
+}
+
+extern "C" int csa_index_topk(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                              int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                              const int32_t* cand, int C, int k, int32_t* out_idx,
+                              int32_t* out_score, void* workspace, int64_t ws_bytes,
+                              hipStream_t stream) {
+  CSA_IDX_ARGS;
+  int st = idx_phase(a, 0);
+  if (st != CSA_OK) return st;
+  return idx_phase(a, 1);
+}
+
+extern "C" int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream) {
+  if (bytes < 0 || bytes % 4) return CSA_ERR_SHAPE;
+  if (bytes == 0) return CSA_OK;
+  if (!ws) return CSA_ERR_NULL;
+  if (!csa_aligned(ws, 4)) return CSA_ERR_ALIGN;
+  const int64_t n = bytes / 4;
+  int64_t grid = (n + 255) / 256;
+  grid = grid > 65536 ? 65536 : grid;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<uint32_t*>(ws), n);
+  CSA_TRY_LAUNCH();
+  return CSA_OK;
+}

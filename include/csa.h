@@ -1,0 +1,213 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) compressed sparse attention library.
+ *
+ * The method (DeepSeek-V4-style compressed sparse attention) as described on
+ * the public pages this library follows:
+ *  - "Frontier Architecture Decoding Notes (4): DeepSeek V4", section 1
+ *    "Attention: CSA + HCA Hybrid": the KV is compressed into 4-token blocks
+ *    and a top-k of blocks is attended (CSA); a much heavier compression (up
+ *    to 128 tokens per entry) is attended densely (HCA); the newest 128
+ *    tokens are attended uncompressed.
+ *  - "Recent Developments in LLM Architectures: KV Sharing, mHC, and
+ *    Compressed Attention", section "Data": the cache is shortened along the
+ *    sequence by summarising groups of tokens.
+ *  - podcast transcript "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+ *    Compression": cue 8 (one shared latent entry serves every query head),
+ *    cue 12 (Full / Reindex / Reuse layer modes), cue 14 (the indexer scores
+ *    every causally visible entry; Reindex layers search a shared candidate
+ *    pool), cue 16 (the main cache is MXFP4 with E2M1 elements and is
+ *    dequantised just before attention).
+ * Steps the pages leave open are fixed as follows: a block's entry is the
+ * softmax-gated weighted sum of its m token latents (one gate logit per
+ * token); MXFP4 follows the OCP MX v1.0 rule (one E8M0 scale per 32
+ * elements, exponent floor(log2 amax) - 2, round-to-nearest-even on the E2M1
+ * grid, saturating); the indexer score of block b is
+ * sum_h w[h] * max(0, q[h] . key[b]) in exact int32, ties broken toward the
+ * lower block index; all selected entries and the window share one softmax,
+ * keys and values both being the latent row.
+ *
+ * Conventions for every call:
+ *  - All data pointers are DEVICE pointers on the current HIP device. The
+ *    caller owns every buffer; the library allocates nothing.
+ *  - Calls are asynchronous: they enqueue kernels on `stream` and return.
+ *    Argument errors are detected on the host before anything is launched
+ *    and return a negative csa_status; a failed launch returns CSA_ERR_HIP.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - bfloat16 data is passed as uint16_t bit patterns.
+ *  - Layouts are dense and row-major in the order the brackets give.
+ *  - Calls that share a workspace must not overlap in time (same stream, or
+ *    externally ordered). Calls with distinct workspaces are independent.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_NULL = -1,       /* a required pointer is NULL                     */
+  CSA_ERR_SHAPE = -2,      /* unsupported or inconsistent sizes              */
+  CSA_ERR_RANGE = -3,      /* positions / block ranges outside the buffers   */
+  CSA_ERR_WORKSPACE = -4,  /* workspace missing or smaller than required     */
+  CSA_ERR_DTYPE = -5,      /* unknown dtype code                             */
+  CSA_ERR_HIP = -6,        /* a HIP launch or runtime call failed            */
+  CSA_ERR_ALIGN = -7       /* a pointer or stride breaks the stated alignment */
+};
+
+enum csa_dtype { CSA_BF16 = 0, CSA_F32 = 1, CSA_F16 = 2 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* csa_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int csa_version(void);
+
+/* Closed form, host only: bytes of MXFP4 codes + scales for n_tokens tokens
+ * compressed m tokens per entry, d channels: ceil(n_tokens/m) * (d/2 + d/32).
+ * Returns -1 for n_tokens < 0, m < 1 or d not a positive multiple of 32. */
+int64_t csa_cache_bytes(int64_t n_tokens, int d, int m);
+
+/* ---------------------------------------------------------------------------
+ * Block compression + MXFP4 quantisation (the compressed cache write).
+ * Summarises tokens [tok0, tok0 + n_tok) of each of B sequences into entries
+ * tok0/m .. ceil((tok0 + n_tok)/m) - 1 ("Frontier Architecture Decoding
+ * Notes (4)", section 1: 4-token CSA blocks, up to 128 for HCA; podcast
+ * cue 16: FP4 cache). For each block, w = softmax(gate over its tokens) and
+ * p = sum_j w_j * kv_j, computed in float64; then every 32-channel group of p
+ * is quantised to MXFP4. A final partial block pools the tokens present.
+ *   kv     float32 [B][n_tok][kv_ld] (first d columns used), 16-byte aligned,
+ *          kv_ld % 4 == 0
+ *   gate   float32 [B][n_tok]
+ *   codes  uint8  [B][blk_cap][d/2]  E2M1 codes, channel 2i in the low nibble
+ *          of byte i (sign in bit 3); 4-byte aligned
+ *   scales uint8  [B][blk_cap][d/32] E8M0 exponents (value 2^(byte-127))
+ * Requires 1 <= m <= 128, tok0 % m == 0, d in {32, 64, 128, 256, 512},
+ * n_tok >= 0, and the last entry < blk_cap (else CSA_ERR_RANGE).
+ * Inputs must be finite. Entries outside the range are left untouched.
+ * ------------------------------------------------------------------------- */
+int csa_compress_quantize(const float* kv, int64_t kv_ld, const float* gate,
+                          int B, int64_t tok0, int64_t n_tok, int d, int m,
+                          uint8_t* codes, uint8_t* scales, int64_t blk_cap,
+                          hipStream_t stream);
+
+/* Dequantise entries [blk0, blk0 + n_blk) of each sequence (podcast cue 16:
+ * the cache is expanded just before attention) with the same conversion the
+ * attention kernels use. out: [B][n_blk][d] in out_dtype (CSA_BF16, CSA_F16
+ * or CSA_F32). BF16 and F32 are exact for scale bytes up to 252 (the largest
+ * a finite float32 input can produce; above it large codes overflow to
+ * +-inf); F16 is exact for scale bytes in [104, 140]. */
+int csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t blk_cap,
+                   int B, int64_t blk0, int64_t n_blk, int d,
+                   void* out, int out_dtype, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Indexer + top-k (podcast cues 12 and 14: a light indexer scores every
+ * causally visible compressed entry and keeps the top-k; a Reindex layer
+ * scores only a candidate pool that an earlier Full layer chose).
+ * Queries sit at positions pos0 .. pos0 + T - 1 of every sequence. Block b is
+ * visible to position t when (b + 1) * m - 1 <= t (and b < blk_cap).
+ *   q_idx  int8 [B][T][Hi][Di]        indexer queries, 16-byte aligned
+ *   w      int8 [B][T][Hi]            head weights, must lie in [0, 127]
+ *   keys   int8 [B][blk_cap][Di]      one key per entry, 16-byte aligned
+ *   cand   int32 [B][T][C] or NULL    Reindex pool: block ids in ascending
+ *          order, -1 entries anywhere are ignored, and so are blocks that are
+ *          not visible. The tie-break then follows the pool order, which for
+ *          an ascending pool is the block order.
+ *   out_idx   int32 [B][T][k]  the k_eff = min(k, #candidates) best blocks in
+ *             ascending block order, then -1
+ *   out_score int32 [B][T][k] or NULL: their scores (-1 in padding)
+ * Score: s(b) = sum_h w[h] * max(0, sum_c q_idx[h][c] * keys[b][c]), exact in
+ * int32 (Hi * Di <= 1024 keeps it below 2^31). Order: score descending, then
+ * lower block index. Supports 1 <= Hi <= 16, Di in {32, 64, 128}, k >= 1.
+ * Workspace: csa_index_topk_workspace(...) bytes of device memory. Its head
+ * holds per-query counters and histograms whose layout depends on B*T only:
+ * zero-fill the workspace (csa_workspace_clear) after allocating it, again
+ * whenever B*T changes, and after any failed call. A successful call leaves
+ * that head zero again, so a decode loop with a fixed B*T reuses one
+ * workspace without clearing, whatever n_max does. n_max is the largest
+ * number of candidates a query can have: C when a pool is given, else
+ * min(blk_cap, (pos0+T)/m).
+ * ------------------------------------------------------------------------- */
+int64_t csa_index_topk_workspace(int B, int T, int64_t n_max, int k, int cand_given);
+
+int csa_index_topk(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                   int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                   const int32_t* cand, int C, int k,
+                   int32_t* out_idx, int32_t* out_score,
+                   void* workspace, int64_t ws_bytes, hipStream_t stream);
+
+/* The two launches csa_index_topk makes, exposed so a caller can place events
+ * or other work between them: csa_index_topk == csa_index_scan followed by
+ * csa_index_select with identical arguments. For few queries per sequence
+ * (T < 16) or a candidate pool, scan streams the keys and writes exact scores
+ * plus a per-query score histogram into the workspace, and select turns them
+ * into the sorted index list. For longer query runs scan does the whole job
+ * and select enqueues nothing. */
+int csa_index_scan(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                   int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                   const int32_t* cand, int C, int k,
+                   int32_t* out_idx, int32_t* out_score,
+                   void* workspace, int64_t ws_bytes, hipStream_t stream);
+int csa_index_select(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                     int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                     const int32_t* cand, int C, int k,
+                     int32_t* out_idx, int32_t* out_score,
+                     void* workspace, int64_t ws_bytes, hipStream_t stream);
+
+/* Zero-fill a workspace with a kernel on `stream` (no hipMemset, so it may be
+ * captured in a graph). bytes must be a multiple of 4 and ws 4-byte aligned. */
+int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse attention with sliding window ("Frontier Architecture Decoding
+ * Notes (4)", section 1; podcast cues 12 and 16). For the query at position
+ * t = pos0 + i of sequence b, every one of the H heads attends, under ONE
+ * softmax, to
+ *   - the entries idx[b][i][0..k) (-1 or out-of-range slots are skipped;
+ *     order is irrelevant; a Reuse layer passes an earlier layer's idx), each
+ *     dequantised from MXFP4, and
+ *   - the window tokens max(0, t-W+1) .. t, read from the bfloat16 ring
+ *     win[b][p % Wcap].
+ * Keys and values are both the latent row; logit = softmax_scale * <q_h, row>.
+ *   q    bf16 [B][T][H][d]         16-byte aligned
+ *   win  bf16 [B][Wcap][d]         16-byte aligned; Wcap >= W + T - 1
+ *   out  [B][T][H][d] in out_dtype (CSA_BF16 or CSA_F32)
+ *   lse  float32 [B][T][H] or NULL: natural-log log-sum-exp of the logits
+ * Supports d in {128, 256, 512}, 1 <= H <= 64, 1 <= W <= Wcap, k >= 0.
+ * Numerics: q.k products use the exact bfloat16 values with float32
+ * accumulation; probabilities and values enter the value product as float16
+ * (entries are exact in float16 while their scale byte lies in [104, 140]),
+ * accumulated in float32. Workspace: csa_attn_workspace(...) bytes (no
+ * initialisation needed); it may be NULL when that size is 0.
+ * ------------------------------------------------------------------------- */
+int64_t csa_attn_workspace(int B, int T, int H, int d, int64_t n_slots);
+
+int csa_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                    int64_t blk_cap, const int32_t* idx, int k,
+                    const uint16_t* win, int Wcap, int W,
+                    int B, int T, int H, int d, int64_t pos0, float softmax_scale,
+                    void* out, int out_dtype, float* lse,
+                    void* workspace, int64_t ws_bytes, hipStream_t stream);
+
+/* Heavily compressed (dense) attention: csa_sparse_attn with the entry set =
+ * every visible block of an m-token cache, b with (b + 1) * m - 1 <= t
+ * ("Frontier Architecture Decoding Notes (4)", section 1: HCA, up to 128
+ * tokens per entry, attended densely). n_slots for the workspace query is
+ * min(blk_cap, (pos0 + T) / m) + W. */
+int hca_dense_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                   int64_t blk_cap, int m,
+                   const uint16_t* win, int Wcap, int W,
+                   int B, int T, int H, int d, int64_t pos0, float softmax_scale,
+                   void* out, int out_dtype, float* lse,
+                   void* workspace, int64_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

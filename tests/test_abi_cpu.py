@@ -1,0 +1,91 @@
+"""The C-ABI library loads and exports every symbol the header declares; host
+only argument checks return their status codes (no GPU needed: these calls
+return before any HIP call)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import compressed_sparse_attention_compress_amd as csa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(csa.LIB_PATH):
+        from compressed_sparse_attention_compress_amd import _build
+        _build.build()
+    return csa.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "csa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:csa|hca)_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) >= 12
+    assert sorted(csa.EXPORTED) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    for s in range(-7, 1):
+        assert L.csa_status_string(s).startswith(b"CSA")
+    assert L.csa_version() >= 100
+
+
+def test_cache_bytes_closed_form(L):
+    for d in (32, 128, 512):
+        for m in (1, 4, 128):
+            for n in (0, 1, 4, 5, 1 << 20, 3 * (1 << 20) + 1):
+                assert L.csa_cache_bytes(n, d, m) == math.ceil(n / m) * (d // 2 + d // 32)
+    assert L.csa_cache_bytes((1 << 20) * 8, 512, 4) == 8 * 262144 * 272
+    assert L.csa_cache_bytes(-1, 512, 4) == -1
+    assert L.csa_cache_bytes(8, 100, 4) == -1
+
+
+def test_argument_errors_before_launch(L):
+    P = ctypes.c_void_p
+    fake = P(256)
+    # compress: m out of range, d unsupported, tok0 not block aligned, NULL
+    assert L.csa_compress_quantize(fake, 512, fake, 1, 0, 8, 512, 0, fake, fake, 4, None) == -2
+    assert L.csa_compress_quantize(fake, 512, fake, 1, 0, 8, 100, 4, fake, fake, 4, None) == -2
+    assert L.csa_compress_quantize(fake, 512, fake, 1, 2, 8, 512, 4, fake, fake, 4, None) == -3
+    assert L.csa_compress_quantize(None, 512, fake, 1, 0, 8, 512, 4, fake, fake, 4, None) == -1
+    assert L.csa_compress_quantize(fake, 512, fake, 1, 0, 8, 512, 4, fake, fake, 1, None) == -3
+    assert L.csa_compress_quantize(P(258), 512, fake, 1, 0, 8, 512, 4, fake, fake, 4, None) == -7
+    # indexer: bad Hi / Di / k, missing workspace
+    args = lambda Hi, Di, k, ws: (fake, fake, fake, 100, 1, 1, Hi, Di, 4, 399, None, 0, k,
+                                  fake, None, ws, 1 << 20, None)
+    assert L.csa_index_topk(*args(0, 64, 8, fake)) == -2
+    assert L.csa_index_topk(*args(8, 48, 8, fake)) == -2
+    assert L.csa_index_topk(*args(8, 64, 0, fake)) == -2
+    assert L.csa_index_topk(*args(8, 64, 8, None)) == -4
+    assert L.csa_index_topk(fake, fake, fake, 100, 1, 1, 8, 64, 4, 399, None, 0, 8, fake, None,
+                            fake, 16, None) == -4
+    # attention: bad d, H, window ring too small, dtype
+    a = lambda d, H, W, Wcap, T, dt: (fake, fake, fake, 100, fake, 8, fake, Wcap, W, 1, T, H, d,
+                                      399, ctypes.c_float(1.0), fake, dt, None, fake, 1 << 30,
+                                      None)
+    assert L.csa_sparse_attn(*a(96, 8, 128, 128, 1, 0)) == -2
+    assert L.csa_sparse_attn(*a(512, 65, 128, 128, 1, 0)) == -2
+    assert L.csa_sparse_attn(*a(512, 64, 128, 128, 2, 0)) == -3
+    assert L.csa_sparse_attn(*a(512, 64, 0, 128, 1, 0)) == -2
+    assert L.csa_sparse_attn(*a(512, 64, 128, 128, 1, 7)) == -5
+
+
+def test_workspace_sizes(L):
+    # decode: split scan needs a workspace, long query runs need none
+    assert L.csa_index_topk_workspace(8, 1, 262144, 1024, 0) > 8 * 262144 * 12
+    assert L.csa_index_topk_workspace(1, 8192, 32768, 512, 0) == 0
+    assert L.csa_index_topk_workspace(16, 1, 4096, 512, 1) > 0
+    assert L.csa_attn_workspace(1, 8192, 64, 512, 640) == 0
+    assert L.csa_attn_workspace(8, 1, 64, 512, 1152) >= 8 * 9 * 64 * 512 * 4

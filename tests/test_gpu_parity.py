@@ -1,0 +1,385 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs. Cache bytes and top-k index sets must be bit-identical;
+attention outputs must stay within 2e-3 x RMS(reference) beyond the final
+output rounding."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_compress_amd as csa
+import oracle.csa_oracle as O
+import synth
+from parity_util import REL_TOL, attn_excess_error, bf16_bits, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def gen(seed, *parts):
+    return synth.generator(DEV, seed, *parts)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------ dequantise ----
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+def test_dequantize_exact(dtype):
+    say("dequantize", dtype)
+    B, cap, d = 2, 64, 512
+    g = gen(1, "deq")
+    codes = torch.randint(0, 256, (B, cap, d // 2), generator=g, device=DEV, dtype=torch.uint8)
+    if dtype == torch.float16:
+        sc = torch.randint(104, 141, (B, cap, d // 32), generator=g, device=DEV)
+    else:
+        pool = torch.tensor([1, 2, 60, 100, 103, 120, 126, 127, 128, 140, 142, 200, 251, 252],
+                            device=DEV)
+        sc = pool[torch.randint(0, len(pool), (B, cap, d // 32), generator=g, device=DEV)]
+    scales = sc.to(torch.uint8).contiguous()
+    out = torch.empty(B, 40, d, device=DEV, dtype=dtype)
+    csa.dequantize(codes, scales, 7, 40, out)
+    torch.cuda.synchronize()
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    for b in range(B):
+        ref = O.dequantize_rows(c[b, 7:47], s[b, 7:47])
+        got = out[b].cpu().double().numpy()
+        assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:5]
+
+
+def test_dequantize_scale_byte_zero():
+    """E8M0 byte 0 (2^-127): values are bfloat16 subnormals."""
+    say("dequantize scale 0")
+    codes = torch.arange(256, device=DEV, dtype=torch.int32).to(torch.uint8).reshape(1, 1, 256)
+    scales = torch.zeros(1, 1, 16, device=DEV, dtype=torch.uint8)
+    out = torch.empty(1, 1, 512, device=DEV, dtype=torch.float32)
+    csa.dequantize(codes, scales, 0, 1, out)
+    ref = O.dequantize_rows(codes[0].cpu().numpy(), scales[0].cpu().numpy())
+    assert np.array_equal(out[0].cpu().double().numpy(), ref)
+
+
+# -------------------------------------------------------------- compress ----
+
+def _compress_case(B, L, d, m, tok0, seed, scale=1.0, chunks=None):
+    g = gen(seed, "cmp", B, L, d, m)
+    kv = torch.randn(B, L, d, generator=g, device=DEV) * scale
+    gate = torch.randn(B, L, generator=g, device=DEV)
+    cap = O.n_blocks(tok0 + L, m) + 3
+    codes = torch.full((B, cap, d // 2), 0xAB, device=DEV, dtype=torch.uint8)
+    scales = torch.full((B, cap, d // 32), 0xCD, device=DEV, dtype=torch.uint8)
+    chunks = chunks or [L]
+    t = 0
+    for n in chunks:
+        csa.compress_quantize(kv[:, t:t + n].contiguous(), gate[:, t:t + n].contiguous(),
+                              tok0 + t, m, codes, scales)
+        t += n
+    torch.cuda.synchronize()
+    kvn, gn = kv.cpu().numpy(), gate.cpu().numpy()
+    cn, sn = codes.cpu().numpy(), scales.cpu().numpy()
+    b0 = tok0 // m
+    for b in range(B):
+        rc, rs = O.compress_quantize(kvn[b], gn[b], m)
+        nb = rc.shape[0]
+        flag = O.near_decision_mask(kvn[b], gn[b], m)
+        assert not flag.any()
+        assert np.array_equal(cn[b, b0:b0 + nb], rc), (b, np.argwhere(cn[b, b0:b0 + nb] != rc)[:4])
+        assert np.array_equal(sn[b, b0:b0 + nb], rs)
+        # untouched outside the written range
+        assert (cn[b, :b0] == 0xAB).all() and (cn[b, b0 + nb:] == 0xAB).all()
+        assert (sn[b, b0 + nb:] == 0xCD).all()
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256, 512])
+@pytest.mark.parametrize("m", [1, 3, 4, 128])
+def test_compress_shapes(d, m):
+    say("compress", d, m)
+    _compress_case(2, 517, d, m, 0, seed=3)
+
+
+def test_compress_offset_and_chunks():
+    say("compress chunks")
+    _compress_case(1, 4096 + 6, 512, 4, 8, seed=4, chunks=[1024, 2048, 1030])
+    _compress_case(3, 300, 128, 4, 400, seed=5, scale=1e-30)
+    _compress_case(1, 256, 512, 128, 0, seed=6, scale=3e4)
+
+
+def test_compress_tiny_workload():
+    """The tiny causal workload (1 x 1024 tokens, d=128, m=4) from synth."""
+    say("compress tiny_causal")
+    wl = synth.WORKLOADS["tiny_causal"]
+    kv = synth.latent_range(wl, 0, 0, wl.L, DEV)[None].contiguous()
+    gate = synth.latent_range(wl, 0, 0, wl.L, DEV, gate=True)[None].contiguous()
+    codes = torch.empty(1, wl.n_blocks, wl.d // 2, device=DEV, dtype=torch.uint8)
+    scales = torch.empty(1, wl.n_blocks, wl.d // 32, device=DEV, dtype=torch.uint8)
+    csa.compress_quantize(kv, gate, 0, wl.m, codes, scales)
+    rc, rs = O.compress_quantize(kv[0].cpu().numpy(), gate[0].cpu().numpy(), wl.m)
+    assert np.array_equal(codes[0].cpu().numpy(), rc)
+    assert np.array_equal(scales[0].cpu().numpy(), rs)
+
+
+# --------------------------------------------------------------- indexer ----
+
+def _index_case(B, T, Hi, Di, m, pos0, k, blk_cap, seed, cand_C=0, wzero=False, keyrange=8,
+                phases=False):
+    g = gen(seed, "idx", B, T, Hi, Di)
+    q = torch.randint(-8, 8, (B, T, Hi, Di), generator=g, device=DEV, dtype=torch.int8)
+    w = torch.randint(0, 4, (B, T, Hi), generator=g, device=DEV, dtype=torch.int8)
+    if wzero:
+        w.zero_()
+    keys = torch.randint(-keyrange, keyrange, (B, blk_cap, Di), generator=g, device=DEV,
+                         dtype=torch.int8)
+    cand = None
+    if cand_C:
+        nv = min(blk_cap, (pos0 + T) // m)
+        pool = torch.stack([torch.randperm(nv + 50, generator=g, device=DEV)[:cand_C]
+                            for _ in range(B * T)]).reshape(B, T, cand_C)
+        pool = torch.where(pool >= nv + 40, torch.full_like(pool, -1), pool)
+        cand = torch.sort(torch.where(pool < 0, torch.full_like(pool, 1 << 30), pool), dim=2)[0]
+        cand = torch.where(cand == (1 << 30), torch.full_like(cand, -1), cand).to(torch.int32)
+        cand = cand.contiguous()
+    oi = torch.full((B, T, k), -7, device=DEV, dtype=torch.int32)
+    os_ = torch.full((B, T, k), -7, device=DEV, dtype=torch.int32)
+    if phases:
+        csa.index_scan(q, w, keys, m, pos0, k, oi, os_, cand=cand)
+        csa.index_select(q, w, keys, m, pos0, k, oi, os_, cand=cand)
+    else:
+        csa.index_topk(q, w, keys, m, pos0, k, oi, os_, cand=cand)
+    torch.cuda.synchronize()
+    qn, wn, kn = q.cpu().numpy(), w.cpu().numpy(), keys.cpu().numpy()
+    oin, osn = oi.cpu().numpy(), os_.cpu().numpy()
+    cn = cand.cpu().numpy() if cand is not None else None
+    for b in range(B):
+        for ti in range(T):
+            ref_i, ref_s = O.index_topk(qn[b, ti], wn[b, ti], kn[b], m, pos0 + ti, k,
+                                        cand=None if cn is None else cn[b, ti])
+            assert np.array_equal(oin[b, ti], ref_i), (b, ti, oin[b, ti][:8], ref_i[:8])
+            assert np.array_equal(osn[b, ti], ref_s), (b, ti)
+    return oi
+
+
+@pytest.mark.parametrize("Hi,Di", [(1, 32), (3, 64), (4, 32), (8, 64), (16, 64), (8, 128)])
+def test_index_decode_shapes(Hi, Di):
+    say("index decode", Hi, Di)
+    _index_case(3, 2, Hi, Di, 4, 4 * 5000 - 2, 64, 5100, seed=7)
+
+
+def test_index_decode_edges():
+    say("index decode edges")
+    _index_case(2, 1, 8, 64, 4, 2, 16, 64, seed=8)             # no visible block yet
+    _index_case(2, 1, 8, 64, 4, 40, 64, 64, seed=9)            # k > visible
+    _index_case(2, 3, 8, 64, 4, 4 * 3000, 100, 3000, seed=10, wzero=True)  # all ties
+    _index_case(2, 1, 8, 64, 4, 4 * 9000, 300, 9000, seed=11, keyrange=1)  # massive ties
+    _index_case(1, 1, 8, 64, 1, 2047, 2048, 4096, seed=12)     # k == visible exactly
+    _index_case(2, 2, 8, 64, 4, 4 * 20000, 1000, 20000, seed=13, phases=True)
+
+
+def test_index_candidates():
+    say("index candidates")
+    _index_case(4, 1, 8, 64, 4, 4 * 10000 - 1, 128, 10000, seed=14, cand_C=4096)
+    _index_case(2, 2, 8, 64, 4, 4 * 3000 - 1, 512, 3000, seed=15, cand_C=600)
+    _index_case(2, 1, 8, 64, 4, 4 * 3000 - 1, 64, 3000, seed=16, cand_C=300, wzero=True)
+
+
+@pytest.mark.parametrize("Hi,Di", [(4, 32), (8, 64), (16, 64), (2, 128), (5, 64)])
+def test_index_prefill_shapes(Hi, Di):
+    say("index prefill", Hi, Di)
+    _index_case(2, 100, Hi, Di, 4, 3000, 40, 2000, seed=17)
+
+
+def test_index_prefill_edges():
+    say("index prefill edges")
+    _index_case(1, 64, 8, 64, 4, 0, 16, 64, seed=18)             # starts at position 0
+    _index_case(1, 40, 8, 64, 4, 400, 32, 200, seed=19, wzero=True)
+    _index_case(1, 33, 8, 64, 4, 800, 64, 1000, seed=20, keyrange=1)
+    _index_case(1, 17, 8, 64, 1, 1000, 600, 1100, seed=21)
+
+
+def test_index_tiny_workload():
+    """All 1024 queries of the tiny causal workload (Hi=4, Di=32, k=16)."""
+    say("index tiny_causal")
+    wl = synth.WORKLOADS["tiny_causal"]
+    q, w = synth.indexer_queries(wl, DEV)
+    keys = synth.indexer_keys(wl, DEV)
+    oi = torch.empty(1, wl.T, wl.k, device=DEV, dtype=torch.int32)
+    csa.index_topk(q, w, keys, wl.m, 0, wl.k, oi)
+    qn, wn, kn, oin = q.cpu().numpy(), w.cpu().numpy(), keys.cpu().numpy(), oi.cpu().numpy()
+    for t in range(wl.T):
+        ref, _ = O.index_topk(qn[0, t], wn[0, t], kn[0], wl.m, t, wl.k)
+        assert np.array_equal(oin[0, t], ref), t
+
+
+# ------------------------------------------------------------- attention ----
+
+def _attn_world(B, L, d, m, Wcap, seed, H, T, W=128):
+    g = gen(seed, "attn", B, L, d, m)
+    kv = torch.randn(B, L, d, generator=g, device=DEV)
+    gate = torch.randn(B, L, generator=g, device=DEV)
+    cap = O.n_blocks(L, m)
+    codes = torch.empty(B, cap, d // 2, device=DEV, dtype=torch.uint8)
+    scales = torch.empty(B, cap, d // 32, device=DEV, dtype=torch.uint8)
+    csa.compress_quantize(kv, gate, 0, m, codes, scales)
+    win = torch.zeros(B, Wcap, d, device=DEV, dtype=torch.bfloat16)
+    t0 = max(0, L - Wcap)
+    pos = torch.arange(t0, L, device=DEV)
+    win[:, pos % Wcap] = kv[:, t0:L].to(torch.bfloat16)
+    q = (torch.randn(B, T, H, d, generator=g, device=DEV) / math.sqrt(d)).to(torch.bfloat16)
+    return dict(codes=codes, scales=scales, win=win, q=q, cap=cap)
+
+
+def _check_attn(wd, idx, pos0, W, out, lse, dense_m=None, scale=1.0):
+    torch.cuda.synchronize()
+    B, T, H, d = wd["q"].shape
+    cn, sn = wd["codes"].cpu().numpy(), wd["scales"].cpu().numpy()
+    wn = bf16_bits(wd["win"])
+    qn = bf16_bits(wd["q"])
+    on = to_np(out)
+    ln = lse.cpu().numpy() if lse is not None else None
+    idn = idx.cpu().numpy() if idx is not None else None
+    refs, lrefs = [], []
+    for b in range(B):
+        for ti in range(T):
+            t = pos0 + ti
+            if dense_m is None:
+                o, l = O.sparse_attn(qn[b, ti], cn[b], sn[b], idn[b, ti], wn[b], wn.shape[1], W, t,
+                                     scale)
+            else:
+                o, l = O.hca_dense_attn(qn[b, ti], cn[b], sn[b], dense_m, wn[b], wn.shape[1], W, t,
+                                        scale)
+            refs.append(o)
+            lrefs.append(l)
+    ref = np.stack(refs).reshape(B, T, H, d)
+    lref = np.stack(lrefs).reshape(B, T, H)
+    ex, rms = attn_excess_error(on, ref, out.dtype == torch.bfloat16)
+    say(f"   excess error / rms = {ex:.3e} (rms {rms:.3e})")
+    assert ex <= REL_TOL, ex
+    if ln is not None:
+        assert np.abs(ln - lref).max() <= 1e-4 * max(1.0, np.abs(lref).max())
+    return ex
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_sparse_attn_tiny_workload(out_dtype):
+    """All 1024 queries of the tiny causal workload with the oracle's own top-k."""
+    say("attn tiny_causal", out_dtype)
+    wl = synth.WORKLOADS["tiny_causal"]
+    kv = synth.latent_range(wl, 0, 0, wl.L, DEV)[None].contiguous()
+    gate = synth.latent_range(wl, 0, 0, wl.L, DEV, gate=True)[None].contiguous()
+    codes = torch.empty(1, wl.n_blocks, wl.d // 2, device=DEV, dtype=torch.uint8)
+    scales = torch.empty(1, wl.n_blocks, wl.d // 32, device=DEV, dtype=torch.uint8)
+    csa.compress_quantize(kv, gate, 0, wl.m, codes, scales)
+    win = synth.window_ring(wl, wl.L - 1, DEV)
+    q = synth.queries(wl, DEV)
+    qi, w = synth.indexer_queries(wl, DEV)
+    keys = synth.indexer_keys(wl, DEV)
+    qin, wn, kn = qi.cpu().numpy(), w.cpu().numpy(), keys.cpu().numpy()
+    idx = np.stack([O.index_topk(qin[0, t], wn[0, t], kn[0], wl.m, t, wl.k)[0]
+                    for t in range(wl.T)])[None]
+    idx_t = torch.from_numpy(idx).to(DEV).contiguous()
+    out = torch.empty(1, wl.T, wl.H, wl.d, device=DEV, dtype=out_dtype)
+    lse = torch.empty(1, wl.T, wl.H, device=DEV, dtype=torch.float32)
+    csa.sparse_attn(q, codes, scales, idx_t, win, wl.W, 0, 1.0, out, lse)
+    wd = dict(codes=codes, scales=scales, win=win, q=q)
+    _check_attn(wd, idx_t, 0, wl.W, out, lse)
+
+
+@pytest.mark.parametrize("d,H", [(512, 64), (128, 8), (256, 20)])
+def test_sparse_attn_decode(d, H):
+    say("attn decode", d, H)
+    B, L, m, k, W = 3, 4 * 1500, 4, 512, 128
+    wd = _attn_world(B, L, d, m, 128, seed=22, H=H, T=1)
+    g = gen(23, "idx")
+    nv = L // m
+    idx = torch.stack([torch.randperm(nv, generator=g, device=DEV)[:k] for _ in range(B)])
+    idx[:, 5] = -1
+    idx[1, 7:20] = -1
+    idx = idx.reshape(B, 1, k).to(torch.int32).contiguous()
+    for od in (torch.bfloat16, torch.float32):
+        out = torch.empty(B, 1, H, d, device=DEV, dtype=od)
+        lse = torch.empty(B, 1, H, device=DEV, dtype=torch.float32)
+        csa.sparse_attn(wd["q"], wd["codes"], wd["scales"], idx, wd["win"], W, L - 1, 1.0, out, lse)
+        _check_attn(wd, idx, L - 1, W, out, lse)
+
+
+def test_sparse_attn_prefill_block():
+    """64 consecutive queries, 512 entries each (one workgroup per query)."""
+    say("attn prefill block")
+    B, L, d, m, H, T, k, W = 1, 4096, 512, 4, 64, 64, 512, 128
+    wd = _attn_world(B, L, d, m, 2048, seed=24, H=H, T=T)
+    pos0 = L - T
+    g = gen(25, "idx")
+    idx = torch.stack([torch.randperm((pos0 + i + 1) // m, generator=g, device=DEV)[:k]
+                       for i in range(T)]).reshape(1, T, k).to(torch.int32).contiguous()
+    out = torch.empty(B, T, H, d, device=DEV, dtype=torch.bfloat16)
+    lse = torch.empty(B, T, H, device=DEV, dtype=torch.float32)
+    csa.sparse_attn(wd["q"], wd["codes"], wd["scales"], idx, wd["win"], W, pos0, 1.0, out, lse)
+    _check_attn(wd, idx, pos0, W, out, lse)
+
+
+def test_sparse_attn_edges():
+    say("attn edges")
+    B, L, d, m, H = 2, 512, 128, 4, 16
+    wd = _attn_world(B, L, d, m, 256, seed=26, H=H, T=1)
+    # only -1 slots: window alone; early position: window clipped at 0
+    idx = torch.full((B, 1, 40), -1, device=DEV, dtype=torch.int32)
+    out = torch.empty(B, 1, H, d, device=DEV, dtype=torch.float32)
+    csa.sparse_attn(wd["q"], wd["codes"], wd["scales"], idx, wd["win"], 128, L - 1, 1.0, out)
+    _check_attn(wd, idx, L - 1, 128, out, None)
+    wd2 = _attn_world(B, 20, d, m, 256, seed=27, H=H, T=1)
+    idx2 = torch.tensor([[[0, 3, -1, 4]]] * B, device=DEV, dtype=torch.int32)
+    csa.sparse_attn(wd2["q"], wd2["codes"], wd2["scales"], idx2, wd2["win"], 128, 19, 0.5, out)
+    _check_attn(wd2, idx2, 19, 128, out, None, scale=0.5)
+    # k = 0
+    idx0 = torch.empty(B, 1, 0, device=DEV, dtype=torch.int32)
+    csa.sparse_attn(wd["q"], wd["codes"], wd["scales"], idx0, wd["win"], 7, L - 1, 1.0, out)
+    _check_attn(wd, idx0, L - 1, 7, out, None)
+
+
+@pytest.mark.parametrize("T", [1, 20])
+def test_hca_dense(T):
+    say("hca dense", T)
+    B, L, d, m, H, W = 2, 128 * 300, 512, 128, 64, 128
+    wd = _attn_world(B, L, d, m, 256, seed=28, H=H, T=T)
+    pos0 = L - T
+    out = torch.empty(B, T, H, d, device=DEV, dtype=torch.bfloat16)
+    lse = torch.empty(B, T, H, device=DEV, dtype=torch.float32)
+    csa.hca_dense_attn(wd["q"], wd["codes"], wd["scales"], m, wd["win"], W, pos0, 1.0, out, lse)
+    _check_attn(wd, None, pos0, W, out, lse, dense_m=m)
+
+
+# ------------------------------------------------------------ properties ----
+
+def test_determinism_and_batch_invariance():
+    """A sequence's outputs are bit-identical across runs and whether it is
+    decoded alone or inside a larger batch."""
+    say("determinism / batch invariance")
+    B, L, d, m, H, k, W = 6, 4 * 3000, 512, 4, 64, 256, 128
+    wd = _attn_world(B, L, d, m, 128, seed=29, H=H, T=1)
+    g = gen(30, "bi")
+    qi = torch.randint(-8, 8, (B, 1, 8, 64), generator=g, device=DEV, dtype=torch.int8)
+    w = torch.randint(0, 4, (B, 1, 8), generator=g, device=DEV, dtype=torch.int8)
+    keys = torch.randint(-8, 8, (B, wd["cap"], 64), generator=g, device=DEV, dtype=torch.int8)
+
+    def run(sl):
+        oi = torch.empty(len(range(*sl.indices(B))), 1, k, device=DEV, dtype=torch.int32)
+        csa.index_topk(qi[sl].contiguous(), w[sl].contiguous(), keys[sl].contiguous(), m, L - 1,
+                       k, oi)
+        out = torch.empty(oi.shape[0], 1, H, d, device=DEV, dtype=torch.bfloat16)
+        csa.sparse_attn(wd["q"][sl].contiguous(), wd["codes"][sl].contiguous(),
+                        wd["scales"][sl].contiguous(), oi, wd["win"][sl].contiguous(), W, L - 1,
+                        1.0, out)
+        torch.cuda.synchronize()
+        return oi.cpu(), out.cpu()
+
+    i_all, o_all = run(slice(0, B))
+    i_again, o_again = run(slice(0, B))
+    assert torch.equal(i_all, i_again) and torch.equal(o_all.view(torch.int16), o_again.view(torch.int16))
+    for b in (0, 3, 5):
+        i1, o1 = run(slice(b, b + 1))
+        assert torch.equal(i1[0], i_all[b])
+        assert torch.equal(o1[0].view(torch.int16), o_all[b].view(torch.int16))
