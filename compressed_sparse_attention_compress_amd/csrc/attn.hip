@@ -9,22 +9,33 @@
 //
 // One workgroup = one query (all H <= 64 heads, 16 per wave) x one range of
 // slots; slots are the selected entries followed by the W window tokens, and
-// all of them share one softmax. Slots are processed 32 at a time: the
-// workgroup gathers the 32 rows, dequantises each value once into LDS in two
+// all of them share one softmax. Slots are processed 64 at a time: the
+// workgroup gathers the 64 rows, dequantises each value once into LDS in two
 // layouts (entry-major bf16 for q.k, channel-major fp16 for p.v), then every
-// wave runs S^T = K Q^T (16x16x32 bf16 MFMA, K = d) and O^T += V^T P^T
-// (16x16x32 fp16 MFMA, K = 32 slots) with an online softmax whose head index
-// is the lane's column in both products, so no register shuffles are needed
-// between them. Ranges of slots of one query can be split over workgroups
+// wave runs S^T = K Q^T (16x16x32 bf16 MFMA, K = d, four independent 16-slot
+// tiles) and O^T += V^T P^T (16x16x32 fp16 MFMA, two 32-slot k-steps) with an
+// online softmax whose head index is the lane's column in both products, so
+// no register shuffles are needed between them. O is rescaled only in passes
+// where some head's running maximum grew. Ranges of slots of one query can be
+// split over workgroups
 // (decode); their partial (o, max, sum) are merged in a fixed order.
 #include "csa_internal.h"
 
+#include <type_traits>
+
 namespace {
 
-constexpr int CH = 32;                     // slots per LDS chunk
-constexpr int VST = 36;                    // channel-major row stride (halfs)
-constexpr int SLOT_INVALID = -1;           // slot code: nothing there
-// slot code >= 0: compressed block id; <= -2: window ring row (-2 - row)
+constexpr int CH = 64;        // slots per staging pass (two 32-slot MFMA k-steps)
+constexpr int VST = CH + 8;   // channel-major row stride (halfs)
+constexpr int IDX_CAP = 1024; // entry block ids cached in LDS per refill
+constexpr float RESCALE_LOG2 = 0.f;  // rescale whenever a head's max grows (see below)
+
+// Raw bytes of the 4 slots of one staging task (16 channels each): an MXFP4
+// entry uses lo.x, lo.y (8 code bytes) and lo.z (its scale byte); a window
+// token uses lo and hi (16 bf16).
+struct RawSlots {
+  uint4 lo[4], hi[4];
+};
 
 template <int D, int NW, bool DENSE>
 __global__ __launch_bounds__(NW * 64) void k_attn(
@@ -32,14 +43,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
     const uint8_t* __restrict__ scales, int64_t blk_cap, const int32_t* __restrict__ idx, int k,
     int m, const uint16_t* __restrict__ win, int Wcap, int W, int T, int H, int64_t pos0,
     float scale_log2, int nsplit, int spl, void* __restrict__ out, int out_dtype,
-    float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    float* __restrict__ lse, _Float16* __restrict__ part_o, float2* __restrict__ part_ml) {
   constexpr int NT = NW * 64;
   constexpr int KST = D + 8;  // entry-major row stride (bf16)
   constexpr int KSTEPS = D / 32;
   constexpr int CT = D / 16;
+  constexpr int SG = CH / 4;                  // slot groups of 4 per pass
+  constexpr int TASKS = SG * (D / 16);
+  constexpr int TPT = (TASKS + NT - 1) / NT;  // staging tasks per thread
+  constexpr int ET = CH / 16;                 // 16-slot score tiles per pass
   __shared__ __attribute__((aligned(16))) __bf16 Ks[CH * KST];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[D * VST];
-  __shared__ int s_code[CH];
+  __shared__ int s_blk[IDX_CAP];
 
   const int split = blockIdx.x % nsplit;
   const int qi = blockIdx.x / nsplit;
@@ -71,55 +86,81 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
   for (int ct = 0; ct < CT; ++ct) O[ct] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int64_t c0 = s_begin; c0 < s_end; c0 += CH) {
-    if (threadIdx.x < CH) {
-      const int64_t slot = c0 + threadIdx.x;
-      int code = SLOT_INVALID;
-      if (slot < s_end) {
-        if (slot < nsel) {
-          const int64_t blk = DENSE ? slot : (int64_t)idx[(int64_t)qi * k + slot];
-          if (blk >= 0 && blk < blk_cap) code = (int)blk;
+  const uint8_t* cbase = codes + (int64_t)b * blk_cap * (D / 2);
+  const uint8_t* sbase = scales + (int64_t)b * blk_cap * (D / 32);
+  const uint16_t* wbase = win + (int64_t)b * Wcap * D;
+  const int32_t* ibase = DENSE ? nullptr : idx + (int64_t)qi * k;
+
+  // One homogeneous phase: entries (IS_WIN false) or window tokens, slots
+  // [p0, p1). Loads are unconditional (clamped rows), validity is applied to
+  // the logits; in the entry phase the next pass's raw bytes are fetched
+  // while the current pass is in the matrix cores.
+  auto phase = [&](auto is_win_tag, int64_t p0, int64_t p1) {
+    constexpr bool IS_WIN = decltype(is_win_tag)::value;
+    if (p0 >= p1) return;
+    int64_t tab0 = p0;  // first slot whose block id sits in s_blk[0]
+    auto refill = [&](int64_t from) {
+      __syncthreads();
+      tab0 = from;
+      for (int i = threadIdx.x; i < IDX_CAP; i += NT) {
+        const int64_t sl = from + i;
+        int blk = -1;
+        if (sl < p1) {
+          const int64_t v = DENSE ? sl : (int64_t)ibase[sl];
+          blk = (v >= 0 && v < blk_cap) ? (int)v : -1;
+        }
+        s_blk[i] = blk;
+      }
+      __syncthreads();
+    };
+    if (!IS_WIN) refill(p0);
+    // task -> (slot group sg, 16-channel segment cs), sg fastest across lanes
+    // so that the channel-major writes of a wave spread over all LDS banks
+    auto load_task = [&](RawSlots& r, int task, int64_t c0) {
+      const int sg = (task < TASKS ? task : 0) % SG;
+      const int cs = (task < TASKS ? task : 0) / SG;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t sl = c0 + 4 * sg + u;
+        if (IS_WIN) {
+          int64_t p = t - W + 1 + (sl - nsel);
+          p = p < 0 ? 0 : p;
+          const uint16_t* src = wbase + (p % Wcap) * D + cs * 16;
+          r.lo[u] = *reinterpret_cast<const uint4*>(src);
+          r.hi[u] = *reinterpret_cast<const uint4*>(src + 8);
         } else {
-          const int64_t p = t - W + 1 + (slot - nsel);
-          if (p >= 0) code = -2 - (int)(p % Wcap);
+          int blk = (sl < p1 && sl - tab0 < IDX_CAP) ? s_blk[sl - tab0] : -1;
+          blk = blk < 0 ? 0 : blk;
+          const uint2 cw =
+              *reinterpret_cast<const uint2*>(cbase + (int64_t)blk * (D / 2) + cs * 8);
+          r.lo[u].x = cw.x;
+          r.lo[u].y = cw.y;
+          r.lo[u].z = sbase[(int64_t)blk * (D / 32) + cs / 2];
         }
       }
-      s_code[threadIdx.x] = code;
-    }
-    __syncthreads();
-
-    // gather + dequantise: task = (group of 4 slots, 16-channel segment)
-    for (int task = threadIdx.x; task < 8 * (D / 16); task += NT) {
-      const int sg = task / (D / 16);
-      const int cs = task - sg * (D / 16);
+    };
+    auto convert_task = [&](const RawSlots& r, int task) {
+      const int sg = task % SG;
+      const int cs = task / SG;
       v8h vh[4][2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int slot = 4 * sg + u;
-        const int code = s_code[slot];
         v8bf k0, k1;
-        if (code >= 0) {
-          const int64_t row = (int64_t)b * blk_cap + code;
-          const uint2 cw = *reinterpret_cast<const uint2*>(codes + row * (D / 2) + cs * 8);
-          const float sc = e8m0_to_f32(scales[row * (D / 32) + cs / 2]);
-          k0 = fp4x8_to_bf16(cw.x, sc);
-          k1 = fp4x8_to_bf16(cw.y, sc);
-          vh[u][0] = fp4x8_to_f16(cw.x, sc);
-          vh[u][1] = fp4x8_to_f16(cw.y, sc);
-        } else if (code <= -2) {
-          const uint16_t* src = win + ((int64_t)b * Wcap + (-2 - code)) * D + cs * 16;
-          k0 = *reinterpret_cast<const v8bf*>(src);
-          k1 = *reinterpret_cast<const v8bf*>(src + 8);
+        if (IS_WIN) {
+          k0 = __builtin_bit_cast(v8bf, r.lo[u]);
+          k1 = __builtin_bit_cast(v8bf, r.hi[u]);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             vh[u][0][i] = (_Float16)(float)k0[i];
             vh[u][1][i] = (_Float16)(float)k1[i];
           }
         } else {
-          k0 = v8bf{};
-          k1 = v8bf{};
-          vh[u][0] = v8h{};
-          vh[u][1] = v8h{};
+          const float sc = e8m0_to_f32(r.lo[u].z & 0xffu);
+          k0 = fp4x8_to_bf16(r.lo[u].x, sc);
+          k1 = fp4x8_to_bf16(r.lo[u].y, sc);
+          vh[u][0] = fp4x8_to_f16(r.lo[u].x, sc);
+          vh[u][1] = fp4x8_to_f16(r.lo[u].y, sc);
         }
         *reinterpret_cast<v8bf*>(&Ks[slot * KST + cs * 16]) = k0;
         *reinterpret_cast<v8bf*>(&Ks[slot * KST + cs * 16 + 8]) = k1;
@@ -133,61 +174,123 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
         col[3] = vh[3][c >> 3][c & 7];
         *reinterpret_cast<v4h*>(&Vs[(cs * 16 + c) * VST + 4 * sg]) = col;
       }
-    }
-    __syncthreads();
+    };
+    // prefetch (whole pass ahead) only where the raw bytes are small
+    // (entries) and a thread owns at most two tasks; otherwise each task is
+    // loaded right before it is converted
+    constexpr bool PREFETCH = !IS_WIN && TPT <= 2;
+    constexpr int NRAW = PREFETCH ? TPT : 1;
+    RawSlots raw[NRAW];
+    auto load_all = [&](int64_t c0) {
+#pragma unroll
+      for (int tt = 0; tt < NRAW; ++tt) load_task(raw[tt], threadIdx.x + tt * NT, c0);
+    };
+    if (PREFETCH) load_all(p0);
+    for (int64_t c0 = p0; c0 < p1; c0 += CH) {
+      if (!IS_WIN && c0 + CH > tab0 + IDX_CAP) {
+        refill(c0);
+        if (PREFETCH) load_all(c0);
+      }
+      // convert the raw bytes into LDS: entry-major bf16 and channel-major fp16
+#pragma unroll
+      for (int tt = 0; tt < TPT; ++tt) {
+        const int task = threadIdx.x + tt * NT;
+        if (task < TASKS) {
+          if (PREFETCH) {
+            convert_task(raw[tt < NRAW ? tt : 0], task);
+          } else {
+            load_task(raw[0], task, c0);
+            convert_task(raw[0], task);
+          }
+        }
+      }
+      // validity of this lane's logit slots: tile et, row 4g + r
+      bool ok[ET][4];
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t sl = c0 + 16 * et + 4 * g + r;
+          if (IS_WIN)
+            ok[et][r] = sl < p1 && t - W + 1 + (sl - nsel) >= 0;
+          else
+            ok[et][r] = sl < p1 && s_blk[sl - tab0] >= 0;
+        }
+      if (PREFETCH && c0 + CH < p1 && c0 + 2 * CH <= tab0 + IDX_CAP) load_all(c0 + CH);
+      __syncthreads();
 
-    // S^T[entry][head] for two 16-entry tiles
-    v4f S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+      // S^T[slot][head] for the pass's 16-slot tiles (independent chains)
+      v4f S[ET];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const v8bf a0 = *reinterpret_cast<const v8bf*>(&Ks[i16 * KST + 32 * kk + 8 * g]);
-      const v8bf a1 = *reinterpret_cast<const v8bf*>(&Ks[(16 + i16) * KST + 32 * kk + 8 * g]);
-      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, Qop[kk], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, Qop[kk], S1, 0, 0, 0);
+      for (int et = 0; et < ET; ++et) S[et] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          const v8bf a = *reinterpret_cast<const v8bf*>(&Ks[(16 * et + i16) * KST + 32 * kk + 8 * g]);
+          S[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qop[kk], S[et], 0, 0, 0);
+        }
+      float x[ET][4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[et][r] = ok[et][r] ? S[et][r] * scale_log2 : -INFINITY;
+          cmax = fmaxf(cmax, x[et][r]);
+        }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      // online-softmax rescale, skipped when no head of the wave saw its max
+      // grow (the branch is wave-uniform; heads whose max did not grow get
+      // alpha = 1). Letting the reference max lag (p up to 2^k in fp16) was
+      // measured to raise the p.v error steadily with k, so it never lags.
+      if (__ballot(cmax > m_run + RESCALE_LOG2)) {
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) O[ct] *= alpha;
+        m_run = m_new;
+      }
+      const bool none = m_run == -INFINITY;
+      // P^T slot order for the two 32-slot k-steps: slot e(g, s) =
+      // 32*kh + (s < 4 ? 4g + s : 16 + 4g + s - 4)
+      v8h P[ET / 2];
+      float psum = 0.f;
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = none ? 0.f : exp2f(x[et][r] - m_run);
+          psum += pv;
+          P[et >> 1][(et & 1) * 4 + r] = (_Float16)pv;
+        }
+      l_run += psum;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const _Float16* vrow = &Vs[(ct * 16 + i16) * VST];
+#pragma unroll
+        for (int kh = 0; kh < ET / 2; ++kh) {
+          const v4h lo = *reinterpret_cast<const v4h*>(vrow + 32 * kh + 4 * g);
+          const v4h hi = *reinterpret_cast<const v4h*>(vrow + 32 * kh + 16 + 4 * g);
+          v8h A;
+          A[0] = lo[0]; A[1] = lo[1]; A[2] = lo[2]; A[3] = lo[3];
+          A[4] = hi[0]; A[5] = hi[1]; A[6] = hi[2]; A[7] = hi[3];
+          O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, P[kh], O[ct], 0, 0, 0);
+        }
+      }
+      __syncthreads();
     }
-    float x[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = s_code[4 * g + r] != SLOT_INVALID ? S0[r] * scale_log2 : -INFINITY;
-      x[4 + r] = s_code[16 + 4 * g + r] != SLOT_INVALID ? S1[r] * scale_log2 : -INFINITY;
-    }
-    float cmax = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, x[i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const bool none = m_new == -INFINITY;
-    const float alpha = none ? 1.f : exp2f(m_run - m_new);
-    v8h P;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = none ? 0.f : exp2f(x[i] - m_new);
-      psum += p;
-      P[i] = (_Float16)p;
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      O[ct] *= alpha;
-      const _Float16* vrow = &Vs[(ct * 16 + i16) * VST];
-      const v4h lo = *reinterpret_cast<const v4h*>(vrow + 4 * g);
-      const v4h hi = *reinterpret_cast<const v4h*>(vrow + 16 + 4 * g);
-      v8h A;
-      A[0] = lo[0]; A[1] = lo[1]; A[2] = lo[2]; A[3] = lo[3];
-      A[4] = hi[0]; A[5] = hi[1]; A[6] = hi[2]; A[7] = hi[3];
-      O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, P, O[ct], 0, 0, 0);
-    }
-    __syncthreads();
-  }
+  };
+  phase(std::false_type{}, s_begin, s_end < nsel ? s_end : nsel);
+  phase(std::true_type{}, s_begin > nsel ? s_begin : nsel, s_end);
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (head >= H) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (nsplit == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t base = ((int64_t)qi * H + head) * D;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -206,39 +309,62 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
     }
     if (lse && g == 0) lse[(int64_t)qi * H + head] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
   } else {
+    // normalised partial output in float16 (|o| <= max |row|), m and l in float32
     const int64_t pbase = (((int64_t)qi * nsplit + split) * H + head);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int c = ct * 16 + 4 * g;
-      float4 v;
-      v.x = O[ct][0]; v.y = O[ct][1]; v.z = O[ct][2]; v.w = O[ct][3];
-      *reinterpret_cast<float4*>(part_o + pbase * D + c) = v;
+      v4h v;
+      v[0] = (_Float16)(O[ct][0] * inv); v[1] = (_Float16)(O[ct][1] * inv);
+      v[2] = (_Float16)(O[ct][2] * inv); v[3] = (_Float16)(O[ct][3] * inv);
+      *reinterpret_cast<v4h*>(part_o + pbase * D + c) = v;
     }
     if (g == 0) part_ml[pbase] = float2{m_run, l_tot};
   }
 }
 
-// Merge of the split partials of one (query, head), splits in index order.
+// Merge of the split partials of one (query, head), splits in index order:
+// weights l_s * 2^(m_s - M) / L on the normalised partial outputs. The split
+// maxima and sums are staged in LDS first so the partial loads are independent.
+constexpr int MERGE_MAX = 256;  // splits per query handled by the merge
 template <int D>
-__global__ __launch_bounds__(D / 4) void k_attn_merge(const float* __restrict__ part_o,
+__global__ __launch_bounds__(D / 4) void k_attn_merge(const _Float16* __restrict__ part_o,
                                                       const float2* __restrict__ part_ml,
                                                       int nsplit, int H, void* __restrict__ out,
                                                       int out_dtype, float* __restrict__ lse) {
+  __shared__ float s_m[MERGE_MAX], s_f[MERGE_MAX];
+  __shared__ float s_M, s_L;
   const int64_t qh = blockIdx.x;
   const int64_t qi = qh / H;
   const int h = (int)(qh - qi * H);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(qi * nsplit + s) * H + h].x);
-  float L = 0.f;
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
+  for (int s = threadIdx.x; s < nsplit; s += D / 4) {
     const float2 ml = part_ml[(qi * nsplit + s) * H + h];
-    if (ml.x == -INFINITY) continue;
-    const float f = exp2f(ml.x - M);
-    L += ml.y * f;
-    const float4 o =
-        *reinterpret_cast<const float4*>(part_o + ((qi * nsplit + s) * H + h) * D + 4 * threadIdx.x);
-    acc.x += o.x * f; acc.y += o.y * f; acc.z += o.z * f; acc.w += o.w * f;
+    s_m[s] = ml.x;
+    s_f[s] = ml.y;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, s_m[s]);
+    float L = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float f = s_m[s] == -INFINITY ? 0.f : s_f[s] * exp2f(s_m[s] - M);
+      s_f[s] = f;
+      L += f;
+    }
+    s_M = M;
+    s_L = L;
+  }
+  __syncthreads();
+  const float L = s_L;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  const _Float16* src = part_o + (qi * nsplit * H + h) * D + 4 * threadIdx.x;
+#pragma unroll 4
+  for (int s = 0; s < nsplit; ++s) {
+    const float f = s_f[s];
+    const v4h o = *reinterpret_cast<const v4h*>(src + (int64_t)s * H * D);
+    acc.x += (float)o[0] * f; acc.y += (float)o[1] * f;
+    acc.z += (float)o[2] * f; acc.w += (float)o[3] * f;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const int64_t base = qh * D + 4 * threadIdx.x;
@@ -253,7 +379,7 @@ __global__ __launch_bounds__(D / 4) void k_attn_merge(const float* __restrict__ 
     v[2] = (__bf16)(acc.z * inv); v[3] = (__bf16)(acc.w * inv);
     *reinterpret_cast<v4bf*>(reinterpret_cast<__bf16*>(out) + base) = v;
   }
-  if (lse && threadIdx.x == 0) lse[qh] = (M + log2f(L)) * 0.69314718055994531f;
+  if (lse && threadIdx.x == 0) lse[qh] = (s_M + log2f(L)) * 0.69314718055994531f;
 }
 
 struct AttnPlan {
@@ -261,23 +387,27 @@ struct AttnPlan {
   int64_t ws_bytes;
 };
 
+// Decode (T < 16): slots are split over workgroups so that a query keeps
+// ~32 workgroups busy (whole 64-slot passes; >= n/16 slots for very long
+// dense ranges, where the partials would otherwise dominate). The split depends only
+// on per-sequence sizes, never on B, so a sequence's output is the same in
+// any batch. Longer query runs take one workgroup per query.
 static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots) {
   AttnPlan p;
-  if (T >= 16 || n_slots <= 128) {
+  if (T >= 16 || n_slots <= CH) {
     p.nsplit = 1;
     p.spl = (int)(((n_slots + CH - 1) / CH) * CH);
     if (p.spl < CH) p.spl = CH;
   } else {
-    int64_t spl = (n_slots + 15) / 16;
+    int64_t spl = (n_slots + (n_slots > 4096 ? 15 : 31)) / (n_slots > 4096 ? 16 : 32);
     spl = ((spl + CH - 1) / CH) * CH;
-    if (spl < 128) spl = 128;
     p.spl = (int)spl;
     p.nsplit = (int)((n_slots + spl - 1) / spl);
   }
   p.ws_bytes = 0;
   if (p.nsplit > 1) {
     const int64_t units = (int64_t)B * T * p.nsplit * H;
-    p.ws_bytes = units * d * 4 + 256 + units * 8;
+    p.ws_bytes = ((units * d * 2 + 255) / 256) * 256 + units * 8;
   }
   return p;
 }
@@ -290,7 +420,7 @@ struct AttnArgs {
 };
 
 template <int D, bool DENSE>
-static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, float2* part_ml) {
+static void launch_attn(const AttnArgs& a, const AttnPlan& p, _Float16* part_o, float2* part_ml) {
   const int nw = (a.H + 15) / 16;
   const dim3 grid((unsigned)((int64_t)a.B * a.T * p.nsplit));
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
@@ -333,15 +463,15 @@ static int attn_run(const AttnArgs& a, bool dense) {
   if (nsel > 0 && !csa_aligned(a.codes, 8)) return CSA_ERR_ALIGN;
   const AttnPlan p = attn_plan(a.B, a.T, a.H, a.d, nsel + a.W);
   if ((int64_t)a.B * a.T * p.nsplit > 0x7fffffffLL) return CSA_ERR_SHAPE;
-  float* part_o = nullptr;
+  _Float16* part_o = nullptr;
   float2* part_ml = nullptr;
   if (p.nsplit > 1) {
     if (!a.ws || a.ws_bytes < p.ws_bytes) return CSA_ERR_WORKSPACE;
     if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
     const int64_t units = (int64_t)a.B * a.T * p.nsplit * a.H;
-    part_o = reinterpret_cast<float*>(a.ws);
+    part_o = reinterpret_cast<_Float16*>(a.ws);
     part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a.ws) +
-                                        ((units * a.d * 4 + 255) / 256) * 256);
+                                        ((units * a.d * 2 + 255) / 256) * 256);
   }
   if (dense) {
     if (a.d == 128) launch_attn<128, true>(a, p, part_o, part_ml);

@@ -13,14 +13,16 @@
 // Two execution plans, both exact (hence bit-identical results):
 //  * split scan (few queries per sequence, or a candidate pool): the entry
 //    range of every query is cut into 2048-entry tiles, one workgroup each.
-//    k_idx_scan streams the int8 keys once (HBM-bound), writes every score to
-//    a slab and adds a 512-bin monotone histogram of its scores into a
-//    per-query global histogram; the last tile to finish derives the
-//    threshold bin. k_idx_select re-reads each tile's slab (same grid, so the
-//    same XCD and its L2), keeps the entries at or above the threshold bin in
-//    index order, and the last tile of each query resolves the exact k-th
-//    score among those few candidates by radix refinement and writes the
-//    ascending index list.
+//    k_idx_scan streams the int8 keys once (HBM-bound: every load is issued
+//    unconditionally so a wave keeps 8 KB in flight), writes each score to a
+//    slab and adds a 512-bin monotone histogram of the scores into a
+//    per-query global histogram. k_idx_select (same grid) reads the finished
+//    histogram, derives the threshold bin and keeps the tile's entries at or
+//    above it, in index order. k_idx_final (one workgroup per query) gathers
+//    those few thousand candidates into LDS, narrows the threshold to the
+//    exact k-th score by radix refinement and writes the ascending list.
+//    Kernel boundaries, not fences, order the hand-offs: an agent-scope fence
+//    inside a workgroup writes back and invalidates the XCD's whole L2.
 //  * multi-pass (long query runs sharing a sequence's keys, i.e. prefill
 //    chunks): one workgroup per group of consecutive queries streams the
 //    L2-resident keys once per pass, recomputing the scores on the matrix
@@ -52,30 +54,6 @@ __device__ inline int score_tile(const v4i (&A)[KS], const v4i (&Bk)[KS], const 
   p += __shfl_xor(p, 32, 64);
   return p;
 }
-
-// Coherent (agent-scope) stores/loads for data handed between workgroups of
-// one kernel; together with wait_vmem() before the hand-off counter they need
-// no L2 write-back or invalidate.
-__device__ inline uint64_t pack_cand(int score, int entry) {
-  return (uint64_t)(uint32_t)score | ((uint64_t)(uint32_t)entry << 32);
-}
-__device__ inline void st_coherent(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_coherent32(int32_t* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline int ld_coherent32(const int32_t* p) {
-  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline int2 ld_cand(const int2* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<int2*>(p)),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return int2{(int)(uint32_t)v, (int)(uint32_t)(v >> 32)};
-}
-// s_waitcnt vmcnt(0): every vector memory access of this wave has completed
-// (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15).
-__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Exclusive prefix sum, in place, of an LDS array of n <= 2048 ints, by a
 // 256-thread workgroup. Ends with a barrier.
@@ -204,48 +182,20 @@ __global__ __launch_bounds__(256) void k_idx_scan(
 }
 
 // ------------------------------------------------------------------------
-// split scan, phase 2: candidates at or above the threshold bin, then the
-// exact resolution by the last tile of each query
+// split scan, phase 2a: per tile, the entries at or above the threshold bin
 // ------------------------------------------------------------------------
-// Dynamic LDS: t_off[MAX_TILES] ints, then a candidate area of cap_lds
-// (score, entry) pairs. The last tile of a query copies the candidates of all
-// tiles into that area in one parallel pass (index order kept) and resolves
-// everything there; a query with more candidates than cap_lds (massive ties)
-// takes the slower path that walks the per-tile lists in global memory.
-__global__ __launch_bounds__(256) void k_idx_select(
-    int T, int m, int64_t pos0, int64_t blk_cap, const int32_t* __restrict__ cand, int C, int k,
-    int n_tiles, int64_t npad, const int32_t* __restrict__ slab, int2* __restrict__ cbuf,
-    int32_t* __restrict__ cnt, uint32_t* __restrict__ hist, uint32_t* __restrict__ done2,
-    int32_t* __restrict__ out_idx, int32_t* __restrict__ out_score, int cap_lds) {
-  extern __shared__ __attribute__((aligned(16))) int smem[];
-  __shared__ int tmp[4];
-  __shared__ int s_last;
-  __shared__ uint32_t bh[256];
-  __shared__ int s_red[8];
-  int* t_off = smem;                    // [MAX_TILES]
-  int* area = smem + MAX_TILES;         // [2 * cap_lds]
-  const int tile = blockIdx.x;
-  const int qi = blockIdx.y;
-  const int b = qi / T;
-  const int64_t t = pos0 + (qi - b * T);
-  int64_t nv = (t + 1) / m;
-  nv = nv < blk_cap ? nv : blk_cap;
-  const int64_t N = cand ? (int64_t)C : nv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int2* cq = cbuf + (int64_t)qi * npad;
-
-  // Threshold bin T1 from the finished histogram (same result in every
-  // workgroup of the query): the bin where the count from the top first
-  // reaches k_eff; A1 = entries in higher bins. Thread j owns bins 511-2j and
-  // 510-2j, so the prefix runs from the top bin down.
-  uint32_t* hq = hist + (int64_t)qi * NB1;
+// Threshold bin T1 of a query from its finished histogram: the bin where the
+// count from the top first reaches k_eff; A1 = entries in higher bins. Thread
+// j owns bins 511-2j and 510-2j, so the prefix runs from the top bin down.
+// Returns k_eff; T1 and A1 come back through s_red[0..1] (valid if k_eff > 0).
+__device__ inline int threshold_bin(const uint32_t* hq, int k, int* tmp, int* s_red) {
   const int hb = NB1 - 1 - 2 * (int)threadIdx.x;
   const int c_hi = (int)hq[hb];
   const int c_lo = (int)hq[hb - 1];
-  int total_valid;
-  const int incl = wg_scan_incl<256>(c_hi + c_lo, tmp, &total_valid);
+  int total;
+  const int incl = wg_scan_incl<256>(c_hi + c_lo, tmp, &total);
   const int excl = incl - c_hi - c_lo;
-  const int keff = k < total_valid ? k : total_valid;
+  const int keff = k < total ? k : total;
   if (keff > 0) {
     if (excl + c_hi >= keff && excl < keff) {
       s_red[0] = hb;
@@ -257,48 +207,79 @@ __global__ __launch_bounds__(256) void k_idx_select(
     }
   }
   __syncthreads();
-  const int T1 = s_red[0], A1 = s_red[1];
-  __syncthreads();
+  return keff;
+}
 
-  if (keff > 0) {
-    const int64_t e0 = (int64_t)tile * TILE + threadIdx.x * 8;
-    const int32_t* sq = slab + (int64_t)qi * npad;
-    int s[8];
-    if (e0 + 8 <= N) {
-      const int4 a = *reinterpret_cast<const int4*>(sq + e0);
-      const int4 c = *reinterpret_cast<const int4*>(sq + e0 + 4);
-      s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
-      s[4] = c.x; s[5] = c.y; s[6] = c.z; s[7] = c.w;
-    } else {
+__global__ __launch_bounds__(256) void k_idx_select(
+    int T, int m, int64_t pos0, int64_t blk_cap, int C, int k, int n_tiles, int64_t npad,
+    const int32_t* __restrict__ slab, int2* __restrict__ cbuf, int32_t* __restrict__ cnt,
+    const uint32_t* __restrict__ hist, bool cand_mode) {
+  __shared__ int tmp[4];
+  __shared__ int s_red[2];
+  const int tile = blockIdx.x;
+  const int qi = blockIdx.y;
+  const int b = qi / T;
+  const int64_t t = pos0 + (qi - b * T);
+  int64_t nv = (t + 1) / m;
+  nv = nv < blk_cap ? nv : blk_cap;
+  const int64_t N = cand_mode ? (int64_t)C : nv;
+  const int64_t e0 = (int64_t)tile * TILE + threadIdx.x * 8;
+  const int32_t* sq = slab + (int64_t)qi * npad;
+  int s[8];  // issued before the histogram scan so both loads overlap
+  if (e0 + 8 <= N) {
+    const int4 a = *reinterpret_cast<const int4*>(sq + e0);
+    const int4 c = *reinterpret_cast<const int4*>(sq + e0 + 4);
+    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
+    s[4] = c.x; s[5] = c.y; s[6] = c.z; s[7] = c.w;
+  } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s[j] = (e0 + j < N) ? sq[e0 + j] : -1;
-    }
-    int f = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f += (s[j] >= 0 && score_bin512(s[j]) >= T1);
-    int total;
-    int pos = wg_scan_incl<256>(f, tmp, &total) - f;
-    // candidates and counts are read by another workgroup of this kernel:
-    // agent-scope atomic stores keep them coherent across XCDs without
-    // writing back or invalidating any L2
-    uint64_t* dst = reinterpret_cast<uint64_t*>(cq + (int64_t)tile * TILE);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (s[j] >= 0 && score_bin512(s[j]) >= T1)
-        st_coherent(dst + pos++, pack_cand(s[j], (int)(e0 + j)));
-    if (threadIdx.x == 0) st_coherent32(cnt + (int64_t)qi * n_tiles + tile, total);
+    for (int j = 0; j < 8; ++j) s[j] = (e0 + j < N) ? sq[e0 + j] : -1;
   }
-  wait_vmem();  // this thread's stores are complete
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&done2[qi], 1u) == (uint32_t)(n_tiles - 1));
-  __syncthreads();
-  if (!s_last) return;
-  // every workgroup of this query has read the histogram: clear it (and the
-  // counter) for the next call
-  __hip_atomic_store(&hq[hb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&hq[hb - 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&done2[qi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int keff = threshold_bin(hist + (int64_t)qi * NB1, k, tmp, s_red);
+  if (keff == 0) return;
+  const int T1 = s_red[0];
+  int f = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f += (s[j] >= 0 && score_bin512(s[j]) >= T1);
+  int total;
+  int pos = wg_scan_incl<256>(f, tmp, &total) - f;
+  int2* dst = cbuf + (int64_t)qi * npad + (int64_t)tile * TILE;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (s[j] >= 0 && score_bin512(s[j]) >= T1) dst[pos++] = int2{s[j], (int)(e0 + j)};
+  if (threadIdx.x == 0) cnt[(int64_t)qi * n_tiles + tile] = total;
+}
+
+// ------------------------------------------------------------------------
+// split scan, phase 2b: one workgroup per query resolves the exact k-th score
+// among the candidates and writes the ascending index list
+// ------------------------------------------------------------------------
+// Dynamic LDS: t_off[MAX_TILES] ints, then cap_lds (score, entry) pairs. The
+// candidates of all tiles are copied there in one parallel pass (index order
+// kept); a query with more candidates than cap_lds (massive ties) walks the
+// per-tile lists in global memory instead. The histogram of the query is
+// cleared for the next call.
+__global__ __launch_bounds__(256) void k_idx_final(
+    int T, int m, int64_t pos0, int64_t blk_cap, const int32_t* __restrict__ cand, int C, int k,
+    int n_tiles, int64_t npad, const int2* __restrict__ cbuf, const int32_t* __restrict__ cnt,
+    uint32_t* __restrict__ hist, int32_t* __restrict__ out_idx, int32_t* __restrict__ out_score,
+    int cap_lds) {
+  extern __shared__ __attribute__((aligned(16))) int smem[];
+  __shared__ int tmp[4];
+  __shared__ uint32_t bh[256];
+  __shared__ int s_red[8];
+  __shared__ int w_gt[4], w_eq[4];
+  int* t_off = smem;             // [MAX_TILES]
+  int* area = smem + MAX_TILES;  // [2 * cap_lds]
+  const int qi = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int2* cq = cbuf + (int64_t)qi * npad;
+  uint32_t* hq = hist + (int64_t)qi * NB1;
+  const int keff = threshold_bin(hq, k, tmp, s_red);
+  const int T1 = s_red[0], A1 = s_red[1];
+  // histogram consumed: clear it for the next call
+  hq[NB1 - 1 - 2 * threadIdx.x] = 0u;
+  hq[NB1 - 2 - 2 * threadIdx.x] = 0u;
 
   int32_t* oi = out_idx + (int64_t)qi * k;
   int32_t* os = out_score ? out_score + (int64_t)qi * k : nullptr;
@@ -310,7 +291,7 @@ __global__ __launch_bounds__(256) void k_idx_select(
   if (keff == 0) return;
 
   const int32_t* cntq = cnt + (int64_t)qi * n_tiles;
-  for (int i = threadIdx.x; i < n_tiles; i += 256) t_off[i] = ld_coherent32(cntq + i);
+  for (int i = threadIdx.x; i < n_tiles; i += 256) t_off[i] = cntq[i];
   __syncthreads();
   const int last_cnt = t_off[n_tiles - 1];
   __syncthreads();
@@ -319,7 +300,7 @@ __global__ __launch_bounds__(256) void k_idx_select(
 
   int need = keff - A1;  // threshold-bin candidates still to take
   if (M <= cap_lds) {
-    // ---- fast path: all candidates in LDS, index order kept
+    // ---- fast path: every candidate in LDS, index order kept
     int* cs = area;
     int* ce = area + cap_lds;
     for (int i = threadIdx.x; i < M; i += 256) {
@@ -328,7 +309,7 @@ __global__ __launch_bounds__(256) void k_idx_select(
         const int mid = (lo + hi + 1) >> 1;
         if (t_off[mid] <= i) lo = mid; else hi = mid - 1;
       }
-      const int2 v = ld_cand(cq + (int64_t)lo * TILE + (i - t_off[lo]));
+      const int2 v = cq[(int64_t)lo * TILE + (i - t_off[lo])];
       cs[i] = v.x;
       ce[i] = v.y;
     }
@@ -382,24 +363,52 @@ __global__ __launch_bounds__(256) void k_idx_select(
     }
     const int tau = lo;
     const int take_eq = need;
+    // ordered emission: wave w owns the contiguous range [w*Q, (w+1)*Q)
+    const int Q = (M + 3) / 4;
+    const int r0 = wave * Q, r1 = min(M, r0 + Q);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int gt = 0, eq = 0;
+    for (int i = r0 + lane; i < r1; i += 64) {
+      const int sv = cs[i];
+      gt += sv > tau;
+      eq += sv == tau;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      gt += __shfl_xor(gt, off, 64);
+      eq += __shfl_xor(eq, off, 64);
+    }
+    if (lane == 0) {
+      w_gt[wave] = gt;
+      w_eq[wave] = eq;
+    }
+    __syncthreads();
     int eq_run = 0, out_run = 0;
-    for (int base = 0; base < M; base += 256) {
-      const int i = base + threadIdx.x;
-      const bool in = i < M;
+    for (int w2 = 0; w2 < wave; ++w2) {
+      int take = take_eq - eq_run;
+      take = take < 0 ? 0 : (take > w_eq[w2] ? w_eq[w2] : take);
+      out_run += w_gt[w2] + take;
+      eq_run += w_eq[w2];
+    }
+    for (int i0 = r0; i0 < r1; i0 += 64) {
+      const int i = i0 + lane;
+      const bool in = i < r1;
       const int sv = in ? cs[i] : -1;
-      const int is_eq = (in && sv == tau) ? 1 : 0;
-      int eq_tot;
-      const int eq_rank = eq_run + wg_scan_incl<256>(is_eq, tmp, &eq_tot) - is_eq;
-      const int take = (in && (sv > tau || (is_eq && eq_rank < take_eq))) ? 1 : 0;
-      int tk_tot;
-      const int pos = out_run + wg_scan_incl<256>(take, tmp, &tk_tot) - take;
-      if (take && pos < keff) {
-        const int e = ce[i];
-        oi[pos] = cqq ? cqq[e] : e;
-        if (os) os[pos] = sv;
+      const bool is_eq = in && sv == tau;
+      const uint64_t meq = __ballot(is_eq);
+      const int eq_rank = eq_run + __popcll(meq & below);
+      const bool take = in && (sv > tau || (is_eq && eq_rank < take_eq));
+      const uint64_t mt = __ballot(take);
+      if (take) {
+        const int pos = out_run + __popcll(mt & below);
+        if (pos < keff) {
+          const int e = ce[i];
+          oi[pos] = cqq ? cqq[e] : e;
+          if (os) os[pos] = sv;
+        }
       }
-      eq_run += eq_tot;
-      out_run += tk_tot;
+      eq_run += __popcll(meq);
+      out_run += __popcll(mt);
     }
     return;
   }
@@ -409,13 +418,13 @@ __global__ __launch_bounds__(256) void k_idx_select(
   int* t_gt = area + MAX_TILES;
   int* t_eq = area + 2 * MAX_TILES;
   int* t_eqb = area + 3 * MAX_TILES;
-  for (int i = threadIdx.x; i < n_tiles; i += 256) t_cnt[i] = ld_coherent32(cntq + i);
+  for (int i = threadIdx.x; i < n_tiles; i += 256) t_cnt[i] = cntq[i];
   __syncthreads();
   int vmin = 0x7fffffff, vmax = -1;
   for (int tl = wave; tl < n_tiles; tl += 4) {
     const int c = t_cnt[tl];
     for (int j = lane; j < c; j += 64) {
-      const int sv = ld_cand(cq + (int64_t)tl * TILE + j).x;
+      const int sv = cq[(int64_t)tl * TILE + j].x;
       if (score_bin512(sv) == T1) {
         vmin = min(vmin, sv);
         vmax = max(vmax, sv);
@@ -444,7 +453,7 @@ __global__ __launch_bounds__(256) void k_idx_select(
     for (int tl = wave; tl < n_tiles; tl += 4) {
       const int c = t_cnt[tl];
       for (int j = lane; j < c; j += 64) {
-        const int sv = ld_cand(cq + (int64_t)tl * TILE + j).x;
+        const int sv = cq[(int64_t)tl * TILE + j].x;
         if (score_bin512(sv) == T1 && sv >= lo && sv - lo <= R)
           atomicAdd(&bh[(sv - lo) >> shift], 1u);
       }
@@ -470,7 +479,7 @@ __global__ __launch_bounds__(256) void k_idx_select(
     const int c = t_cnt[tl];
     int gt = 0, eq = 0;
     for (int j = lane; j < c; j += 64) {
-      const int sv = ld_cand(cq + (int64_t)tl * TILE + j).x;
+      const int sv = cq[(int64_t)tl * TILE + j].x;
       gt += sv > tau;
       eq += sv == tau;
     }
@@ -501,7 +510,7 @@ __global__ __launch_bounds__(256) void k_idx_select(
     for (int j0 = 0; j0 < c; j0 += 64) {
       const int j = j0 + lane;
       int2 v = int2{-1, -1};
-      if (j < c) v = ld_cand(cq + (int64_t)tl * TILE + j);
+      if (j < c) v = cq[(int64_t)tl * TILE + j];
       const bool is_eq = j < c && v.x == tau;
       const uint64_t meq = __ballot(is_eq);
       const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -760,7 +769,7 @@ __global__ __launch_bounds__(256) void k_idx_prefill(
 struct IdxLayout {
   int n_tiles;
   int64_t npad;
-  int64_t off_slab, off_cbuf, off_hist, off_cnt, off_done2, bytes;
+  int64_t off_slab, off_cbuf, off_hist, off_cnt, bytes;
 };
 
 static inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -772,7 +781,6 @@ static IdxLayout idx_layout(int64_t BT, int64_t n_max) {
   L.npad = (int64_t)L.n_tiles * TILE;
   int64_t o = 0;
   // header: depends on B*T only, kept zero between calls
-  L.off_done2 = o; o = align_up(o + BT * 4, 256);
   L.off_hist = o; o = align_up(o + BT * NB1 * 4, 256);
   // body: rewritten by every call
   L.off_cnt = o; o = align_up(o + BT * L.n_tiles * 4, 256);
@@ -835,7 +843,6 @@ static int idx_phase(const IdxArgs& a, int phase) {
     int2* cbuf = reinterpret_cast<int2*>(ws + L.off_cbuf);
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.off_hist);
     int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.off_cnt);
-    uint32_t* done2 = reinterpret_cast<uint32_t*>(ws + L.off_done2);
     const int C = a.cand ? a.C : 0;
     dim3 grid(L.n_tiles, BT);
     if (phase == 0) {
@@ -853,15 +860,18 @@ static int idx_phase(const IdxArgs& a, int phase) {
       }
 #undef CSA_LAUNCH_SCAN
     } else {
+      hipLaunchKernelGGL(k_idx_select, grid, dim3(256), 0, a.stream, a.T, a.m, a.pos0,
+                         a.blk_cap, C, a.k, L.n_tiles, L.npad, slab, cbuf, cnt, hist,
+                         a.cand != nullptr);
       const int cap_lds = select_cap(a.k);
       const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int);
       if (lds > 65536 &&
-          hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_select),
+          hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_final),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return CSA_ERR_HIP;
-      hipLaunchKernelGGL(k_idx_select, grid, dim3(256), lds, a.stream, a.T, a.m, a.pos0,
-                         a.blk_cap, a.cand, C, a.k, L.n_tiles, L.npad, slab, cbuf, cnt, hist,
-                         done2, a.out_idx, a.out_score, cap_lds);
+      hipLaunchKernelGGL(k_idx_final, dim3(BT), dim3(256), lds, a.stream, a.T, a.m, a.pos0,
+                         a.blk_cap, a.cand, C, a.k, L.n_tiles, L.npad, cbuf, cnt, hist,
+                         a.out_idx, a.out_score, cap_lds);
     }
     CSA_TRY_LAUNCH();
     return CSA_OK;
