@@ -134,6 +134,39 @@ def cpu_baseline_decode(sets, wl, n_queries, check=True):
 # main
 # --------------------------------------------------------------------------
 
+SCAN_SOURCE = os.path.join(ROOT, "compressed_sparse_attention_compress_amd", "csrc", "indexer.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_idx_scan_decode_1m_traffic.json")
+
+
+def scan_source_hash() -> str:
+    import hashlib
+    return hashlib.sha256(open(SCAN_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per scan launch from the committed rocprofv3 counter runs, or
+    None when they are missing or were taken on a different kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != scan_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters (each launch reads and writes nbytes)."""
+    import torch
+    src = torch.ones(nbytes // 4, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,7 +176,12 @@ def main():
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--cpu-queries", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
               "is described in DESIGN.md and not run.", file=sys.stderr)
@@ -242,7 +280,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_launch_us": round(scan_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": scan_bytes,
         },
