@@ -42,7 +42,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t blk_cap, const int32_t* __restrict__ idx, int k,
     int m, const uint16_t* __restrict__ win, int Wcap, int W, int T, int H, int64_t pos0,
-    float scale_log2, int nsplit, int spl, void* __restrict__ out, int out_dtype,
+    float scale_log2, int nsplit, int spl, int n_queries, void* __restrict__ out, int out_dtype,
     float* __restrict__ lse, _Float16* __restrict__ part_o, float2* __restrict__ part_ml) {
   constexpr int NT = NW * 64;
   constexpr int KST = D + 8;  // entry-major row stride (bf16)
@@ -56,8 +56,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
   __shared__ __attribute__((aligned(16))) _Float16 Vs[D * VST];
   __shared__ int s_blk[IDX_CAP];
 
-  const int split = blockIdx.x % nsplit;
-  const int qi = blockIdx.x / nsplit;
+  // Workgroups are dealt to the 8 XCDs round-robin by id; all splits of a
+  // query are mapped onto one XCD so its q rows are fetched from HBM once and
+  // then served by that XCD's L2.
+  const int xcd = blockIdx.x & 7;
+  const int jx = blockIdx.x >> 3;
+  const int qi = xcd + 8 * (jx / nsplit);
+  const int split = jx % nsplit;
+  if (qi >= n_queries) return;
   const int b = qi / T;
   const int64_t t = pos0 + (qi - b * T);
   int64_t nsel = k;
@@ -309,77 +315,99 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
     }
     if (lse && g == 0) lse[(int64_t)qi * H + head] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
   } else {
-    // normalised partial output in float16 (|o| <= max |row|), m and l in float32
-    const int64_t pbase = (((int64_t)qi * nsplit + split) * H + head);
+    // normalised partial output in float16 (|o| <= max |row|), stored in
+    // register order [query][split][wave][ct][lane][4] so every store of a
+    // wave is 512 contiguous bytes; m and l in float32
+    _Float16* pw = part_o + ((((int64_t)qi * nsplit + split) * NW + wave) * CT) * 256 + lane * 4;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const int c = ct * 16 + 4 * g;
       v4h v;
       v[0] = (_Float16)(O[ct][0] * inv); v[1] = (_Float16)(O[ct][1] * inv);
       v[2] = (_Float16)(O[ct][2] * inv); v[3] = (_Float16)(O[ct][3] * inv);
-      *reinterpret_cast<v4h*>(part_o + pbase * D + c) = v;
+      *reinterpret_cast<v4h*>(pw + ct * 256) = v;
     }
-    if (g == 0) part_ml[pbase] = float2{m_run, l_tot};
+    if (g == 0) part_ml[((int64_t)qi * nsplit + split) * H + head] = float2{m_run, l_tot};
   }
 }
 
-// Merge of the split partials of one (query, head), splits in index order:
-// weights l_s * 2^(m_s - M) / L on the normalised partial outputs. The split
-// maxima and sums are staged in LDS first so the partial loads are independent.
+// Merge of the split partials, one workgroup per (query, 16-head block, 4
+// column tiles), one thread per (column tile, lane), splits in index order: weights l_s * 2^(m_s - M) / L on the normalised
+// partial outputs. The partials are read in the register order the attention
+// kernel wrote them ([ct][lane][4] per 16-head block), 512 contiguous bytes
+// per wave load; lane (j + 16g) of column tile ct holds head j, channels
+// 16ct + 4g .. +3.
 constexpr int MERGE_MAX = 256;  // splits per query handled by the merge
 template <int D>
-__global__ __launch_bounds__(D / 4) void k_attn_merge(const _Float16* __restrict__ part_o,
-                                                      const float2* __restrict__ part_ml,
-                                                      int nsplit, int H, void* __restrict__ out,
-                                                      int out_dtype, float* __restrict__ lse) {
-  __shared__ float s_m[MERGE_MAX], s_f[MERGE_MAX];
-  __shared__ float s_M, s_L;
-  const int64_t qh = blockIdx.x;
-  const int64_t qi = qh / H;
-  const int h = (int)(qh - qi * H);
-  for (int s = threadIdx.x; s < nsplit; s += D / 4) {
-    const float2 ml = part_ml[(qi * nsplit + s) * H + h];
-    s_m[s] = ml.x;
-    s_f[s] = ml.y;
+__global__ __launch_bounds__(256) void k_attn_merge(const _Float16* __restrict__ part_o,
+                                                    const float2* __restrict__ part_ml,
+                                                    int nsplit, int H, int NW,
+                                                    void* __restrict__ out, int out_dtype,
+                                                    float* __restrict__ lse) {
+  constexpr int CT = D / 16;
+  __shared__ float s_m[16][MERGE_MAX], s_f[16][MERGE_MAX];
+  __shared__ float s_inv[16];
+  // workgroup -> (query, 16-head block, group of 4 column tiles); thread ->
+  // one (ct, lane) pair
+  constexpr int CG = CT / 4;
+  const int cg = blockIdx.x % CG;
+  const int64_t qw = blockIdx.x / CG;
+  const int64_t qi = qw / NW;
+  const int w = (int)(qw - qi * NW);
+  // stage every (max, sum) of the block's 16 heads in one round of loads
+  for (int i = threadIdx.x; i < 16 * nsplit; i += 256) {
+    const int j = i & 15, sp = i >> 4;
+    const int h = w * 16 + j;
+    const float2 ml = h < H ? part_ml[(qi * nsplit + sp) * H + h] : float2{-INFINITY, 0.f};
+    s_m[j][sp] = ml.x;
+    s_f[j][sp] = ml.y;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 16) {
+    const int j = threadIdx.x;
+    const int h = w * 16 + j;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, s_m[s]);
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_m[j][sp]);
     float L = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float f = s_m[s] == -INFINITY ? 0.f : s_f[s] * exp2f(s_m[s] - M);
-      s_f[s] = f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float f = s_m[j][sp] == -INFINITY ? 0.f : s_f[j][sp] * exp2f(s_m[j][sp] - M);
+      s_f[j][sp] = f;
       L += f;
     }
-    s_M = M;
-    s_L = L;
+    s_inv[j] = L > 0.f ? 1.f / L : 0.f;
+    if (lse && cg == 0 && h < H) lse[qi * H + h] = (M + log2f(L)) * 0.69314718055994531f;
   }
   __syncthreads();
-  const float L = s_L;
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
-  const _Float16* src = part_o + (qi * nsplit * H + h) * D + 4 * threadIdx.x;
-#pragma unroll 4
-  for (int s = 0; s < nsplit; ++s) {
-    const float f = s_f[s];
-    const v4h o = *reinterpret_cast<const v4h*>(src + (int64_t)s * H * D);
-    acc.x += (float)o[0] * f; acc.y += (float)o[1] * f;
-    acc.z += (float)o[2] * f; acc.w += (float)o[3] * f;
+  const int64_t split_stride = (int64_t)NW * CT * 256;
+  const _Float16* base = part_o + (qi * nsplit * NW + w) * CT * 256;
+  {
+    const int pr = cg * 256 + threadIdx.x;
+    const int ct = pr >> 6, ln = pr & 63;
+    const int j = ln & 15, g = ln >> 4;
+    const int h = w * 16 + j;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    const _Float16* src = base + ct * 256 + ln * 4;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) {
+      const float f = s_f[j][s];
+      const v4h o = *reinterpret_cast<const v4h*>(src + (int64_t)s * split_stride);
+      acc.x += (float)o[0] * f; acc.y += (float)o[1] * f;
+      acc.z += (float)o[2] * f; acc.w += (float)o[3] * f;
+    }
+    if (h >= H) return;
+    const float inv = s_inv[j];
+    const int64_t o_off = (qi * H + h) * D + ct * 16 + 4 * g;
+    if (out_dtype == CSA_F32) {
+      float4 v;
+      v.x = acc.x * inv; v.y = acc.y * inv; v.z = acc.z * inv; v.w = acc.w * inv;
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o_off) = v;
+    } else {
+      typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+      v4bf v;
+      v[0] = (__bf16)(acc.x * inv); v[1] = (__bf16)(acc.y * inv);
+      v[2] = (__bf16)(acc.z * inv); v[3] = (__bf16)(acc.w * inv);
+      *reinterpret_cast<v4bf*>(reinterpret_cast<__bf16*>(out) + o_off) = v;
+    }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const int64_t base = qh * D + 4 * threadIdx.x;
-  if (out_dtype == CSA_F32) {
-    float4 v;
-    v.x = acc.x * inv; v.y = acc.y * inv; v.z = acc.z * inv; v.w = acc.w * inv;
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + base) = v;
-  } else {
-    typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-    v4bf v;
-    v[0] = (__bf16)(acc.x * inv); v[1] = (__bf16)(acc.y * inv);
-    v[2] = (__bf16)(acc.z * inv); v[3] = (__bf16)(acc.w * inv);
-    *reinterpret_cast<v4bf*>(reinterpret_cast<__bf16*>(out) + base) = v;
-  }
-  if (lse && threadIdx.x == 0) lse[qh] = (s_M + log2f(L)) * 0.69314718055994531f;
 }
 
 struct AttnPlan {
@@ -406,8 +434,9 @@ static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots) {
   }
   p.ws_bytes = 0;
   if (p.nsplit > 1) {
-    const int64_t units = (int64_t)B * T * p.nsplit * H;
-    p.ws_bytes = ((units * d * 2 + 255) / 256) * 256 + units * 8;
+    const int64_t units = (int64_t)B * T * p.nsplit;
+    const int64_t hpad = 16 * ((H + 15) / 16);
+    p.ws_bytes = ((units * hpad * d * 2 + 255) / 256) * 256 + units * H * 8;
   }
   return p;
 }
@@ -422,12 +451,13 @@ struct AttnArgs {
 template <int D, bool DENSE>
 static void launch_attn(const AttnArgs& a, const AttnPlan& p, _Float16* part_o, float2* part_ml) {
   const int nw = (a.H + 15) / 16;
-  const dim3 grid((unsigned)((int64_t)a.B * a.T * p.nsplit));
+  const int64_t nq = (int64_t)a.B * a.T;
+  const dim3 grid((unsigned)(((nq + 7) / 8) * 8 * p.nsplit));
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
 #define CSA_LAUNCH_ATTN(NW)                                                                  \
   hipLaunchKernelGGL((k_attn<D, NW, DENSE>), grid, dim3(NW * 64), 0, a.stream, a.q, a.codes, \
                      a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, a.H, a.pos0, \
-                     sl2, p.nsplit, p.spl, a.out, a.out_dtype, a.lse, part_o, part_ml)
+                     sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse, part_o, part_ml)
   switch (nw) {
     case 1: CSA_LAUNCH_ATTN(1); break;
     case 2: CSA_LAUNCH_ATTN(2); break;
@@ -436,8 +466,8 @@ static void launch_attn(const AttnArgs& a, const AttnPlan& p, _Float16* part_o, 
   }
 #undef CSA_LAUNCH_ATTN
   if (p.nsplit > 1)
-    hipLaunchKernelGGL(k_attn_merge<D>, dim3((unsigned)((int64_t)a.B * a.T * a.H)), dim3(D / 4),
-                       0, a.stream, part_o, part_ml, p.nsplit, a.H, a.out, a.out_dtype, a.lse);
+    hipLaunchKernelGGL(k_attn_merge<D>, dim3((unsigned)(nq * nw * (D / 64))), dim3(256), 0, a.stream,
+                       part_o, part_ml, p.nsplit, a.H, nw, a.out, a.out_dtype, a.lse);
 }
 
 static int attn_run(const AttnArgs& a, bool dense) {
@@ -462,16 +492,17 @@ static int attn_run(const AttnArgs& a, bool dense) {
   if (!csa_aligned(a.q, 16) || !csa_aligned(a.win, 16) || !csa_aligned(a.out, 16)) return CSA_ERR_ALIGN;
   if (nsel > 0 && !csa_aligned(a.codes, 8)) return CSA_ERR_ALIGN;
   const AttnPlan p = attn_plan(a.B, a.T, a.H, a.d, nsel + a.W);
-  if ((int64_t)a.B * a.T * p.nsplit > 0x7fffffffLL) return CSA_ERR_SHAPE;
+  if (((int64_t)a.B * a.T + 7) / 8 * 8 * p.nsplit > 0x7fffffffLL) return CSA_ERR_SHAPE;
   _Float16* part_o = nullptr;
   float2* part_ml = nullptr;
   if (p.nsplit > 1) {
     if (!a.ws || a.ws_bytes < p.ws_bytes) return CSA_ERR_WORKSPACE;
     if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
-    const int64_t units = (int64_t)a.B * a.T * p.nsplit * a.H;
+    const int64_t units = (int64_t)a.B * a.T * p.nsplit;
+    const int64_t hpad = 16 * ((a.H + 15) / 16);
     part_o = reinterpret_cast<_Float16*>(a.ws);
     part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a.ws) +
-                                        ((units * a.d * 2 + 255) / 256) * 256);
+                                        ((units * hpad * a.d * 2 + 255) / 256) * 256);
   }
   if (dense) {
     if (a.d == 128) launch_attn<128, true>(a, p, part_o, part_ml);

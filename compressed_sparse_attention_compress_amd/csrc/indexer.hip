@@ -254,32 +254,87 @@ __global__ __launch_bounds__(256) void k_idx_select(
 // split scan, phase 2b: one workgroup per query resolves the exact k-th score
 // among the candidates and writes the ascending index list
 // ------------------------------------------------------------------------
-// Dynamic LDS: t_off[MAX_TILES] ints, then cap_lds (score, entry) pairs. The
-// candidates of all tiles are copied there in one parallel pass (index order
-// kept); a query with more candidates than cap_lds (massive ties) walks the
-// per-tile lists in global memory instead. The histogram of the query is
-// cleared for the next call.
+// Dynamic LDS: t_off[MAX_TILES] ints, then cap_lds (score, entry) pairs, then
+// the speculative staging area. The histogram, the per-tile counts and the
+// first SPEC candidates of every tile are all loaded in one round (the
+// candidates speculatively, before their counts are known); only tiles with
+// more than SPEC candidates need a second round. A query with more candidates
+// than cap_lds (massive ties) walks the per-tile lists in global memory
+// instead. The histogram of the query is cleared for the next call.
+constexpr int SPEC = 32;
 __global__ __launch_bounds__(256) void k_idx_final(
     int T, int m, int64_t pos0, int64_t blk_cap, const int32_t* __restrict__ cand, int C, int k,
     int n_tiles, int64_t npad, const int2* __restrict__ cbuf, const int32_t* __restrict__ cnt,
     uint32_t* __restrict__ hist, int32_t* __restrict__ out_idx, int32_t* __restrict__ out_score,
-    int cap_lds) {
+    int cap_lds, int spec_tiles) {
   extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ int tmp[4];
   __shared__ uint32_t bh[256];
   __shared__ int s_red[8];
   __shared__ int w_gt[4], w_eq[4];
-  int* t_off = smem;             // [MAX_TILES]
-  int* area = smem + MAX_TILES;  // [2 * cap_lds]
+  int* t_off = smem;                                  // [MAX_TILES]
+  int* area = smem + MAX_TILES;                       // [2 * cap_lds]
+  int2* spec = reinterpret_cast<int2*>(area + 2 * cap_lds);  // [spec_tiles * SPEC]
   const int qi = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int2* cq = cbuf + (int64_t)qi * npad;
   uint32_t* hq = hist + (int64_t)qi * NB1;
-  const int keff = threshold_bin(hq, k, tmp, s_red);
-  const int T1 = s_red[0], A1 = s_red[1];
+  const int32_t* cntq = cnt + (int64_t)qi * n_tiles;
+
+  // ---- one round of independent loads
+  const int hb = NB1 - 1 - 2 * (int)threadIdx.x;
+  const int c_hi = (int)hq[hb];
+  const int c_lo = (int)hq[hb - 1];
+  // loads first, LDS stores after: a load feeding an LDS store in the same
+  // loop iteration would make each iteration wait for its load
+  const int nspec = spec_tiles * SPEC;
+  {
+    constexpr int SPT = 4096 / 256;  // speculative candidates per thread (max)
+    int2 r[SPT];
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      int i = threadIdx.x + 256 * u;
+      i = i < nspec ? i : 0;
+      r[u] = cq[(int64_t)(i / SPEC) * TILE + (i % SPEC)];
+    }
+    int cr[MAX_TILES / 256];
+#pragma unroll
+    for (int u = 0; u < MAX_TILES / 256; ++u) {
+      const int i = threadIdx.x + 256 * u;
+      cr[u] = i < n_tiles ? cntq[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int i = threadIdx.x + 256 * u;
+      if (i < nspec) spec[i] = r[u];
+    }
+#pragma unroll
+    for (int u = 0; u < MAX_TILES / 256; ++u) {
+      const int i = threadIdx.x + 256 * u;
+      if (i < n_tiles) t_off[i] = cr[u];
+    }
+  }
   // histogram consumed: clear it for the next call
-  hq[NB1 - 1 - 2 * threadIdx.x] = 0u;
-  hq[NB1 - 2 - 2 * threadIdx.x] = 0u;
+  hq[hb] = 0u;
+  hq[hb - 1] = 0u;
+
+  // ---- threshold bin (thread j owns bins 511-2j and 510-2j)
+  int total_valid;
+  const int incl = wg_scan_incl<256>(c_hi + c_lo, tmp, &total_valid);
+  const int excl = incl - c_hi - c_lo;
+  const int keff = k < total_valid ? k : total_valid;
+  if (keff > 0) {
+    if (excl + c_hi >= keff && excl < keff) {
+      s_red[0] = hb;
+      s_red[1] = excl;
+    }
+    if (incl >= keff && excl + c_hi < keff) {
+      s_red[0] = hb - 1;
+      s_red[1] = excl + c_hi;
+    }
+  }
+  __syncthreads();
+  const int T1 = s_red[0], A1 = s_red[1];
 
   int32_t* oi = out_idx + (int64_t)qi * k;
   int32_t* os = out_score ? out_score + (int64_t)qi * k : nullptr;
@@ -290,8 +345,6 @@ __global__ __launch_bounds__(256) void k_idx_final(
   }
   if (keff == 0) return;
 
-  const int32_t* cntq = cnt + (int64_t)qi * n_tiles;
-  for (int i = threadIdx.x; i < n_tiles; i += 256) t_off[i] = cntq[i];
   __syncthreads();
   const int last_cnt = t_off[n_tiles - 1];
   __syncthreads();
@@ -309,7 +362,9 @@ __global__ __launch_bounds__(256) void k_idx_final(
         const int mid = (lo + hi + 1) >> 1;
         if (t_off[mid] <= i) lo = mid; else hi = mid - 1;
       }
-      const int2 v = cq[(int64_t)lo * TILE + (i - t_off[lo])];
+      const int j = i - t_off[lo];
+      const int2 v = (lo < spec_tiles && j < SPEC) ? spec[lo * SPEC + j]
+                                                   : cq[(int64_t)lo * TILE + j];
       cs[i] = v.x;
       ce[i] = v.y;
     }
@@ -846,9 +901,9 @@ static int idx_phase(const IdxArgs& a, int phase) {
     const int C = a.cand ? a.C : 0;
     dim3 grid(L.n_tiles, BT);
     if (phase == 0) {
-#define CSA_LAUNCH_SCAN(DD, CC)                                                              \
-  hipLaunchKernelGGL((k_idx_scan<DD, CC>), grid, dim3(256), 0, a.stream, a.q_idx, a.w, a.keys, \
-                     a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.cand, C, L.npad, slab, hist)
+#define CSA_LAUNCH_SCAN(DD, CC)                                                       \
+  hipLaunchKernelGGL((k_idx_scan<DD, CC>), grid, dim3(256), 0, a.stream, a.q_idx, a.w, \
+                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.cand, C, L.npad, slab, hist)
       if (a.cand) {
         if (a.Di == 32) CSA_LAUNCH_SCAN(32, true);
         else if (a.Di == 64) CSA_LAUNCH_SCAN(64, true);
@@ -864,14 +919,18 @@ static int idx_phase(const IdxArgs& a, int phase) {
                          a.blk_cap, C, a.k, L.n_tiles, L.npad, slab, cbuf, cnt, hist,
                          a.cand != nullptr);
       const int cap_lds = select_cap(a.k);
-      const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int);
+      // speculative first-round candidates: SPEC per tile while they fit in
+      // 32 KiB of LDS
+      const int spec_tiles = L.n_tiles < 4096 / SPEC ? L.n_tiles : 4096 / SPEC;
+      const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int) +
+                         (size_t)spec_tiles * SPEC * sizeof(int2);
       if (lds > 65536 &&
           hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_final),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return CSA_ERR_HIP;
       hipLaunchKernelGGL(k_idx_final, dim3(BT), dim3(256), lds, a.stream, a.T, a.m, a.pos0,
                          a.blk_cap, a.cand, C, a.k, L.n_tiles, L.npad, cbuf, cnt, hist,
-                         a.out_idx, a.out_score, cap_lds);
+                         a.out_idx, a.out_score, cap_lds, spec_tiles);
     }
     CSA_TRY_LAUNCH();
     return CSA_OK;

@@ -186,6 +186,14 @@ def test_index_candidates():
     _index_case(2, 1, 8, 64, 4, 4 * 3000 - 1, 64, 3000, seed=16, cand_C=300, wzero=True)
 
 
+def test_index_many_queries():
+    """Split scan with many short query runs (1920 queries, 1000 blocks
+    each) and with several ragged tiles per query."""
+    say("index many queries")
+    _index_case(128, 15, 8, 64, 4, 4 * 1000 - 15, 96, 1007, seed=40)
+    _index_case(30, 10, 8, 64, 4, 4 * 13000 - 10, 96, 13007, seed=41, phases=True)
+
+
 @pytest.mark.parametrize("Hi,Di", [(4, 32), (8, 64), (16, 64), (2, 128), (5, 64)])
 def test_index_prefill_shapes(Hi, Di):
     say("index prefill", Hi, Di)
