@@ -1,11 +1,22 @@
 """Benchmark of the compressed sparse attention hot path on one MI355X.
 
-Default: the long-context decode workload (8 sequences at 1,048,576 tokens,
-d=512, m=4 -> 262,144 MXFP4 entries each, 64 heads, 8x64 int8 indexer,
-top-1024 + 128-token window). One step = csa_index_topk + csa_sparse_attn for
-one new query per sequence, on inputs resident in HBM. Several independent
-input sets are rotated so that the 134 MB of indexer keys per step is read
-from HBM rather than from the 256 MB Infinity Cache.
+Default workload, decode_1m: 8 sequences at 1,048,576 tokens, d=512, m=4
+(262,144 MXFP4 entries each), 64 heads, 8x64 int8 indexer, top-1024 plus the
+128-token window. One step = csa_index_topk + csa_sparse_attn for one new
+query per sequence, on inputs resident in HBM. Several independent input
+sets are rotated so that the 134 MB of indexer keys per step is read from
+HBM rather than from the 256 MB Infinity Cache. Steps are enqueued eagerly
+(--graph captures one HIP graph per input set and replays those instead;
+on this path graph replay was measured slower than eager launches).
+
+Other workloads (--workload), each printing its own line:
+  decode_32k      64 sequences at 32,768 tokens, top-512 (same step).
+  prefill_128k    one 131,072-token sequence in 16 chunks of 8192 queries:
+                  per chunk compress + index + attention; one step = all 16.
+  hca_reindex_1m  16 sequences at 1M tokens, one decode query each through
+                  four layers: HCA (m=128, dense), a CSA Full layer (top-4096
+                  pool, then its own top-512) and two Reindex layers scoring
+                  the pool.
 
 Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
 """
@@ -13,8 +24,8 @@ Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -26,6 +37,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0
 METRIC = "CSA decode queries/sec + achieved HBM GB/s (% peak) at 1M ctx, 1 MI355X"
+CSRC = os.path.join(ROOT, "compressed_sparse_attention_compress_amd", "csrc")
+KERNEL_SOURCE = {"k_idx_scan": "indexer.hip", "k_idx_prefill": "indexer.hip",
+                 "k_attn": "attn.hip", "k_compress_quantize": "compress.hip"}
 
 
 def log(*a):
@@ -61,21 +75,26 @@ def decode_set(csa, synth, wl, dev, seed):
     idx = torch.empty(wl.B, 1, wl.k, device=dev, dtype=torch.int32)
     out = torch.empty(wl.B, 1, wl.H, wl.d, device=dev, dtype=torch.bfloat16)
     return dict(codes=codes, scales=scales, keys=keys, q_idx=q_idx, w=w, q=q, win=win, idx=idx,
-                out=out, ws=csa.Workspace(dev))
+                out=out, ws=csa.Workspace(dev), ws_attn=csa.Workspace(dev))
 
 
 # --------------------------------------------------------------------------
 # algorithmic work
 # --------------------------------------------------------------------------
 
+def entry_bytes(wl):
+    return wl.d // 2 + wl.d // 32
+
+
 def decode_bytes_per_query(wl):
-    """Bytes the decode step must move per query."""
+    """Bytes one decode query must move through one CSA layer: its keys, its
+    indexer query and weights, the top-k list (written, read back), the
+    selected entries, the window, q and out."""
     nv = wl.L // wl.m
-    ent = wl.d // 2 + wl.d // 32
     keys = nv * wl.Di
     qw = wl.Hi * wl.Di + wl.Hi
-    idx = 2 * 4 * wl.k                    # idx written by the indexer, read by attention
-    entries = wl.k * ent
+    idx = 2 * 4 * wl.k
+    entries = wl.k * entry_bytes(wl)
     window = wl.W * wl.d * 2
     q_out = 2 * wl.H * wl.d * 2
     return dict(keys=keys, qw=qw, idx=idx, entries=entries, window=window, q_out=q_out,
@@ -88,69 +107,73 @@ def scan_bytes_per_query(wl):
     return (wl.L // wl.m) * wl.Di + wl.Hi * wl.Di + wl.Hi
 
 
+def attn_flops(H, d, n_slots):
+    """q.k and p.v multiply-adds (2 flops each) over n_slots slots, H heads."""
+    return 4 * H * d * n_slots
+
+
 # --------------------------------------------------------------------------
-# CPU baseline: the oracle, as it stands, on a bounded sample
+# timing helpers
 # --------------------------------------------------------------------------
 
-def cpu_baseline_decode(sets, wl, n_queries, check=True):
-    import numpy as np
+def capture_graphs(fns):
+    """One HIP graph per callable (each already run eagerly once, so every
+    workspace exists before capture)."""
     import torch
-    from threadpoolctl import threadpool_limits
-
-    import oracle.csa_oracle as O
-    s = sets[0]
-    keys = s["keys"].cpu().numpy()
-    q_idx, w = s["q_idx"].cpu().numpy(), s["w"].cpu().numpy()
-    qb = s["q"].cpu().view(torch.int16).numpy().view(np.uint16)
-    win = s["win"].cpu().view(torch.int16).numpy().view(np.uint16)
-    gpu_idx = s["idx"].cpu().numpy()
-    gpu_out = s["out"].cpu().float().numpy()
-    t_total = 0.0
-    worst = 0.0
-    idx_ok = True
-    with threadpool_limits(limits=1):
-        for b in range(n_queries):
-            codes = s["codes"][b].cpu().numpy()
-            scales = s["scales"][b].cpu().numpy()
-            t0 = time.perf_counter()
-            ri, _ = O.index_topk(q_idx[b, 0], w[b, 0], keys[b], wl.m, wl.L - 1, wl.k)
-            ro, _ = O.sparse_attn(qb[b, 0], codes, scales, ri, win[b], wl.Wcap, wl.W, wl.L - 1,
-                                  1.0)
-            t_total += time.perf_counter() - t0
-            if check:
-                idx_ok &= bool(np.array_equal(ri, gpu_idx[b, 0]))
-                rms = float(np.sqrt(np.mean(ro ** 2)))
-                err = np.abs(gpu_out[b, 0] - ro)
-                half_ulp = np.ldexp(1.0, (np.floor(np.log2(np.maximum(
-                    np.maximum(np.abs(gpu_out[b, 0]), np.abs(ro)), 1e-30))) - 8).astype(int))
-                worst = max(worst, float(np.maximum(0, err - half_ulp).max()) / rms)
-    return dict(value=n_queries / t_total, unit="queries/s", cores=1, kind="oracle",
-                sample=f"{n_queries} of the {wl.B} decode queries of one step (full 262,144-entry "
-                       f"index scan + top-{wl.k} + attention each), numpy fp64/int64, 1 thread",
-                seconds=round(t_total, 3)), dict(topk_exact=idx_ok, attn_excess_over_rms=worst)
+    graphs = []
+    for f in fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
 
 
-# --------------------------------------------------------------------------
-# main
-# --------------------------------------------------------------------------
+def time_steps(runs, steps, warmup):
+    """Warm up, then time exactly `steps` calls of runs[i % len(runs)]
+    bracketed by device synchronisations. Returns seconds."""
+    import torch
+    for i in range(warmup):
+        runs[i % len(runs)]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        runs[i % len(runs)]()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
-SCAN_SOURCE = os.path.join(ROOT, "compressed_sparse_attention_compress_amd", "csrc", "indexer.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_idx_scan_decode_1m_traffic.json")
+
+def split_event_ms(first, second, n_sets, reps):
+    """Average device time (ms) of first(i) measured with events on the
+    current stream, second(i) following it untimed; i rotates over sets."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record(stream)
+        first(r % n_sets)
+        ev[r][1].record(stream)
+        if second is not None:
+            second(r % n_sets)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
 
 
-def scan_source_hash() -> str:
-    import hashlib
-    return hashlib.sha256(open(SCAN_SOURCE, "rb").read()).hexdigest()[:16]
+def source_hash(kernel) -> str:
+    path = os.path.join(CSRC, KERNEL_SOURCE[kernel])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per scan launch from the committed rocprofv3 counter runs, or
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or
     None when they are missing or were taken on a different kernel source."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != scan_source_hash():
+    if rec.get("source_sha256_16") != source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -167,99 +190,123 @@ def copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_1m", choices=["decode_1m", "decode_32k"])
-    ap.add_argument("--sets", type=int, default=4)
-    ap.add_argument("--cpu-queries", type=int, default=4)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES (counter calibration)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration, 5)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
-              "is described in DESIGN.md and not run.", file=sys.stderr)
-        sys.exit(2)
+def bf16_excess(got, ref):
+    """max(|got - ref| - half a bfloat16 ulp of the larger, 0) / rms(ref)."""
+    import numpy as np
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    half_ulp = np.ldexp(1.0, (np.floor(np.log2(np.maximum(
+        np.maximum(np.abs(got), np.abs(ref)), 1e-30))) - 8).astype(int))
+    return float(np.maximum(0, np.abs(got - ref) - half_ulp).max()) / rms
 
+
+def host_bits(t):
+    import numpy as np
     import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
 
-    import compressed_sparse_attention_compress_amd as csa
-    import synth
 
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
+def timing_name(args):
+    return "hip graph replay" if args.graph else "eager launches"
+
+
+# --------------------------------------------------------------------------
+# decode (decode_1m, decode_32k)
+# --------------------------------------------------------------------------
+
+def cpu_baseline_decode(s, wl, n_queries):
+    """The oracle on the first n_queries queries of input set s (index + top-k
+    + attention each), one thread; also checks the device results of those
+    queries."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.csa_oracle as O
+    keys = s["keys"].cpu().numpy()
+    q_idx, w = s["q_idx"].cpu().numpy(), s["w"].cpu().numpy()
+    qb, win = host_bits(s["q"]), host_bits(s["win"])
+    gpu_idx = s["idx"].cpu().numpy()
+    gpu_out = s["out"].cpu().float().numpy()
+    t_total, worst, idx_ok = 0.0, 0.0, True
+    with threadpool_limits(limits=1):
+        for b in range(n_queries):
+            codes = s["codes"][b].cpu().numpy()
+            scales = s["scales"][b].cpu().numpy()
+            t0 = time.perf_counter()
+            ri, _ = O.index_topk(q_idx[b, 0], w[b, 0], keys[b], wl.m, wl.L - 1, wl.k)
+            ro, _ = O.sparse_attn(qb[b, 0], codes, scales, ri, win[b], wl.Wcap, wl.W, wl.L - 1,
+                                  1.0)
+            t_total += time.perf_counter() - t0
+            idx_ok &= bool(np.array_equal(ri, gpu_idx[b, 0]))
+            worst = max(worst, bf16_excess(gpu_out[b, 0], ro))
+    nv = wl.L // wl.m
+    return dict(value=n_queries / t_total, unit="queries/s", cores=1, kind="oracle",
+                sample=f"{n_queries} of the {wl.B} decode queries of one step (full {nv:,}-entry "
+                       f"index scan + top-{wl.k} + attention each), numpy fp64/int64, 1 thread",
+                seconds=round(t_total, 3)), dict(topk_exact=idx_ok, attn_excess_over_rms=worst)
+
+
+def run_decode(args, csa, synth, wl, dev):
+    import torch
     t_setup = time.time()
     sets = [decode_set(csa, synth, wl, dev, seed) for seed in range(args.sets)]
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s: {args.sets} input sets of {wl.name}")
+    pos = wl.L - 1
 
-    def step(s):
-        csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, wl.L - 1, wl.k, s["idx"],
+    def scan(i):
+        s = sets[i]
+        csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
                        workspace=s["ws"])
-        csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, wl.L - 1, 1.0,
-                        s["out"])
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    value = wl.B * args.steps / (t1 - t0)
-    log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s")
-
-    # dominant kernel: the indexer scan, timed with events on the launch stream
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    for i in range(args.steps):
-        s = sets[i % len(sets)]
-        ev_step[i][0].record(stream)
-        ev[i][0].record(stream)
-        csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, wl.L - 1, wl.k, s["idx"],
-                       workspace=s["ws"])
-        ev[i][1].record(stream)
-        csa.index_select(s["q_idx"], s["w"], s["keys"], wl.m, wl.L - 1, wl.k, s["idx"],
+    def select_attend(i):
+        s = sets[i]
+        csa.index_select(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
                          workspace=s["ws"])
-        csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, wl.L - 1, 1.0,
-                        s["out"])
-        ev_step[i][1].record(stream)
+        csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, pos, 1.0,
+                        s["out"], workspace=s["ws_attn"])
+
+    def step_fn(i):
+        def f():
+            s = sets[i]
+            csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
+                           workspace=s["ws"])
+            csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, pos, 1.0,
+                            s["out"], workspace=s["ws_attn"])
+        return f
+
+    eager = [step_fn(i) for i in range(len(sets))]
+    for f in eager:
+        f()
     torch.cuda.synchronize()
-    scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-    step_ev_ms = sum(a.elapsed_time(b) for a, b in ev_step) / len(ev_step)
+    runs = [g.replay for g in capture_graphs(eager)] if args.graph else eager
+    secs = time_steps(runs, args.steps, args.warmup)
+    ms_per_step = secs * 1e3 / args.steps
+    value = wl.B * args.steps / secs
+    log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s ({timing_name(args)})")
+
+    # dominant kernel: the indexer scan, timed with events on its launch stream
+    scan_ms = split_event_ms(scan, select_attend, len(sets), args.steps)
     scan_bytes = scan_bytes_per_query(wl) * wl.B
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     per_q = decode_bytes_per_query(wl)
     step_gbs = per_q["total"] * wl.B / (ms_per_step * 1e-3) / 1e9
-    log(f"scan {scan_ms * 1e3:.1f} us -> {achieved:.0f} GB/s; step (events) {step_ev_ms * 1e3:.1f} us")
+    log(f"scan {scan_ms * 1e3:.1f} us -> {achieved:.0f} GB/s")
 
-    cpu = None
-    parity = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        step(sets[0])
+        eager[0]()
         torch.cuda.synchronize()
-        cpu, parity = cpu_baseline_decode(sets, wl, min(args.cpu_queries, wl.B))
+        cpu, parity = cpu_baseline_decode(sets[0], wl, min(args.cpu_queries, wl.B))
         log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
 
-    rec = {
-        "metric": METRIC,
+    return {
+        "metric": METRIC if wl.name == "decode_1m" else
+        f"CSA decode queries/sec + achieved HBM GB/s (% peak) at {wl.L // 1024}K ctx, 1 MI355X",
         "value": round(value, 1),
         "unit": "queries/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -270,6 +317,7 @@ def main():
             "workload": wl.name, "batch": wl.B, "context": wl.L, "d": wl.d, "m": wl.m,
             "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8", "top_k": wl.k, "window": wl.W,
             "cache": "MXFP4 e2m1 + e8m0/32", "input_sets_rotated": args.sets,
+            "timing": timing_name(args),
         },
         "step_hbm": {"algorithmic_bytes_per_query": per_q["total"],
                      "GB/s": round(step_gbs, 1), "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
@@ -280,14 +328,421 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic("k_idx_scan", wl.name),
             "avg_launch_us": round(scan_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": scan_bytes,
         },
         "cpu_baseline": cpu,
         "parity": parity,
     }
-    print(json.dumps(rec), flush=True)
+
+
+# --------------------------------------------------------------------------
+# prefill (prefill_128k)
+# --------------------------------------------------------------------------
+
+def prefill_work(wl):
+    """Per chunk: attention flops and indexer int8 ops of its queries."""
+    att, ind = [], []
+    T = wl.chunk
+    for c in range(wl.L // T):
+        a = i = 0
+        for t in range(c * T, (c + 1) * T):
+            nv = (t + 1) // wl.m
+            a += attn_flops(wl.H, wl.d, min(wl.k, nv) + min(wl.W, t + 1))
+            i += 2 * nv * wl.Hi * wl.Di
+        att.append(a)
+        ind.append(i)
+    return att, ind
+
+
+def cpu_baseline_prefill(wl, x, keys, codes, scales, c, n_queries):
+    """The oracle on the last n_queries queries of chunk c (index + top-k +
+    attention each), one thread, checked against the device results."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.csa_oracle as O
+    T = wl.chunk
+    kn = keys[0].cpu().numpy()
+    cn, sn = codes[0].cpu().numpy(), scales[0].cpu().numpy()
+    qi, wn = x["q_idx"][0].cpu().numpy(), x["w"][0].cpu().numpy()
+    qb, win = host_bits(x["q"])[0], host_bits(x["win"])[0]
+    gi = x["idx"][0].cpu().numpy()
+    go = x["out"][0].cpu().float().numpy()
+    t_total, worst, ok = 0.0, 0.0, True
+    with threadpool_limits(limits=1):
+        for ti in range(T - n_queries, T):
+            t = c * T + ti
+            t0 = time.perf_counter()
+            ri, _ = O.index_topk(qi[ti], wn[ti], kn, wl.m, t, wl.k)
+            ro, _ = O.sparse_attn(qb[ti], cn, sn, ri, win, wl.Wcap, wl.W, t, 1.0)
+            t_total += time.perf_counter() - t0
+            ok &= bool(np.array_equal(ri, gi[ti]))
+            worst = max(worst, bf16_excess(go[ti], ro))
+    return dict(value=n_queries / t_total, unit="queries/s", cores=1, kind="oracle",
+                sample=f"last {n_queries} queries of the last {T}-query chunk (index over "
+                       f"{(c + 1) * T // wl.m:,} blocks + top-{wl.k} + attention each), "
+                       "numpy fp64/int64, 1 thread", seconds=round(t_total, 3)), \
+        dict(topk_exact=ok, attn_excess_over_rms=worst)
+
+
+def run_prefill(args, csa, synth, wl, dev):
+    import torch
+    T = wl.chunk
+    nch = wl.L // T
+    t_setup = time.time()
+    codes = torch.empty(1, wl.n_blocks, wl.d // 2, device=dev, dtype=torch.uint8)
+    scales = torch.empty(1, wl.n_blocks, wl.d // 32, device=dev, dtype=torch.uint8)
+    keys = synth.indexer_keys(wl, dev)
+    ch = []
+    for c in range(nch):
+        q_idx, w = synth.indexer_queries(wl, dev, layer=f"chunk{c}")
+        ch.append(dict(
+            kv=synth.latent_chunk(wl, 0, c, dev)[None].contiguous(),
+            gate=synth.gate_chunk(wl, 0, c, dev)[None].contiguous(),
+            q_idx=q_idx, w=w, q=synth.queries(wl, dev, layer=f"chunk{c}"),
+            win=synth.window_ring(wl, (c + 1) * T - 1, dev),
+            idx=torch.empty(1, T, wl.k, device=dev, dtype=torch.int32),
+            out=torch.empty(1, T, wl.H, wl.d, device=dev, dtype=torch.bfloat16)))
+    ws = csa.Workspace(dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s: {nch} chunks of {T} queries")
+
+    def compress(c):
+        x = ch[c]
+        csa.compress_quantize(x["kv"], x["gate"], c * T, wl.m, codes, scales)
+
+    def index(c):
+        x = ch[c]
+        csa.index_topk(x["q_idx"], x["w"], keys, wl.m, c * T, wl.k, x["idx"], workspace=ws)
+
+    def attend(c):
+        x = ch[c]
+        csa.sparse_attn(x["q"], codes, scales, x["idx"], x["win"], wl.W, c * T, 1.0, x["out"])
+
+    def step():
+        for c in range(nch):
+            compress(c)
+            index(c)
+            attend(c)
+
+    step()
+    torch.cuda.synchronize()
+    runs = [g.replay for g in capture_graphs([step])] if args.graph else [step]
+    secs = time_steps(runs, args.steps, args.warmup)
+    ms_per_step = secs * 1e3 / args.steps
+    value = wl.L * args.steps / secs
+    log(f"prefill step {ms_per_step:.2f} ms, {value:.0f} tokens/s ({timing_name(args)})")
+
+    # per-kernel device times (eager, events), one pass over the chunks
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nch)]
+    for c in range(nch):
+        ev[c][0].record(stream)
+        compress(c)
+        ev[c][1].record(stream)
+        index(c)
+        ev[c][2].record(stream)
+        attend(c)
+        ev[c][3].record(stream)
+    torch.cuda.synchronize()
+    t_cmp = sum(ev[c][0].elapsed_time(ev[c][1]) for c in range(nch))
+    t_idx = sum(ev[c][1].elapsed_time(ev[c][2]) for c in range(nch))
+    t_att = sum(ev[c][2].elapsed_time(ev[c][3]) for c in range(nch))
+    att, ind = prefill_work(wl)
+    att_tf = sum(att) / (t_att * 1e-3) / 1e12
+    ind_tops = sum(ind) / (t_idx * 1e-3) / 1e12
+    cmp_bytes = wl.L * (wl.d * 4 + 4) + (wl.L // wl.m) * entry_bytes(wl)
+    cmp_gbs = cmp_bytes / (t_cmp * 1e-3) / 1e9
+    log(f"attention {t_att:.2f} ms -> {att_tf:.0f} TFLOP/s; indexer {t_idx:.2f} ms -> "
+        f"{ind_tops:.0f} TOP/s; compress {t_cmp:.3f} ms -> {cmp_gbs:.0f} GB/s")
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline_prefill(wl, ch[-1], keys, codes, scales, nch - 1,
+                                           args.cpu_queries)
+        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
+
+    return {
+        "metric": "CSA prefill tokens/sec at 128K ctx (16 chunks of 8192) + MFMA utilisation, "
+                  "1 MI355X",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+fp16+int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "context": wl.L, "chunk": T, "d": wl.d, "m": wl.m,
+                   "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8", "top_k": wl.k,
+                   "window": wl.W, "timing": timing_name(args)},
+        "kernels_ms_per_step": {"compress": round(t_cmp, 4), "index_topk": round(t_idx, 4),
+                                "attention": round(t_att, 4)},
+        "indexer": {"bound": "mfma", "achieved": round(ind_tops, 1), "peak": INT8_PEAK_TOPS,
+                    "unit": "TOP/s", "frac": round(ind_tops / INT8_PEAK_TOPS, 4),
+                    "int8_ops_per_step": sum(ind)},
+        "compress": {"bound": "hbm", "achieved": round(cmp_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(cmp_gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_step": cmp_bytes},
+        "roofline": {
+            "kernel": "k_attn (sparse attention, one workgroup per query)",
+            "bound": "mfma",
+            "achieved": round(att_tf, 1),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(att_tf / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic("k_attn", wl.name),
+            "avg_launch_us": round(t_att * 1e3 / nch, 2),
+            "algorithmic_flops_per_launch": round(sum(att) / nch),
+        },
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+
+
+# --------------------------------------------------------------------------
+# four-layer decode (hca_reindex_1m)
+# --------------------------------------------------------------------------
+
+LAYERS = ("full", "reindex1", "reindex2")
+
+
+def layers_set(csa, synth, wl, dev, seed):
+    import torch
+    t = wl.L - 1
+    s = {}
+    s["h_codes"], s["h_scales"] = build_cache(csa, synth, wl, dev, seed, "hca", wl.m_hca, wl.L)
+    s["h_win"] = synth.window_ring(wl, t, dev, seed, layer="hca")
+    s["h_q"] = synth.queries(wl, dev, seed, layer="hca")
+    s["h_out"] = torch.empty(wl.B, 1, wl.H, wl.d, device=dev, dtype=torch.bfloat16)
+    s["codes"], s["scales"] = build_cache(csa, synth, wl, dev, seed, "main", wl.m, wl.L)
+    s["keys"] = synth.indexer_keys(wl, dev, seed)
+    s["win"] = synth.window_ring(wl, t, dev, seed)
+    s["pool"] = torch.empty(wl.B, 1, wl.pool, device=dev, dtype=torch.int32)
+    for layer in LAYERS:
+        q_idx, w = synth.indexer_queries(wl, dev, seed, layer=layer)
+        s[layer] = dict(q_idx=q_idx, w=w, q=synth.queries(wl, dev, seed, layer=layer),
+                        idx=torch.empty(wl.B, 1, wl.k, device=dev, dtype=torch.int32),
+                        out=torch.empty(wl.B, 1, wl.H, wl.d, device=dev, dtype=torch.bfloat16))
+    s["ws"] = csa.Workspace(dev)
+    s["ws_attn"] = csa.Workspace(dev)
+    return s
+
+
+def cpu_baseline_layers(s, wl, n_queries):
+    """The oracle on the first n_queries sequences through all four layers,
+    one thread, checked against the device results."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.csa_oracle as O
+    t = wl.L - 1
+    keys = s["keys"].cpu().numpy()
+    win, h_win = host_bits(s["win"]), host_bits(s["h_win"])
+    t_total, worst, ok = 0.0, 0.0, True
+    with threadpool_limits(limits=1):
+        for b in range(n_queries):
+            cn, sn = s["codes"][b].cpu().numpy(), s["scales"][b].cpu().numpy()
+            hc, hs = s["h_codes"][b].cpu().numpy(), s["h_scales"][b].cpu().numpy()
+            hq = host_bits(s["h_q"])[b, 0]
+            qs = {layer: (s[layer]["q_idx"][b, 0].cpu().numpy(),
+                          s[layer]["w"][b, 0].cpu().numpy(), host_bits(s[layer]["q"])[b, 0])
+                  for layer in LAYERS}
+            t0 = time.perf_counter()
+            ho, _ = O.hca_dense_attn(hq, hc, hs, wl.m_hca, h_win[b], wl.Wcap, wl.W, t, 1.0)
+            pool, _ = O.index_topk(qs["full"][0], qs["full"][1], keys[b], wl.m, t, wl.pool)
+            outs = {}
+            for layer in LAYERS:
+                qi, wi, qb = qs[layer]
+                ri, _ = O.index_topk(qi, wi, keys[b], wl.m, t, wl.k, cand=pool)
+                ro, _ = O.sparse_attn(qb, cn, sn, ri, win[b], wl.Wcap, wl.W, t, 1.0)
+                outs[layer] = (ri, ro)
+            t_total += time.perf_counter() - t0
+            ok &= bool(np.array_equal(pool, s["pool"][b, 0].cpu().numpy()))
+            worst = max(worst, bf16_excess(s["h_out"][b, 0].cpu().float().numpy(), ho))
+            for layer in LAYERS:
+                ri, ro = outs[layer]
+                ok &= bool(np.array_equal(ri, s[layer]["idx"][b, 0].cpu().numpy()))
+                worst = max(worst, bf16_excess(s[layer]["out"][b, 0].cpu().float().numpy(), ro))
+    return dict(value=n_queries / t_total, unit="queries/s", cores=1, kind="oracle",
+                sample=f"{n_queries} of the {wl.B} sequences through all four layers (HCA dense "
+                       f"over {wl.L // wl.m_hca:,} entries, top-{wl.pool} pool over "
+                       f"{wl.L // wl.m:,} blocks, three top-{wl.k} rescorings of the pool + "
+                       "attention), numpy fp64/int64, 1 thread",
+                seconds=round(t_total, 3)), dict(topk_exact=ok, attn_excess_over_rms=worst)
+
+
+def run_layers(args, csa, synth, wl, dev):
+    import torch
+    t = wl.L - 1
+    t_setup = time.time()
+    n_sets = min(args.sets, 2)
+    sets = [layers_set(csa, synth, wl, dev, seed) for seed in range(n_sets)]
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s: {n_sets} input sets of {wl.name}")
+
+    def hca(i):
+        s = sets[i]
+        csa.hca_dense_attn(s["h_q"], s["h_codes"], s["h_scales"], wl.m_hca, s["h_win"], wl.W, t,
+                           1.0, s["h_out"], workspace=s["ws_attn"])
+
+    def pool(i, fn="index_topk"):
+        s = sets[i]
+        x = s["full"]
+        getattr(csa, fn)(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.pool, s["pool"],
+                         workspace=s["ws"])
+
+    def csa_layer(i, layer):
+        s = sets[i]
+        x = s[layer]
+        csa.index_topk(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.k, x["idx"], cand=s["pool"],
+                       workspace=s["ws"])
+        csa.sparse_attn(x["q"], s["codes"], s["scales"], x["idx"], s["win"], wl.W, t, 1.0,
+                        x["out"], workspace=s["ws_attn"])
+
+    def step_fn(i):
+        def f():
+            hca(i)
+            pool(i)
+            for layer in LAYERS:
+                csa_layer(i, layer)
+        return f
+
+    eager = [step_fn(i) for i in range(n_sets)]
+    for f in eager:
+        f()
+    torch.cuda.synchronize()
+    runs = [g.replay for g in capture_graphs(eager)] if args.graph else eager
+    secs = time_steps(runs, args.steps, args.warmup)
+    ms_per_step = secs * 1e3 / args.steps
+    value = wl.B * args.steps / secs
+    log(f"4-layer step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s ({timing_name(args)})")
+
+    # per-layer device times (eager, events)
+    reps = max(4, min(args.steps, 20))
+    t_hca = split_event_ms(hca, None, n_sets, reps)
+    t_pool = split_event_ms(pool, None, n_sets, reps)
+    t_full = split_event_ms(lambda i: csa_layer(i, "full"), None, n_sets, reps)
+    t_re = split_event_ms(lambda i: csa_layer(i, "reindex1"), None, n_sets, reps)
+    scan_ms = split_event_ms(lambda i: pool(i, "index_scan"),
+                             lambda i: pool(i, "index_select"), n_sets, reps)
+    nv = wl.L // wl.m
+    scan_bytes = scan_bytes_per_query(wl) * wl.B
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    n_hca = wl.L // wl.m_hca
+    hca_flops = attn_flops(wl.H, wl.d, n_hca + wl.W) * wl.B
+    hca_tf = hca_flops / (t_hca * 1e-3) / 1e12
+    # algorithmic bytes per query. HCA: entries + window + q/out. Full: keys,
+    # indexer query, pool list (written, read back), top-k list, entries,
+    # window, q/out. Reindex: pool keys + pool ids, indexer query, top-k list,
+    # entries, window, q/out.
+    eb = entry_bytes(wl)
+    qo = 2 * wl.H * wl.d * 2
+    win_b = wl.W * wl.d * 2
+    qw = wl.Hi * wl.Di + wl.Hi
+    hca_b = n_hca * eb + win_b + qo
+    full_b = nv * wl.Di + qw + 2 * 4 * wl.pool + 2 * 4 * wl.k + wl.k * eb + win_b + qo
+    re_b = wl.pool * (wl.Di + 4) + qw + 2 * 4 * wl.k + wl.k * eb + win_b + qo
+    per_q = hca_b + full_b + 2 * re_b
+    step_gbs = per_q * wl.B / (ms_per_step * 1e-3) / 1e9
+    log(f"hca {t_hca * 1e3:.1f} us ({hca_tf:.0f} TFLOP/s); pool {t_pool * 1e3:.1f} us "
+        f"(scan {scan_ms * 1e3:.1f} us, {achieved:.0f} GB/s); full top-512+attn "
+        f"{t_full * 1e3:.1f} us; reindex {t_re * 1e3:.1f} us")
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        eager[0]()
+        torch.cuda.synchronize()
+        cpu, parity = cpu_baseline_layers(sets[0], wl, min(args.cpu_queries, 2))
+        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
+
+    return {
+        "metric": "CSA2 four-layer decode queries/sec (HCA + Full + 2 Reindex) at 1M ctx, "
+                  "1 MI355X",
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "context": wl.L, "d": wl.d, "m": wl.m,
+                   "m_hca": wl.m_hca, "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8",
+                   "pool": wl.pool, "top_k": wl.k, "window": wl.W,
+                   "input_sets_rotated": n_sets, "timing": timing_name(args)},
+        "layers_us": {"hca": round(t_hca * 1e3, 2), "full_pool_topk": round(t_pool * 1e3, 2),
+                      "full_topk_attn": round(t_full * 1e3, 2),
+                      "reindex_topk_attn": round(t_re * 1e3, 2)},
+        "step_hbm": {"algorithmic_bytes_per_query": per_q, "GB/s": round(step_gbs, 1),
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "hca": {"bound": "mfma", "achieved": round(hca_tf, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(hca_tf / BF16_PEAK_TFLOPS, 4),
+                "flops_per_launch": hca_flops},
+        "roofline": {
+            "kernel": "k_idx_scan (Full layer key scan)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("k_idx_scan", wl.name),
+            "avg_launch_us": round(scan_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": scan_bytes,
+        },
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+
+
+# --------------------------------------------------------------------------
+# main
+# --------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_1m",
+                    choices=["decode_1m", "decode_32k", "prefill_128k", "hca_reindex_1m"])
+    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--cpu-queries", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP graph replays instead of eager launches")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
+              "is described in DESIGN.md and not run.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        ap.error("--steps must be at least 1")
+
+    import torch
+
+    import compressed_sparse_attention_compress_amd as csa
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    if args.workload == "prefill_128k":
+        rec = run_prefill(args, csa, synth, wl, dev)
+    elif args.workload == "hca_reindex_1m":
+        rec = run_layers(args, csa, synth, wl, dev)
+    else:
+        rec = run_decode(args, csa, synth, wl, dev)
+    head = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
+    print(json.dumps({**head, **rec}), flush=True)
 
 
 if __name__ == "__main__":

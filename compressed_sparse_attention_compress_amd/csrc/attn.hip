@@ -7,17 +7,19 @@
 // (every query head reads one shared latent entry) and cue 16 (the FP4 cache
 // is dequantised right before attention, no FP4 arithmetic needed).
 //
-// One workgroup = one query (all H <= 64 heads, 16 per wave) x one range of
-// slots; slots are the selected entries followed by the W window tokens, and
-// all of them share one softmax. Slots are processed 64 at a time: the
-// workgroup gathers the 64 rows, dequantises each value once into LDS in two
-// layouts (entry-major bf16 for q.k, channel-major fp16 for p.v), then every
-// wave runs S^T = K Q^T (16x16x32 bf16 MFMA, K = d, four independent 16-slot
-// tiles) and O^T += V^T P^T (16x16x32 fp16 MFMA, two 32-slot k-steps) with an
-// online softmax whose head index is the lane's column in both products, so
-// no register shuffles are needed between them. O is rescaled only in passes
-// where some head's running maximum grew. Ranges of slots of one query can be
-// split over workgroups
+// One workgroup = one query (all H <= 64 heads) x one range of slots; slots
+// are the selected entries followed by the W window tokens, and all of them
+// share one softmax. Slots are processed 64 at a time: the workgroup gathers
+// the 64 rows and dequantises each value once into LDS in two layouts
+// (entry-major bf16 for q.k, channel-major fp16 for p.v). Two waves serve
+// each group of 16 heads: for q.k each takes 32 of the 64 slots over all d
+// channels (S^T = K Q^T, 16x16x32 bf16 MFMA); the pair exchanges its
+// per-head maxima and its P^T operands through LDS; for p.v each takes half
+// of the d channels over all 64 slots (O^T += V^T P^T, 16x16x32 fp16 MFMA).
+// The head index is the lane's column in both products, so no register
+// shuffles are needed between them, and every LDS byte of a pass is read by
+// four waves at most. O is rescaled only in passes where some head's running
+// maximum grew. Ranges of slots of one query can be split over workgroups
 // (decode); their partial (o, max, sum) are merged in a fixed order.
 #include "csa_internal.h"
 
@@ -38,23 +40,25 @@ struct RawSlots {
 };
 
 template <int D, int NW, bool DENSE>
-__global__ __launch_bounds__(NW * 64) void k_attn(
+__global__ __launch_bounds__(NW * 128) void k_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t blk_cap, const int32_t* __restrict__ idx, int k,
     int m, const uint16_t* __restrict__ win, int Wcap, int W, int T, int H, int64_t pos0,
     float scale_log2, int nsplit, int spl, int n_queries, void* __restrict__ out, int out_dtype,
-    float* __restrict__ lse, _Float16* __restrict__ part_o, float2* __restrict__ part_ml) {
-  constexpr int NT = NW * 64;
-  constexpr int KST = D + 8;  // entry-major row stride (bf16)
-  constexpr int KSTEPS = D / 32;
-  constexpr int CT = D / 16;
+    float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml) {
+  constexpr int NWV = 2 * NW;                 // waves: (head group, half)
+  constexpr int NT = NWV * 64;
+  constexpr int KST = D + 8;                  // entry-major row stride (bf16)
+  constexpr int KSTEPS = D / 32;              // q.k k-steps of 32 channels
+  constexpr int CTH = D / 32;                 // 16-channel output tiles of one half of d
   constexpr int SG = CH / 4;                  // slot groups of 4 per pass
   constexpr int TASKS = SG * (D / 16);
   constexpr int TPT = (TASKS + NT - 1) / NT;  // staging tasks per thread
-  constexpr int ET = CH / 16;                 // 16-slot score tiles per pass
   __shared__ __attribute__((aligned(16))) __bf16 Ks[CH * KST];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[D * VST];
   __shared__ int s_blk[IDX_CAP];
+  __shared__ __attribute__((aligned(16))) v8h s_p[NWV][64];  // each wave's P^T operand
+  __shared__ float s_x[NWV][16];                             // per-head max / sum exchange
 
   // Workgroups are dealt to the 8 XCDs round-robin by id; all splits of a
   // query are mapped onto one XCD so its q rows are fetched from HBM once and
@@ -76,8 +80,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
   const int64_t s_end = (s_begin + spl < n_slots) ? s_begin + spl : n_slots;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hg = wave >> 1, half = wave & 1, partner = wave ^ 1;
   const int i16 = lane & 15, g = lane >> 4;
-  const int head = wave * 16 + i16;
+  const int head = hg * 16 + i16;
 
   v8bf Qop[KSTEPS];
 #pragma unroll
@@ -87,9 +92,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
     else
       Qop[kk] = v8bf{};
   }
-  v4f O[CT];
+  v4f O[CTH];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) O[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < CTH; ++ct) O[ct] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
   const uint8_t* cbase = codes + (int64_t)b * blk_cap * (D / 2);
@@ -210,13 +215,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
           }
         }
       }
-      // validity of this lane's logit slots: tile et, row 4g + r
-      bool ok[ET][4];
+      // validity of this lane's logit slots: this wave's half, tile et, row 4g + r
+      const int64_t h0 = c0 + 32 * half;
+      bool ok[2][4];
 #pragma unroll
-      for (int et = 0; et < ET; ++et)
+      for (int et = 0; et < 2; ++et)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int64_t sl = c0 + 16 * et + 4 * g + r;
+          const int64_t sl = h0 + 16 * et + 4 * g + r;
           if (IS_WIN)
             ok[et][r] = sl < p1 && t - W + 1 + (sl - nsel) >= 0;
           else
@@ -225,21 +231,21 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
       if (PREFETCH && c0 + CH < p1 && c0 + 2 * CH <= tab0 + IDX_CAP) load_all(c0 + CH);
       __syncthreads();
 
-      // S^T[slot][head] for the pass's 16-slot tiles (independent chains)
-      v4f S[ET];
-#pragma unroll
-      for (int et = 0; et < ET; ++et) S[et] = v4f{0.f, 0.f, 0.f, 0.f};
+      // S^T[slot][head] for this wave's 32 slots (two independent 16-slot
+      // tiles) over all d channels
+      v4f S[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-        for (int et = 0; et < ET; ++et) {
-          const v8bf a = *reinterpret_cast<const v8bf*>(&Ks[(16 * et + i16) * KST + 32 * kk + 8 * g]);
+        for (int et = 0; et < 2; ++et) {
+          const v8bf a = *reinterpret_cast<const v8bf*>(
+              &Ks[(32 * half + 16 * et + i16) * KST + 32 * kk + 8 * g]);
           S[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qop[kk], S[et], 0, 0, 0);
         }
-      float x[ET][4];
+      float x[2][4];
       float cmax = -INFINITY;
 #pragma unroll
-      for (int et = 0; et < ET; ++et)
+      for (int et = 0; et < 2; ++et)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           x[et][r] = ok[et][r] ? S[et][r] * scale_log2 : -INFINITY;
@@ -247,43 +253,52 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
         }
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      if (g == 0) s_x[wave][i16] = cmax;
+      __syncthreads();
+      cmax = fmaxf(cmax, s_x[partner][i16]);
       // online-softmax rescale, skipped when no head of the wave saw its max
-      // grow (the branch is wave-uniform; heads whose max did not grow get
-      // alpha = 1). Letting the reference max lag (p up to 2^k in fp16) was
-      // measured to raise the p.v error steadily with k, so it never lags.
+      // grow (the branch is wave-uniform, and both waves of a head group see
+      // the same maxima; heads whose max did not grow get alpha = 1). Letting
+      // the reference max lag (p up to 2^k in fp16) was measured to raise the
+      // p.v error steadily with k, so it never lags.
       if (__ballot(cmax > m_run + RESCALE_LOG2)) {
         const float m_new = fmaxf(m_run, cmax);
         const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) O[ct] *= alpha;
+        for (int ct = 0; ct < CTH; ++ct) O[ct] *= alpha;
         m_run = m_new;
       }
       const bool none = m_run == -INFINITY;
-      // P^T slot order for the two 32-slot k-steps: slot e(g, s) =
-      // 32*kh + (s < 4 ? 4g + s : 16 + 4g + s - 4)
-      v8h P[ET / 2];
+      // P^T operand of the k-step over this half's 32 slots: element s of
+      // lane (j + 16g) is slot (s < 4 ? 4g + s : 16 + 4g + s - 4), head j
+      v8h P;
       float psum = 0.f;
 #pragma unroll
-      for (int et = 0; et < ET; ++et)
+      for (int et = 0; et < 2; ++et)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float pv = none ? 0.f : exp2f(x[et][r] - m_run);
           psum += pv;
-          P[et >> 1][(et & 1) * 4 + r] = (_Float16)pv;
+          P[et * 4 + r] = (_Float16)pv;
         }
       l_run += psum;
+      s_p[wave][lane] = P;
+      __syncthreads();
+      const v8h Pq = s_p[partner][lane];
+      // O^T[channel][head] += V^T P^T over both halves' slots, for this
+      // wave's half of the channels
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const _Float16* vrow = &Vs[(ct * 16 + i16) * VST];
+      for (int ct = 0; ct < CTH; ++ct) {
+        const _Float16* vrow = &Vs[(half * (D / 2) + ct * 16 + i16) * VST];
 #pragma unroll
-        for (int kh = 0; kh < ET / 2; ++kh) {
+        for (int kh = 0; kh < 2; ++kh) {
           const v4h lo = *reinterpret_cast<const v4h*>(vrow + 32 * kh + 4 * g);
           const v4h hi = *reinterpret_cast<const v4h*>(vrow + 32 * kh + 16 + 4 * g);
           v8h A;
           A[0] = lo[0]; A[1] = lo[1]; A[2] = lo[2]; A[3] = lo[3];
           A[4] = hi[0]; A[5] = hi[1]; A[6] = hi[2]; A[7] = hi[3];
-          O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, P[kh], O[ct], 0, 0, 0);
+          O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, kh == half ? P : Pq, O[ct], 0, 0, 0);
         }
       }
       __syncthreads();
@@ -292,14 +307,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
   phase(std::false_type{}, s_begin, s_end < nsel ? s_end : nsel);
   phase(std::true_type{}, s_begin > nsel ? s_begin : nsel, s_end);
 
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  // softmax denominator: this lane's slots, then the wave's, then the pair's
+  float l_own = l_run + __shfl_xor(l_run, 16, 64);
+  l_own += __shfl_xor(l_own, 32, 64);
+  if (g == 0) s_x[wave][i16] = l_own;
+  __syncthreads();
+  const float l_tot = l_own + s_x[partner][i16];
   if (head >= H) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (nsplit == 1) {
-    const int64_t base = ((int64_t)qi * H + head) * D;
+    const int64_t base = ((int64_t)qi * H + head) * D + half * (D / 2);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
+    for (int ct = 0; ct < CTH; ++ct) {
       const int c = ct * 16 + 4 * g;
       if (out_dtype == CSA_F32) {
         float4 v;
@@ -313,20 +332,22 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
         *reinterpret_cast<v4bf*>(reinterpret_cast<__bf16*>(out) + base + c) = v;
       }
     }
-    if (lse && g == 0) lse[(int64_t)qi * H + head] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+    if (lse && half == 0 && g == 0)
+      lse[(int64_t)qi * H + head] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
   } else {
-    // normalised partial output in float16 (|o| <= max |row|), stored in
-    // register order [query][split][wave][ct][lane][4] so every store of a
-    // wave is 512 contiguous bytes; m and l in float32
-    _Float16* pw = part_o + ((((int64_t)qi * nsplit + split) * NW + wave) * CT) * 256 + lane * 4;
+    // normalised partial output in float32, stored in register order
+    // [query][split][head group][column tile][lane][4] (the two halves of a
+    // head group hold column tiles 0..CTH-1 and CTH..2CTH-1), so every store
+    // of a wave is 1 KB contiguous; m and l in float32
+    float* pw = part_o + ((((int64_t)qi * nsplit + split) * NWV + wave) * CTH) * 256 + lane * 4;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      v4h v;
-      v[0] = (_Float16)(O[ct][0] * inv); v[1] = (_Float16)(O[ct][1] * inv);
-      v[2] = (_Float16)(O[ct][2] * inv); v[3] = (_Float16)(O[ct][3] * inv);
-      *reinterpret_cast<v4h*>(pw + ct * 256) = v;
+    for (int ct = 0; ct < CTH; ++ct) {
+      float4 v;
+      v.x = O[ct][0] * inv; v.y = O[ct][1] * inv; v.z = O[ct][2] * inv; v.w = O[ct][3] * inv;
+      *reinterpret_cast<float4*>(pw + ct * 256) = v;
     }
-    if (g == 0) part_ml[((int64_t)qi * nsplit + split) * H + head] = float2{m_run, l_tot};
+    if (half == 0 && g == 0)
+      part_ml[((int64_t)qi * nsplit + split) * H + head] = float2{m_run, l_tot};
   }
 }
 
@@ -338,7 +359,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
 // 16ct + 4g .. +3.
 constexpr int MERGE_MAX = 256;  // splits per query handled by the merge
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_merge(const _Float16* __restrict__ part_o,
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
                                                     int nsplit, int H, int NW,
                                                     void* __restrict__ out, int out_dtype,
@@ -378,20 +399,20 @@ __global__ __launch_bounds__(256) void k_attn_merge(const _Float16* __restrict__
   }
   __syncthreads();
   const int64_t split_stride = (int64_t)NW * CT * 256;
-  const _Float16* base = part_o + (qi * nsplit * NW + w) * CT * 256;
+  const float* base = part_o + (qi * nsplit * NW + w) * CT * 256;
   {
     const int pr = cg * 256 + threadIdx.x;
     const int ct = pr >> 6, ln = pr & 63;
     const int j = ln & 15, g = ln >> 4;
     const int h = w * 16 + j;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    const _Float16* src = base + ct * 256 + ln * 4;
+    const float* src = base + ct * 256 + ln * 4;
 #pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
       const float f = s_f[j][s];
-      const v4h o = *reinterpret_cast<const v4h*>(src + (int64_t)s * split_stride);
-      acc.x += (float)o[0] * f; acc.y += (float)o[1] * f;
-      acc.z += (float)o[2] * f; acc.w += (float)o[3] * f;
+      const float4 o = *reinterpret_cast<const float4*>(src + (int64_t)s * split_stride);
+      acc.x += o.x * f; acc.y += o.y * f;
+      acc.z += o.z * f; acc.w += o.w * f;
     }
     if (h >= H) return;
     const float inv = s_inv[j];
@@ -436,7 +457,7 @@ static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots) {
   if (p.nsplit > 1) {
     const int64_t units = (int64_t)B * T * p.nsplit;
     const int64_t hpad = 16 * ((H + 15) / 16);
-    p.ws_bytes = ((units * hpad * d * 2 + 255) / 256) * 256 + units * H * 8;
+    p.ws_bytes = ((units * hpad * d * 4 + 255) / 256) * 256 + units * H * 8;
   }
   return p;
 }
@@ -449,13 +470,13 @@ struct AttnArgs {
 };
 
 template <int D, bool DENSE>
-static void launch_attn(const AttnArgs& a, const AttnPlan& p, _Float16* part_o, float2* part_ml) {
+static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, float2* part_ml) {
   const int nw = (a.H + 15) / 16;
   const int64_t nq = (int64_t)a.B * a.T;
   const dim3 grid((unsigned)(((nq + 7) / 8) * 8 * p.nsplit));
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
 #define CSA_LAUNCH_ATTN(NW)                                                                  \
-  hipLaunchKernelGGL((k_attn<D, NW, DENSE>), grid, dim3(NW * 64), 0, a.stream, a.q, a.codes, \
+  hipLaunchKernelGGL((k_attn<D, NW, DENSE>), grid, dim3(NW * 128), 0, a.stream, a.q, a.codes, \
                      a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, a.H, a.pos0, \
                      sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse, part_o, part_ml)
   switch (nw) {
@@ -493,16 +514,16 @@ static int attn_run(const AttnArgs& a, bool dense) {
   if (nsel > 0 && !csa_aligned(a.codes, 8)) return CSA_ERR_ALIGN;
   const AttnPlan p = attn_plan(a.B, a.T, a.H, a.d, nsel + a.W);
   if (((int64_t)a.B * a.T + 7) / 8 * 8 * p.nsplit > 0x7fffffffLL) return CSA_ERR_SHAPE;
-  _Float16* part_o = nullptr;
+  float* part_o = nullptr;
   float2* part_ml = nullptr;
   if (p.nsplit > 1) {
     if (!a.ws || a.ws_bytes < p.ws_bytes) return CSA_ERR_WORKSPACE;
     if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
     const int64_t units = (int64_t)a.B * a.T * p.nsplit;
     const int64_t hpad = 16 * ((a.H + 15) / 16);
-    part_o = reinterpret_cast<_Float16*>(a.ws);
+    part_o = reinterpret_cast<float*>(a.ws);
     part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a.ws) +
-                                        ((units * hpad * a.d * 2 + 255) / 256) * 256);
+                                        ((units * hpad * a.d * 4 + 255) / 256) * 256);
   }
   if (dense) {
     if (a.d == 128) launch_attn<128, true>(a, p, part_o, part_ml);

@@ -31,6 +31,8 @@
 //    blocks in ascending order directly.
 #include "csa_internal.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int TILE = 2048;       // entries per split-scan workgroup
@@ -81,7 +83,7 @@ __device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
 // ------------------------------------------------------------------------
 // Every load is unconditional (addresses clamped into the buffers, invalid
 // entries masked after the product) so that a wave keeps 8 x 1 KB of keys in
-// flight; the scores of 4 column tiles are stored by all 64 lanes at once.
+// flight; scores are staged in LDS and written to the slab at the end.
 template <int DI, bool CAND>
 __global__ __launch_bounds__(256) void k_idx_scan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
@@ -91,6 +93,7 @@ __global__ __launch_bounds__(256) void k_idx_scan(
   constexpr int KS = (DI + 63) / 64;
   constexpr int BATCH = 8;
   __shared__ uint32_t lh[NB1];
+  __shared__ __attribute__((aligned(16))) int ssc[TILE];
   const int tile = blockIdx.x;
   const int qi = blockIdx.y;
   const int b = qi / T;
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(256) void k_idx_scan(
         const int v = g == 0 ? sc[4 * h] : (g == 1 ? sc[4 * h + 1] : (g == 2 ? sc[4 * h + 2] : sc[4 * h + 3]));
         const int64_t e = ebase + 64 * h + lane;
         if (e < N) {
-          sq[e] = v;
+          ssc[e - (int64_t)tile * TILE] = v;
           if (v >= 0) atomicAdd(&lh[score_bin512(v)], 1u);
         }
       }
@@ -176,6 +179,18 @@ __global__ __launch_bounds__(256) void k_idx_scan(
     }
   }
   __syncthreads();
+  // the tile's scores leave in one burst of 16-byte stores once every key
+  // load is done (stores issued between loads would be waited on with them)
+  {
+    const int j0 = threadIdx.x * 8;
+    const int64_t e0 = (int64_t)tile * TILE + j0;
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = e0 + j < N ? ssc[j0 + j] : -1;
+    int4* d = reinterpret_cast<int4*>(sq + e0);
+    d[0] = int4{v[0], v[1], v[2], v[3]};
+    d[1] = int4{v[4], v[5], v[6], v[7]};
+  }
   uint32_t* hq = hist + (int64_t)qi * NB1;
   for (int i = threadIdx.x; i < NB1; i += 256)
     if (lh[i]) atomicAdd(&hq[i], lh[i]);
@@ -853,6 +868,22 @@ static int select_cap(int k) {
   return c;
 }
 
+// Raise k_idx_final's dynamic LDS limit once per device (to the largest
+// size asked so far), so calls inside a graph capture make no attribute call.
+static bool final_lds_allow(size_t lds) {
+  static std::mutex mu;
+  static size_t allowed[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (allowed[dev] >= lds) return true;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_final),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return false;
+  allowed[dev] = lds;
+  return true;
+}
+
 static bool split_plan(int T, const int32_t* cand, int cand_given) {
   return cand != nullptr || cand_given || T < PREFILL_MIN_T;
 }
@@ -924,10 +955,7 @@ static int idx_phase(const IdxArgs& a, int phase) {
       const int spec_tiles = L.n_tiles < 4096 / SPEC ? L.n_tiles : 4096 / SPEC;
       const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int) +
                          (size_t)spec_tiles * SPEC * sizeof(int2);
-      if (lds > 65536 &&
-          hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_final),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return CSA_ERR_HIP;
+      if (lds > 65536 && !final_lds_allow(lds)) return CSA_ERR_HIP;
       hipLaunchKernelGGL(k_idx_final, dim3(BT), dim3(256), lds, a.stream, a.T, a.m, a.pos0,
                          a.blk_cap, a.cand, C, a.k, L.n_tiles, L.npad, cbuf, cnt, hist,
                          a.out_idx, a.out_score, cap_lds, spec_tiles);

@@ -182,8 +182,11 @@ int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);
  * Numerics: q.k products use the exact bfloat16 values with float32
  * accumulation; probabilities and values enter the value product as float16
  * (entries are exact in float16 while their scale byte lies in [104, 140]),
- * accumulated in float32. Workspace: csa_attn_workspace(...) bytes (no
- * initialisation needed); it may be NULL when that size is 0.
+ * accumulated in float32; when the slots of a query are split over
+ * workgroups (few queries per sequence), the normalised partial outputs are
+ * kept in float32 and merged in a fixed order. Workspace:
+ * csa_attn_workspace(...) bytes (no initialisation needed); it may be NULL
+ * when that size is 0.
  * ------------------------------------------------------------------------- */
 int64_t csa_attn_workspace(int B, int T, int H, int d, int64_t n_slots);
 
