@@ -82,10 +82,11 @@ __device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
 // split scan, phase 1: scores -> slab, per-query score histogram
 // ------------------------------------------------------------------------
 // Every load is unconditional (addresses clamped into the buffers, invalid
-// entries masked after the product) so that a wave keeps 8 x 1 KB of keys in
-// flight; scores are staged in LDS and written to the slab at the end.
+// entries masked after the product) and double-buffered, so that a wave keeps
+// 8 column tiles of keys in flight while the previous 8 are scored; scores
+// are staged in LDS and written to the slab at the end.
 template <int DI, bool CAND>
-__global__ __launch_bounds__(256) void k_idx_scan(
+__global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
     const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
     const int32_t* __restrict__ cand, int C, int64_t npad, int32_t* __restrict__ slab,
@@ -134,38 +135,41 @@ __global__ __launch_bounds__(256) void k_idx_scan(
   for (int ks = 0; ks < KS; ++ks) coff[ks] = (ks * 64 + 16 * g) % DI;
   const bool loads_ok = nv > 0;  // some key row exists to clamp to
   if (e_wave < N) {
-#pragma unroll 1
-    for (int bt = 0; bt < TILE / 4 / 16; bt += BATCH) {
-      const int64_t ebase = e_wave + (int64_t)bt * 16;
-      int64_t blk[BATCH];
-      bool valid[BATCH];
+    // two register buffers: the keys of batch bt + 1 are in flight while
+    // batch bt is in the matrix cores
+    constexpr int NBT = TILE / 4 / 16 / BATCH;  // batches of BATCH column tiles per wave
+    v4i Bk[2][BATCH][KS];
+    bool valid[2][BATCH];
+    auto issue = [&](int buf, int bt) {
+      const int64_t ebase = e_wave + (int64_t)bt * BATCH * 16;
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int64_t e = ebase + u * 16 + i16;
+        int64_t blk;
         if (CAND) {
           const int64_t c = cq[e < N ? e : N - 1];
-          valid[u] = e < N && c >= 0 && c < nv;
-          blk[u] = valid[u] ? c : 0;
+          valid[buf][u] = e < N && c >= 0 && c < nv;
+          blk = valid[buf][u] ? c : 0;
         } else {
-          valid[u] = e < nv;
-          blk[u] = valid[u] ? e : nv - 1;
+          valid[buf][u] = e < nv;
+          blk = valid[buf][u] ? e : nv - 1;
         }
-      }
-      v4i Bk[BATCH][KS];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          Bk[u][ks] = loads_ok ? __builtin_nontemporal_load(
-                                     reinterpret_cast<const v4i*>(kb + blk[u] * DI + coff[ks]))
-                               : v4i{0, 0, 0, 0};
+          Bk[buf][u][ks] = loads_ok ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(
+                                          kb + blk * DI + coff[ks]))
+                                    : v4i{0, 0, 0, 0};
+      }
+    };
+    auto consume = [&](int buf, int bt) {
+      const int64_t ebase = e_wave + (int64_t)bt * BATCH * 16;
       int sc[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
-        const int s = score_tile<KS>(A, Bk[u], wr);
-        sc[u] = valid[u] ? s : -1;
+        const int s = score_tile<KS>(A, Bk[buf][u], wr);
+        sc[u] = valid[buf][u] ? s : -1;
       }
-      // lane (j + 16g) stores tile 4h+g, entry j: 64 consecutive entries
+      // lane (j + 16g) takes tile 4h+g, entry j: 64 consecutive entries
 #pragma unroll
       for (int h = 0; h < BATCH / 4; ++h) {
         const int v = g == 0 ? sc[4 * h] : (g == 1 ? sc[4 * h + 1] : (g == 2 ? sc[4 * h + 2] : sc[4 * h + 3]));
@@ -175,7 +179,12 @@ __global__ __launch_bounds__(256) void k_idx_scan(
           if (v >= 0) atomicAdd(&lh[score_bin512(v)], 1u);
         }
       }
-      if (ebase + BATCH * 16 >= N) break;
+    };
+    issue(0, 0);
+#pragma unroll
+    for (int bt = 0; bt < NBT; ++bt) {
+      if (bt + 1 < NBT) issue((bt + 1) & 1, bt + 1);
+      consume(bt & 1, bt);
     }
   }
   __syncthreads();
@@ -368,28 +377,24 @@ __global__ __launch_bounds__(256) void k_idx_final(
 
   int need = keff - A1;  // threshold-bin candidates still to take
   if (M <= cap_lds) {
-    // ---- fast path: every candidate in LDS, index order kept
+    // ---- fast path: every candidate in LDS, index order kept. Two threads
+    // per tile copy its candidates (from the speculative stage, or from
+    // global memory past it) and track the score range of the threshold bin.
     int* cs = area;
     int* ce = area + cap_lds;
-    for (int i = threadIdx.x; i < M; i += 256) {
-      int lo = 0, hi = n_tiles - 1;  // last tile with t_off <= i
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (t_off[mid] <= i) lo = mid; else hi = mid - 1;
-      }
-      const int j = i - t_off[lo];
-      const int2 v = (lo < spec_tiles && j < SPEC) ? spec[lo * SPEC + j]
-                                                   : cq[(int64_t)lo * TILE + j];
-      cs[i] = v.x;
-      ce[i] = v.y;
-    }
-    __syncthreads();
     int vmin = 0x7fffffff, vmax = -1;
-    for (int i = threadIdx.x; i < M; i += 256) {
-      const int sv = cs[i];
-      if (score_bin512(sv) == T1) {
-        vmin = min(vmin, sv);
-        vmax = max(vmax, sv);
+    for (int tl = threadIdx.x >> 1; tl < n_tiles; tl += 128) {
+      const int base = t_off[tl];
+      const int c = (tl + 1 < n_tiles ? t_off[tl + 1] : M) - base;
+      for (int j = threadIdx.x & 1; j < c; j += 2) {
+        const int2 v = (tl < spec_tiles && j < SPEC) ? spec[tl * SPEC + j]
+                                                     : cq[(int64_t)tl * TILE + j];
+        cs[base + j] = v.x;
+        ce[base + j] = v.y;
+        if (score_bin512(v.x) == T1) {
+          vmin = min(vmin, v.x);
+          vmax = max(vmax, v.x);
+        }
       }
     }
 #pragma unroll
@@ -433,52 +438,43 @@ __global__ __launch_bounds__(256) void k_idx_final(
     }
     const int tau = lo;
     const int take_eq = need;
-    // ordered emission: wave w owns the contiguous range [w*Q, (w+1)*Q)
-    const int Q = (M + 3) / 4;
-    const int r0 = wave * Q, r1 = min(M, r0 + Q);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int gt = 0, eq = 0;
-    for (int i = r0 + lane; i < r1; i += 64) {
-      const int sv = cs[i];
-      gt += sv > tau;
-      eq += sv == tau;
-    }
+    // ordered emission: thread j owns entries [8j, 8j + 8) of each 2048-entry
+    // round; one scan of the packed (greater, equal) counts gives every
+    // entry's output position: #greater before it + min(#equal before it,
+    // take_eq)
+    int run_gt = 0, run_eq = 0;
+    for (int r0 = 0; r0 < M; r0 += 2048) {
+      const int i0 = r0 + 8 * (int)threadIdx.x;
+      int sv[8];
+      int gtc = 0, eqc = 0;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      gt += __shfl_xor(gt, off, 64);
-      eq += __shfl_xor(eq, off, 64);
-    }
-    if (lane == 0) {
-      w_gt[wave] = gt;
-      w_eq[wave] = eq;
-    }
-    __syncthreads();
-    int eq_run = 0, out_run = 0;
-    for (int w2 = 0; w2 < wave; ++w2) {
-      int take = take_eq - eq_run;
-      take = take < 0 ? 0 : (take > w_eq[w2] ? w_eq[w2] : take);
-      out_run += w_gt[w2] + take;
-      eq_run += w_eq[w2];
-    }
-    for (int i0 = r0; i0 < r1; i0 += 64) {
-      const int i = i0 + lane;
-      const bool in = i < r1;
-      const int sv = in ? cs[i] : -1;
-      const bool is_eq = in && sv == tau;
-      const uint64_t meq = __ballot(is_eq);
-      const int eq_rank = eq_run + __popcll(meq & below);
-      const bool take = in && (sv > tau || (is_eq && eq_rank < take_eq));
-      const uint64_t mt = __ballot(take);
-      if (take) {
-        const int pos = out_run + __popcll(mt & below);
-        if (pos < keff) {
-          const int e = ce[i];
+      for (int j = 0; j < 8; ++j) {
+        sv[j] = i0 + j < M ? cs[i0 + j] : -1;
+        gtc += sv[j] > tau;
+        eqc += sv[j] == tau;
+      }
+      const int mine = (gtc << 16) | eqc;
+      int tot;
+      const int before = wg_scan_incl<256>(mine, tmp, &tot) - mine;
+      int gb = run_gt + (before >> 16), eb = run_eq + (before & 0xffff);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int pos = -1;
+        if (sv[j] > tau) {
+          pos = gb + min(eb, take_eq);
+          ++gb;
+        } else if (sv[j] == tau) {
+          if (eb < take_eq) pos = gb + eb;
+          ++eb;
+        }
+        if (pos >= 0 && pos < keff) {
+          const int e = ce[i0 + j];
           oi[pos] = cqq ? cqq[e] : e;
-          if (os) os[pos] = sv;
+          if (os) os[pos] = sv[j];
         }
       }
-      eq_run += __popcll(meq);
-      out_run += __popcll(mt);
+      run_gt += tot >> 16;
+      run_eq += tot & 0xffff;
     }
     return;
   }
