@@ -84,14 +84,18 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
   const int i16 = lane & 15, g = lane >> 4;
   const int head = hg * 16 + i16;
 
+  // q rows are loaded after the first entry ids and raw entries have been
+  // requested, so that waiting for those does not wait for q as well
   v8bf Qop[KSTEPS];
+  bool q_loaded = false;
+  auto load_q = [&]() {
+    if (q_loaded) return;
+    q_loaded = true;
+    const int hq = head < H ? head : H - 1;
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    if (head < H)
-      Qop[kk] = *reinterpret_cast<const v8bf*>(q + ((int64_t)qi * H + head) * D + 32 * kk + 8 * g);
-    else
-      Qop[kk] = v8bf{};
-  }
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      Qop[kk] = *reinterpret_cast<const v8bf*>(q + ((int64_t)qi * H + hq) * D + 32 * kk + 8 * g);
+  };
   v4f O[CTH];
 #pragma unroll
   for (int ct = 0; ct < CTH; ++ct) O[ct] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -110,17 +114,23 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
     constexpr bool IS_WIN = decltype(is_win_tag)::value;
     if (p0 >= p1) return;
     int64_t tab0 = p0;  // first slot whose block id sits in s_blk[0]
+    // entry ids of slots [from, from + IDX_CAP) into LDS; all loads issued
+    // before the first is used (addresses clamped into the phase)
     auto refill = [&](int64_t from) {
+      constexpr int RPT = (IDX_CAP + NT - 1) / NT;
       __syncthreads();
       tab0 = from;
-      for (int i = threadIdx.x; i < IDX_CAP; i += NT) {
+      int64_t v[RPT];
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const int64_t sl = from + threadIdx.x + r * NT;
+        v[r] = DENSE ? sl : (int64_t)ibase[sl < p1 ? sl : p1 - 1];
+      }
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const int i = threadIdx.x + r * NT;
         const int64_t sl = from + i;
-        int blk = -1;
-        if (sl < p1) {
-          const int64_t v = DENSE ? sl : (int64_t)ibase[sl];
-          blk = (v >= 0 && v < blk_cap) ? (int)v : -1;
-        }
-        s_blk[i] = blk;
+        if (i < IDX_CAP) s_blk[i] = (sl < p1 && v[r] >= 0 && v[r] < blk_cap) ? (int)v[r] : -1;
       }
       __syncthreads();
     };
@@ -197,6 +207,7 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
       for (int tt = 0; tt < NRAW; ++tt) load_task(raw[tt], threadIdx.x + tt * NT, c0);
     };
     if (PREFETCH) load_all(p0);
+    load_q();
     for (int64_t c0 = p0; c0 < p1; c0 += CH) {
       if (!IS_WIN && c0 + CH > tab0 + IDX_CAP) {
         refill(c0);
@@ -374,45 +385,76 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   const int64_t qw = blockIdx.x / CG;
   const int64_t qi = qw / NW;
   const int w = (int)(qw - qi * NW);
-  // stage every (max, sum) of the block's 16 heads in one round of loads
-  for (int i = threadIdx.x; i < 16 * nsplit; i += 256) {
-    const int j = i & 15, sp = i >> 4;
-    const int h = w * 16 + j;
-    const float2 ml = h < H ? part_ml[(qi * nsplit + sp) * H + h] : float2{-INFINITY, 0.f};
-    s_m[j][sp] = ml.x;
-    s_f[j][sp] = ml.y;
+  const int pr = cg * 256 + threadIdx.x;
+  const int ct = pr >> 6, ln = pr & 63;
+  const int j = ln & 15, g = ln >> 4;
+  const int h = w * 16 + j;
+  const int64_t split_stride = (int64_t)NW * CT * 256;
+  const float* src = part_o + (qi * nsplit * NW + w) * CT * 256 + ct * 256 + ln * 4;
+  // the first PB partials are requested before the (max, sum) staging so that
+  // both rounds of loads overlap (indices clamped; surplus ones get weight 0)
+  constexpr int PB = 8;
+  float4 pre[PB];
+#pragma unroll
+  for (int u = 0; u < PB; ++u)
+    pre[u] = *reinterpret_cast<const float4*>(src + (int64_t)(u < nsplit ? u : 0) * split_stride);
+  // stage every (max, sum) of the block's 16 heads, two loads per thread in
+  // flight per round
+  for (int i0 = threadIdx.x; i0 < 16 * nsplit; i0 += 512) {
+    float2 ml[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = i0 + 256 * r;
+      const int jj = i & 15, sp = i >> 4;
+      const int hh = w * 16 + jj;
+      ml[r] = (i < 16 * nsplit && hh < H) ? part_ml[(qi * nsplit + sp) * H + hh]
+                                          : float2{-INFINITY, 0.f};
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = i0 + 256 * r;
+      if (i < 16 * nsplit) {
+        s_m[i & 15][i >> 4] = ml[r].x;
+        s_f[i & 15][i >> 4] = ml[r].y;
+      }
+    }
   }
   __syncthreads();
   if (threadIdx.x < 16) {
-    const int j = threadIdx.x;
-    const int h = w * 16 + j;
+    const int jj = threadIdx.x;
+    const int hh = w * 16 + jj;
     float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_m[j][sp]);
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_m[jj][sp]);
     float L = 0.f;
     for (int sp = 0; sp < nsplit; ++sp) {
-      const float f = s_m[j][sp] == -INFINITY ? 0.f : s_f[j][sp] * exp2f(s_m[j][sp] - M);
-      s_f[j][sp] = f;
+      const float f = s_m[jj][sp] == -INFINITY ? 0.f : s_f[jj][sp] * exp2f(s_m[jj][sp] - M);
+      s_f[jj][sp] = f;
       L += f;
     }
-    s_inv[j] = L > 0.f ? 1.f / L : 0.f;
-    if (lse && cg == 0 && h < H) lse[qi * H + h] = (M + log2f(L)) * 0.69314718055994531f;
+    s_inv[jj] = L > 0.f ? 1.f / L : 0.f;
+    if (lse && cg == 0 && hh < H) lse[qi * H + hh] = (M + log2f(L)) * 0.69314718055994531f;
   }
   __syncthreads();
-  const int64_t split_stride = (int64_t)NW * CT * 256;
-  const float* base = part_o + (qi * nsplit * NW + w) * CT * 256;
   {
-    const int pr = cg * 256 + threadIdx.x;
-    const int ct = pr >> 6, ln = pr & 63;
-    const int j = ln & 15, g = ln >> 4;
-    const int h = w * 16 + j;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    const float* src = base + ct * 256 + ln * 4;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) {
-      const float f = s_f[j][s];
-      const float4 o = *reinterpret_cast<const float4*>(src + (int64_t)s * split_stride);
-      acc.x += o.x * f; acc.y += o.y * f;
-      acc.z += o.z * f; acc.w += o.w * f;
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const float f = u < nsplit ? s_f[j][u] : 0.f;
+      acc.x += pre[u].x * f; acc.y += pre[u].y * f;
+      acc.z += pre[u].z * f; acc.w += pre[u].w * f;
+    }
+    for (int s0 = PB; s0 < nsplit; s0 += PB) {
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int sp = s0 + u < nsplit ? s0 + u : 0;
+        pre[u] = *reinterpret_cast<const float4*>(src + (int64_t)sp * split_stride);
+      }
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const float f = s0 + u < nsplit ? s_f[j][s0 + u] : 0.f;
+        acc.x += pre[u].x * f; acc.y += pre[u].y * f;
+        acc.z += pre[u].z * f; acc.w += pre[u].w * f;
+      }
     }
     if (h >= H) return;
     const float inv = s_inv[j];
