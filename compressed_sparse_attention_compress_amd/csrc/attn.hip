@@ -478,11 +478,14 @@ struct AttnPlan {
   int64_t ws_bytes;
 };
 
-// Decode (T < 16): slots are split over workgroups so that a query keeps
-// ~32 workgroups busy (whole 64-slot passes; >= n/16 slots for very long
-// dense ranges, where the partials would otherwise dominate). The split depends only
-// on per-sequence sizes, never on B, so a sequence's output is the same in
-// any batch. Longer query runs take one workgroup per query.
+// Decode (T < 16): the slots of a query are split over workgroups in whole
+// 64-slot passes, at most ~32 per query (>= n/16 slots for very long dense
+// ranges, where the partials would otherwise dominate), and no more than it
+// takes to give every compute unit one workgroup: with many queries each
+// workgroup takes more passes instead, which keeps the partial outputs (128
+// KiB per workgroup at 64 heads x 512) small. A sequence's output is
+// therefore the same in any batch of up to 256 / (most splits) queries.
+// Longer query runs take one workgroup per query.
 static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots) {
   AttnPlan p;
   if (T >= 16 || n_slots <= CH) {
@@ -490,8 +493,13 @@ static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots) {
     p.spl = (int)(((n_slots + CH - 1) / CH) * CH);
     if (p.spl < CH) p.spl = CH;
   } else {
-    int64_t spl = (n_slots + (n_slots > 4096 ? 15 : 31)) / (n_slots > 4096 ? 16 : 32);
-    spl = ((spl + CH - 1) / CH) * CH;
+    const int64_t div = n_slots > 4096 ? 16 : 32;
+    int64_t spl = ((n_slots + div - 1) / div + CH - 1) / CH * CH;
+    const int64_t most = (n_slots + spl - 1) / spl;
+    const int64_t nq = (int64_t)B * T;
+    const int64_t fill = nq > 0 ? (256 + nq - 1) / nq : most;
+    const int64_t ns = most < fill ? most : fill;
+    spl = ((n_slots + ns - 1) / ns + CH - 1) / CH * CH;
     p.spl = (int)spl;
     p.nsplit = (int)((n_slots + spl - 1) / spl);
   }

@@ -85,7 +85,7 @@ __device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
 // entries masked after the product) and double-buffered, so that a wave keeps
 // 8 column tiles of keys in flight while the previous 8 are scored; scores
 // are staged in LDS and written to the slab at the end.
-template <int DI, bool CAND>
+template <int DI, bool CAND, int SUB>
 __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
     const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
@@ -93,9 +93,10 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     uint32_t* __restrict__ hist) {
   constexpr int KS = (DI + 63) / 64;
   constexpr int BATCH = 8;
+  constexpr int SPAN = TILE / SUB;  // entries per workgroup (SUB workgroups per tile)
   __shared__ uint32_t lh[NB1];
-  __shared__ __attribute__((aligned(16))) int ssc[TILE];
-  const int tile = blockIdx.x;
+  __shared__ __attribute__((aligned(16))) int ssc[SPAN];
+  const int64_t wg0 = (int64_t)blockIdx.x * SPAN;  // first entry of the workgroup
   const int qi = blockIdx.y;
   const int b = qi / T;
   const int64_t t = pos0 + (qi - b * T);
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   }
   __syncthreads();
 
-  const int64_t e_wave = (int64_t)tile * TILE + wave * (TILE / 4);
+  const int64_t e_wave = wg0 + wave * (SPAN / 4);
   const int8_t* kb = keys + (int64_t)b * blk_cap * DI;
   const int32_t* cq = CAND ? cand + (int64_t)qi * C : nullptr;
   int32_t* sq = slab + (int64_t)qi * npad;
@@ -137,9 +138,21 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   if (e_wave < N) {
     // two register buffers: the keys of batch bt + 1 are in flight while
     // batch bt is in the matrix cores
-    constexpr int NBT = TILE / 4 / 16 / BATCH;  // batches of BATCH column tiles per wave
+    constexpr int NBT = SPAN / 4 / 16 / BATCH;  // batches of BATCH column tiles per wave
     v4i Bk[2][BATCH][KS];
     bool valid[2][BATCH];
+    // pool entries: every block id of the wave is requested up front, so the
+    // key loads of a batch do not wait for its ids
+    int cid[CAND ? NBT : 1][BATCH];
+    if (CAND) {
+#pragma unroll
+      for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int64_t e = e_wave + (int64_t)bt * BATCH * 16 + u * 16 + i16;
+          cid[CAND ? bt : 0][u] = cq[e < N ? e : N - 1];
+        }
+    }
     auto issue = [&](int buf, int bt) {
       const int64_t ebase = e_wave + (int64_t)bt * BATCH * 16;
 #pragma unroll
@@ -147,7 +160,7 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
         const int64_t e = ebase + u * 16 + i16;
         int64_t blk;
         if (CAND) {
-          const int64_t c = cq[e < N ? e : N - 1];
+          const int64_t c = cid[CAND ? bt : 0][u];
           valid[buf][u] = e < N && c >= 0 && c < nv;
           blk = valid[buf][u] ? c : 0;
         } else {
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
         const int v = g == 0 ? sc[4 * h] : (g == 1 ? sc[4 * h + 1] : (g == 2 ? sc[4 * h + 2] : sc[4 * h + 3]));
         const int64_t e = ebase + 64 * h + lane;
         if (e < N) {
-          ssc[e - (int64_t)tile * TILE] = v;
+          ssc[e - wg0] = v;
           if (v >= 0) atomicAdd(&lh[score_bin512(v)], 1u);
         }
       }
@@ -188,11 +201,11 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     }
   }
   __syncthreads();
-  // the tile's scores leave in one burst of 16-byte stores once every key
-  // load is done (stores issued between loads would be waited on with them)
-  {
+  // the scores leave in one burst of 16-byte stores once every key load is
+  // done (stores issued between loads would be waited on with them)
+  if (threadIdx.x * 8 < SPAN) {
     const int j0 = threadIdx.x * 8;
-    const int64_t e0 = (int64_t)tile * TILE + j0;
+    const int64_t e0 = wg0 + j0;
     int v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = e0 + j < N ? ssc[j0 + j] : -1;
@@ -280,17 +293,17 @@ __global__ __launch_bounds__(256) void k_idx_select(
 // ------------------------------------------------------------------------
 // Dynamic LDS: t_off[MAX_TILES] ints, then cap_lds (score, entry) pairs, then
 // the speculative staging area. The histogram, the per-tile counts and the
-// first SPEC candidates of every tile are all loaded in one round (the
+// first 2^spec_shift candidates of every tile are all loaded in one round (the
 // candidates speculatively, before their counts are known); only tiles with
-// more than SPEC candidates need a second round. A query with more candidates
+// more candidates than that need a second round. A query with more candidates
 // than cap_lds (massive ties) walks the per-tile lists in global memory
 // instead. The histogram of the query is cleared for the next call.
-constexpr int SPEC = 32;
+constexpr int SPEC_SLOTS = 4096;  // speculative candidates staged per query (32 KiB)
 __global__ __launch_bounds__(256) void k_idx_final(
     int T, int m, int64_t pos0, int64_t blk_cap, const int32_t* __restrict__ cand, int C, int k,
     int n_tiles, int64_t npad, const int2* __restrict__ cbuf, const int32_t* __restrict__ cnt,
     uint32_t* __restrict__ hist, int32_t* __restrict__ out_idx, int32_t* __restrict__ out_score,
-    int cap_lds, int spec_tiles) {
+    int cap_lds, int spec_tiles, int spec_shift) {
   extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ int tmp[4];
   __shared__ uint32_t bh[256];
@@ -298,7 +311,7 @@ __global__ __launch_bounds__(256) void k_idx_final(
   __shared__ int w_gt[4], w_eq[4];
   int* t_off = smem;                                  // [MAX_TILES]
   int* area = smem + MAX_TILES;                       // [2 * cap_lds]
-  int2* spec = reinterpret_cast<int2*>(area + 2 * cap_lds);  // [spec_tiles * SPEC]
+  int2* spec = reinterpret_cast<int2*>(area + 2 * cap_lds);  // [spec_tiles << spec_shift]
   const int qi = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int2* cq = cbuf + (int64_t)qi * npad;
@@ -311,15 +324,16 @@ __global__ __launch_bounds__(256) void k_idx_final(
   const int c_lo = (int)hq[hb - 1];
   // loads first, LDS stores after: a load feeding an LDS store in the same
   // loop iteration would make each iteration wait for its load
-  const int nspec = spec_tiles * SPEC;
+  const int nspec = spec_tiles << spec_shift;
+  const int spt = 1 << spec_shift;
   {
-    constexpr int SPT = 4096 / 256;  // speculative candidates per thread (max)
+    constexpr int SPT = SPEC_SLOTS / 256;  // speculative candidates per thread (max)
     int2 r[SPT];
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
       int i = threadIdx.x + 256 * u;
       i = i < nspec ? i : 0;
-      r[u] = cq[(int64_t)(i / SPEC) * TILE + (i % SPEC)];
+      r[u] = cq[(int64_t)(i >> spec_shift) * TILE + (i & (spt - 1))];
     }
     int cr[MAX_TILES / 256];
 #pragma unroll
@@ -387,7 +401,7 @@ __global__ __launch_bounds__(256) void k_idx_final(
       const int base = t_off[tl];
       const int c = (tl + 1 < n_tiles ? t_off[tl + 1] : M) - base;
       for (int j = threadIdx.x & 1; j < c; j += 2) {
-        const int2 v = (tl < spec_tiles && j < SPEC) ? spec[tl * SPEC + j]
+        const int2 v = (tl < spec_tiles && j < spt) ? spec[(tl << spec_shift) + j]
                                                      : cq[(int64_t)tl * TILE + j];
         cs[base + j] = v.x;
         ce[base + j] = v.y;
@@ -928,33 +942,48 @@ static int idx_phase(const IdxArgs& a, int phase) {
     const int C = a.cand ? a.C : 0;
     dim3 grid(L.n_tiles, BT);
     if (phase == 0) {
-#define CSA_LAUNCH_SCAN(DD, CC)                                                       \
-  hipLaunchKernelGGL((k_idx_scan<DD, CC>), grid, dim3(256), 0, a.stream, a.q_idx, a.w, \
+      // small scans split each tile over 2 or 4 workgroups so that about 512
+      // workgroups stream the keys
+      const int64_t nwg = (int64_t)L.n_tiles * BT;
+      const int sub = nwg >= 512 ? 1 : (nwg >= 256 ? 2 : 4);
+      const dim3 sgrid(L.n_tiles * sub, BT);
+#define CSA_LAUNCH_SCAN(DD, CC, SS)                                                          \
+  hipLaunchKernelGGL((k_idx_scan<DD, CC, SS>), sgrid, dim3(256), 0, a.stream, a.q_idx, a.w, \
                      a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.cand, C, L.npad, slab, hist)
+#define CSA_LAUNCH_SCAN_S(DD, CC)                  \
+  do {                                            \
+    if (sub == 1) CSA_LAUNCH_SCAN(DD, CC, 1);     \
+    else if (sub == 2) CSA_LAUNCH_SCAN(DD, CC, 2); \
+    else CSA_LAUNCH_SCAN(DD, CC, 4);              \
+  } while (0)
       if (a.cand) {
-        if (a.Di == 32) CSA_LAUNCH_SCAN(32, true);
-        else if (a.Di == 64) CSA_LAUNCH_SCAN(64, true);
-        else CSA_LAUNCH_SCAN(128, true);
+        if (a.Di == 32) CSA_LAUNCH_SCAN_S(32, true);
+        else if (a.Di == 64) CSA_LAUNCH_SCAN_S(64, true);
+        else CSA_LAUNCH_SCAN_S(128, true);
       } else {
-        if (a.Di == 32) CSA_LAUNCH_SCAN(32, false);
-        else if (a.Di == 64) CSA_LAUNCH_SCAN(64, false);
-        else CSA_LAUNCH_SCAN(128, false);
+        if (a.Di == 32) CSA_LAUNCH_SCAN_S(32, false);
+        else if (a.Di == 64) CSA_LAUNCH_SCAN_S(64, false);
+        else CSA_LAUNCH_SCAN_S(128, false);
       }
+#undef CSA_LAUNCH_SCAN_S
 #undef CSA_LAUNCH_SCAN
     } else {
       hipLaunchKernelGGL(k_idx_select, grid, dim3(256), 0, a.stream, a.T, a.m, a.pos0,
                          a.blk_cap, C, a.k, L.n_tiles, L.npad, slab, cbuf, cnt, hist,
                          a.cand != nullptr);
       const int cap_lds = select_cap(a.k);
-      // speculative first-round candidates: SPEC per tile while they fit in
-      // 32 KiB of LDS
-      const int spec_tiles = L.n_tiles < 4096 / SPEC ? L.n_tiles : 4096 / SPEC;
+      // speculative first-round candidates: the staging area is shared out
+      // evenly, a power of two per tile between 32 and TILE
+      int spec_shift = 5;
+      while ((1 << (spec_shift + 1)) <= TILE && ((int64_t)L.n_tiles << (spec_shift + 1)) <= SPEC_SLOTS)
+        ++spec_shift;
+      const int spec_tiles = L.n_tiles < (SPEC_SLOTS >> spec_shift) ? L.n_tiles : (SPEC_SLOTS >> spec_shift);
       const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int) +
-                         (size_t)spec_tiles * SPEC * sizeof(int2);
+                         ((size_t)spec_tiles << spec_shift) * sizeof(int2);
       if (lds > 65536 && !final_lds_allow(lds)) return CSA_ERR_HIP;
       hipLaunchKernelGGL(k_idx_final, dim3(BT), dim3(256), lds, a.stream, a.T, a.m, a.pos0,
                          a.blk_cap, a.cand, C, a.k, L.n_tiles, L.npad, cbuf, cnt, hist,
-                         a.out_idx, a.out_score, cap_lds, spec_tiles);
+                         a.out_idx, a.out_score, cap_lds, spec_tiles, spec_shift);
     }
     CSA_TRY_LAUNCH();
     return CSA_OK;

@@ -188,10 +188,15 @@ def test_index_candidates():
 
 def test_index_many_queries():
     """Split scan with many short query runs (1920 queries, 1000 blocks
-    each) and with several ragged tiles per query."""
+    each), with several ragged tiles per query, and with enough work that a
+    scan workgroup takes two or four 2048-entry tiles (ragged last group)."""
     say("index many queries")
     _index_case(128, 15, 8, 64, 4, 4 * 1000 - 15, 96, 1007, seed=40)
     _index_case(30, 10, 8, 64, 4, 4 * 13000 - 10, 96, 13007, seed=41, phases=True)
+    _index_case(128, 2, 8, 64, 4, 4 * 3000 - 2, 96, 3007, seed=42)     # 2 tiles per workgroup
+    _index_case(64, 2, 8, 64, 4, 4 * 9500 - 2, 96, 9507, seed=43)      # 4 per workgroup, ragged
+    _index_case(128, 2, 4, 128, 4, 4 * 3000 - 2, 64, 3007, seed=44)    # 128-dim keys, 2 per group
+    _index_case(64, 2, 8, 64, 4, 4 * 9500 - 2, 96, 9507, seed=45, cand_C=4500)  # pool, 3 tiles
 
 
 @pytest.mark.parametrize("Hi,Di", [(4, 32), (8, 64), (16, 64), (2, 128), (5, 64)])
@@ -364,7 +369,8 @@ def test_hca_dense(T):
 
 def test_determinism_and_batch_invariance():
     """A sequence's outputs are bit-identical across runs and whether it is
-    decoded alone or inside a larger batch."""
+    decoded alone or inside a larger batch (a batch this small does not
+    change how the slots of a query are split over workgroups)."""
     say("determinism / batch invariance")
     B, L, d, m, H, k, W = 6, 4 * 3000, 512, 4, 64, 256, 128
     wd = _attn_world(B, L, d, m, 128, seed=29, H=H, T=1)
