@@ -10,25 +10,23 @@
 // int32 accumulation on the int8 matrix cores (v_mfma_i32_16x16x64_i8).
 // Selection order: score descending, then lower block index; output ascending.
 //
-// Two execution plans, both exact (hence bit-identical results):
-//  * split scan (few queries per sequence, or a candidate pool): the entry
-//    range of every query is cut into 2048-entry tiles, one workgroup each.
-//    k_idx_scan streams the int8 keys once (HBM-bound: every load is issued
-//    unconditionally so a wave keeps 8 KB in flight), writes each score to a
-//    slab and adds a 512-bin monotone histogram of the scores into a
-//    per-query global histogram. k_idx_select (same grid) reads the finished
+// Plan: the entry range of every query is cut into 2048-entry tiles.
+//  * phase 1 scores every tile. Few queries per sequence, or a candidate
+//    pool: k_idx_scan, one workgroup per (query, tile, or part of a tile),
+//    streams the int8 keys once (HBM-bound: every load is issued
+//    unconditionally and double-buffered). Runs of >= 16 queries per sequence
+//    (prefill chunks): k_idx_bscan, one workgroup per (group of 8-32
+//    consecutive queries, tile), so each key loaded feeds the whole group.
+//    Both write each score to a slab and add a 512-bin monotone histogram of
+//    the scores into a per-query global histogram.
+//  * k_idx_select (one workgroup per query and tile) reads the finished
 //    histogram, derives the threshold bin and keeps the tile's entries at or
-//    above it, in index order. k_idx_final (one workgroup per query) gathers
-//    those few thousand candidates into LDS, narrows the threshold to the
-//    exact k-th score by radix refinement and writes the ascending list.
-//    Kernel boundaries, not fences, order the hand-offs: an agent-scope fence
-//    inside a workgroup writes back and invalidates the XCD's whole L2.
-//  * multi-pass (long query runs sharing a sequence's keys, i.e. prefill
-//    chunks): one workgroup per group of consecutive queries streams the
-//    L2-resident keys once per pass, recomputing the scores on the matrix
-//    cores: pass 1 builds per-query histograms, refinement passes narrow the
-//    threshold to one exact score, and the final pass emits the selected
-//    blocks in ascending order directly.
+//    above it, in index order.
+//  * k_idx_final (one workgroup per query) gathers those candidates into LDS,
+//    narrows the threshold to the exact k-th score by radix refinement and
+//    writes the ascending list.
+// Kernel boundaries, not fences, order the hand-offs: an agent-scope fence
+// inside a workgroup writes back and invalidates the XCD's whole L2.
 #include "csa_internal.h"
 
 #include <mutex>
@@ -216,6 +214,134 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   uint32_t* hq = hist + (int64_t)qi * NB1;
   for (int i = threadIdx.x; i < NB1; i += 256)
     if (lh[i]) atomicAdd(&hq[i], lh[i]);
+}
+
+// ------------------------------------------------------------------------
+// split scan, phase 1 for runs of consecutive queries (prefill chunks): one
+// workgroup = QG queries of one sequence x one 2048-entry tile, so every key
+// loaded feeds QG queries. Rows of an MFMA tile are (query, head) pairs:
+// QPT = 16 / HP queries per row tile, RT row tiles per wave, all waves share
+// the queries and split the tile's entries. Scores go straight to the slab
+// (entries a query cannot see yet get -1), the per-query histograms to LDS
+// and then to the global histogram.
+// ------------------------------------------------------------------------
+template <int DI, int HP>
+__global__ __launch_bounds__(256) void k_idx_bscan(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
+    const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
+    int64_t npad, int n_groups, int32_t* __restrict__ slab, uint32_t* __restrict__ hist) {
+  constexpr int KS = (DI + 63) / 64;
+  constexpr int QPT = 16 / HP;
+  constexpr int RT = 8 / KS;
+  constexpr int QG = RT * QPT;
+  constexpr int GPQ = HP / 4;  // lane groups per query in the score layout
+  constexpr int BATCH = 4;     // column tiles per load round
+  __shared__ uint32_t lh[QG][NB1];
+  const int tile = blockIdx.x;
+  const int b = blockIdx.y / n_groups;
+  const int t0 = (blockIdx.y - b * n_groups) * QG;  // first query (index within T)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+
+  for (int i = threadIdx.x; i < QG * NB1; i += 256) (&lh[0][0])[i] = 0;
+
+  v4i A[RT][KS];
+  int wr[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int ti = t0 + rt * QPT + i16 / HP;
+    const int h = i16 % HP;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = ks * 64 + 16 * g;
+      if (ti < T && h < Hi && c0 < DI)
+        A[rt][ks] = *reinterpret_cast<const v4i*>(
+            q_idx + (((int64_t)b * T + ti) * Hi + h) * DI + c0);
+      else
+        A[rt][ks] = v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      const int tq = t0 + rt * QPT + row / HP;
+      const int hh = row % HP;
+      wr[rt][r] = (tq < T && hh < Hi) ? (int)w[((int64_t)b * T + tq) * Hi + hh] : 0;
+    }
+  }
+  // the score lanes: lane group g holds query g / GPQ of each row tile; the
+  // first lane group of each query owns its scores
+  const bool owner = (g % GPQ) == 0;
+  int64_t my_nv[RT];
+  int32_t* my_row[RT];
+  bool my_real[RT];  // padding queries of the last group store nothing
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int ti = t0 + rt * QPT + g / GPQ;
+    int64_t nv = (pos0 + ti + 1) / m;
+    nv = nv < blk_cap ? nv : blk_cap;
+    my_real[rt] = ti < T;
+    my_nv[rt] = ti < T ? nv : 0;
+    my_row[rt] = slab + ((int64_t)b * T + (ti < T ? ti : T - 1)) * npad;
+  }
+  const int t_last = (t0 + QG < T ? t0 + QG : T) - 1;
+  int64_t n_end = (pos0 + t_last + 1) / m;  // entries any query of the group can see
+  n_end = n_end < blk_cap ? n_end : blk_cap;
+  __syncthreads();
+
+  const int64_t e_wave = (int64_t)tile * TILE + wave * (TILE / 4);
+  const int8_t* kb = keys + (int64_t)b * blk_cap * DI;
+  int coff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) coff[ks] = (ks * 64 + 16 * g) % DI;
+  if (n_end > 0 && e_wave < n_end) {
+    constexpr int NBT = TILE / 4 / 16 / BATCH;
+    v4i Bk[2][BATCH][KS];
+    auto issue = [&](int buf, int bt) {
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        int64_t e = e_wave + (int64_t)(bt * BATCH + u) * 16 + i16;
+        e = e < n_end ? e : n_end - 1;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          Bk[buf][u][ks] = *reinterpret_cast<const v4i*>(kb + e * DI + coff[ks]);
+      }
+    };
+    auto consume = [&](int buf, int bt) {
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t e = e_wave + (int64_t)(bt * BATCH + u) * 16 + i16;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          v4i acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[rt][ks], Bk[buf][u][ks], acc, 0, 0, 0);
+          int p = wr[rt][0] * max(acc[0], 0) + wr[rt][1] * max(acc[1], 0) +
+                  wr[rt][2] * max(acc[2], 0) + wr[rt][3] * max(acc[3], 0);
+          if (GPQ >= 2) p += __shfl_xor(p, 16, 64);
+          if (GPQ >= 4) p += __shfl_xor(p, 32, 64);
+          if (owner && my_real[rt] && e < npad) {
+            const int sc = e < my_nv[rt] ? p : -1;
+            my_row[rt][e] = sc;
+            if (sc >= 0) atomicAdd(&lh[rt * QPT + g / GPQ][score_bin512(sc)], 1u);
+          }
+        }
+      }
+    };
+    issue(0, 0);
+#pragma unroll
+    for (int bt = 0; bt < NBT; ++bt) {
+      if (bt + 1 < NBT) issue((bt + 1) & 1, bt + 1);
+      consume(bt & 1, bt);
+    }
+  }
+  // (slab entries past a query's visible range are never read)
+  __syncthreads();
+  for (int i = threadIdx.x; i < QG * NB1; i += 256) {
+    const int ql = i / NB1;
+    const uint32_t c = (&lh[0][0])[i];
+    if (c && t0 + ql < T) atomicAdd(&hist[((int64_t)b * T + t0 + ql) * NB1 + (i % NB1)], c);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -611,239 +737,6 @@ __global__ __launch_bounds__(256) void k_idx_final(
 }
 
 // ------------------------------------------------------------------------
-// multi-pass plan for long query runs (prefill chunks)
-// ------------------------------------------------------------------------
-// HP = padded head count (4, 8 or 16); rows of an MFMA tile are
-// (query, head) pairs, QPT = 16 / HP queries per row tile; RT row tiles per
-// wave; QG queries per workgroup.
-template <int DI, int HP, int RT>
-__global__ __launch_bounds__(256) void k_idx_prefill(
-    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
-    const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0, int k,
-    int32_t* __restrict__ out_idx, int32_t* __restrict__ out_score) {
-  constexpr int KS = (DI + 63) / 64;
-  constexpr int QPT = 16 / HP;
-  constexpr int QW = QPT * RT;
-  constexpr int QG = 4 * QW;
-  constexpr int NB = 256;
-  constexpr int GPQ = HP / 4;  // lane groups per query in the score layout
-  __shared__ uint32_t hist[QG][NB];
-  __shared__ int st_keff[QG], st_T1[QG], st_need[QG], st_lo[QG], st_R[QG];
-  __shared__ int s_any;
-
-  const int b = blockIdx.y;
-  const int q0 = blockIdx.x * QG;  // first query (index within T) of the workgroup
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, g = lane >> 4;
-
-  // A operands and weights for the RT row tiles of this wave
-  v4i A[RT][KS];
-  int wr[RT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int ql = wave * QW + rt * QPT + i16 / HP;
-    const int h = i16 % HP;
-    const int ti = q0 + ql;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c0 = ks * 64 + 16 * g;
-      if (ti < T && h < Hi && c0 < DI)
-        A[rt][ks] = *reinterpret_cast<const v4i*>(
-            q_idx + (((int64_t)b * T + ti) * Hi + h) * DI + c0);
-      else
-        A[rt][ks] = v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * g + r;
-      const int qq = q0 + wave * QW + rt * QPT + row / HP;
-      const int hh = row % HP;
-      wr[rt][r] = (qq < T && hh < Hi) ? (int)w[((int64_t)b * T + qq) * Hi + hh] : 0;
-    }
-  }
-  // the score lanes: lane group g holds query (g / GPQ) of each row tile;
-  // the first lane group of each query "owns" it
-  const bool owner = (g % GPQ) == 0;
-  int my_ti[RT];
-  int64_t my_nv[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    my_ti[rt] = q0 + wave * QW + rt * QPT + g / GPQ;
-    int64_t nv = (pos0 + my_ti[rt] + 1) / m;
-    nv = nv < blk_cap ? nv : blk_cap;
-    my_nv[rt] = my_ti[rt] < T ? nv : 0;
-  }
-  const int t_last = (q0 + QG < T ? q0 + QG : T) - 1;
-  int64_t n_end = (pos0 + t_last + 1) / m;
-  n_end = n_end < blk_cap ? n_end : blk_cap;
-  const int8_t* kb = keys + (int64_t)b * blk_cap * DI;
-
-  // Streams every key tile once and hands the scores to `f(rt, entry, s)`
-  // on owner lanes for visible entries.
-  auto sweep = [&](auto&& f) {
-#pragma unroll 1
-    for (int64_t e0 = 0; e0 < n_end; e0 += 64) {
-      v4i Bk[4][KS];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int64_t e = e0 + u * 16 + i16;
-        e = e < n_end ? e : n_end - 1;  // clamped; entries past n_end are masked
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          Bk[u][ks] = *reinterpret_cast<const v4i*>(kb + e * DI + (ks * 64 + 16 * g) % DI);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t e = e0 + u * 16 + i16;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          v4i acc = {0, 0, 0, 0};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[rt][ks], Bk[u][ks], acc, 0, 0, 0);
-          int p = wr[rt][0] * max(acc[0], 0) + wr[rt][1] * max(acc[1], 0) +
-                  wr[rt][2] * max(acc[2], 0) + wr[rt][3] * max(acc[3], 0);
-          if (GPQ >= 2) p += __shfl_xor(p, 16, 64);
-          if (GPQ >= 4) p += __shfl_xor(p, 32, 64);
-          f(rt, e, p, owner && e < my_nv[rt]);
-        }
-      }
-    }
-  };
-
-  for (int i = threadIdx.x; i < QG * NB; i += 256) (&hist[0][0])[i] = 0;
-  __syncthreads();
-  // pass 1: level-1 histogram (8 bins per octave)
-  sweep([&](int rt, int64_t e, int s, bool ok) {
-    if (ok) atomicAdd(&hist[wave * QW + rt * QPT + g / GPQ][score_bin256(s)], 1u);
-  });
-  __syncthreads();
-  // threshold bin per query (one thread per query scans from the top)
-  if (threadIdx.x < QG) {
-    const int ql = threadIdx.x;
-    const int ti = q0 + ql;
-    int64_t nv = (pos0 + ti + 1) / m;
-    nv = nv < blk_cap ? nv : blk_cap;
-    const int nvalid = ti < T ? (int)nv : 0;
-    const int keff = k < nvalid ? k : nvalid;
-    int acc = 0, T1 = 0, A1 = 0;
-    if (keff > 0) {
-      for (int bin = NB - 1; bin >= 0; --bin) {
-        const int c = (int)hist[ql][bin];
-        if (acc + c >= keff) {
-          T1 = bin;
-          A1 = acc;
-          break;
-        }
-        acc += c;
-      }
-    }
-    st_keff[ql] = keff;
-    st_T1[ql] = T1;
-    st_need[ql] = keff - A1;
-    // integer range of scores mapped to bin T1 (a little wider than exact
-    // above 2^24, where int->float rounds; the bin test keeps it exact)
-    int lo = 0, R = 0;
-    if (T1 > 0) {
-      const uint32_t fb = (uint32_t)(T1 + 1015) << 20;
-      const double flo = (double)__uint_as_float(fb);
-      const double fhi = (double)__uint_as_float(fb + (1u << 20));
-      const double ulp = flo >= 16777216.0 ? flo / 8388608.0 : 0.0;
-      double dlo = flo - ulp, dhi = fhi + ulp;
-      if (dlo < 0) dlo = 0;
-      if (dhi > 2147483647.0) dhi = 2147483647.0;
-      lo = (int)dlo;
-      R = (int)dhi - lo;
-    }
-    st_lo[ql] = lo;
-    st_R[ql] = (keff > 0) ? R : 0;
-  }
-  __syncthreads();
-
-  // refinement passes until every query has one exact threshold score
-  while (true) {
-    if (threadIdx.x == 0) s_any = 0;
-    __syncthreads();
-    if (threadIdx.x < QG && st_R[threadIdx.x] > 0) s_any = 1;
-    for (int i = threadIdx.x; i < QG * NB; i += 256) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    if (!s_any) break;
-    sweep([&](int rt, int64_t e, int s, bool ok) {
-      const int ql = wave * QW + rt * QPT + g / GPQ;
-      const int R = st_R[ql];
-      if (ok && R > 0 && score_bin256(s) == st_T1[ql]) {
-        const int lo = st_lo[ql];
-        const int bits = 32 - __clz(R);
-        const int shift = bits > 8 ? bits - 8 : 0;
-        if (s >= lo && s - lo <= R) atomicAdd(&hist[ql][(s - lo) >> shift], 1u);
-      }
-    });
-    __syncthreads();
-    if (threadIdx.x < QG) {
-      const int ql = threadIdx.x;
-      const int R = st_R[ql];
-      if (R > 0) {
-        const int bits = 32 - __clz(R);
-        const int shift = bits > 8 ? bits - 8 : 0;
-        int need = st_need[ql], acc = 0, beta = 0;
-        for (int bk = NB - 1; bk >= 0; --bk) {
-          const int c = (int)hist[ql][bk];
-          if (acc + c >= need) {
-            beta = bk;
-            break;
-          }
-          acc += c;
-        }
-        st_need[ql] = need - acc;
-        st_lo[ql] += beta << shift;
-        st_R[ql] = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
-      }
-    }
-    __syncthreads();
-  }
-
-  // emission pass: wave-local, in ascending entry order per query
-  int tau[RT], take_eq[RT], eq_run[RT], out_run[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int ql = wave * QW + rt * QPT + g / GPQ;
-    tau[rt] = st_keff[ql] > 0 ? st_lo[ql] : 0x7fffffff;
-    take_eq[rt] = st_need[ql];
-    eq_run[rt] = 0;
-    out_run[rt] = 0;
-  }
-  const uint64_t below16 = (i16 == 0) ? 0ull : (~0ull >> (64 - i16));
-  sweep([&](int rt, int64_t e, int s, bool ok) {
-    const bool is_eq = ok && s == tau[rt];
-    const uint64_t meq = (__ballot(is_eq) >> (16 * g)) & 0xffffull;
-    const int eq_rank = eq_run[rt] + __popcll(meq & below16);
-    const bool take = ok && (s > tau[rt] || (is_eq && eq_rank < take_eq[rt]));
-    const uint64_t mt = (__ballot(take) >> (16 * g)) & 0xffffull;
-    if (take) {
-      const int64_t row = (int64_t)b * T + my_ti[rt];
-      const int pos = out_run[rt] + __popcll(mt & below16);
-      if (pos < k) {
-        out_idx[row * k + pos] = (int32_t)e;
-        if (out_score) out_score[row * k + pos] = s;
-      }
-    }
-    eq_run[rt] += __popcll(meq);
-    out_run[rt] += __popcll(mt);
-  });
-  // -1 padding after the k_eff selected entries
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    if (owner && my_ti[rt] < T) {
-      const int64_t row = (int64_t)b * T + my_ti[rt];
-      for (int i = out_run[rt] + i16; i < k; i += 16) {
-        out_idx[row * k + i] = -1;
-        if (out_score) out_score[row * k + i] = -1;
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------
 struct IdxLayout {
@@ -894,8 +787,11 @@ static bool final_lds_allow(size_t lds) {
   return true;
 }
 
-static bool split_plan(int T, const int32_t* cand, int cand_given) {
-  return cand != nullptr || cand_given || T < PREFILL_MIN_T;
+// Runs of at least PREFILL_MIN_T queries per sequence (prefill chunks) are
+// scored by the batched scan; fewer queries, or a candidate pool, by the
+// one-query scan. Both feed the same select and final passes.
+static bool batched_plan(int T, const int32_t* cand) {
+  return cand == nullptr && T >= PREFILL_MIN_T;
 }
 
 struct IdxArgs {
@@ -911,7 +807,7 @@ static int idx_check(const IdxArgs& a, int64_t* n_max) {
   if (a.Hi * a.Di > 1024) return CSA_ERR_SHAPE;
   if (a.m < 1 || a.k < 1) return CSA_ERR_SHAPE;
   if (a.cand && a.C < 0) return CSA_ERR_SHAPE;
-  if ((int64_t)a.B * a.T > 65535 * 32768LL) return CSA_ERR_SHAPE;
+  if ((int64_t)a.B * a.T > 65535) return CSA_ERR_SHAPE;  // queries per call (grid y)
   if (a.pos0 + a.T > (int64_t)1 << 40) return CSA_ERR_RANGE;
   if (a.B == 0 || a.T == 0) return CSA_OK;
   if (!a.q_idx || !a.w || !a.keys || !a.out_idx) return CSA_ERR_NULL;
@@ -929,7 +825,7 @@ static int idx_phase(const IdxArgs& a, int phase) {
   int st = idx_check(a, &n_max);
   if (st != CSA_OK || a.B == 0 || a.T == 0) return st;
   const int BT = a.B * a.T;
-  if (split_plan(a.T, a.cand, 0)) {
+  {
     IdxLayout L = idx_layout(BT, n_max);
     if (!a.ws) return CSA_ERR_WORKSPACE;
     if (a.ws_bytes < L.bytes) return CSA_ERR_WORKSPACE;
@@ -941,7 +837,23 @@ static int idx_phase(const IdxArgs& a, int phase) {
     int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.off_cnt);
     const int C = a.cand ? a.C : 0;
     dim3 grid(L.n_tiles, BT);
-    if (phase == 0) {
+    if (phase == 0 && batched_plan(a.T, a.cand)) {
+      const int HP = a.Hi <= 4 ? 4 : (a.Hi <= 8 ? 8 : 16);
+      const int KS = (a.Di + 63) / 64;
+      const int QG = (8 / KS) * (16 / HP);
+      const int n_groups = (a.T + QG - 1) / QG;
+      const dim3 bgrid(L.n_tiles, a.B * n_groups);
+#define CSA_LAUNCH_BSCAN(DD, HH)                                                           \
+  hipLaunchKernelGGL((k_idx_bscan<DD, HH>), bgrid, dim3(256), 0, a.stream, a.q_idx, a.w,  \
+                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, L.npad, n_groups, slab, hist)
+#define CSA_LAUNCH_BSCAN_H(DD) \
+  if (HP == 4) CSA_LAUNCH_BSCAN(DD, 4); else if (HP == 8) CSA_LAUNCH_BSCAN(DD, 8); else CSA_LAUNCH_BSCAN(DD, 16)
+      if (a.Di == 32) { CSA_LAUNCH_BSCAN_H(32); }
+      else if (a.Di == 64) { CSA_LAUNCH_BSCAN_H(64); }
+      else { CSA_LAUNCH_BSCAN_H(128); }
+#undef CSA_LAUNCH_BSCAN_H
+#undef CSA_LAUNCH_BSCAN
+    } else if (phase == 0) {
       // small scans split each tile over 2 or 4 workgroups so that about 512
       // workgroups stream the keys
       const int64_t nwg = (int64_t)L.n_tiles * BT;
@@ -988,23 +900,6 @@ static int idx_phase(const IdxArgs& a, int phase) {
     CSA_TRY_LAUNCH();
     return CSA_OK;
   }
-  if (phase != 0) return CSA_OK;
-  const int HP = a.Hi <= 4 ? 4 : (a.Hi <= 8 ? 8 : 16);
-  constexpr int RT = 2;
-  const int QG = 4 * RT * (16 / HP);
-  dim3 grid((a.T + QG - 1) / QG, a.B);
-#define CSA_LAUNCH_PRE(DD, HH)                                                              \
-  hipLaunchKernelGGL((k_idx_prefill<DD, HH, RT>), grid, dim3(256), 0, a.stream, a.q_idx, a.w, \
-                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.k, a.out_idx, a.out_score)
-#define CSA_LAUNCH_PRE_H(DD) \
-  if (HP == 4) CSA_LAUNCH_PRE(DD, 4); else if (HP == 8) CSA_LAUNCH_PRE(DD, 8); else CSA_LAUNCH_PRE(DD, 16)
-  if (a.Di == 32) { CSA_LAUNCH_PRE_H(32); }
-  else if (a.Di == 64) { CSA_LAUNCH_PRE_H(64); }
-  else { CSA_LAUNCH_PRE_H(128); }
-#undef CSA_LAUNCH_PRE_H
-#undef CSA_LAUNCH_PRE
-  CSA_TRY_LAUNCH();
-  return CSA_OK;
 }
 
 __global__ void k_fill_zero(uint32_t* p, int64_t n) {
@@ -1017,8 +912,8 @@ __global__ void k_fill_zero(uint32_t* p, int64_t n) {
 
 extern "C" int64_t csa_index_topk_workspace(int B, int T, int64_t n_max, int k, int cand_given) {
   (void)k;
+  (void)cand_given;
   if (B < 0 || T < 0 || n_max < 0) return -1;
-  if (!split_plan(T, nullptr, cand_given)) return 0;
   return idx_layout((int64_t)B * T, n_max).bytes;
 }
 

@@ -123,7 +123,8 @@ int csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t blk_cap,
  *   out_score int32 [B][T][k] or NULL: their scores (-1 in padding)
  * Score: s(b) = sum_h w[h] * max(0, sum_c q_idx[h][c] * keys[b][c]), exact in
  * int32 (Hi * Di <= 1024 keeps it below 2^31). Order: score descending, then
- * lower block index. Supports 1 <= Hi <= 16, Di in {32, 64, 128}, k >= 1.
+ * lower block index. Supports 1 <= Hi <= 16, Di in {32, 64, 128}, k >= 1,
+ * B*T <= 65535 queries per call.
  * Workspace: csa_index_topk_workspace(...) bytes of device memory. Its head
  * holds per-query counters and histograms whose layout depends on B*T only:
  * zero-fill the workspace (csa_workspace_clear) after allocating it, again
@@ -131,7 +132,9 @@ int csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t blk_cap,
  * that head zero again, so a decode loop with a fixed B*T reuses one
  * workspace without clearing, whatever n_max does. n_max is the largest
  * number of candidates a query can have: C when a pool is given, else
- * min(blk_cap, (pos0+T)/m).
+ * min(blk_cap, (pos0+T)/m). The size is about B*T*n_max*12 bytes (a score
+ * and a candidate slot per entry), e.g. 3 GiB for an 8192-query chunk at
+ * 32,768 visible blocks.
  * ------------------------------------------------------------------------- */
 int64_t csa_index_topk_workspace(int B, int T, int64_t n_max, int k, int cand_given);
 
@@ -143,11 +146,10 @@ int csa_index_topk(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
 
 /* The two launches csa_index_topk makes, exposed so a caller can place events
  * or other work between them: csa_index_topk == csa_index_scan followed by
- * csa_index_select with identical arguments. For few queries per sequence
- * (T < 16) or a candidate pool, scan streams the keys and writes exact scores
- * plus a per-query score histogram into the workspace, and select turns them
- * into the sorted index list. For longer query runs scan does the whole job
- * and select enqueues nothing. */
+ * csa_index_select with identical arguments. Scan computes every exact score
+ * into the workspace (one key stream per query for T < 16 or a pool; for
+ * runs of T >= 16 queries one key stream per group of 8-32 queries) plus a
+ * per-query score histogram; select turns them into the sorted index list. */
 int csa_index_scan(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
                    int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
                    const int32_t* cand, int C, int k,

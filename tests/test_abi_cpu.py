@@ -83,9 +83,9 @@ def test_argument_errors_before_launch(L):
 
 
 def test_workspace_sizes(L):
-    # decode: split scan needs a workspace, long query runs need none
+    # every plan keeps a score and a candidate slot per visible entry
     assert L.csa_index_topk_workspace(8, 1, 262144, 1024, 0) > 8 * 262144 * 12
-    assert L.csa_index_topk_workspace(1, 8192, 32768, 512, 0) == 0
+    assert L.csa_index_topk_workspace(1, 8192, 32768, 512, 0) > 8192 * 32768 * 12
     assert L.csa_index_topk_workspace(16, 1, 4096, 512, 1) > 0
     assert L.csa_attn_workspace(1, 8192, 64, 512, 640) == 0
     assert L.csa_attn_workspace(8, 1, 64, 512, 1152) >= 8 * 9 * 64 * 512 * 4
