@@ -379,19 +379,25 @@ constexpr int MERGE_MAX = 256;  // splits per query handled by the merge
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
-                                                    int nsplit, int H, int NW,
+                                                    int nsplit, int H, int NW, int n_queries,
                                                     void* __restrict__ out, int out_dtype,
                                                     float* __restrict__ lse) {
   constexpr int CT = D / 16;
   __shared__ float s_m[16][MERGE_MAX], s_f[16][MERGE_MAX];
   __shared__ float s_inv[16];
   // workgroup -> (query, 16-head block, group of 4 column tiles); thread ->
-  // one (ct, lane) pair
+  // one (ct, lane) pair. Workgroups are dealt to the XCDs round-robin; every
+  // workgroup of query qi goes to XCD qi % 8, where the attention kernel
+  // wrote that query's partials, so they are read from that XCD's L2.
   constexpr int CG = CT / 4;
-  const int cg = blockIdx.x % CG;
-  const int64_t qw = blockIdx.x / CG;
-  const int64_t qi = qw / NW;
-  const int w = (int)(qw - qi * NW);
+  const int per_q = NW * CG;
+  const int xcd = blockIdx.x & 7;
+  const int jx = blockIdx.x >> 3;
+  const int64_t qi = xcd + 8 * (int64_t)(jx / per_q);
+  if (qi >= n_queries) return;
+  const int r = jx % per_q;
+  const int cg = r % CG;
+  const int w = r / CG;
   const int pr = cg * 256 + threadIdx.x;
   const int ct = pr >> 6, ln = pr & 63;
   const int j = ln & 15, g = ln >> 4;
@@ -544,8 +550,9 @@ static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, flo
   }
 #undef CSA_LAUNCH_ATTN
   if (p.nsplit > 1)
-    hipLaunchKernelGGL(k_attn_merge<D>, dim3((unsigned)(nq * nw * (D / 64))), dim3(256), 0, a.stream,
-                       part_o, part_ml, p.nsplit, a.H, nw, a.out, a.out_dtype, a.lse);
+    hipLaunchKernelGGL(k_attn_merge<D>, dim3((unsigned)(((nq + 7) / 8) * 8 * nw * (D / 64))),
+                       dim3(256), 0, a.stream, part_o, part_ml, p.nsplit, a.H, nw, (int)nq, a.out,
+                       a.out_dtype, a.lse);
 }
 
 static int attn_run(const AttnArgs& a, bool dense) {
