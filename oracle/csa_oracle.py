@@ -276,6 +276,38 @@ def index_topk(q_idx, w, keys, m: int, t: int, k: int, cand=None):
     return select_topk(blocks, s, k)
 
 
+def block_pool(q_idx, w, keys, m: int, t: int, group: int, n_keep: int):
+    """Blockwise candidate pool of a Full-mode layer ([PODCAST] cue 14: take
+    the highest score of each block of positions, keep the best blocks and
+    pool their positions for the Reindex layers).
+
+    The causally visible entries 0 .. nv-1 are cut into groups of `group`
+    consecutive entries (the last one may be partial); a group's score is the
+    largest score of its visible entries (reading A22). The n_keep best groups
+    under (score descending, group index ascending) are kept (reading A23).
+    Returns int32 [group * n_keep]: kept group i (ascending group order)
+    fills slots i*group .. i*group + group - 1 with its entries, -1 where an
+    entry is not visible yet; slots of unused groups are -1.
+    """
+    nv = min(n_visible(t, m), len(keys))
+    pool = np.full(group * n_keep, -1, dtype=np.int32)
+    if nv == 0:
+        return pool
+    s = index_scores(q_idx, w, np.asarray(keys)[:nv])
+    ng = -(-nv // group)
+    padded = np.full(ng * group, -1, dtype=np.int64)   # scores are >= 0
+    padded[:nv] = s
+    gscore = padded.reshape(ng, group).max(axis=1)
+    kept, _ = select_topk(np.arange(ng), gscore, n_keep)
+    for i, gi in enumerate(kept):
+        if gi < 0:
+            break
+        for r in range(group):
+            e = int(gi) * group + r
+            pool[i * group + r] = e if e < nv else -1
+    return pool
+
+
 # --------------------------------------------------------------------------
 # a5 + a6 + a7: attention
 # --------------------------------------------------------------------------
@@ -349,4 +381,6 @@ READINGS = {
     "A12": "window = positions max(0, t-W+1)..t, no de-duplication against entries, one softmax",
     "A15": "K = V = the latent row",
     "A17": "window rows are bf16",
+    "A22": "blockwise pool: groups of `group` consecutive compressed entries (8 per [PODCAST] cue 14); group score = max over its visible entries",
+    "A23": "blockwise pool keeps n_keep groups (about 2000 per cue 14), ties to the lower group; the pool lists their visible entries ascending, -1 elsewhere",
 }

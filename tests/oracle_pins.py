@@ -66,6 +66,18 @@ def load_indexer_golden():
             np.array(scores), selects)
 
 
+def load_pool_golden():
+    pools = []
+    with open(os.path.join(GOLDEN, "indexer_small.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line.startswith("pool"):
+                lhs, rhs = line[4:].split(":")
+                m, t, G, n = (int(v) for v in lhs.split())
+                pools.append((m, t, G, n, [int(v) for v in rhs.split()]))
+    return pools
+
+
 # ---------------------------------------------------------------- MXFP4 ----
 
 def pin_golden_groups(O):
@@ -302,6 +314,67 @@ def pin_reindex_consistency(O):
     cand = np.array([5, -1, 2999, 7, 1000], np.int64)
     idx, _ = O.index_topk(q, w, keys, 4, 4 * 1000 - 1, 10, cand=cand)   # 2999 not visible
     assert set(idx[idx >= 0]) == {5, 7} and sorted(idx[idx >= 0]) == list(idx[:2])
+
+
+def pin_block_pool_golden(O):
+    q, w, keys, _, _ = load_indexer_golden()
+    for m, t, G, n, want in load_pool_golden():
+        got = O.block_pool(q, w, keys, m, t, G, n)
+        assert list(got) == want, (m, t, G, n, list(got), want)
+
+
+def pin_block_pool_brute_force(O):
+    """Pure-Python grouping and ordering on tiny random inputs (many ties),
+    and two special cases: groups of one entry give the plain top-k; keeping
+    every group pools every visible entry."""
+    rng = np.random.default_rng(10)
+    q = rng.integers(-8, 8, (3, 6)).astype(np.int8)
+    w = rng.integers(0, 4, 3).astype(np.int8)
+    keys = rng.integers(-2, 3, (90, 6)).astype(np.int8)
+    for m, t, G, n in ((1, 89, 8, 4), (4, 200, 8, 3), (1, 60, 5, 7), (2, 150, 4, 30), (1, 2, 8, 2)):
+        nv = min((t + 1) // m, len(keys))
+        sc = []
+        for b in range(nv):
+            tot = 0
+            for h in range(3):
+                dot = sum(int(q[h, c]) * int(keys[b, c]) for c in range(6))
+                tot += int(w[h]) * max(0, dot)
+            sc.append(tot)
+        groups = {}
+        for b in range(nv):
+            groups.setdefault(b // G, []).append(b)
+        ranked = sorted(groups, key=lambda gi: (-max(sc[b] for b in groups[gi]), gi))[:n]
+        want = []
+        for gi in sorted(ranked):
+            want += [gi * G + r if gi * G + r < nv else -1 for r in range(G)]
+        want += [-1] * (G * n - len(want))
+        assert list(O.block_pool(q, w, keys, m, t, G, n)) == want, (m, t, G, n)
+    t = 4 * 90 - 1
+    top, _ = O.index_topk(q, w, keys, 4, t, 17)
+    assert np.array_equal(O.block_pool(q, w, keys, 4, t, 1, 17), top)
+    every = O.block_pool(q, w, keys, 4, t, 8, 12)
+    assert sorted(e for e in every if e >= 0) == list(range(90))
+
+
+def pin_block_pool_contains_topk(O):
+    """Every group holding an entry scored at least s_k (the k-th best score)
+    has a maximum >= s_k, and every other group a maximum < s_k; when there
+    are at most n such groups, a pool of n groups therefore holds every entry
+    scored >= s_k, so a Reindex top-k over it equals the Full top-k."""
+    rng = np.random.default_rng(11)
+    q = rng.integers(-8, 8, (4, 32)).astype(np.int8)
+    w = np.array([1, 2, 3, 1], np.int8)
+    keys = rng.integers(-8, 8, (4000, 32)).astype(np.int8)
+    t, k, G, n = 4 * 4000 - 1, 64, 8, 64
+    s = O.index_scores(q, w, keys)
+    s_k = np.sort(s)[::-1][k - 1]
+    hot = np.flatnonzero(s >= s_k)
+    assert len(set(hot // G)) <= n
+    full, _ = O.index_topk(q, w, keys, 4, t, k)
+    pool = O.block_pool(q, w, keys, 4, t, G, n)
+    assert set(hot) <= set(pool) and set(full) <= set(pool)
+    re, _ = O.index_topk(q, w, keys, 4, t, k, cand=pool)
+    assert np.array_equal(re, full)
 
 
 # ------------------------------------------------------------ attention ----

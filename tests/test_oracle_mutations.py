@@ -146,6 +146,31 @@ def m_gather_no_window(codes, scales, blocks, win, Wcap, t, W):
     return rows[:-nwin] if rows.shape[0] > nwin else rows
 
 
+def _pool_variant(q, w, keys, m, t, group, n_keep, reduce="max", tie_low=True, visible=True,
+                  shift=0):
+    """block_pool with one planted deviation (group score reduction, tie
+    order, visibility, or groups shifted by `shift` entries)."""
+    nv = min(O.n_visible(t, m), len(keys)) if visible else len(keys)
+    pool = np.full(group * n_keep, -1, np.int32)
+    if nv == 0:
+        return pool
+    s = O.index_scores(q, w, np.asarray(keys)[:nv])
+    first = [0] + list(range(shift, nv, group)) if shift else list(range(0, nv, group))
+    first = sorted(set(first))
+    bounds = first + [nv]
+    gs = []
+    for a, z in zip(bounds[:-1], bounds[1:]):
+        seg = s[a:z]
+        gs.append(seg.max() if reduce == "max" else (seg.min() if reduce == "min" else seg[0]))
+    order = sorted(range(len(gs)), key=lambda i: (-gs[i], i if tie_low else -i))[:n_keep]
+    slot = 0
+    for i in sorted(order):
+        for e in range(bounds[i], bounds[i] + group):
+            pool[slot] = e if e < bounds[i + 1] else -1
+            slot += 1
+    return pool
+
+
 MUTANTS = {
     "scale exponent off by one": {"scale_exponent": m_scale_off_by_one},
     "scale exponent not clamped": {"scale_exponent": m_no_clamp},
@@ -165,6 +190,11 @@ MUTANTS = {
     "softmax scale ignored": {"attend": m_attend_no_scale},
     "softmax over heads": {"attend": m_attend_softmax_heads},
     "window dropped": {"gather_rows": m_gather_no_window},
+    "pool group score is the minimum": {"block_pool": lambda *a: _pool_variant(*a, reduce="min")},
+    "pool group score is the first entry": {"block_pool": lambda *a: _pool_variant(*a, reduce="first")},
+    "pool ties to the higher group": {"block_pool": lambda *a: _pool_variant(*a, tie_low=False)},
+    "pool ignores visibility": {"block_pool": lambda *a: _pool_variant(*a, visible=False)},
+    "pool groups shifted": {"block_pool": lambda *a: _pool_variant(*a, shift=1)},
 }
 
 
