@@ -509,7 +509,7 @@ def run_prefill(args, csa, synth, wl, dev):
 LAYERS = ("full", "reindex1", "reindex2")
 
 
-def layers_set(csa, synth, wl, dev, seed):
+def layers_set(csa, synth, wl, dev, seed, pool_len):
     import torch
     t = wl.L - 1
     s = {}
@@ -520,7 +520,7 @@ def layers_set(csa, synth, wl, dev, seed):
     s["codes"], s["scales"] = build_cache(csa, synth, wl, dev, seed, "main", wl.m, wl.L)
     s["keys"] = synth.indexer_keys(wl, dev, seed)
     s["win"] = synth.window_ring(wl, t, dev, seed)
-    s["pool"] = torch.empty(wl.B, 1, wl.pool, device=dev, dtype=torch.int32)
+    s["pool"] = torch.empty(wl.B, 1, pool_len, device=dev, dtype=torch.int32)
     for layer in LAYERS:
         q_idx, w = synth.indexer_queries(wl, dev, seed, layer=layer)
         s[layer] = dict(q_idx=q_idx, w=w, q=synth.queries(wl, dev, seed, layer=layer),
@@ -531,9 +531,11 @@ def layers_set(csa, synth, wl, dev, seed):
     return s
 
 
-def cpu_baseline_layers(s, wl, n_queries):
+def cpu_baseline_layers(s, wl, n_queries, n_groups):
     """The oracle on the first n_queries sequences through all four layers,
-    one thread, checked against the device results."""
+    one thread, checked against the device results. n_groups > 0: the Full
+    layer keeps a blockwise pool of n_groups 8-entry groups and attends its
+    own top-k; else its pool is its top-`pool` entries, rescored to top-k."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -552,11 +554,15 @@ def cpu_baseline_layers(s, wl, n_queries):
                   for layer in LAYERS}
             t0 = time.perf_counter()
             ho, _ = O.hca_dense_attn(hq, hc, hs, wl.m_hca, h_win[b], wl.Wcap, wl.W, t, 1.0)
-            pool, _ = O.index_topk(qs["full"][0], qs["full"][1], keys[b], wl.m, t, wl.pool)
+            if n_groups:
+                pool = O.block_pool(qs["full"][0], qs["full"][1], keys[b], wl.m, t, 8, n_groups)
+            else:
+                pool, _ = O.index_topk(qs["full"][0], qs["full"][1], keys[b], wl.m, t, wl.pool)
             outs = {}
             for layer in LAYERS:
                 qi, wi, qb = qs[layer]
-                ri, _ = O.index_topk(qi, wi, keys[b], wl.m, t, wl.k, cand=pool)
+                cand = None if (n_groups and layer == "full") else pool
+                ri, _ = O.index_topk(qi, wi, keys[b], wl.m, t, wl.k, cand=cand)
                 ro, _ = O.sparse_attn(qb, cn, sn, ri, win[b], wl.Wcap, wl.W, t, 1.0)
                 outs[layer] = (ri, ro)
             t_total += time.perf_counter() - t0
@@ -566,11 +572,15 @@ def cpu_baseline_layers(s, wl, n_queries):
                 ri, ro = outs[layer]
                 ok &= bool(np.array_equal(ri, s[layer]["idx"][b, 0].cpu().numpy()))
                 worst = max(worst, bf16_excess(s[layer]["out"][b, 0].cpu().float().numpy(), ro))
+    pool_txt = (f"top-{wl.k} + blockwise pool of {n_groups} 8-entry groups over "
+                f"{wl.L // wl.m:,} blocks, two top-{wl.k} rescorings of the pool"
+                if n_groups else
+                f"top-{wl.pool} pool over {wl.L // wl.m:,} blocks, three top-{wl.k} "
+                "rescorings of the pool")
     return dict(value=n_queries / t_total, unit="queries/s", cores=1, kind="oracle",
                 sample=f"{n_queries} of the {wl.B} sequences through all four layers (HCA dense "
-                       f"over {wl.L // wl.m_hca:,} entries, top-{wl.pool} pool over "
-                       f"{wl.L // wl.m:,} blocks, three top-{wl.k} rescorings of the pool + "
-                       "attention), numpy fp64/int64, 1 thread",
+                       f"over {wl.L // wl.m_hca:,} entries, {pool_txt} + attention), numpy "
+                       "fp64/int64, 1 thread",
                 seconds=round(t_total, 3)), dict(topk_exact=ok, attn_excess_over_rms=worst)
 
 
@@ -579,7 +589,11 @@ def run_layers(args, csa, synth, wl, dev):
     t = wl.L - 1
     t_setup = time.time()
     n_sets = min(args.sets, 2)
-    sets = [layers_set(csa, synth, wl, dev, seed) for seed in range(n_sets)]
+    # blockwise pool: as many 8-entry groups as make the flat pool's length,
+    # unless --pool-groups says otherwise
+    n_groups = (args.pool_groups or wl.pool // 8) if args.pool_kind == "blocks" else 0
+    pool_len = 8 * n_groups if n_groups else wl.pool
+    sets = [layers_set(csa, synth, wl, dev, seed, pool_len) for seed in range(n_sets)]
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s: {n_sets} input sets of {wl.name}")
 
@@ -591,14 +605,21 @@ def run_layers(args, csa, synth, wl, dev):
     def pool(i, fn="index_topk"):
         s = sets[i]
         x = s["full"]
-        getattr(csa, fn)(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.pool, s["pool"],
-                         workspace=s["ws"])
+        if n_groups:  # the Full layer's own top-k and the group pool, one key scan
+            fn = {"index_topk": "index_topk_pool", "index_scan": "index_pool_scan",
+                  "index_select": "index_pool_select"}[fn]
+            getattr(csa, fn)(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.k, x["idx"], n_groups,
+                             s["pool"], workspace=s["ws"])
+        else:
+            getattr(csa, fn)(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.pool, s["pool"],
+                             workspace=s["ws"])
 
     def csa_layer(i, layer):
         s = sets[i]
         x = s[layer]
-        csa.index_topk(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.k, x["idx"], cand=s["pool"],
-                       workspace=s["ws"])
+        if not (n_groups and layer == "full"):
+            csa.index_topk(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.k, x["idx"],
+                           cand=s["pool"], workspace=s["ws"])
         csa.sparse_attn(x["q"], s["codes"], s["scales"], x["idx"], s["win"], wl.W, t, 1.0,
                         x["out"], workspace=s["ws_attn"])
 
@@ -637,25 +658,27 @@ def run_layers(args, csa, synth, wl, dev):
     # algorithmic bytes per query. HCA: entries + window + q/out. Full: keys,
     # indexer query, pool list (written, read back), top-k list, entries,
     # window, q/out. Reindex: pool keys + pool ids, indexer query, top-k list,
-    # entries, window, q/out.
+    # entries, window, q/out. (The block pool's Full layer reads no pool back;
+    # the flat-pool figure is kept for both as the bound is set by the keys.)
     eb = entry_bytes(wl)
     qo = 2 * wl.H * wl.d * 2
     win_b = wl.W * wl.d * 2
     qw = wl.Hi * wl.Di + wl.Hi
     hca_b = n_hca * eb + win_b + qo
-    full_b = nv * wl.Di + qw + 2 * 4 * wl.pool + 2 * 4 * wl.k + wl.k * eb + win_b + qo
-    re_b = wl.pool * (wl.Di + 4) + qw + 2 * 4 * wl.k + wl.k * eb + win_b + qo
+    full_b = nv * wl.Di + qw + 2 * 4 * pool_len + 2 * 4 * wl.k + wl.k * eb + win_b + qo
+    re_b = pool_len * (wl.Di + 4) + qw + 2 * 4 * wl.k + wl.k * eb + win_b + qo
     per_q = hca_b + full_b + 2 * re_b
     step_gbs = per_q * wl.B / (ms_per_step * 1e-3) / 1e9
     log(f"hca {t_hca * 1e3:.1f} us ({hca_tf:.0f} TFLOP/s); pool {t_pool * 1e3:.1f} us "
-        f"(scan {scan_ms * 1e3:.1f} us, {achieved:.0f} GB/s); full top-512+attn "
-        f"{t_full * 1e3:.1f} us; reindex {t_re * 1e3:.1f} us")
+        f"(scan {scan_ms * 1e3:.1f} us, {achieved:.0f} GB/s); full "
+        f"{'attn' if n_groups else 'top-512+attn'} {t_full * 1e3:.1f} us; reindex "
+        f"{t_re * 1e3:.1f} us")
 
     cpu = parity = None
     if not args.no_cpu_baseline:
         eager[0]()
         torch.cuda.synchronize()
-        cpu, parity = cpu_baseline_layers(sets[0], wl, min(args.cpu_queries, 2))
+        cpu, parity = cpu_baseline_layers(sets[0], wl, min(args.cpu_queries, 2), n_groups)
         log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
 
     return {
@@ -671,10 +694,12 @@ def run_layers(args, csa, synth, wl, dev):
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "context": wl.L, "d": wl.d, "m": wl.m,
                    "m_hca": wl.m_hca, "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8",
-                   "pool": wl.pool, "top_k": wl.k, "window": wl.W,
+                   "pool": pool_len, "pool_kind": args.pool_kind,
+                   **({"pool_groups": n_groups} if n_groups else {}),
+                   "top_k": wl.k, "window": wl.W,
                    "input_sets_rotated": n_sets, "timing": timing_name(args)},
         "layers_us": {"hca": round(t_hca * 1e3, 2), "full_pool_topk": round(t_pool * 1e3, 2),
-                      "full_topk_attn": round(t_full * 1e3, 2),
+                      ("full_attn" if n_groups else "full_topk_attn"): round(t_full * 1e3, 2),
                       "reindex_topk_attn": round(t_re * 1e3, 2)},
         "step_hbm": {"algorithmic_bytes_per_query": per_q, "GB/s": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
@@ -688,7 +713,8 @@ def run_layers(args, csa, synth, wl, dev):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("k_idx_scan", wl.name),
+            "traffic": measured_traffic("k_idx_scan",
+                                        wl.name + ("_blockpool" if n_groups else "")),
             "avg_launch_us": round(scan_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": scan_bytes,
         },
@@ -709,6 +735,11 @@ def main():
     ap.add_argument("--workload", default="decode_1m",
                     choices=["decode_1m", "decode_32k", "prefill_128k", "hca_reindex_1m"])
     ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--pool-kind", default="entries", choices=["entries", "blocks"],
+                    help="hca_reindex_1m: the Full layer's pool is its top-`pool` entries "
+                         "(entries) or a blockwise pool of 8-entry groups (blocks)")
+    ap.add_argument("--pool-groups", type=int, default=0,
+                    help="groups kept by the blockwise pool (default: pool / 8)")
     ap.add_argument("--cpu-queries", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",

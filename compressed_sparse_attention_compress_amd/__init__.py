@@ -16,7 +16,9 @@ import torch
 
 __all__ = [
     "CSAError", "lib", "cache_bytes", "compress_quantize", "dequantize", "index_topk",
-    "index_scan", "index_select", "index_topk_workspace", "workspace_clear", "sparse_attn",
+    "index_scan", "index_select", "index_topk_workspace", "index_topk_pool",
+    "index_topk_pool_workspace", "index_pool_scan", "index_pool_select", "workspace_clear",
+    "sparse_attn",
     "hca_dense_attn", "attn_workspace", "Workspace", "BF16", "F32", "F16", "EXPORTED",
 ]
 
@@ -28,8 +30,9 @@ LIB_PATH = os.path.join(_PKG, "libcsa.so")
 EXPORTED = [
     "csa_status_string", "csa_version", "csa_cache_bytes", "csa_compress_quantize",
     "csa_dequantize", "csa_index_topk_workspace", "csa_index_topk", "csa_index_scan",
-    "csa_index_select", "csa_workspace_clear", "csa_attn_workspace", "csa_sparse_attn",
-    "hca_dense_attn",
+    "csa_index_select", "csa_index_topk_pool_workspace", "csa_index_topk_pool",
+    "csa_index_pool_scan", "csa_index_pool_select",
+    "csa_workspace_clear", "csa_attn_workspace", "csa_sparse_attn", "hca_dense_attn",
 ]
 
 
@@ -58,6 +61,13 @@ def lib() -> ctypes.CDLL:
             "csa_index_topk": (I, [P, P, P, I64, I, I, I, I, I, I64, P, I, I, P, P, P, I64, P]),
             "csa_index_scan": (I, [P, P, P, I64, I, I, I, I, I, I64, P, I, I, P, P, P, I64, P]),
             "csa_index_select": (I, [P, P, P, I64, I, I, I, I, I, I64, P, I, I, P, P, P, I64, P]),
+            "csa_index_topk_pool_workspace": (I64, [I, I, I64]),
+            "csa_index_topk_pool": (I, [P, P, P, I64, I, I, I, I, I, I64, I, P, P, I, I, P, P,
+                                        I64, P]),
+            "csa_index_pool_scan": (I, [P, P, P, I64, I, I, I, I, I, I64, I, P, P, I, I, P, P,
+                                        I64, P]),
+            "csa_index_pool_select": (I, [P, P, P, I64, I, I, I, I, I, I64, I, P, P, I, I, P, P,
+                                          I64, P]),
             "csa_workspace_clear": (I, [P, I64, P]),
             "csa_attn_workspace": (I64, [I, I, I, I, I64]),
             "csa_sparse_attn": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, I64, F, P, I, P,
@@ -214,6 +224,51 @@ def index_scan(*args, **kw):
 
 def index_select(*args, **kw):
     _index_call("csa_index_select", *args, **kw)
+
+
+def index_topk_pool_workspace(B, T, n_max) -> int:
+    return lib().csa_index_topk_pool_workspace(B, T, n_max)
+
+
+def index_topk_pool(*args, **kw):
+    """Full-mode top-k plus the blockwise candidate pool; see
+    csa_index_topk_pool in include/csa.h. out_pool: int32 [B][T][group*n_keep]."""
+    _pool_call("csa_index_topk_pool", *args, **kw)
+
+
+def index_pool_scan(*args, **kw):
+    _pool_call("csa_index_pool_scan", *args, **kw)
+
+
+def index_pool_select(*args, **kw):
+    _pool_call("csa_index_pool_select", *args, **kw)
+
+
+def _pool_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, n_keep, out_pool, out_score=None,
+               group=8, workspace=None):
+    _need(q_idx, torch.int8, "q_idx", 4)
+    _need(w, torch.int8, "w", 3)
+    _need(keys, torch.int8, "keys", 3)
+    _need(out_idx, torch.int32, "out_idx", 3)
+    _need(out_score, torch.int32, "out_score", 3)
+    _need(out_pool, torch.int32, "out_pool", 3)
+    B, T, Hi, Di = q_idx.shape
+    if w.shape != (B, T, Hi) or keys.shape[0] != B or keys.shape[2] != Di:
+        raise ValueError("index_topk_pool: inconsistent shapes")
+    if out_idx.shape != (B, T, k) or (out_score is not None and out_score.shape != (B, T, k)):
+        raise ValueError("index_topk_pool: out_idx / out_score must be [B][T][k]")
+    if out_pool.shape != (B, T, group * n_keep):
+        raise ValueError("index_topk_pool: out_pool must be [B][T][group * n_keep]")
+    blk_cap = keys.shape[1]
+    n_max = min(blk_cap, (pos0 + T) // m)
+    need = index_topk_pool_workspace(B, T, n_max)
+    if workspace is None:
+        workspace = _default_ws(q_idx.device)
+    ws = workspace.get(need, key=B * T) if isinstance(workspace, Workspace) else workspace
+    ws_bytes = 0 if ws is None else ws.numel()
+    _check(getattr(lib(), fn_name)(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di, m,
+                                   pos0, k, _ptr(out_idx), _ptr(out_score), group, n_keep,
+                                   _ptr(out_pool), _ptr(ws), ws_bytes, _stream()), fn_name)
 
 
 def workspace_clear(ws):

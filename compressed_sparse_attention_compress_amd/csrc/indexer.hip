@@ -37,6 +37,7 @@ constexpr int TILE = 2048;       // entries per split-scan workgroup
 constexpr int NB1 = 512;         // split-scan histogram bins
 constexpr int MAX_TILES = 2048;  // split-scan limit: n_max <= TILE * MAX_TILES
 constexpr int PREFILL_MIN_T = 16;
+constexpr int POOL_G = 8;        // entries per group of the blockwise pool
 
 // One 16-entry column tile: A = indexer queries (rows = heads), B = keys
 // (columns = entries). Lane (j + 16g) holds D[head 4g + r][entry j] in
@@ -83,16 +84,21 @@ __device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
 // entries masked after the product) and double-buffered, so that a wave keeps
 // 8 column tiles of keys in flight while the previous 8 are scored; scores
 // are staged in LDS and written to the slab at the end.
-template <int DI, bool CAND, int SUB>
+// POOL: the tile's scores are also reduced to the best score of each group of
+// POOL_G consecutive entries (group slab + group histogram), for the
+// blockwise candidate pool.
+template <int DI, bool CAND, int SUB, bool POOL>
 __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
     const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
     const int32_t* __restrict__ cand, int C, int64_t npad, int32_t* __restrict__ slab,
-    uint32_t* __restrict__ hist) {
+    uint32_t* __restrict__ hist, int64_t gpad, int32_t* __restrict__ gslab,
+    uint32_t* __restrict__ ghist) {
   constexpr int KS = (DI + 63) / 64;
   constexpr int BATCH = 8;
   constexpr int SPAN = TILE / SUB;  // entries per workgroup (SUB workgroups per tile)
   __shared__ uint32_t lh[NB1];
+  __shared__ uint32_t lhg[POOL ? NB1 : 1];
   __shared__ __attribute__((aligned(16))) int ssc[SPAN];
   const int64_t wg0 = (int64_t)blockIdx.x * SPAN;  // first entry of the workgroup
   const int qi = blockIdx.y;
@@ -104,7 +110,10 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
 
-  for (int i = threadIdx.x; i < NB1; i += 256) lh[i] = 0;
+  for (int i = threadIdx.x; i < NB1; i += 256) {
+    lh[i] = 0;
+    if (POOL) lhg[i] = 0;
+  }
 
   v4i A[KS];
 #pragma unroll
@@ -210,10 +219,20 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     int4* d = reinterpret_cast<int4*>(sq + e0);
     d[0] = int4{v[0], v[1], v[2], v[3]};
     d[1] = int4{v[4], v[5], v[6], v[7]};
+    if (POOL) {  // this thread's 8 entries are exactly one group
+      int mx = v[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = max(mx, v[j]);
+      gslab[(int64_t)qi * gpad + e0 / POOL_G] = mx;
+      if (mx >= 0) atomicAdd(&lhg[score_bin512(mx)], 1u);
+    }
   }
+  if (POOL) __syncthreads();
   uint32_t* hq = hist + (int64_t)qi * NB1;
-  for (int i = threadIdx.x; i < NB1; i += 256)
+  for (int i = threadIdx.x; i < NB1; i += 256) {
     if (lh[i]) atomicAdd(&hq[i], lh[i]);
+    if (POOL && lhg[i]) atomicAdd(&ghist[(int64_t)qi * NB1 + i], lhg[i]);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -344,6 +363,21 @@ __global__ __launch_bounds__(256) void k_idx_bscan(
   }
 }
 
+// One selection of the select and final passes: over the entries themselves,
+// or (gshift > 0) over groups of 2^gshift consecutive entries, each scored by
+// its best visible entry, whose kept groups are written out entry by entry.
+struct Level {
+  const int32_t* slab;  // [BT][npad] scores
+  int2* cbuf;           // [BT][npad] (score, index) candidates per tile
+  int32_t* cnt;         // [BT][n_tiles] candidate counts
+  uint32_t* hist;       // [BT][NB1] score histogram
+  int64_t npad;
+  int n_tiles, k, gshift;
+  int spec_tiles, spec_shift;
+  int32_t* out;         // [BT][k << gshift]
+  int32_t* out_score;   // [BT][k] or null (entries only)
+};
+
 // ------------------------------------------------------------------------
 // split scan, phase 2a: per tile, the entries at or above the threshold bin
 // ------------------------------------------------------------------------
@@ -373,21 +407,27 @@ __device__ inline int threshold_bin(const uint32_t* hq, int k, int* tmp, int* s_
   return keff;
 }
 
-__global__ __launch_bounds__(256) void k_idx_select(
-    int T, int m, int64_t pos0, int64_t blk_cap, int C, int k, int n_tiles, int64_t npad,
-    const int32_t* __restrict__ slab, int2* __restrict__ cbuf, int32_t* __restrict__ cnt,
-    const uint32_t* __restrict__ hist, bool cand_mode) {
+__global__ __launch_bounds__(256) void k_idx_select(int T, int m, int64_t pos0, int64_t blk_cap,
+                                                    int C, bool cand_mode, Level L0, Level L1) {
   __shared__ int tmp[4];
   __shared__ int s_red[2];
-  const int tile = blockIdx.x;
+  // tiles of the entry selection first, then those of the group selection
+  const bool lv1 = (int)blockIdx.x >= L0.n_tiles;
+  const Level L = lv1 ? L1 : L0;
+  const int tile = lv1 ? blockIdx.x - L0.n_tiles : blockIdx.x;
+  const int n_tiles = L.n_tiles, k = L.k;
+  const int64_t npad = L.npad;
+  int2* cbuf = L.cbuf;
+  int32_t* cnt = L.cnt;
+  const uint32_t* hist = L.hist;
   const int qi = blockIdx.y;
   const int b = qi / T;
   const int64_t t = pos0 + (qi - b * T);
   int64_t nv = (t + 1) / m;
   nv = nv < blk_cap ? nv : blk_cap;
-  const int64_t N = cand_mode ? (int64_t)C : nv;
+  const int64_t N = lv1 ? (nv + (1 << L.gshift) - 1) >> L.gshift : (cand_mode ? (int64_t)C : nv);
   const int64_t e0 = (int64_t)tile * TILE + threadIdx.x * 8;
-  const int32_t* sq = slab + (int64_t)qi * npad;
+  const int32_t* sq = L.slab + (int64_t)qi * npad;
   int s[8];  // issued before the histogram scan so both loads overlap
   if (e0 + 8 <= N) {
     const int4 a = *reinterpret_cast<const int4*>(sq + e0);
@@ -425,11 +465,9 @@ __global__ __launch_bounds__(256) void k_idx_select(
 // than cap_lds (massive ties) walks the per-tile lists in global memory
 // instead. The histogram of the query is cleared for the next call.
 constexpr int SPEC_SLOTS = 4096;  // speculative candidates staged per query (32 KiB)
-__global__ __launch_bounds__(256) void k_idx_final(
-    int T, int m, int64_t pos0, int64_t blk_cap, const int32_t* __restrict__ cand, int C, int k,
-    int n_tiles, int64_t npad, const int2* __restrict__ cbuf, const int32_t* __restrict__ cnt,
-    uint32_t* __restrict__ hist, int32_t* __restrict__ out_idx, int32_t* __restrict__ out_score,
-    int cap_lds, int spec_tiles, int spec_shift) {
+__global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0, int64_t blk_cap,
+                                                   const int32_t* __restrict__ cand, int C,
+                                                   int cap_lds, int BT, Level L0, Level L1) {
   extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ int tmp[4];
   __shared__ uint32_t bh[256];
@@ -438,7 +476,22 @@ __global__ __launch_bounds__(256) void k_idx_final(
   int* t_off = smem;                                  // [MAX_TILES]
   int* area = smem + MAX_TILES;                       // [2 * cap_lds]
   int2* spec = reinterpret_cast<int2*>(area + 2 * cap_lds);  // [spec_tiles << spec_shift]
-  const int qi = blockIdx.x;
+  // queries of the entry selection first, then those of the group selection
+  const bool lv1 = (int)blockIdx.x >= BT;
+  const Level L = lv1 ? L1 : L0;
+  const int qi = lv1 ? blockIdx.x - BT : blockIdx.x;
+  const int k = L.k, n_tiles = L.n_tiles, gs = L.gshift;
+  const int spec_tiles = L.spec_tiles, spec_shift = L.spec_shift;
+  const int64_t npad = L.npad;
+  const int2* cbuf = L.cbuf;
+  const int32_t* cnt = L.cnt;
+  uint32_t* hist = L.hist;
+  int64_t nv;  // visible entries of the query (bounds the expanded groups)
+  {
+    const int b = qi / T;
+    nv = (pos0 + (qi - b * T) + 1) / m;
+    nv = nv < blk_cap ? nv : blk_cap;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int2* cq = cbuf + (int64_t)qi * npad;
   uint32_t* hq = hist + (int64_t)qi * NB1;
@@ -500,13 +553,25 @@ __global__ __launch_bounds__(256) void k_idx_final(
   __syncthreads();
   const int T1 = s_red[0], A1 = s_red[1];
 
-  int32_t* oi = out_idx + (int64_t)qi * k;
-  int32_t* os = out_score ? out_score + (int64_t)qi * k : nullptr;
+  int32_t* oi = L.out + ((int64_t)qi * k << gs);
+  int32_t* os = L.out_score ? L.out_score + (int64_t)qi * k : nullptr;
   const int32_t* cqq = cand ? cand + (int64_t)qi * C : nullptr;
-  for (int i = keff + threadIdx.x; i < k; i += 256) {
-    oi[i] = -1;
-    if (os) os[i] = -1;
-  }
+  for (int i = (keff << gs) + threadIdx.x; i < (k << gs); i += 256) oi[i] = -1;
+  if (os)
+    for (int i = keff + threadIdx.x; i < k; i += 256) os[i] = -1;
+  // selected item number pos: an entry id, or a group written out entry by
+  // entry (entries not visible yet as -1)
+  auto emit = [&](int pos, int e, int sv) {
+    if (gs == 0) {
+      oi[pos] = cqq ? cqq[e] : e;
+      if (os) os[pos] = sv;
+    } else {
+      for (int r = 0; r < (1 << gs); ++r) {
+        const int64_t ent = ((int64_t)e << gs) + r;
+        oi[(pos << gs) + r] = ent < nv ? (int)ent : -1;
+      }
+    }
+  };
   if (keff == 0) return;
 
   __syncthreads();
@@ -607,11 +672,7 @@ __global__ __launch_bounds__(256) void k_idx_final(
           if (eb < take_eq) pos = gb + eb;
           ++eb;
         }
-        if (pos >= 0 && pos < keff) {
-          const int e = ce[i0 + j];
-          oi[pos] = cqq ? cqq[e] : e;
-          if (os) os[pos] = sv[j];
-        }
+        if (pos >= 0 && pos < keff) emit(pos, ce[i0 + j], sv[j]);
       }
       run_gt += tot >> 16;
       run_eq += tot & 0xffff;
@@ -726,8 +787,7 @@ __global__ __launch_bounds__(256) void k_idx_final(
       if (take) {
         const int pos = out_run + __popcll(mt & below);
         if (pos < keff) {
-          oi[pos] = cqq ? cqq[v.y] : v.y;
-          if (os) os[pos] = v.x;
+          emit(pos, v.y, v.x);
         }
       }
       eq_run += __popcll(meq);
@@ -740,35 +800,52 @@ __global__ __launch_bounds__(256) void k_idx_final(
 // host side
 // ------------------------------------------------------------------------
 struct IdxLayout {
-  int n_tiles;
-  int64_t npad;
-  int64_t off_slab, off_cbuf, off_hist, off_cnt, bytes;
+  int n_tiles, g_tiles;  // entry tiles; group tiles (0 without a pool)
+  int64_t npad, gpad;
+  int64_t off_hist, off_ghist, off_cnt, off_slab, off_cbuf, off_gcnt, off_gslab, off_gcbuf, bytes;
 };
 
 static inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-static IdxLayout idx_layout(int64_t BT, int64_t n_max) {
+static IdxLayout idx_layout(int64_t BT, int64_t n_max, bool pool) {
   IdxLayout L;
   int64_t nt = (n_max + TILE - 1) / TILE;
   L.n_tiles = (int)(nt < 1 ? 1 : nt);
   L.npad = (int64_t)L.n_tiles * TILE;
+  L.g_tiles = pool ? (int)((L.npad / POOL_G + TILE - 1) / TILE) : 0;
+  L.gpad = (int64_t)L.g_tiles * TILE;
   int64_t o = 0;
   // header: depends on B*T only, kept zero between calls
   L.off_hist = o; o = align_up(o + BT * NB1 * 4, 256);
+  L.off_ghist = o; o = align_up(o + BT * NB1 * 4, 256);
   // body: rewritten by every call
   L.off_cnt = o; o = align_up(o + BT * L.n_tiles * 4, 256);
   L.off_slab = o; o = align_up(o + BT * L.npad * 4, 256);
   L.off_cbuf = o; o = align_up(o + BT * L.npad * 8, 256);
+  L.off_gcnt = o; o = align_up(o + BT * L.g_tiles * 4, 256);
+  L.off_gslab = o; o = align_up(o + BT * L.gpad * 4, 256);
+  L.off_gcbuf = o; o = align_up(o + BT * L.gpad * 8, 256);
   L.bytes = o;
   return L;
 }
 
-// Candidates the select kernel keeps in LDS: about twice k (the entries above
-// the threshold bin plus that bin), at least enough for the slow-path arrays.
+// Candidates the final kernel keeps in LDS: about twice k (the entries above
+// the threshold bin plus that bin), at least enough for the slow-path arrays,
+// at most 8192 so that the kernel's LDS stays within 104 KiB (larger k take
+// the slow path, which reads the per-tile lists from global memory).
 static int select_cap(int k) {
   int c = 4096;
-  while (c < 2 * k && c < 16384) c *= 2;
+  while (c < 2 * k && c < 8192) c *= 2;
   return c;
+}
+
+// Speculative first-round candidates of the final pass: the staging area is
+// shared out evenly, a power of two per tile between 32 and TILE.
+static void spec_plan(int n_tiles, int* spec_tiles, int* spec_shift) {
+  int sh = 5;
+  while ((1 << (sh + 1)) <= TILE && ((int64_t)n_tiles << (sh + 1)) <= SPEC_SLOTS) ++sh;
+  *spec_shift = sh;
+  *spec_tiles = n_tiles < (SPEC_SLOTS >> sh) ? n_tiles : (SPEC_SLOTS >> sh);
 }
 
 // Raise k_idx_final's dynamic LDS limit once per device (to the largest
@@ -787,18 +864,20 @@ static bool final_lds_allow(size_t lds) {
   return true;
 }
 
-// Runs of at least PREFILL_MIN_T queries per sequence (prefill chunks) are
-// scored by the batched scan; fewer queries, or a candidate pool, by the
-// one-query scan. Both feed the same select and final passes.
-static bool batched_plan(int T, const int32_t* cand) {
-  return cand == nullptr && T >= PREFILL_MIN_T;
-}
-
 struct IdxArgs {
   const int8_t* q_idx; const int8_t* w; const int8_t* keys; int64_t blk_cap;
   int B, T, Hi, Di, m; int64_t pos0; const int32_t* cand; int C, k;
   int32_t* out_idx; int32_t* out_score; void* ws; int64_t ws_bytes; hipStream_t stream;
+  int n_keep = 0;              // blockwise pool: groups kept (0 = no pool)
+  int32_t* out_pool = nullptr;  // [B][T][POOL_G * n_keep]
 };
+
+// Runs of at least PREFILL_MIN_T queries per sequence (prefill chunks) are
+// scored by the batched scan; fewer queries, a candidate pool or a blockwise
+// pool by the one-query scan. All feed the same select and final passes.
+static bool batched_plan(const IdxArgs& a) {
+  return a.cand == nullptr && a.out_pool == nullptr && a.T >= PREFILL_MIN_T;
+}
 
 static int idx_check(const IdxArgs& a, int64_t* n_max) {
   if (a.B < 0 || a.T < 0 || a.blk_cap < 0 || a.pos0 < 0) return CSA_ERR_SHAPE;
@@ -807,6 +886,8 @@ static int idx_check(const IdxArgs& a, int64_t* n_max) {
   if (a.Hi * a.Di > 1024) return CSA_ERR_SHAPE;
   if (a.m < 1 || a.k < 1) return CSA_ERR_SHAPE;
   if (a.cand && a.C < 0) return CSA_ERR_SHAPE;
+  if (a.out_pool && (a.cand || a.n_keep < 1)) return CSA_ERR_SHAPE;
+  if ((int64_t)a.n_keep * POOL_G > 0x7fffffff || a.k > 0x7fffffff / 2) return CSA_ERR_SHAPE;
   if ((int64_t)a.B * a.T > 65535) return CSA_ERR_SHAPE;  // queries per call (grid y)
   if (a.pos0 + a.T > (int64_t)1 << 40) return CSA_ERR_RANGE;
   if (a.B == 0 || a.T == 0) return CSA_OK;
@@ -825,81 +906,89 @@ static int idx_phase(const IdxArgs& a, int phase) {
   int st = idx_check(a, &n_max);
   if (st != CSA_OK || a.B == 0 || a.T == 0) return st;
   const int BT = a.B * a.T;
-  {
-    IdxLayout L = idx_layout(BT, n_max);
-    if (!a.ws) return CSA_ERR_WORKSPACE;
-    if (a.ws_bytes < L.bytes) return CSA_ERR_WORKSPACE;
-    if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
-    char* ws = reinterpret_cast<char*>(a.ws);
-    int32_t* slab = reinterpret_cast<int32_t*>(ws + L.off_slab);
-    int2* cbuf = reinterpret_cast<int2*>(ws + L.off_cbuf);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.off_hist);
-    int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.off_cnt);
-    const int C = a.cand ? a.C : 0;
-    dim3 grid(L.n_tiles, BT);
-    if (phase == 0 && batched_plan(a.T, a.cand)) {
-      const int HP = a.Hi <= 4 ? 4 : (a.Hi <= 8 ? 8 : 16);
-      const int KS = (a.Di + 63) / 64;
-      const int QG = (8 / KS) * (16 / HP);
-      const int n_groups = (a.T + QG - 1) / QG;
-      const dim3 bgrid(L.n_tiles, a.B * n_groups);
+  const bool pool = a.out_pool != nullptr;
+  IdxLayout L = idx_layout(BT, n_max, pool);
+  if (!a.ws) return CSA_ERR_WORKSPACE;
+  if (a.ws_bytes < L.bytes) return CSA_ERR_WORKSPACE;
+  if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
+  char* ws = reinterpret_cast<char*>(a.ws);
+  int32_t* slab = reinterpret_cast<int32_t*>(ws + L.off_slab);
+  int2* cbuf = reinterpret_cast<int2*>(ws + L.off_cbuf);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.off_hist);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.off_cnt);
+  int32_t* gslab = reinterpret_cast<int32_t*>(ws + L.off_gslab);
+  int2* gcbuf = reinterpret_cast<int2*>(ws + L.off_gcbuf);
+  uint32_t* ghist = reinterpret_cast<uint32_t*>(ws + L.off_ghist);
+  int32_t* gcnt = reinterpret_cast<int32_t*>(ws + L.off_gcnt);
+  const int C = a.cand ? a.C : 0;
+  if (phase == 0 && batched_plan(a)) {
+    const int HP = a.Hi <= 4 ? 4 : (a.Hi <= 8 ? 8 : 16);
+    const int KS = (a.Di + 63) / 64;
+    const int QG = (8 / KS) * (16 / HP);
+    const int n_groups = (a.T + QG - 1) / QG;
+    const dim3 bgrid(L.n_tiles, a.B * n_groups);
 #define CSA_LAUNCH_BSCAN(DD, HH)                                                           \
   hipLaunchKernelGGL((k_idx_bscan<DD, HH>), bgrid, dim3(256), 0, a.stream, a.q_idx, a.w,  \
                      a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, L.npad, n_groups, slab, hist)
 #define CSA_LAUNCH_BSCAN_H(DD) \
   if (HP == 4) CSA_LAUNCH_BSCAN(DD, 4); else if (HP == 8) CSA_LAUNCH_BSCAN(DD, 8); else CSA_LAUNCH_BSCAN(DD, 16)
-      if (a.Di == 32) { CSA_LAUNCH_BSCAN_H(32); }
-      else if (a.Di == 64) { CSA_LAUNCH_BSCAN_H(64); }
-      else { CSA_LAUNCH_BSCAN_H(128); }
+    if (a.Di == 32) { CSA_LAUNCH_BSCAN_H(32); }
+    else if (a.Di == 64) { CSA_LAUNCH_BSCAN_H(64); }
+    else { CSA_LAUNCH_BSCAN_H(128); }
 #undef CSA_LAUNCH_BSCAN_H
 #undef CSA_LAUNCH_BSCAN
-    } else if (phase == 0) {
-      // small scans split each tile over 2 or 4 workgroups so that about 512
-      // workgroups stream the keys
-      const int64_t nwg = (int64_t)L.n_tiles * BT;
-      const int sub = nwg >= 512 ? 1 : (nwg >= 256 ? 2 : 4);
-      const dim3 sgrid(L.n_tiles * sub, BT);
-#define CSA_LAUNCH_SCAN(DD, CC, SS)                                                          \
-  hipLaunchKernelGGL((k_idx_scan<DD, CC, SS>), sgrid, dim3(256), 0, a.stream, a.q_idx, a.w, \
-                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.cand, C, L.npad, slab, hist)
-#define CSA_LAUNCH_SCAN_S(DD, CC)                  \
-  do {                                            \
-    if (sub == 1) CSA_LAUNCH_SCAN(DD, CC, 1);     \
-    else if (sub == 2) CSA_LAUNCH_SCAN(DD, CC, 2); \
-    else CSA_LAUNCH_SCAN(DD, CC, 4);              \
+  } else if (phase == 0) {
+    // small scans split each tile over 2 or 4 workgroups so that about 512
+    // workgroups stream the keys
+    const int64_t nwg = (int64_t)L.n_tiles * BT;
+    const int sub = nwg >= 512 ? 1 : (nwg >= 256 ? 2 : 4);
+    const dim3 sgrid(L.n_tiles * sub, BT);
+#define CSA_LAUNCH_SCAN(DD, CC, SS, PP)                                                         \
+  hipLaunchKernelGGL((k_idx_scan<DD, CC, SS, PP>), sgrid, dim3(256), 0, a.stream, a.q_idx, a.w, \
+                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.cand, C, L.npad, slab, hist,   \
+                     L.gpad, gslab, ghist)
+#define CSA_LAUNCH_SCAN_S(DD, CC, PP)                  \
+  do {                                                \
+    if (sub == 1) CSA_LAUNCH_SCAN(DD, CC, 1, PP);     \
+    else if (sub == 2) CSA_LAUNCH_SCAN(DD, CC, 2, PP); \
+    else CSA_LAUNCH_SCAN(DD, CC, 4, PP);              \
   } while (0)
-      if (a.cand) {
-        if (a.Di == 32) CSA_LAUNCH_SCAN_S(32, true);
-        else if (a.Di == 64) CSA_LAUNCH_SCAN_S(64, true);
-        else CSA_LAUNCH_SCAN_S(128, true);
-      } else {
-        if (a.Di == 32) CSA_LAUNCH_SCAN_S(32, false);
-        else if (a.Di == 64) CSA_LAUNCH_SCAN_S(64, false);
-        else CSA_LAUNCH_SCAN_S(128, false);
-      }
+    if (a.cand) {
+      if (a.Di == 32) CSA_LAUNCH_SCAN_S(32, true, false);
+      else if (a.Di == 64) CSA_LAUNCH_SCAN_S(64, true, false);
+      else CSA_LAUNCH_SCAN_S(128, true, false);
+    } else if (pool) {
+      if (a.Di == 32) CSA_LAUNCH_SCAN_S(32, false, true);
+      else if (a.Di == 64) CSA_LAUNCH_SCAN_S(64, false, true);
+      else CSA_LAUNCH_SCAN_S(128, false, true);
+    } else {
+      if (a.Di == 32) CSA_LAUNCH_SCAN_S(32, false, false);
+      else if (a.Di == 64) CSA_LAUNCH_SCAN_S(64, false, false);
+      else CSA_LAUNCH_SCAN_S(128, false, false);
+    }
 #undef CSA_LAUNCH_SCAN_S
 #undef CSA_LAUNCH_SCAN
-    } else {
-      hipLaunchKernelGGL(k_idx_select, grid, dim3(256), 0, a.stream, a.T, a.m, a.pos0,
-                         a.blk_cap, C, a.k, L.n_tiles, L.npad, slab, cbuf, cnt, hist,
-                         a.cand != nullptr);
-      const int cap_lds = select_cap(a.k);
-      // speculative first-round candidates: the staging area is shared out
-      // evenly, a power of two per tile between 32 and TILE
-      int spec_shift = 5;
-      while ((1 << (spec_shift + 1)) <= TILE && ((int64_t)L.n_tiles << (spec_shift + 1)) <= SPEC_SLOTS)
-        ++spec_shift;
-      const int spec_tiles = L.n_tiles < (SPEC_SLOTS >> spec_shift) ? L.n_tiles : (SPEC_SLOTS >> spec_shift);
-      const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int) +
-                         ((size_t)spec_tiles << spec_shift) * sizeof(int2);
-      if (lds > 65536 && !final_lds_allow(lds)) return CSA_ERR_HIP;
-      hipLaunchKernelGGL(k_idx_final, dim3(BT), dim3(256), lds, a.stream, a.T, a.m, a.pos0,
-                         a.blk_cap, a.cand, C, a.k, L.n_tiles, L.npad, cbuf, cnt, hist,
-                         a.out_idx, a.out_score, cap_lds, spec_tiles, spec_shift);
-    }
-    CSA_TRY_LAUNCH();
-    return CSA_OK;
+  } else if (phase == 1) {
+    Level L0{slab, cbuf, cnt, hist, L.npad, L.n_tiles, a.k, 0, 0, 0, a.out_idx, a.out_score};
+    Level L1{gslab, gcbuf, gcnt, ghist, L.gpad, L.g_tiles, a.n_keep, 3, 0, 0, a.out_pool,
+             nullptr};
+    spec_plan(L.n_tiles, &L0.spec_tiles, &L0.spec_shift);
+    if (pool) spec_plan(L.g_tiles, &L1.spec_tiles, &L1.spec_shift);
+    hipLaunchKernelGGL(k_idx_select, dim3(L.n_tiles + L.g_tiles, BT), dim3(256), 0, a.stream,
+                       a.T, a.m, a.pos0, a.blk_cap, C, a.cand != nullptr, L0, L1);
+    const int cap_lds = select_cap(pool && a.n_keep > a.k ? a.n_keep : a.k);
+    const int spec_slots = (L0.spec_tiles << L0.spec_shift) >
+                                   (pool ? (L1.spec_tiles << L1.spec_shift) : 0)
+                               ? (L0.spec_tiles << L0.spec_shift)
+                               : (L1.spec_tiles << L1.spec_shift);
+    const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int) +
+                       (size_t)spec_slots * sizeof(int2);
+    if (lds > 65536 && !final_lds_allow(lds)) return CSA_ERR_HIP;
+    hipLaunchKernelGGL(k_idx_final, dim3(BT * (pool ? 2 : 1)), dim3(256), lds, a.stream, a.T,
+                       a.m, a.pos0, a.blk_cap, a.cand, C, cap_lds, BT, L0, L1);
   }
+  CSA_TRY_LAUNCH();
+  return CSA_OK;
 }
 
 __global__ void k_fill_zero(uint32_t* p, int64_t n) {
@@ -914,7 +1003,12 @@ extern "C" int64_t csa_index_topk_workspace(int B, int T, int64_t n_max, int k, 
   (void)k;
   (void)cand_given;
   if (B < 0 || T < 0 || n_max < 0) return -1;
-  return idx_layout((int64_t)B * T, n_max).bytes;
+  return idx_layout((int64_t)B * T, n_max, false).bytes;
+}
+
+extern "C" int64_t csa_index_topk_pool_workspace(int B, int T, int64_t n_max) {
+  if (B < 0 || T < 0 || n_max < 0) return -1;
+  return idx_layout((int64_t)B * T, n_max, true).bytes;
 }
 
 #define CSA_IDX_ARGS                                                                      \
@@ -949,6 +1043,40 @@ extern "C" int csa_index_topk(const int8_t* q_idx, const int8_t* w, const int8_t
   if (st != CSA_OK) return st;
   return idx_phase(a, 1);
 }
+
+static int pool_phases(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                       int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0, int k,
+                       int32_t* out_idx, int32_t* out_score, int group, int n_keep,
+                       int32_t* out_pool, void* workspace, int64_t ws_bytes, hipStream_t stream,
+                       int first, int last) {
+  if (group != POOL_G || n_keep < 1) return CSA_ERR_SHAPE;
+  if (!out_pool && B > 0 && T > 0) return CSA_ERR_NULL;
+  IdxArgs a{q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos0, nullptr, 0, k, out_idx, out_score,
+            workspace, ws_bytes, stream};
+  a.n_keep = n_keep;
+  a.out_pool = out_pool;
+  for (int ph = first; ph <= last; ++ph) {
+    const int st = idx_phase(a, ph);
+    if (st != CSA_OK) return st;
+  }
+  return CSA_OK;
+}
+
+#define CSA_POOL_PARAMS                                                                       \
+  const int8_t *q_idx, const int8_t *w, const int8_t *keys, int64_t blk_cap, int B, int T,    \
+      int Hi, int Di, int m, int64_t pos0, int k, int32_t *out_idx, int32_t *out_score,        \
+      int group, int n_keep, int32_t *out_pool, void *workspace, int64_t ws_bytes,             \
+      hipStream_t stream
+#define CSA_POOL_ARGS                                                                        \
+  q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos0, k, out_idx, out_score, group, n_keep,      \
+      out_pool, workspace, ws_bytes, stream
+
+extern "C" int csa_index_topk_pool(CSA_POOL_PARAMS) { return pool_phases(CSA_POOL_ARGS, 0, 1); }
+extern "C" int csa_index_pool_scan(CSA_POOL_PARAMS) { return pool_phases(CSA_POOL_ARGS, 0, 0); }
+extern "C" int csa_index_pool_select(CSA_POOL_PARAMS) { return pool_phases(CSA_POOL_ARGS, 1, 1); }
+
+#undef CSA_POOL_ARGS
+#undef CSA_POOL_PARAMS
 
 extern "C" int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream) {
   if (bytes < 0 || bytes % 4) return CSA_ERR_SHAPE;

@@ -161,6 +161,45 @@ int csa_index_select(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
                      int32_t* out_idx, int32_t* out_score,
                      void* workspace, int64_t ws_bytes, hipStream_t stream);
 
+/* Full-mode top-k plus a blockwise candidate pool in one pass over the keys
+ * (podcast cue 14: the best score of each block of positions decides which
+ * blocks a later Reindex layer may choose from). Same arguments, layouts and
+ * top-k result as csa_index_topk without a pool (cand = NULL), and:
+ *   group     entries per group; must be 8 (CSA_ERR_SHAPE otherwise)
+ *   n_keep    groups kept, >= 1
+ *   out_pool  int32 [B][T][group * n_keep]  kept group i (ascending group
+ *             order) fills slots i*group .. i*group + group - 1 with its
+ *             entry ids, -1 for entries not visible yet; slots of groups
+ *             beyond the number of visible groups are -1. Ascending, so it
+ *             is a valid `cand` for csa_index_topk.
+ * The causally visible entries are cut into groups of 8 consecutive entries
+ * (the last may be partial); a group's score is the largest score of its
+ * visible entries; groups are ordered by score descending, then lower group
+ * index. Runs of queries use the one-query scan (no batched prefill scan).
+ * Workspace: csa_index_topk_pool_workspace(B, T, n_max) bytes, with the same
+ * head rules as csa_index_topk (the head layout depends on B*T only and is the
+ * same for both calls, so one workspace serves both). */
+int64_t csa_index_topk_pool_workspace(int B, int T, int64_t n_max);
+int csa_index_topk_pool(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                        int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                        int k, int32_t* out_idx, int32_t* out_score,
+                        int group, int n_keep, int32_t* out_pool,
+                        void* workspace, int64_t ws_bytes, hipStream_t stream);
+
+/* The two launches of csa_index_topk_pool (scan: entry scores and group
+ * maxima with their histograms; select: both selections), with identical
+ * arguments, so a caller can place events or other work between them. */
+int csa_index_pool_scan(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                        int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                        int k, int32_t* out_idx, int32_t* out_score,
+                        int group, int n_keep, int32_t* out_pool,
+                        void* workspace, int64_t ws_bytes, hipStream_t stream);
+int csa_index_pool_select(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                          int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                          int k, int32_t* out_idx, int32_t* out_score,
+                          int group, int n_keep, int32_t* out_pool,
+                          void* workspace, int64_t ws_bytes, hipStream_t stream);
+
 /* Zero-fill a workspace with a kernel on `stream` (no hipMemset, so it may be
  * captured in a graph). bytes must be a multiple of 4 and ws 4-byte aligned. */
 int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);

@@ -71,6 +71,12 @@ def test_argument_errors_before_launch(L):
     assert L.csa_index_topk(*args(8, 64, 8, None)) == -4
     assert L.csa_index_topk(fake, fake, fake, 100, 1, 1, 8, 64, 4, 399, None, 0, 8, fake, None,
                             fake, 16, None) == -4
+    # blockwise pool: group other than 8, n_keep < 1, missing pool output
+    pool = lambda group, n_keep, out: (fake, fake, fake, 100, 1, 1, 8, 64, 4, 399, 8, fake, None,
+                                       group, n_keep, out, fake, 1 << 20, None)
+    assert L.csa_index_topk_pool(*pool(4, 16, fake)) == -2
+    assert L.csa_index_topk_pool(*pool(8, 0, fake)) == -2
+    assert L.csa_index_topk_pool(*pool(8, 16, None)) == -1
     # attention: bad d, H, window ring too small, dtype
     a = lambda d, H, W, Wcap, T, dt: (fake, fake, fake, 100, fake, 8, fake, Wcap, W, 1, T, H, d,
                                       399, ctypes.c_float(1.0), fake, dt, None, fake, 1 << 30,
@@ -87,5 +93,10 @@ def test_workspace_sizes(L):
     assert L.csa_index_topk_workspace(8, 1, 262144, 1024, 0) > 8 * 262144 * 12
     assert L.csa_index_topk_workspace(1, 8192, 32768, 512, 0) > 8192 * 32768 * 12
     assert L.csa_index_topk_workspace(16, 1, 4096, 512, 1) > 0
+    # the pool adds a group score and a group candidate slot per 8 entries
+    for BT, n in ((8, 262144), (1, 100), (64, 4096)):
+        plain = L.csa_index_topk_workspace(BT, 1, n, 512, 0)
+        assert L.csa_index_topk_pool_workspace(BT, 1, n) >= plain + BT * (n // 8) * 12
+    assert L.csa_index_topk_pool_workspace(-1, 1, 8) == -1
     assert L.csa_attn_workspace(1, 8192, 64, 512, 640) == 0
     assert L.csa_attn_workspace(8, 1, 64, 512, 1152) >= 8 * 9 * 64 * 512 * 4

@@ -176,6 +176,7 @@ def test_index_decode_edges():
     _index_case(2, 3, 8, 64, 4, 4 * 3000, 100, 3000, seed=10, wzero=True)  # all ties
     _index_case(2, 1, 8, 64, 4, 4 * 9000, 300, 9000, seed=11, keyrange=1)  # massive ties
     _index_case(1, 1, 8, 64, 1, 2047, 2048, 4096, seed=12)     # k == visible exactly
+    _index_case(2, 1, 8, 64, 4, 4 * 20000 - 1, 6000, 20000, seed=22)  # k > LDS capacity
     _index_case(2, 2, 8, 64, 4, 4 * 20000, 1000, 20000, seed=13, phases=True)
 
 
@@ -197,6 +198,68 @@ def test_index_many_queries():
     _index_case(64, 2, 8, 64, 4, 4 * 9500 - 2, 96, 9507, seed=43)      # 4 per workgroup, ragged
     _index_case(128, 2, 4, 128, 4, 4 * 3000 - 2, 64, 3007, seed=44)    # 128-dim keys, 2 per group
     _index_case(64, 2, 8, 64, 4, 4 * 9500 - 2, 96, 9507, seed=45, cand_C=4500)  # pool, 3 tiles
+
+
+def _pool_case(B, T, Hi, Di, m, pos0, k, n_keep, blk_cap, seed, wzero=False, keyrange=8,
+               reindex_k=0):
+    """Full-mode top-k plus the blockwise pool against the oracle's top-k and
+    block pool, element by element; with reindex_k, a Reindex top-k over the
+    produced pool (partial groups leave -1 inside it) against the oracle."""
+    g = gen(seed, "pool", B, T, Hi, Di)
+    q = torch.randint(-8, 8, (B, T, Hi, Di), generator=g, device=DEV, dtype=torch.int8)
+    w = torch.randint(0, 4, (B, T, Hi), generator=g, device=DEV, dtype=torch.int8)
+    if wzero:
+        w.zero_()
+    keys = torch.randint(-keyrange, keyrange, (B, blk_cap, Di), generator=g, device=DEV,
+                         dtype=torch.int8)
+    oi = torch.full((B, T, k), -7, device=DEV, dtype=torch.int32)
+    os_ = torch.full((B, T, k), -7, device=DEV, dtype=torch.int32)
+    op = torch.full((B, T, 8 * n_keep), -7, device=DEV, dtype=torch.int32)
+    csa.index_topk_pool(q, w, keys, m, pos0, k, oi, n_keep, op, out_score=os_)
+    plain = torch.full((B, T, k), -7, device=DEV, dtype=torch.int32)
+    csa.index_topk(q, w, keys, m, pos0, k, plain)
+    ri = None
+    if reindex_k:
+        ri = torch.full((B, T, reindex_k), -7, device=DEV, dtype=torch.int32)
+        csa.index_topk(q, w, keys, m, pos0, reindex_k, ri, cand=op)
+    torch.cuda.synchronize()
+    assert torch.equal(oi, plain)
+    qn, wn, kn = q.cpu().numpy(), w.cpu().numpy(), keys.cpu().numpy()
+    oin, osn, opn = oi.cpu().numpy(), os_.cpu().numpy(), op.cpu().numpy()
+    rin = ri.cpu().numpy() if ri is not None else None
+    for b in range(B):
+        for ti in range(T):
+            t = pos0 + ti
+            ref_i, ref_s = O.index_topk(qn[b, ti], wn[b, ti], kn[b], m, t, k)
+            assert np.array_equal(oin[b, ti], ref_i), (b, ti)
+            assert np.array_equal(osn[b, ti], ref_s), (b, ti)
+            ref_p = O.block_pool(qn[b, ti], wn[b, ti], kn[b], m, t, 8, n_keep)
+            assert np.array_equal(opn[b, ti], ref_p), (b, ti, opn[b, ti][:16], ref_p[:16])
+            if rin is not None:
+                ref_r, _ = O.index_topk(qn[b, ti], wn[b, ti], kn[b], m, t, reindex_k,
+                                        cand=ref_p)
+                assert np.array_equal(rin[b, ti], ref_r), (b, ti)
+
+
+@pytest.mark.parametrize("Hi,Di", [(8, 64), (4, 32), (16, 64), (8, 128)])
+def test_index_block_pool_shapes(Hi, Di):
+    """Decode queries: a 20,000-entry context (10 tiles, ragged) keeping 256
+    groups, then a Reindex top-k over the pool."""
+    say("index block pool", Hi, Di)
+    _pool_case(4, 1, Hi, Di, 4, 4 * 20000 - 1, 512, 256, 20003, seed=60, reindex_k=256)
+
+
+def test_index_block_pool_edges():
+    say("index block pool edges")
+    _pool_case(2, 1, 8, 64, 4, 2, 16, 8, 64, seed=61)                 # nothing visible
+    _pool_case(2, 1, 8, 64, 4, 4 * 101 - 1, 32, 64, 400, seed=62)     # 13 groups < n_keep, partial
+    _pool_case(2, 3, 8, 64, 4, 4 * 3000, 100, 40, 3000, seed=63, wzero=True)   # all ties
+    _pool_case(2, 1, 8, 64, 4, 4 * 9000, 300, 500, 9000, seed=64, keyrange=1)  # massive ties
+    _pool_case(1, 20, 8, 64, 4, 4 * 5000 - 20, 64, 100, 5007, seed=65,          # query run
+               reindex_k=64)
+    _pool_case(1, 1, 8, 64, 1, 2047, 2048, 256, 4096, seed=66)        # n_keep == visible groups
+    # the long-context keep size (2,000 groups of a 32,768-entry context)
+    _pool_case(2, 1, 8, 64, 4, 4 * 32768 - 1, 512, 2000, 32768, seed=67, reindex_k=512)
 
 
 @pytest.mark.parametrize("Hi,Di", [(4, 32), (8, 64), (16, 64), (2, 128), (5, 64)])
