@@ -45,7 +45,7 @@ import numpy as np
 E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 E2M1_EMAX = 2          # exponent of the largest E2M1 power of two (4 = 2**2)
 E8M0_BIAS = 127
-GROUP = 32             # elements sharing one E8M0 scale (BASELINE format)
+GROUP = 32             # elements sharing one E8M0 scale (reading A1)
 
 
 # --------------------------------------------------------------------------
