@@ -367,6 +367,40 @@ def hca_dense_attn(q_bf16, codes, scales, m: int, win, Wcap: int, W: int, t: int
                        softmax_scale)
 
 
+# --------------------------------------------------------------------------
+# f2: the cache of a decoding sequence
+# --------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to
+    the even pattern (reading A17; finite inputs). The 16 dropped bits are
+    compared with half of the last kept bit's weight."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    hi = u >> 16
+    lo = u & 0xFFFF
+    up = (lo > 0x8000) | ((lo == 0x8000) & ((hi & 1) == 1))
+    return (hi + up.astype(np.uint64)).astype(np.uint16)
+
+
+def cache_after_appends(kv: np.ndarray, gate: np.ndarray, m: int, n_tok: int, Wcap: int):
+    """State of one sequence's caches once its tokens 0 .. n_tok-1 have been
+    appended ([NOTES4] s.1: finished blocks go to the compressed cache, the
+    newest tokens stay uncompressed; reading A24).
+
+    Returns (codes, scales, ring):
+      codes, scales  the n_tok // m complete blocks, exactly as a one-shot
+                     compression of tokens 0 .. (n_tok // m) * m - 1;
+      ring           {slot: bf16 bits [d]} for the tokens p = max(0, n_tok -
+                     Wcap) .. n_tok - 1, each in slot p % Wcap.
+    A block still being filled has no entry (no query can see it, A8)."""
+    nb = n_tok // m
+    kv = np.asarray(kv, dtype=np.float32)
+    gate = np.asarray(gate, dtype=np.float32)
+    codes, scales = compress_quantize(kv[:nb * m], gate[:nb * m], m)
+    ring = {int(p % Wcap): f32_to_bf16_bits(kv[p]) for p in range(max(0, n_tok - Wcap), n_tok)}
+    return codes, scales, ring
+
+
 READINGS = {
     "A1": "MXFP4 uses one E8M0 scale per 32 elements (OCP MX), not the E4M3-per-16 variant of [PODCAST] cue 16",
     "A2": "scale exponent = floor(log2 amax) - 2, clamped to [-127, 127]; amax 0 -> byte 0",
@@ -383,4 +417,5 @@ READINGS = {
     "A17": "window rows are bf16",
     "A22": "blockwise pool: groups of `group` consecutive compressed entries (8 per [PODCAST] cue 14); group score = max over its visible entries",
     "A23": "blockwise pool keeps n_keep groups (about 2000 per cue 14), ties to the lower group; the pool lists their visible entries ascending, -1 elsewhere",
+    "A24": "decode append: a block's entry is written once its m-th token arrives, from the block's m float32 tokens; each token also enters the bf16 ring at slot p % Wcap; sequences of a batch may sit at different positions",
 }

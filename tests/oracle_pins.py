@@ -473,4 +473,53 @@ def pin_attention_invariants(O):
     assert np.array_equal(rows, exact)
 
 
+# --------------------------------------------------------- decode append ----
+
+def pin_bf16_rounding(O):
+    """Hand-derived roundings (ties to even), then agreement with torch's
+    float32 -> bfloat16 conversion over every exponent range."""
+    f = lambda v: int(O.f32_to_bf16_bits(np.float32(v)))
+    assert f(1.0) == 0x3F80 and f(-1.5) == 0xBFC0 and f(0.0) == 0 and f(-0.0) == 0x8000
+    assert f(1 + 2.0 ** -8) == 0x3F80                   # tie, 0x3F80 is even
+    assert f(1 + 3 * 2.0 ** -8) == 0x3F82               # tie, rounds up to the even 0x3F82
+    assert f(1 + 2.0 ** -8 + 2.0 ** -20) == 0x3F81      # just above the tie
+    assert f(1 + 2.0 ** -7 - 2.0 ** -20) == 0x3F81      # just below 0x3F81 + half
+    # subnormals: 2^-133 is the smallest bfloat16 step; halfway cases go to even
+    assert f(2.0 ** -133) == 0x0001 and f(2.0 ** -134) == 0x0000 and f(3 * 2.0 ** -134) == 0x0002
+    rng = np.random.default_rng(20)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-60, 60, 200000))).astype(np.float32)
+    bits = rng.integers(0, 1 << 16, 20000, dtype=np.uint32)  # every low half, exact ties included
+    y = ((np.uint32(0x3F12) << 16) | bits).view(np.float32)
+    for v in (x, y, -y):
+        assert np.array_equal(O.f32_to_bf16_bits(v), _bf16_bits(v))
+
+
+def pin_cache_after_appends_brute_force(O):
+    """Token-by-token simulation (ring slot p % Wcap; a staging area of m
+    rows; a block pooled and quantised when its m-th token arrives) against
+    the closed description, for block sizes 1, 3 and 4 and lengths that end
+    on and inside a block, shorter and longer than the ring."""
+    rng = np.random.default_rng(21)
+    d, Wcap = 32, 8
+    for m in (1, 3, 4):
+        L = 29
+        kv = rng.standard_normal((L, d)).astype(np.float32)
+        g = rng.standard_normal(L).astype(np.float32)
+        ring, stage_x, stage_g, entries = {}, [None] * m, [None] * m, []
+        for n_tok in range(1, L + 1):
+            p = n_tok - 1
+            ring[p % Wcap] = _bf16_bits(kv[p])
+            stage_x[p % m], stage_g[p % m] = kv[p], g[p]
+            if (p + 1) % m == 0:
+                c, sc = O.quantize_rows(O.pool_blocks(np.stack(stage_x), np.array(stage_g), m))
+                entries.append((c[0], sc[0]))
+            codes, scales, r = O.cache_after_appends(kv, g, m, n_tok, Wcap)
+            assert codes.shape[0] == len(entries) == n_tok // m, (m, n_tok)
+            for i, (c, sc) in enumerate(entries):
+                assert np.array_equal(codes[i], c) and np.array_equal(scales[i], sc), (m, n_tok, i)
+            assert sorted(r) == sorted(ring) if n_tok >= Wcap else sorted(r) == list(range(n_tok))
+            for slot, row in r.items():
+                assert np.array_equal(row, ring[slot]), (m, n_tok, slot)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -33,6 +33,8 @@ orig_attend = O.attend
 orig_win = O.window_positions
 orig_nvis = O.n_visible
 orig_gather = O.gather_rows
+orig_bf16 = O.f32_to_bf16_bits
+orig_append = O.cache_after_appends
 
 
 def m_scale_off_by_one(a):
@@ -171,6 +173,33 @@ def _pool_variant(q, w, keys, m, t, group, n_keep, reduce="max", tie_low=True, v
     return pool
 
 
+def m_bf16_truncate(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def m_bf16_ties_up(x):
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x8000) >> 16).astype(np.uint16)
+
+
+def m_append_ring_shift(kv, gate, m, n_tok, Wcap):
+    c, s, r = orig_append(kv, gate, m, n_tok, Wcap)
+    return c, s, {(k + 1) % Wcap: v for k, v in r.items()}
+
+
+def m_append_partial_block(kv, gate, m, n_tok, Wcap):
+    _, _, r = orig_append(kv, gate, m, n_tok, Wcap)
+    c, s = O.compress_quantize(np.asarray(kv)[:n_tok], np.asarray(gate)[:n_tok], m)
+    return c, s, r
+
+
+def m_append_ring_short(kv, gate, m, n_tok, Wcap):
+    c, s, r = orig_append(kv, gate, m, n_tok, Wcap)
+    first = max(0, n_tok - Wcap)
+    r.pop(first % Wcap, None)
+    return c, s, r
+
+
 MUTANTS = {
     "scale exponent off by one": {"scale_exponent": m_scale_off_by_one},
     "scale exponent not clamped": {"scale_exponent": m_no_clamp},
@@ -195,6 +224,11 @@ MUTANTS = {
     "pool ties to the higher group": {"block_pool": lambda *a: _pool_variant(*a, tie_low=False)},
     "pool ignores visibility": {"block_pool": lambda *a: _pool_variant(*a, visible=False)},
     "pool groups shifted": {"block_pool": lambda *a: _pool_variant(*a, shift=1)},
+    "bf16 by truncation": {"f32_to_bf16_bits": m_bf16_truncate},
+    "bf16 ties rounded up": {"f32_to_bf16_bits": m_bf16_ties_up},
+    "append ring slot off by one": {"cache_after_appends": m_append_ring_shift},
+    "append writes the partial block": {"cache_after_appends": m_append_partial_block},
+    "append ring drops its oldest token": {"cache_after_appends": m_append_ring_short},
 }
 
 
