@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "CSAError", "lib", "cache_bytes", "compress_quantize", "dequantize", "index_topk",
     "index_scan", "index_select", "index_topk_workspace", "index_topk_pool",
-    "index_topk_pool_workspace", "index_pool_scan", "index_pool_select", "workspace_clear",
+    "index_topk_pool_workspace", "index_pool_scan", "index_pool_select", "decode_append",
+    "workspace_clear",
     "sparse_attn",
     "hca_dense_attn", "attn_workspace", "Workspace", "BF16", "F32", "F16", "EXPORTED",
 ]
@@ -31,7 +32,8 @@ EXPORTED = [
     "csa_status_string", "csa_version", "csa_cache_bytes", "csa_compress_quantize",
     "csa_dequantize", "csa_index_topk_workspace", "csa_index_topk", "csa_index_scan",
     "csa_index_select", "csa_index_topk_pool_workspace", "csa_index_topk_pool",
-    "csa_index_pool_scan", "csa_index_pool_select",
+    "csa_index_pool_scan", "csa_index_pool_select", "csa_decode_append",
+    "csa_index_topk_ragged", "csa_sparse_attn_ragged", "hca_dense_attn_ragged",
     "csa_workspace_clear", "csa_attn_workspace", "csa_sparse_attn", "hca_dense_attn",
 ]
 
@@ -68,6 +70,13 @@ def lib() -> ctypes.CDLL:
                                         I64, P]),
             "csa_index_pool_select": (I, [P, P, P, I64, I, I, I, I, I, I64, I, P, P, I, I, P, P,
                                           I64, P]),
+            "csa_decode_append": (I, [P, I64, P, P, I, I, I, P, P, P, P, I64, P, I, P]),
+            "csa_index_topk_ragged": (I, [P, P, P, I64, I, I, I, I, I, P, I64, P, I, I, P, P, P,
+                                          I64, P]),
+            "csa_sparse_attn_ragged": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, P, I64, F, P,
+                                           I, P, P, I64, P]),
+            "hca_dense_attn_ragged": (I, [P, P, P, I64, I, P, I, I, I, I, I, I, P, I64, F, P, I,
+                                          P, P, I64, P]),
             "csa_workspace_clear": (I, [P, I64, P]),
             "csa_attn_workspace": (I64, [I, I, I, I, I64]),
             "csa_sparse_attn": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, I64, F, P, I, P,
@@ -167,6 +176,31 @@ def compress_quantize(kv, gate, tok0: int, m: int, codes, scales):
            "csa_compress_quantize")
 
 
+def decode_append(kv, gate, pos, m: int, stage, stage_gate, codes, scales, win):
+    """One new token per sequence at its own position; see csa_decode_append.
+    kv float32 [B][kv_ld] (d = codes.shape[2]*2 columns used), gate float32
+    [B], pos int64 [B] (device; < 0 skips a sequence), stage float32
+    [B][m][d], stage_gate float32 [B][m], win bfloat16 [B][Wcap][d]."""
+    _need(kv, torch.float32, "kv", 2)
+    _need(gate, torch.float32, "gate", 1)
+    _need(pos, torch.int64, "pos", 1)
+    _need(stage, torch.float32, "stage", 3)
+    _need(stage_gate, torch.float32, "stage_gate", 2)
+    _need(codes, torch.uint8, "codes", 3)
+    _need(scales, torch.uint8, "scales", 3)
+    _need(win, torch.bfloat16, "win", 3)
+    B, ld = kv.shape
+    d = codes.shape[2] * 2
+    if (gate.shape != (B,) or pos.shape != (B,) or stage.shape != (B, m, d)
+            or stage_gate.shape != (B, m) or codes.shape[0] != B
+            or scales.shape != (B, codes.shape[1], d // 32) or win.shape[0] != B
+            or win.shape[2] != d):
+        raise ValueError("decode_append: inconsistent shapes")
+    _check(lib().csa_decode_append(_ptr(kv), ld, _ptr(gate), _ptr(pos), B, d, m, _ptr(stage),
+                                   _ptr(stage_gate), _ptr(codes), _ptr(scales), codes.shape[1],
+                                   _ptr(win), win.shape[1], _stream()), "csa_decode_append")
+
+
 def dequantize(codes, scales, blk0: int, n_blk: int, out):
     _need(codes, torch.uint8, "codes", 3)
     _need(scales, torch.uint8, "scales", 3)
@@ -183,8 +217,21 @@ def index_topk_workspace(B, T, n_max, k, cand_given=False) -> int:
     return lib().csa_index_topk_workspace(B, T, n_max, k, int(bool(cand_given)))
 
 
+def _positions(pos0, pos_max, B, device, what):
+    """(host pos0 or pos_max, device positions or None): pos0 is an int, or an
+    int64 [B] tensor of per-sequence positions bounded by pos_max."""
+    if not isinstance(pos0, torch.Tensor):
+        return int(pos0), None
+    if pos_max is None:
+        raise ValueError(f"{what}: per-sequence positions need pos_max")
+    _need(pos0, torch.int64, "pos", 1)
+    if pos0.shape != (B,) or pos0.device != device:
+        raise ValueError(f"{what}: pos must be an int64 [B] tensor on the data's device")
+    return int(pos_max), pos0
+
+
 def _index_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, out_score=None, cand=None,
-                workspace=None):
+                workspace=None, pos_max=None):
     _need(q_idx, torch.int8, "q_idx", 4)
     _need(w, torch.int8, "w", 3)
     _need(keys, torch.int8, "keys", 3)
@@ -192,6 +239,9 @@ def _index_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, out_score=None, ca
     _need(out_score, torch.int32, "out_score", 3)
     _need(cand, torch.int32, "cand", 3)
     B, T, Hi, Di = q_idx.shape
+    pos0, pos = _positions(pos0, pos_max, B, q_idx.device, "index_topk")
+    if pos is not None and fn_name != "csa_index_topk":
+        raise ValueError(f"{fn_name}: per-sequence positions are taken by index_topk only")
     if w.shape != (B, T, Hi) or keys.shape[0] != B or keys.shape[2] != Di:
         raise ValueError("index_topk: inconsistent shapes")
     if out_idx.shape != (B, T, k) or (out_score is not None and out_score.shape != (B, T, k)):
@@ -208,13 +258,21 @@ def _index_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, out_score=None, ca
         workspace = _default_ws(q_idx.device)
     ws = workspace.get(need, key=B * T) if isinstance(workspace, Workspace) else workspace
     ws_bytes = 0 if ws is None else ws.numel()
+    if pos is not None:
+        _check(lib().csa_index_topk_ragged(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi,
+                                           Di, m, _ptr(pos), pos0, _ptr(cand), C, k,
+                                           _ptr(out_idx), _ptr(out_score), _ptr(ws), ws_bytes,
+                                           _stream()), "csa_index_topk_ragged")
+        return
     _check(getattr(lib(), fn_name)(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di, m,
                                    pos0, _ptr(cand), C, k, _ptr(out_idx), _ptr(out_score),
                                    _ptr(ws), ws_bytes, _stream()), fn_name)
 
 
 def index_topk(*args, **kw):
-    """Indexer scores + top-k; see csa_index_topk in include/csa.h."""
+    """Indexer scores + top-k; see csa_index_topk in include/csa.h. pos0 may
+    be an int64 [B] tensor of per-sequence positions (then pass pos_max; see
+    csa_index_topk_ragged)."""
     _index_call("csa_index_topk", *args, **kw)
 
 
@@ -301,9 +359,12 @@ def _attn_common(q, codes, scales, win, out, lse):
 
 
 def sparse_attn(q, codes, scales, idx, win, W, pos0, softmax_scale, out, lse=None,
-                workspace=None):
-    """Attention over the idx-selected entries plus the window; see csa_sparse_attn."""
+                workspace=None, pos_max=None):
+    """Attention over the idx-selected entries plus the window; see
+    csa_sparse_attn (csa_sparse_attn_ragged when pos0 is an int64 [B] tensor
+    of per-sequence positions, bounded by pos_max)."""
     B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse)
+    pos0, pos = _positions(pos0, pos_max, B, q.device, "sparse_attn")
     _need(idx, torch.int32, "idx", 3)
     k = idx.shape[2]
     if idx.shape[:2] != (B, T):
@@ -313,6 +374,13 @@ def sparse_attn(q, codes, scales, idx, win, W, pos0, softmax_scale, out, lse=Non
     if need > 0 and ws is None:
         ws = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if ws is None else ws.numel()
+    if pos is not None:
+        _check(lib().csa_sparse_attn_ragged(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1],
+                                            _ptr(idx), k, _ptr(win), win.shape[1], W, B, T, H, d,
+                                            _ptr(pos), pos0, float(softmax_scale), _ptr(out), dt,
+                                            _ptr(lse), _ptr(ws), ws_bytes, _stream()),
+               "csa_sparse_attn_ragged")
+        return
     _check(lib().csa_sparse_attn(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1], _ptr(idx), k,
                                  _ptr(win), win.shape[1], W, B, T, H, d, pos0,
                                  float(softmax_scale), _ptr(out), dt, _ptr(lse), _ptr(ws),
@@ -320,15 +388,25 @@ def sparse_attn(q, codes, scales, idx, win, W, pos0, softmax_scale, out, lse=Non
 
 
 def hca_dense_attn(q, codes, scales, m, win, W, pos0, softmax_scale, out, lse=None,
-                   workspace=None):
-    """Attention over every visible entry of an m-token cache plus the window."""
+                   workspace=None, pos_max=None):
+    """Attention over every visible entry of an m-token cache plus the window
+    (hca_dense_attn_ragged when pos0 is an int64 [B] tensor, bounded by
+    pos_max)."""
     B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse)
+    pos0, pos = _positions(pos0, pos_max, B, q.device, "hca_dense_attn")
     n_slots = min(codes.shape[1], (pos0 + T) // m) + W
     need = attn_workspace(B, T, H, d, n_slots)
     ws = workspace.get(need) if isinstance(workspace, Workspace) else workspace
     if need > 0 and ws is None:
         ws = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if ws is None else ws.numel()
+    if pos is not None:
+        _check(lib().hca_dense_attn_ragged(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1], m,
+                                           _ptr(win), win.shape[1], W, B, T, H, d, _ptr(pos),
+                                           pos0, float(softmax_scale), _ptr(out), dt, _ptr(lse),
+                                           _ptr(ws), ws_bytes, _stream()),
+               "hca_dense_attn_ragged")
+        return
     _check(lib().hca_dense_attn(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1], m, _ptr(win),
                                 win.shape[1], W, B, T, H, d, pos0, float(softmax_scale),
                                 _ptr(out), dt, _ptr(lse), _ptr(ws), ws_bytes, _stream()),

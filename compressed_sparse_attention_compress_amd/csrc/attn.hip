@@ -47,7 +47,8 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t blk_cap, const int32_t* __restrict__ idx, int k,
     int m, const uint16_t* __restrict__ win, int Wcap, int W, int T, int H, int64_t pos0,
-    float scale_log2, int nsplit, int spl, int n_queries, void* __restrict__ out, int out_dtype,
+    const int64_t* __restrict__ qpos, float scale_log2, int nsplit, int spl, int n_queries,
+    void* __restrict__ out, int out_dtype,
     float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml) {
   constexpr int NWV = 2 * NW;                 // waves: (head group, half)
   constexpr int NT = NWV * 64;
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
   const int split = jx % nsplit;
   if (qi >= n_queries) return;
   const int b = qi / T;
-  const int64_t t = pos0 + (qi - b * T);
+  const int64_t t = query_base(qpos, pos0, b) + (qi - b * T);
   int64_t nsel = k;
   if (DENSE) {
     nsel = (t + 1) / m;
@@ -530,6 +531,7 @@ struct AttnArgs {
   const int32_t* idx; int k; int m; const uint16_t* win; int Wcap, W, B, T, H, d;
   int64_t pos0; float softmax_scale; void* out; int out_dtype; float* lse; void* ws;
   int64_t ws_bytes; hipStream_t stream;
+  const int64_t* pos = nullptr;  // per-sequence first positions (pos0 = their bound) or null
 };
 
 template <int D, bool DENSE>
@@ -541,7 +543,7 @@ static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, flo
 #define CSA_LAUNCH_ATTN(NW)                                                                  \
   hipLaunchKernelGGL((k_attn<D, NW, DENSE>), grid, dim3(NW * 128), 0, a.stream, a.q, a.codes, \
                      a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, a.H, a.pos0, \
-                     sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse, part_o, part_ml)
+                     a.pos, sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse, part_o, part_ml)
   switch (nw) {
     case 1: CSA_LAUNCH_ATTN(1); break;
     case 2: CSA_LAUNCH_ATTN(2); break;
@@ -626,5 +628,33 @@ extern "C" int hca_dense_attn(const uint16_t* q, const uint8_t* codes, const uin
                               hipStream_t stream) {
   AttnArgs a{q, codes, scales, blk_cap, nullptr, 0, m, win, Wcap, W, B, T, H, d, pos0,
              softmax_scale, out, out_dtype, lse, workspace, ws_bytes, stream};
+  return attn_run(a, true);
+}
+
+extern "C" int csa_sparse_attn_ragged(const uint16_t* q, const uint8_t* codes,
+                                      const uint8_t* scales, int64_t blk_cap, const int32_t* idx,
+                                      int k, const uint16_t* win, int Wcap, int W, int B, int T,
+                                      int H, int d, const int64_t* pos, int64_t pos_max,
+                                      float softmax_scale, void* out, int out_dtype, float* lse,
+                                      void* workspace, int64_t ws_bytes, hipStream_t stream) {
+  if (B > 0 && T > 0 && !pos) return CSA_ERR_NULL;
+  if (pos && !csa_aligned(pos, 8)) return CSA_ERR_ALIGN;
+  AttnArgs a{q, codes, scales, blk_cap, idx, k, 1, win, Wcap, W, B, T, H, d, pos_max,
+             softmax_scale, out, out_dtype, lse, workspace, ws_bytes, stream};
+  a.pos = pos;
+  return attn_run(a, false);
+}
+
+extern "C" int hca_dense_attn_ragged(const uint16_t* q, const uint8_t* codes,
+                                     const uint8_t* scales, int64_t blk_cap, int m,
+                                     const uint16_t* win, int Wcap, int W, int B, int T, int H,
+                                     int d, const int64_t* pos, int64_t pos_max,
+                                     float softmax_scale, void* out, int out_dtype, float* lse,
+                                     void* workspace, int64_t ws_bytes, hipStream_t stream) {
+  if (B > 0 && T > 0 && !pos) return CSA_ERR_NULL;
+  if (pos && !csa_aligned(pos, 8)) return CSA_ERR_ALIGN;
+  AttnArgs a{q, codes, scales, blk_cap, nullptr, 0, m, win, Wcap, W, B, T, H, d, pos_max,
+             softmax_scale, out, out_dtype, lse, workspace, ws_bytes, stream};
+  a.pos = pos;
   return attn_run(a, true);
 }

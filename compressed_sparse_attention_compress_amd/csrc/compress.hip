@@ -19,47 +19,31 @@
 
 namespace {
 
-// One lane owns 8 consecutive channels of one block; D/8 lanes cover a block
-// row, so a wave holds 64/(D/8) blocks.
-template <int D>
-__global__ __launch_bounds__(256) void k_compress_quantize(
-    const float* __restrict__ kv, int64_t kv_ld, const float* __restrict__ gate,
-    int64_t n_tok, int m, int64_t nblk, int64_t total, int64_t blk_first,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t blk_cap) {
-  constexpr int LPB = D / 8;
-  constexpr int BPW = 64 / LPB;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t gb = ((int64_t)blockIdx.x * 4 + wave) * BPW + lane / LPB;
-  if (gb >= total) return;  // whole 4-lane groups leave together
-  const int64_t b = gb / nblk;
-  const int64_t bi = gb - b * nblk;
-  const int64_t j0 = bi * m;
-  const int n = (int)((n_tok - j0) < m ? (n_tok - j0) : m);
-  const int seg = lane % LPB;
-  const float* g = gate + b * n_tok + j0;
-  const float* x = kv + (b * n_tok + j0) * kv_ld + seg * 8;
-
-  double gmax = (double)g[0];
-  for (int j = 1; j < n; ++j) gmax = fmax(gmax, (double)g[j]);
-  double den = exp((double)g[0] - gmax);
-  for (int j = 1; j < n; ++j) den = den + exp((double)g[j] - gmax);
+// Pools the n tokens of one block over this lane's 8 channels and quantises
+// them: gate_at(j) is token j's gate logit, row_at(j, a, c) loads its 8
+// channels. The 4 lanes of a 32-channel scale group must call it together.
+// Returns the 8 packed E2M1 codes and the scale exponent.
+template <class GateAt, class RowAt>
+__device__ inline uint32_t pool_quantize8(int n, GateAt gate_at, RowAt row_at, int* e_out) {
+  double gmax = (double)gate_at(0);
+  for (int j = 1; j < n; ++j) gmax = fmax(gmax, (double)gate_at(j));
+  double den = exp((double)gate_at(0) - gmax);
+  for (int j = 1; j < n; ++j) den = den + exp((double)gate_at(j) - gmax);
 
   double p[8];
   {
-    const double w0 = exp((double)g[0] - gmax) / den;
-    const float4 a = *reinterpret_cast<const float4*>(x);
-    const float4 c = *reinterpret_cast<const float4*>(x + 4);
+    const double w0 = exp((double)gate_at(0) - gmax) / den;
+    float4 a, c;
+    row_at(0, a, c);
     p[0] = w0 * (double)a.x; p[1] = w0 * (double)a.y;
     p[2] = w0 * (double)a.z; p[3] = w0 * (double)a.w;
     p[4] = w0 * (double)c.x; p[5] = w0 * (double)c.y;
     p[6] = w0 * (double)c.z; p[7] = w0 * (double)c.w;
   }
   for (int j = 1; j < n; ++j) {
-    const double wj = exp((double)g[j] - gmax) / den;
-    const float* xj = x + (int64_t)j * kv_ld;
-    const float4 a = *reinterpret_cast<const float4*>(xj);
-    const float4 c = *reinterpret_cast<const float4*>(xj + 4);
+    const double wj = exp((double)gate_at(j) - gmax) / den;
+    float4 a, c;
+    row_at(j, a, c);
     p[0] = p[0] + wj * (double)a.x; p[1] = p[1] + wj * (double)a.y;
     p[2] = p[2] + wj * (double)a.z; p[3] = p[3] + wj * (double)a.w;
     p[4] = p[4] + wj * (double)c.x; p[5] = p[5] + wj * (double)c.y;
@@ -90,7 +74,106 @@ __global__ __launch_bounds__(256) void k_compress_quantize(
     uint32_t code = (signbit(y) ? 8u : 0u) | mag;
     word |= code << (4 * i);
   }
+  *e_out = e;
+  return word;
+}
+
+// One lane owns 8 consecutive channels of one block; D/8 lanes cover a block
+// row, so a wave holds 64/(D/8) blocks.
+template <int D>
+__global__ __launch_bounds__(256) void k_compress_quantize(
+    const float* __restrict__ kv, int64_t kv_ld, const float* __restrict__ gate,
+    int64_t n_tok, int m, int64_t nblk, int64_t total, int64_t blk_first,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t blk_cap) {
+  constexpr int LPB = D / 8;
+  constexpr int BPW = 64 / LPB;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t gb = ((int64_t)blockIdx.x * 4 + wave) * BPW + lane / LPB;
+  if (gb >= total) return;  // whole 4-lane groups leave together
+  const int64_t b = gb / nblk;
+  const int64_t bi = gb - b * nblk;
+  const int64_t j0 = bi * m;
+  const int n = (int)((n_tok - j0) < m ? (n_tok - j0) : m);
+  const int seg = lane % LPB;
+  const float* g = gate + b * n_tok + j0;
+  const float* x = kv + (b * n_tok + j0) * kv_ld + seg * 8;
+  int e;
+  const uint32_t word = pool_quantize8(
+      n, [&](int j) { return g[j]; },
+      [&](int j, float4& a, float4& c) {
+        const float* xj = x + (int64_t)j * kv_ld;
+        a = *reinterpret_cast<const float4*>(xj);
+        c = *reinterpret_cast<const float4*>(xj + 4);
+      },
+      &e);
   const int64_t row = b * blk_cap + blk_first + bi;
+  *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + seg * 4) = word;
+  if ((seg & 3) == 0) scales[row * (D / 32) + seg / 4] = (uint8_t)(e + 127);
+}
+
+// Decode append: one new token per sequence, at its own position pos[b]
+// (sequences with pos[b] < 0 are skipped). The token goes to the bf16 ring
+// slot pos % Wcap and, in float32, to the staging row pos % m; when it is the
+// block's m-th token the block is pooled from the m staged rows (this token
+// from registers) and quantised into entry pos / m, with the same arithmetic
+// as k_compress_quantize. Lanes as in k_compress_quantize, one sequence per
+// D/8 lanes.
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_append(
+    const float* __restrict__ kv, int64_t kv_ld, const float* __restrict__ gate,
+    const int64_t* __restrict__ pos, int B, int m, float* __restrict__ stage,
+    float* __restrict__ stage_gate, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    int64_t blk_cap, uint16_t* __restrict__ win, int Wcap) {
+  constexpr int LPB = D / 8;
+  constexpr int BPW = 64 / LPB;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t b = ((int64_t)blockIdx.x * 4 + wave) * BPW + lane / LPB;
+  if (b >= B) return;  // whole sequences leave together
+  const int64_t t = pos[b];
+  if (t < 0) return;
+  const int seg = lane % LPB;
+  const float* x = kv + b * kv_ld + seg * 8;
+  const float4 xa = *reinterpret_cast<const float4*>(x);
+  const float4 xc = *reinterpret_cast<const float4*>(x + 4);
+  const float gt = gate[b];
+
+  // bf16 ring row (round to nearest even)
+  {
+    v8bf v;
+    v[0] = (__bf16)xa.x; v[1] = (__bf16)xa.y; v[2] = (__bf16)xa.z; v[3] = (__bf16)xa.w;
+    v[4] = (__bf16)xc.x; v[5] = (__bf16)xc.y; v[6] = (__bf16)xc.z; v[7] = (__bf16)xc.w;
+    *reinterpret_cast<v8bf*>(win + (b * Wcap + t % Wcap) * D + seg * 8) = v;
+  }
+  // staging row of the block being filled
+  const int j = (int)(t % m);
+  float* st = stage + b * m * D;
+  {
+    float* sr = st + (int64_t)j * D + seg * 8;
+    *reinterpret_cast<float4*>(sr) = xa;
+    *reinterpret_cast<float4*>(sr + 4) = xc;
+    if (seg == 0) stage_gate[b * m + j] = gt;
+  }
+  if (j != m - 1) return;
+  const int64_t blk = t / m;
+  if (blk >= blk_cap) return;
+  const float* sg = stage_gate + b * m;
+  int e;
+  const uint32_t word = pool_quantize8(
+      m, [&](int i) { return i == j ? gt : sg[i]; },
+      [&](int i, float4& a, float4& c) {
+        if (i == j) {
+          a = xa;
+          c = xc;
+        } else {
+          const float* sr = st + (int64_t)i * D + seg * 8;
+          a = *reinterpret_cast<const float4*>(sr);
+          c = *reinterpret_cast<const float4*>(sr + 4);
+        }
+      },
+      &e);
+  const int64_t row = b * blk_cap + blk;
   *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + seg * 4) = word;
   if ((seg & 3) == 0) scales[row * (D / 32) + seg / 4] = (uint8_t)(e + 127);
 }
@@ -162,6 +245,37 @@ extern "C" int csa_compress_quantize(const float* kv, int64_t kv_ld, const float
     default: CSA_LAUNCH_COMPRESS(512); break;
   }
 #undef CSA_LAUNCH_COMPRESS
+  CSA_TRY_LAUNCH();
+  return CSA_OK;
+}
+
+extern "C" int csa_decode_append(const float* kv, int64_t kv_ld, const float* gate,
+                                 const int64_t* pos, int B, int d, int m, float* stage,
+                                 float* stage_gate, uint8_t* codes, uint8_t* scales,
+                                 int64_t blk_cap, uint16_t* win, int Wcap, hipStream_t stream) {
+  if (B < 0 || blk_cap < 0 || Wcap < 1) return CSA_ERR_SHAPE;
+  if (m < 1 || m > 128) return CSA_ERR_SHAPE;
+  if (d != 32 && d != 64 && d != 128 && d != 256 && d != 512) return CSA_ERR_SHAPE;
+  if (kv_ld < d || kv_ld % 4) return CSA_ERR_ALIGN;
+  if (B == 0) return CSA_OK;
+  if (!kv || !gate || !pos || !stage || !stage_gate || !win) return CSA_ERR_NULL;
+  if (blk_cap > 0 && (!codes || !scales)) return CSA_ERR_NULL;
+  if (!csa_aligned(kv, 16) || !csa_aligned(stage, 16) || !csa_aligned(win, 16) ||
+      !csa_aligned(pos, 8) || (blk_cap > 0 && !csa_aligned(codes, 4)))
+    return CSA_ERR_ALIGN;
+  const int spw = 4 * (64 / (d / 8));  // sequences per workgroup
+  const int grid = (B + spw - 1) / spw;
+#define CSA_LAUNCH_APPEND(DD)                                                                 \
+  hipLaunchKernelGGL(k_decode_append<DD>, dim3(grid), dim3(256), 0, stream, kv, kv_ld, gate,  \
+                     pos, B, m, stage, stage_gate, codes, scales, blk_cap, win, Wcap)
+  switch (d) {
+    case 32: CSA_LAUNCH_APPEND(32); break;
+    case 64: CSA_LAUNCH_APPEND(64); break;
+    case 128: CSA_LAUNCH_APPEND(128); break;
+    case 256: CSA_LAUNCH_APPEND(256); break;
+    default: CSA_LAUNCH_APPEND(512); break;
+  }
+#undef CSA_LAUNCH_APPEND
   CSA_TRY_LAUNCH();
   return CSA_OK;
 }

@@ -26,6 +26,15 @@ static inline bool csa_aligned(const void* p, uintptr_t a) {
 
 // ---------------------------------------------------------------- scans ----
 
+// First query position of sequence b: pos0 for every sequence, or, with
+// per-sequence positions, pos[b] clamped into [0, pos0] (pos0 is then the
+// bound the launch plan and the workspace were sized for).
+__device__ inline int64_t query_base(const int64_t* pos, int64_t pos0, int b) {
+  if (!pos) return pos0;
+  const int64_t p = pos[b];
+  return p < 0 ? 0 : (p > pos0 ? pos0 : p);
+}
+
 // Inclusive prefix sum over the NT threads of a workgroup (NT multiple of
 // 64). `tmp` must hold NT/64 ints of LDS. Returns the inclusive prefix and
 // writes the workgroup total to *total. Contains two barriers.

@@ -91,7 +91,8 @@ template <int DI, bool CAND, int SUB, bool POOL>
 __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
     const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
-    const int32_t* __restrict__ cand, int C, int64_t npad, int32_t* __restrict__ slab,
+    const int64_t* __restrict__ qpos, const int32_t* __restrict__ cand, int C, int64_t npad,
+    int32_t* __restrict__ slab,
     uint32_t* __restrict__ hist, int64_t gpad, int32_t* __restrict__ gslab,
     uint32_t* __restrict__ ghist) {
   constexpr int KS = (DI + 63) / 64;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   const int64_t wg0 = (int64_t)blockIdx.x * SPAN;  // first entry of the workgroup
   const int qi = blockIdx.y;
   const int b = qi / T;
-  const int64_t t = pos0 + (qi - b * T);
+  const int64_t t = query_base(qpos, pos0, b) + (qi - b * T);
   int64_t nv = (t + 1) / m;
   nv = nv < blk_cap ? nv : blk_cap;
   const int64_t N = CAND ? (int64_t)C : nv;
@@ -248,7 +249,8 @@ template <int DI, int HP>
 __global__ __launch_bounds__(256) void k_idx_bscan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
     const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
-    int64_t npad, int n_groups, int32_t* __restrict__ slab, uint32_t* __restrict__ hist) {
+    const int64_t* __restrict__ qpos, int64_t npad, int n_groups, int32_t* __restrict__ slab,
+    uint32_t* __restrict__ hist) {
   constexpr int KS = (DI + 63) / 64;
   constexpr int QPT = 16 / HP;
   constexpr int RT = 8 / KS;
@@ -259,6 +261,7 @@ __global__ __launch_bounds__(256) void k_idx_bscan(
   const int tile = blockIdx.x;
   const int b = blockIdx.y / n_groups;
   const int t0 = (blockIdx.y - b * n_groups) * QG;  // first query (index within T)
+  const int64_t base = query_base(qpos, pos0, b);     // position of query 0
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
 
@@ -296,14 +299,14 @@ __global__ __launch_bounds__(256) void k_idx_bscan(
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int ti = t0 + rt * QPT + g / GPQ;
-    int64_t nv = (pos0 + ti + 1) / m;
+    int64_t nv = (base + ti + 1) / m;
     nv = nv < blk_cap ? nv : blk_cap;
     my_real[rt] = ti < T;
     my_nv[rt] = ti < T ? nv : 0;
     my_row[rt] = slab + ((int64_t)b * T + (ti < T ? ti : T - 1)) * npad;
   }
   const int t_last = (t0 + QG < T ? t0 + QG : T) - 1;
-  int64_t n_end = (pos0 + t_last + 1) / m;  // entries any query of the group can see
+  int64_t n_end = (base + t_last + 1) / m;  // entries any query of the group can see
   n_end = n_end < blk_cap ? n_end : blk_cap;
   __syncthreads();
 
@@ -407,8 +410,10 @@ __device__ inline int threshold_bin(const uint32_t* hq, int k, int* tmp, int* s_
   return keff;
 }
 
-__global__ __launch_bounds__(256) void k_idx_select(int T, int m, int64_t pos0, int64_t blk_cap,
-                                                    int C, bool cand_mode, Level L0, Level L1) {
+__global__ __launch_bounds__(256) void k_idx_select(int T, int m, int64_t pos0,
+                                                    const int64_t* __restrict__ qpos,
+                                                    int64_t blk_cap, int C, bool cand_mode,
+                                                    Level L0, Level L1) {
   __shared__ int tmp[4];
   __shared__ int s_red[2];
   // tiles of the entry selection first, then those of the group selection
@@ -422,7 +427,7 @@ __global__ __launch_bounds__(256) void k_idx_select(int T, int m, int64_t pos0, 
   const uint32_t* hist = L.hist;
   const int qi = blockIdx.y;
   const int b = qi / T;
-  const int64_t t = pos0 + (qi - b * T);
+  const int64_t t = query_base(qpos, pos0, b) + (qi - b * T);
   int64_t nv = (t + 1) / m;
   nv = nv < blk_cap ? nv : blk_cap;
   const int64_t N = lv1 ? (nv + (1 << L.gshift) - 1) >> L.gshift : (cand_mode ? (int64_t)C : nv);
@@ -465,7 +470,9 @@ __global__ __launch_bounds__(256) void k_idx_select(int T, int m, int64_t pos0, 
 // than cap_lds (massive ties) walks the per-tile lists in global memory
 // instead. The histogram of the query is cleared for the next call.
 constexpr int SPEC_SLOTS = 4096;  // speculative candidates staged per query (32 KiB)
-__global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0, int64_t blk_cap,
+__global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
+                                                   const int64_t* __restrict__ qpos,
+                                                   int64_t blk_cap,
                                                    const int32_t* __restrict__ cand, int C,
                                                    int cap_lds, int BT, Level L0, Level L1) {
   extern __shared__ __attribute__((aligned(16))) int smem[];
@@ -489,7 +496,7 @@ __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0, i
   int64_t nv;  // visible entries of the query (bounds the expanded groups)
   {
     const int b = qi / T;
-    nv = (pos0 + (qi - b * T) + 1) / m;
+    nv = (query_base(qpos, pos0, b) + (qi - b * T) + 1) / m;
     nv = nv < blk_cap ? nv : blk_cap;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -868,6 +875,7 @@ struct IdxArgs {
   const int8_t* q_idx; const int8_t* w; const int8_t* keys; int64_t blk_cap;
   int B, T, Hi, Di, m; int64_t pos0; const int32_t* cand; int C, k;
   int32_t* out_idx; int32_t* out_score; void* ws; int64_t ws_bytes; hipStream_t stream;
+  const int64_t* pos = nullptr;  // per-sequence first positions (pos0 = their bound) or null
   int n_keep = 0;              // blockwise pool: groups kept (0 = no pool)
   int32_t* out_pool = nullptr;  // [B][T][POOL_G * n_keep]
 };
@@ -929,7 +937,7 @@ static int idx_phase(const IdxArgs& a, int phase) {
     const dim3 bgrid(L.n_tiles, a.B * n_groups);
 #define CSA_LAUNCH_BSCAN(DD, HH)                                                           \
   hipLaunchKernelGGL((k_idx_bscan<DD, HH>), bgrid, dim3(256), 0, a.stream, a.q_idx, a.w,  \
-                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, L.npad, n_groups, slab, hist)
+                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.pos, L.npad, n_groups, slab, hist)
 #define CSA_LAUNCH_BSCAN_H(DD) \
   if (HP == 4) CSA_LAUNCH_BSCAN(DD, 4); else if (HP == 8) CSA_LAUNCH_BSCAN(DD, 8); else CSA_LAUNCH_BSCAN(DD, 16)
     if (a.Di == 32) { CSA_LAUNCH_BSCAN_H(32); }
@@ -945,8 +953,8 @@ static int idx_phase(const IdxArgs& a, int phase) {
     const dim3 sgrid(L.n_tiles * sub, BT);
 #define CSA_LAUNCH_SCAN(DD, CC, SS, PP)                                                         \
   hipLaunchKernelGGL((k_idx_scan<DD, CC, SS, PP>), sgrid, dim3(256), 0, a.stream, a.q_idx, a.w, \
-                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.cand, C, L.npad, slab, hist,   \
-                     L.gpad, gslab, ghist)
+                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.pos, a.cand, C, L.npad, slab,  \
+                     hist, L.gpad, gslab, ghist)
 #define CSA_LAUNCH_SCAN_S(DD, CC, PP)                  \
   do {                                                \
     if (sub == 1) CSA_LAUNCH_SCAN(DD, CC, 1, PP);     \
@@ -975,7 +983,7 @@ static int idx_phase(const IdxArgs& a, int phase) {
     spec_plan(L.n_tiles, &L0.spec_tiles, &L0.spec_shift);
     if (pool) spec_plan(L.g_tiles, &L1.spec_tiles, &L1.spec_shift);
     hipLaunchKernelGGL(k_idx_select, dim3(L.n_tiles + L.g_tiles, BT), dim3(256), 0, a.stream,
-                       a.T, a.m, a.pos0, a.blk_cap, C, a.cand != nullptr, L0, L1);
+                       a.T, a.m, a.pos0, a.pos, a.blk_cap, C, a.cand != nullptr, L0, L1);
     const int cap_lds = select_cap(pool && a.n_keep > a.k ? a.n_keep : a.k);
     const int spec_slots = (L0.spec_tiles << L0.spec_shift) >
                                    (pool ? (L1.spec_tiles << L1.spec_shift) : 0)
@@ -985,7 +993,7 @@ static int idx_phase(const IdxArgs& a, int phase) {
                        (size_t)spec_slots * sizeof(int2);
     if (lds > 65536 && !final_lds_allow(lds)) return CSA_ERR_HIP;
     hipLaunchKernelGGL(k_idx_final, dim3(BT * (pool ? 2 : 1)), dim3(256), lds, a.stream, a.T,
-                       a.m, a.pos0, a.blk_cap, a.cand, C, cap_lds, BT, L0, L1);
+                       a.m, a.pos0, a.pos, a.blk_cap, a.cand, C, cap_lds, BT, L0, L1);
   }
   CSA_TRY_LAUNCH();
   return CSA_OK;
@@ -1039,6 +1047,21 @@ extern "C" int csa_index_topk(const int8_t* q_idx, const int8_t* w, const int8_t
                               int32_t* out_score, void* workspace, int64_t ws_bytes,
                               hipStream_t stream) {
   CSA_IDX_ARGS;
+  int st = idx_phase(a, 0);
+  if (st != CSA_OK) return st;
+  return idx_phase(a, 1);
+}
+
+extern "C" int csa_index_topk_ragged(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                                     int64_t blk_cap, int B, int T, int Hi, int Di, int m,
+                                     const int64_t* pos, int64_t pos_max, const int32_t* cand,
+                                     int C, int k, int32_t* out_idx, int32_t* out_score,
+                                     void* workspace, int64_t ws_bytes, hipStream_t stream) {
+  if (B > 0 && T > 0 && !pos) return CSA_ERR_NULL;
+  if (pos && !csa_aligned(pos, 8)) return CSA_ERR_ALIGN;
+  IdxArgs a{q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos_max, cand, C, k, out_idx, out_score,
+            workspace, ws_bytes, stream};
+  a.pos = pos;
   int st = idx_phase(a, 0);
   if (st != CSA_OK) return st;
   return idx_phase(a, 1);

@@ -106,6 +106,34 @@ int csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t blk_cap,
                    void* out, int out_dtype, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode append: one new token for each of B sequences, each at its own
+ * position ("Frontier Architecture Decoding Notes (4)", section 1: finished
+ * 4-token blocks are compressed, the newest 128 tokens stay uncompressed).
+ * For sequence b with t = pos[b] >= 0 (sequences with pos[b] < 0 are left
+ * untouched):
+ *   - the token's bf16 rounding (nearest, ties to even) goes to win[b][t % Wcap];
+ *   - its float32 latent and gate go to the staging row stage[b][t % m];
+ *   - if t % m == m - 1, the block's m staged tokens are pooled and quantised
+ *     into entry t / m exactly as csa_compress_quantize would (skipped when
+ *     t / m >= blk_cap).
+ * A block still being filled gets no entry (no query can see it). After a
+ * one-shot csa_compress_quantize of tokens 0 .. P-1 that ends inside a
+ * block, the caller copies that block's P % m tokens and gates into staging
+ * rows 0 .. P % m - 1 before the first append.
+ *   kv     float32 [B][kv_ld] (first d used), 16-byte aligned, kv_ld % 4 == 0
+ *   gate   float32 [B]
+ *   pos    int64 [B] DEVICE array, 8-byte aligned
+ *   stage  float32 [B][m][d], 16-byte aligned;  stage_gate float32 [B][m]
+ *   codes / scales  as in csa_compress_quantize;  win bf16 [B][Wcap][d], 16-byte aligned
+ * Requires 1 <= m <= 128, d in {32, 64, 128, 256, 512}, Wcap >= 1.
+ * ------------------------------------------------------------------------- */
+int csa_decode_append(const float* kv, int64_t kv_ld, const float* gate,
+                      const int64_t* pos, int B, int d, int m,
+                      float* stage, float* stage_gate,
+                      uint8_t* codes, uint8_t* scales, int64_t blk_cap,
+                      uint16_t* win, int Wcap, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Indexer + top-k (podcast cues 12 and 14: a light indexer scores every
  * causally visible compressed entry and keeps the top-k; a Reindex layer
  * scores only a candidate pool that an earlier Full layer chose).
@@ -143,6 +171,21 @@ int csa_index_topk(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
                    const int32_t* cand, int C, int k,
                    int32_t* out_idx, int32_t* out_score,
                    void* workspace, int64_t ws_bytes, hipStream_t stream);
+
+/* csa_index_topk for a batch whose sequences sit at different positions:
+ * the queries of sequence b are at pos[b] .. pos[b] + T - 1, with pos an
+ * int64 [B] DEVICE array (8-byte aligned) read by the kernels, so a decode
+ * loop can advance it on the device. pos_max bounds every pos[b] (values
+ * outside [0, pos_max] are clamped into it); the launch plan and the
+ * workspace (n_max = min(blk_cap, (pos_max + T) / m) without a pool) are
+ * sized for it. Results per query are those of csa_index_topk at its own
+ * position. */
+int csa_index_topk_ragged(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                          int64_t blk_cap, int B, int T, int Hi, int Di, int m,
+                          const int64_t* pos, int64_t pos_max,
+                          const int32_t* cand, int C, int k,
+                          int32_t* out_idx, int32_t* out_score,
+                          void* workspace, int64_t ws_bytes, hipStream_t stream);
 
 /* The two launches csa_index_topk makes, exposed so a caller can place events
  * or other work between them: csa_index_topk == csa_index_scan followed by
@@ -249,6 +292,25 @@ int hca_dense_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scale
                    int B, int T, int H, int d, int64_t pos0, float softmax_scale,
                    void* out, int out_dtype, float* lse,
                    void* workspace, int64_t ws_bytes, hipStream_t stream);
+
+/* csa_sparse_attn and hca_dense_attn for sequences at different positions:
+ * the queries of sequence b are at pos[b] .. pos[b] + T - 1 (pos: int64 [B]
+ * DEVICE array, 8-byte aligned; values outside [0, pos_max] are clamped into
+ * it). The split plan and the workspace are those of a batch at pos_max
+ * (csa_attn_workspace with n_slots = k + W, or min(blk_cap, (pos_max + T) /
+ * m) + W for the dense call). */
+int csa_sparse_attn_ragged(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                           int64_t blk_cap, const int32_t* idx, int k,
+                           const uint16_t* win, int Wcap, int W,
+                           int B, int T, int H, int d, const int64_t* pos, int64_t pos_max,
+                           float softmax_scale, void* out, int out_dtype, float* lse,
+                           void* workspace, int64_t ws_bytes, hipStream_t stream);
+int hca_dense_attn_ragged(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                          int64_t blk_cap, int m,
+                          const uint16_t* win, int Wcap, int W,
+                          int B, int T, int H, int d, const int64_t* pos, int64_t pos_max,
+                          float softmax_scale, void* out, int out_dtype, float* lse,
+                          void* workspace, int64_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

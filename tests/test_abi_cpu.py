@@ -77,6 +77,18 @@ def test_argument_errors_before_launch(L):
     assert L.csa_index_topk_pool(*pool(4, 16, fake)) == -2
     assert L.csa_index_topk_pool(*pool(8, 0, fake)) == -2
     assert L.csa_index_topk_pool(*pool(8, 16, None)) == -1
+    # ragged indexer: positions missing or misaligned
+    rag = lambda pos: (fake, fake, fake, 100, 1, 1, 8, 64, 4, pos, 399, None, 0, 8, fake, None,
+                       fake, 1 << 20, None)
+    assert L.csa_index_topk_ragged(*rag(None)) == -1
+    assert L.csa_index_topk_ragged(*rag(P(260))) == -7
+    # decode append: bad m, bad d, missing positions, misaligned stage
+    app = lambda d, m, pos, stage: (fake, 512, fake, pos, 2, d, m, stage, fake, fake, fake, 10,
+                                    fake, 128, None)
+    assert L.csa_decode_append(*app(512, 0, fake, fake)) == -2
+    assert L.csa_decode_append(*app(96, 4, fake, fake)) == -2
+    assert L.csa_decode_append(*app(512, 4, None, fake)) == -1
+    assert L.csa_decode_append(*app(512, 4, fake, P(264))) == -7
     # attention: bad d, H, window ring too small, dtype
     a = lambda d, H, W, Wcap, T, dt: (fake, fake, fake, 100, fake, 8, fake, Wcap, W, 1, T, H, d,
                                       399, ctypes.c_float(1.0), fake, dt, None, fake, 1 << 30,
@@ -86,6 +98,13 @@ def test_argument_errors_before_launch(L):
     assert L.csa_sparse_attn(*a(512, 64, 128, 128, 2, 0)) == -3
     assert L.csa_sparse_attn(*a(512, 64, 0, 128, 1, 0)) == -2
     assert L.csa_sparse_attn(*a(512, 64, 128, 128, 1, 7)) == -5
+    # ragged attention: positions missing
+    ra = (fake, fake, fake, 100, fake, 8, fake, 128, 128, 1, 1, 64, 512, None, 399,
+          ctypes.c_float(1.0), fake, 0, None, fake, 1 << 30, None)
+    assert L.csa_sparse_attn_ragged(*ra) == -1
+    rh = (fake, fake, fake, 100, 4, fake, 128, 128, 1, 1, 64, 512, None, 399,
+          ctypes.c_float(1.0), fake, 0, None, fake, 1 << 30, None)
+    assert L.hca_dense_attn_ragged(*rh) == -1
 
 
 def test_workspace_sizes(L):
