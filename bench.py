@@ -343,6 +343,182 @@ def run_decode(args, csa, synth, wl, dev):
 
 
 # --------------------------------------------------------------------------
+# ragged decode (decode_ragged_1m)
+# --------------------------------------------------------------------------
+
+def ragged_set(csa, synth, wl, dev, seed):
+    """decode_set plus, per sequence, its position, its new token (latent and
+    gate) and the staging rows of its block being filled."""
+    import torch
+    s = decode_set(csa, synth, wl, dev, seed)
+    pos = wl.positions()
+    s["pos_list"] = pos
+    s["pos"] = torch.tensor(pos, dtype=torch.int64, device=dev)
+    # the ring before the step holds tokens up to t - 1; the step appends t
+    s["win"] = synth.window_ring(wl, [t - 1 for t in pos], dev, seed)
+    s["kv_new"] = torch.stack([synth.latent_range(wl, b, t, t + 1, dev, seed)[0]
+                               for b, t in enumerate(pos)]).contiguous()
+    s["gate_new"] = torch.stack([synth.latent_range(wl, b, t, t + 1, dev, seed, gate=True)[0]
+                                 for b, t in enumerate(pos)]).contiguous()
+    s["dev"], s["seed"] = dev, seed
+    s["stage"] = torch.zeros(wl.B, wl.m, wl.d, device=dev)
+    s["stage_gate"] = torch.zeros(wl.B, wl.m, device=dev)
+    for b, t in enumerate(pos):
+        r = t % wl.m
+        if r:
+            s["stage"][b, :r] = synth.latent_range(wl, b, t - r, t, dev, seed)
+            s["stage_gate"][b, :r] = synth.latent_range(wl, b, t - r, t, dev, seed, gate=True)
+    return s
+
+
+def cpu_baseline_ragged(s, wl, n_queries, min_seconds):
+    """The oracle on the first n_queries sequences of a ragged step (index +
+    top-k + attention at each sequence's own position), one thread, repeated
+    until min_seconds of oracle time have passed; the first pass also checks
+    the device results, and the entries the step's append completed against
+    the oracle's compression of those blocks' tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.csa_oracle as O
+    import synth
+    keys = s["keys"].cpu().numpy()
+    q_idx, w = s["q_idx"].cpu().numpy(), s["w"].cpu().numpy()
+    qb, win = host_bits(s["q"]), host_bits(s["win"])
+    gpu_idx = s["idx"].cpu().numpy()
+    gpu_out = s["out"].cpu().float().numpy()
+    pos = s["pos_list"]
+    ok = True
+    for b, t in enumerate(pos):  # appended entries
+        if (t + 1) % wl.m == 0:
+            j0 = t + 1 - wl.m
+            kv = synth.latent_range(wl, b, j0, t + 1, s["dev"], s["seed"]).cpu().numpy()
+            g = synth.latent_range(wl, b, j0, t + 1, s["dev"], s["seed"], gate=True).cpu().numpy()
+            rc, rs = O.compress_quantize(kv, g, wl.m)
+            blk = t // wl.m
+            ok &= bool(np.array_equal(s["codes"][b, blk].cpu().numpy(), rc[0]))
+            ok &= bool(np.array_equal(s["scales"][b, blk].cpu().numpy(), rs[0]))
+    t_total, worst, done = 0.0, 0.0, 0
+    codes = [s["codes"][b].cpu().numpy() for b in range(n_queries)]
+    scales = [s["scales"][b].cpu().numpy() for b in range(n_queries)]
+    with threadpool_limits(limits=1):
+        while done == 0 or t_total < min_seconds:
+            for b in range(n_queries):
+                t = pos[b]
+                t0 = time.perf_counter()
+                ri, _ = O.index_topk(q_idx[b, 0], w[b, 0], keys[b], wl.m, t, wl.k)
+                ro, _ = O.sparse_attn(qb[b, 0], codes[b], scales[b], ri, win[b], wl.Wcap, wl.W,
+                                      t, 1.0)
+                t_total += time.perf_counter() - t0
+                if done < n_queries:
+                    ok &= bool(np.array_equal(ri, gpu_idx[b, 0]))
+                    worst = max(worst, bf16_excess(gpu_out[b, 0], ro))
+                done += 1
+    return dict(value=done / t_total, unit="queries/s", cores=1, kind="oracle",
+                sample=f"{n_queries} of the {wl.B} decode queries of one ragged step (index "
+                       f"scans of {pos[n_queries - 1] // wl.m:,}-{pos[0] // wl.m:,} entries + "
+                       f"top-{wl.k} + attention each), run {done // n_queries} times over, "
+                       "numpy fp64/int64, 1 thread",
+                seconds=round(t_total, 3)), dict(exact=ok, attn_excess_over_rms=worst)
+
+
+def run_decode_ragged(args, csa, synth, wl, dev):
+    """One step = append each sequence's new token, then index + attend at
+    each sequence's own position (one launch each for the whole batch)."""
+    import torch
+    t_setup = time.time()
+    sets = [ragged_set(csa, synth, wl, dev, seed) for seed in range(args.sets)]
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s: {args.sets} input sets of {wl.name}")
+    pos_max = wl.L - 1
+
+    def append(i):
+        s = sets[i]
+        csa.decode_append(s["kv_new"], s["gate_new"], s["pos"], wl.m, s["stage"],
+                          s["stage_gate"], s["codes"], s["scales"], s["win"])
+
+    def scan(i):
+        s = sets[i]
+        csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
+                       workspace=s["ws"], pos_max=pos_max)
+
+    def select_attend(i):
+        s = sets[i]
+        csa.index_select(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
+                         workspace=s["ws"], pos_max=pos_max)
+        csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, s["pos"],
+                        1.0, s["out"], workspace=s["ws_attn"], pos_max=pos_max)
+
+    def step_fn(i):
+        def f():
+            s = sets[i]
+            append(i)
+            csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
+                           workspace=s["ws"], pos_max=pos_max)
+            csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, s["pos"],
+                            1.0, s["out"], workspace=s["ws_attn"], pos_max=pos_max)
+        return f
+
+    eager = [step_fn(i) for i in range(len(sets))]
+    for f in eager:
+        f()
+    torch.cuda.synchronize()
+    runs = [g.replay for g in capture_graphs(eager)] if args.graph else eager
+    secs = time_steps(runs, args.steps, args.warmup)
+    ms_per_step = secs * 1e3 / args.steps
+    value = wl.B * args.steps / secs
+    log(f"ragged step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s ({timing_name(args)})")
+
+    # dominant kernel: the ragged indexer scan, timed with events on its stream
+    scan_ms = split_event_ms(scan, select_attend, len(sets), args.steps)
+    t_append = split_event_ms(append, None, len(sets), args.steps)
+    pos = wl.positions()
+    scan_bytes = sum((t + 1) // wl.m * wl.Di + wl.Hi * wl.Di + wl.Hi for t in pos)
+    log(f"append {t_append * 1e3:.1f} us; scan {scan_ms * 1e3:.1f} us")
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        eager[0]()
+        torch.cuda.synchronize()
+        cpu, parity = cpu_baseline_ragged(sets[0], wl, min(args.cpu_queries, wl.B),
+                                          args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    return {
+        "metric": "CSA ragged decode queries/sec (append + index + attention) at 590K-1M ctx, "
+                  "1 MI355X",
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.B, "positions": pos, "d": wl.d, "m": wl.m,
+            "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8", "top_k": wl.k, "window": wl.W,
+            "cache": "MXFP4 e2m1 + e8m0/32", "input_sets_rotated": args.sets,
+            "timing": timing_name(args),
+        },
+        "append_us": round(t_append * 1e3, 2),
+        "roofline": {
+            "kernel": "k_idx_scan (ragged indexer key scan)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("k_idx_scan", wl.name),
+            "avg_launch_us": round(scan_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": scan_bytes,
+        },
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+
+
+# --------------------------------------------------------------------------
 # prefill (prefill_128k)
 # --------------------------------------------------------------------------
 
@@ -757,7 +933,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m",
-                    choices=["decode_1m", "decode_32k", "prefill_128k", "hca_reindex_1m"])
+                    choices=["decode_1m", "decode_32k", "prefill_128k", "hca_reindex_1m",
+                             "decode_ragged_1m"])
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--pool-kind", default="entries", choices=["entries", "blocks"],
                     help="hca_reindex_1m: the Full layer's pool is its top-`pool` entries "
@@ -796,6 +973,8 @@ def main():
         rec = run_prefill(args, csa, synth, wl, dev)
     elif args.workload == "hca_reindex_1m":
         rec = run_layers(args, csa, synth, wl, dev)
+    elif args.workload == "decode_ragged_1m":
+        rec = run_decode_ragged(args, csa, synth, wl, dev)
     else:
         rec = run_decode(args, csa, synth, wl, dev)
     head = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"),

@@ -33,7 +33,8 @@ EXPORTED = [
     "csa_dequantize", "csa_index_topk_workspace", "csa_index_topk", "csa_index_scan",
     "csa_index_select", "csa_index_topk_pool_workspace", "csa_index_topk_pool",
     "csa_index_pool_scan", "csa_index_pool_select", "csa_decode_append",
-    "csa_index_topk_ragged", "csa_sparse_attn_ragged", "hca_dense_attn_ragged",
+    "csa_index_topk_ragged", "csa_index_scan_ragged", "csa_index_select_ragged",
+    "csa_sparse_attn_ragged", "hca_dense_attn_ragged",
     "csa_workspace_clear", "csa_attn_workspace", "csa_sparse_attn", "hca_dense_attn",
 ]
 
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
             "csa_decode_append": (I, [P, I64, P, P, I, I, I, P, P, P, P, I64, P, I, P]),
             "csa_index_topk_ragged": (I, [P, P, P, I64, I, I, I, I, I, P, I64, P, I, I, P, P, P,
                                           I64, P]),
+            "csa_index_scan_ragged": (I, [P, P, P, I64, I, I, I, I, I, P, I64, P, I, I, P, P, P,
+                                          I64, P]),
+            "csa_index_select_ragged": (I, [P, P, P, I64, I, I, I, I, I, P, I64, P, I, I, P, P,
+                                            P, I64, P]),
             "csa_sparse_attn_ragged": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, P, I64, F, P,
                                            I, P, P, I64, P]),
             "hca_dense_attn_ragged": (I, [P, P, P, I64, I, P, I, I, I, I, I, I, P, I64, F, P, I,
@@ -240,8 +245,6 @@ def _index_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, out_score=None, ca
     _need(cand, torch.int32, "cand", 3)
     B, T, Hi, Di = q_idx.shape
     pos0, pos = _positions(pos0, pos_max, B, q_idx.device, "index_topk")
-    if pos is not None and fn_name != "csa_index_topk":
-        raise ValueError(f"{fn_name}: per-sequence positions are taken by index_topk only")
     if w.shape != (B, T, Hi) or keys.shape[0] != B or keys.shape[2] != Di:
         raise ValueError("index_topk: inconsistent shapes")
     if out_idx.shape != (B, T, k) or (out_score is not None and out_score.shape != (B, T, k)):
@@ -259,10 +262,10 @@ def _index_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, out_score=None, ca
     ws = workspace.get(need, key=B * T) if isinstance(workspace, Workspace) else workspace
     ws_bytes = 0 if ws is None else ws.numel()
     if pos is not None:
-        _check(lib().csa_index_topk_ragged(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi,
-                                           Di, m, _ptr(pos), pos0, _ptr(cand), C, k,
-                                           _ptr(out_idx), _ptr(out_score), _ptr(ws), ws_bytes,
-                                           _stream()), "csa_index_topk_ragged")
+        fn_name += "_ragged"
+        _check(getattr(lib(), fn_name)(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di,
+                                       m, _ptr(pos), pos0, _ptr(cand), C, k, _ptr(out_idx),
+                                       _ptr(out_score), _ptr(ws), ws_bytes, _stream()), fn_name)
         return
     _check(getattr(lib(), fn_name)(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di, m,
                                    pos0, _ptr(cand), C, k, _ptr(out_idx), _ptr(out_score),

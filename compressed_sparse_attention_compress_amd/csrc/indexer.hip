@@ -210,10 +210,11 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   }
   __syncthreads();
   // the scores leave in one burst of 16-byte stores once every key load is
-  // done (stores issued between loads would be waited on with them)
-  if (threadIdx.x * 8 < SPAN) {
+  // done (stores issued between loads would be waited on with them); entries
+  // at or past N are never read, so whole 8-entry runs past it are not stored
+  const int64_t e0 = wg0 + threadIdx.x * 8;
+  if (threadIdx.x * 8 < SPAN && e0 < N) {
     const int j0 = threadIdx.x * 8;
-    const int64_t e0 = wg0 + j0;
     int v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = e0 + j < N ? ssc[j0 + j] : -1;
@@ -1052,20 +1053,44 @@ extern "C" int csa_index_topk(const int8_t* q_idx, const int8_t* w, const int8_t
   return idx_phase(a, 1);
 }
 
-extern "C" int csa_index_topk_ragged(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
-                                     int64_t blk_cap, int B, int T, int Hi, int Di, int m,
-                                     const int64_t* pos, int64_t pos_max, const int32_t* cand,
-                                     int C, int k, int32_t* out_idx, int32_t* out_score,
-                                     void* workspace, int64_t ws_bytes, hipStream_t stream) {
+static int ragged_phases(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                         int64_t blk_cap, int B, int T, int Hi, int Di, int m,
+                         const int64_t* pos, int64_t pos_max, const int32_t* cand, int C, int k,
+                         int32_t* out_idx, int32_t* out_score, void* workspace,
+                         int64_t ws_bytes, hipStream_t stream, int first, int last) {
   if (B > 0 && T > 0 && !pos) return CSA_ERR_NULL;
   if (pos && !csa_aligned(pos, 8)) return CSA_ERR_ALIGN;
   IdxArgs a{q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos_max, cand, C, k, out_idx, out_score,
             workspace, ws_bytes, stream};
   a.pos = pos;
-  int st = idx_phase(a, 0);
-  if (st != CSA_OK) return st;
-  return idx_phase(a, 1);
+  for (int ph = first; ph <= last; ++ph) {
+    const int st = idx_phase(a, ph);
+    if (st != CSA_OK) return st;
+  }
+  return CSA_OK;
 }
+
+#define CSA_RAGGED_PARAMS                                                                     \
+  const int8_t *q_idx, const int8_t *w, const int8_t *keys, int64_t blk_cap, int B, int T,    \
+      int Hi, int Di, int m, const int64_t *pos, int64_t pos_max, const int32_t *cand, int C,  \
+      int k, int32_t *out_idx, int32_t *out_score, void *workspace, int64_t ws_bytes,          \
+      hipStream_t stream
+#define CSA_RAGGED_ARGS                                                                      \
+  q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos, pos_max, cand, C, k, out_idx, out_score,    \
+      workspace, ws_bytes, stream
+
+extern "C" int csa_index_topk_ragged(CSA_RAGGED_PARAMS) {
+  return ragged_phases(CSA_RAGGED_ARGS, 0, 1);
+}
+extern "C" int csa_index_scan_ragged(CSA_RAGGED_PARAMS) {
+  return ragged_phases(CSA_RAGGED_ARGS, 0, 0);
+}
+extern "C" int csa_index_select_ragged(CSA_RAGGED_PARAMS) {
+  return ragged_phases(CSA_RAGGED_ARGS, 1, 1);
+}
+
+#undef CSA_RAGGED_ARGS
+#undef CSA_RAGGED_PARAMS
 
 static int pool_phases(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
                        int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0, int k,

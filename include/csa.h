@@ -186,6 +186,19 @@ int csa_index_topk_ragged(const int8_t* q_idx, const int8_t* w, const int8_t* ke
                           const int32_t* cand, int C, int k,
                           int32_t* out_idx, int32_t* out_score,
                           void* workspace, int64_t ws_bytes, hipStream_t stream);
+/* Its two launches, as csa_index_scan / csa_index_select below. */
+int csa_index_scan_ragged(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                          int64_t blk_cap, int B, int T, int Hi, int Di, int m,
+                          const int64_t* pos, int64_t pos_max,
+                          const int32_t* cand, int C, int k,
+                          int32_t* out_idx, int32_t* out_score,
+                          void* workspace, int64_t ws_bytes, hipStream_t stream);
+int csa_index_select_ragged(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                            int64_t blk_cap, int B, int T, int Hi, int Di, int m,
+                            const int64_t* pos, int64_t pos_max,
+                            const int32_t* cand, int C, int k,
+                            int32_t* out_idx, int32_t* out_score,
+                            void* workspace, int64_t ws_bytes, hipStream_t stream);
 
 /* The two launches csa_index_topk makes, exposed so a caller can place events
  * or other work between them: csa_index_topk == csa_index_scan followed by

@@ -44,6 +44,11 @@ class Workload:
     m_hca: int = 128  # block size of the dense heavily-compressed cache
     pool: int = 0     # candidate pool size for reindex layers (0 = none)
     chunk: int = 0    # prefill chunk length (0 = not chunked)
+    len_step: int = 0  # ragged batches: sequence b decodes at position L - 1 - b * len_step
+
+    def positions(self) -> list:
+        """Decode position of each sequence (all L - 1 unless ragged)."""
+        return [self.L - 1 - b * self.len_step for b in range(self.B)]
 
     @property
     def n_blocks(self) -> int:
@@ -59,6 +64,8 @@ WORKLOADS = {
                           k=1024),
     "prefill_128k": Workload("prefill_128k", B=1, L=131072, d=512, m=4, H=64, Hi=8, Di=64,
                              k=512, T=8192, Wcap=16384, chunk=8192),
+    "decode_ragged_1m": Workload("decode_ragged_1m", B=8, L=1 << 20, d=512, m=4, H=64, Hi=8,
+                                 Di=64, k=1024, len_step=65_543),
     "hca_reindex_1m": Workload("hca_reindex_1m", B=16, L=1 << 20, d=512, m=4, H=64, Hi=8,
                                Di=64, k=512, pool=4096, m_hca=128),
 }
@@ -114,16 +121,18 @@ def latent_range(wl: Workload, b: int, t0: int, t1: int, device, seed: int = 0,
     return torch.cat(parts, 0)
 
 
-def window_ring(wl: Workload, t_last: int, device, seed: int = 0, layer: str = "main",
+def window_ring(wl: Workload, t_last, device, seed: int = 0, layer: str = "main",
                 span: int | None = None):
     """bfloat16 ring [B][Wcap][d] holding tokens max(0, t_last-span+1) .. t_last
-    in slot p % Wcap (span defaults to Wcap)."""
+    in slot p % Wcap (span defaults to Wcap); t_last is one position for every
+    sequence or a list of per-sequence positions."""
     span = wl.Wcap if span is None else span
     ring = torch.zeros(wl.B, wl.Wcap, wl.d, device=device, dtype=torch.bfloat16)
-    t0 = max(0, t_last - span + 1)
-    pos = torch.arange(t0, t_last + 1, device=device) % wl.Wcap
     for b in range(wl.B):
-        ring[b, pos] = latent_range(wl, b, t0, t_last + 1, device, seed, layer).to(torch.bfloat16)
+        tl = t_last[b] if isinstance(t_last, (list, tuple)) else t_last
+        t0 = max(0, tl - span + 1)
+        pos = torch.arange(t0, tl + 1, device=device) % wl.Wcap
+        ring[b, pos] = latent_range(wl, b, t0, tl + 1, device, seed, layer).to(torch.bfloat16)
     return ring
 
 

@@ -117,7 +117,7 @@ def test_decode_append_block_cap_and_skip():
 
 # ---------------------------------------------------------- ragged index ----
 
-def _ragged_index_case(T, Hi, Di, m, pos, pos_max, k, blk_cap, seed, cand_C=0):
+def _ragged_index_case(T, Hi, Di, m, pos, pos_max, k, blk_cap, seed, cand_C=0, phases=False):
     B = len(pos)
     g = gen(seed, "ragged-idx", B, T)
     q = torch.randint(-8, 8, (B, T, Hi, Di), generator=g, device=DEV, dtype=torch.int8)
@@ -130,7 +130,11 @@ def _ragged_index_case(T, Hi, Di, m, pos, pos_max, k, blk_cap, seed, cand_C=0):
     oi = torch.full((B, T, k), -7, device=DEV, dtype=torch.int32)
     os_ = torch.full((B, T, k), -7, device=DEV, dtype=torch.int32)
     pt = torch.tensor(pos, dtype=torch.int64, device=DEV)
-    csa.index_topk(q, w, keys, m, pt, k, oi, os_, cand=cand, pos_max=pos_max)
+    if phases:
+        csa.index_scan(q, w, keys, m, pt, k, oi, os_, cand=cand, pos_max=pos_max)
+        csa.index_select(q, w, keys, m, pt, k, oi, os_, cand=cand, pos_max=pos_max)
+    else:
+        csa.index_topk(q, w, keys, m, pt, k, oi, os_, cand=cand, pos_max=pos_max)
     torch.cuda.synchronize()
     qn, wn, kn = q.cpu().numpy(), w.cpu().numpy(), keys.cpu().numpy()
     oin, osn = oi.cpu().numpy(), os_.cpu().numpy()
@@ -151,6 +155,8 @@ def test_index_ragged_decode():
                        4 * 20000 - 1, 512, 20003, seed=73)
     _ragged_index_case(2, 8, 64, 4, [4 * 9000, 5, 4 * 2048 - 2], 4 * 9000, 256, 9003, seed=74,
                        cand_C=3000)
+    _ragged_index_case(1, 8, 64, 4, [4 * 30000 - 1, 4 * 7000 + 1, 4 * 29000], 4 * 30000 - 1, 1024,
+                       30000, seed=81, phases=True)
 
 
 def test_index_ragged_prefill():
