@@ -187,6 +187,88 @@ def dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return np.ldexp(val.reshape(nb, d // GROUP, GROUP), e[:, :, None]).reshape(nb, d)
 
 
+# --------------------------------------------------------------------------
+# f3: the E4M3-per-16 scale variant ([PODCAST] cue 16)
+# --------------------------------------------------------------------------
+
+GROUP16 = 16           # elements sharing one E4M3 scale (reading A25)
+E4M3_MAX_BYTE = 0x7E   # 448, the largest finite OCP E4M3 value
+E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def e4m3_value(byte) -> np.ndarray:
+    """Value of a non-negative OCP FP8 E4M3 byte (0 .. 0x7E): exponent field
+    bits 6..3 with bias 7, mantissa bits 2..0; exponent field 0 encodes the
+    subnormals m * 2**-9. Returns float64 (exact)."""
+    b = np.asarray(byte, dtype=np.int64)
+    e = (b >> 3) & 0xF
+    mnt = b & 7
+    return np.where(e == 0, np.ldexp(mnt.astype(np.float64), -9),
+                    np.ldexp((8 + mnt).astype(np.float64), e - 10))
+
+
+def e4m3_scale_byte(amax) -> np.ndarray:
+    """Scale byte of a 16-element group: the E4M3 value nearest to amax / 6
+    (6 = the largest E2M1 magnitude), halfway cases to the even byte, values
+    past 448 saturating to 448 (reading A25). Decided without dividing: amax
+    is compared with 6 v (the candidates) and with 3 (v_lo + v_hi) (their
+    midpoint times 6), products that are exact in float64."""
+    amax = np.asarray(amax, dtype=np.float64)
+    vals = e4m3_value(np.arange(E4M3_MAX_BYTE + 1))          # ascending
+    i = np.searchsorted(6.0 * vals, amax, side="right") - 1  # 6 v_i <= amax
+    i = np.clip(i, 0, E4M3_MAX_BYTE)
+    j = np.minimum(i + 1, E4M3_MAX_BYTE)
+    mid6 = 3.0 * (vals[i] + vals[j])
+    up = (i < E4M3_MAX_BYTE) & ((amax > mid6) | ((amax == mid6) & (i % 2 == 1)))
+    return (i + up).astype(np.uint8)
+
+
+def e2m1_magnitude_code_scaled(a: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """e2m1_magnitude_code(a / s) decided without dividing: a is compared
+    with s times each midpoint of the E2M1 grid (exact products, as s has at
+    most 4 significant bits); s == 0 gives code 0."""
+    a = np.asarray(a, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    # a tie at midpoint k goes to the even code: down (a > m) between codes
+    # 2j and 2j + 1, up (a >= m) between codes 2j + 1 and 2j + 2
+    mag = np.zeros(np.broadcast(a, s).shape, dtype=np.int64)
+    for k, mid in enumerate(E2M1_MIDPOINTS):
+        mag += (a > s * mid) if k % 2 == 0 else (a >= s * mid)
+    return np.where(s == 0.0, 0, mag)
+
+
+def quantize_rows_e4m3(p: np.ndarray):
+    """FP4 with one E4M3 scale per 16 channels (no global scale; readings A25,
+    A4 for nibble order and signed zero). Returns (codes uint8 [nb][d/2],
+    scales uint8 [nb][d/16])."""
+    p = np.asarray(p, dtype=np.float64)
+    nb, d = p.shape
+    g = p.reshape(nb, d // GROUP16, GROUP16)
+    sb = e4m3_scale_byte(np.abs(g).max(axis=2))
+    mag = e2m1_magnitude_code_scaled(np.abs(g), e4m3_value(sb)[:, :, None])
+    code = ((np.signbit(g).astype(np.int64) << 3) | mag).reshape(nb, d)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sb
+
+
+def dequantize_rows_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """value = (-1)**s * E2M1[mag] * e4m3_value(scale), float64 [nb][d]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    nb, half = codes.shape
+    d = 2 * half
+    nib = np.empty((nb, d), dtype=np.int64)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    mag = np.array(E2M1_MAGNITUDES)[nib & 7]
+    val = np.where(nib & 8, -mag, mag).reshape(nb, d // GROUP16, GROUP16)
+    return (val * e4m3_value(scales)[:, :, None]).reshape(nb, d)
+
+
+def compress_quantize_e4m3(kv: np.ndarray, gate: np.ndarray, m: int):
+    """a1 + the E4M3-per-16 quantisation for one sequence."""
+    return quantize_rows_e4m3(pool_blocks(kv, gate, m))
+
+
 def compress_quantize(kv: np.ndarray, gate: np.ndarray, m: int):
     """a1 + a2 for one sequence whose first token starts block 0."""
     return quantize_rows(pool_blocks(kv, gate, m))
@@ -337,34 +419,36 @@ def window_positions(t: int, W: int) -> np.ndarray:
     return np.arange(max(0, t - W + 1), t + 1)
 
 
-def gather_rows(codes, scales, blocks, win, Wcap: int, t: int, W: int) -> np.ndarray:
+def gather_rows(codes, scales, blocks, win, Wcap: int, t: int, W: int,
+                fmt: str = "e8m0") -> np.ndarray:
     """Rows attended by the query at t: the dequantised entries of `blocks`
     followed by the bf16 window tokens (ring slot p % Wcap), all under one
-    softmax (readings A12, A17)."""
+    softmax (readings A12, A17). fmt "e4m3" reads E4M3-per-16 scales."""
     blocks = np.asarray(blocks, dtype=np.int64)
     blocks = blocks[blocks >= 0]
-    ent = dequantize_rows(np.asarray(codes)[blocks], np.asarray(scales)[blocks])
+    deq = dequantize_rows_e4m3 if fmt == "e4m3" else dequantize_rows
+    ent = deq(np.asarray(codes)[blocks], np.asarray(scales)[blocks])
     pos = window_positions(t, W)
     wr = bf16_to_f64(np.asarray(win)[pos % Wcap])
     return np.concatenate([ent, wr], axis=0)
 
 
 def sparse_attn(q_bf16, codes, scales, idx, win, Wcap: int, W: int, t: int,
-                softmax_scale: float):
+                softmax_scale: float, fmt: str = "e8m0"):
     """Compressed sparse attention of one query: the selected entries plus
     the window ([NOTES4] s.1; [PODCAST] cues 12 and 16). q_bf16: [H][d]
     uint16. Returns (o [H][d], lse [H]) float64."""
-    rows = gather_rows(codes, scales, idx, win, Wcap, t, W)
+    rows = gather_rows(codes, scales, idx, win, Wcap, t, W, fmt)
     return attend(bf16_to_f64(q_bf16), rows, softmax_scale)
 
 
 def hca_dense_attn(q_bf16, codes, scales, m: int, win, Wcap: int, W: int, t: int,
-                   softmax_scale: float):
+                   softmax_scale: float, fmt: str = "e8m0"):
     """Heavily compressed attention: every visible entry of an m-token cache
     (m up to 128) plus the window, no indexer ([NOTES4] s.1; [RASCHKA] Data)."""
     nv = min(n_visible(t, m), len(codes))
     return sparse_attn(q_bf16, codes, scales, np.arange(nv), win, Wcap, W, t,
-                       softmax_scale)
+                       softmax_scale, fmt)
 
 
 # --------------------------------------------------------------------------
@@ -417,5 +501,6 @@ READINGS = {
     "A17": "window rows are bf16",
     "A22": "blockwise pool: groups of `group` consecutive compressed entries (8 per [PODCAST] cue 14); group score = max over its visible entries",
     "A23": "blockwise pool keeps n_keep groups (about 2000 per cue 14), ties to the lower group; the pool lists their visible entries ascending, -1 elsewhere",
+    "A25": "E4M3 variant: one OCP E4M3 scale per 16 elements, no global scale; scale = the E4M3 value nearest amax/6 (ties to the even byte, saturating at 448); elements to the nearest E2M1 multiple of the scale (ties to even, saturating at 6); a zero scale gives zero codes",
     "A24": "decode append: a block's entry is written once its m-th token arrives, from the block's m float32 tokens; each token also enters the bf16 ring at slot p % Wcap; sequences of a batch may sit at different positions",
 }

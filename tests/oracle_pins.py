@@ -473,6 +473,110 @@ def pin_attention_invariants(O):
     assert np.array_equal(rows, exact)
 
 
+# ------------------------------------------------------- E4M3-per-16 ----
+
+def _e4m3_torch(byte):
+    return torch.tensor(np.asarray(byte, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_e4m3_values(O):
+    """Hand-derived values, then every finite non-negative byte against
+    torch's float8_e4m3fn decoding."""
+    v = lambda b: float(O.e4m3_value(b))
+    assert v(0x00) == 0.0 and v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9
+    assert v(0x08) == 2.0 ** -6 and v(0x38) == 1.0 and v(0x3C) == 1.5 and v(0x7E) == 448.0
+    b = np.arange(0x7F)
+    assert np.array_equal(O.e4m3_value(b), _e4m3_torch(b))
+    assert np.all(np.diff(O.e4m3_value(b)) > 0)
+
+
+def pin_e4m3_scale_rule(O):
+    """The scale byte is the E4M3 rounding of amax / 6: against torch's
+    float -> float8_e4m3fn conversion (round to nearest even) away from ties,
+    at constructed exact ties (to the even byte), and at the ends."""
+    rng = np.random.default_rng(22)
+    amax = np.abs(rng.standard_normal(20000)) * np.exp2(rng.integers(-12, 12, 20000))
+    amax = amax[(amax / 6 < 440) & (amax / 6 > 2.0 ** -8)]
+    ref = torch.from_numpy(amax / 6).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_scale_byte(amax)
+    vals = O.e4m3_value(np.arange(0x7F))
+    mids = 3.0 * (vals[:-1] + vals[1:])            # 6 x every midpoint
+    near = np.isin(amax, mids)
+    assert np.array_equal(got[~near], ref[~near])
+    i = np.arange(0x7E)
+    assert np.array_equal(O.e4m3_scale_byte(mids), np.where(i % 2 == 1, i + 1, i))
+    assert np.array_equal(O.e4m3_scale_byte(np.nextafter(mids, np.inf)), i + 1)
+    assert np.array_equal(O.e4m3_scale_byte(np.nextafter(mids, 0)), i)
+    assert int(O.e4m3_scale_byte(0.0)) == 0 and int(O.e4m3_scale_byte(6 * 448.0)) == 0x7E
+    assert int(O.e4m3_scale_byte(1e30)) == 0x7E
+
+
+def pin_e4m3_quantize_brute_force(O):
+    """Each element is the nearest signed E2M1 multiple of its group's scale
+    (ties to the even code, saturating at 6 s; a zero scale gives zero codes):
+    brute force over the 8 magnitudes, with exact ties planted."""
+    rng = np.random.default_rng(23)
+    nb, d = 40, 64
+    p = rng.standard_normal((nb, d)) * np.exp2(rng.integers(-8, 8, (nb, 1)))
+    p[0, :16] = 0.0
+    codes, sb = O.quantize_rows_e4m3(p)
+    s = O.e4m3_value(sb)
+    assert sb.shape == (nb, d // 16) and sb[0, 0] == 0
+    # plant exact midpoints: in row 1 group 0, element c = s * midpoint
+    s10 = s[1, 0]
+    q = p.copy()
+    for c, mid in enumerate(O.E2M1_MIDPOINTS):
+        q[1, 1 + c] = s10 * mid
+    q[1, 0] = np.abs(p[1, :16]).max() * np.sign(p[1, 0] or 1.0)  # keep the group max
+    codes2, sb2 = O.quantize_rows_e4m3(q)
+    grid = np.array(O.E2M1_MAGNITUDES)
+    for pp, cc, ss in ((p, codes, sb), (q, codes2, sb2)):
+        nib = np.empty((nb, d), np.int64)
+        nib[:, 0::2], nib[:, 1::2] = cc & 15, cc >> 4
+        sc = np.repeat(O.e4m3_value(ss), 16, axis=1)
+        for r in range(nb):
+            for c in range(d):
+                a, sv = abs(pp[r, c]), sc[r, c]
+                if sv == 0:
+                    want = 0
+                else:
+                    dist = [abs(min(a, 6 * sv) - g * sv) for g in grid]
+                    best = min(dist)
+                    cand = [k for k in range(8) if dist[k] == best]
+                    even = [k for k in cand if k % 2 == 0]
+                    want = (even or cand)[0]
+                assert nib[r, c] & 7 == want, (r, c)
+                assert (nib[r, c] >> 3) == int(np.signbit(pp[r, c])), (r, c)
+    # the planted ties went to the even code
+    assert [int(x) for x in (codes2[1, 0] >> 4, codes2[1, 1] & 15)] == [0, 2]
+
+
+def pin_e4m3_dequantize(O):
+    """Dequantised values are the codes times the E4M3 scale, and quantising
+    them again with the same scales reproduces the codes (the grid is a
+    fixed point); the group maximum is within half a grid step of its value."""
+    rng = np.random.default_rng(24)
+    p = rng.standard_normal((30, 128))
+    codes, sb = O.quantize_rows_e4m3(p)
+    x = O.dequantize_rows_e4m3(codes, sb)
+    ref_scale = np.repeat(_e4m3_torch(sb), 16, axis=1)
+    grid = np.array(O.E2M1_MAGNITUDES)
+    nib = np.empty(p.shape, np.int64)
+    nib[:, 0::2], nib[:, 1::2] = codes & 15, codes >> 4
+    assert np.array_equal(x, np.where(nib & 8, -1, 1) * grid[nib & 7] * ref_scale)
+    c2 = (O.e2m1_magnitude_code_scaled(np.abs(x).reshape(30, 8, 16),
+                                       O.e4m3_value(sb)[:, :, None]).reshape(30, 128))
+    assert np.array_equal(c2, nib & 7)
+    g = np.abs(p).reshape(30, 8, 16)
+    gm = g.max(axis=2)
+    xm = np.abs(x).reshape(30, 8, 16)[np.arange(30)[:, None], np.arange(8)[None], g.argmax(axis=2)]
+    assert np.all(np.abs(gm - xm) <= O.e4m3_value(sb) * 1.0 + 1e-300)
+    # attention reads the E4M3 rows when asked to
+    win = np.zeros((4, 128), np.uint16)
+    rows = O.gather_rows(codes, sb, np.array([5, -1, 2]), win, 4, 3, 2, fmt="e4m3")
+    assert np.array_equal(rows[:2], x[[5, 2]]) and rows.shape == (4, 128)
+
+
 # --------------------------------------------------------- decode append ----
 
 def pin_bf16_rounding(O):

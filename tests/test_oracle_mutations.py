@@ -34,6 +34,8 @@ orig_win = O.window_positions
 orig_nvis = O.n_visible
 orig_gather = O.gather_rows
 orig_bf16 = O.f32_to_bf16_bits
+orig_sbyte = O.e4m3_scale_byte
+orig_quant16 = O.quantize_rows_e4m3
 orig_append = O.cache_after_appends
 
 
@@ -200,6 +202,35 @@ def m_append_ring_short(kv, gate, m, n_tok, Wcap):
     return c, s, r
 
 
+def m_e4m3_scale_truncated(amax):
+    vals = O.e4m3_value(np.arange(0x7F))
+    i = np.searchsorted(6.0 * vals, np.asarray(amax, np.float64), side="right") - 1
+    return np.clip(i, 0, 0x7E).astype(np.uint8)
+
+
+def m_e4m3_ties_odd(amax):
+    b = orig_sbyte(amax).astype(np.int64)
+    vals = O.e4m3_value(np.arange(0x7F))
+    mid6 = 3.0 * (vals[np.maximum(b - 1, 0)] + vals[b])
+    tie = (np.asarray(amax) == mid6) & (b > 0)
+    return np.where(tie, b - 1, b).astype(np.uint8)
+
+
+def m_e4m3_over_four(amax):
+    return orig_sbyte(np.asarray(amax, np.float64) * 1.5)
+
+
+def m_e4m3_group32(p):
+    p = np.asarray(p, np.float64)
+    nb, d = p.shape
+    g = p.reshape(nb, d // 32, 32)
+    sb = np.repeat(orig_sbyte(np.abs(g).max(axis=2)), 2, axis=1)
+    mag = O.e2m1_magnitude_code_scaled(np.abs(p.reshape(nb, d // 16, 16)),
+                                       O.e4m3_value(sb)[:, :, None])
+    code = ((np.signbit(p).astype(np.int64) << 3) | mag.reshape(nb, d))
+    return (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8), sb
+
+
 MUTANTS = {
     "scale exponent off by one": {"scale_exponent": m_scale_off_by_one},
     "scale exponent not clamped": {"scale_exponent": m_no_clamp},
@@ -229,6 +260,10 @@ MUTANTS = {
     "append ring slot off by one": {"cache_after_appends": m_append_ring_shift},
     "append writes the partial block": {"cache_after_appends": m_append_partial_block},
     "append ring drops its oldest token": {"cache_after_appends": m_append_ring_short},
+    "e4m3 scale truncated": {"e4m3_scale_byte": m_e4m3_scale_truncated},
+    "e4m3 scale ties to odd": {"e4m3_scale_byte": m_e4m3_ties_odd},
+    "e4m3 scale from amax / 4": {"e4m3_scale_byte": m_e4m3_over_four},
+    "e4m3 scale shared by 32": {"quantize_rows_e4m3": m_e4m3_group32},
 }
 
 
