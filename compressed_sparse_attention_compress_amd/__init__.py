@@ -24,6 +24,9 @@ __all__ = [
 ]
 
 BF16, F32, F16 = 0, 1, 2
+# scale formats of the FP4 cache: E8M0 per 32 channels, E4M3 per 16 channels
+SCALE_FMT = {"e8m0": 0, "e4m3": 1}
+SCALE_GROUP = {"e8m0": 32, "e4m3": 16}
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa.so")
 
@@ -57,9 +60,9 @@ def lib() -> ctypes.CDLL:
         sig = {
             "csa_status_string": (ctypes.c_char_p, [I]),
             "csa_version": (I, []),
-            "csa_cache_bytes": (I64, [I64, I, I]),
-            "csa_compress_quantize": (I, [P, I64, P, I, I64, I64, I, I, P, P, I64, P]),
-            "csa_dequantize": (I, [P, P, I64, I, I64, I64, I, P, I, P]),
+            "csa_cache_bytes": (I64, [I64, I, I, I]),
+            "csa_compress_quantize": (I, [P, I64, P, I, I64, I64, I, I, P, P, I64, I, P]),
+            "csa_dequantize": (I, [P, P, I64, I, I64, I64, I, P, I, I, P]),
             "csa_index_topk_workspace": (I64, [I, I, I64, I, I]),
             "csa_index_topk": (I, [P, P, P, I64, I, I, I, I, I, I64, P, I, I, P, P, P, I64, P]),
             "csa_index_scan": (I, [P, P, P, I64, I, I, I, I, I, I64, P, I, I, P, P, P, I64, P]),
@@ -71,7 +74,7 @@ def lib() -> ctypes.CDLL:
                                         I64, P]),
             "csa_index_pool_select": (I, [P, P, P, I64, I, I, I, I, I, I64, I, P, P, I, I, P, P,
                                           I64, P]),
-            "csa_decode_append": (I, [P, I64, P, P, I, I, I, P, P, P, P, I64, P, I, P]),
+            "csa_decode_append": (I, [P, I64, P, P, I, I, I, P, P, P, P, I64, P, I, I, P]),
             "csa_index_topk_ragged": (I, [P, P, P, I64, I, I, I, I, I, P, I64, P, I, I, P, P, P,
                                           I64, P]),
             "csa_index_scan_ragged": (I, [P, P, P, I64, I, I, I, I, I, P, I64, P, I, I, P, P, P,
@@ -79,15 +82,15 @@ def lib() -> ctypes.CDLL:
             "csa_index_select_ragged": (I, [P, P, P, I64, I, I, I, I, I, P, I64, P, I, I, P, P,
                                             P, I64, P]),
             "csa_sparse_attn_ragged": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, P, I64, F, P,
-                                           I, P, P, I64, P]),
+                                           I, P, P, I64, I, P]),
             "hca_dense_attn_ragged": (I, [P, P, P, I64, I, P, I, I, I, I, I, I, P, I64, F, P, I,
-                                          P, P, I64, P]),
+                                          P, P, I64, I, P]),
             "csa_workspace_clear": (I, [P, I64, P]),
             "csa_attn_workspace": (I64, [I, I, I, I, I64]),
             "csa_sparse_attn": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, I64, F, P, I, P,
-                                    P, I64, P]),
+                                    P, I64, I, P]),
             "hca_dense_attn": (I, [P, P, P, I64, I, P, I, I, I, I, I, I, I64, F, P, I, P, P,
-                                   I64, P]),
+                                   I64, I, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -124,8 +127,19 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
 
 
-def cache_bytes(n_tokens: int, d: int, m: int) -> int:
-    return lib().csa_cache_bytes(n_tokens, d, m)
+def _fmt_code(fmt):
+    if fmt not in SCALE_FMT:
+        raise ValueError(f"unknown scale format {fmt!r} (e8m0 or e4m3)")
+    return SCALE_FMT[fmt]
+
+
+def _check_scales(scales, codes, fmt, what):
+    if scales.shape[:2] != codes.shape[:2] or scales.shape[2] * SCALE_GROUP[fmt] != codes.shape[2] * 2:
+        raise ValueError(f"{what}: scales must be [B][blk_cap][d/{SCALE_GROUP[fmt]}] for {fmt}")
+
+
+def cache_bytes(n_tokens: int, d: int, m: int, fmt: str = "e8m0") -> int:
+    return lib().csa_cache_bytes(n_tokens, d, m, _fmt_code(fmt))
 
 
 class Workspace:
@@ -162,26 +176,26 @@ def _default_ws(device):
     return _DEFAULT_WS[key]
 
 
-def compress_quantize(kv, gate, tok0: int, m: int, codes, scales):
+def compress_quantize(kv, gate, tok0: int, m: int, codes, scales, fmt: str = "e8m0"):
     """kv float32 [B][n_tok][kv_ld] (d = codes.shape[2]*2 columns used),
     gate float32 [B][n_tok], codes uint8 [B][blk_cap][d/2], scales uint8
-    [B][blk_cap][d/32]."""
+    [B][blk_cap][d/32] (fmt "e8m0") or [B][blk_cap][d/16] (fmt "e4m3")."""
     _need(kv, torch.float32, "kv", 3)
     _need(gate, torch.float32, "gate", 2)
     _need(codes, torch.uint8, "codes", 3)
     _need(scales, torch.uint8, "scales", 3)
     B, n_tok, ld = kv.shape
     d = codes.shape[2] * 2
-    if gate.shape != (B, n_tok) or codes.shape[0] != B or scales.shape[:2] != codes.shape[:2]:
+    if gate.shape != (B, n_tok) or codes.shape[0] != B:
         raise ValueError("compress_quantize: inconsistent shapes")
-    if scales.shape[2] * 32 != d:
-        raise ValueError("compress_quantize: scales width must be d/32")
+    _check_scales(scales, codes, fmt, "compress_quantize")
     _check(lib().csa_compress_quantize(_ptr(kv), ld, _ptr(gate), B, tok0, n_tok, d, m,
-                                       _ptr(codes), _ptr(scales), codes.shape[1], _stream()),
-           "csa_compress_quantize")
+                                       _ptr(codes), _ptr(scales), codes.shape[1], _fmt_code(fmt),
+                                       _stream()), "csa_compress_quantize")
 
 
-def decode_append(kv, gate, pos, m: int, stage, stage_gate, codes, scales, win):
+def decode_append(kv, gate, pos, m: int, stage, stage_gate, codes, scales, win,
+                  fmt: str = "e8m0"):
     """One new token per sequence at its own position; see csa_decode_append.
     kv float32 [B][kv_ld] (d = codes.shape[2]*2 columns used), gate float32
     [B], pos int64 [B] (device; < 0 skips a sequence), stage float32
@@ -198,24 +212,26 @@ def decode_append(kv, gate, pos, m: int, stage, stage_gate, codes, scales, win):
     d = codes.shape[2] * 2
     if (gate.shape != (B,) or pos.shape != (B,) or stage.shape != (B, m, d)
             or stage_gate.shape != (B, m) or codes.shape[0] != B
-            or scales.shape != (B, codes.shape[1], d // 32) or win.shape[0] != B
-            or win.shape[2] != d):
+            or win.shape[0] != B or win.shape[2] != d):
         raise ValueError("decode_append: inconsistent shapes")
+    _check_scales(scales, codes, fmt, "decode_append")
     _check(lib().csa_decode_append(_ptr(kv), ld, _ptr(gate), _ptr(pos), B, d, m, _ptr(stage),
                                    _ptr(stage_gate), _ptr(codes), _ptr(scales), codes.shape[1],
-                                   _ptr(win), win.shape[1], _stream()), "csa_decode_append")
+                                   _ptr(win), win.shape[1], _fmt_code(fmt), _stream()),
+           "csa_decode_append")
 
 
-def dequantize(codes, scales, blk0: int, n_blk: int, out):
+def dequantize(codes, scales, blk0: int, n_blk: int, out, fmt: str = "e8m0"):
     _need(codes, torch.uint8, "codes", 3)
     _need(scales, torch.uint8, "scales", 3)
+    _check_scales(scales, codes, fmt, "dequantize")
     B, cap, half = codes.shape
     dt = {torch.bfloat16: BF16, torch.float32: F32, torch.float16: F16}[out.dtype]
     _need(out, out.dtype, "out", 3)
     if out.shape != (B, n_blk, 2 * half):
         raise ValueError("dequantize: out must be [B][n_blk][d]")
     _check(lib().csa_dequantize(_ptr(codes), _ptr(scales), cap, B, blk0, n_blk, 2 * half,
-                                _ptr(out), dt, _stream()), "csa_dequantize")
+                                _ptr(out), dt, _fmt_code(fmt), _stream()), "csa_dequantize")
 
 
 def index_topk_workspace(B, T, n_max, k, cand_given=False) -> int:
@@ -342,7 +358,7 @@ def attn_workspace(B, T, H, d, n_slots) -> int:
     return lib().csa_attn_workspace(B, T, H, d, n_slots)
 
 
-def _attn_common(q, codes, scales, win, out, lse):
+def _attn_common(q, codes, scales, win, out, lse, fmt):
     _need(q, torch.bfloat16, "q", 4)
     _need(codes, torch.uint8, "codes", 3)
     _need(scales, torch.uint8, "scales", 3)
@@ -354,19 +370,20 @@ def _attn_common(q, codes, scales, win, out, lse):
     B, T, H, d = q.shape
     if out.shape != q.shape or win.shape[0] != B or win.shape[2] != d:
         raise ValueError("attention: inconsistent shapes")
-    if codes.shape[0] != B or codes.shape[2] * 2 != d or scales.shape[:2] != codes.shape[:2]:
+    if codes.shape[0] != B or codes.shape[2] * 2 != d:
         raise ValueError("attention: cache shape mismatch")
+    _check_scales(scales, codes, fmt, "attention")
     if lse is not None and lse.shape != (B, T, H):
         raise ValueError("lse must be [B][T][H]")
     return B, T, H, d, (BF16 if out.dtype == torch.bfloat16 else F32)
 
 
 def sparse_attn(q, codes, scales, idx, win, W, pos0, softmax_scale, out, lse=None,
-                workspace=None, pos_max=None):
+                workspace=None, pos_max=None, fmt: str = "e8m0"):
     """Attention over the idx-selected entries plus the window; see
     csa_sparse_attn (csa_sparse_attn_ragged when pos0 is an int64 [B] tensor
     of per-sequence positions, bounded by pos_max)."""
-    B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse)
+    B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse, fmt)
     pos0, pos = _positions(pos0, pos_max, B, q.device, "sparse_attn")
     _need(idx, torch.int32, "idx", 3)
     k = idx.shape[2]
@@ -381,21 +398,21 @@ def sparse_attn(q, codes, scales, idx, win, W, pos0, softmax_scale, out, lse=Non
         _check(lib().csa_sparse_attn_ragged(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1],
                                             _ptr(idx), k, _ptr(win), win.shape[1], W, B, T, H, d,
                                             _ptr(pos), pos0, float(softmax_scale), _ptr(out), dt,
-                                            _ptr(lse), _ptr(ws), ws_bytes, _stream()),
-               "csa_sparse_attn_ragged")
+                                            _ptr(lse), _ptr(ws), ws_bytes, _fmt_code(fmt),
+                                            _stream()), "csa_sparse_attn_ragged")
         return
     _check(lib().csa_sparse_attn(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1], _ptr(idx), k,
                                  _ptr(win), win.shape[1], W, B, T, H, d, pos0,
                                  float(softmax_scale), _ptr(out), dt, _ptr(lse), _ptr(ws),
-                                 ws_bytes, _stream()), "csa_sparse_attn")
+                                 ws_bytes, _fmt_code(fmt), _stream()), "csa_sparse_attn")
 
 
 def hca_dense_attn(q, codes, scales, m, win, W, pos0, softmax_scale, out, lse=None,
-                   workspace=None, pos_max=None):
+                   workspace=None, pos_max=None, fmt: str = "e8m0"):
     """Attention over every visible entry of an m-token cache plus the window
     (hca_dense_attn_ragged when pos0 is an int64 [B] tensor, bounded by
     pos_max)."""
-    B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse)
+    B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse, fmt)
     pos0, pos = _positions(pos0, pos_max, B, q.device, "hca_dense_attn")
     n_slots = min(codes.shape[1], (pos0 + T) // m) + W
     need = attn_workspace(B, T, H, d, n_slots)
@@ -407,10 +424,10 @@ def hca_dense_attn(q, codes, scales, m, win, W, pos0, softmax_scale, out, lse=No
         _check(lib().hca_dense_attn_ragged(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1], m,
                                            _ptr(win), win.shape[1], W, B, T, H, d, _ptr(pos),
                                            pos0, float(softmax_scale), _ptr(out), dt, _ptr(lse),
-                                           _ptr(ws), ws_bytes, _stream()),
+                                           _ptr(ws), ws_bytes, _fmt_code(fmt), _stream()),
                "hca_dense_attn_ragged")
         return
     _check(lib().hca_dense_attn(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1], m, _ptr(win),
                                 win.shape[1], W, B, T, H, d, pos0, float(softmax_scale),
-                                _ptr(out), dt, _ptr(lse), _ptr(ws), ws_bytes, _stream()),
-           "hca_dense_attn")
+                                _ptr(out), dt, _ptr(lse), _ptr(ws), ws_bytes, _fmt_code(fmt),
+                                _stream()), "hca_dense_attn")

@@ -42,7 +42,7 @@ struct RawSlots {
   uint4 lo[4], hi[4];
 };
 
-template <int D, int NW, bool DENSE>
+template <int D, int NW, bool DENSE, int FMT>
 __global__ __launch_bounds__(NW * 128) void k_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t blk_cap, const int32_t* __restrict__ idx, int k,
@@ -110,7 +110,9 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
   float m_run = -INFINITY, l_run = 0.f;
 
   const uint8_t* cbase = codes + (int64_t)b * blk_cap * (D / 2);
-  const uint8_t* sbase = scales + (int64_t)b * blk_cap * (D / 32);
+  constexpr bool E4 = FMT == CSA_SCALE_E4M3_16;
+  constexpr int SPE = E4 ? D / 16 : D / 32;  // scale bytes per entry
+  const uint8_t* sbase = scales + (int64_t)b * blk_cap * SPE;
   const uint16_t* wbase = win + (int64_t)b * Wcap * D;
   const int32_t* ibase = DENSE ? nullptr : idx + (int64_t)qi * k;
 
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
               *reinterpret_cast<const uint2*>(cbase + (int64_t)blk * (D / 2) + cs * 8);
           r.lo[u].x = cw.x;
           r.lo[u].y = cw.y;
-          r.lo[u].z = sbase[(int64_t)blk * (D / 32) + cs / 2];
+          r.lo[u].z = sbase[(int64_t)blk * SPE + (E4 ? cs : cs / 2)];
         }
       }
     };
@@ -185,11 +187,19 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
             vh[u][1][i] = (_Float16)(float)k1[i];
           }
         } else {
-          const float sc = e8m0_to_f32(r.lo[u].z & 0xffu);
-          k0 = fp4x8_to_bf16(r.lo[u].x, sc);
-          k1 = fp4x8_to_bf16(r.lo[u].y, sc);
-          vh[u][0] = fp4x8_to_f16(r.lo[u].x, sc);
-          vh[u][1] = fp4x8_to_f16(r.lo[u].y, sc);
+          if (E4) {
+            const float sc = e4m3_to_f32(r.lo[u].z & 0xffu);
+            k0 = fp4x8_to_bf16_mul(r.lo[u].x, sc);
+            k1 = fp4x8_to_bf16_mul(r.lo[u].y, sc);
+            vh[u][0] = fp4x8_to_f16_mul(r.lo[u].x, sc);
+            vh[u][1] = fp4x8_to_f16_mul(r.lo[u].y, sc);
+          } else {
+            const float sc = e8m0_to_f32(r.lo[u].z & 0xffu);
+            k0 = fp4x8_to_bf16(r.lo[u].x, sc);
+            k1 = fp4x8_to_bf16(r.lo[u].y, sc);
+            vh[u][0] = fp4x8_to_f16(r.lo[u].x, sc);
+            vh[u][1] = fp4x8_to_f16(r.lo[u].y, sc);
+          }
         }
         *reinterpret_cast<v8bf*>(&Ks[ks_at(slot, 2 * cs)]) = k0;
         *reinterpret_cast<v8bf*>(&Ks[ks_at(slot, 2 * cs + 1)]) = k1;
@@ -532,16 +542,17 @@ struct AttnArgs {
   int64_t pos0; float softmax_scale; void* out; int out_dtype; float* lse; void* ws;
   int64_t ws_bytes; hipStream_t stream;
   const int64_t* pos = nullptr;  // per-sequence first positions (pos0 = their bound) or null
+  int scale_fmt = CSA_SCALE_E8M0_32;
 };
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, int FMT>
 static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, float2* part_ml) {
   const int nw = (a.H + 15) / 16;
   const int64_t nq = (int64_t)a.B * a.T;
   const dim3 grid((unsigned)(((nq + 7) / 8) * 8 * p.nsplit));
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
 #define CSA_LAUNCH_ATTN(NW)                                                                  \
-  hipLaunchKernelGGL((k_attn<D, NW, DENSE>), grid, dim3(NW * 128), 0, a.stream, a.q, a.codes, \
+  hipLaunchKernelGGL((k_attn<D, NW, DENSE, FMT>), grid, dim3(NW * 128), 0, a.stream, a.q, a.codes, \
                      a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, a.H, a.pos0, \
                      a.pos, sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse, part_o, part_ml)
   switch (nw) {
@@ -566,6 +577,7 @@ static int attn_run(const AttnArgs& a, bool dense) {
   if (!dense && a.k < 0) return CSA_ERR_SHAPE;
   if (dense && (a.m < 1 || a.m > 1 << 20)) return CSA_ERR_SHAPE;
   if (a.out_dtype != CSA_BF16 && a.out_dtype != CSA_F32) return CSA_ERR_DTYPE;
+  if (a.scale_fmt != CSA_SCALE_E8M0_32 && a.scale_fmt != CSA_SCALE_E4M3_16) return CSA_ERR_DTYPE;
   if (a.B == 0 || a.T == 0) return CSA_OK;
   if (!a.q || !a.win || !a.out) return CSA_ERR_NULL;
   if (!dense && a.k > 0 && !a.idx) return CSA_ERR_NULL;
@@ -591,15 +603,18 @@ static int attn_run(const AttnArgs& a, bool dense) {
     part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a.ws) +
                                         ((units * hpad * a.d * 4 + 255) / 256) * 256);
   }
-  if (dense) {
-    if (a.d == 128) launch_attn<128, true>(a, p, part_o, part_ml);
-    else if (a.d == 256) launch_attn<256, true>(a, p, part_o, part_ml);
-    else launch_attn<512, true>(a, p, part_o, part_ml);
+#define CSA_ATTN_D(DN, FF)                                             \
+  if (a.d == 128) launch_attn<128, DN, FF>(a, p, part_o, part_ml);      \
+  else if (a.d == 256) launch_attn<256, DN, FF>(a, p, part_o, part_ml); \
+  else launch_attn<512, DN, FF>(a, p, part_o, part_ml)
+  if (a.scale_fmt == CSA_SCALE_E4M3_16) {
+    if (dense) { CSA_ATTN_D(true, CSA_SCALE_E4M3_16); }
+    else { CSA_ATTN_D(false, CSA_SCALE_E4M3_16); }
   } else {
-    if (a.d == 128) launch_attn<128, false>(a, p, part_o, part_ml);
-    else if (a.d == 256) launch_attn<256, false>(a, p, part_o, part_ml);
-    else launch_attn<512, false>(a, p, part_o, part_ml);
+    if (dense) { CSA_ATTN_D(true, CSA_SCALE_E8M0_32); }
+    else { CSA_ATTN_D(false, CSA_SCALE_E8M0_32); }
   }
+#undef CSA_ATTN_D
   CSA_TRY_LAUNCH();
   return CSA_OK;
 }
@@ -615,9 +630,11 @@ extern "C" int csa_sparse_attn(const uint16_t* q, const uint8_t* codes, const ui
                                int64_t blk_cap, const int32_t* idx, int k, const uint16_t* win,
                                int Wcap, int W, int B, int T, int H, int d, int64_t pos0,
                                float softmax_scale, void* out, int out_dtype, float* lse,
-                               void* workspace, int64_t ws_bytes, hipStream_t stream) {
+                               void* workspace, int64_t ws_bytes, int scale_fmt,
+                               hipStream_t stream) {
   AttnArgs a{q, codes, scales, blk_cap, idx, k, 1, win, Wcap, W, B, T, H, d, pos0,
              softmax_scale, out, out_dtype, lse, workspace, ws_bytes, stream};
+  a.scale_fmt = scale_fmt;
   return attn_run(a, false);
 }
 
@@ -625,9 +642,10 @@ extern "C" int hca_dense_attn(const uint16_t* q, const uint8_t* codes, const uin
                               int64_t blk_cap, int m, const uint16_t* win, int Wcap, int W, int B,
                               int T, int H, int d, int64_t pos0, float softmax_scale, void* out,
                               int out_dtype, float* lse, void* workspace, int64_t ws_bytes,
-                              hipStream_t stream) {
+                              int scale_fmt, hipStream_t stream) {
   AttnArgs a{q, codes, scales, blk_cap, nullptr, 0, m, win, Wcap, W, B, T, H, d, pos0,
              softmax_scale, out, out_dtype, lse, workspace, ws_bytes, stream};
+  a.scale_fmt = scale_fmt;
   return attn_run(a, true);
 }
 
@@ -636,12 +654,14 @@ extern "C" int csa_sparse_attn_ragged(const uint16_t* q, const uint8_t* codes,
                                       int k, const uint16_t* win, int Wcap, int W, int B, int T,
                                       int H, int d, const int64_t* pos, int64_t pos_max,
                                       float softmax_scale, void* out, int out_dtype, float* lse,
-                                      void* workspace, int64_t ws_bytes, hipStream_t stream) {
+                                      void* workspace, int64_t ws_bytes, int scale_fmt,
+                                      hipStream_t stream) {
   if (B > 0 && T > 0 && !pos) return CSA_ERR_NULL;
   if (pos && !csa_aligned(pos, 8)) return CSA_ERR_ALIGN;
   AttnArgs a{q, codes, scales, blk_cap, idx, k, 1, win, Wcap, W, B, T, H, d, pos_max,
              softmax_scale, out, out_dtype, lse, workspace, ws_bytes, stream};
   a.pos = pos;
+  a.scale_fmt = scale_fmt;
   return attn_run(a, false);
 }
 
@@ -650,11 +670,13 @@ extern "C" int hca_dense_attn_ragged(const uint16_t* q, const uint8_t* codes,
                                      const uint16_t* win, int Wcap, int W, int B, int T, int H,
                                      int d, const int64_t* pos, int64_t pos_max,
                                      float softmax_scale, void* out, int out_dtype, float* lse,
-                                     void* workspace, int64_t ws_bytes, hipStream_t stream) {
+                                     void* workspace, int64_t ws_bytes, int scale_fmt,
+                                     hipStream_t stream) {
   if (B > 0 && T > 0 && !pos) return CSA_ERR_NULL;
   if (pos && !csa_aligned(pos, 8)) return CSA_ERR_ALIGN;
   AttnArgs a{q, codes, scales, blk_cap, nullptr, 0, m, win, Wcap, W, B, T, H, d, pos_max,
              softmax_scale, out, out_dtype, lse, workspace, ws_bytes, stream};
   a.pos = pos;
+  a.scale_fmt = scale_fmt;
   return attn_run(a, true);
 }

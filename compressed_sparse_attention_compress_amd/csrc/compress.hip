@@ -19,18 +19,14 @@
 
 namespace {
 
-// Pools the n tokens of one block over this lane's 8 channels and quantises
-// them: gate_at(j) is token j's gate logit, row_at(j, a, c) loads its 8
-// channels. The 4 lanes of a 32-channel scale group must call it together.
-// Returns the 8 packed E2M1 codes and the scale exponent.
+// Pools the n tokens of one block over this lane's 8 channels: gate_at(j) is
+// token j's gate logit, row_at(j, a, c) loads its 8 channels.
 template <class GateAt, class RowAt>
-__device__ inline uint32_t pool_quantize8(int n, GateAt gate_at, RowAt row_at, int* e_out) {
+__device__ inline void pool8(int n, GateAt gate_at, RowAt row_at, double p[8]) {
   double gmax = (double)gate_at(0);
   for (int j = 1; j < n; ++j) gmax = fmax(gmax, (double)gate_at(j));
   double den = exp((double)gate_at(0) - gmax);
   for (int j = 1; j < n; ++j) den = den + exp((double)gate_at(j) - gmax);
-
-  double p[8];
   {
     const double w0 = exp((double)gate_at(0) - gmax) / den;
     float4 a, c;
@@ -49,14 +45,16 @@ __device__ inline uint32_t pool_quantize8(int n, GateAt gate_at, RowAt row_at, i
     p[4] = p[4] + wj * (double)c.x; p[5] = p[5] + wj * (double)c.y;
     p[6] = p[6] + wj * (double)c.z; p[7] = p[7] + wj * (double)c.w;
   }
+}
 
-  // group amax over the 4 lanes (32 channels) of a scale group
+// MXFP4 (E8M0 per 32): the 4 lanes of a scale group call it together.
+// Returns the 8 packed codes; *sbyte = the scale byte (exponent + 127).
+__device__ inline uint32_t quantize8_e8m0(const double p[8], uint32_t* sbyte) {
   double amax = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(p[i]));
   amax = fmax(amax, __shfl_xor(amax, 1, 64));
   amax = fmax(amax, __shfl_xor(amax, 2, 64));
-
   int e = -127;
   if (amax > 0.0) {
     int ex;
@@ -74,13 +72,71 @@ __device__ inline uint32_t pool_quantize8(int n, GateAt gate_at, RowAt row_at, i
     uint32_t code = (signbit(y) ? 8u : 0u) | mag;
     word |= code << (4 * i);
   }
-  *e_out = e;
+  *sbyte = (uint32_t)(e + 127);
   return word;
+}
+
+__device__ inline double e4m3_f64(int b) {
+  const int e = (b >> 3) & 15, mnt = b & 7;
+  return e ? ldexp((double)(8 + mnt), e - 10) : ldexp((double)mnt, -9);
+}
+
+// FP4 with one E4M3 scale per 16 channels: the 2 lanes of a scale group call
+// it together. The scale is the E4M3 value nearest to amax / 6 (ties to the
+// even byte, saturating at 448), found without dividing: a binary search for
+// the largest byte with 6 v <= amax, then amax against 3 (v + v_next). The
+// codes round to the nearest multiple of the scale by comparing |p| with the
+// scale times each midpoint of the E2M1 grid (exact products in float64).
+__device__ inline uint32_t quantize8_e4m3(const double p[8], uint32_t* sbyte) {
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(p[i]));
+  amax = fmax(amax, __shfl_xor(amax, 1, 64));
+  int lo = 0, hi = 0x7E;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (6.0 * e4m3_f64(mid) <= amax) lo = mid;
+    else hi = mid - 1;
+  }
+  int b = lo;
+  if (lo < 0x7E) {
+    const double mid6 = 3.0 * (e4m3_f64(lo) + e4m3_f64(lo + 1));
+    if (amax > mid6 || (amax == mid6 && (lo & 1))) b = lo + 1;
+  }
+  const double sc = e4m3_f64(b);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double a = fabs(p[i]);
+    uint32_t mag = sc == 0.0 ? 0u
+                             : (a > sc * 0.25) + (a >= sc * 0.75) + (a > sc * 1.25) +
+                                   (a >= sc * 1.75) + (a > sc * 2.5) + (a >= sc * 3.5) +
+                                   (a > sc * 5.0);
+    uint32_t code = (signbit(p[i]) ? 8u : 0u) | mag;
+    word |= code << (4 * i);
+  }
+  *sbyte = (uint32_t)b;
+  return word;
+}
+
+// Writes one lane's 8 codes and, from the first lane of its scale group, the
+// scale byte of entry `row`.
+template <int D, int FMT>
+__device__ inline void store_entry(const double p[8], int seg, int64_t row,
+                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  uint32_t sb;
+  const uint32_t word = FMT == CSA_SCALE_E4M3_16 ? quantize8_e4m3(p, &sb) : quantize8_e8m0(p, &sb);
+  *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + seg * 4) = word;
+  if (FMT == CSA_SCALE_E4M3_16) {
+    if ((seg & 1) == 0) scales[row * (D / 16) + seg / 2] = (uint8_t)sb;
+  } else {
+    if ((seg & 3) == 0) scales[row * (D / 32) + seg / 4] = (uint8_t)sb;
+  }
 }
 
 // One lane owns 8 consecutive channels of one block; D/8 lanes cover a block
 // row, so a wave holds 64/(D/8) blocks.
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void k_compress_quantize(
     const float* __restrict__ kv, int64_t kv_ld, const float* __restrict__ gate,
     int64_t n_tok, int m, int64_t nblk, int64_t total, int64_t blk_first,
@@ -98,18 +154,16 @@ __global__ __launch_bounds__(256) void k_compress_quantize(
   const int seg = lane % LPB;
   const float* g = gate + b * n_tok + j0;
   const float* x = kv + (b * n_tok + j0) * kv_ld + seg * 8;
-  int e;
-  const uint32_t word = pool_quantize8(
+  double p[8];
+  pool8(
       n, [&](int j) { return g[j]; },
       [&](int j, float4& a, float4& c) {
         const float* xj = x + (int64_t)j * kv_ld;
         a = *reinterpret_cast<const float4*>(xj);
         c = *reinterpret_cast<const float4*>(xj + 4);
       },
-      &e);
-  const int64_t row = b * blk_cap + blk_first + bi;
-  *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + seg * 4) = word;
-  if ((seg & 3) == 0) scales[row * (D / 32) + seg / 4] = (uint8_t)(e + 127);
+      p);
+  store_entry<D, FMT>(p, seg, b * blk_cap + blk_first + bi, codes, scales);
 }
 
 // Decode append: one new token per sequence, at its own position pos[b]
@@ -119,7 +173,7 @@ __global__ __launch_bounds__(256) void k_compress_quantize(
 // from registers) and quantised into entry pos / m, with the same arithmetic
 // as k_compress_quantize. Lanes as in k_compress_quantize, one sequence per
 // D/8 lanes.
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void k_decode_append(
     const float* __restrict__ kv, int64_t kv_ld, const float* __restrict__ gate,
     const int64_t* __restrict__ pos, int B, int m, float* __restrict__ stage,
@@ -159,8 +213,8 @@ __global__ __launch_bounds__(256) void k_decode_append(
   const int64_t blk = t / m;
   if (blk >= blk_cap) return;
   const float* sg = stage_gate + b * m;
-  int e;
-  const uint32_t word = pool_quantize8(
+  double p[8];
+  pool8(
       m, [&](int i) { return i == j ? gt : sg[i]; },
       [&](int i, float4& a, float4& c) {
         if (i == j) {
@@ -172,13 +226,11 @@ __global__ __launch_bounds__(256) void k_decode_append(
           c = *reinterpret_cast<const float4*>(sr + 4);
         }
       },
-      &e);
-  const int64_t row = b * blk_cap + blk;
-  *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + seg * 4) = word;
-  if ((seg & 3) == 0) scales[row * (D / 32) + seg / 4] = (uint8_t)(e + 127);
+      p);
+  store_entry<D, FMT>(p, seg, b * blk_cap + blk, codes, scales);
 }
 
-template <int OUT>
+template <int OUT, int FMT>
 __global__ __launch_bounds__(256) void k_dequantize(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t blk_cap,
     int64_t blk0, int64_t n_blk, int d, int64_t total, void* __restrict__ out) {
@@ -191,15 +243,17 @@ __global__ __launch_bounds__(256) void k_dequantize(
   const int64_t bi = row - b * n_blk;
   const int64_t src = b * blk_cap + blk0 + bi;
   const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + src * (d / 2) + seg * 4);
-  const float sc = e8m0_to_f32(scales[src * (d / 32) + seg / 4]);
+  const bool e4 = FMT == CSA_SCALE_E4M3_16;
+  const float sc = e4 ? e4m3_to_f32(scales[src * (d / 16) + seg / 2])
+                      : e8m0_to_f32(scales[src * (d / 32) + seg / 4]);
   if (OUT == CSA_BF16) {
-    v8bf v = fp4x8_to_bf16(word, sc);
+    v8bf v = e4 ? fp4x8_to_bf16_mul(word, sc) : fp4x8_to_bf16(word, sc);
     *reinterpret_cast<v8bf*>(reinterpret_cast<__bf16*>(out) + u * 8) = v;
   } else if (OUT == CSA_F16) {
-    v8h v = fp4x8_to_f16(word, sc);
+    v8h v = e4 ? fp4x8_to_f16_mul(word, sc) : fp4x8_to_f16(word, sc);
     *reinterpret_cast<v8h*>(reinterpret_cast<_Float16*>(out) + u * 8) = v;
   } else {
-    v8bf v = fp4x8_to_bf16(word, sc);
+    v8bf v = e4 ? fp4x8_to_bf16_mul(word, sc) : fp4x8_to_bf16(word, sc);
     float* o = reinterpret_cast<float*>(out) + u * 8;
     float4 a, c;
     a.x = (float)v[0]; a.y = (float)v[1]; a.z = (float)v[2]; a.w = (float)v[3];
@@ -211,14 +265,19 @@ __global__ __launch_bounds__(256) void k_dequantize(
 
 }  // namespace
 
-extern "C" int64_t csa_cache_bytes(int64_t n_tokens, int d, int m) {
-  if (n_tokens < 0 || m < 1 || d <= 0 || d % 32) return -1;
-  return ((n_tokens + m - 1) / m) * (int64_t)(d / 2 + d / 32);
+static inline bool valid_fmt(int f) { return f == CSA_SCALE_E8M0_32 || f == CSA_SCALE_E4M3_16; }
+
+extern "C" int64_t csa_cache_bytes(int64_t n_tokens, int d, int m, int scale_fmt) {
+  if (n_tokens < 0 || m < 1 || d <= 0 || d % 32 || !valid_fmt(scale_fmt)) return -1;
+  const int sb = scale_fmt == CSA_SCALE_E4M3_16 ? d / 16 : d / 32;
+  return ((n_tokens + m - 1) / m) * (int64_t)(d / 2 + sb);
 }
 
 extern "C" int csa_compress_quantize(const float* kv, int64_t kv_ld, const float* gate, int B,
                                      int64_t tok0, int64_t n_tok, int d, int m, uint8_t* codes,
-                                     uint8_t* scales, int64_t blk_cap, hipStream_t stream) {
+                                     uint8_t* scales, int64_t blk_cap, int scale_fmt,
+                                     hipStream_t stream) {
+  if (!valid_fmt(scale_fmt)) return CSA_ERR_DTYPE;
   if (B < 0 || n_tok < 0 || tok0 < 0 || blk_cap < 0) return CSA_ERR_SHAPE;
   if (m < 1 || m > 128) return CSA_ERR_SHAPE;
   if (d != 32 && d != 64 && d != 128 && d != 256 && d != 512) return CSA_ERR_SHAPE;
@@ -234,9 +293,12 @@ extern "C" int csa_compress_quantize(const float* kv, int64_t kv_ld, const float
   const int bpwg = 4 * (64 / (d / 8));
   const int64_t grid = (total + bpwg - 1) / bpwg;
   if (grid > 0x7fffffff) return CSA_ERR_SHAPE;
-#define CSA_LAUNCH_COMPRESS(DD)                                                            \
-  hipLaunchKernelGGL(k_compress_quantize<DD>, dim3((unsigned)grid), dim3(256), 0, stream, kv, \
-                     kv_ld, gate, n_tok, m, nblk, total, blk_first, codes, scales, blk_cap)
+#define CSA_LAUNCH_COMPRESS1(DD, FF)                                                          \
+  hipLaunchKernelGGL((k_compress_quantize<DD, FF>), dim3((unsigned)grid), dim3(256), 0, stream, \
+                     kv, kv_ld, gate, n_tok, m, nblk, total, blk_first, codes, scales, blk_cap)
+#define CSA_LAUNCH_COMPRESS(DD)                                         \
+  if (scale_fmt == CSA_SCALE_E4M3_16) CSA_LAUNCH_COMPRESS1(DD, CSA_SCALE_E4M3_16); \
+  else CSA_LAUNCH_COMPRESS1(DD, CSA_SCALE_E8M0_32)
   switch (d) {
     case 32: CSA_LAUNCH_COMPRESS(32); break;
     case 64: CSA_LAUNCH_COMPRESS(64); break;
@@ -245,6 +307,7 @@ extern "C" int csa_compress_quantize(const float* kv, int64_t kv_ld, const float
     default: CSA_LAUNCH_COMPRESS(512); break;
   }
 #undef CSA_LAUNCH_COMPRESS
+#undef CSA_LAUNCH_COMPRESS1
   CSA_TRY_LAUNCH();
   return CSA_OK;
 }
@@ -252,7 +315,9 @@ extern "C" int csa_compress_quantize(const float* kv, int64_t kv_ld, const float
 extern "C" int csa_decode_append(const float* kv, int64_t kv_ld, const float* gate,
                                  const int64_t* pos, int B, int d, int m, float* stage,
                                  float* stage_gate, uint8_t* codes, uint8_t* scales,
-                                 int64_t blk_cap, uint16_t* win, int Wcap, hipStream_t stream) {
+                                 int64_t blk_cap, uint16_t* win, int Wcap, int scale_fmt,
+                                 hipStream_t stream) {
+  if (!valid_fmt(scale_fmt)) return CSA_ERR_DTYPE;
   if (B < 0 || blk_cap < 0 || Wcap < 1) return CSA_ERR_SHAPE;
   if (m < 1 || m > 128) return CSA_ERR_SHAPE;
   if (d != 32 && d != 64 && d != 128 && d != 256 && d != 512) return CSA_ERR_SHAPE;
@@ -265,9 +330,12 @@ extern "C" int csa_decode_append(const float* kv, int64_t kv_ld, const float* ga
     return CSA_ERR_ALIGN;
   const int spw = 4 * (64 / (d / 8));  // sequences per workgroup
   const int grid = (B + spw - 1) / spw;
-#define CSA_LAUNCH_APPEND(DD)                                                                 \
-  hipLaunchKernelGGL(k_decode_append<DD>, dim3(grid), dim3(256), 0, stream, kv, kv_ld, gate,  \
-                     pos, B, m, stage, stage_gate, codes, scales, blk_cap, win, Wcap)
+#define CSA_LAUNCH_APPEND1(DD, FF)                                                          \
+  hipLaunchKernelGGL((k_decode_append<DD, FF>), dim3(grid), dim3(256), 0, stream, kv, kv_ld,  \
+                     gate, pos, B, m, stage, stage_gate, codes, scales, blk_cap, win, Wcap)
+#define CSA_LAUNCH_APPEND(DD)                                                       \
+  if (scale_fmt == CSA_SCALE_E4M3_16) CSA_LAUNCH_APPEND1(DD, CSA_SCALE_E4M3_16); \
+  else CSA_LAUNCH_APPEND1(DD, CSA_SCALE_E8M0_32)
   switch (d) {
     case 32: CSA_LAUNCH_APPEND(32); break;
     case 64: CSA_LAUNCH_APPEND(64); break;
@@ -276,13 +344,15 @@ extern "C" int csa_decode_append(const float* kv, int64_t kv_ld, const float* ga
     default: CSA_LAUNCH_APPEND(512); break;
   }
 #undef CSA_LAUNCH_APPEND
+#undef CSA_LAUNCH_APPEND1
   CSA_TRY_LAUNCH();
   return CSA_OK;
 }
 
 extern "C" int csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t blk_cap, int B,
                               int64_t blk0, int64_t n_blk, int d, void* out, int out_dtype,
-                              hipStream_t stream) {
+                              int scale_fmt, hipStream_t stream) {
+  if (!valid_fmt(scale_fmt)) return CSA_ERR_DTYPE;
   if (B < 0 || blk0 < 0 || n_blk < 0 || blk_cap < 0) return CSA_ERR_SHAPE;
   if (d <= 0 || d % 32 || d > 4096) return CSA_ERR_SHAPE;
   if (out_dtype != CSA_BF16 && out_dtype != CSA_F16 && out_dtype != CSA_F32) return CSA_ERR_DTYPE;
@@ -293,15 +363,21 @@ extern "C" int csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64
   const int64_t total = (int64_t)B * n_blk * (d / 8);
   const int64_t grid = (total + 255) / 256;
   if (grid > 0x7fffffff) return CSA_ERR_SHAPE;
-  if (out_dtype == CSA_BF16)
-    hipLaunchKernelGGL(k_dequantize<CSA_BF16>, dim3((unsigned)grid), dim3(256), 0, stream, codes,
-                       scales, blk_cap, blk0, n_blk, d, total, out);
-  else if (out_dtype == CSA_F16)
-    hipLaunchKernelGGL(k_dequantize<CSA_F16>, dim3((unsigned)grid), dim3(256), 0, stream, codes,
-                       scales, blk_cap, blk0, n_blk, d, total, out);
-  else
-    hipLaunchKernelGGL(k_dequantize<CSA_F32>, dim3((unsigned)grid), dim3(256), 0, stream, codes,
-                       scales, blk_cap, blk0, n_blk, d, total, out);
+#define CSA_LAUNCH_DEQ(OO)                                                                   \
+  if (scale_fmt == CSA_SCALE_E4M3_16)                                                        \
+    hipLaunchKernelGGL((k_dequantize<OO, CSA_SCALE_E4M3_16>), dim3((unsigned)grid), dim3(256), \
+                       0, stream, codes, scales, blk_cap, blk0, n_blk, d, total, out);        \
+  else                                                                                       \
+    hipLaunchKernelGGL((k_dequantize<OO, CSA_SCALE_E8M0_32>), dim3((unsigned)grid), dim3(256), \
+                       0, stream, codes, scales, blk_cap, blk0, n_blk, d, total, out)
+  if (out_dtype == CSA_BF16) {
+    CSA_LAUNCH_DEQ(CSA_BF16);
+  } else if (out_dtype == CSA_F16) {
+    CSA_LAUNCH_DEQ(CSA_F16);
+  } else {
+    CSA_LAUNCH_DEQ(CSA_F32);
+  }
+#undef CSA_LAUNCH_DEQ
   CSA_TRY_LAUNCH();
   return CSA_OK;
 }

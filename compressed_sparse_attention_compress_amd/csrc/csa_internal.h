@@ -108,6 +108,35 @@ __device__ inline v8h fp4x8_to_f16(uint32_t word, float scale) {
   return r;
 }
 
+// ---------------------------------------------- FP4 with E4M3 scales -----
+
+// Non-negative OCP E4M3 byte (0 .. 0x7E) -> float32, exact: exponent field
+// bits 6..3 (bias 7), mantissa bits 2..0, exponent field 0 subnormal.
+__device__ inline float e4m3_to_f32(uint32_t b) {
+  const int e = (b >> 3) & 15, mnt = b & 7;
+  return e ? ldexpf((float)(8 + mnt), e - 10) : ldexpf((float)mnt, -9);
+}
+
+// Eight E2M1 codes times an E4M3 scale. The scale is not a power of two, so
+// the codes are converted unscaled and multiplied in float32; E2M1 (2
+// significant bits) times E4M3 (4 bits) is exact in float32, bfloat16 and
+// float16 over the whole E4M3 range.
+__device__ inline v8bf fp4x8_to_bf16_mul(uint32_t word, float scale) {
+  const v8bf u = fp4x8_to_bf16(word, 1.0f);
+  v8bf r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)((float)u[i] * scale);
+  return r;
+}
+
+__device__ inline v8h fp4x8_to_f16_mul(uint32_t word, float scale) {
+  const v8h u = fp4x8_to_f16(word, 1.0f);
+  v8h r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (_Float16)((float)u[i] * scale);
+  return r;
+}
+
 // ----------------------------------------------------------- indexer ----
 
 // Monotone (non-decreasing) map of a non-negative int32 score to one of 512

@@ -61,31 +61,49 @@ enum csa_status {
 
 enum csa_dtype { CSA_BF16 = 0, CSA_F32 = 1, CSA_F16 = 2 };
 
+/* Scale format of the FP4 cache (every call that reads or writes codes and
+ * scales takes one; an unknown value returns CSA_ERR_DTYPE):
+ *  CSA_SCALE_E8M0_32  one E8M0 byte per 32 channels, the OCP MX v1.0 MXFP4
+ *                     rule: exponent floor(log2 amax) - 2; scales [..][d/32].
+ *  CSA_SCALE_E4M3_16  one OCP E4M3 byte per 16 channels, no global scale
+ *                     (podcast cue 16 names E4M3 scales per 16 channels): the
+ *                     E4M3 value nearest to amax / 6, ties to the even byte,
+ *                     saturating at 448; codes round to the nearest multiple
+ *                     of the scale on the E2M1 grid, ties to even, saturating
+ *                     at 6; a zero scale gives zero codes; scales [..][d/16].
+ * Both formats dequantise exactly to bfloat16, and to float16 (E8M0 only for
+ * scale bytes in [104, 140], E4M3 over its whole range). */
+enum csa_scale_fmt { CSA_SCALE_E8M0_32 = 0, CSA_SCALE_E4M3_16 = 1 };
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* csa_status_string(int status);
 
 /* Library ABI version (major * 100 + minor). */
 int csa_version(void);
 
-/* Closed form, host only: bytes of MXFP4 codes + scales for n_tokens tokens
- * compressed m tokens per entry, d channels: ceil(n_tokens/m) * (d/2 + d/32).
- * Returns -1 for n_tokens < 0, m < 1 or d not a positive multiple of 32. */
-int64_t csa_cache_bytes(int64_t n_tokens, int d, int m);
+/* Closed form, host only: bytes of FP4 codes + scales for n_tokens tokens
+ * compressed m tokens per entry, d channels: ceil(n_tokens/m) * (d/2 + d/32)
+ * (E8M0 scales) or ceil(n_tokens/m) * (d/2 + d/16) (E4M3 scales). Returns -1
+ * for n_tokens < 0, m < 1, d not a positive multiple of 32 or an unknown
+ * scale format. */
+int64_t csa_cache_bytes(int64_t n_tokens, int d, int m, int scale_fmt);
 
 /* ---------------------------------------------------------------------------
- * Block compression + MXFP4 quantisation (the compressed cache write).
+ * Block compression + FP4 quantisation (the compressed cache write).
  * Summarises tokens [tok0, tok0 + n_tok) of each of B sequences into entries
  * tok0/m .. ceil((tok0 + n_tok)/m) - 1 ("Frontier Architecture Decoding
  * Notes (4)", section 1: 4-token CSA blocks, up to 128 for HCA; podcast
  * cue 16: FP4 cache). For each block, w = softmax(gate over its tokens) and
- * p = sum_j w_j * kv_j, computed in float64; then every 32-channel group of p
- * is quantised to MXFP4. A final partial block pools the tokens present.
+ * p = sum_j w_j * kv_j, computed in float64; then p is quantised to FP4 in
+ * scale_fmt (every 32-channel group with an E8M0 scale, or every 16-channel
+ * group with an E4M3 scale). A final partial block pools the tokens present.
  *   kv     float32 [B][n_tok][kv_ld] (first d columns used), 16-byte aligned,
  *          kv_ld % 4 == 0
  *   gate   float32 [B][n_tok]
  *   codes  uint8  [B][blk_cap][d/2]  E2M1 codes, channel 2i in the low nibble
  *          of byte i (sign in bit 3); 4-byte aligned
- *   scales uint8  [B][blk_cap][d/32] E8M0 exponents (value 2^(byte-127))
+ *   scales uint8  [B][blk_cap][d/32] E8M0 exponents (value 2^(byte-127)), or
+ *          [B][blk_cap][d/16] E4M3 scales
  * Requires 1 <= m <= 128, tok0 % m == 0, d in {32, 64, 128, 256, 512},
  * n_tok >= 0, and the last entry < blk_cap (else CSA_ERR_RANGE).
  * Inputs must be finite. Entries outside the range are left untouched.
@@ -93,17 +111,18 @@ int64_t csa_cache_bytes(int64_t n_tokens, int d, int m);
 int csa_compress_quantize(const float* kv, int64_t kv_ld, const float* gate,
                           int B, int64_t tok0, int64_t n_tok, int d, int m,
                           uint8_t* codes, uint8_t* scales, int64_t blk_cap,
-                          hipStream_t stream);
+                          int scale_fmt, hipStream_t stream);
 
 /* Dequantise entries [blk0, blk0 + n_blk) of each sequence (podcast cue 16:
  * the cache is expanded just before attention) with the same conversion the
  * attention kernels use. out: [B][n_blk][d] in out_dtype (CSA_BF16, CSA_F16
- * or CSA_F32). BF16 and F32 are exact for scale bytes up to 252 (the largest
- * a finite float32 input can produce; above it large codes overflow to
- * +-inf); F16 is exact for scale bytes in [104, 140]. */
+ * or CSA_F32). E8M0: BF16 and F32 are exact for scale bytes up to 252 (the
+ * largest a finite float32 input can produce; above it large codes overflow
+ * to +-inf); F16 is exact for scale bytes in [104, 140]. E4M3: exact in all
+ * three. */
 int csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t blk_cap,
                    int B, int64_t blk0, int64_t n_blk, int d,
-                   void* out, int out_dtype, hipStream_t stream);
+                   void* out, int out_dtype, int scale_fmt, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Decode append: one new token for each of B sequences, each at its own
@@ -131,7 +150,7 @@ int csa_decode_append(const float* kv, int64_t kv_ld, const float* gate,
                       const int64_t* pos, int B, int d, int m,
                       float* stage, float* stage_gate,
                       uint8_t* codes, uint8_t* scales, int64_t blk_cap,
-                      uint16_t* win, int Wcap, hipStream_t stream);
+                      uint16_t* win, int Wcap, int scale_fmt, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Indexer + top-k (podcast cues 12 and 14: a light indexer scores every
@@ -292,7 +311,7 @@ int csa_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scal
                     const uint16_t* win, int Wcap, int W,
                     int B, int T, int H, int d, int64_t pos0, float softmax_scale,
                     void* out, int out_dtype, float* lse,
-                    void* workspace, int64_t ws_bytes, hipStream_t stream);
+                    void* workspace, int64_t ws_bytes, int scale_fmt, hipStream_t stream);
 
 /* Heavily compressed (dense) attention: csa_sparse_attn with the entry set =
  * every visible block of an m-token cache, b with (b + 1) * m - 1 <= t
@@ -304,7 +323,7 @@ int hca_dense_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scale
                    const uint16_t* win, int Wcap, int W,
                    int B, int T, int H, int d, int64_t pos0, float softmax_scale,
                    void* out, int out_dtype, float* lse,
-                   void* workspace, int64_t ws_bytes, hipStream_t stream);
+                   void* workspace, int64_t ws_bytes, int scale_fmt, hipStream_t stream);
 
 /* csa_sparse_attn and hca_dense_attn for sequences at different positions:
  * the queries of sequence b are at pos[b] .. pos[b] + T - 1 (pos: int64 [B]
@@ -317,13 +336,13 @@ int csa_sparse_attn_ragged(const uint16_t* q, const uint8_t* codes, const uint8_
                            const uint16_t* win, int Wcap, int W,
                            int B, int T, int H, int d, const int64_t* pos, int64_t pos_max,
                            float softmax_scale, void* out, int out_dtype, float* lse,
-                           void* workspace, int64_t ws_bytes, hipStream_t stream);
+                           void* workspace, int64_t ws_bytes, int scale_fmt, hipStream_t stream);
 int hca_dense_attn_ragged(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                           int64_t blk_cap, int m,
                           const uint16_t* win, int Wcap, int W,
                           int B, int T, int H, int d, const int64_t* pos, int64_t pos_max,
                           float softmax_scale, void* out, int out_dtype, float* lse,
-                          void* workspace, int64_t ws_bytes, hipStream_t stream);
+                          void* workspace, int64_t ws_bytes, int scale_fmt, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -46,22 +46,28 @@ def test_cache_bytes_closed_form(L):
     for d in (32, 128, 512):
         for m in (1, 4, 128):
             for n in (0, 1, 4, 5, 1 << 20, 3 * (1 << 20) + 1):
-                assert L.csa_cache_bytes(n, d, m) == math.ceil(n / m) * (d // 2 + d // 32)
-    assert L.csa_cache_bytes((1 << 20) * 8, 512, 4) == 8 * 262144 * 272
-    assert L.csa_cache_bytes(-1, 512, 4) == -1
-    assert L.csa_cache_bytes(8, 100, 4) == -1
+                assert L.csa_cache_bytes(n, d, m, 0) == math.ceil(n / m) * (d // 2 + d // 32)
+                assert L.csa_cache_bytes(n, d, m, 1) == math.ceil(n / m) * (d // 2 + d // 16)
+    assert L.csa_cache_bytes((1 << 20) * 8, 512, 4, 0) == 8 * 262144 * 272
+    assert L.csa_cache_bytes((1 << 20) * 8, 512, 4, 1) == 8 * 262144 * 288
+    assert L.csa_cache_bytes(-1, 512, 4, 0) == -1
+    assert L.csa_cache_bytes(8, 100, 4, 0) == -1
+    assert L.csa_cache_bytes(8, 512, 4, 2) == -1
 
 
 def test_argument_errors_before_launch(L):
     P = ctypes.c_void_p
     fake = P(256)
     # compress: m out of range, d unsupported, tok0 not block aligned, NULL
-    assert L.csa_compress_quantize(fake, 512, fake, 1, 0, 8, 512, 0, fake, fake, 4, None) == -2
-    assert L.csa_compress_quantize(fake, 512, fake, 1, 0, 8, 100, 4, fake, fake, 4, None) == -2
-    assert L.csa_compress_quantize(fake, 512, fake, 1, 2, 8, 512, 4, fake, fake, 4, None) == -3
-    assert L.csa_compress_quantize(None, 512, fake, 1, 0, 8, 512, 4, fake, fake, 4, None) == -1
-    assert L.csa_compress_quantize(fake, 512, fake, 1, 0, 8, 512, 4, fake, fake, 1, None) == -3
-    assert L.csa_compress_quantize(P(258), 512, fake, 1, 0, 8, 512, 4, fake, fake, 4, None) == -7
+    cq = lambda kv, tok0, d, m, cap, fmt=0: L.csa_compress_quantize(kv, 512, fake, 1, tok0, 8, d,
+                                                                    m, fake, fake, cap, fmt, None)
+    assert cq(fake, 0, 512, 0, 4) == -2
+    assert cq(fake, 0, 100, 4, 4) == -2
+    assert cq(fake, 2, 512, 4, 4) == -3
+    assert cq(None, 0, 512, 4, 4) == -1
+    assert cq(fake, 0, 512, 4, 1) == -3
+    assert cq(P(258), 0, 512, 4, 4) == -7
+    assert cq(fake, 0, 512, 4, 4, fmt=5) == -5          # unknown scale format
     # indexer: bad Hi / Di / k, missing workspace
     args = lambda Hi, Di, k, ws: (fake, fake, fake, 100, 1, 1, Hi, Di, 4, 399, None, 0, k,
                                   fake, None, ws, 1 << 20, None)
@@ -84,26 +90,27 @@ def test_argument_errors_before_launch(L):
     assert L.csa_index_topk_ragged(*rag(P(260))) == -7
     # decode append: bad m, bad d, missing positions, misaligned stage
     app = lambda d, m, pos, stage: (fake, 512, fake, pos, 2, d, m, stage, fake, fake, fake, 10,
-                                    fake, 128, None)
+                                    fake, 128, 0, None)
     assert L.csa_decode_append(*app(512, 0, fake, fake)) == -2
     assert L.csa_decode_append(*app(96, 4, fake, fake)) == -2
     assert L.csa_decode_append(*app(512, 4, None, fake)) == -1
     assert L.csa_decode_append(*app(512, 4, fake, P(264))) == -7
     # attention: bad d, H, window ring too small, dtype
-    a = lambda d, H, W, Wcap, T, dt: (fake, fake, fake, 100, fake, 8, fake, Wcap, W, 1, T, H, d,
-                                      399, ctypes.c_float(1.0), fake, dt, None, fake, 1 << 30,
-                                      None)
+    a = lambda d, H, W, Wcap, T, dt, fmt=0: (fake, fake, fake, 100, fake, 8, fake, Wcap, W, 1, T,
+                                             H, d, 399, ctypes.c_float(1.0), fake, dt, None, fake,
+                                             1 << 30, fmt, None)
     assert L.csa_sparse_attn(*a(96, 8, 128, 128, 1, 0)) == -2
     assert L.csa_sparse_attn(*a(512, 65, 128, 128, 1, 0)) == -2
     assert L.csa_sparse_attn(*a(512, 64, 128, 128, 2, 0)) == -3
     assert L.csa_sparse_attn(*a(512, 64, 0, 128, 1, 0)) == -2
     assert L.csa_sparse_attn(*a(512, 64, 128, 128, 1, 7)) == -5
+    assert L.csa_sparse_attn(*a(512, 64, 128, 128, 1, 0, fmt=3)) == -5
     # ragged attention: positions missing
     ra = (fake, fake, fake, 100, fake, 8, fake, 128, 128, 1, 1, 64, 512, None, 399,
-          ctypes.c_float(1.0), fake, 0, None, fake, 1 << 30, None)
+          ctypes.c_float(1.0), fake, 0, None, fake, 1 << 30, 0, None)
     assert L.csa_sparse_attn_ragged(*ra) == -1
     rh = (fake, fake, fake, 100, 4, fake, 128, 128, 1, 1, 64, 512, None, 399,
-          ctypes.c_float(1.0), fake, 0, None, fake, 1 << 30, None)
+          ctypes.c_float(1.0), fake, 0, None, fake, 1 << 30, 0, None)
     assert L.hca_dense_attn_ragged(*rh) == -1
 
 
