@@ -36,6 +36,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0
+# scale format of the FP4 caches (--fmt): E8M0 per 32 channels or E4M3 per 16
+FMT = "e8m0"
+SCALE_GROUP = {"e8m0": 32, "e4m3": 16}
+CACHE_NAME = {"e8m0": "MXFP4 e2m1 + e8m0/32", "e4m3": "FP4 e2m1 + e4m3/16"}
+
 METRIC = "CSA decode queries/sec + achieved HBM GB/s (% peak) at 1M ctx, 1 MI355X"
 CSRC = os.path.join(ROOT, "compressed_sparse_attention_compress_amd", "csrc")
 KERNEL_SOURCE = {"k_idx_scan": "indexer.hip", "k_idx_prefill": "indexer.hip",
@@ -56,12 +61,13 @@ def build_cache(csa, synth, wl, dev, seed, layer, m, L):
     import torch
     cap = -(-L // m)
     codes = torch.empty(wl.B, cap, wl.d // 2, device=dev, dtype=torch.uint8)
-    scales = torch.empty(wl.B, cap, wl.d // 32, device=dev, dtype=torch.uint8)
+    scales = torch.empty(wl.B, cap, wl.d // SCALE_GROUP[FMT], device=dev, dtype=torch.uint8)
     for b in range(wl.B):
         for c in range(-(-L // synth.CHUNK)):
             kv = synth.latent_chunk(wl, b, c, dev, seed, layer)[None]
             g = synth.gate_chunk(wl, b, c, dev, seed, layer)[None]
-            csa.compress_quantize(kv, g, c * synth.CHUNK, m, codes[b:b + 1], scales[b:b + 1])
+            csa.compress_quantize(kv, g, c * synth.CHUNK, m, codes[b:b + 1], scales[b:b + 1],
+                                  fmt=FMT)
     return codes, scales
 
 
@@ -83,7 +89,7 @@ def decode_set(csa, synth, wl, dev, seed):
 # --------------------------------------------------------------------------
 
 def entry_bytes(wl):
-    return wl.d // 2 + wl.d // 32
+    return wl.d // 2 + wl.d // SCALE_GROUP[FMT]
 
 
 def decode_bytes_per_query(wl):
@@ -168,7 +174,10 @@ def source_hash(kernel) -> str:
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or
-    None when they are missing or were taken on a different kernel source."""
+    None when they are missing or were taken on a different kernel source
+    (or on the E8M0 cache when the E4M3 one is run)."""
+    if FMT != "e8m0":
+        workload += "_" + FMT
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")))
     except (OSError, ValueError):
@@ -238,7 +247,7 @@ def cpu_baseline_decode(s, wl, n_queries, min_seconds):
                 t0 = time.perf_counter()
                 ri, _ = O.index_topk(q_idx[b, 0], w[b, 0], keys[b], wl.m, wl.L - 1, wl.k)
                 ro, _ = O.sparse_attn(qb[b, 0], codes[b], scales[b], ri, win[b], wl.Wcap, wl.W,
-                                      wl.L - 1, 1.0)
+                                      wl.L - 1, 1.0, fmt=FMT)
                 t_total += time.perf_counter() - t0
                 if done < n_queries:
                     idx_ok &= bool(np.array_equal(ri, gpu_idx[b, 0]))
@@ -270,7 +279,7 @@ def run_decode(args, csa, synth, wl, dev):
         csa.index_select(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
                          workspace=s["ws"])
         csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, pos, 1.0,
-                        s["out"], workspace=s["ws_attn"])
+                        s["out"], workspace=s["ws_attn"], fmt=FMT)
 
     def step_fn(i):
         def f():
@@ -278,7 +287,7 @@ def run_decode(args, csa, synth, wl, dev):
             csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
                            workspace=s["ws"])
             csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, pos, 1.0,
-                            s["out"], workspace=s["ws_attn"])
+                            s["out"], workspace=s["ws_attn"], fmt=FMT)
         return f
 
     eager = [step_fn(i) for i in range(len(sets))]
@@ -321,7 +330,7 @@ def run_decode(args, csa, synth, wl, dev):
         "config": {
             "workload": wl.name, "batch": wl.B, "context": wl.L, "d": wl.d, "m": wl.m,
             "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8", "top_k": wl.k, "window": wl.W,
-            "cache": "MXFP4 e2m1 + e8m0/32", "input_sets_rotated": args.sets,
+            "cache": CACHE_NAME[FMT], "input_sets_rotated": args.sets,
             "timing": timing_name(args),
         },
         "step_hbm": {"algorithmic_bytes_per_query": per_q["total"],
@@ -394,7 +403,8 @@ def cpu_baseline_ragged(s, wl, n_queries, min_seconds):
             j0 = t + 1 - wl.m
             kv = synth.latent_range(wl, b, j0, t + 1, s["dev"], s["seed"]).cpu().numpy()
             g = synth.latent_range(wl, b, j0, t + 1, s["dev"], s["seed"], gate=True).cpu().numpy()
-            rc, rs = O.compress_quantize(kv, g, wl.m)
+            quant = O.compress_quantize_e4m3 if FMT == "e4m3" else O.compress_quantize
+            rc, rs = quant(kv, g, wl.m)
             blk = t // wl.m
             ok &= bool(np.array_equal(s["codes"][b, blk].cpu().numpy(), rc[0]))
             ok &= bool(np.array_equal(s["scales"][b, blk].cpu().numpy(), rs[0]))
@@ -408,7 +418,7 @@ def cpu_baseline_ragged(s, wl, n_queries, min_seconds):
                 t0 = time.perf_counter()
                 ri, _ = O.index_topk(q_idx[b, 0], w[b, 0], keys[b], wl.m, t, wl.k)
                 ro, _ = O.sparse_attn(qb[b, 0], codes[b], scales[b], ri, win[b], wl.Wcap, wl.W,
-                                      t, 1.0)
+                                      t, 1.0, fmt=FMT)
                 t_total += time.perf_counter() - t0
                 if done < n_queries:
                     ok &= bool(np.array_equal(ri, gpu_idx[b, 0]))
@@ -435,7 +445,7 @@ def run_decode_ragged(args, csa, synth, wl, dev):
     def append(i):
         s = sets[i]
         csa.decode_append(s["kv_new"], s["gate_new"], s["pos"], wl.m, s["stage"],
-                          s["stage_gate"], s["codes"], s["scales"], s["win"])
+                          s["stage_gate"], s["codes"], s["scales"], s["win"], fmt=FMT)
 
     def scan(i):
         s = sets[i]
@@ -447,7 +457,7 @@ def run_decode_ragged(args, csa, synth, wl, dev):
         csa.index_select(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
                          workspace=s["ws"], pos_max=pos_max)
         csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, s["pos"],
-                        1.0, s["out"], workspace=s["ws_attn"], pos_max=pos_max)
+                        1.0, s["out"], workspace=s["ws_attn"], pos_max=pos_max, fmt=FMT)
 
     def step_fn(i):
         def f():
@@ -456,7 +466,7 @@ def run_decode_ragged(args, csa, synth, wl, dev):
             csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
                            workspace=s["ws"], pos_max=pos_max)
             csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, s["pos"],
-                            1.0, s["out"], workspace=s["ws_attn"], pos_max=pos_max)
+                            1.0, s["out"], workspace=s["ws_attn"], pos_max=pos_max, fmt=FMT)
         return f
 
     eager = [step_fn(i) for i in range(len(sets))]
@@ -498,7 +508,7 @@ def run_decode_ragged(args, csa, synth, wl, dev):
         "config": {
             "workload": wl.name, "batch": wl.B, "positions": pos, "d": wl.d, "m": wl.m,
             "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8", "top_k": wl.k, "window": wl.W,
-            "cache": "MXFP4 e2m1 + e8m0/32", "input_sets_rotated": args.sets,
+            "cache": CACHE_NAME[FMT], "input_sets_rotated": args.sets,
             "timing": timing_name(args),
         },
         "append_us": round(t_append * 1e3, 2),
@@ -559,7 +569,7 @@ def cpu_baseline_prefill(wl, x, keys, codes, scales, c, n_queries, min_seconds):
                 t = c * T + ti
                 t0 = time.perf_counter()
                 ri, _ = O.index_topk(qi[ti], wn[ti], kn, wl.m, t, wl.k)
-                ro, _ = O.sparse_attn(qb[ti], cn, sn, ri, win, wl.Wcap, wl.W, t, 1.0)
+                ro, _ = O.sparse_attn(qb[ti], cn, sn, ri, win, wl.Wcap, wl.W, t, 1.0, fmt=FMT)
                 t_total += time.perf_counter() - t0
                 if done < n_queries:
                     ok &= bool(np.array_equal(ri, gi[ti]))
@@ -579,7 +589,7 @@ def run_prefill(args, csa, synth, wl, dev):
     nch = wl.L // T
     t_setup = time.time()
     codes = torch.empty(1, wl.n_blocks, wl.d // 2, device=dev, dtype=torch.uint8)
-    scales = torch.empty(1, wl.n_blocks, wl.d // 32, device=dev, dtype=torch.uint8)
+    scales = torch.empty(1, wl.n_blocks, wl.d // SCALE_GROUP[FMT], device=dev, dtype=torch.uint8)
     keys = synth.indexer_keys(wl, dev)
     ch = []
     for c in range(nch):
@@ -597,7 +607,7 @@ def run_prefill(args, csa, synth, wl, dev):
 
     def compress(c):
         x = ch[c]
-        csa.compress_quantize(x["kv"], x["gate"], c * T, wl.m, codes, scales)
+        csa.compress_quantize(x["kv"], x["gate"], c * T, wl.m, codes, scales, fmt=FMT)
 
     def index(c):
         x = ch[c]
@@ -605,7 +615,8 @@ def run_prefill(args, csa, synth, wl, dev):
 
     def attend(c):
         x = ch[c]
-        csa.sparse_attn(x["q"], codes, scales, x["idx"], x["win"], wl.W, c * T, 1.0, x["out"])
+        csa.sparse_attn(x["q"], codes, scales, x["idx"], x["win"], wl.W, c * T, 1.0, x["out"],
+                        fmt=FMT)
 
     def step():
         for c in range(nch):
@@ -662,6 +673,7 @@ def run_prefill(args, csa, synth, wl, dev):
         "dtype": "bf16+fp16+int8",
         "data": "synthetic",
         "config": {"workload": wl.name, "context": wl.L, "chunk": T, "d": wl.d, "m": wl.m,
+                   "cache": CACHE_NAME[FMT],
                    "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8", "top_k": wl.k,
                    "window": wl.W, "timing": timing_name(args)},
         "kernels_ms_per_step": {"compress": round(t_cmp, 4), "index_topk": round(t_idx, 4),
@@ -746,7 +758,7 @@ def cpu_baseline_layers(s, wl, n_queries, n_groups, min_seconds):
                 qs = h["qs"]
                 t0 = time.perf_counter()
                 ho, _ = O.hca_dense_attn(h["hq"], h["hc"], h["hs"], wl.m_hca, h_win[b], wl.Wcap,
-                                         wl.W, t, 1.0)
+                                         wl.W, t, 1.0, fmt=FMT)
                 if n_groups:
                     pool = O.block_pool(qs["full"][0], qs["full"][1], keys[b], wl.m, t, 8,
                                         n_groups)
@@ -759,7 +771,7 @@ def cpu_baseline_layers(s, wl, n_queries, n_groups, min_seconds):
                     cand = None if (n_groups and layer == "full") else pool
                     ri, _ = O.index_topk(qi, wi, keys[b], wl.m, t, wl.k, cand=cand)
                     ro, _ = O.sparse_attn(qb, h["cn"], h["sn"], ri, win[b], wl.Wcap, wl.W, t,
-                                          1.0)
+                                          1.0, fmt=FMT)
                     outs[layer] = (ri, ro)
                 t_total += time.perf_counter() - t0
                 if done < n_queries:
@@ -799,7 +811,7 @@ def run_layers(args, csa, synth, wl, dev):
     def hca(i):
         s = sets[i]
         csa.hca_dense_attn(s["h_q"], s["h_codes"], s["h_scales"], wl.m_hca, s["h_win"], wl.W, t,
-                           1.0, s["h_out"], workspace=s["ws_attn"])
+                           1.0, s["h_out"], workspace=s["ws_attn"], fmt=FMT)
 
     def pool(i, fn="index_topk"):
         s = sets[i]
@@ -820,7 +832,7 @@ def run_layers(args, csa, synth, wl, dev):
             csa.index_topk(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.k, x["idx"],
                            cand=s["pool"], workspace=s["ws"])
         csa.sparse_attn(x["q"], s["codes"], s["scales"], x["idx"], s["win"], wl.W, t, 1.0,
-                        x["out"], workspace=s["ws_attn"])
+                        x["out"], workspace=s["ws_attn"], fmt=FMT)
 
     def step_fn(i):
         def f():
@@ -893,6 +905,7 @@ def run_layers(args, csa, synth, wl, dev):
         "dtype": "int8+bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "context": wl.L, "d": wl.d, "m": wl.m,
+                   "cache": CACHE_NAME[FMT],
                    "m_hca": wl.m_hca, "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8",
                    "pool": pool_len, "pool_kind": args.pool_kind,
                    **({"pool_groups": n_groups} if n_groups else {}),
@@ -941,6 +954,8 @@ def main():
                          "(entries) or a blockwise pool of 8-entry groups (blocks)")
     ap.add_argument("--pool-groups", type=int, default=0,
                     help="groups kept by the blockwise pool (default: pool / 8)")
+    ap.add_argument("--fmt", default="e8m0", choices=["e8m0", "e4m3"],
+                    help="FP4 cache scales: E8M0 per 32 channels (MXFP4) or E4M3 per 16")
     ap.add_argument("--cpu-queries", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time the cpu_baseline sample is repeated up to")
@@ -950,6 +965,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+    global FMT
+    FMT = args.fmt
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
         return

@@ -188,11 +188,9 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
           }
         } else {
           if (E4) {
-            const float sc = e4m3_to_f32(r.lo[u].z & 0xffu);
-            k0 = fp4x8_to_bf16_mul(r.lo[u].x, sc);
-            k1 = fp4x8_to_bf16_mul(r.lo[u].y, sc);
-            vh[u][0] = fp4x8_to_f16_mul(r.lo[u].x, sc);
-            vh[u][1] = fp4x8_to_f16_mul(r.lo[u].y, sc);
+            const _Float16 sc = (_Float16)e4m3_to_f32(r.lo[u].z & 0xffu);
+            fp4x8_e4m3_both(r.lo[u].x, sc, vh[u][0], k0);
+            fp4x8_e4m3_both(r.lo[u].y, sc, vh[u][1], k1);
           } else {
             const float sc = e8m0_to_f32(r.lo[u].z & 0xffu);
             k0 = fp4x8_to_bf16(r.lo[u].x, sc);

@@ -137,6 +137,17 @@ __device__ inline v8h fp4x8_to_f16_mul(uint32_t word, float scale) {
   return r;
 }
 
+// Both at once, for the attention staging: the products are formed in
+// float16 (exact: at most 5 significant bits, magnitudes 2^-10 .. 2688), and
+// the bfloat16 copy is converted from them. (The gfx950 scaled FP4
+// conversions use only the exponent of their scale operand, so they cannot
+// apply an E4M3 scale themselves.)
+__device__ inline void fp4x8_e4m3_both(uint32_t word, _Float16 scale, v8h& h, v8bf& bf) {
+  h = fp4x8_to_f16(word, 1.0f) * scale;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bf[i] = (__bf16)(float)h[i];
+}
+
 // ----------------------------------------------------------- indexer ----
 
 // Monotone (non-decreasing) map of a non-negative int32 score to one of 512
