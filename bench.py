@@ -5,9 +5,10 @@ Default workload, decode_1m: 8 sequences at 1,048,576 tokens, d=512, m=4
 128-token window. One step = csa_index_topk + csa_sparse_attn for one new
 query per sequence, on inputs resident in HBM. Several independent input
 sets are rotated so that the 134 MB of indexer keys per step is read from
-HBM rather than from the 256 MB Infinity Cache. Steps are enqueued eagerly
-(--graph captures one HIP graph per input set and replays those instead;
-on this path graph replay was measured slower than eager launches).
+HBM rather than from the 256 MB Infinity Cache. Steps are enqueued eagerly,
+each library call with its arguments marshalled once beforehand (--python-launch
+times the Python wrappers instead; --graph captures one HIP graph per input set
+and replays those, measured slower than eager launches on this path).
 
 Other workloads (--workload), each printing its own line:
   decode_32k      64 sequences at 32,768 tokens, top-512 (same step).
@@ -218,7 +219,21 @@ def host_bits(t):
 
 
 def timing_name(args):
-    return "hip graph replay" if args.graph else "eager launches"
+    if args.graph:
+        return "hip graph replay"
+    return "eager launches (Python wrappers)" if args.python_launch else "eager launches"
+
+
+def timed_runs(args, csa, steps):
+    """The callables the timed loop issues, one per input set: HIP graph
+    replays (--graph), the Python wrappers themselves (--python-launch), or by
+    default the same library calls with their arguments marshalled once
+    (csa.prepare), as a serving loop that reuses its buffers would issue them."""
+    if args.graph:
+        return [g.replay for g in capture_graphs(steps)]
+    if args.python_launch:
+        return steps
+    return [csa.prepare(f) for f in steps]
 
 
 # --------------------------------------------------------------------------
@@ -294,7 +309,7 @@ def run_decode(args, csa, synth, wl, dev):
     for f in eager:
         f()
     torch.cuda.synchronize()
-    runs = [g.replay for g in capture_graphs(eager)] if args.graph else eager
+    runs = timed_runs(args, csa, eager)
     secs = time_steps(runs, args.steps, args.warmup)
     ms_per_step = secs * 1e3 / args.steps
     value = wl.B * args.steps / secs
@@ -473,7 +488,7 @@ def run_decode_ragged(args, csa, synth, wl, dev):
     for f in eager:
         f()
     torch.cuda.synchronize()
-    runs = [g.replay for g in capture_graphs(eager)] if args.graph else eager
+    runs = timed_runs(args, csa, eager)
     secs = time_steps(runs, args.steps, args.warmup)
     ms_per_step = secs * 1e3 / args.steps
     value = wl.B * args.steps / secs
@@ -626,7 +641,7 @@ def run_prefill(args, csa, synth, wl, dev):
 
     step()
     torch.cuda.synchronize()
-    runs = [g.replay for g in capture_graphs([step])] if args.graph else [step]
+    runs = timed_runs(args, csa, [step])
     secs = time_steps(runs, args.steps, args.warmup)
     ms_per_step = secs * 1e3 / args.steps
     value = wl.L * args.steps / secs
@@ -846,7 +861,7 @@ def run_layers(args, csa, synth, wl, dev):
     for f in eager:
         f()
     torch.cuda.synchronize()
-    runs = [g.replay for g in capture_graphs(eager)] if args.graph else eager
+    runs = timed_runs(args, csa, eager)
     secs = time_steps(runs, args.steps, args.warmup)
     ms_per_step = secs * 1e3 / args.steps
     value = wl.B * args.steps / secs
@@ -960,6 +975,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time the cpu_baseline sample is repeated up to")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--python-launch", action="store_true",
+                    help="time the Python wrappers instead of pre-marshalled calls")
     ap.add_argument("--graph", action="store_true",
                     help="time HIP graph replays instead of eager launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

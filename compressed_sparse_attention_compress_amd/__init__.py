@@ -21,6 +21,7 @@ __all__ = [
     "workspace_clear",
     "sparse_attn",
     "hca_dense_attn", "attn_workspace", "Workspace", "BF16", "F32", "F16", "EXPORTED",
+    "prepare",
 ]
 
 BF16, F32, F16 = 0, 1, 2
@@ -47,9 +48,50 @@ class CSAError(RuntimeError):
 
 
 _lib = None
+_RECORD = None  # list of (C function, marshalled arguments) while prepare() runs
+_QUERIES = ("csa_status_string", "csa_version", "csa_cache_bytes")
 
 
-def lib() -> ctypes.CDLL:
+class _RecordingLib:
+    """The library seen through prepare(): size queries pass through, every
+    other call is stored with its marshalled arguments instead of issued."""
+
+    def __init__(self, L):
+        self._L = L
+
+    def __getattr__(self, name):
+        fn = getattr(self._L, name)
+        if name.endswith("_workspace") or name in _QUERIES:
+            return fn
+
+        def record(*args):
+            _RECORD.append((name, fn, args))
+            return 0
+        return record
+
+
+def prepare(fn):
+    """Run fn() once with every library launch it makes marshalled and stored
+    instead of issued (workspaces are sized and allocated now). Returns a
+    callable that issues exactly those launches again, on the streams that
+    were current when they were recorded, with the same buffers: the argument
+    marshalling of a serving loop done once."""
+    global _RECORD
+    _RECORD = []
+    try:
+        fn()
+    finally:
+        calls, _RECORD = _RECORD, None
+
+    def run():
+        for name, f, args in calls:
+            st = f(*args)
+            if st:
+                _check(st, name)
+    return run
+
+
+def lib():
     """The loaded libcsa.so (raises if it was never built)."""
     global _lib
     if _lib is None:
@@ -97,7 +139,7 @@ def lib() -> ctypes.CDLL:
             fn.restype = res
             fn.argtypes = args
         _lib = L
-    return _lib
+    return _lib if _RECORD is None else _RecordingLib(_lib)
 
 
 def _check(status: int, what: str):

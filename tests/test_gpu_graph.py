@@ -119,3 +119,40 @@ def test_graph_replay_decode():
         o, _ = O.hca_dense_attn(qb[b, 0], hcn[b], hsn[b], hca_m, winb[b], winb.shape[1], W, t, 1.0)
         ex, _ = attn_excess_error(to_np(ref[5])[b, 0][None], o[None], False)
         assert ex <= REL_TOL, ex
+
+
+def test_prepared_calls_replay():
+    """csa.prepare records a step's launches with their marshalled arguments;
+    replaying them reproduces the eager results bit for bit, also after other
+    calls have used the same workspaces, and recording issues nothing."""
+    B, L, d, H, m, Hi, Di, k, W = 2, 4 * 6000, 512, 64, 4, 8, 64, 256, 128
+    t = L - 1
+    x = _world(6, B, L, d, H, m, Hi, Di)
+    ws, ws_a = csa.Workspace(DEV), csa.Workspace(DEV)
+    idx = torch.full((B, 1, k), -5, device=DEV, dtype=torch.int32)
+    out = torch.zeros(B, 1, H, d, device=DEV, dtype=torch.bfloat16)
+
+    def step():
+        csa.index_topk(x["q_idx"], x["w"], x["keys"], m, t, k, idx, workspace=ws)
+        csa.sparse_attn(x["q"], x["codes"], x["scales"], idx, x["win"], W, t, 1.0, out,
+                        workspace=ws_a)
+
+    run = csa.prepare(step)
+    torch.cuda.synchronize()
+    assert (idx == -5).all() and (out == 0).all()   # nothing was issued while recording
+    step()
+    torch.cuda.synchronize()
+    ref_i, ref_o = idx.clone(), out.clone()
+    other = _world(7, B, L, d, H, m, Hi, Di)
+    o_idx = torch.empty_like(idx)
+    for r in range(3):
+        idx.fill_(-3)
+        out.fill_(7)
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_i) and torch.equal(out, ref_o), r
+        csa.index_topk(other["q_idx"], other["w"], other["keys"], m, t - 9, k, o_idx, workspace=ws)
+    kn, qin, wn = x["keys"].cpu().numpy(), x["q_idx"].cpu().numpy(), x["w"].cpu().numpy()
+    for b in range(B):
+        ri, _ = O.index_topk(qin[b, 0], wn[b, 0], kn[b], m, t, k)
+        assert np.array_equal(ref_i[b, 0].cpu().numpy(), ri)
