@@ -459,6 +459,182 @@ __global__ __launch_bounds__(256) void k_idx_select(int T, int m, int64_t pos0,
   if (threadIdx.x == 0) cnt[(int64_t)qi * n_tiles + tile] = total;
 }
 
+// Exact k-th score among LDS candidates: cs[0..M) holds scores, those in
+// bin T1 span [lo, hi], and `need` of them are still to be taken. Radix
+// refinement over (score - lo): a 256-bin histogram of the remaining range
+// per round, narrowed to the bin where the count from the top reaches need.
+// Returns tau; *take_eq = how many candidates equal to tau are taken. All
+// 256 threads call it; it ends with a barrier.
+__device__ inline int refine_tau(const int* cs, int M, int T1, int lo, int hi, int need,
+                                 uint32_t* bh, int* tmp, int* s_red, int* take_eq) {
+  int R = hi - lo;
+  while (R > 0) {
+    const int bits = 32 - __clz(R);
+    const int shift = bits > 8 ? bits - 8 : 0;
+    bh[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < M; i += 256) {
+      const int sv = cs[i];
+      if (score_bin512(sv) == T1 && sv >= lo && sv - lo <= R)
+        atomicAdd(&bh[(sv - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    const int v = (int)bh[255 - threadIdx.x];
+    int tot;
+    const int inc = wg_scan_incl<256>(v, tmp, &tot);
+    if (inc >= need && inc - v < need) {
+      s_red[0] = 255 - (int)threadIdx.x;
+      s_red[1] = need - (inc - v);
+    }
+    __syncthreads();
+    const int beta = s_red[0];
+    need = s_red[1];
+    __syncthreads();
+    lo += beta << shift;
+    R = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
+  }
+  *take_eq = need;
+  return lo;
+}
+
+// Ordered emission of the selected candidates of cs/ce[0..M) (kept in index
+// order): thread j owns entries [8j, 8j + 8) of each 2048-entry round; one
+// scan of the packed (greater, equal) counts gives every entry's output
+// position: #greater before it + min(#equal before it, take_eq).
+// emit(pos, ce[i], cs[i]) for the keff selected ones.
+template <class Emit>
+__device__ inline void emit_ordered(const int* cs, const int* ce, int M, int tau, int take_eq,
+                                    int keff, int* tmp, Emit emit) {
+  int run_gt = 0, run_eq = 0;
+  for (int r0 = 0; r0 < M; r0 += 2048) {
+    const int i0 = r0 + 8 * (int)threadIdx.x;
+    int sv[8];
+    int gtc = 0, eqc = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sv[j] = i0 + j < M ? cs[i0 + j] : -1;
+      gtc += sv[j] > tau;
+      eqc += sv[j] == tau;
+    }
+    const int mine = (gtc << 16) | eqc;
+    int tot;
+    const int before = wg_scan_incl<256>(mine, tmp, &tot) - mine;
+    int gb = run_gt + (before >> 16), eb = run_eq + (before & 0xffff);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int pos = -1;
+      if (sv[j] > tau) {
+        pos = gb + min(eb, take_eq);
+        ++gb;
+      } else if (sv[j] == tau) {
+        if (eb < take_eq) pos = gb + eb;
+        ++eb;
+      }
+      if (pos >= 0 && pos < keff) emit(pos, ce[i0 + j], sv[j]);
+    }
+    run_gt += tot >> 16;
+    run_eq += tot & 0xffff;
+  }
+}
+
+// ------------------------------------------------------------------------
+// small candidate pools, phase 2: one workgroup per query
+// ------------------------------------------------------------------------
+// For a Reindex pool of at most SMALL_C entries the per-tile select pass is
+// not needed: one workgroup per query loads the query's whole score row and
+// histogram (left by k_idx_scan), finds the threshold bin, compacts the
+// scores at or above it in pool order, then refine_tau and emit_ordered as in
+// k_idx_final. It clears the histogram for the next call.
+constexpr int SMALL_C = 4096;
+__global__ __launch_bounds__(256) void k_idx_pick(int C, int k, int64_t npad,
+                                                  const int32_t* __restrict__ slab,
+                                                  uint32_t* __restrict__ hist,
+                                                  const int32_t* __restrict__ cand,
+                                                  int32_t* __restrict__ out_idx,
+                                                  int32_t* __restrict__ out_score) {
+  constexpr int PER = SMALL_C / 256;  // pool positions per thread
+  __shared__ int cs[SMALL_C];
+  __shared__ int ce[SMALL_C];
+  __shared__ uint32_t bh[256];
+  __shared__ int tmp[4];
+  __shared__ int s_red[8];
+  const int qi = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t* sq = slab + (int64_t)qi * npad;
+  const int32_t* cq = cand + (int64_t)qi * C;
+  uint32_t* hq = hist + (int64_t)qi * NB1;
+  // this thread's 16 scores (pool positions [16j, 16j + 16)), issued before
+  // the histogram scan so that both loads overlap
+  const int p0 = PER * (int)threadIdx.x;
+  int sv[PER];
+  if (p0 + PER <= C) {
+#pragma unroll
+    for (int j = 0; j < PER; j += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(sq + p0 + j);
+      sv[j] = v.x; sv[j + 1] = v.y; sv[j + 2] = v.z; sv[j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) sv[j] = p0 + j < C ? sq[p0 + j] : -1;
+  }
+  const int keff = threshold_bin(hq, k, tmp, s_red);
+  // histogram consumed: clear it for the next call (thread j owns two bins)
+  hq[NB1 - 1 - 2 * (int)threadIdx.x] = 0u;
+  hq[NB1 - 2 - 2 * (int)threadIdx.x] = 0u;
+  int32_t* oi = out_idx + (int64_t)qi * k;
+  int32_t* os = out_score ? out_score + (int64_t)qi * k : nullptr;
+  for (int i = keff + threadIdx.x; i < k; i += 256) {
+    oi[i] = -1;
+    if (os) os[i] = -1;
+  }
+  if (keff == 0) return;
+  const int T1 = s_red[0];
+  const int need = keff - s_red[1];
+  __syncthreads();
+  // in-order compaction of the scores at or above bin T1, and the score
+  // range of bin T1
+  int f = 0;
+  int vmin = 0x7fffffff, vmax = -1;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool in = sv[j] >= 0 && score_bin512(sv[j]) >= T1;
+    f += in;
+    if (in && score_bin512(sv[j]) == T1) {
+      vmin = min(vmin, sv[j]);
+      vmax = max(vmax, sv[j]);
+    }
+  }
+  int M;
+  int at = wg_scan_incl<256>(f, tmp, &M) - f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (sv[j] >= 0 && score_bin512(sv[j]) >= T1) {
+      cs[at] = sv[j];
+      ce[at] = p0 + j;
+      ++at;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    vmin = min(vmin, __shfl_xor(vmin, off, 64));
+    vmax = max(vmax, __shfl_xor(vmax, off, 64));
+  }
+  if (lane == 0) {
+    s_red[wave] = vmin;
+    s_red[4 + wave] = vmax;
+  }
+  __syncthreads();
+  const int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
+  const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
+  __syncthreads();
+  int take_eq;
+  const int tau = refine_tau(cs, M, T1, lo, hi, need, bh, tmp, s_red, &take_eq);
+  emit_ordered(cs, ce, M, tau, take_eq, keff, tmp, [&](int pos, int e, int v) {
+    oi[pos] = cq[e];
+    if (os) os[pos] = v;
+  });
+}
+
 // ------------------------------------------------------------------------
 // split scan, phase 2b: one workgroup per query resolves the exact k-th score
 // among the candidates and writes the ascending index list
@@ -620,71 +796,12 @@ __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
       s_red[4 + wave] = vmax;
     }
     __syncthreads();
-    int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
+    const int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
     const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
     __syncthreads();
-    int R = hi - lo;
-    while (R > 0) {
-      const int bits = 32 - __clz(R);
-      const int shift = bits > 8 ? bits - 8 : 0;
-      bh[threadIdx.x] = 0;
-      __syncthreads();
-      for (int i = threadIdx.x; i < M; i += 256) {
-        const int sv = cs[i];
-        if (score_bin512(sv) == T1 && sv >= lo && sv - lo <= R)
-          atomicAdd(&bh[(sv - lo) >> shift], 1u);
-      }
-      __syncthreads();
-      const int v = (int)bh[255 - threadIdx.x];
-      int tot;
-      const int inc = wg_scan_incl<256>(v, tmp, &tot);
-      if (inc >= need && inc - v < need) {
-        s_red[0] = 255 - (int)threadIdx.x;
-        s_red[1] = need - (inc - v);
-      }
-      __syncthreads();
-      const int beta = s_red[0];
-      need = s_red[1];
-      __syncthreads();
-      lo += beta << shift;
-      R = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
-    }
-    const int tau = lo;
-    const int take_eq = need;
-    // ordered emission: thread j owns entries [8j, 8j + 8) of each 2048-entry
-    // round; one scan of the packed (greater, equal) counts gives every
-    // entry's output position: #greater before it + min(#equal before it,
-    // take_eq)
-    int run_gt = 0, run_eq = 0;
-    for (int r0 = 0; r0 < M; r0 += 2048) {
-      const int i0 = r0 + 8 * (int)threadIdx.x;
-      int sv[8];
-      int gtc = 0, eqc = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        sv[j] = i0 + j < M ? cs[i0 + j] : -1;
-        gtc += sv[j] > tau;
-        eqc += sv[j] == tau;
-      }
-      const int mine = (gtc << 16) | eqc;
-      int tot;
-      const int before = wg_scan_incl<256>(mine, tmp, &tot) - mine;
-      int gb = run_gt + (before >> 16), eb = run_eq + (before & 0xffff);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        int pos = -1;
-        if (sv[j] > tau) {
-          pos = gb + min(eb, take_eq);
-          ++gb;
-        } else if (sv[j] == tau) {
-          if (eb < take_eq) pos = gb + eb;
-          ++eb;
-        }
-        if (pos >= 0 && pos < keff) emit(pos, ce[i0 + j], sv[j]);
-      }
-      run_gt += tot >> 16;
-      run_eq += tot & 0xffff;
-    }
+    int take_eq;
+    const int tau = refine_tau(cs, M, T1, lo, hi, need, bh, tmp, s_red, &take_eq);
+    emit_ordered(cs, ce, M, tau, take_eq, keff, tmp, emit);
     return;
   }
 
@@ -930,6 +1047,14 @@ static int idx_phase(const IdxArgs& a, int phase) {
   uint32_t* ghist = reinterpret_cast<uint32_t*>(ws + L.off_ghist);
   int32_t* gcnt = reinterpret_cast<int32_t*>(ws + L.off_gcnt);
   const int C = a.cand ? a.C : 0;
+  const bool small = a.cand && C > 0 && C <= SMALL_C && !pool;
+  if (small && phase == 1) {
+    // the select and final passes in one workgroup per query
+    hipLaunchKernelGGL(k_idx_pick, dim3(BT), dim3(256), 0, a.stream, C, a.k, L.npad, slab, hist,
+                       a.cand, a.out_idx, a.out_score);
+    CSA_TRY_LAUNCH();
+    return CSA_OK;
+  }
   if (phase == 0 && batched_plan(a)) {
     const int HP = a.Hi <= 4 ? 4 : (a.Hi <= 8 ? 8 : 16);
     const int KS = (a.Di + 63) / 64;

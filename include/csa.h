@@ -224,7 +224,9 @@ int csa_index_select_ragged(const int8_t* q_idx, const int8_t* w, const int8_t* 
  * csa_index_select with identical arguments. Scan computes every exact score
  * into the workspace (one key stream per query for T < 16 or a pool; for
  * runs of T >= 16 queries one key stream per group of 8-32 queries) plus a
- * per-query score histogram; select turns them into the sorted index list. */
+ * per-query score histogram; select turns them into the sorted index list.
+ * For a candidate pool of at most 4096 entries, select is one workgroup per
+ * query that reads the query's whole score row (one launch instead of two). */
 int csa_index_scan(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
                    int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
                    const int32_t* cand, int C, int k,

@@ -185,6 +185,14 @@ def test_index_candidates():
     _index_case(4, 1, 8, 64, 4, 4 * 10000 - 1, 128, 10000, seed=14, cand_C=4096)
     _index_case(2, 2, 8, 64, 4, 4 * 3000 - 1, 512, 3000, seed=15, cand_C=600)
     _index_case(2, 1, 8, 64, 4, 4 * 3000 - 1, 64, 3000, seed=16, cand_C=300, wzero=True)
+    # pools of at most 4096 entries take the one-workgroup select: both phases,
+    # massive ties, k above the pool, 32- and 128-dim keys, a pool of one tile
+    _index_case(2, 2, 8, 64, 4, 4 * 3000 - 1, 128, 3000, seed=30, cand_C=600, phases=True)
+    _index_case(2, 1, 8, 64, 4, 4 * 3000 - 1, 200, 3000, seed=31, cand_C=1000, keyrange=1)
+    _index_case(2, 1, 8, 64, 4, 4 * 3000 - 1, 512, 3000, seed=32, cand_C=300)
+    _index_case(3, 1, 4, 32, 4, 4 * 5000 - 1, 256, 5000, seed=33, cand_C=4096)
+    _index_case(2, 1, 4, 128, 4, 4 * 5000 - 1, 100, 5000, seed=34, cand_C=2049)
+    _index_case(1, 1, 8, 64, 4, 4 * 5000 - 1, 16, 5000, seed=35, cand_C=13)
 
 
 def test_index_many_queries():
