@@ -538,36 +538,47 @@ __device__ inline void emit_ordered(const int* cs, const int* ce, int M, int tau
 }
 
 // ------------------------------------------------------------------------
-// small candidate pools, phase 2: one workgroup per query
+// small selections, phase 2: one workgroup per query
 // ------------------------------------------------------------------------
-// For a Reindex pool of at most SMALL_C entries the per-tile select pass is
-// not needed: one workgroup per query loads the query's whole score row and
+// When a query has at most PICK_MAX candidates (a small Reindex pool, or a
+// context of at most PICK_MAX entries) the per-tile select pass is not
+// needed: one workgroup per query loads the query's whole score row and
 // histogram (left by k_idx_scan), finds the threshold bin, compacts the
-// scores at or above it in pool order, then refine_tau and emit_ordered as in
-// k_idx_final. It clears the histogram for the next call.
-constexpr int SMALL_C = 4096;
-__global__ __launch_bounds__(256) void k_idx_pick(int C, int k, int64_t npad,
+// scores at or above it in index order, then refine_tau and emit_ordered as
+// in k_idx_final. It clears the histogram for the next call. PER = entries
+// per thread (PICK_MAX / 256 at most).
+constexpr int PICK_MAX = 8192;
+template <int PER>
+__global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
+                                                  const int64_t* __restrict__ qpos,
+                                                  int64_t blk_cap, int C, int k, int64_t npad,
                                                   const int32_t* __restrict__ slab,
                                                   uint32_t* __restrict__ hist,
                                                   const int32_t* __restrict__ cand,
                                                   int32_t* __restrict__ out_idx,
                                                   int32_t* __restrict__ out_score) {
-  constexpr int PER = SMALL_C / 256;  // pool positions per thread
-  __shared__ int cs[SMALL_C];
-  __shared__ int ce[SMALL_C];
+  __shared__ int cs[PER * 256];
+  __shared__ int ce[PER * 256];
   __shared__ uint32_t bh[256];
   __shared__ int tmp[4];
   __shared__ int s_red[8];
   const int qi = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int N;  // candidates of the query: the pool, or its visible entries
+  {
+    const int b = qi / T;
+    int64_t nv = (query_base(qpos, pos0, b) + (qi - b * T) + 1) / m;
+    nv = nv < blk_cap ? nv : blk_cap;
+    N = cand ? C : (int)nv;
+  }
   const int32_t* sq = slab + (int64_t)qi * npad;
-  const int32_t* cq = cand + (int64_t)qi * C;
+  const int32_t* cq = cand ? cand + (int64_t)qi * C : nullptr;
   uint32_t* hq = hist + (int64_t)qi * NB1;
-  // this thread's 16 scores (pool positions [16j, 16j + 16)), issued before
+  // this thread's PER scores (positions [PER j, PER j + PER)), issued before
   // the histogram scan so that both loads overlap
   const int p0 = PER * (int)threadIdx.x;
   int sv[PER];
-  if (p0 + PER <= C) {
+  if (p0 + PER <= N) {
 #pragma unroll
     for (int j = 0; j < PER; j += 4) {
       const int4 v = *reinterpret_cast<const int4*>(sq + p0 + j);
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(256) void k_idx_pick(int C, int k, int64_t npad,
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) sv[j] = p0 + j < C ? sq[p0 + j] : -1;
+    for (int j = 0; j < PER; ++j) sv[j] = p0 + j < N ? sq[p0 + j] : -1;
   }
   const int keff = threshold_bin(hq, k, tmp, s_red);
   // histogram consumed: clear it for the next call (thread j owns two bins)
@@ -630,7 +641,7 @@ __global__ __launch_bounds__(256) void k_idx_pick(int C, int k, int64_t npad,
   int take_eq;
   const int tau = refine_tau(cs, M, T1, lo, hi, need, bh, tmp, s_red, &take_eq);
   emit_ordered(cs, ce, M, tau, take_eq, keff, tmp, [&](int pos, int e, int v) {
-    oi[pos] = cq[e];
+    oi[pos] = cq ? cq[e] : e;
     if (os) os[pos] = v;
   });
 }
@@ -1047,11 +1058,17 @@ static int idx_phase(const IdxArgs& a, int phase) {
   uint32_t* ghist = reinterpret_cast<uint32_t*>(ws + L.off_ghist);
   int32_t* gcnt = reinterpret_cast<int32_t*>(ws + L.off_gcnt);
   const int C = a.cand ? a.C : 0;
-  const bool small = a.cand && C > 0 && C <= SMALL_C && !pool;
-  if (small && phase == 1) {
-    // the select and final passes in one workgroup per query
-    hipLaunchKernelGGL(k_idx_pick, dim3(BT), dim3(256), 0, a.stream, C, a.k, L.npad, slab, hist,
-                       a.cand, a.out_idx, a.out_score);
+  // a query with at most PICK_MAX candidates: the select and final passes in
+  // one workgroup per query
+  if (!pool && n_max > 0 && n_max <= PICK_MAX && phase == 1) {
+    if (n_max <= PICK_MAX / 2)
+      hipLaunchKernelGGL(k_idx_pick<PICK_MAX / 512>, dim3(BT), dim3(256), 0, a.stream, a.T, a.m,
+                         a.pos0, a.pos, a.blk_cap, C, a.k, L.npad, slab, hist, a.cand, a.out_idx,
+                         a.out_score);
+    else
+      hipLaunchKernelGGL(k_idx_pick<PICK_MAX / 256>, dim3(BT), dim3(256), 0, a.stream, a.T, a.m,
+                         a.pos0, a.pos, a.blk_cap, C, a.k, L.npad, slab, hist, a.cand, a.out_idx,
+                         a.out_score);
     CSA_TRY_LAUNCH();
     return CSA_OK;
   }
