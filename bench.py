@@ -151,6 +151,27 @@ def time_steps(runs, steps, warmup):
     return time.perf_counter() - t0
 
 
+def back_to_back_ms(fn, n_sets, reps, workspaces):
+    """Average device time (ms) of fn(i) launched `reps` times back to back
+    (i rotating over the input sets) between two events on the current
+    stream, so that the event overhead is spread over all launches. fn is a
+    scan phase, which adds into the workspaces' histograms: they are zeroed
+    afterwards."""
+    import torch
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn(0)
+    a.record(stream)
+    for r in range(reps):
+        fn(r % n_sets)
+    b.record(stream)
+    torch.cuda.synchronize()
+    for ws in workspaces:
+        ws.buf.zero_()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def split_event_ms(first, second, n_sets, reps):
     """Average device time (ms) of first(i) measured with events on the
     current stream, second(i) following it untimed; i rotates over sets."""
@@ -289,13 +310,6 @@ def run_decode(args, csa, synth, wl, dev):
         csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
                        workspace=s["ws"])
 
-    def select_attend(i):
-        s = sets[i]
-        csa.index_select(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
-                         workspace=s["ws"])
-        csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, pos, 1.0,
-                        s["out"], workspace=s["ws_attn"], fmt=FMT)
-
     def step_fn(i):
         def f():
             s = sets[i]
@@ -316,7 +330,8 @@ def run_decode(args, csa, synth, wl, dev):
     log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s ({timing_name(args)})")
 
     # dominant kernel: the indexer scan, timed with events on its launch stream
-    scan_ms = split_event_ms(scan, select_attend, len(sets), args.steps)
+    # over back-to-back launches
+    scan_ms = back_to_back_ms(scan, len(sets), args.steps, [s["ws"] for s in sets])
     scan_bytes = scan_bytes_per_query(wl) * wl.B
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     per_q = decode_bytes_per_query(wl)
@@ -467,13 +482,6 @@ def run_decode_ragged(args, csa, synth, wl, dev):
         csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
                        workspace=s["ws"], pos_max=pos_max)
 
-    def select_attend(i):
-        s = sets[i]
-        csa.index_select(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
-                         workspace=s["ws"], pos_max=pos_max)
-        csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, s["pos"],
-                        1.0, s["out"], workspace=s["ws_attn"], pos_max=pos_max, fmt=FMT)
-
     def step_fn(i):
         def f():
             s = sets[i]
@@ -495,7 +503,7 @@ def run_decode_ragged(args, csa, synth, wl, dev):
     log(f"ragged step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s ({timing_name(args)})")
 
     # dominant kernel: the ragged indexer scan, timed with events on its stream
-    scan_ms = split_event_ms(scan, select_attend, len(sets), args.steps)
+    scan_ms = back_to_back_ms(scan, len(sets), args.steps, [s["ws"] for s in sets])
     t_append = split_event_ms(append, None, len(sets), args.steps)
     pos = wl.positions()
     scan_bytes = sum((t + 1) // wl.m * wl.Di + wl.Hi * wl.Di + wl.Hi for t in pos)
@@ -873,8 +881,8 @@ def run_layers(args, csa, synth, wl, dev):
     t_pool = split_event_ms(pool, None, n_sets, reps)
     t_full = split_event_ms(lambda i: csa_layer(i, "full"), None, n_sets, reps)
     t_re = split_event_ms(lambda i: csa_layer(i, "reindex1"), None, n_sets, reps)
-    scan_ms = split_event_ms(lambda i: pool(i, "index_scan"),
-                             lambda i: pool(i, "index_select"), n_sets, reps)
+    scan_ms = back_to_back_ms(lambda i: pool(i, "index_scan"), n_sets, reps,
+                              [s["ws"] for s in sets])
     nv = wl.L // wl.m
     scan_bytes = scan_bytes_per_query(wl) * wl.B
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
