@@ -116,24 +116,33 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     if (POOL) lhg[i] = 0;
   }
 
+  // query rows and head weights: every load unconditional (indexes clamped
+  // into the row, padding masked afterwards), so that all of them are in
+  // flight together instead of one round trip each
   v4i A[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int c0 = ks * 64 + 16 * g;
-    if (i16 < Hi && c0 < DI)
-      A[ks] = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)qi * Hi + i16) * DI + c0);
-    else
-      A[ks] = v4i{0, 0, 0, 0};
+    const int hr = i16 < Hi ? i16 : Hi - 1;
+    const v4i v = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)qi * Hi + hr) * DI +
+                                                (c0 < DI ? c0 : 0));
+    A[ks] = (i16 < Hi && c0 < DI) ? v : v4i{0, 0, 0, 0};
   }
   int wr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * g + r;
-    wr[r] = h < Hi ? (int)w[(int64_t)qi * Hi + h] : 0;
+    const int wv = (int)w[(int64_t)qi * Hi + (h < Hi ? h : Hi - 1)];
+    wr[r] = h < Hi ? wv : 0;
   }
   __syncthreads();
 
-  const int64_t e_wave = wg0 + wave * (SPAN / 4);
+  // column tile u of batch bt of this wave: the workgroup's 4 waves take
+  // interleaved 16-entry tiles, so each batch of the workgroup reads one
+  // contiguous 4 x BATCH KiB stretch of keys
+  auto tile_e = [&](int bt, int u) -> int64_t {
+    return wg0 + ((int64_t)(bt * BATCH + u) * 4 + wave) * 16;
+  };
   const int8_t* kb = keys + (int64_t)b * blk_cap * DI;
   const int32_t* cq = CAND ? cand + (int64_t)qi * C : nullptr;
   int32_t* sq = slab + (int64_t)qi * npad;
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) coff[ks] = (ks * 64 + 16 * g) % DI;
   const bool loads_ok = nv > 0;  // some key row exists to clamp to
-  if (e_wave < N) {
+  if (wg0 < N) {
     // two register buffers: the keys of batch bt + 1 are in flight while
     // batch bt is in the matrix cores
     constexpr int NBT = SPAN / 4 / 16 / BATCH;  // batches of BATCH column tiles per wave
@@ -157,15 +166,14 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
       for (int bt = 0; bt < NBT; ++bt)
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-          const int64_t e = e_wave + (int64_t)bt * BATCH * 16 + u * 16 + i16;
+          const int64_t e = tile_e(bt, u) + i16;
           cid[CAND ? bt : 0][u] = cq[e < N ? e : N - 1];
         }
     }
     auto issue = [&](int buf, int bt) {
-      const int64_t ebase = e_wave + (int64_t)bt * BATCH * 16;
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
-        const int64_t e = ebase + u * 16 + i16;
+        const int64_t e = tile_e(bt, u) + i16;
         int64_t blk;
         if (CAND) {
           const int64_t c = cid[CAND ? bt : 0][u];
@@ -183,18 +191,17 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
       }
     };
     auto consume = [&](int buf, int bt) {
-      const int64_t ebase = e_wave + (int64_t)bt * BATCH * 16;
       int sc[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int s = score_tile<KS>(A, Bk[buf][u], wr);
         sc[u] = valid[buf][u] ? s : -1;
       }
-      // lane (j + 16g) takes tile 4h+g, entry j: 64 consecutive entries
+      // lane (j + 16g) takes tile 4h+g, entry j
 #pragma unroll
       for (int h = 0; h < BATCH / 4; ++h) {
         const int v = g == 0 ? sc[4 * h] : (g == 1 ? sc[4 * h + 1] : (g == 2 ? sc[4 * h + 2] : sc[4 * h + 3]));
-        const int64_t e = ebase + 64 * h + lane;
+        const int64_t e = tile_e(bt, 4 * h + g) + i16;
         if (e < N) {
           ssc[e - wg0] = v;
           if (v >= 0) atomicAdd(&lh[score_bin512(v)], 1u);
@@ -274,21 +281,22 @@ __global__ __launch_bounds__(256) void k_idx_bscan(
   for (int rt = 0; rt < RT; ++rt) {
     const int ti = t0 + rt * QPT + i16 / HP;
     const int h = i16 % HP;
+    // unconditional loads, clamped indexes, padding masked afterwards
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c0 = ks * 64 + 16 * g;
-      if (ti < T && h < Hi && c0 < DI)
-        A[rt][ks] = *reinterpret_cast<const v4i*>(
-            q_idx + (((int64_t)b * T + ti) * Hi + h) * DI + c0);
-      else
-        A[rt][ks] = v4i{0, 0, 0, 0};
+      const int tc = ti < T ? ti : T - 1, hc = h < Hi ? h : Hi - 1;
+      const v4i v = *reinterpret_cast<const v4i*>(
+          q_idx + (((int64_t)b * T + tc) * Hi + hc) * DI + (c0 < DI ? c0 : 0));
+      A[rt][ks] = (ti < T && h < Hi && c0 < DI) ? v : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * g + r;
       const int tq = t0 + rt * QPT + row / HP;
       const int hh = row % HP;
-      wr[rt][r] = (tq < T && hh < Hi) ? (int)w[((int64_t)b * T + tq) * Hi + hh] : 0;
+      const int wv = (int)w[((int64_t)b * T + (tq < T ? tq : T - 1)) * Hi + (hh < Hi ? hh : Hi - 1)];
+      wr[rt][r] = (tq < T && hh < Hi) ? wv : 0;
     }
   }
   // the score lanes: lane group g holds query g / GPQ of each row tile; the
