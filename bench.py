@@ -730,7 +730,7 @@ def run_prefill(args, csa, synth, wl, dev):
 LAYERS = ("full", "reindex1", "reindex2")
 
 
-def layers_set(csa, synth, wl, dev, seed, pool_len):
+def layers_set(csa, synth, wl, dev, seed, pool_len, n_reuse):
     import torch
     t = wl.L - 1
     s = {}
@@ -747,6 +747,10 @@ def layers_set(csa, synth, wl, dev, seed, pool_len):
         s[layer] = dict(q_idx=q_idx, w=w, q=synth.queries(wl, dev, seed, layer=layer),
                         idx=torch.empty(wl.B, 1, wl.k, device=dev, dtype=torch.int32),
                         out=torch.empty(wl.B, 1, wl.H, wl.d, device=dev, dtype=torch.bfloat16))
+    # Reuse layers: their own queries, the Full layer's top-k ([PODCAST] cue 12)
+    s["reuse"] = [dict(q=synth.queries(wl, dev, seed, layer=f"reuse{j}"),
+                       out=torch.empty(wl.B, 1, wl.H, wl.d, device=dev, dtype=torch.bfloat16))
+                  for j in range(n_reuse)]
     s["ws"] = csa.Workspace(dev)
     s["ws_attn"] = csa.Workspace(dev)
     return s
@@ -772,7 +776,8 @@ def cpu_baseline_layers(s, wl, n_queries, n_groups, min_seconds):
             hc=s["h_codes"][b].cpu().numpy(), hs=s["h_scales"][b].cpu().numpy(),
             hq=host_bits(s["h_q"])[b, 0],
             qs={layer: (s[layer]["q_idx"][b, 0].cpu().numpy(), s[layer]["w"][b, 0].cpu().numpy(),
-                        host_bits(s[layer]["q"])[b, 0]) for layer in LAYERS}))
+                        host_bits(s[layer]["q"])[b, 0]) for layer in LAYERS},
+            rq=[host_bits(r["q"])[b, 0] for r in s["reuse"]]))
     t_total, worst, ok, done = 0.0, 0.0, True, 0
     with threadpool_limits(limits=1):
         while done == 0 or t_total < min_seconds:
@@ -796,6 +801,8 @@ def cpu_baseline_layers(s, wl, n_queries, n_groups, min_seconds):
                     ro, _ = O.sparse_attn(qb, h["cn"], h["sn"], ri, win[b], wl.Wcap, wl.W, t,
                                           1.0, fmt=FMT)
                     outs[layer] = (ri, ro)
+                reuse_o = [O.sparse_attn(rq, h["cn"], h["sn"], outs["full"][0], win[b], wl.Wcap,
+                                         wl.W, t, 1.0, fmt=FMT)[0] for rq in h["rq"]]
                 t_total += time.perf_counter() - t0
                 if done < n_queries:
                     ok &= bool(np.array_equal(pool, s["pool"][b, 0].cpu().numpy()))
@@ -805,15 +812,19 @@ def cpu_baseline_layers(s, wl, n_queries, n_groups, min_seconds):
                         ok &= bool(np.array_equal(ri, s[layer]["idx"][b, 0].cpu().numpy()))
                         worst = max(worst, bf16_excess(s[layer]["out"][b, 0].cpu().float().numpy(),
                                                        ro))
+                    for r, ro in zip(s["reuse"], reuse_o):
+                        worst = max(worst, bf16_excess(r["out"][b, 0].cpu().float().numpy(), ro))
                 done += 1
     pool_txt = (f"top-{wl.k} + blockwise pool of {n_groups} 8-entry groups over "
                 f"{wl.L // wl.m:,} blocks, two top-{wl.k} rescorings of the pool"
                 if n_groups else
                 f"top-{wl.pool} pool over {wl.L // wl.m:,} blocks, three top-{wl.k} "
                 "rescorings of the pool")
+    reuse_txt = (f", {len(s['reuse'])} Reuse layers attending the Full layer's top-{wl.k}"
+                 if s["reuse"] else "")
     return dict(value=done / t_total, unit="queries/s", cores=1, kind="oracle",
-                sample=f"{n_queries} of the {wl.B} sequences through all four layers (HCA dense "
-                       f"over {wl.L // wl.m_hca:,} entries, {pool_txt} + attention), run "
+                sample=f"{n_queries} of the {wl.B} sequences through all layers (HCA dense "
+                       f"over {wl.L // wl.m_hca:,} entries, {pool_txt} + attention{reuse_txt}), run "
                        f"{done // n_queries} times over, numpy fp64/int64, 1 thread",
                 seconds=round(t_total, 3)), dict(topk_exact=ok, attn_excess_over_rms=worst)
 
@@ -827,7 +838,8 @@ def run_layers(args, csa, synth, wl, dev):
     # unless --pool-groups says otherwise
     n_groups = (args.pool_groups or wl.pool // 8) if args.pool_kind == "blocks" else 0
     pool_len = 8 * n_groups if n_groups else wl.pool
-    sets = [layers_set(csa, synth, wl, dev, seed, pool_len) for seed in range(n_sets)]
+    n_reuse = args.reuse_layers
+    sets = [layers_set(csa, synth, wl, dev, seed, pool_len, n_reuse) for seed in range(n_sets)]
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s: {n_sets} input sets of {wl.name}")
 
@@ -857,12 +869,20 @@ def run_layers(args, csa, synth, wl, dev):
         csa.sparse_attn(x["q"], s["codes"], s["scales"], x["idx"], s["win"], wl.W, t, 1.0,
                         x["out"], workspace=s["ws_attn"], fmt=FMT)
 
+    def reuse_layer(i, j):
+        s = sets[i]
+        r = s["reuse"][j]
+        csa.sparse_attn(r["q"], s["codes"], s["scales"], s["full"]["idx"], s["win"], wl.W, t,
+                        1.0, r["out"], workspace=s["ws_attn"], fmt=FMT)
+
     def step_fn(i):
         def f():
             hca(i)
             pool(i)
             for layer in LAYERS:
                 csa_layer(i, layer)
+            for j in range(n_reuse):
+                reuse_layer(i, j)
         return f
 
     eager = [step_fn(i) for i in range(n_sets)]
@@ -873,7 +893,8 @@ def run_layers(args, csa, synth, wl, dev):
     secs = time_steps(runs, args.steps, args.warmup)
     ms_per_step = secs * 1e3 / args.steps
     value = wl.B * args.steps / secs
-    log(f"4-layer step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s ({timing_name(args)})")
+    log(f"{4 + n_reuse}-layer step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s "
+        f"({timing_name(args)})")
 
     # per-layer device times (eager, events)
     reps = max(4, min(args.steps, 20))
@@ -881,6 +902,7 @@ def run_layers(args, csa, synth, wl, dev):
     t_pool = split_event_ms(pool, None, n_sets, reps)
     t_full = split_event_ms(lambda i: csa_layer(i, "full"), None, n_sets, reps)
     t_re = split_event_ms(lambda i: csa_layer(i, "reindex1"), None, n_sets, reps)
+    t_reuse = split_event_ms(lambda i: reuse_layer(i, 0), None, n_sets, reps) if n_reuse else 0.0
     scan_ms = back_to_back_ms(lambda i: pool(i, "index_scan"), n_sets, reps,
                               [s["ws"] for s in sets])
     nv = wl.L // wl.m
@@ -901,12 +923,13 @@ def run_layers(args, csa, synth, wl, dev):
     hca_b = n_hca * eb + win_b + qo
     full_b = nv * wl.Di + qw + 2 * 4 * pool_len + 2 * 4 * wl.k + wl.k * eb + win_b + qo
     re_b = pool_len * (wl.Di + 4) + qw + 2 * 4 * wl.k + wl.k * eb + win_b + qo
-    per_q = hca_b + full_b + 2 * re_b
+    reuse_b = 4 * wl.k + wl.k * eb + win_b + qo  # top-k list read, entries, window, q/out
+    per_q = hca_b + full_b + 2 * re_b + n_reuse * reuse_b
     step_gbs = per_q * wl.B / (ms_per_step * 1e-3) / 1e9
     log(f"hca {t_hca * 1e3:.1f} us ({hca_tf:.0f} TFLOP/s); pool {t_pool * 1e3:.1f} us "
         f"(scan {scan_ms * 1e3:.1f} us, {achieved:.0f} GB/s); full "
         f"{'attn' if n_groups else 'top-512+attn'} {t_full * 1e3:.1f} us; reindex "
-        f"{t_re * 1e3:.1f} us")
+        f"{t_re * 1e3:.1f} us" + (f"; reuse {t_reuse * 1e3:.1f} us" if n_reuse else ""))
 
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -917,8 +940,10 @@ def run_layers(args, csa, synth, wl, dev):
         log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
 
     return {
-        "metric": "CSA2 four-layer decode queries/sec (HCA + Full + 2 Reindex) at 1M ctx, "
-                  "1 MI355X",
+        "metric": ("CSA2 four-layer decode queries/sec (HCA + Full + 2 Reindex) at 1M ctx, "
+                   "1 MI355X" if not n_reuse else
+                   f"CSA2 {4 + n_reuse}-layer decode queries/sec (HCA + Full + 2 Reindex + "
+                   f"{n_reuse} Reuse) at 1M ctx, 1 MI355X"),
         "value": round(value, 1),
         "unit": "queries/s",
         "ms_per_step": round(ms_per_step, 5),
@@ -930,13 +955,14 @@ def run_layers(args, csa, synth, wl, dev):
         "config": {"workload": wl.name, "batch": wl.B, "context": wl.L, "d": wl.d, "m": wl.m,
                    "cache": CACHE_NAME[FMT],
                    "m_hca": wl.m_hca, "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8",
-                   "pool": pool_len, "pool_kind": args.pool_kind,
+                   "pool": pool_len, "pool_kind": args.pool_kind, "reuse_layers": n_reuse,
                    **({"pool_groups": n_groups} if n_groups else {}),
                    "top_k": wl.k, "window": wl.W,
                    "input_sets_rotated": n_sets, "timing": timing_name(args)},
         "layers_us": {"hca": round(t_hca * 1e3, 2), "full_pool_topk": round(t_pool * 1e3, 2),
                       ("full_attn" if n_groups else "full_topk_attn"): round(t_full * 1e3, 2),
-                      "reindex_topk_attn": round(t_re * 1e3, 2)},
+                      "reindex_topk_attn": round(t_re * 1e3, 2),
+                      **({"reuse_attn": round(t_reuse * 1e3, 2)} if n_reuse else {})},
         "step_hbm": {"algorithmic_bytes_per_query": per_q, "GB/s": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "hca": {"bound": "mfma", "achieved": round(hca_tf, 1), "peak": BF16_PEAK_TFLOPS,
@@ -975,6 +1001,8 @@ def main():
     ap.add_argument("--pool-kind", default="entries", choices=["entries", "blocks"],
                     help="hca_reindex_1m: the Full layer's pool is its top-`pool` entries "
                          "(entries) or a blockwise pool of 8-entry groups (blocks)")
+    ap.add_argument("--reuse-layers", type=int, default=0,
+                    help="hca_reindex_1m: add Reuse layers that attend the Full layer's top-k")
     ap.add_argument("--pool-groups", type=int, default=0,
                     help="groups kept by the blockwise pool (default: pool / 8)")
     ap.add_argument("--fmt", default="e8m0", choices=["e8m0", "e4m3"],
