@@ -44,7 +44,7 @@ CACHE_NAME = {"e8m0": "MXFP4 e2m1 + e8m0/32", "e4m3": "FP4 e2m1 + e4m3/16"}
 
 METRIC = "CSA decode queries/sec + achieved HBM GB/s (% peak) at 1M ctx, 1 MI355X"
 CSRC = os.path.join(ROOT, "compressed_sparse_attention_compress_amd", "csrc")
-KERNEL_SOURCE = {"k_idx_scan": "indexer.hip", "k_idx_prefill": "indexer.hip",
+KERNEL_SOURCE = {"k_idx_scan": "indexer.hip", "k_idx_bscan": "indexer.hip",
                  "k_attn": "attn.hip", "k_compress_quantize": "compress.hip"}
 
 
