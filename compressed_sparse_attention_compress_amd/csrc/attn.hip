@@ -10,63 +10,79 @@
 // One workgroup = one query (all H <= 64 heads) x one range of slots; slots
 // are the selected entries followed by the W window tokens, and all of them
 // share one softmax. Slots are processed 64 at a time: the workgroup gathers
-// the 64 rows and dequantises each value once into LDS in two layouts
-// (entry-major bf16 for q.k, channel-major fp16 for p.v). Two waves serve
-// each group of 16 heads: for q.k each takes 32 of the 64 slots over all d
-// channels (S^T = K Q^T, 16x16x32 bf16 MFMA); the pair exchanges its
-// per-head maxima and its P^T operands through LDS; for p.v each takes half
-// of the d channels over all 64 slots (O^T += V^T P^T, 16x16x32 fp16 MFMA).
-// The head index is the lane's column in both products, so no register
-// shuffles are needed between them, and every LDS byte of a pass is read by
-// four waves at most. O is rescaled only in passes where some head's running
-// maximum grew. Ranges of slots of one query can be split over workgroups
-// (decode); their partial (o, max, sum) are merged in a fixed order.
+// the 64 rows and dequantises each once into LDS as float16, entry-major.
+// Keys and values are the same latent rows, so that one copy feeds both
+// products: q.k reads it row-wise, p.v reads it through the gfx950
+// transposing LDS load, so no transposed second copy is written. Two waves
+// serve each group of 32 heads with 32x32x16 f16 MFMA tiles (every LDS byte
+// read serves 32 heads): for q.k each takes 32 of the 64 slots over all d
+// channels (S^T = K Q^T); the pair exchanges its per-head maxima and its P^T
+// operands through LDS; for p.v each takes half of the d channels over all
+// 64 slots (O^T += V^T P^T). The head index is the lane's column in both
+// products, so no register shuffles are needed between them. The stage is
+// double-buffered: the next 64 rows are converted while the current q.k is
+// in the matrix cores. O is rescaled only in passes where some head's
+// running maximum grew. Ranges of slots of one query can be split over
+// workgroups (decode); their partial (o, max, sum) are merged in a fixed
+// order.
 #include "csa_internal.h"
 
 #include <type_traits>
 
 namespace {
 
-constexpr int CH = 64;        // slots per staging pass (two 32-slot MFMA k-steps)
-// channel-major row stride (halfs): 34 dwords. Measured on the LDS bank
-// conflict counter against 36 (and against a store order that pairs
-// channels 8 apart), this layout conflicts least.
-constexpr int VST = CH + 4;
+constexpr int CH = 64;        // slots per staging pass (two 32-slot halves)
 constexpr int IDX_CAP = 1024; // entry block ids cached in LDS per refill
-constexpr float RESCALE_LOG2 = 0.f;  // rescale whenever a head's max grows (see below)
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-// Raw bytes of the 4 slots of one staging task (16 channels each): an MXFP4
-// entry uses lo.x, lo.y (8 code bytes) and lo.z (its scale byte); a window
-// token uses lo and hi (16 bf16).
-struct RawSlots {
-  uint4 lo[4], hi[4];
-};
+// Row stride of the float16 stage, in halfs: d plus 16 (a row is then 8
+// dwords past a multiple of the 64 LDS banks). A q.k operand read (32 rows,
+// 32 bytes each) and a transposed p.v read (8 rows, 64 bytes each) both spread
+// evenly over the banks.
+template <int D>
+constexpr int row_stride() { return D + 16; }
 
-template <int D, int NW, bool DENSE, int FMT>
-__global__ __launch_bounds__(NW * 128) void k_attn(
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// i % 4 of the 4-half words addressed by lanes 4j + i / 4 (j = 0..3).
+__device__ inline v4h lds_read_tr(const _Float16* p) {
+  return __builtin_bit_cast(
+      v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(const_cast<_Float16*>(p))));
+}
+
+// bfloat16 bits -> float16 (exact in float16's normal range)
+__device__ inline _Float16 bf16_to_f16(uint32_t bits) {
+  return (_Float16)__uint_as_float(bits << 16);
+}
+
+// One workgroup per compute unit is all the LDS allows at d = 512, so the
+// compiler is told to schedule for one wave per SIMD (registers for LDS
+// reads in flight rather than for occupancy).
+template <int D, int NG, bool DENSE, int FMT>
+__global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t blk_cap, const int32_t* __restrict__ idx, int k,
     int m, const uint16_t* __restrict__ win, int Wcap, int W, int T, int H, int64_t pos0,
     const int64_t* __restrict__ qpos, float scale_log2, int nsplit, int spl, int n_queries,
     void* __restrict__ out, int out_dtype,
     float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml) {
-  constexpr int NWV = 2 * NW;                 // waves: (head group, half)
+  constexpr int NWV = 2 * NG;                 // waves: (head group, half)
   constexpr int NT = NWV * 64;
-  constexpr int KST = D + 8;                  // entry-major row stride (bf16)
-  // 16-byte chunk c of entry row r sits at chunk c ^ ((r >> 4) & 3): a q.k
-  // operand load (16 consecutive rows, one chunk) and a staging store (rows
-  // 4 apart, 4 row groups) both touch 16 distinct 4-bank groups
-  auto ks_at = [](int r, int c) { return r * KST + ((c ^ ((r >> 4) & 3)) << 3); };
-  constexpr int KSTEPS = D / 32;              // q.k k-steps of 32 channels
-  constexpr int CTH = D / 32;                 // 16-channel output tiles of one half of d
-  constexpr int SG = CH / 4;                  // slot groups of 4 per pass
-  constexpr int TASKS = SG * (D / 16);
-  constexpr int TPT = (TASKS + NT - 1) / NT;  // staging tasks per thread
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[CH * KST];
-  __shared__ __attribute__((aligned(16))) _Float16 Vs[D * VST];
+  constexpr int RS = row_stride<D>();
+  constexpr int KS2 = D / 32;                 // q.k k-steps of 16 channels in one half of d
+  constexpr int CT = D / 64;                  // 32-channel output tiles of one half of d
+  constexpr int CHUNKS = D / 32;              // 32-channel chunks of a row
+  constexpr int TASKS = CH * CHUNKS;          // staging tasks (slot, chunk) per pass
+  constexpr int TPT = TASKS / NT;             // staging tasks per thread
+  static_assert(TASKS % NT == 0, "tasks must divide evenly");
+  constexpr bool E4 = FMT == CSA_SCALE_E4M3_16;
+  constexpr int SPE = E4 ? D / 16 : D / 32;   // scale bytes per entry
+  __shared__ __attribute__((aligned(16))) _Float16 Rs[CH * RS];
   __shared__ int s_blk[IDX_CAP];
-  __shared__ __attribute__((aligned(16))) v8h s_p[NWV][64];  // each wave's P^T operand
-  __shared__ float s_x[NWV][16];                             // per-head max / sum exchange
+  // each wave's partial logits of both 32-slot tiles, in register order
+  __shared__ __attribute__((aligned(16))) float4 s_S[NWV][2][4][64];
+  __shared__ unsigned long long s_valid;      // entry slots of the staged pass that are valid
 
   // Workgroups are dealt to the 8 XCDs round-robin by id; all splits of a
   // query are mapped onto one XCD so its q rows are fetched from HBM once and
@@ -89,45 +105,65 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hg = wave >> 1, half = wave & 1, partner = wave ^ 1;
-  const int i16 = lane & 15, g = lane >> 4;
-  const int head = hg * 16 + i16;
+  const int i32 = lane & 31, gg = lane >> 5;
+  const int head = hg * 32 + i32;
 
-  // q rows are loaded after the first entry ids and raw entries have been
-  // requested, so that waiting for those does not wait for q as well
-  v8bf Qop[KSTEPS];
-  bool q_loaded = false;
-  auto load_q = [&]() {
-    if (q_loaded) return;
-    q_loaded = true;
+  const int32_t* ibase = DENSE ? nullptr : idx + (int64_t)qi * k;
+  // entry ids of the first table (slots [s_begin, s_begin + IDX_CAP) of the
+  // entry range), requested before the q rows so that both latencies overlap
+  constexpr int RPT = (IDX_CAP + NT - 1) / NT;
+  const int64_t e_end = s_end < nsel ? s_end : nsel;
+  int64_t first_ids[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int64_t sl = s_begin + threadIdx.x + r * NT;
+    first_ids[r] = (DENSE || s_begin >= e_end) ? sl : (int64_t)ibase[sl < e_end ? sl : e_end - 1];
+  }
+  // q.k operand: the two waves of a head group split d; lane (i + 32 gg) of
+  // wave half h holds head i's channels h d/2 + 16 kk + 8 gg .. +7 of every
+  // k-step kk, as float16
+  v8h Qop[KS2];
+  {
     const int hq = head < H ? head : H - 1;
+    const uint16_t* qr = q + ((int64_t)qi * H + hq) * D + half * (D / 2) + 8 * gg;
+    v8us raw[KS2];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      Qop[kk] = *reinterpret_cast<const v8bf*>(q + ((int64_t)qi * H + hq) * D + 32 * kk + 8 * g);
-  };
-  v4f O[CTH];
+    for (int kk = 0; kk < KS2; ++kk) raw[kk] = *reinterpret_cast<const v8us*>(qr + 16 * kk);
 #pragma unroll
-  for (int ct = 0; ct < CTH; ++ct) O[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < KS2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Qop[kk][e] = bf16_to_f16(raw[kk][e]);
+  }
+  v16f O[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[ct][r] = 0.f;
+  // running max and sum; both waves of a head group compute the same values
   float m_run = -INFINITY, l_run = 0.f;
 
   const uint8_t* cbase = codes + (int64_t)b * blk_cap * (D / 2);
-  constexpr bool E4 = FMT == CSA_SCALE_E4M3_16;
-  constexpr int SPE = E4 ? D / 16 : D / 32;  // scale bytes per entry
   const uint8_t* sbase = scales + (int64_t)b * blk_cap * SPE;
   const uint16_t* wbase = win + (int64_t)b * Wcap * D;
-  const int32_t* ibase = DENSE ? nullptr : idx + (int64_t)qi * k;
 
   // One homogeneous phase: entries (IS_WIN false) or window tokens, slots
   // [p0, p1). Loads are unconditional (clamped rows), validity is applied to
-  // the logits; in the entry phase the next pass's raw bytes are fetched
-  // while the current pass is in the matrix cores.
+  // the logits.
   auto phase = [&](auto is_win_tag, int64_t p0, int64_t p1) {
     constexpr bool IS_WIN = decltype(is_win_tag)::value;
     if (p0 >= p1) return;
     int64_t tab0 = p0;  // first slot whose block id sits in s_blk[0]
     // entry ids of slots [from, from + IDX_CAP) into LDS; all loads issued
     // before the first is used (addresses clamped into the phase)
+    auto store_ids = [&](int64_t from, const int64_t* v) {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const int i = threadIdx.x + r * NT;
+        const int64_t sl = from + i;
+        if (i < IDX_CAP) s_blk[i] = (sl < p1 && v[r] >= 0 && v[r] < blk_cap) ? (int)v[r] : -1;
+      }
+    };
     auto refill = [&](int64_t from) {
-      constexpr int RPT = (IDX_CAP + NT - 1) / NT;
       __syncthreads();
       tab0 = from;
       int64_t v[RPT];
@@ -136,283 +172,312 @@ __global__ __launch_bounds__(NW * 128) void k_attn(
         const int64_t sl = from + threadIdx.x + r * NT;
         v[r] = DENSE ? sl : (int64_t)ibase[sl < p1 ? sl : p1 - 1];
       }
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        const int i = threadIdx.x + r * NT;
-        const int64_t sl = from + i;
-        if (i < IDX_CAP) s_blk[i] = (sl < p1 && v[r] >= 0 && v[r] < blk_cap) ? (int)v[r] : -1;
-      }
+      store_ids(from, v);
       __syncthreads();
     };
-    if (!IS_WIN) refill(p0);
-    // task -> (slot group sg, 16-channel segment cs), sg fastest across lanes
-    // so that the channel-major writes of a wave spread over all LDS banks
-    auto load_task = [&](RawSlots& r, int task, int64_t c0) {
-      const int sg = (task < TASKS ? task : 0) % SG;
-      const int cs = (task < TASKS ? task : 0) / SG;
+    // task (slot s, 32-channel chunk c), chunk fastest across lanes, so that
+    // 16 lanes (d = 512) read one entry's 256 code bytes contiguously
+    struct Raw {
+      uint4 w[IS_WIN ? 4 : 1];
+      uint32_t sc;
+    };
+    auto load_task = [&](Raw& r, int task, int64_t c0) {
+      const int c = task % CHUNKS, s = task / CHUNKS;
+      const int64_t sl = c0 + s;
+      if (IS_WIN) {
+        int64_t p = t - W + 1 + (sl - nsel);
+        p = p < 0 ? 0 : p;
+        const uint4* src = reinterpret_cast<const uint4*>(wbase + (p % Wcap) * D + 32 * c);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t sl = c0 + 4 * sg + u;
-        if (IS_WIN) {
-          int64_t p = t - W + 1 + (sl - nsel);
-          p = p < 0 ? 0 : p;
-          const uint16_t* src = wbase + (p % Wcap) * D + cs * 16;
-          r.lo[u] = *reinterpret_cast<const uint4*>(src);
-          r.hi[u] = *reinterpret_cast<const uint4*>(src + 8);
-        } else {
-          int blk = (sl < p1 && sl - tab0 < IDX_CAP) ? s_blk[sl - tab0] : -1;
-          blk = blk < 0 ? 0 : blk;
-          const uint2 cw =
-              *reinterpret_cast<const uint2*>(cbase + (int64_t)blk * (D / 2) + cs * 8);
-          r.lo[u].x = cw.x;
-          r.lo[u].y = cw.y;
-          r.lo[u].z = sbase[(int64_t)blk * SPE + (E4 ? cs : cs / 2)];
-        }
+        for (int u = 0; u < 4; ++u) r.w[u] = src[u];
+        r.sc = 0;
+      } else {
+        int blk = (sl < p1 && sl - tab0 < IDX_CAP) ? s_blk[sl - tab0] : -1;
+        blk = blk < 0 ? 0 : blk;
+        r.w[0] = *reinterpret_cast<const uint4*>(cbase + (int64_t)blk * (D / 2) + 16 * c);
+        const uint8_t* sp = sbase + (int64_t)blk * SPE + (E4 ? 2 * c : c);
+        r.sc = E4 ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : (uint32_t)sp[0];
       }
     };
-    auto convert_task = [&](const RawSlots& r, int task) {
-      const int sg = task % SG;
-      const int cs = task / SG;
-      v8h vh[4][2];
+    auto convert_task = [&](const Raw& r, int task) {
+      const int c = task % CHUNKS, s = task / CHUNKS;
+      v8h h[4];
+      if (IS_WIN) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int slot = 4 * sg + u;
-        v8bf k0, k1;
-        if (IS_WIN) {
-          k0 = __builtin_bit_cast(v8bf, r.lo[u]);
-          k1 = __builtin_bit_cast(v8bf, r.hi[u]);
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t wd[4] = {r.w[u].x, r.w[u].y, r.w[u].z, r.w[u].w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            vh[u][0][i] = (_Float16)(float)k0[i];
-            vh[u][1][i] = (_Float16)(float)k1[i];
-          }
-        } else {
-          if (E4) {
-            const _Float16 sc = (_Float16)e4m3_to_f32(r.lo[u].z & 0xffu);
-            fp4x8_e4m3_both(r.lo[u].x, sc, vh[u][0], k0);
-            fp4x8_e4m3_both(r.lo[u].y, sc, vh[u][1], k1);
-          } else {
-            const float sc = e8m0_to_f32(r.lo[u].z & 0xffu);
-            k0 = fp4x8_to_bf16(r.lo[u].x, sc);
-            k1 = fp4x8_to_bf16(r.lo[u].y, sc);
-            vh[u][0] = fp4x8_to_f16(r.lo[u].x, sc);
-            vh[u][1] = fp4x8_to_f16(r.lo[u].y, sc);
+          for (int e = 0; e < 4; ++e) {
+            h[u][2 * e] = bf16_to_f16(wd[e] & 0xffffu);
+            h[u][2 * e + 1] = bf16_to_f16(wd[e] >> 16);
           }
         }
-        *reinterpret_cast<v8bf*>(&Ks[ks_at(slot, 2 * cs)]) = k0;
-        *reinterpret_cast<v8bf*>(&Ks[ks_at(slot, 2 * cs + 1)]) = k1;
+      } else if (E4) {
+        // E2M1 times an E4M3 scale, formed in float16 (exact: at most 5
+        // significant bits, magnitudes 2^-10 .. 2688)
+        const _Float16 s0 = (_Float16)e4m3_to_f32(r.sc & 0xffu);
+        const _Float16 s1 = (_Float16)e4m3_to_f32(r.sc >> 8);
+        h[0] = fp4x8_to_f16(r.w[0].x, 1.0f) * s0;
+        h[1] = fp4x8_to_f16(r.w[0].y, 1.0f) * s0;
+        h[2] = fp4x8_to_f16(r.w[0].z, 1.0f) * s1;
+        h[3] = fp4x8_to_f16(r.w[0].w, 1.0f) * s1;
+      } else {
+        const float sc = e8m0_to_f32(r.sc);
+        h[0] = fp4x8_to_f16(r.w[0].x, sc);
+        h[1] = fp4x8_to_f16(r.w[0].y, sc);
+        h[2] = fp4x8_to_f16(r.w[0].z, sc);
+        h[3] = fp4x8_to_f16(r.w[0].w, sc);
+      }
+      v8h* dst = reinterpret_cast<v8h*>(Rs + s * RS + 32 * c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dst[u] = h[u];
+    };
+    // entries: raw bytes prefetched one pass ahead (they are small); window
+    // rows: loaded right before they are converted, two tasks in flight
+    Raw raw[IS_WIN ? 1 : TPT];
+    bool have_raw = false;  // raw[] holds the pass to be staged (entries only)
+    auto stage = [&](int64_t c0) {
+      if (IS_WIN) {
+        Raw wr[2];
+        load_task(wr[0], threadIdx.x, c0);
+#pragma unroll
+        for (int tt = 0; tt < TPT; ++tt) {
+          if (tt + 1 < TPT) load_task(wr[(tt + 1) & 1], threadIdx.x + (tt + 1) * NT, c0);
+          convert_task(wr[tt & 1], threadIdx.x + tt * NT);
+        }
+        return;
+      }
+      if (!have_raw) {
+#pragma unroll
+        for (int tt = 0; tt < TPT; ++tt) load_task(raw[tt], threadIdx.x + tt * NT, c0);
       }
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        v4h col;
-        col[0] = vh[0][c >> 3][c & 7];
-        col[1] = vh[1][c >> 3][c & 7];
-        col[2] = vh[2][c >> 3][c & 7];
-        col[3] = vh[3][c >> 3][c & 7];
-        *reinterpret_cast<v4h*>(&Vs[(cs * 16 + c) * VST + 4 * sg]) = col;
+      for (int tt = 0; tt < TPT; ++tt) convert_task(raw[tt], threadIdx.x + tt * NT);
+      // validity of the staged slots as one 64-bit mask
+      if (wave == 0) {
+        const int64_t sl = c0 + lane;
+        const unsigned long long vm = __ballot(sl < p1 && s_blk[sl - tab0] >= 0);
+        if (lane == 0) s_valid = vm;
+      }
+      // the next pass's raw entries, if its ids are in the table
+      have_raw = false;
+      if (c0 + CH < p1 && c0 + 2 * CH <= tab0 + IDX_CAP) {
+#pragma unroll
+        for (int tt = 0; tt < TPT; ++tt) load_task(raw[tt], threadIdx.x + tt * NT, c0 + CH);
+        have_raw = true;
       }
     };
-    // prefetch (whole pass ahead) only where the raw bytes are small
-    // (entries) and a thread owns at most two tasks; otherwise each task is
-    // loaded right before it is converted
-    constexpr bool PREFETCH = !IS_WIN && TPT <= 2;
-    constexpr int NRAW = PREFETCH ? TPT : 1;
-    RawSlots raw[NRAW];
-    auto load_all = [&](int64_t c0) {
-#pragma unroll
-      for (int tt = 0; tt < NRAW; ++tt) load_task(raw[tt], threadIdx.x + tt * NT, c0);
-    };
-    if (PREFETCH) load_all(p0);
-    load_q();
+    if (!IS_WIN) {
+      // the first table: the entry range starts at s_begin, its ids are loaded
+      store_ids(p0, first_ids);
+      __syncthreads();
+    }
+    stage(p0);
     for (int64_t c0 = p0; c0 < p1; c0 += CH) {
-      if (!IS_WIN && c0 + CH > tab0 + IDX_CAP) {
-        refill(c0);
-        if (PREFETCH) load_all(c0);
-      }
-      // convert the raw bytes into LDS: entry-major bf16 and channel-major fp16
+      __syncthreads();  // this pass's rows are staged
+      // validity of this lane's logit slots: tile et, register r holds slot
+      // 32 et + 8 (r / 4) + 4 gg + r % 4 of the pass; bit 16 et + r
+      uint32_t okm = 0;
+      if (IS_WIN) {
 #pragma unroll
-      for (int tt = 0; tt < TPT; ++tt) {
-        const int task = threadIdx.x + tt * NT;
-        if (task < TASKS) {
-          if (PREFETCH) {
-            convert_task(raw[tt < NRAW ? tt : 0], task);
-          } else {
-            load_task(raw[0], task, c0);
-            convert_task(raw[0], task);
-          }
+        for (int r = 0; r < 32; ++r) {
+          const int64_t sl = c0 + 32 * (r >> 4) + 8 * ((r >> 2) & 3) + 4 * gg + (r & 3);
+          okm |= (uint32_t)(sl < p1 && t - W + 1 + (sl - nsel) >= 0) << r;
         }
+      } else {
+        const unsigned long long vm = s_valid >> (4 * gg);
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+          okm |= (uint32_t)((vm >> (32 * (n >> 2) + 8 * (n & 3))) & 0xfu) << (4 * n);
       }
-      // validity of this lane's logit slots: this wave's half, tile et, row 4g + r
-      const int64_t h0 = c0 + 32 * half;
-      bool ok[2][4];
+      // partial S^T[slot][head] of both 32-slot tiles over this wave's half of d
+      v16f S[2];
 #pragma unroll
       for (int et = 0; et < 2; ++et)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t sl = h0 + 16 * et + 4 * g + r;
-          if (IS_WIN)
-            ok[et][r] = sl < p1 && t - W + 1 + (sl - nsel) >= 0;
-          else
-            ok[et][r] = sl < p1 && s_blk[sl - tab0] >= 0;
-        }
-      if (PREFETCH && c0 + CH < p1 && c0 + 2 * CH <= tab0 + IDX_CAP) load_all(c0 + CH);
+        for (int r = 0; r < 16; ++r) S[et][r] = 0.f;
+      const _Float16* krow = Rs + i32 * RS + half * (D / 2) + 8 * gg;
+      // key operands read 8 at a time ahead of their products, so that the
+      // LDS latency is paid once per batch
+#pragma unroll
+      for (int k0 = 0; k0 < KS2; k0 += 4) {
+        v8h ka[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int et = 0; et < 2; ++et)
+            ka[u][et] = *reinterpret_cast<const v8h*>(krow + 32 * et * RS + 16 * (k0 + u));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int et = 0; et < 2; ++et)
+            S[et] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[u][et], Qop[k0 + u], S[et], 0, 0, 0);
+      }
+#pragma unroll
+      for (int et = 0; et < 2; ++et)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          s_S[wave][et][q4][lane] = float4{S[et][4 * q4], S[et][4 * q4 + 1], S[et][4 * q4 + 2],
+                                           S[et][4 * q4 + 3]};
       __syncthreads();
-
-      // S^T[slot][head] for this wave's 32 slots (two independent 16-slot
-      // tiles) over all d channels
-      v4f S[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-        for (int et = 0; et < 2; ++et) {
-          const v8bf a = *reinterpret_cast<const v8bf*>(
-              &Ks[ks_at(32 * half + 16 * et + i16, 4 * kk + g)]);
-          S[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qop[kk], S[et], 0, 0, 0);
-        }
-      float x[2][4];
+      // full logits of the 64 slots (own half of d + the partner's)
+      float x[32];
       float cmax = -INFINITY;
 #pragma unroll
       for (int et = 0; et < 2; ++et)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[et][r] = ok[et][r] ? S[et][r] * scale_log2 : -INFINITY;
-          cmax = fmaxf(cmax, x[et][r]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 o = s_S[partner][et][q4][lane];
+          const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * et + 4 * q4 + e;
+            // the same sum in both waves: lower half of d first
+            const float sv = half == 0 ? S[et][4 * q4 + e] + ov[e] : ov[e] + S[et][4 * q4 + e];
+            x[r] = (okm >> r) & 1u ? sv * scale_log2 : -INFINITY;
+            cmax = fmaxf(cmax, x[r]);
+          }
         }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      if (g == 0) s_x[wave][i16] = cmax;
-      __syncthreads();
-      cmax = fmaxf(cmax, s_x[partner][i16]);
       // online-softmax rescale, skipped when no head of the wave saw its max
-      // grow (the branch is wave-uniform, and both waves of a head group see
-      // the same maxima; heads whose max did not grow get alpha = 1). Letting
-      // the reference max lag (p up to 2^k in fp16) was measured to raise the
-      // p.v error steadily with k, so it never lags.
-      if (__ballot(cmax > m_run + RESCALE_LOG2)) {
+      // grow (the branch is wave-uniform; heads whose max did not grow get
+      // alpha = 1). Letting the reference max lag (p above 1 in fp16) was
+      // measured to raise the p.v error steadily with the lag, so it never
+      // lags.
+      if (__ballot(cmax > m_run)) {
         const float m_new = fmaxf(m_run, cmax);
-        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
-        for (int ct = 0; ct < CTH; ++ct) O[ct] *= alpha;
+        for (int ct = 0; ct < CT; ++ct) O[ct] *= alpha;
         m_run = m_new;
       }
       const bool none = m_run == -INFINITY;
-      // P^T operand of the k-step over this half's 32 slots: element s of
-      // lane (j + 16g) is slot (s < 4 ? 4g + s : 16 + 4g + s - 4), head j
-      v8h P;
+      // P^T operands of the four 16-slot k-steps: element e of lane
+      // (i + 32 gg) in k-step ks = 2 et + s is slot 32 et + 16 s + 8 (e / 4) +
+      // 4 gg + e % 4, head i (logit registers 8 s .. 8 s + 7 of tile et)
+      v8h P[4];
       float psum = 0.f;
 #pragma unroll
-      for (int et = 0; et < 2; ++et)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = none ? 0.f : exp2f(x[et][r] - m_run);
-          psum += pv;
-          P[et * 4 + r] = (_Float16)pv;
-        }
-      l_run += psum;
-      s_p[wave][lane] = P;
-      __syncthreads();
-      const v8h Pq = s_p[partner][lane];
-      // O^T[channel][head] += V^T P^T over both halves' slots, for this
-      // wave's half of the channels
-#pragma unroll
-      for (int ct = 0; ct < CTH; ++ct) {
-        const _Float16* vrow = &Vs[(half * (D / 2) + ct * 16 + i16) * VST];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const v4h lo = *reinterpret_cast<const v4h*>(vrow + 32 * kh + 4 * g);
-          const v4h hi = *reinterpret_cast<const v4h*>(vrow + 32 * kh + 16 + 4 * g);
-          v8h A;
-          A[0] = lo[0]; A[1] = lo[1]; A[2] = lo[2]; A[3] = lo[3];
-          A[4] = hi[0]; A[5] = hi[1]; A[6] = hi[2]; A[7] = hi[3];
-          O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, kh == half ? P : Pq, O[ct], 0, 0, 0);
-        }
+      for (int r = 0; r < 32; ++r) {
+        // hardware exp2 (results below 2^-126 flush to 0, far under the
+        // float16 probabilities' resolution)
+        const float pv = none ? 0.f : __builtin_amdgcn_exp2f(x[r] - m_run);
+        psum += pv;
+        P[r >> 3][r & 7] = (_Float16)pv;
       }
-      __syncthreads();
+      l_run += psum;
+      // O^T[channel][head] += V^T P^T over the 64 slots, for this wave's half
+      // of the channels. V^T operand of k-step ks (slots 16 ks ..): lane
+      // (i + 32 gg) needs slot 16 ks + 8 a + 4 gg + j of channel i for a = 0, 1
+      // and j = 0..3; in the transposing read, lane 16 G + 4 j + c (G = lane /
+      // 16) addresses row 16 ks + 8 a + 4 (G / 2) + j, channels 16 (G % 2) + 4 c
+      // .. + 3 of the tile.
+      const int G = lane >> 4, jj = (lane >> 2) & 3, cc = lane & 3;
+      const _Float16* vbase = Rs + (4 * (G >> 1) + jj) * RS + half * (D / 2) + 16 * (G & 1) + 4 * cc;
+      // one k-step at a time: the scheduler is kept from hoisting every
+      // transposed read of the pass (their registers would push the q.k
+      // operands out of the VGPRs)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const _Float16* vp = vbase + 16 * ks * RS + 32 * ct;
+          const v4h lo = lds_read_tr(vp);
+          const v4h hi = lds_read_tr(vp + 8 * RS);
+          const v8h A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, P[ks], O[ct], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c0 + CH < p1) {
+        __syncthreads();  // every read of this pass's rows is done
+        if (!IS_WIN && c0 + 2 * CH > tab0 + IDX_CAP) refill(c0 + CH);
+        stage(c0 + CH);
+      }
     }
+    __syncthreads();  // the stage may be rewritten by the next phase
   };
   phase(std::false_type{}, s_begin, s_end < nsel ? s_end : nsel);
   phase(std::true_type{}, s_begin > nsel ? s_begin : nsel, s_end);
 
-  // softmax denominator: this lane's slots, then the wave's, then the pair's
-  float l_own = l_run + __shfl_xor(l_run, 16, 64);
-  l_own += __shfl_xor(l_own, 32, 64);
-  if (g == 0) s_x[wave][i16] = l_own;
-  __syncthreads();
-  const float l_tot = l_own + s_x[partner][i16];
+  // softmax denominator: the two lanes of a head hold the two halves of the slots
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (head >= H) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // output register r of tile ct: channel half (d/2) + 32 ct + 8 (r / 4) + 4 gg + r % 4
   if (nsplit == 1) {
-    const int64_t base = ((int64_t)qi * H + head) * D + half * (D / 2);
+    const int64_t base = ((int64_t)qi * H + head) * D + half * (D / 2) + 4 * gg;
 #pragma unroll
-    for (int ct = 0; ct < CTH; ++ct) {
-      const int c = ct * 16 + 4 * g;
-      if (out_dtype == CSA_F32) {
-        float4 v;
-        v.x = O[ct][0] * inv; v.y = O[ct][1] * inv; v.z = O[ct][2] * inv; v.w = O[ct][3] * inv;
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + base + c) = v;
-      } else {
-        typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-        v4bf v;
-        v[0] = (__bf16)(O[ct][0] * inv); v[1] = (__bf16)(O[ct][1] * inv);
-        v[2] = (__bf16)(O[ct][2] * inv); v[3] = (__bf16)(O[ct][3] * inv);
-        *reinterpret_cast<v4bf*>(reinterpret_cast<__bf16*>(out) + base + c) = v;
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = 32 * ct + 8 * q4;
+        const float v0 = O[ct][4 * q4] * inv, v1 = O[ct][4 * q4 + 1] * inv;
+        const float v2 = O[ct][4 * q4 + 2] * inv, v3 = O[ct][4 * q4 + 3] * inv;
+        if (out_dtype == CSA_F32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + base + c) =
+              float4{v0, v1, v2, v3};
+        } else {
+          typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+          const v4bf v = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+          *reinterpret_cast<v4bf*>(reinterpret_cast<__bf16*>(out) + base + c) = v;
+        }
       }
-    }
-    if (lse && half == 0 && g == 0)
+    if (lse && half == 0 && gg == 0)
       lse[(int64_t)qi * H + head] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
   } else {
     // normalised partial output in float32, stored in register order
-    // [query][split][head group][column tile][lane][4] (the two halves of a
-    // head group hold column tiles 0..CTH-1 and CTH..2CTH-1), so every store
-    // of a wave is 1 KB contiguous; m and l in float32
-    float* pw = part_o + ((((int64_t)qi * nsplit + split) * NWV + wave) * CTH) * 256 + lane * 4;
+    // [query][split][wave][column tile][r / 4][lane][4], so every store of a
+    // wave is 1 KB contiguous; m and l in float32
+    float* pw = part_o + (((int64_t)qi * nsplit + split) * NWV + wave) * (CT * 1024) + lane * 4;
 #pragma unroll
-    for (int ct = 0; ct < CTH; ++ct) {
-      float4 v;
-      v.x = O[ct][0] * inv; v.y = O[ct][1] * inv; v.z = O[ct][2] * inv; v.w = O[ct][3] * inv;
-      *reinterpret_cast<float4*>(pw + ct * 256) = v;
-    }
-    if (half == 0 && g == 0)
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(pw + (4 * ct + q4) * 256) =
+            float4{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
+                   O[ct][4 * q4 + 3] * inv};
+    if (half == 0 && gg == 0)
       part_ml[((int64_t)qi * nsplit + split) * H + head] = float2{m_run, l_tot};
   }
 }
 
-// Merge of the split partials, one workgroup per (query, 16-head block, 4
-// column tiles), one thread per (column tile, lane), splits in index order: weights l_s * 2^(m_s - M) / L on the normalised
-// partial outputs. The partials are read in the register order the attention
-// kernel wrote them ([ct][lane][4] per 16-head block), 512 contiguous bytes
-// per wave load; lane (j + 16g) of column tile ct holds head j, channels
-// 16ct + 4g .. +3.
-constexpr int MERGE_MAX = 256;  // splits per query handled by the merge
+// Merge of the split partials, one workgroup per (query, 32-head group,
+// 32-channel tile), one thread per (register quad, lane) of that tile, splits
+// in index order: weights l_s * 2^(m_s - M) / L on the normalised partial
+// outputs. The partials are read in the register order the attention kernel
+// wrote them, 4 KB contiguous per split; thread (q4, lane) holds head lane %
+// 32 and channels 8 q4 + 4 (lane / 32) .. +3 of the tile.
+constexpr int MERGE_MAX = 64;  // splits per query handled by the merge
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
-                                                    int nsplit, int H, int NW, int n_queries,
+                                                    int nsplit, int H, int NG, int n_queries,
                                                     void* __restrict__ out, int out_dtype,
                                                     float* __restrict__ lse) {
-  constexpr int CT = D / 16;
-  __shared__ float s_m[16][MERGE_MAX], s_f[16][MERGE_MAX];
-  __shared__ float s_inv[16];
-  // workgroup -> (query, 16-head block, group of 4 column tiles); thread ->
-  // one (ct, lane) pair. Workgroups are dealt to the XCDs round-robin; every
-  // workgroup of query qi goes to XCD qi % 8, where the attention kernel
-  // wrote that query's partials, so they are read from that XCD's L2.
-  constexpr int CG = CT / 4;
-  const int per_q = NW * CG;
+  constexpr int CT = D / 64;      // tiles per wave (half of d)
+  constexpr int TILES = D / 32;   // tiles of a head group
+  __shared__ float s_m[32][MERGE_MAX], s_f[32][MERGE_MAX];
+  __shared__ float s_inv[32];
+  // Workgroups are dealt to the XCDs round-robin; every workgroup of query qi
+  // goes to XCD qi % 8, where the attention kernel wrote that query's
+  // partials, so they are read from that XCD's L2.
+  const int per_q = NG * TILES;
   const int xcd = blockIdx.x & 7;
   const int jx = blockIdx.x >> 3;
   const int64_t qi = xcd + 8 * (int64_t)(jx / per_q);
   if (qi >= n_queries) return;
-  const int r = jx % per_q;
-  const int cg = r % CG;
-  const int w = r / CG;
-  const int pr = cg * 256 + threadIdx.x;
-  const int ct = pr >> 6, ln = pr & 63;
-  const int j = ln & 15, g = ln >> 4;
-  const int h = w * 16 + j;
-  const int64_t split_stride = (int64_t)NW * CT * 256;
-  const float* src = part_o + (qi * nsplit * NW + w) * CT * 256 + ct * 256 + ln * 4;
+  const int rr = jx % per_q;
+  const int tile = rr % TILES, hg = rr / TILES;
+  const int hf = tile / CT, ct = tile % CT;
+  const int wave = 2 * hg + hf;
+  const int q4 = threadIdx.x >> 6, ln = threadIdx.x & 63;
+  const int j = ln & 31, gg = ln >> 5;
+  const int h = hg * 32 + j;
+  const int NWV = 2 * NG;
+  const int64_t split_stride = (int64_t)NWV * CT * 1024;
+  const float* src = part_o + (qi * nsplit * NWV + wave) * (CT * 1024) + (4 * ct + q4) * 256 + ln * 4;
   // the first PB partials are requested before the (max, sum) staging so that
   // both rounds of loads overlap (indices clamped; surplus ones get weight 0)
   constexpr int PB = 8;
@@ -420,31 +485,17 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 #pragma unroll
   for (int u = 0; u < PB; ++u)
     pre[u] = *reinterpret_cast<const float4*>(src + (int64_t)(u < nsplit ? u : 0) * split_stride);
-  // stage every (max, sum) of the block's 16 heads, two loads per thread in
-  // flight per round
-  for (int i0 = threadIdx.x; i0 < 16 * nsplit; i0 += 512) {
-    float2 ml[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int i = i0 + 256 * r;
-      const int jj = i & 15, sp = i >> 4;
-      const int hh = w * 16 + jj;
-      ml[r] = (i < 16 * nsplit && hh < H) ? part_ml[(qi * nsplit + sp) * H + hh]
-                                          : float2{-INFINITY, 0.f};
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int i = i0 + 256 * r;
-      if (i < 16 * nsplit) {
-        s_m[i & 15][i >> 4] = ml[r].x;
-        s_f[i & 15][i >> 4] = ml[r].y;
-      }
-    }
+  for (int i = threadIdx.x; i < 32 * nsplit; i += 256) {
+    const int jj = i & 31, sp = i >> 5;
+    const int hh = hg * 32 + jj;
+    const float2 ml = hh < H ? part_ml[(qi * nsplit + sp) * H + hh] : float2{-INFINITY, 0.f};
+    s_m[jj][sp] = ml.x;
+    s_f[jj][sp] = ml.y;
   }
   __syncthreads();
-  if (threadIdx.x < 16) {
+  if (threadIdx.x < 32) {
     const int jj = threadIdx.x;
-    const int hh = w * 16 + jj;
+    const int hh = hg * 32 + jj;
     float M = -INFINITY;
     for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_m[jj][sp]);
     float L = 0.f;
@@ -454,44 +505,40 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
       L += f;
     }
     s_inv[jj] = L > 0.f ? 1.f / L : 0.f;
-    if (lse && cg == 0 && hh < H) lse[qi * H + hh] = (M + log2f(L)) * 0.69314718055994531f;
+    if (lse && tile == 0 && hh < H) lse[qi * H + hh] = (M + log2f(L)) * 0.69314718055994531f;
   }
   __syncthreads();
-  {
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < PB; ++u) {
+    const float f = u < nsplit ? s_f[j][u] : 0.f;
+    acc.x += pre[u].x * f; acc.y += pre[u].y * f;
+    acc.z += pre[u].z * f; acc.w += pre[u].w * f;
+  }
+  for (int s0 = PB; s0 < nsplit; s0 += PB) {
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      const float f = u < nsplit ? s_f[j][u] : 0.f;
+      const int sp = s0 + u < nsplit ? s0 + u : 0;
+      pre[u] = *reinterpret_cast<const float4*>(src + (int64_t)sp * split_stride);
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const float f = s0 + u < nsplit ? s_f[j][s0 + u] : 0.f;
       acc.x += pre[u].x * f; acc.y += pre[u].y * f;
       acc.z += pre[u].z * f; acc.w += pre[u].w * f;
     }
-    for (int s0 = PB; s0 < nsplit; s0 += PB) {
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        const int sp = s0 + u < nsplit ? s0 + u : 0;
-        pre[u] = *reinterpret_cast<const float4*>(src + (int64_t)sp * split_stride);
-      }
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        const float f = s0 + u < nsplit ? s_f[j][s0 + u] : 0.f;
-        acc.x += pre[u].x * f; acc.y += pre[u].y * f;
-        acc.z += pre[u].z * f; acc.w += pre[u].w * f;
-      }
-    }
-    if (h >= H) return;
-    const float inv = s_inv[j];
-    const int64_t o_off = (qi * H + h) * D + ct * 16 + 4 * g;
-    if (out_dtype == CSA_F32) {
-      float4 v;
-      v.x = acc.x * inv; v.y = acc.y * inv; v.z = acc.z * inv; v.w = acc.w * inv;
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o_off) = v;
-    } else {
-      typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-      v4bf v;
-      v[0] = (__bf16)(acc.x * inv); v[1] = (__bf16)(acc.y * inv);
-      v[2] = (__bf16)(acc.z * inv); v[3] = (__bf16)(acc.w * inv);
-      *reinterpret_cast<v4bf*>(reinterpret_cast<__bf16*>(out) + o_off) = v;
-    }
+  }
+  if (h >= H) return;
+  const float inv = s_inv[j];
+  const int64_t o_off = (qi * H + h) * D + hf * (D / 2) + 32 * ct + 8 * q4 + 4 * gg;
+  if (out_dtype == CSA_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o_off) =
+        float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  } else {
+    typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+    const v4bf v = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv),
+                    (__bf16)(acc.w * inv)};
+    *reinterpret_cast<v4bf*>(reinterpret_cast<__bf16*>(out) + o_off) = v;
   }
 }
 
@@ -528,7 +575,7 @@ static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots) {
   p.ws_bytes = 0;
   if (p.nsplit > 1) {
     const int64_t units = (int64_t)B * T * p.nsplit;
-    const int64_t hpad = 16 * ((H + 15) / 16);
+    const int64_t hpad = 32 * ((H + 31) / 32);
     p.ws_bytes = ((units * hpad * d * 4 + 255) / 256) * 256 + units * H * 8;
   }
   return p;
@@ -545,24 +592,20 @@ struct AttnArgs {
 
 template <int D, bool DENSE, int FMT>
 static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, float2* part_ml) {
-  const int nw = (a.H + 15) / 16;
+  const int ng = (a.H + 31) / 32;
   const int64_t nq = (int64_t)a.B * a.T;
   const dim3 grid((unsigned)(((nq + 7) / 8) * 8 * p.nsplit));
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
-#define CSA_LAUNCH_ATTN(NW)                                                                  \
-  hipLaunchKernelGGL((k_attn<D, NW, DENSE, FMT>), grid, dim3(NW * 128), 0, a.stream, a.q, a.codes, \
+#define CSA_LAUNCH_ATTN(NG)                                                                  \
+  hipLaunchKernelGGL((k_attn<D, NG, DENSE, FMT>), grid, dim3(NG * 128), 0, a.stream, a.q, a.codes, \
                      a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, a.H, a.pos0, \
                      a.pos, sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse, part_o, part_ml)
-  switch (nw) {
-    case 1: CSA_LAUNCH_ATTN(1); break;
-    case 2: CSA_LAUNCH_ATTN(2); break;
-    case 3: CSA_LAUNCH_ATTN(3); break;
-    default: CSA_LAUNCH_ATTN(4); break;
-  }
+  if (ng == 1) CSA_LAUNCH_ATTN(1);
+  else CSA_LAUNCH_ATTN(2);
 #undef CSA_LAUNCH_ATTN
   if (p.nsplit > 1)
-    hipLaunchKernelGGL(k_attn_merge<D>, dim3((unsigned)(((nq + 7) / 8) * 8 * nw * (D / 64))),
-                       dim3(256), 0, a.stream, part_o, part_ml, p.nsplit, a.H, nw, (int)nq, a.out,
+    hipLaunchKernelGGL(k_attn_merge<D>, dim3((unsigned)(((nq + 7) / 8) * 8 * ng * (D / 32))),
+                       dim3(256), 0, a.stream, part_o, part_ml, p.nsplit, a.H, ng, (int)nq, a.out,
                        a.out_dtype, a.lse);
 }
 
@@ -587,7 +630,7 @@ static int attn_run(const AttnArgs& a, bool dense) {
   if (nsel > 0 && (!a.codes || !a.scales)) return CSA_ERR_NULL;
   if (nsel > 0x3fffffff) return CSA_ERR_SHAPE;
   if (!csa_aligned(a.q, 16) || !csa_aligned(a.win, 16) || !csa_aligned(a.out, 16)) return CSA_ERR_ALIGN;
-  if (nsel > 0 && !csa_aligned(a.codes, 8)) return CSA_ERR_ALIGN;
+  if (nsel > 0 && !csa_aligned(a.codes, 16)) return CSA_ERR_ALIGN;
   const AttnPlan p = attn_plan(a.B, a.T, a.H, a.d, nsel + a.W);
   if (((int64_t)a.B * a.T + 7) / 8 * 8 * p.nsplit > 0x7fffffffLL) return CSA_ERR_SHAPE;
   float* part_o = nullptr;
@@ -596,7 +639,7 @@ static int attn_run(const AttnArgs& a, bool dense) {
     if (!a.ws || a.ws_bytes < p.ws_bytes) return CSA_ERR_WORKSPACE;
     if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
     const int64_t units = (int64_t)a.B * a.T * p.nsplit;
-    const int64_t hpad = 16 * ((a.H + 15) / 16);
+    const int64_t hpad = 32 * ((a.H + 31) / 32);
     part_o = reinterpret_cast<float*>(a.ws);
     part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a.ws) +
                                         ((units * hpad * a.d * 4 + 255) / 256) * 256);

@@ -297,14 +297,16 @@ int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);
  *   out  [B][T][H][d] in out_dtype (CSA_BF16 or CSA_F32)
  *   lse  float32 [B][T][H] or NULL: natural-log log-sum-exp of the logits
  * Supports d in {128, 256, 512}, 1 <= H <= 64, 1 <= W <= Wcap, k >= 0.
- * Numerics: q.k products use the exact bfloat16 values with float32
- * accumulation; probabilities and values enter the value product as float16
- * (entries are exact in float16 while their scale byte lies in [104, 140]),
- * accumulated in float32; when the slots of a query are split over
- * workgroups (few queries per sequence), the normalised partial outputs are
- * kept in float32 and merged in a fixed order. Workspace:
- * csa_attn_workspace(...) bytes (no initialisation needed); it may be NULL
- * when that size is 0.
+ * codes must be 16-byte aligned here (one entry's codes are read as 16-byte
+ * words). Numerics: q, the dequantised entries and the window rows enter both
+ * products as float16 (exact for values in float16's normal range: bfloat16
+ * values of magnitude 2^-14 .. 65504, and entries while their scale byte lies
+ * in [104, 140]; q values below 2^-14 keep float16's subnormal resolution of
+ * 2^-24); q.k and p.v accumulate in float32, probabilities are float16; when
+ * the slots of a query are split over workgroups (few queries per sequence),
+ * the normalised partial outputs are kept in float32 and merged in a fixed
+ * order. Workspace: csa_attn_workspace(...) bytes (no initialisation
+ * needed); it may be NULL when that size is 0.
  * ------------------------------------------------------------------------- */
 int64_t csa_attn_workspace(int B, int T, int H, int d, int64_t n_slots);
 
