@@ -444,13 +444,16 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
 }
 
 // Merge of the split partials, one workgroup per (query, 32-head group,
-// 32-channel tile), one thread per (register quad, lane) of that tile, splits
-// in index order: weights l_s * 2^(m_s - M) / L on the normalised partial
-// outputs. The partials are read in the register order the attention kernel
+// 32-channel tile), one thread per (register quad, lane) of that tile: weights
+// l_s * 2^(m_s - M) / L on the normalised partial outputs, summed in split
+// order. The partials are read in the register order the attention kernel
 // wrote them, 4 KB contiguous per split; thread (q4, lane) holds head lane %
-// 32 and channels 8 q4 + 4 (lane / 32) .. +3 of the tile.
-constexpr int MERGE_MAX = 64;  // splits per query handled by the merge
-template <int D>
+// 32 and channels 8 q4 + 4 (lane / 32) .. +3 of the tile. Every thread loads
+// its head's (max, sum) of all splits and its partials of all splits in one
+// round (indices clamped, surplus splits weighted 0), so the merge is one
+// memory round trip with no LDS and no barrier.
+constexpr int MERGE_MAX = 32;  // splits per query handled by the merge
+template <int D, int NS>       // NS >= nsplit loads in flight per thread
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
                                                     int nsplit, int H, int NG, int n_queries,
@@ -458,8 +461,6 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
                                                     float* __restrict__ lse) {
   constexpr int CT = D / 64;      // tiles per wave (half of d)
   constexpr int TILES = D / 32;   // tiles of a head group
-  __shared__ float s_m[32][MERGE_MAX], s_f[32][MERGE_MAX];
-  __shared__ float s_inv[32];
   // Workgroups are dealt to the XCDs round-robin; every workgroup of query qi
   // goes to XCD qi % 8, where the attention kernel wrote that query's
   // partials, so they are read from that XCD's L2.
@@ -475,61 +476,36 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   const int q4 = threadIdx.x >> 6, ln = threadIdx.x & 63;
   const int j = ln & 31, gg = ln >> 5;
   const int h = hg * 32 + j;
+  const int hc = h < H ? h : H - 1;
   const int NWV = 2 * NG;
   const int64_t split_stride = (int64_t)NWV * CT * 1024;
   const float* src = part_o + (qi * nsplit * NWV + wave) * (CT * 1024) + (4 * ct + q4) * 256 + ln * 4;
-  // the first PB partials are requested before the (max, sum) staging so that
-  // both rounds of loads overlap (indices clamped; surplus ones get weight 0)
-  constexpr int PB = 8;
-  float4 pre[PB];
+  const float2* mls = part_ml + qi * nsplit * H + hc;
+  float2 ml[NS];
+  float4 po[NS];
 #pragma unroll
-  for (int u = 0; u < PB; ++u)
-    pre[u] = *reinterpret_cast<const float4*>(src + (int64_t)(u < nsplit ? u : 0) * split_stride);
-  for (int i = threadIdx.x; i < 32 * nsplit; i += 256) {
-    const int jj = i & 31, sp = i >> 5;
-    const int hh = hg * 32 + jj;
-    const float2 ml = hh < H ? part_ml[(qi * nsplit + sp) * H + hh] : float2{-INFINITY, 0.f};
-    s_m[jj][sp] = ml.x;
-    s_f[jj][sp] = ml.y;
+  for (int s = 0; s < NS; ++s) {
+    const int sp = s < nsplit ? s : 0;
+    ml[s] = mls[(int64_t)sp * H];
+    po[s] = *reinterpret_cast<const float4*>(src + (int64_t)sp * split_stride);
   }
-  __syncthreads();
-  if (threadIdx.x < 32) {
-    const int jj = threadIdx.x;
-    const int hh = hg * 32 + jj;
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_m[jj][sp]);
-    float L = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float f = s_m[jj][sp] == -INFINITY ? 0.f : s_f[jj][sp] * exp2f(s_m[jj][sp] - M);
-      s_f[jj][sp] = f;
-      L += f;
-    }
-    s_inv[jj] = L > 0.f ? 1.f / L : 0.f;
-    if (lse && tile == 0 && hh < H) lse[qi * H + hh] = (M + log2f(L)) * 0.69314718055994531f;
-  }
-  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < nsplit) M = fmaxf(M, ml[s].x);
+  float L = 0.f;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < PB; ++u) {
-    const float f = u < nsplit ? s_f[j][u] : 0.f;
-    acc.x += pre[u].x * f; acc.y += pre[u].y * f;
-    acc.z += pre[u].z * f; acc.w += pre[u].w * f;
-  }
-  for (int s0 = PB; s0 < nsplit; s0 += PB) {
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int sp = s0 + u < nsplit ? s0 + u : 0;
-      pre[u] = *reinterpret_cast<const float4*>(src + (int64_t)sp * split_stride);
-    }
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const float f = s0 + u < nsplit ? s_f[j][s0 + u] : 0.f;
-      acc.x += pre[u].x * f; acc.y += pre[u].y * f;
-      acc.z += pre[u].z * f; acc.w += pre[u].w * f;
-    }
+  for (int s = 0; s < NS; ++s) {
+    const float f = (s >= nsplit || ml[s].x == -INFINITY) ? 0.f : ml[s].y * exp2f(ml[s].x - M);
+    L += f;
+    acc.x += po[s].x * f; acc.y += po[s].y * f;
+    acc.z += po[s].z * f; acc.w += po[s].w * f;
   }
   if (h >= H) return;
-  const float inv = s_inv[j];
+  if (lse && tile == 0 && q4 == 0 && gg == 0)
+    lse[qi * H + h] = (M + log2f(L)) * 0.69314718055994531f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   const int64_t o_off = (qi * H + h) * D + hf * (D / 2) + 32 * ct + 8 * q4 + 4 * gg;
   if (out_dtype == CSA_F32) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o_off) =
@@ -603,10 +579,16 @@ static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, flo
   if (ng == 1) CSA_LAUNCH_ATTN(1);
   else CSA_LAUNCH_ATTN(2);
 #undef CSA_LAUNCH_ATTN
-  if (p.nsplit > 1)
-    hipLaunchKernelGGL(k_attn_merge<D>, dim3((unsigned)(((nq + 7) / 8) * 8 * ng * (D / 32))),
-                       dim3(256), 0, a.stream, part_o, part_ml, p.nsplit, a.H, ng, (int)nq, a.out,
-                       a.out_dtype, a.lse);
+  if (p.nsplit > 1) {
+    const dim3 mgrid((unsigned)(((nq + 7) / 8) * 8 * ng * (D / 32)));
+#define CSA_LAUNCH_MERGE(NS)                                                                 \
+  hipLaunchKernelGGL((k_attn_merge<D, NS>), mgrid, dim3(256), 0, a.stream, part_o, part_ml, \
+                     p.nsplit, a.H, ng, (int)nq, a.out, a.out_dtype, a.lse)
+    if (p.nsplit <= 8) CSA_LAUNCH_MERGE(8);
+    else if (p.nsplit <= 16) CSA_LAUNCH_MERGE(16);
+    else CSA_LAUNCH_MERGE(MERGE_MAX);
+#undef CSA_LAUNCH_MERGE
+  }
 }
 
 static int attn_run(const AttnArgs& a, bool dense) {
@@ -633,6 +615,7 @@ static int attn_run(const AttnArgs& a, bool dense) {
   if (nsel > 0 && !csa_aligned(a.codes, 16)) return CSA_ERR_ALIGN;
   const AttnPlan p = attn_plan(a.B, a.T, a.H, a.d, nsel + a.W);
   if (((int64_t)a.B * a.T + 7) / 8 * 8 * p.nsplit > 0x7fffffffLL) return CSA_ERR_SHAPE;
+  if (p.nsplit > MERGE_MAX) return CSA_ERR_SHAPE;  // the plan keeps it at <= 32
   float* part_o = nullptr;
   float2* part_ml = nullptr;
   if (p.nsplit > 1) {
