@@ -348,8 +348,13 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         const float m_new = fmaxf(m_run, cmax);
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
+        // a head that has seen no finite logit yet has O = 0, so the multiply
+        // is skipped while that holds for every head of the wave (the first
+        // pass of every workgroup)
+        if (__ballot(m_run != -INFINITY)) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) O[ct] *= alpha;
+          for (int ct = 0; ct < CT; ++ct) O[ct] *= alpha;
+        }
         m_run = m_new;
       }
       const bool none = m_run == -INFINITY;
