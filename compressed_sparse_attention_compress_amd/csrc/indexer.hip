@@ -658,8 +658,11 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
 // split scan, phase 2b: one workgroup per query resolves the exact k-th score
 // among the candidates and writes the ascending index list
 // ------------------------------------------------------------------------
-// Dynamic LDS: t_off[MAX_TILES] ints, then cap_lds (score, entry) pairs, then
-// the speculative staging area. The histogram, the per-tile counts and the
+// Dynamic LDS: t_off[toff_n] ints (toff_n >= the tiles of either level), then
+// cap_lds (score, entry) pairs (2 cap_lds >= 4 toff_n, for the slow path's
+// per-tile arrays), then the speculative staging area. Many queries (prefill
+// chunks) get a compact budget so that several workgroups share a compute
+// unit. The histogram, the per-tile counts and the
 // first 2^spec_shift candidates of every tile are all loaded in one round (the
 // candidates speculatively, before their counts are known); only tiles with
 // more candidates than that need a second round. A query with more candidates
@@ -670,14 +673,15 @@ __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
                                                    const int64_t* __restrict__ qpos,
                                                    int64_t blk_cap,
                                                    const int32_t* __restrict__ cand, int C,
-                                                   int cap_lds, int BT, Level L0, Level L1) {
+                                                   int cap_lds, int toff_n, int BT, Level L0,
+                                                   Level L1) {
   extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ int tmp[4];
   __shared__ uint32_t bh[256];
   __shared__ int s_red[8];
   __shared__ int w_gt[4], w_eq[4];
-  int* t_off = smem;                                  // [MAX_TILES]
-  int* area = smem + MAX_TILES;                       // [2 * cap_lds]
+  int* t_off = smem;                                  // [toff_n]
+  int* area = smem + toff_n;                          // [2 * cap_lds]
   int2* spec = reinterpret_cast<int2*>(area + 2 * cap_lds);  // [spec_tiles << spec_shift]
   // queries of the entry selection first, then those of the group selection
   const bool lv1 = (int)blockIdx.x >= BT;
@@ -826,9 +830,9 @@ __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
 
   // ---- slow path: per-tile lists in global memory (arrays alias the area)
   int* t_cnt = area;
-  int* t_gt = area + MAX_TILES;
-  int* t_eq = area + 2 * MAX_TILES;
-  int* t_eqb = area + 3 * MAX_TILES;
+  int* t_gt = area + toff_n;
+  int* t_eq = area + 2 * toff_n;
+  int* t_eqb = area + 3 * toff_n;
   for (int i = threadIdx.x; i < n_tiles; i += 256) t_cnt[i] = cntq[i];
   __syncthreads();
   int vmin = 0x7fffffff, vmax = -1;
@@ -974,23 +978,29 @@ static IdxLayout idx_layout(int64_t BT, int64_t n_max, bool pool) {
 }
 
 // Candidates the final kernel keeps in LDS: about twice k (the entries above
-// the threshold bin plus that bin), at least enough for the slow-path arrays,
-// at most 8192 so that the kernel's LDS stays within 104 KiB (larger k take
-// the slow path, which reads the per-tile lists from global memory).
-static int select_cap(int k) {
-  int c = 4096;
+// the threshold bin plus that bin), at least `least` and enough for the
+// slow-path arrays (2 cap >= 4 toff_n), at most 8192 so that the kernel's LDS
+// stays within 104 KiB (larger k take the slow path, which reads the per-tile
+// lists from global memory).
+static int select_cap(int k, int toff_n, int least) {
+  int c = least;
   while (c < 2 * k && c < 8192) c *= 2;
-  return c;
+  return c > 2 * toff_n ? c : 2 * toff_n;
 }
 
-// Speculative first-round candidates of the final pass: the staging area is
-// shared out evenly, a power of two per tile between 32 and TILE.
-static void spec_plan(int n_tiles, int* spec_tiles, int* spec_shift) {
+// Speculative first-round candidates of the final pass: a staging area of
+// `slots` shared out evenly, a power of two per tile between 32 and TILE.
+static void spec_plan(int n_tiles, int slots, int* spec_tiles, int* spec_shift) {
   int sh = 5;
-  while ((1 << (sh + 1)) <= TILE && ((int64_t)n_tiles << (sh + 1)) <= SPEC_SLOTS) ++sh;
+  while ((1 << (sh + 1)) <= TILE && ((int64_t)n_tiles << (sh + 1)) <= slots) ++sh;
   *spec_shift = sh;
-  *spec_tiles = n_tiles < (SPEC_SLOTS >> sh) ? n_tiles : (SPEC_SLOTS >> sh);
+  *spec_tiles = n_tiles < (slots >> sh) ? n_tiles : (slots >> sh);
 }
+
+// A launch of at least this many queries has workgroups to spare: its final
+// pass uses the compact LDS budget (2,048 candidates, as many speculative
+// slots), which lets four workgroups share a compute unit at k <= 1024.
+constexpr int FINAL_COMPACT_BT = 1024;
 
 // Raise k_idx_final's dynamic LDS limit once per device (to the largest
 // size asked so far), so calls inside a graph capture make no attribute call.
@@ -1131,20 +1141,24 @@ static int idx_phase(const IdxArgs& a, int phase) {
     Level L0{slab, cbuf, cnt, hist, L.npad, L.n_tiles, a.k, 0, 0, 0, a.out_idx, a.out_score};
     Level L1{gslab, gcbuf, gcnt, ghist, L.gpad, L.g_tiles, a.n_keep, 3, 0, 0, a.out_pool,
              nullptr};
-    spec_plan(L.n_tiles, &L0.spec_tiles, &L0.spec_shift);
-    if (pool) spec_plan(L.g_tiles, &L1.spec_tiles, &L1.spec_shift);
+    const bool compact = BT >= FINAL_COMPACT_BT;
+    const int toff_n = ((L.n_tiles > L.g_tiles ? L.n_tiles : L.g_tiles) + 3) / 4 * 4;
+    const int cap_lds = select_cap(pool && a.n_keep > a.k ? a.n_keep : a.k, toff_n,
+                                   compact ? 2048 : 4096);
+    const int slots = compact && cap_lds < SPEC_SLOTS ? cap_lds : SPEC_SLOTS;
+    spec_plan(L.n_tiles, slots, &L0.spec_tiles, &L0.spec_shift);
+    if (pool) spec_plan(L.g_tiles, slots, &L1.spec_tiles, &L1.spec_shift);
     hipLaunchKernelGGL(k_idx_select, dim3(L.n_tiles + L.g_tiles, BT), dim3(256), 0, a.stream,
                        a.T, a.m, a.pos0, a.pos, a.blk_cap, C, a.cand != nullptr, L0, L1);
-    const int cap_lds = select_cap(pool && a.n_keep > a.k ? a.n_keep : a.k);
     const int spec_slots = (L0.spec_tiles << L0.spec_shift) >
                                    (pool ? (L1.spec_tiles << L1.spec_shift) : 0)
                                ? (L0.spec_tiles << L0.spec_shift)
                                : (L1.spec_tiles << L1.spec_shift);
-    const size_t lds = (size_t)(MAX_TILES + 2 * cap_lds) * sizeof(int) +
+    const size_t lds = (size_t)(toff_n + 2 * cap_lds) * sizeof(int) +
                        (size_t)spec_slots * sizeof(int2);
     if (lds > 65536 && !final_lds_allow(lds)) return CSA_ERR_HIP;
     hipLaunchKernelGGL(k_idx_final, dim3(BT * (pool ? 2 : 1)), dim3(256), lds, a.stream, a.T,
-                       a.m, a.pos0, a.pos, a.blk_cap, a.cand, C, cap_lds, BT, L0, L1);
+                       a.m, a.pos0, a.pos, a.blk_cap, a.cand, C, cap_lds, toff_n, BT, L0, L1);
   }
   CSA_TRY_LAUNCH();
   return CSA_OK;
