@@ -551,10 +551,12 @@ __device__ inline void emit_ordered(const int* cs, const int* ce, int M, int tau
 // When a query has at most PICK_MAX candidates (a small Reindex pool, or a
 // context of at most PICK_MAX entries) the per-tile select pass is not
 // needed: one workgroup per query loads the query's whole score row and
-// histogram (left by k_idx_scan), finds the threshold bin, compacts the
-// scores at or above it in index order, then refine_tau and emit_ordered as
-// in k_idx_final. It clears the histogram for the next call. PER = entries
-// per thread (PICK_MAX / 256 at most).
+// histogram (left by k_idx_scan) and finds the threshold bin; the scores
+// stay in registers (thread j holds entries [PER j, PER j + PER)), where the
+// radix refinement of refine_tau and the packed-scan ordered emission of
+// emit_ordered run directly, so the kernel needs almost no LDS and several
+// workgroups share a compute unit. It clears the histogram for the next call.
+// PER = entries per thread (PICK_MAX / 256 at most).
 constexpr int PICK_MAX = 8192;
 template <int PER>
 __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
@@ -565,8 +567,6 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
                                                   const int32_t* __restrict__ cand,
                                                   int32_t* __restrict__ out_idx,
                                                   int32_t* __restrict__ out_score) {
-  __shared__ int cs[PER * 256];
-  __shared__ int ce[PER * 256];
   __shared__ uint32_t bh[256];
   __shared__ int tmp[4];
   __shared__ int s_red[8];
@@ -610,27 +610,13 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
   const int T1 = s_red[0];
   const int need = keff - s_red[1];
   __syncthreads();
-  // in-order compaction of the scores at or above bin T1, and the score
-  // range of bin T1
-  int f = 0;
+  // the score range of bin T1 (every thread's scores stay in its registers)
   int vmin = 0x7fffffff, vmax = -1;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const bool in = sv[j] >= 0 && score_bin512(sv[j]) >= T1;
-    f += in;
-    if (in && score_bin512(sv[j]) == T1) {
+    if (sv[j] >= 0 && score_bin512(sv[j]) == T1) {
       vmin = min(vmin, sv[j]);
       vmax = max(vmax, sv[j]);
-    }
-  }
-  int M;
-  int at = wg_scan_incl<256>(f, tmp, &M) - f;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if (sv[j] >= 0 && score_bin512(sv[j]) >= T1) {
-      cs[at] = sv[j];
-      ce[at] = p0 + j;
-      ++at;
     }
   }
 #pragma unroll
@@ -643,15 +629,68 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
     s_red[4 + wave] = vmax;
   }
   __syncthreads();
-  const int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
+  int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
   const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
   __syncthreads();
-  int take_eq;
-  const int tau = refine_tau(cs, M, T1, lo, hi, need, bh, tmp, s_red, &take_eq);
-  emit_ordered(cs, ce, M, tau, take_eq, keff, tmp, [&](int pos, int e, int v) {
-    oi[pos] = cq ? cq[e] : e;
-    if (os) os[pos] = v;
-  });
+  // exact k-th score: radix refinement of bin T1 as in refine_tau, over the
+  // registers
+  int nd = need;
+  int R = hi - lo;
+  while (R > 0) {
+    const int bits = 32 - __clz(R);
+    const int shift = bits > 8 ? bits - 8 : 0;
+    bh[threadIdx.x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int v = sv[j];
+      if (v >= 0 && score_bin512(v) == T1 && v >= lo && v - lo <= R)
+        atomicAdd(&bh[(v - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    const int c = (int)bh[255 - threadIdx.x];
+    int tot;
+    const int inc = wg_scan_incl<256>(c, tmp, &tot);
+    if (inc >= nd && inc - c < nd) {
+      s_red[0] = 255 - (int)threadIdx.x;
+      s_red[1] = nd - (inc - c);
+    }
+    __syncthreads();
+    const int beta = s_red[0];
+    nd = s_red[1];
+    __syncthreads();
+    lo += beta << shift;
+    R = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
+  }
+  const int tau = lo, take_eq = nd;
+  // ordered emission: thread j's scores are entries [PER j, PER j + PER), so
+  // one scan of the packed (greater, equal) counts gives every output position
+  int gtc = 0, eqc = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    gtc += sv[j] > tau;
+    eqc += sv[j] == tau;
+  }
+  const int mine = (gtc << 16) | eqc;
+  int tot;
+  const int before = wg_scan_incl<256>(mine, tmp, &tot) - mine;
+  int gb = before >> 16, eb = before & 0xffff;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    int pos = -1;
+    if (sv[j] > tau) {
+      pos = gb + min(eb, take_eq);
+      ++gb;
+    } else if (sv[j] == tau) {
+      if (eb < take_eq) pos = gb + eb;
+      ++eb;
+    }
+    if (pos >= 0 && pos < keff) {
+      const int e = p0 + j;
+      oi[pos] = cq ? cq[e] : e;
+      if (os) os[pos] = sv[j];
+    }
+  }
 }
 
 // ------------------------------------------------------------------------
