@@ -126,7 +126,7 @@ def test_compress_tiny_workload():
 # --------------------------------------------------------------- indexer ----
 
 def _index_case(B, T, Hi, Di, m, pos0, k, blk_cap, seed, cand_C=0, wzero=False, keyrange=8,
-                phases=False):
+                phases=False, sample=None):
     g = gen(seed, "idx", B, T, Hi, Di)
     q = torch.randint(-8, 8, (B, T, Hi, Di), generator=g, device=DEV, dtype=torch.int8)
     w = torch.randint(0, 4, (B, T, Hi), generator=g, device=DEV, dtype=torch.int8)
@@ -154,8 +154,14 @@ def _index_case(B, T, Hi, Di, m, pos0, k, blk_cap, seed, cand_C=0, wzero=False, 
     qn, wn, kn = q.cpu().numpy(), w.cpu().numpy(), keys.cpu().numpy()
     oin, osn = oi.cpu().numpy(), os_.cpu().numpy()
     cn = cand.cpu().numpy() if cand is not None else None
-    for b in range(B):
-        for ti in range(T):
+    pairs = [(b, ti) for b in range(B) for ti in range(T)]
+    if sample is not None:  # the first and last queries and a seeded sample of the rest
+        rs = np.random.default_rng(seed)
+        pick = set(rs.choice(len(pairs), size=min(sample, len(pairs)), replace=False).tolist())
+        pick |= {0, len(pairs) - 1}
+        pairs = [pairs[i] for i in sorted(pick)]
+    for b, ti in pairs:
+        if True:
             ref_i, ref_s = O.index_topk(qn[b, ti], wn[b, ti], kn[b], m, pos0 + ti, k,
                                         cand=None if cn is None else cn[b, ti])
             assert np.array_equal(oin[b, ti], ref_i), (b, ti, oin[b, ti][:8], ref_i[:8])
@@ -167,6 +173,23 @@ def _index_case(B, T, Hi, Di, m, pos0, k, blk_cap, seed, cand_C=0, wzero=False, 
 def test_index_decode_shapes(Hi, Di):
     say("index decode", Hi, Di)
     _index_case(3, 2, Hi, Di, 4, 4 * 5000 - 2, 64, 5100, seed=7)
+
+
+def test_index_many_queries_compact():
+    """A 1024-query run over more than 8,192 visible entries: batched scan, per-tile
+    select, and the final pass with its compact LDS budget (launches of >= 1024
+    queries); sampled queries against the oracle."""
+    say("index 1024 queries, compact final pass")
+    _index_case(1, 1024, 8, 64, 4, 4 * 9000, 512, 9000 + 260, seed=12, sample=40)
+
+
+def test_index_many_queries_ties():
+    """The same launch with every score tied (all weights zero) and with keys of
+    one value: more candidates than the compact budget holds, so the final pass
+    walks the per-tile lists in global memory."""
+    say("index 1024 queries, ties")
+    _index_case(1, 1024, 8, 64, 4, 4 * 9000, 512, 9000 + 260, seed=13, wzero=True, sample=12)
+    _index_case(1, 1024, 4, 64, 4, 4 * 9000, 300, 9000 + 260, seed=14, keyrange=1, sample=12)
 
 
 def test_index_decode_edges():
