@@ -551,13 +551,14 @@ __device__ inline void emit_ordered(const int* cs, const int* ce, int M, int tau
 // When a query has at most PICK_MAX candidates (a small Reindex pool, or a
 // context of at most PICK_MAX entries) the per-tile select pass is not
 // needed: one workgroup per query loads the query's whole score row and
-// histogram (left by k_idx_scan) and finds the threshold bin; the scores
-// stay in registers (thread j holds entries [PER j, PER j + PER)), where the
-// radix refinement of refine_tau and the packed-scan ordered emission of
-// emit_ordered run directly, so the kernel needs almost no LDS and several
-// workgroups share a compute unit. It clears the histogram for the next call.
+// histogram (left by k_idx_scan) and finds the threshold bin; thread j holds
+// entries [PER j, PER j + PER) in registers. Up to PICK_LDS candidates at or
+// above the bin are compacted into LDS for refine_tau and emit_ordered; more
+// (heavy ties) are refined and emitted straight from the registers, so the
+// kernel needs 17 KB of LDS and several workgroups share a compute unit. It clears the histogram for the next call.
 // PER = entries per thread (PICK_MAX / 256 at most).
 constexpr int PICK_MAX = 8192;
+constexpr int PICK_LDS = 2048;  // candidates compacted into LDS (more stay in registers)
 template <int PER>
 __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
                                                   const int64_t* __restrict__ qpos,
@@ -567,6 +568,8 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
                                                   const int32_t* __restrict__ cand,
                                                   int32_t* __restrict__ out_idx,
                                                   int32_t* __restrict__ out_score) {
+  __shared__ int cs[PICK_LDS];
+  __shared__ int ce[PICK_LDS];
   __shared__ uint32_t bh[256];
   __shared__ int tmp[4];
   __shared__ int s_red[8];
@@ -610,15 +613,23 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
   const int T1 = s_red[0];
   const int need = keff - s_red[1];
   __syncthreads();
-  // the score range of bin T1 (every thread's scores stay in its registers)
-  int vmin = 0x7fffffff, vmax = -1;
+  // the score range of bin T1, and the count of scores at or above it
+  int vmin = 0x7fffffff, vmax = -1, f = 0;
+  uint32_t in_mask = 0;  // bit j: sv[j] is at or above bin T1
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    if (sv[j] >= 0 && score_bin512(sv[j]) == T1) {
+    const int bj = sv[j] >= 0 ? score_bin512(sv[j]) : -1;
+    if (bj >= T1) {
+      in_mask |= 1u << j;
+      ++f;
+    }
+    if (bj == T1) {
       vmin = min(vmin, sv[j]);
       vmax = max(vmax, sv[j]);
     }
   }
+  int M;
+  int at = wg_scan_incl<256>(f, tmp, &M) - f;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     vmin = min(vmin, __shfl_xor(vmin, off, 64));
@@ -632,8 +643,28 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
   int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
   const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
   __syncthreads();
-  // exact k-th score: radix refinement of bin T1 as in refine_tau, over the
-  // registers
+  if (M <= PICK_LDS) {
+    // few candidates (the usual case): compacted into LDS in index order, so
+    // the refinement and the emission loop over them only
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if ((in_mask >> j) & 1u) {
+        cs[at] = sv[j];
+        ce[at] = p0 + j;
+        ++at;
+      }
+    }
+    __syncthreads();
+    int take_eq;
+    const int tau = refine_tau(cs, M, T1, lo, hi, need, bh, tmp, s_red, &take_eq);
+    emit_ordered(cs, ce, M, tau, take_eq, keff, tmp, [&](int pos, int e, int v) {
+      oi[pos] = cq ? cq[e] : e;
+      if (os) os[pos] = v;
+    });
+    return;
+  }
+  // many candidates (heavy ties): exact k-th score by the radix refinement of
+  // refine_tau, over the registers
   int nd = need;
   int R = hi - lo;
   while (R > 0) {
