@@ -1177,10 +1177,10 @@ static int idx_phase(const IdxArgs& a, int phase) {
 #undef CSA_LAUNCH_BSCAN_H
 #undef CSA_LAUNCH_BSCAN
   } else if (phase == 0) {
-    // small scans split each tile over 2 or 4 workgroups so that about 512
-    // workgroups stream the keys
+    // small scans split each tile over 2 or 4 workgroups so that about 1024
+    // workgroups (four per compute unit, all resident at once) stream the keys
     const int64_t nwg = (int64_t)L.n_tiles * BT;
-    const int sub = nwg >= 512 ? 1 : (nwg >= 256 ? 2 : 4);
+    const int sub = nwg >= 1024 ? 1 : (nwg >= 512 ? 2 : 4);
     const dim3 sgrid(L.n_tiles * sub, BT);
 #define CSA_LAUNCH_SCAN(DD, CC, SS, PP)                                                         \
   hipLaunchKernelGGL((k_idx_scan<DD, CC, SS, PP>), sgrid, dim3(256), 0, a.stream, a.q_idx, a.w, \
