@@ -253,8 +253,11 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
 // (entries a query cannot see yet get -1), the per-query histograms to LDS
 // and then to the global histogram.
 // ------------------------------------------------------------------------
+// byte r of a packed word of int8 head weights, sign-extended
+__device__ inline int wbyte(uint32_t pk, int r) { return (int)(int8_t)(pk >> (8 * r)); }
+
 template <int DI, int HP>
-__global__ __launch_bounds__(256) void k_idx_bscan(
+__global__ __launch_bounds__(256, DI <= 64 ? 4 : 1) void k_idx_bscan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
     const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
     const int64_t* __restrict__ qpos, int64_t npad, int n_groups, int32_t* __restrict__ slab,
@@ -275,35 +278,59 @@ __global__ __launch_bounds__(256) void k_idx_bscan(
 
   for (int i = threadIdx.x; i < QG * NB1; i += 256) (&lh[0][0])[i] = 0;
 
+  // Query rows and head weights: unconditional loads with clamped indexes.
+  // A row of a padding query or head keeps the clamped row: its product is
+  // multiplied by a zero weight. Only chunks past DI (DI = 32) are zeroed. The
+  // weights of this lane's four output rows (four consecutive heads of one
+  // query) are packed as int8 in one word, loaded as one word when Hi is a
+  // multiple of 4.
   v4i A[RT][KS];
-  int wr[RT][4];
+  uint32_t wr[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int ti = t0 + rt * QPT + i16 / HP;
     const int h = i16 % HP;
-    // unconditional loads, clamped indexes, padding masked afterwards
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c0 = ks * 64 + 16 * g;
       const int tc = ti < T ? ti : T - 1, hc = h < Hi ? h : Hi - 1;
       const v4i v = *reinterpret_cast<const v4i*>(
           q_idx + (((int64_t)b * T + tc) * Hi + hc) * DI + (c0 < DI ? c0 : 0));
-      A[rt][ks] = (ti < T && h < Hi && c0 < DI) ? v : v4i{0, 0, 0, 0};
+      A[rt][ks] = (DI >= 64 || c0 < DI) ? v : v4i{0, 0, 0, 0};
     }
+  }
+  if ((Hi & 3) == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * g + r;
-      const int tq = t0 + rt * QPT + row / HP;
-      const int hh = row % HP;
-      const int wv = (int)w[((int64_t)b * T + (tq < T ? tq : T - 1)) * Hi + (hh < Hi ? hh : Hi - 1)];
-      wr[rt][r] = (tq < T && hh < Hi) ? wv : 0;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int tq = t0 + rt * QPT + (4 * g) / HP;
+      const int hh0 = (4 * g) % HP;
+      const uint32_t wv = *reinterpret_cast<const uint32_t*>(
+          w + ((int64_t)b * T + (tq < T ? tq : T - 1)) * Hi + (hh0 < Hi ? hh0 : 0));
+      wr[rt] = (tq < T && hh0 < Hi) ? wv : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        const int tq = t0 + rt * QPT + row / HP;
+        const int hh = row % HP;
+        const uint32_t wv =
+            (uint8_t)w[((int64_t)b * T + (tq < T ? tq : T - 1)) * Hi + (hh < Hi ? hh : Hi - 1)];
+        pk |= ((tq < T && hh < Hi) ? wv : 0u) << (8 * r);
+      }
+      wr[rt] = pk;
     }
   }
   // the score lanes: lane group g holds query g / GPQ of each row tile; the
   // first lane group of each query owns its scores
   const bool owner = (g % GPQ) == 0;
-  int64_t my_nv[RT];
-  int32_t* my_row[RT];
+  // 32-bit per row tile: visible entries and the row offset from the group's
+  // first row, so that nothing 64-bit is kept (or recomputed) per score
+  int my_nv[RT];
+  int my_off[RT];
   bool my_real[RT];  // padding queries of the last group store nothing
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -311,8 +338,8 @@ __global__ __launch_bounds__(256) void k_idx_bscan(
     int64_t nv = (base + ti + 1) / m;
     nv = nv < blk_cap ? nv : blk_cap;
     my_real[rt] = ti < T;
-    my_nv[rt] = ti < T ? nv : 0;
-    my_row[rt] = slab + ((int64_t)b * T + (ti < T ? ti : T - 1)) * npad;
+    my_nv[rt] = ti < T ? (int)nv : 0;
+    my_off[rt] = ((ti < T ? ti : T - 1) - t0) * (int)npad;
   }
   const int t_last = (t0 + QG < T ? t0 + QG : T) - 1;
   int64_t n_end = (base + t_last + 1) / m;  // entries any query of the group can see
@@ -320,6 +347,9 @@ __global__ __launch_bounds__(256) void k_idx_bscan(
   __syncthreads();
 
   const int64_t e_wave = (int64_t)tile * TILE + wave * (TILE / 4);
+  // the group's first score row, from this wave's first entry on
+  int32_t* const slab_w = slab + ((int64_t)b * T + t0) * npad + e_wave;
+  const int nv_w = (int)(e_wave < 0x7fffffff ? e_wave : 0x7fffffff);
   const int8_t* kb = keys + (int64_t)b * blk_cap * DI;
   int coff[KS];
 #pragma unroll
@@ -337,23 +367,39 @@ __global__ __launch_bounds__(256) void k_idx_bscan(
           Bk[buf][u][ks] = *reinterpret_cast<const v4i*>(kb + e * DI + coff[ks]);
       }
     };
+    // Per score the vector work is kept small (it, not the matrix cores,
+    // bounds this kernel): 24-bit multiplies (an int8 weight times a ReLU'd
+    // product of at most DI x 2^14 fits), the cross-lane sum as a ds_swizzle
+    // (xor 16 within 32 lanes, no address register), 32-bit store offsets;
+    // e < npad always holds inside the tile.
     auto consume = [&](int buf, int bt) {
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
-        const int64_t e = e_wave + (int64_t)(bt * BATCH + u) * 16 + i16;
+        const int el = (bt * BATCH + u) * 16 + i16;  // entry within the wave's range
+        // the RT products of the column tile first (independent MFMAs), then
+        // their head sums and cross-lane reductions, then the stores
+        int p[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           v4i acc = {0, 0, 0, 0};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[rt][ks], Bk[buf][u][ks], acc, 0, 0, 0);
-          int p = wr[rt][0] * max(acc[0], 0) + wr[rt][1] * max(acc[1], 0) +
-                  wr[rt][2] * max(acc[2], 0) + wr[rt][3] * max(acc[3], 0);
-          if (GPQ >= 2) p += __shfl_xor(p, 16, 64);
-          if (GPQ >= 4) p += __shfl_xor(p, 32, 64);
-          if (owner && my_real[rt] && e < npad) {
-            const int sc = e < my_nv[rt] ? p : -1;
-            my_row[rt][e] = sc;
+          p[rt] = __mul24(wbyte(wr[rt], 0), max(acc[0], 0)) +
+                  __mul24(wbyte(wr[rt], 1), max(acc[1], 0)) +
+                  __mul24(wbyte(wr[rt], 2), max(acc[2], 0)) +
+                  __mul24(wbyte(wr[rt], 3), max(acc[3], 0));
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          if (GPQ >= 2) p[rt] += __builtin_amdgcn_ds_swizzle(p[rt], 0x401F);  // lane ^ 16
+          if (GPQ >= 4) p[rt] += __shfl_xor(p[rt], 32, 64);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          if (owner && my_real[rt]) {
+            const int sc = el < my_nv[rt] - nv_w ? p[rt] : -1;
+            slab_w[my_off[rt] + el] = sc;
             if (sc >= 0) atomicAdd(&lh[rt * QPT + g / GPQ][score_bin512(sc)], 1u);
           }
         }
