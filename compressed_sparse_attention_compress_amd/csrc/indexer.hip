@@ -49,10 +49,13 @@ __device__ inline int score_tile(const v4i (&A)[KS], const v4i (&Bk)[KS], const 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[ks], Bk[ks], acc, 0, 0, 0);
-  int p = wr[0] * max(acc[0], 0) + wr[1] * max(acc[1], 0) + wr[2] * max(acc[2], 0) +
-          wr[3] * max(acc[3], 0);
-  p += __shfl_xor(p, 16, 64);
-  p += __shfl_xor(p, 32, 64);
+  // 24-bit multiplies (an int8 weight times a ReLU'd product of at most
+  // DI x 2^14 fits), the sum over lane groups as a swizzle (xor 16 within 32
+  // lanes) and one permute (xor 32) whose address is fixed per lane
+  int p = __mul24(wr[0], max(acc[0], 0)) + __mul24(wr[1], max(acc[1], 0)) +
+          __mul24(wr[2], max(acc[2], 0)) + __mul24(wr[3], max(acc[3], 0));
+  p += __builtin_amdgcn_ds_swizzle(p, 0x401F);
+  p += __builtin_amdgcn_ds_bpermute((int)((threadIdx.x & 63) ^ 32) << 2, p);
   return p;
 }
 
