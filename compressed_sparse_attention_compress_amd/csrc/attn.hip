@@ -37,12 +37,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-// Row stride of the float16 stage, in halfs: d plus 16 (a row is then 8
-// dwords past a multiple of the 64 LDS banks). A q.k operand read (32 rows,
-// 32 bytes each) and a transposed p.v read (8 rows, 64 bytes each) both spread
-// evenly over the banks.
+// Row stride of the float16 stage, in halfs: d plus 24 (three 16-byte chunks
+// past a multiple of the 64 LDS banks). Under this stride the q.k operand
+// reads (32 rows, two chunks each) and the staging writes (4 rows x 16 chunks
+// 4 apart) spread evenly over the banks and the transposed p.v reads (8 rows x
+// 4 chunks) take 1.5x their minimum; with d + 16 the staging writes took 2x
+// (measured: the larger part of the kernel's LDS bank-conflict cycles).
 template <int D>
-constexpr int row_stride() { return D + 16; }
+constexpr int row_stride() { return D + 24; }
 
 // Transposing LDS read: within each 16-lane group, lane i receives element
 // i % 4 of the 4-half words addressed by lanes 4j + i / 4 (j = 0..3).
