@@ -93,7 +93,7 @@ __device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
 template <int DI, bool CAND, int SUB, bool POOL>
 __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
-    const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
+    const int8_t* keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
     const int64_t* __restrict__ qpos, const int32_t* __restrict__ cand, int C, int64_t npad,
     int32_t* __restrict__ slab,
     uint32_t* __restrict__ hist, int64_t gpad, int32_t* __restrict__ gslab,
@@ -154,8 +154,12 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   int coff[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) coff[ks] = (ks * 64 + 16 * g) % DI;
-  const bool loads_ok = nv > 0;  // some key row exists to clamp to
-  if (wg0 < N) {
+  // with no visible key row to clamp to (a pool query before its first
+  // block completes) every entry scores -1 and no key is read; otherwise the
+  // loads below carry no condition, so they issue back to back
+  if (wg0 < N && nv == 0) {
+    for (int j = threadIdx.x; j < SPAN; j += 256) ssc[j] = -1;
+  } else if (wg0 < N) {
     // two register buffers: the keys of batch bt + 1 are in flight while
     // batch bt is in the matrix cores
     constexpr int NBT = SPAN / 4 / 16 / BATCH;  // batches of BATCH column tiles per wave
@@ -188,16 +192,15 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          Bk[buf][u][ks] = loads_ok ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(
-                                          kb + blk * DI + coff[ks]))
-                                    : v4i{0, 0, 0, 0};
+          Bk[buf][u][ks] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4i*>(kb + blk * DI + coff[ks]));
       }
     };
-    auto consume = [&](int buf, int bt) {
+    auto consume = [&](int buf, int bt, const v4i (&Aq)[KS]) {
       int sc[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
-        const int s = score_tile<KS>(A, Bk[buf][u], wr);
+        const int s = score_tile<KS>(Aq, Bk[buf][u], wr);
         sc[u] = valid[buf][u] ? s : -1;
       }
       // lane (j + 16g) takes tile 4h+g, entry j
@@ -215,7 +218,18 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
 #pragma unroll
     for (int bt = 0; bt < NBT; ++bt) {
       if (bt + 1 < NBT) issue((bt + 1) & 1, bt + 1);
-      consume(bt & 1, bt);
+      // the compiler would otherwise sink the next batch's loads below this
+      // batch's products, and the in-order load counter would then wait for
+      // both batches together: the empty statement orders the key loads
+      // before it (memory clobber) and the products after it (their query
+      // operand takes a zero it yields)
+      int dep = 0;
+      asm volatile("" : "+v"(dep)::"memory");
+      v4i Aq[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) Aq[ks] = A[ks];
+      Aq[0][0] += dep;
+      consume(bt & 1, bt, Aq);
     }
   }
   __syncthreads();
