@@ -61,7 +61,7 @@ __device__ inline _Float16 bf16_to_f16(uint32_t bits) {
 // One workgroup per compute unit is all the LDS allows at d = 512, so the
 // compiler is told to schedule for one wave per SIMD (registers for LDS
 // reads in flight rather than for occupancy).
-template <int D, int NG, bool DENSE, int FMT>
+template <int D, int NG, bool DENSE, int FMT, bool WF>
 __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t blk_cap, const int32_t* __restrict__ idx, int k,
@@ -125,12 +125,36 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   // wave half h holds head i's channels h d/2 + 16 kk + 8 gg .. +7 of every
   // k-step kk, as float16
   v8h Qop[KS2];
+  const uint8_t* cbase = codes + (int64_t)b * blk_cap * (D / 2);
+  const uint8_t* sbase = scales + (int64_t)b * blk_cap * SPE;
+  const uint16_t* wbase = win + (int64_t)b * Wcap * D;
+  const int64_t ep0 = s_begin, ep1 = e_end;                          // entry slots
+  const int64_t wp0 = s_begin > nsel ? s_begin : nsel, wp1 = s_end;  // window slots
+  // window staging task (slot c0 + s, 32-channel chunk c): 64 bytes of a row
+  struct RawW {
+    uint4 w[4];
+  };
+  auto load_win = [&](RawW& r, int task, int64_t c0) {
+    const int c = task % CHUNKS, s = task / CHUNKS;
+    const int64_t sl = c0 + s;
+    int64_t p = t - W + 1 + (sl - nsel);
+    p = p < 0 ? 0 : p;
+    const uint4* src = reinterpret_cast<const uint4*>(wbase + (p % Wcap) * D + 32 * c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r.w[u] = src[u];
+  };
+  constexpr int NPRE = TPT < 2 ? TPT : 2;
+  RawW wpre[NPRE];  // the first window tasks, requested with the q rows
   {
     const int hq = head < H ? head : H - 1;
     const uint16_t* qr = q + ((int64_t)qi * H + hq) * D + half * (D / 2) + 8 * gg;
     v8us raw[KS2];
 #pragma unroll
     for (int kk = 0; kk < KS2; ++kk) raw[kk] = *reinterpret_cast<const v8us*>(qr + 16 * kk);
+    if (WF && wp0 < wp1) {
+#pragma unroll
+      for (int u = 0; u < NPRE; ++u) load_win(wpre[u], threadIdx.x + u * NT, wp0);
+    }
 #pragma unroll
     for (int kk = 0; kk < KS2; ++kk)
 #pragma unroll
@@ -144,27 +168,48 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   // running max and sum; both waves of a head group compute the same values
   float m_run = -INFINITY, l_run = 0.f;
 
-  const uint8_t* cbase = codes + (int64_t)b * blk_cap * (D / 2);
-  const uint8_t* sbase = scales + (int64_t)b * blk_cap * SPE;
-  const uint16_t* wbase = win + (int64_t)b * Wcap * D;
+  // The window phase runs first: its rows need no ids, so their loads go out
+  // with the q rows and the ids; the first entry gather is then issued during
+  // the window passes (its ids are in LDS by then) and converted when the
+  // entry phase starts.
+  struct RawE {
+    uint4 w;
+    uint32_t sc;
+  };
+  RawE eraw[TPT];          // raw bytes of the next entry pass to be staged
+  bool eraw_ok = false;    // eraw holds the entry phase's first pass
+  bool ids_stored = false; // s_blk holds the entry phase's first table
+  // entry ids of slots [from, from + IDX_CAP) into LDS
+  auto store_ids = [&](int64_t from, const int64_t* v) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int i = threadIdx.x + r * NT;
+      const int64_t sl = from + i;
+      if (i < IDX_CAP) s_blk[i] = (sl < ep1 && v[r] >= 0 && v[r] < blk_cap) ? (int)v[r] : -1;
+    }
+  };
+  // raw bytes of entry task (slot c0 + s, 32-channel chunk c), chunk fastest
+  // across lanes so that 16 lanes (d = 512) read one entry's 256 code bytes
+  // contiguously; tab0 is the first slot of the id table in s_blk
+  auto load_entry = [&](RawE& r, int task, int64_t c0, int64_t tab0) {
+    const int c = task % CHUNKS, s = task / CHUNKS;
+    const int64_t sl = c0 + s;
+    int blk = (sl < ep1 && sl - tab0 < IDX_CAP) ? s_blk[sl - tab0] : -1;
+    blk = blk < 0 ? 0 : blk;
+    r.w = *reinterpret_cast<const uint4*>(cbase + (int64_t)blk * (D / 2) + 16 * c);
+    const uint8_t* sp = sbase + (int64_t)blk * SPE + (E4 ? 2 * c : c);
+    r.sc = E4 ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : (uint32_t)sp[0];
+  };
 
-  // One homogeneous phase: entries (IS_WIN false) or window tokens, slots
+  // One homogeneous phase: window tokens (IS_WIN true) or entries, slots
   // [p0, p1). Loads are unconditional (clamped rows), validity is applied to
   // the logits.
   auto phase = [&](auto is_win_tag, int64_t p0, int64_t p1) {
     constexpr bool IS_WIN = decltype(is_win_tag)::value;
     if (p0 >= p1) return;
     int64_t tab0 = p0;  // first slot whose block id sits in s_blk[0]
-    // entry ids of slots [from, from + IDX_CAP) into LDS; all loads issued
-    // before the first is used (addresses clamped into the phase)
-    auto store_ids = [&](int64_t from, const int64_t* v) {
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        const int i = threadIdx.x + r * NT;
-        const int64_t sl = from + i;
-        if (i < IDX_CAP) s_blk[i] = (sl < p1 && v[r] >= 0 && v[r] < blk_cap) ? (int)v[r] : -1;
-      }
-    };
+    // a later id table: all loads issued before the first is used
+    // (addresses clamped into the phase)
     auto refill = [&](int64_t from) {
       __syncthreads();
       tab0 = from;
@@ -177,34 +222,17 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       store_ids(from, v);
       __syncthreads();
     };
-    // task (slot s, 32-channel chunk c), chunk fastest across lanes, so that
-    // 16 lanes (d = 512) read one entry's 256 code bytes contiguously
-    struct Raw {
-      uint4 w[IS_WIN ? 4 : 1];
-      uint32_t sc;
-    };
+    using Raw = typename std::conditional<IS_WIN, RawW, RawE>::type;
     auto load_task = [&](Raw& r, int task, int64_t c0) {
-      const int c = task % CHUNKS, s = task / CHUNKS;
-      const int64_t sl = c0 + s;
-      if (IS_WIN) {
-        int64_t p = t - W + 1 + (sl - nsel);
-        p = p < 0 ? 0 : p;
-        const uint4* src = reinterpret_cast<const uint4*>(wbase + (p % Wcap) * D + 32 * c);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r.w[u] = src[u];
-        r.sc = 0;
-      } else {
-        int blk = (sl < p1 && sl - tab0 < IDX_CAP) ? s_blk[sl - tab0] : -1;
-        blk = blk < 0 ? 0 : blk;
-        r.w[0] = *reinterpret_cast<const uint4*>(cbase + (int64_t)blk * (D / 2) + 16 * c);
-        const uint8_t* sp = sbase + (int64_t)blk * SPE + (E4 ? 2 * c : c);
-        r.sc = E4 ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : (uint32_t)sp[0];
-      }
+      if constexpr (IS_WIN)
+        load_win(r, task, c0);
+      else
+        load_entry(r, task, c0, tab0);
     };
     auto convert_task = [&](const Raw& r, int task) {
       const int c = task % CHUNKS, s = task / CHUNKS;
       v8h h[4];
-      if (IS_WIN) {
+      if constexpr (IS_WIN) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const uint32_t wd[4] = {r.w[u].x, r.w[u].y, r.w[u].z, r.w[u].w};
@@ -219,36 +247,43 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         // significant bits, magnitudes 2^-10 .. 2688)
         const _Float16 s0 = (_Float16)e4m3_to_f32(r.sc & 0xffu);
         const _Float16 s1 = (_Float16)e4m3_to_f32(r.sc >> 8);
-        h[0] = fp4x8_to_f16(r.w[0].x, 1.0f) * s0;
-        h[1] = fp4x8_to_f16(r.w[0].y, 1.0f) * s0;
-        h[2] = fp4x8_to_f16(r.w[0].z, 1.0f) * s1;
-        h[3] = fp4x8_to_f16(r.w[0].w, 1.0f) * s1;
+        h[0] = fp4x8_to_f16(r.w.x, 1.0f) * s0;
+        h[1] = fp4x8_to_f16(r.w.y, 1.0f) * s0;
+        h[2] = fp4x8_to_f16(r.w.z, 1.0f) * s1;
+        h[3] = fp4x8_to_f16(r.w.w, 1.0f) * s1;
       } else {
         const float sc = e8m0_to_f32(r.sc);
-        h[0] = fp4x8_to_f16(r.w[0].x, sc);
-        h[1] = fp4x8_to_f16(r.w[0].y, sc);
-        h[2] = fp4x8_to_f16(r.w[0].z, sc);
-        h[3] = fp4x8_to_f16(r.w[0].w, sc);
+        h[0] = fp4x8_to_f16(r.w.x, sc);
+        h[1] = fp4x8_to_f16(r.w.y, sc);
+        h[2] = fp4x8_to_f16(r.w.z, sc);
+        h[3] = fp4x8_to_f16(r.w.w, sc);
       }
       v8h* dst = reinterpret_cast<v8h*>(Rs + s * RS + 32 * c);
 #pragma unroll
       for (int u = 0; u < 4; ++u) dst[u] = h[u];
     };
     // entries: raw bytes prefetched one pass ahead (they are small); window
-    // rows: loaded right before they are converted, two tasks in flight
-    Raw raw[IS_WIN ? 1 : TPT];
-    bool have_raw = false;  // raw[] holds the pass to be staged (entries only)
-    auto stage = [&](int64_t c0) {
-      if (IS_WIN) {
+    // rows: loaded right before they are converted, two tasks in flight (the
+    // first two tasks of the phase's first pass were issued at kernel start)
+    RawE (&raw)[TPT] = eraw;
+    bool& have_raw = eraw_ok;  // raw[] holds the pass to be staged (entries only)
+    auto stage = [&](int64_t c0, auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
+      if constexpr (IS_WIN) {
         Raw wr[2];
-        load_task(wr[0], threadIdx.x, c0);
+        if constexpr (WF && FIRST) {
+#pragma unroll
+          for (int u = 0; u < NPRE; ++u) wr[u] = wpre[u];
+        } else {
+          load_task(wr[0], threadIdx.x, c0);
+        }
 #pragma unroll
         for (int tt = 0; tt < TPT; ++tt) {
-          if (tt + 1 < TPT) load_task(wr[(tt + 1) & 1], threadIdx.x + (tt + 1) * NT, c0);
+          if (tt + 1 < TPT && !(WF && FIRST && tt + 1 < NPRE))
+            load_task(wr[(tt + 1) & 1], threadIdx.x + (tt + 1) * NT, c0);
           convert_task(wr[tt & 1], threadIdx.x + tt * NT);
         }
-        return;
-      }
+      } else {
       if (!have_raw) {
 #pragma unroll
         for (int tt = 0; tt < TPT; ++tt) load_task(raw[tt], threadIdx.x + tt * NT, c0);
@@ -268,15 +303,37 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int tt = 0; tt < TPT; ++tt) load_task(raw[tt], threadIdx.x + tt * NT, c0 + CH);
         have_raw = true;
       }
+      }
     };
-    if (!IS_WIN) {
-      // the first table: the entry range starts at s_begin, its ids are loaded
-      store_ids(p0, first_ids);
-      __syncthreads();
+    if constexpr (!IS_WIN) {
+      // the first table (unless the window phase wrote it): the entry range
+      // starts at s_begin, its ids were loaded at kernel start
+      if (!ids_stored) {
+        store_ids(p0, first_ids);
+        ids_stored = true;
+        __syncthreads();
+      }
     }
-    stage(p0);
+    stage(p0, std::true_type{});
+    if constexpr (IS_WIN && WF) {
+      // the entry phase's first id table, once the window rows are requested
+      // (made visible by the barrier below)
+      if (ep0 < ep1) {
+        store_ids(ep0, first_ids);
+        ids_stored = true;
+      }
+    }
     for (int64_t c0 = p0; c0 < p1; c0 += CH) {
       __syncthreads();  // this pass's rows are staged
+      if constexpr (IS_WIN && WF && TPT <= 4) {
+        // the entry phase's first gather, in flight during the window passes
+        // (not with 8 tasks per thread: their registers would spill)
+        if (ids_stored && !eraw_ok) {
+#pragma unroll
+          for (int tt = 0; tt < TPT; ++tt) load_entry(eraw[tt], threadIdx.x + tt * NT, ep0, ep0);
+          eraw_ok = true;
+        }
+      }
       // validity of this lane's logit slots: tile et, register r holds slot
       // 32 et + 8 (r / 4) + 4 gg + r % 4 of the pass; bit 16 et + r
       uint32_t okm = 0;
@@ -400,13 +457,18 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (c0 + CH < p1) {
         __syncthreads();  // every read of this pass's rows is done
         if (!IS_WIN && c0 + 2 * CH > tab0 + IDX_CAP) refill(c0 + CH);
-        stage(c0 + CH);
+        stage(c0 + CH, std::false_type{});
       }
     }
     __syncthreads();  // the stage may be rewritten by the next phase
   };
-  phase(std::false_type{}, s_begin, s_end < nsel ? s_end : nsel);
-  phase(std::true_type{}, s_begin > nsel ? s_begin : nsel, s_end);
+  if constexpr (WF) {
+    phase(std::true_type{}, wp0, wp1);
+    phase(std::false_type{}, ep0, ep1);
+  } else {
+    phase(std::false_type{}, ep0, ep1);
+    phase(std::true_type{}, wp0, wp1);
+  }
 
   // softmax denominator: the two lanes of a head hold the two halves of the slots
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -579,12 +641,21 @@ static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, flo
   const int64_t nq = (int64_t)a.B * a.T;
   const dim3 grid((unsigned)(((nq + 7) / 8) * 8 * p.nsplit));
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
-#define CSA_LAUNCH_ATTN(NG)                                                                  \
-  hipLaunchKernelGGL((k_attn<D, NG, DENSE, FMT>), grid, dim3(NG * 128), 0, a.stream, a.q, a.codes, \
-                     a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, a.H, a.pos0, \
-                     a.pos, sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse, part_o, part_ml)
-  if (ng == 1) CSA_LAUNCH_ATTN(1);
-  else CSA_LAUNCH_ATTN(2);
+#define CSA_LAUNCH_ATTN(NG, WF)                                                              \
+  hipLaunchKernelGGL((k_attn<D, NG, DENSE, FMT, WF>), grid, dim3(NG * 128), 0, a.stream, a.q,   \
+                     a.codes, a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, a.H, \
+                     a.pos0, a.pos, sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse,   \
+                     part_o, part_ml)
+  // a workgroup that takes a whole query (runs of queries) stages the window
+  // first so that its start-up loads overlap; split queries keep the entries
+  // first (measured faster there)
+  if (p.nsplit == 1) {
+    if (ng == 1) CSA_LAUNCH_ATTN(1, true);
+    else CSA_LAUNCH_ATTN(2, true);
+  } else {
+    if (ng == 1) CSA_LAUNCH_ATTN(1, false);
+    else CSA_LAUNCH_ATTN(2, false);
+  }
 #undef CSA_LAUNCH_ATTN
   if (p.nsplit > 1) {
     const dim3 mgrid((unsigned)(((nq + 7) / 8) * 8 * ng * (D / 32)));
