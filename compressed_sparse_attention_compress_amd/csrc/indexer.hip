@@ -90,6 +90,8 @@ __device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
 // POOL: the tile's scores are also reduced to the best score of each group of
 // POOL_G consecutive entries (group slab + group histogram), for the
 // blockwise candidate pool.
+// (keys carries no restrict: loads through it then stay ordered with the
+// empty asm statement that paces the batches below)
 template <int DI, bool CAND, int SUB, bool POOL>
 __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
