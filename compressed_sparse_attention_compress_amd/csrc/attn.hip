@@ -83,7 +83,9 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ __attribute__((aligned(16))) _Float16 Rs[CH * RS];
   __shared__ int s_blk[IDX_CAP];
   // each wave's partial logits of both 32-slot tiles, in register order
-  __shared__ __attribute__((aligned(16))) float4 s_S[NWV][2][4][64];
+  // (a plain vector type: the HIP float4 struct was read back as single
+  // dwords, four bank-conflicted reads per value instead of one)
+  __shared__ __attribute__((aligned(16))) v4f s_S[NWV][2][4][64];
   __shared__ unsigned long long s_valid;      // entry slots of the staged pass that are valid
 
   // Workgroups are dealt to the 8 XCDs round-robin by id; all splits of a
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int et = 0; et < 2; ++et)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          s_S[wave][et][q4][lane] = float4{S[et][4 * q4], S[et][4 * q4 + 1], S[et][4 * q4 + 2],
+          s_S[wave][et][q4][lane] = v4f{S[et][4 * q4], S[et][4 * q4 + 1], S[et][4 * q4 + 2],
                                            S[et][4 * q4 + 3]};
       __syncthreads();
       // full logits of the 64 slots (own half of d + the partner's)
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int et = 0; et < 2; ++et)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 o = s_S[partner][et][q4][lane];
+          const v4f o = s_S[partner][et][q4][lane];
           const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
