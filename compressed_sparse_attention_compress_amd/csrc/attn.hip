@@ -141,7 +141,10 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int64_t sl = c0 + s;
     int64_t p = t - W + 1 + (sl - nsel);
     p = p < 0 ? 0 : p;
-    const uint4* src = reinterpret_cast<const uint4*>(wbase + (p % Wcap) * D + 32 * c);
+    // positions and the ring size are below 2^31 (checked at the entry
+    // points), so the ring slot takes a 32-bit remainder, not a 64-bit one
+    const uint32_t ring = (uint32_t)p % (uint32_t)Wcap;
+    const uint4* src = reinterpret_cast<const uint4*>(wbase + (int64_t)ring * D + 32 * c);
 #pragma unroll
     for (int u = 0; u < 4; ++u) r.w[u] = src[u];
   };
@@ -677,6 +680,7 @@ static int attn_run(const AttnArgs& a, bool dense) {
   if (a.H < 1 || a.H > 64) return CSA_ERR_SHAPE;
   if (a.W < 1 || a.Wcap < a.W) return CSA_ERR_SHAPE;
   if ((int64_t)a.Wcap < (int64_t)a.W + a.T - 1) return CSA_ERR_RANGE;
+  if (a.pos0 > 0x7fffffffLL - a.T) return CSA_ERR_RANGE;  // positions fit 31 bits
   if (!dense && a.k < 0) return CSA_ERR_SHAPE;
   if (dense && (a.m < 1 || a.m > 1 << 20)) return CSA_ERR_SHAPE;
   if (a.out_dtype != CSA_BF16 && a.out_dtype != CSA_F32) return CSA_ERR_DTYPE;

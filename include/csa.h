@@ -296,7 +296,8 @@ int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);
  *   win  bf16 [B][Wcap][d]         16-byte aligned; Wcap >= W + T - 1
  *   out  [B][T][H][d] in out_dtype (CSA_BF16 or CSA_F32)
  *   lse  float32 [B][T][H] or NULL: natural-log log-sum-exp of the logits
- * Supports d in {128, 256, 512}, 1 <= H <= 64, 1 <= W <= Wcap, k >= 0.
+ * Supports d in {128, 256, 512}, 1 <= H <= 64, 1 <= W <= Wcap, k >= 0,
+ * pos0 + T <= 2^31 - 1 (else CSA_ERR_RANGE).
  * codes must be 16-byte aligned here (one entry's codes are read as 16-byte
  * words). Numerics: q, the dequantised entries and the window rows enter both
  * products as float16 (exact for values in float16's normal range: bfloat16

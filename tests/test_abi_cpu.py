@@ -105,6 +105,10 @@ def test_argument_errors_before_launch(L):
     assert L.csa_sparse_attn(*a(512, 64, 0, 128, 1, 0)) == -2
     assert L.csa_sparse_attn(*a(512, 64, 128, 128, 1, 7)) == -5
     assert L.csa_sparse_attn(*a(512, 64, 128, 128, 1, 0, fmt=3)) == -5
+    # positions must fit 31 bits (the window ring slot is a 32-bit remainder)
+    far = list(a(512, 64, 128, 128, 1, 0))
+    far[13] = (1 << 31) - 1
+    assert L.csa_sparse_attn(*far) == -3
     # ragged attention: positions missing
     ra = (fake, fake, fake, 100, fake, 8, fake, 128, 128, 1, 1, 64, 512, None, 399,
           ctypes.c_float(1.0), fake, 0, None, fake, 1 << 30, 0, None)
