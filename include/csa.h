@@ -303,7 +303,9 @@ int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);
  * products as float16 (exact for values in float16's normal range: bfloat16
  * values of magnitude 2^-14 .. 65504, and entries while their scale byte lies
  * in [104, 140]; q values below 2^-14 keep float16's subnormal resolution of
- * 2^-24); q.k and p.v accumulate in float32, probabilities are float16; when
+ * 2^-24); q.k and p.v accumulate in float32, probabilities are float16
+ * (taken against a running max that lags the true one by at most a factor
+ * of 2, so they stay at most 2); when
  * the slots of a query are split over workgroups (few queries per sequence),
  * the normalised partial outputs are kept in float32 and merged in a fixed
  * order. Workspace: csa_attn_workspace(...) bytes (no initialisation
