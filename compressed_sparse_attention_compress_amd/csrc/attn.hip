@@ -149,6 +149,12 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int u = 0; u < 4; ++u) r.w[u] = src[u];
   };
   constexpr int NPRE = TPT < 2 ? TPT : 2;
+  struct RawE {
+    uint4 w;
+    uint32_t sc;
+  };
+  RawE eraw[TPT];          // raw bytes of the next entry pass to be staged
+  bool eraw_ok = false;    // eraw holds the entry phase's first pass
   RawW wpre[NPRE];  // the first window tasks, requested with the q rows
   {
     const int hq = head < H ? head : H - 1;
@@ -159,6 +165,24 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (WF && wp0 < wp1) {
 #pragma unroll
       for (int u = 0; u < NPRE; ++u) load_win(wpre[u], threadIdx.x + u * NT, wp0);
+    }
+    // dense attention needs no ids (slot = block), so its first entry pass is
+    // requested with the q rows as well (slots past the range read row ep0
+    // and are masked like any invalid slot)
+    if constexpr (DENSE && !WF && TPT <= 4) {
+      if (ep0 < ep1) {
+#pragma unroll
+        for (int tt = 0; tt < TPT; ++tt) {
+          const int task = threadIdx.x + tt * NT;
+          const int c = task % CHUNKS;
+          const int64_t sl = ep0 + task / CHUNKS;
+          const int64_t blk = sl < ep1 ? sl : ep0;
+          eraw[tt].w = *reinterpret_cast<const uint4*>(cbase + blk * (D / 2) + 16 * c);
+          const uint8_t* sp = sbase + blk * SPE + (E4 ? 2 * c : c);
+          eraw[tt].sc = E4 ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : (uint32_t)sp[0];
+        }
+        eraw_ok = true;
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < KS2; ++kk)
@@ -177,12 +201,6 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   // with the q rows and the ids; the first entry gather is then issued during
   // the window passes (its ids are in LDS by then) and converted when the
   // entry phase starts.
-  struct RawE {
-    uint4 w;
-    uint32_t sc;
-  };
-  RawE eraw[TPT];          // raw bytes of the next entry pass to be staged
-  bool eraw_ok = false;    // eraw holds the entry phase's first pass
   bool ids_stored = false; // s_blk holds the entry phase's first table
   // entry ids of slots [from, from + IDX_CAP) into LDS
   auto store_ids = [&](int64_t from, const int64_t* v) {
