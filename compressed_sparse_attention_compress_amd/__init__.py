@@ -48,7 +48,12 @@ class CSAError(RuntimeError):
 
 
 _lib = None
-_RECORD = None  # list of (C function, marshalled arguments) while prepare() runs
+# While prepare() runs: the recorded calls, each (name, C function, marshalled
+# arguments, index-workspace head requirement or None), and every tensor whose
+# address was marshalled (kept alive by the recording).
+_RECORD = None
+_KEEP = None
+_PENDING_HEAD = None  # head requirement of the index call being marshalled
 _QUERIES = ("csa_status_string", "csa_version", "csa_cache_bytes")
 
 
@@ -65,9 +70,26 @@ class _RecordingLib:
             return fn
 
         def record(*args):
-            _RECORD.append((name, fn, args))
+            global _PENDING_HEAD
+            _RECORD.append((name, fn, args, _PENDING_HEAD))
+            _PENDING_HEAD = None
             return 0
         return record
+
+
+def _ensure_head(buf, key, stream=None):
+    """An index workspace's head (per-query histograms) must be zero for the
+    layout of `key` (B*T) when a call starts; every successful call leaves it
+    so. A buffer last used under another key is zero-filled first (with the
+    library's fill kernel on `stream`, or torch's on the current stream)."""
+    if key is None or getattr(buf, "_csa_key", None) == key:
+        return
+    if stream is None:
+        buf.zero_()
+    else:
+        _check(_lib.csa_workspace_clear(ctypes.c_void_p(buf.data_ptr()), buf.numel() // 4 * 4,
+                                        stream), "csa_workspace_clear")
+    buf._csa_key = key
 
 
 def prepare(fn):
@@ -75,19 +97,29 @@ def prepare(fn):
     instead of issued (workspaces are sized and allocated now). Returns a
     callable that issues exactly those launches again, on the streams that
     were current when they were recorded, with the same buffers: the argument
-    marshalling of a serving loop done once."""
-    global _RECORD
-    _RECORD = []
+    marshalling of a serving loop done once.
+
+    The callable keeps every tensor whose address was recorded alive
+    (temporary workspaces included), so a replay never writes into freed
+    memory. Before each recorded index call it checks that the workspace's
+    head is laid out for that call's B*T; if another call has used the buffer
+    under a different B*T since, the buffer is zero-filled on the recorded
+    stream first."""
+    global _RECORD, _KEEP, _PENDING_HEAD
+    _RECORD, _KEEP, _PENDING_HEAD = [], [], None
     try:
         fn()
     finally:
-        calls, _RECORD = _RECORD, None
+        calls, keep, _RECORD, _KEEP, _PENDING_HEAD = _RECORD, _KEEP, None, None, None
 
     def run():
-        for name, f, args in calls:
+        for name, f, args, head in calls:
+            if head is not None:
+                _ensure_head(*head)
             st = f(*args)
             if st:
                 _check(st, name)
+    run.kept_tensors = keep
     return run
 
 
@@ -149,7 +181,11 @@ def _check(status: int, what: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    if _KEEP is not None:
+        _KEEP.append(t)
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream():
@@ -195,13 +231,14 @@ class Workspace:
     def get(self, nbytes: int, key=None):
         """A buffer of at least nbytes. `key` names the layout of the
         workspace head (B*T for the indexer); the buffer is zero-filled
-        again whenever it changes."""
+        again whenever it changes (the key is kept on the buffer itself, so
+        replays of prepare() see what eager calls did to it)."""
         if nbytes <= 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device or "cuda")
-        elif key is not None and key != self.key:
-            self.buf.zero_()
+            self.buf._csa_key = key
+        _ensure_head(self.buf, key)
         self.key = key
         return self.buf
 
@@ -276,6 +313,15 @@ def dequantize(codes, scales, blk0: int, n_blk: int, out, fmt: str = "e8m0"):
                                 _ptr(out), dt, _fmt_code(fmt), _stream()), "csa_dequantize")
 
 
+def _note_head(workspace, ws, key):
+    """While recording: the next recorded call needs the head of ws (a buffer
+    of a Workspace) laid out for `key`. Raw tensors passed as workspaces are
+    the caller's to clear, as in eager calls."""
+    global _PENDING_HEAD
+    if _RECORD is not None and ws is not None and isinstance(workspace, Workspace):
+        _PENDING_HEAD = (ws, key, _stream())
+
+
 def index_topk_workspace(B, T, n_max, k, cand_given=False) -> int:
     return lib().csa_index_topk_workspace(B, T, n_max, k, int(bool(cand_given)))
 
@@ -319,6 +365,7 @@ def _index_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, out_score=None, ca
         workspace = _default_ws(q_idx.device)
     ws = workspace.get(need, key=B * T) if isinstance(workspace, Workspace) else workspace
     ws_bytes = 0 if ws is None else ws.numel()
+    _note_head(workspace, ws, B * T)
     if pos is not None:
         fn_name += "_ragged"
         _check(getattr(lib(), fn_name)(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di,
@@ -385,6 +432,7 @@ def _pool_call(fn_name, q_idx, w, keys, m, pos0, k, out_idx, n_keep, out_pool, o
         workspace = _default_ws(q_idx.device)
     ws = workspace.get(need, key=B * T) if isinstance(workspace, Workspace) else workspace
     ws_bytes = 0 if ws is None else ws.numel()
+    _note_head(workspace, ws, B * T)
     _check(getattr(lib(), fn_name)(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di, m,
                                    pos0, k, _ptr(out_idx), _ptr(out_score), group, n_keep,
                                    _ptr(out_pool), _ptr(ws), ws_bytes, _stream()), fn_name)

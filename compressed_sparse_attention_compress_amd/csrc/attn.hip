@@ -196,6 +196,10 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int r = 0; r < 16; ++r) O[ct][r] = 0.f;
   // running max and sum; both waves of a head group compute the same values
   float m_run = -INFINITY, l_run = 0.f;
+  // set when a staged row leaves float16's range: an E8M0 entry with a scale
+  // byte above 140 (its largest codes overflow), or a window value of
+  // magnitude 2^16 or more (or not finite); the query's output is then NaN
+  bool out_of_range = false;
 
   // The window phase runs first: its rows need no ids, so their loads go out
   // with the q rows and the ids; the first entry gather is then issued during
@@ -218,10 +222,14 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int c = task % CHUNKS, s = task / CHUNKS;
     const int64_t sl = c0 + s;
     int blk = (sl < ep1 && sl - tab0 < IDX_CAP) ? s_blk[sl - tab0] : -1;
-    blk = blk < 0 ? 0 : blk;
+    const bool used = blk >= 0;
+    blk = used ? blk : 0;
     r.w = *reinterpret_cast<const uint4*>(cbase + (int64_t)blk * (D / 2) + 16 * c);
     const uint8_t* sp = sbase + (int64_t)blk * SPE + (E4 ? 2 * c : c);
-    r.sc = E4 ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : (uint32_t)sp[0];
+    const uint32_t sb = E4 ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : (uint32_t)sp[0];
+    // an unused slot (masked later) stages row 0 at scale 1, so its scale
+    // byte never raises the range flag
+    r.sc = (E4 || used) ? sb : 127u;
   };
 
   // One homogeneous phase: window tokens (IS_WIN true) or entries, slots
@@ -256,6 +264,18 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       const int c = task % CHUNKS, s = task / CHUNKS;
       v8h h[4];
       if constexpr (IS_WIN) {
+        // largest exponent field of the 32 bfloat16 values (packed halves)
+        typedef unsigned short v2us __attribute__((ext_vector_type(2)));
+        v2us emax = {0, 0};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t wv[4] = {r.w[u].x, r.w[u].y, r.w[u].z, r.w[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            emax = __builtin_elementwise_max(emax,
+                                             __builtin_bit_cast(v2us, wv[e] & 0x7f807f80u));
+        }
+        out_of_range |= (emax[0] >= 0x4780 || emax[1] >= 0x4780);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const uint32_t wd[4] = {r.w[u].x, r.w[u].y, r.w[u].z, r.w[u].w};
@@ -275,6 +295,7 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         h[2] = fp4x8_to_f16(r.w.z, 1.0f) * s1;
         h[3] = fp4x8_to_f16(r.w.w, 1.0f) * s1;
       } else {
+        out_of_range |= r.sc > 140u;
         const float sc = e8m0_to_f32(r.sc);
         h[0] = fp4x8_to_f16(r.w.x, sc);
         h[1] = fp4x8_to_f16(r.w.y, sc);
@@ -496,8 +517,11 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // softmax denominator: the two lanes of a head hold the two halves of the slots
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  // a row outside float16's range anywhere in the workgroup makes the whole
+  // output of the query NaN (a split's NaN partial carries into the merge)
+  const bool bad = __syncthreads_or(out_of_range ? 1 : 0) != 0;
   if (head >= H) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = bad ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
   // output register r of tile ct: channel half (d/2) + 32 ct + 8 (r / 4) + 4 gg + r % 4
   if (nsplit == 1) {
     const int64_t base = ((int64_t)qi * H + head) * D + half * (D / 2) + 4 * gg;
@@ -518,7 +542,8 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
       }
     if (lse && half == 0 && gg == 0)
-      lse[(int64_t)qi * H + head] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+      lse[(int64_t)qi * H + head] =
+          bad ? __builtin_nanf("") : (m_run + log2f(l_tot)) * 0.69314718055994531f;
   } else {
     // normalised partial output in float32, stored in register order
     // [query][split][wave][column tile][r / 4][lane][4], so every store of a
@@ -532,7 +557,8 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
             float4{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
                    O[ct][4 * q4 + 3] * inv};
     if (half == 0 && gg == 0)
-      part_ml[((int64_t)qi * nsplit + split) * H + head] = float2{m_run, l_tot};
+      part_ml[((int64_t)qi * nsplit + split) * H + head] =
+          bad ? float2{__builtin_nanf(""), __builtin_nanf("")} : float2{m_run, l_tot};
   }
 }
 
@@ -693,7 +719,9 @@ static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, flo
   }
 }
 
-static int attn_run(const AttnArgs& a, bool dense) {
+// Host argument checks of attn_run (everything but the workspace); on
+// success *nsel is the number of entry slots per query.
+static int attn_validate(const AttnArgs& a, bool dense, int64_t* nsel_out) {
   if (a.B < 0 || a.T < 0 || a.blk_cap < 0 || a.pos0 < 0) return CSA_ERR_SHAPE;
   if (a.d != 128 && a.d != 256 && a.d != 512) return CSA_ERR_SHAPE;
   if (a.H < 1 || a.H > 64) return CSA_ERR_SHAPE;
@@ -716,6 +744,14 @@ static int attn_run(const AttnArgs& a, bool dense) {
   if (nsel > 0x3fffffff) return CSA_ERR_SHAPE;
   if (!csa_aligned(a.q, 16) || !csa_aligned(a.win, 16) || !csa_aligned(a.out, 16)) return CSA_ERR_ALIGN;
   if (nsel > 0 && !csa_aligned(a.codes, 16)) return CSA_ERR_ALIGN;
+  *nsel_out = nsel;
+  return CSA_OK;
+}
+
+static int attn_run(const AttnArgs& a, bool dense) {
+  int64_t nsel = 0;
+  const int st = attn_validate(a, dense, &nsel);
+  if (st != CSA_OK || a.B == 0 || a.T == 0) return st;
   const AttnPlan p = attn_plan(a.B, a.T, a.H, a.d, nsel + a.W);
   if (((int64_t)a.B * a.T + 7) / 8 * 8 * p.nsplit > 0x7fffffffLL) return CSA_ERR_SHAPE;
   if (p.nsplit > MERGE_MAX) return CSA_ERR_SHAPE;  // the plan keeps it at <= 32

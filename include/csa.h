@@ -308,7 +308,15 @@ int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);
  * of 2, so they stay at most 2); when
  * the slots of a query are split over workgroups (few queries per sequence),
  * the normalised partial outputs are kept in float32 and merged in a fixed
- * order. Workspace: csa_attn_workspace(...) bytes (no initialisation
+ * order. Rows outside float16's range are not attended silently: a query
+ * any of whose staged rows is an E8M0 entry with a scale byte above 140 (a
+ * 32-channel group with amax >= 2^16, whose largest codes overflow float16),
+ * or a window value of magnitude 2^16 or more or not finite, gets NaN in
+ * every head of its output and lse. Entries with scale bytes below 104 (every
+ * value below 2^-21 in magnitude) are staged with float16's reduced subnormal
+ * precision (absolute error below 2^-21 per element); a zero group (byte 0,
+ * zero codes) is exact.
+ * Workspace: csa_attn_workspace(...) bytes (no initialisation
  * needed); it may be NULL when that size is 0.
  * ------------------------------------------------------------------------- */
 int64_t csa_attn_workspace(int B, int T, int H, int d, int64_t n_slots);

@@ -130,3 +130,21 @@ def test_workspace_sizes(L):
     assert L.csa_index_topk_pool_workspace(-1, 1, 8) == -1
     assert L.csa_attn_workspace(1, 8192, 64, 512, 640) == 0
     assert L.csa_attn_workspace(8, 1, 64, 512, 1152) >= 8 * 9 * 64 * 512 * 4
+
+
+def test_prepare_keeps_marshalled_tensors_alive():
+    """prepare() holds every tensor whose address it marshalled, so a replay
+    never reaches freed memory (checked with a CPU tensor: no GPU call)."""
+    import gc
+    import weakref
+
+    import torch
+    t = torch.zeros(16)
+    ref = weakref.ref(t)
+    run = csa.prepare(lambda: csa._ptr(t))
+    del t
+    gc.collect()
+    assert ref() is not None and any(k is ref() for k in run.kept_tensors)
+    del run
+    gc.collect()
+    assert ref() is None

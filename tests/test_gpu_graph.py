@@ -156,3 +156,48 @@ def test_prepared_calls_replay():
     for b in range(B):
         ri, _ = O.index_topk(qin[b, 0], wn[b, 0], kn[b], m, t, k)
         assert np.array_equal(ref_i[b, 0].cpu().numpy(), ri)
+
+
+def test_prepared_replay_keeps_buffers_and_workspace_state():
+    """A recording made with no attention workspace keeps its temporary
+    alive; growing the index workspace afterwards, and an eager call at a
+    different B*T on the recorded buffer (whose body then overlaps the
+    recorded layout's head), leave every replay correct: the head is
+    re-cleared for the recorded layout before the recorded index call."""
+    B, L, d, H, m, Hi, Di, k, W = 4, 4 * 6000, 512, 64, 4, 8, 64, 256, 128
+    t = L - 1
+    x = _world(8, B, L, d, H, m, Hi, Di)
+    ws = csa.Workspace(DEV)
+    idx = torch.empty(B, 1, k, device=DEV, dtype=torch.int32)
+    out = torch.empty(B, 1, H, d, device=DEV, dtype=torch.bfloat16)
+
+    def step():
+        csa.index_topk(x["q_idx"], x["w"], x["keys"], m, t, k, idx, workspace=ws)
+        csa.sparse_attn(x["q"], x["codes"], x["scales"], idx, x["win"], W, t, 1.0, out)
+
+    step()
+    torch.cuda.synchronize()
+    ref_i, ref_o = idx.clone(), out.clone()
+    run = csa.prepare(step)
+    buf0 = ws.buf
+    # a longer context grows the workspace (a new buffer)
+    big = _world(9, 3, 4 * 20000, d, H, m, Hi, Di)
+    o_idx = torch.empty(3, 1, k, device=DEV, dtype=torch.int32)
+    csa.index_topk(big["q_idx"], big["w"], big["keys"], m, 4 * 20000 - 1, k, o_idx, workspace=ws)
+    assert ws.buf is not buf0
+    # allocations that could reuse freed memory, then replays
+    junk = [torch.full((1 << 20,), 7, device=DEV, dtype=torch.int32) for _ in range(8)]
+    one = csa.Workspace(DEV)
+    one.buf = buf0
+    i1 = torch.empty(1, 1, k, device=DEV, dtype=torch.int32)
+    for r in range(3):
+        idx.fill_(-3)
+        out.fill_(5)
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_i) and torch.equal(out, ref_o), r
+        # an eager call of one sequence (B*T = 1) on the recorded buffer
+        csa.index_topk(x["q_idx"][:1].contiguous(), x["w"][:1].contiguous(),
+                       x["keys"][:1].contiguous(), m, t - 3 * r, k, i1, workspace=one)
+        assert one.buf is buf0
+    del junk

@@ -491,3 +491,85 @@ def test_determinism_and_batch_invariance():
         i1, o1 = run(slice(b, b + 1))
         assert torch.equal(i1[0], i_all[b])
         assert torch.equal(o1[0].view(torch.int16), o_all[b].view(torch.int16))
+
+
+# ------------------------------------------- output rounding, row range ----
+
+def test_bf16_output_is_rne_of_f32():
+    """The bfloat16 output is the round-to-nearest-even of the float32 output
+    of the same inputs, bit for bit (the bound on attention error applies to
+    the error beyond that final rounding): split decode queries (merge path),
+    whole-query workgroups and the dense call."""
+    say("bf16 == RNE(f32)")
+    B, L, d, m, H, W = 3, 4 * 1500, 512, 4, 64, 128
+    for T in (1, 20):
+        wd = _attn_world(B, L, d, m, 256, seed=40 + T, H=H, T=T)
+        g = gen(41, "rne", T)
+        pos0 = L - T
+        k = 384
+        idx = torch.stack([torch.randperm((pos0 + 1) // m, generator=g, device=DEV)[:k]
+                           for _ in range(B * T)]).reshape(B, T, k).to(torch.int32).contiguous()
+        for dense in (False, True):
+            o32 = torch.empty(B, T, H, d, device=DEV, dtype=torch.float32)
+            o16 = torch.empty(B, T, H, d, device=DEV, dtype=torch.bfloat16)
+            for o in (o32, o16):
+                if dense:
+                    csa.hca_dense_attn(wd["q"], wd["codes"], wd["scales"], m, wd["win"], W, pos0,
+                                       1.0, o)
+                else:
+                    csa.sparse_attn(wd["q"], wd["codes"], wd["scales"], idx, wd["win"], W, pos0,
+                                    1.0, o)
+            torch.cuda.synchronize()
+            assert torch.isfinite(o32).all()
+            rne = o32.to(torch.bfloat16)   # torch's float32 -> bfloat16 is round-to-nearest-even
+            assert torch.equal(o16.view(torch.int16), rne.view(torch.int16)), (T, dense)
+
+
+def test_rows_outside_float16_range():
+    """A selected E8M0 entry with a scale byte above 140, or a window value of
+    2^16 or more, makes that query's output and lse NaN in every head and
+    leaves the other queries untouched; scale bytes below 104 stay within
+    the error bound (their values are below 2^-21)."""
+    say("rows outside float16 range")
+    B, L, d, m, H, W, k = 3, 4 * 1000, 512, 4, 64, 128, 64
+    wd = _attn_world(B, L, d, m, 256, seed=45, H=H, T=1)
+    g = gen(46, "range")
+    idx = torch.stack([torch.randperm(L // m, generator=g, device=DEV)[:k]
+                       for _ in range(B)]).reshape(B, 1, k).to(torch.int32).contiguous()
+    codes, scales, win = wd["codes"].clone(), wd["scales"].clone(), wd["win"].clone()
+    # sequence 0: one selected entry's first group at scale byte 141 (codes of
+    # magnitude 6 there overflow float16)
+    e0 = int(idx[0, 0, 5])
+    scales[0, e0, 0] = 141
+    codes[0, e0, 0] = 0x77
+    # sequence 1: one selected entry entirely at scale byte 100 (tiny values)
+    e1 = int(idx[1, 0, 9])
+    scales[1, e1, :] = 100
+    # sequence 2: untouched. Then the same with a huge window value in sequence 2.
+    wd1 = dict(wd, codes=codes, scales=scales)
+    for od in (torch.float32, torch.bfloat16):
+        out = torch.empty(B, 1, H, d, device=DEV, dtype=od)
+        lse = torch.empty(B, 1, H, device=DEV, dtype=torch.float32)
+        csa.sparse_attn(wd["q"], codes, scales, idx, wd["win"], W, L - 1, 1.0, out, lse)
+        torch.cuda.synchronize()
+        assert torch.isnan(out[0].float()).all() and torch.isnan(lse[0]).all()
+        assert torch.isfinite(out[1:].float()).all() and torch.isfinite(lse[1:]).all()
+        # sequences 1 and 2 against the oracle (exact dequantisation of every byte)
+        sub = dict(q=wd["q"][1:], codes=codes[1:], scales=scales[1:], win=wd["win"][1:])
+        _check_attn(sub, idx[1:], L - 1, W, out[1:], lse[1:])
+    # window value of 2^16 in sequence 2 (its ring slot of position L - 3)
+    win[2, (L - 3) % win.shape[1], 17] = 65536.0
+    out = torch.empty(B, 1, H, d, device=DEV, dtype=torch.float32)
+    lse = torch.empty(B, 1, H, device=DEV, dtype=torch.float32)
+    csa.sparse_attn(wd["q"], wd["codes"], wd["scales"], idx, win, W, L - 1, 1.0, out, lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[2]).all() and torch.isnan(lse[2]).all()
+    assert torch.isfinite(out[:2]).all()
+    # whole-query workgroups (20 queries per sequence) take the same rule
+    wd20 = _attn_world(1, L, d, m, 256, seed=47, H=H, T=20)
+    sc20 = wd20["scales"].clone()
+    sc20[0, 3, 1] = 200
+    out = torch.empty(1, 20, H, d, device=DEV, dtype=torch.float32)
+    csa.hca_dense_attn(wd20["q"], wd20["codes"], sc20, m, wd20["win"], W, L - 20, 1.0, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()   # entry 3 is visible to every one of the 20 queries
