@@ -21,7 +21,7 @@ __all__ = [
     "workspace_clear",
     "sparse_attn",
     "hca_dense_attn", "attn_workspace", "Workspace", "BF16", "F32", "F16", "EXPORTED",
-    "prepare",
+    "prepare", "sparse_attn_noalloc", "NOALLOC_SCRATCH_MAX",
 ]
 
 BF16, F32, F16 = 0, 1, 2
@@ -40,7 +40,10 @@ EXPORTED = [
     "csa_index_topk_ragged", "csa_index_scan_ragged", "csa_index_select_ragged",
     "csa_sparse_attn_ragged", "hca_dense_attn_ragged",
     "csa_workspace_clear", "csa_attn_workspace", "csa_sparse_attn", "hca_dense_attn",
+    "csa_sparse_attn_noalloc",
 ]
+# bytes of the static device scratch of csa_sparse_attn_noalloc (CSA_NOALLOC_SCRATCH_MAX)
+NOALLOC_SCRATCH_MAX = 64 << 20
 
 
 class CSAError(RuntimeError):
@@ -165,6 +168,8 @@ def lib():
                                     P, I64, I, P]),
             "hca_dense_attn": (I, [P, P, P, I64, I, P, I, I, I, I, I, I, I64, F, P, I, P, P,
                                    I64, I, P]),
+            "csa_sparse_attn_noalloc": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, I64, F, P, I,
+                                            P, I, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -521,3 +526,19 @@ def hca_dense_attn(q, codes, scales, m, win, W, pos0, softmax_scale, out, lse=No
                                 win.shape[1], W, B, T, H, d, pos0, float(softmax_scale),
                                 _ptr(out), dt, _ptr(lse), _ptr(ws), ws_bytes, _fmt_code(fmt),
                                 _stream()), "hca_dense_attn")
+
+
+def sparse_attn_noalloc(q, codes, scales, idx, win, W, pos0, softmax_scale, out, lse=None,
+                        fmt: str = "e8m0"):
+    """sparse_attn without a workspace: the split partials live in the
+    library's static device scratch (csa_sparse_attn_noalloc). Allocates
+    nothing; calls on one GPU must not overlap in time."""
+    B, T, H, d, dt = _attn_common(q, codes, scales, win, out, lse, fmt)
+    _need(idx, torch.int32, "idx", 3)
+    if idx.shape[:2] != (B, T):
+        raise ValueError("idx must be [B][T][k]")
+    _check(lib().csa_sparse_attn_noalloc(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[1],
+                                         _ptr(idx), idx.shape[2], _ptr(win), win.shape[1], W, B, T,
+                                         H, d, int(pos0), float(softmax_scale), _ptr(out), dt,
+                                         _ptr(lse), _fmt_code(fmt), _stream()),
+           "csa_sparse_attn_noalloc")

@@ -11,6 +11,8 @@ extern "C" const char* csa_status_string(int status) {
     case CSA_ERR_DTYPE: return "CSA_ERR_DTYPE: unknown dtype code";
     case CSA_ERR_HIP: return "CSA_ERR_HIP: a HIP launch or runtime call failed";
     case CSA_ERR_ALIGN: return "CSA_ERR_ALIGN: pointer or stride alignment";
+    case CSA_ERR_SCRATCH:
+      return "CSA_ERR_SCRATCH: the call needs more scratch than the static buffer holds";
     default: return "CSA: unknown status";
   }
 }

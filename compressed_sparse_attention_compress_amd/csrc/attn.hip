@@ -27,6 +27,7 @@
 // order.
 #include "csa_internal.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace {
@@ -784,6 +785,30 @@ static int attn_run(const AttnArgs& a, bool dense) {
 
 }  // namespace
 
+// Scratch of csa_sparse_attn_noalloc: the split partials live in this
+// file-scope device array instead of a caller workspace. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in);
+// the device address is looked up once per device with hipGetSymbolAddress
+// and kept.
+constexpr int64_t NOALLOC_SCRATCH_BYTES = (int64_t)CSA_NOALLOC_SCRATCH_MAX;
+__device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device), or null if the lookup failed.
+static void* noalloc_scratch() {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 extern "C" int64_t csa_attn_workspace(int B, int T, int H, int d, int64_t n_slots) {
   if (B < 0 || T < 0 || H < 1 || d < 1 || n_slots < 0) return -1;
   return attn_plan(B, T, H, d, n_slots).ws_bytes;
@@ -842,4 +867,28 @@ extern "C" int hca_dense_attn_ragged(const uint16_t* q, const uint8_t* codes,
   a.pos = pos;
   a.scale_fmt = scale_fmt;
   return attn_run(a, true);
+}
+
+extern "C" int csa_sparse_attn_noalloc(const uint16_t* q, const uint8_t* codes,
+                                       const uint8_t* scales, int64_t blk_cap, const int32_t* idx,
+                                       int k, const uint16_t* win, int Wcap, int W, int B, int T,
+                                       int H, int d, int64_t pos0, float softmax_scale, void* out,
+                                       int out_dtype, float* lse, int scale_fmt,
+                                       hipStream_t stream) {
+  AttnArgs a{q, codes, scales, blk_cap, idx, k, 1, win, Wcap, W, B, T, H, d, pos0,
+             softmax_scale, out, out_dtype, lse, nullptr, 0, stream};
+  a.scale_fmt = scale_fmt;
+  // argument errors first, then the plan's scratch against the static array,
+  // all before the array's address is looked up or anything is launched
+  int64_t nsel = 0;
+  const int st = attn_validate(a, false, &nsel);
+  if (st != CSA_OK || B == 0 || T == 0) return st;
+  const int64_t need = attn_plan(B, T, H, d, nsel + W).ws_bytes;
+  if (need > NOALLOC_SCRATCH_BYTES) return CSA_ERR_SCRATCH;
+  if (need > 0) {
+    a.ws = noalloc_scratch();
+    if (!a.ws) return CSA_ERR_HIP;
+    a.ws_bytes = NOALLOC_SCRATCH_BYTES;
+  }
+  return attn_run(a, false);
 }

@@ -56,8 +56,13 @@ enum csa_status {
   CSA_ERR_WORKSPACE = -4,  /* workspace missing or smaller than required     */
   CSA_ERR_DTYPE = -5,      /* unknown dtype code                             */
   CSA_ERR_HIP = -6,        /* a HIP launch or runtime call failed            */
-  CSA_ERR_ALIGN = -7       /* a pointer or stride breaks the stated alignment */
+  CSA_ERR_ALIGN = -7,      /* a pointer or stride breaks the stated alignment */
+  CSA_ERR_SCRATCH = -8     /* the call needs more scratch than the library's
+                              static buffer holds (csa_sparse_attn_noalloc) */
 };
+
+/* Size of the static device scratch of csa_sparse_attn_noalloc, in bytes. */
+#define CSA_NOALLOC_SCRATCH_MAX (64 << 20)
 
 enum csa_dtype { CSA_BF16 = 0, CSA_F32 = 1, CSA_F16 = 2 };
 
@@ -339,6 +344,28 @@ int hca_dense_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scale
                    int B, int T, int H, int d, int64_t pos0, float softmax_scale,
                    void* out, int out_dtype, float* lse,
                    void* workspace, int64_t ws_bytes, int scale_fmt, hipStream_t stream);
+
+/* csa_sparse_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same call without a workspace argument. The split partials (the only
+ * scratch csa_sparse_attn needs) live in a static device array of
+ * CSA_NOALLOC_SCRATCH_MAX bytes inside the library, one per GPU the library
+ * runs on, held until the process ends; its device address is looked up on
+ * the first call on each device. The call allocates nothing and its results
+ * are bit-identical to csa_sparse_attn's. A call whose launch plan needs more
+ * scratch than the array holds returns CSA_ERR_SCRATCH before launching
+ * (csa_attn_workspace(B, T, H, d, k + W) gives the need; it is 0 for runs of
+ * 16 or more queries per sequence, and e.g. 18.9 MB for 8 decode queries
+ * with k = 1024, d = 512, 64 heads). The scratch needs no initialisation.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or different host threads without ordering)
+ * race on it and give undefined results; order them (one stream) instead. */
+int csa_sparse_attn_noalloc(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                            int64_t blk_cap, const int32_t* idx, int k,
+                            const uint16_t* win, int Wcap, int W,
+                            int B, int T, int H, int d, int64_t pos0, float softmax_scale,
+                            void* out, int out_dtype, float* lse, int scale_fmt,
+                            hipStream_t stream);
 
 /* csa_sparse_attn and hca_dense_attn for sequences at different positions:
  * the queries of sequence b are at pos[b] .. pos[b] + T - 1 (pos: int64 [B]

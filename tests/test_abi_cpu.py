@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert L.csa_status_string(s).startswith(b"CSA")
     assert L.csa_version() >= 100
 
@@ -130,6 +130,35 @@ def test_workspace_sizes(L):
     assert L.csa_index_topk_pool_workspace(-1, 1, 8) == -1
     assert L.csa_attn_workspace(1, 8192, 64, 512, 640) == 0
     assert L.csa_attn_workspace(8, 1, 64, 512, 1152) >= 8 * 9 * 64 * 512 * 4
+
+
+def test_noalloc_scratch_limit(L):
+    """csa_sparse_attn_noalloc refuses, before any HIP call, a plan whose
+    split partials exceed the static scratch; host argument errors come
+    first, as in csa_sparse_attn."""
+    P = ctypes.c_void_p
+    fake = P(256)
+    na = lambda B, T, H, d, k, W, Wcap: (fake, fake, fake, 1 << 20, fake, k, fake, Wcap, W, B, T,
+                                         H, d, 399 + T, ctypes.c_float(1.0), fake, 0, None, 0,
+                                         None)
+    assert L.csa_sparse_attn_noalloc(*na(1, 1, 64, 96, 8, 128, 128)) == -2
+    assert L.csa_sparse_attn_noalloc(*na(1, 1, 65, 512, 8, 128, 128)) == -2
+    assert L.csa_sparse_attn_noalloc(*na(0, 1, 64, 512, 8, 128, 128)) == 0
+    limit = csa.NOALLOC_SCRATCH_MAX
+    over = None
+    for B in (1, 2, 7, 64, 255, 1024, 4096, 65535):
+        for k in (16, 1024, 8192, 65536):
+            if L.csa_attn_workspace(B, 1, 64, 512, k + 128) > limit:
+                over = (B, k)
+                break
+        if over:
+            break
+    if over is not None:
+        B, k = over
+        assert L.csa_sparse_attn_noalloc(*na(B, 1, 64, 512, k, 128, 128)) == -8
+    else:
+        # no decode plan at these shapes needs more than the static scratch
+        assert L.csa_attn_workspace(255, 1, 64, 512, 1024 + 128) <= limit
 
 
 def test_prepare_keeps_marshalled_tensors_alive():
