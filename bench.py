@@ -57,18 +57,18 @@ def log(*a):
 # --------------------------------------------------------------------------
 
 def build_cache(csa, synth, wl, dev, seed, layer, m, L):
-    """Compress L tokens of every sequence into an m-token MXFP4 cache, one
-    8192-token chunk at a time (the cache write path, untimed here)."""
+    """Compress L tokens of every sequence into an m-token MXFP4 cache: one
+    launch per 8192-token chunk covering all B sequences (the cache write
+    path, untimed here)."""
     import torch
     cap = -(-L // m)
     codes = torch.empty(wl.B, cap, wl.d // 2, device=dev, dtype=torch.uint8)
     scales = torch.empty(wl.B, cap, wl.d // SCALE_GROUP[FMT], device=dev, dtype=torch.uint8)
-    for b in range(wl.B):
-        for c in range(-(-L // synth.CHUNK)):
-            kv = synth.latent_chunk(wl, b, c, dev, seed, layer)[None]
-            g = synth.gate_chunk(wl, b, c, dev, seed, layer)[None]
-            csa.compress_quantize(kv, g, c * synth.CHUNK, m, codes[b:b + 1], scales[b:b + 1],
-                                  fmt=FMT)
+    for c in range(-(-L // synth.CHUNK)):
+        kv = torch.stack([synth.latent_chunk(wl, b, c, dev, seed, layer) for b in range(wl.B)])
+        g = torch.stack([synth.gate_chunk(wl, b, c, dev, seed, layer) for b in range(wl.B)])
+        csa.compress_quantize(kv, g, c * synth.CHUNK, m, codes, scales, fmt=FMT)
+        del kv, g
     return codes, scales
 
 
@@ -82,7 +82,8 @@ def decode_set(csa, synth, wl, dev, seed):
     idx = torch.empty(wl.B, 1, wl.k, device=dev, dtype=torch.int32)
     out = torch.empty(wl.B, 1, wl.H, wl.d, device=dev, dtype=torch.bfloat16)
     return dict(codes=codes, scales=scales, keys=keys, q_idx=q_idx, w=w, q=q, win=win, idx=idx,
-                out=out, ws=csa.Workspace(dev), ws_attn=csa.Workspace(dev))
+                out=out, ws=csa.Workspace(dev), ws_attn=csa.Workspace(dev),
+                ws_fused=csa.Workspace(dev))
 
 
 # --------------------------------------------------------------------------
@@ -313,10 +314,15 @@ def run_decode(args, csa, synth, wl, dev):
     def step_fn(i):
         def f():
             s = sets[i]
-            csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
-                           workspace=s["ws"])
-            csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, pos, 1.0,
-                            s["out"], workspace=s["ws_attn"], fmt=FMT)
+            if args.separate:
+                csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
+                               workspace=s["ws"])
+                csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, pos,
+                                1.0, s["out"], workspace=s["ws_attn"], fmt=FMT)
+            else:
+                csa.index_attn(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["q"], s["codes"],
+                               s["scales"], s["win"], wl.W, 1.0, s["idx"], s["out"],
+                               workspace=s["ws_fused"], fmt=FMT)
         return f
 
     eager = [step_fn(i) for i in range(len(sets))]
@@ -362,6 +368,7 @@ def run_decode(args, csa, synth, wl, dev):
             "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8", "top_k": wl.k, "window": wl.W,
             "cache": CACHE_NAME[FMT], "input_sets_rotated": args.sets,
             "timing": timing_name(args),
+            "step": "csa_index_topk + csa_sparse_attn" if args.separate else "csa_index_attn",
         },
         "step_hbm": {"algorithmic_bytes_per_query": per_q["total"],
                      "GB/s": round(step_gbs, 1), "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
@@ -533,6 +540,7 @@ def run_decode_ragged(args, csa, synth, wl, dev):
             "heads": wl.H, "indexer": f"{wl.Hi}x{wl.Di} int8", "top_k": wl.k, "window": wl.W,
             "cache": CACHE_NAME[FMT], "input_sets_rotated": args.sets,
             "timing": timing_name(args),
+            "step": "csa_index_topk + csa_sparse_attn" if args.separate else "csa_index_attn",
         },
         "append_us": round(t_append * 1e3, 2),
         "roofline": {
@@ -1013,6 +1021,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--python-launch", action="store_true",
                     help="time the Python wrappers instead of pre-marshalled calls")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode: time csa_index_topk + csa_sparse_attn as two calls instead of "
+                         "the one-call csa_index_attn")
     ap.add_argument("--graph", action="store_true",
                     help="time HIP graph replays instead of eager launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

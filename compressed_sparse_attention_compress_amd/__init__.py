@@ -21,7 +21,7 @@ __all__ = [
     "workspace_clear",
     "sparse_attn",
     "hca_dense_attn", "attn_workspace", "Workspace", "BF16", "F32", "F16", "EXPORTED",
-    "prepare", "sparse_attn_noalloc", "NOALLOC_SCRATCH_MAX",
+    "prepare", "sparse_attn_noalloc", "NOALLOC_SCRATCH_MAX", "index_attn", "index_attn_workspace",
 ]
 
 BF16, F32, F16 = 0, 1, 2
@@ -40,7 +40,7 @@ EXPORTED = [
     "csa_index_topk_ragged", "csa_index_scan_ragged", "csa_index_select_ragged",
     "csa_sparse_attn_ragged", "hca_dense_attn_ragged",
     "csa_workspace_clear", "csa_attn_workspace", "csa_sparse_attn", "hca_dense_attn",
-    "csa_sparse_attn_noalloc",
+    "csa_sparse_attn_noalloc", "csa_index_attn_workspace", "csa_index_attn",
 ]
 # bytes of the static device scratch of csa_sparse_attn_noalloc (CSA_NOALLOC_SCRATCH_MAX)
 NOALLOC_SCRATCH_MAX = 64 << 20
@@ -170,6 +170,9 @@ def lib():
                                    I64, I, P]),
             "csa_sparse_attn_noalloc": (I, [P, P, P, I64, P, I, P, I, I, I, I, I, I, I64, F, P, I,
                                             P, I, P]),
+            "csa_index_attn_workspace": (I64, [I, I, I64, I, I, I, I]),
+            "csa_index_attn": (I, [P, P, P, I64, I, I, I, I, I, I64, P, P, I, I, P, P, P, P, I, I,
+                                   I, I, F, P, P, P, I, P, P, I64, I, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -542,3 +545,53 @@ def sparse_attn_noalloc(q, codes, scales, idx, win, W, pos0, softmax_scale, out,
                                          H, d, int(pos0), float(softmax_scale), _ptr(out), dt,
                                          _ptr(lse), _fmt_code(fmt), _stream()),
            "csa_sparse_attn_noalloc")
+
+
+def index_attn_workspace(B, T, n_max, k, H, d, W) -> int:
+    return lib().csa_index_attn_workspace(B, T, n_max, k, H, d, W)
+
+
+def index_attn(q_idx, w, keys, m, pos0, k, q, codes, scales, win, W, softmax_scale, out_idx, out,
+               out_score=None, lse=None, cand=None, workspace=None, pos_max=None,
+               fmt: str = "e8m0"):
+    """Indexer top-k + sparse attention of one layer in one call; see
+    csa_index_attn in include/csa.h. Same arguments as index_topk followed
+    by those of sparse_attn (keys and the FP4 cache share blk_cap). pos0 may
+    be an int64 [B] tensor of per-sequence positions bounded by pos_max.
+    workspace: a Workspace (kept per B*T as for index_topk) or a raw uint8
+    tensor the caller keeps cleared."""
+    _need(q_idx, torch.int8, "q_idx", 4)
+    _need(w, torch.int8, "w", 3)
+    _need(keys, torch.int8, "keys", 3)
+    _need(out_idx, torch.int32, "out_idx", 3)
+    _need(out_score, torch.int32, "out_score", 3)
+    _need(cand, torch.int32, "cand", 3)
+    B, T, Hi, Di = q_idx.shape
+    Bq, Tq, H, d, dt = _attn_common(q, codes, scales, win, out, lse, fmt)
+    if (Bq, Tq) != (B, T):
+        raise ValueError("index_attn: q and q_idx disagree on [B][T]")
+    pos0, pos = _positions(pos0, pos_max, B, q_idx.device, "index_attn")
+    if w.shape != (B, T, Hi) or keys.shape[0] != B or keys.shape[2] != Di:
+        raise ValueError("index_attn: inconsistent indexer shapes")
+    if keys.shape[1] != codes.shape[1]:
+        raise ValueError("index_attn: keys and codes must share blk_cap")
+    if out_idx.shape != (B, T, k) or (out_score is not None and out_score.shape != (B, T, k)):
+        raise ValueError("index_attn: out_idx / out_score must be [B][T][k]")
+    C = 0
+    if cand is not None:
+        if cand.shape[:2] != (B, T):
+            raise ValueError("index_attn: cand must be [B][T][C]")
+        C = cand.shape[2]
+    blk_cap = keys.shape[1]
+    n_max = C if cand is not None else min(blk_cap, (pos0 + T) // m)
+    need = index_attn_workspace(B, T, n_max, k, H, d, W)
+    if workspace is None:
+        workspace = _default_ws(q_idx.device)
+    ws = workspace.get(need, key=B * T) if isinstance(workspace, Workspace) else workspace
+    ws_bytes = 0 if ws is None else ws.numel()
+    _note_head(workspace, ws, B * T)
+    _check(lib().csa_index_attn(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di, m, pos0,
+                                _ptr(pos), _ptr(cand), C, k, _ptr(q), _ptr(codes), _ptr(scales),
+                                _ptr(win), win.shape[1], W, H, d, float(softmax_scale),
+                                _ptr(out_idx), _ptr(out_score), _ptr(out), dt, _ptr(lse),
+                                _ptr(ws), ws_bytes, _fmt_code(fmt), _stream()), "csa_index_attn")

@@ -26,11 +26,15 @@
 // workgroups (decode); their partial (o, max, sum) are merged in a fixed
 // order.
 #include "csa_internal.h"
+#include "topk_device.h"
 
 #include <mutex>
 #include <type_traits>
 
 namespace {
+
+using csa_topk::FinalPlan;
+using csa_topk::NB1;
 
 constexpr int CH = 64;        // slots per staging pass (two 32-slot halves)
 constexpr int IDX_CAP = 1024; // entry block ids cached in LDS per refill
@@ -59,17 +63,41 @@ __device__ inline _Float16 bf16_to_f16(uint32_t bits) {
   return (_Float16)__uint_as_float(bits << 16);
 }
 
+// Where the entry ids of a query come from: SEL_IDX, an id list the caller
+// gives (csa_sparse_attn); SEL_LISTS, the indexer scan's short per-unit
+// lists, resolved to the top-k by every workgroup for its own slots
+// (lists_select, whose slow path walks the score row); SEL_ROW, the
+// indexer's whole score row of a query with few candidates (pick_select).
+// With a selection in the kernel, each workgroup writes the out_idx /
+// out_score positions of its own slots.
+enum { SEL_IDX = 0, SEL_LISTS = 1, SEL_ROW = 2 };
+
+struct SelArgs {
+  uint32_t* hist;         // [queries][NB1] score histograms (cleared after use)
+  const int2* tinfo;      // [queries][units] (count, cut bin) of the lists (SEL_LISTS)
+  const int2* comp;       // [queries][units][lcap] listed (score, entry) (SEL_LISTS)
+  const int32_t* slab;    // [queries][npad] scores
+  int64_t npad;
+  csa_topk::ListsPlan lp; // units, log2 of the list length (SEL_LISTS)
+  const int32_t* cand;    // [queries][C] pool, or null
+  int C, m_idx;           // pool size; block size of the indexed cache
+  int32_t* out_idx;       // [queries][k]
+  int32_t* out_score;     // [queries][k] or null
+};
+
+
 // One workgroup per compute unit is all the LDS allows at d = 512, so the
 // compiler is told to schedule for one wave per SIMD (registers for LDS
 // reads in flight rather than for occupancy).
-template <int D, int NG, bool DENSE, int FMT, bool WF>
+template <int D, int NG, bool DENSE, int FMT, bool WF, int SEL>
 __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t blk_cap, const int32_t* __restrict__ idx, int k,
     int m, const uint16_t* __restrict__ win, int Wcap, int W, int T, int H, int64_t pos0,
     const int64_t* __restrict__ qpos, float scale_log2, int nsplit, int spl, int n_queries,
     void* __restrict__ out, int out_dtype,
-    float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    SelArgs sa) {
   constexpr int NWV = 2 * NG;                 // waves: (head group, half)
   constexpr int NT = NWV * 64;
   constexpr int RS = row_stride<D>();
@@ -81,12 +109,17 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   static_assert(TASKS % NT == 0, "tasks must divide evenly");
   constexpr bool E4 = FMT == CSA_SCALE_E4M3_16;
   constexpr int SPE = E4 ? D / 16 : D / 32;   // scale bytes per entry
-  __shared__ __attribute__((aligned(16))) _Float16 Rs[CH * RS];
+  static_assert(SEL == SEL_IDX || NT == 256, "the in-kernel selection needs 256 threads");
+  // the stage (rows of a pass) and each wave's partial logits of both 32-slot
+  // tiles, in register order (a plain vector type: the HIP float4 struct was
+  // read back as single dwords, four bank-conflicted reads per value instead
+  // of one)
+  constexpr int STAGE_BYTES = CH * RS * 2;
+  constexpr int LOGIT_BYTES = NWV * 2 * 4 * 64 * 16;
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[STAGE_BYTES + LOGIT_BYTES];
+  _Float16* const Rs = reinterpret_cast<_Float16*>(s_raw);
+  v4f (*const s_S)[2][4][64] = reinterpret_cast<v4f (*)[2][4][64]>(s_raw + STAGE_BYTES);
   __shared__ int s_blk[IDX_CAP];
-  // each wave's partial logits of both 32-slot tiles, in register order
-  // (a plain vector type: the HIP float4 struct was read back as single
-  // dwords, four bank-conflicted reads per value instead of one)
-  __shared__ __attribute__((aligned(16))) v4f s_S[NWV][2][4][64];
   __shared__ unsigned long long s_valid;      // entry slots of the staged pass that are valid
 
   // Workgroups are dealt to the 8 XCDs round-robin by id; all splits of a
@@ -113,7 +146,7 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int i32 = lane & 31, gg = lane >> 5;
   const int head = hg * 32 + i32;
 
-  const int32_t* ibase = DENSE ? nullptr : idx + (int64_t)qi * k;
+  const int32_t* ibase = (DENSE || SEL != SEL_IDX) ? nullptr : idx + (int64_t)qi * k;
   // entry ids of the first table (slots [s_begin, s_begin + IDX_CAP) of the
   // entry range), requested before the q rows so that both latencies overlap
   constexpr int RPT = (IDX_CAP + NT - 1) / NT;
@@ -122,7 +155,9 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const int64_t sl = s_begin + threadIdx.x + r * NT;
-    first_ids[r] = (DENSE || s_begin >= e_end) ? sl : (int64_t)ibase[sl < e_end ? sl : e_end - 1];
+    first_ids[r] = (DENSE || SEL != SEL_IDX || s_begin >= e_end)
+                       ? sl
+                       : (int64_t)ibase[sl < e_end ? sl : e_end - 1];
   }
   // q.k operand: the two waves of a head group split d; lane (i + 32 gg) of
   // wave half h holds head i's channels h d/2 + 16 kk + 8 gg .. +7 of every
@@ -157,6 +192,16 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   RawE eraw[TPT];          // raw bytes of the next entry pass to be staged
   bool eraw_ok = false;    // eraw holds the entry phase's first pass
   RawW wpre[NPRE];  // the first window tasks, requested with the q rows
+  bool sel_done = false;   // the in-kernel selection put this range's ids in s_blk
+  // an in-kernel selection's loads go out first, before the q rows
+  csa_topk::ListsLoad sel_ld;
+  if constexpr (SEL == SEL_LISTS) {
+    if (ep0 < ep1) {
+      const int64_t nu = sa.lp.units;
+      sel_ld.load(sa.hist + (int64_t)qi * NB1, sa.tinfo + qi * nu,
+                  sa.comp + ((qi * nu) << sa.lp.lshift), sa.lp);
+    }
+  }
   {
     const int hq = head < H ? head : H - 1;
     const uint16_t* qr = q + ((int64_t)qi * H + hq) * D + half * (D / 2) + 8 * gg;
@@ -185,6 +230,59 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         eraw_ok = true;
       }
     }
+    if constexpr (SEL != SEL_IDX) {
+      // the query's top-k, resolved here (its loads go out with the q rows);
+      // this workgroup keeps the ids of its own entry slots [ep0, ep1) and
+      // writes those positions of out_idx / out_score
+      if (ep0 < ep1) {
+        const uint32_t* hq = sa.hist + (int64_t)qi * NB1;
+        const int32_t* cq = sa.cand ? sa.cand + (int64_t)qi * sa.C : nullptr;
+        int32_t* oi = sa.out_idx + (int64_t)qi * k;
+        int32_t* os = sa.out_score ? sa.out_score + (int64_t)qi * k : nullptr;
+        __shared__ uint32_t sel_bh[256];
+        __shared__ int sel_tmp[4];
+        __shared__ int sel_red[8];
+        auto emit = [&](int pos, int e, int v) {
+          if (pos >= ep0 && pos < ep1) {
+            int id = cq ? cq[e] : e;
+            id = (id >= 0 && id < blk_cap) ? id : -1;
+            s_blk[pos - ep0] = id;
+            oi[pos] = id;
+            if (os) os[pos] = v;
+          }
+        };
+        int keff;
+        int64_t nv = (t + 1) / sa.m_idx;
+        nv = nv < blk_cap ? nv : blk_cap;
+        const csa_topk::SelShared sh{nullptr, nullptr, sel_bh, sel_tmp, sel_red};
+        if constexpr (SEL == SEL_LISTS) {
+          keff = sel_ld.resolve(sa.slab + (int64_t)qi * sa.npad, (int)nv, k, sa.lp, sh, emit);
+        } else {
+          const int N = cq ? sa.C : (int)nv;
+          if (N <= csa_topk::PICK_MAX / 2)
+            keff = csa_topk::pick_select<csa_topk::PICK_MAX / 512>(
+                sa.slab + (int64_t)qi * sa.npad, hq, N, k, sh, emit);
+          else
+            keff = csa_topk::pick_select<csa_topk::PICK_MAX / 256>(
+                sa.slab + (int64_t)qi * sa.npad, hq, N, k, sh, emit);
+        }
+        for (int64_t pos = (keff > ep0 ? keff : ep0) + threadIdx.x; pos < ep1; pos += NT) {
+          s_blk[pos - ep0] = -1;
+          oi[pos] = -1;
+          if (os) os[pos] = -1;
+        }
+        // the ids are in place and the selection's LDS is free for the stage;
+        // a workgroup that is the query's only reader of its histogram clears
+        // it for the next call (otherwise the merge does)
+        __syncthreads();
+        if (nsplit == 1) {
+          uint32_t* hw = sa.hist + (int64_t)qi * NB1;
+          hw[NB1 - 1 - 2 * (int)threadIdx.x] = 0u;
+          hw[NB1 - 2 - 2 * (int)threadIdx.x] = 0u;
+        }
+        sel_done = true;
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < KS2; ++kk)
 #pragma unroll
@@ -206,7 +304,7 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   // with the q rows and the ids; the first entry gather is then issued during
   // the window passes (its ids are in LDS by then) and converted when the
   // entry phase starts.
-  bool ids_stored = false; // s_blk holds the entry phase's first table
+  bool ids_stored = sel_done; // s_blk holds the entry phase's first table
   // entry ids of slots [from, from + IDX_CAP) into LDS
   auto store_ids = [&](int64_t from, const int64_t* v) {
 #pragma unroll
@@ -502,7 +600,7 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
       if (c0 + CH < p1) {
         __syncthreads();  // every read of this pass's rows is done
-        if (!IS_WIN && c0 + 2 * CH > tab0 + IDX_CAP) refill(c0 + CH);
+        if (!IS_WIN && SEL == SEL_IDX && c0 + 2 * CH > tab0 + IDX_CAP) refill(c0 + CH);
         stage(c0 + CH, std::false_type{});
       }
     }
@@ -578,7 +676,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
                                                     const float2* __restrict__ part_ml,
                                                     int nsplit, int H, int NG, int n_queries,
                                                     void* __restrict__ out, int out_dtype,
-                                                    float* __restrict__ lse) {
+                                                    float* __restrict__ lse,
+                                                    uint32_t* __restrict__ hist_clear) {
   constexpr int CT = D / 64;      // tiles per wave (half of d)
   constexpr int TILES = D / 32;   // tiles of a head group
   // Workgroups are dealt to the XCDs round-robin; every workgroup of query qi
@@ -590,6 +689,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   const int64_t qi = xcd + 8 * (int64_t)(jx / per_q);
   if (qi >= n_queries) return;
   const int rr = jx % per_q;
+  // an in-kernel selection read the query's indexer histogram in every split:
+  // the first merge workgroup of the query clears it for the next call
+  if (hist_clear && rr == 0) {
+    uint32_t* hq = hist_clear + qi * NB1;
+    hq[NB1 - 1 - 2 * (int)threadIdx.x] = 0u;
+    hq[NB1 - 2 - 2 * (int)threadIdx.x] = 0u;
+  }
   const int tile = rr % TILES, hg = rr / TILES;
   const int hf = tile / CT, ct = tile % CT;
   const int wave = 2 * hg + hf;
@@ -644,15 +750,22 @@ struct AttnPlan {
 };
 
 // Decode (T < 16): the slots of a query are split over workgroups in whole
-// 64-slot passes, at most ~32 per query (>= n/16 slots for very long dense
-// ranges, where the partials would otherwise dominate), and no more than it
-// takes to give every compute unit one workgroup: with many queries each
-// workgroup takes more passes instead, which keeps the partial outputs (128
-// KiB per workgroup at 64 heads x 512) small. A sequence's output is
-// therefore the same in any batch of up to 256 / (most splits) queries.
-// Longer query runs take one workgroup per query.
-static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots) {
+// 64-slot passes, at most ~32 splits per query (~16 for very long dense
+// ranges, >= n/16 slots each, where the partials would otherwise dominate).
+// The plan depends on the query's slot count only, never on the batch: a
+// sequence's output bits are the same in any batch ("batch invariant
+// kernels"). Longer query runs take one workgroup per query. two_groups:
+// the kernel runs both 32-head groups whatever H is (in-kernel selection),
+// so the partials hold 64 heads. alg_bytes > 0 (the fused call, which knows
+// the query's whole algorithmic traffic): the splits are also capped so that
+// their partials, written and read back, cost about the query's own
+// algorithmic HBM bytes at most (rounded up to a whole split: a 1M-token
+// query may split into 1-pass ranges; a 32K-token query keeps a few
+// multi-pass ranges).
+static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots, bool two_groups = false,
+                          int64_t alg_bytes = 0) {
   AttnPlan p;
+  const int64_t hpad = two_groups ? 64 : 32 * ((H + 31) / 32);
   if (T >= 16 || n_slots <= CH) {
     p.nsplit = 1;
     p.spl = (int)(((n_slots + CH - 1) / CH) * CH);
@@ -660,18 +773,19 @@ static AttnPlan attn_plan(int B, int T, int H, int d, int64_t n_slots) {
   } else {
     const int64_t div = n_slots > 4096 ? 16 : 32;
     int64_t spl = ((n_slots + div - 1) / div + CH - 1) / CH * CH;
-    const int64_t most = (n_slots + spl - 1) / spl;
-    const int64_t nq = (int64_t)B * T;
-    const int64_t fill = nq > 0 ? (256 + nq - 1) / nq : most;
-    const int64_t ns = most < fill ? most : fill;
-    spl = ((n_slots + ns - 1) / ns + CH - 1) / CH * CH;
+    if (alg_bytes > 0) {
+      const int64_t prt = 2 * hpad * d * 4;  // a split's partial, written and read back
+      int64_t cap = (alg_bytes + prt - 1) / prt;
+      cap = cap < 1 ? 1 : cap;
+      const int64_t spl_cap = ((n_slots + cap - 1) / cap + CH - 1) / CH * CH;
+      spl = spl > spl_cap ? spl : spl_cap;
+    }
     p.spl = (int)spl;
     p.nsplit = (int)((n_slots + spl - 1) / spl);
   }
   p.ws_bytes = 0;
   if (p.nsplit > 1) {
     const int64_t units = (int64_t)B * T * p.nsplit;
-    const int64_t hpad = 32 * ((H + 31) / 32);
     p.ws_bytes = ((units * hpad * d * 4 + 255) / 256) * 256 + units * H * 8;
   }
   return p;
@@ -684,23 +798,37 @@ struct AttnArgs {
   int64_t ws_bytes; hipStream_t stream;
   const int64_t* pos = nullptr;  // per-sequence first positions (pos0 = their bound) or null
   int scale_fmt = CSA_SCALE_E8M0_32;
+  int sel = SEL_IDX;             // where the entry ids come from
+  SelArgs sa{};                  // the indexer's results, for an in-kernel selection
+  int64_t alg_bytes = 0;         // per-query algorithmic bytes (fused call), for the plan
 };
 
 template <int D, bool DENSE, int FMT>
 static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, float2* part_ml) {
-  const int ng = (a.H + 31) / 32;
+  // an in-kernel selection runs in 256 threads (two head groups)
+  const int ng = a.sel != SEL_IDX ? 2 : (a.H + 31) / 32;
   const int64_t nq = (int64_t)a.B * a.T;
   const dim3 grid((unsigned)(((nq + 7) / 8) * 8 * p.nsplit));
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
-#define CSA_LAUNCH_ATTN(NG, WF)                                                              \
-  hipLaunchKernelGGL((k_attn<D, NG, DENSE, FMT, WF>), grid, dim3(NG * 128), 0, a.stream, a.q,   \
-                     a.codes, a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, a.H, \
-                     a.pos0, a.pos, sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse,   \
-                     part_o, part_ml)
+#define CSA_LAUNCH_ATTN_S(NG, WF, SS)                                                         \
+  hipLaunchKernelGGL((k_attn<D, NG, DENSE, FMT, WF, SS>), grid, dim3(NG * 128), 0, a.stream,     \
+                     a.q, a.codes, a.scales, a.blk_cap, a.idx, a.k, a.m, a.win, a.Wcap, a.W, a.T, \
+                     a.H, a.pos0, a.pos, sl2, p.nsplit, p.spl, (int)nq, a.out, a.out_dtype, a.lse, \
+                     part_o, part_ml, a.sa)
+#define CSA_LAUNCH_ATTN(NG, WF) CSA_LAUNCH_ATTN_S(NG, WF, SEL_IDX)
   // a workgroup that takes a whole query (runs of queries) stages the window
   // first so that its start-up loads overlap; split queries keep the entries
   // first (measured faster there)
-  if (p.nsplit == 1) {
+  if constexpr (!DENSE) {
+    if (a.sel == SEL_LISTS) {
+      CSA_LAUNCH_ATTN_S(2, false, SEL_LISTS);
+    } else if (a.sel == SEL_ROW) {
+      CSA_LAUNCH_ATTN_S(2, false, SEL_ROW);
+    }
+  }
+  if (a.sel != SEL_IDX) {
+    // launched above
+  } else if (p.nsplit == 1) {
     if (ng == 1) CSA_LAUNCH_ATTN(1, true);
     else CSA_LAUNCH_ATTN(2, true);
   } else {
@@ -708,11 +836,13 @@ static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, flo
     else CSA_LAUNCH_ATTN(2, false);
   }
 #undef CSA_LAUNCH_ATTN
+#undef CSA_LAUNCH_ATTN_S
   if (p.nsplit > 1) {
     const dim3 mgrid((unsigned)(((nq + 7) / 8) * 8 * ng * (D / 32)));
 #define CSA_LAUNCH_MERGE(NS)                                                                 \
   hipLaunchKernelGGL((k_attn_merge<D, NS>), mgrid, dim3(256), 0, a.stream, part_o, part_ml, \
-                     p.nsplit, a.H, ng, (int)nq, a.out, a.out_dtype, a.lse)
+                     p.nsplit, a.H, ng, (int)nq, a.out, a.out_dtype, a.lse,                 \
+                     a.sel != SEL_IDX ? a.sa.hist : nullptr)
     if (p.nsplit <= 8) CSA_LAUNCH_MERGE(8);
     else if (p.nsplit <= 16) CSA_LAUNCH_MERGE(16);
     else CSA_LAUNCH_MERGE(MERGE_MAX);
@@ -753,7 +883,8 @@ static int attn_run(const AttnArgs& a, bool dense) {
   int64_t nsel = 0;
   const int st = attn_validate(a, dense, &nsel);
   if (st != CSA_OK || a.B == 0 || a.T == 0) return st;
-  const AttnPlan p = attn_plan(a.B, a.T, a.H, a.d, nsel + a.W);
+  const bool two = a.sel != SEL_IDX;
+  const AttnPlan p = attn_plan(a.B, a.T, a.H, a.d, nsel + a.W, two, a.alg_bytes);
   if (((int64_t)a.B * a.T + 7) / 8 * 8 * p.nsplit > 0x7fffffffLL) return CSA_ERR_SHAPE;
   if (p.nsplit > MERGE_MAX) return CSA_ERR_SHAPE;  // the plan keeps it at <= 32
   float* part_o = nullptr;
@@ -762,7 +893,7 @@ static int attn_run(const AttnArgs& a, bool dense) {
     if (!a.ws || a.ws_bytes < p.ws_bytes) return CSA_ERR_WORKSPACE;
     if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
     const int64_t units = (int64_t)a.B * a.T * p.nsplit;
-    const int64_t hpad = 32 * ((a.H + 31) / 32);
+    const int64_t hpad = two ? 64 : 32 * ((a.H + 31) / 32);
     part_o = reinterpret_cast<float*>(a.ws);
     part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a.ws) +
                                         ((units * hpad * a.d * 4 + 255) / 256) * 256);
@@ -784,6 +915,42 @@ static int attn_run(const AttnArgs& a, bool dense) {
 }
 
 }  // namespace
+
+namespace csa_topk {
+
+// The attention half of csa_index_attn: every workgroup resolves its query's
+// top-k from the indexer results in the workspace, then attends.
+static AttnArgs fused_args(const FusedAttn& f) {
+  // (idx: the call's out_idx, which the kernels write rather than read)
+  AttnArgs a{f.q, f.codes, f.scales, f.blk_cap, f.out_idx, f.k, 1, f.win, f.Wcap, f.W, f.B, f.T,
+             f.H, f.d, f.pos0, f.softmax_scale, f.out, f.out_dtype, f.lse, f.ws, f.ws_bytes,
+             f.stream};
+  a.pos = f.pos;
+  a.scale_fmt = f.scale_fmt;
+  a.sel = f.sel;
+  a.sa = SelArgs{f.hist, f.tinfo, f.comp, f.slab, f.npad, f.lp, f.cand, f.C, f.m_idx,
+                 f.out_idx, f.out_score};
+  a.alg_bytes = f.alg_bytes;
+  return a;
+}
+
+int64_t fused_attn_workspace(int B, int T, int H, int d, int64_t n_slots, int64_t alg_bytes) {
+  return attn_plan(B, T, H, d, n_slots, true, alg_bytes).ws_bytes;
+}
+
+bool fused_attn_fits(int T, int64_t n_slots) {
+  // one id table per workgroup (IDX_CAP slots) and at most MERGE_MAX splits
+  return T < 16 && n_slots <= (int64_t)IDX_CAP * MERGE_MAX;
+}
+
+int fused_attn_check(const FusedAttn& f) {
+  int64_t nsel = 0;
+  return attn_validate(fused_args(f), false, &nsel);
+}
+
+int fused_attn_launch(const FusedAttn& f) { return attn_run(fused_args(f), false); }
+
+}  // namespace csa_topk
 
 // Scratch of csa_sparse_attn_noalloc: the split partials live in this
 // file-scope device array instead of a caller workspace. Host code never

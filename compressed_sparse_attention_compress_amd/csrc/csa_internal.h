@@ -35,6 +35,41 @@ __device__ inline int64_t query_base(const int64_t* pos, int64_t pos0, int b) {
   return p < 0 ? 0 : (p > pos0 ? pos0 : p);
 }
 
+// Cross-lane moves within a wave by DPP (a few cycles each, against ~130 for
+// an LDS-routed shuffle): row_shr:n moves lane i - n to lane i inside each
+// row of 16 lanes; row_bcast:15 / row_bcast:31 copy lane 15 of each row /
+// lane 31 into the following rows selected by the row mask. Lanes with no
+// source (or in rows the mask leaves out) take `fill`.
+template <int CTRL, int ROW_MASK>
+__device__ inline int dpp_move(int x, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum across the 64 lanes of one wave (Hillis-Steele inside
+// each row of 16, then the row totals carried across rows).
+__device__ inline int wave_scan_incl(int x) {
+  x += dpp_move<0x111, 0xf>(x, 0);  // row_shr:1
+  x += dpp_move<0x112, 0xf>(x, 0);  // row_shr:2
+  x += dpp_move<0x114, 0xf>(x, 0);  // row_shr:4
+  x += dpp_move<0x118, 0xf>(x, 0);  // row_shr:8
+  x += dpp_move<0x142, 0xa>(x, 0);  // row_bcast:15 into rows 1 and 3
+  x += dpp_move<0x143, 0xc>(x, 0);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Largest / smallest value over the 64 lanes of a wave, in every lane.
+__device__ inline int wave_max(int x) {
+  constexpr int lo = (int)0x80000000;
+  x = max(x, dpp_move<0x111, 0xf>(x, lo));
+  x = max(x, dpp_move<0x112, 0xf>(x, lo));
+  x = max(x, dpp_move<0x114, 0xf>(x, lo));
+  x = max(x, dpp_move<0x118, 0xf>(x, lo));
+  x = max(x, dpp_move<0x142, 0xa>(x, lo));
+  x = max(x, dpp_move<0x143, 0xc>(x, lo));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+__device__ inline int wave_min(int x) { return -wave_max(-x); }  // (x > INT_MIN)
+
 // Inclusive prefix sum over the NT threads of a workgroup (NT multiple of
 // 64). `tmp` must hold NT/64 ints of LDS. Returns the inclusive prefix and
 // writes the workgroup total to *total. Contains two barriers.
@@ -42,12 +77,7 @@ template <int NT>
 __device__ inline int wg_scan_incl(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_scan_incl(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   int pre = 0, tot = 0;
@@ -60,18 +90,6 @@ __device__ inline int wg_scan_incl(int v, int* tmp, int* total) {
   __syncthreads();
   *total = tot;
   return x + pre;
-}
-
-// Inclusive prefix sum across the 64 lanes of one wave.
-__device__ inline int wave_scan_incl(int v) {
-  const int lane = threadIdx.x & 63;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
 }
 
 // ------------------------------------------------------------ MXFP4 -----

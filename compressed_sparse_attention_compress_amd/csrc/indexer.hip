@@ -28,16 +28,14 @@
 // Kernel boundaries, not fences, order the hand-offs: an agent-scope fence
 // inside a workgroup writes back and invalidates the XCD's whole L2.
 #include "csa_internal.h"
+#include "topk_device.h"
 
 #include <mutex>
 
 namespace {
 
-constexpr int TILE = 2048;       // entries per split-scan workgroup
-constexpr int NB1 = 512;         // split-scan histogram bins
-constexpr int MAX_TILES = 2048;  // split-scan limit: n_max <= TILE * MAX_TILES
+using namespace csa_topk;
 constexpr int PREFILL_MIN_T = 16;
-constexpr int POOL_G = 8;        // entries per group of the blockwise pool
 
 // One 16-entry column tile: A = indexer queries (rows = heads), B = keys
 // (columns = entries). Lane (j + 16g) holds D[head 4g + r][entry j] in
@@ -59,25 +57,46 @@ __device__ inline int score_tile(const v4i (&A)[KS], const v4i (&Bk)[KS], const 
   return p;
 }
 
-// Exclusive prefix sum, in place, of an LDS array of n <= 2048 ints, by a
-// 256-thread workgroup. Ends with a barrier.
-__device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
-  const int base = threadIdx.x * 8;
-  int loc[8];
-  int s = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    loc[j] = (base + j < n) ? a[base + j] : 0;
-    s += loc[j];
-  }
+// The scan unit's short list (k_idx_scan's LISTS tail): its cut bin, the
+// lowest bin whose suffix count (entries in it and above) is at most lcap
+// (NB1, an empty list, when the top bin alone holds more), then its entries
+// of the bins at or above the cut in entry order, and (count, cut). Kept out
+// of line: the scan's main loop runs at the register limit, and this code's
+// values must not stay live across it.
+__device__ __noinline__ void scan_unit_list(const uint32_t* lh, const int* ssc, int span,
+                                            int64_t wg0, int64_t N, int2* lq, int2* info,
+                                            int lcap) {
+  __shared__ int l_tmp[4];
+  __shared__ int l_cut[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hb = NB1 - 1 - 2 * (int)threadIdx.x;
+  const int c_hi = (int)lh[hb], c_lo = (int)lh[hb - 1];
   int tot;
-  int run = wg_scan_incl<256>(s, tmp, &tot) - s;
+  const int incl = wg_scan_incl<256>(c_hi + c_lo, l_tmp, &tot);
+  const int excl = incl - c_hi - c_lo;
+  int cut = NB1;
+  if (excl + c_hi <= lcap) cut = hb;
+  if (incl <= lcap) cut = hb - 1;
+  cut = wave_min(cut);
+  if (lane == 0) l_cut[wave] = cut;
+  __syncthreads();
+  cut = min(min(l_cut[0], l_cut[1]), min(l_cut[2], l_cut[3]));
+  // the listed entries in entry order: thread j takes [8 j, 8 j + 8)
+  const int j0 = threadIdx.x * 8;
+  int v[8];
+  int f = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (base + j < n) a[base + j] = run;
-    run += loc[j];
+    const bool in = j0 + j < span && wg0 + j0 + j < N;
+    v[j] = in ? ssc[j0 + j] : -1;
+    f += v[j] >= 0 && score_bin512(v[j]) >= cut;
   }
-  __syncthreads();
+  int total;
+  int at = wg_scan_incl<256>(f, l_tmp, &total) - f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (v[j] >= 0 && score_bin512(v[j]) >= cut) lq[at++] = int2{v[j], (int)(wg0 + j0 + j)};
+  if (threadIdx.x == 0) *info = int2{total, cut};
 }
 
 // ------------------------------------------------------------------------
@@ -92,14 +111,17 @@ __device__ inline void lds_excl_scan(int* a, int n, int* tmp) {
 // blockwise candidate pool.
 // (keys carries no restrict: loads through it then stay ordered with the
 // empty asm statement that paces the batches below)
-template <int DI, bool CAND, int SUB, bool POOL>
+// LISTS: the workgroup also lists its entries of the top bins (all entries
+// of the bins above its cut, at most lcap, in entry order) with their count
+// and the cut bin, so that a later selection needs no select pass.
+template <int DI, bool CAND, int SUB, bool POOL, bool LISTS>
 __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
     const int8_t* keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
     const int64_t* __restrict__ qpos, const int32_t* __restrict__ cand, int C, int64_t npad,
     int32_t* __restrict__ slab,
     uint32_t* __restrict__ hist, int64_t gpad, int32_t* __restrict__ gslab,
-    uint32_t* __restrict__ ghist) {
+    uint32_t* __restrict__ ghist, int2* __restrict__ tinfo, int2* __restrict__ comp, int lcap) {
   constexpr int KS = (DI + 63) / 64;
   constexpr int BATCH = 8;
   constexpr int SPAN = TILE / SUB;  // entries per workgroup (SUB workgroups per tile)
@@ -261,6 +283,9 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     if (lh[i]) atomicAdd(&hq[i], lh[i]);
     if (POOL && lhg[i]) atomicAdd(&ghist[(int64_t)qi * NB1 + i], lhg[i]);
   }
+  if constexpr (LISTS)
+    scan_unit_list(lh, ssc, SPAN, wg0, N, comp + ((int64_t)qi * gridDim.x + blockIdx.x) * lcap,
+                   tinfo + (int64_t)qi * gridDim.x + blockIdx.x, lcap);
 }
 
 // ------------------------------------------------------------------------
@@ -458,32 +483,6 @@ struct Level {
 // ------------------------------------------------------------------------
 // split scan, phase 2a: per tile, the entries at or above the threshold bin
 // ------------------------------------------------------------------------
-// Threshold bin T1 of a query from its finished histogram: the bin where the
-// count from the top first reaches k_eff; A1 = entries in higher bins. Thread
-// j owns bins 511-2j and 510-2j, so the prefix runs from the top bin down.
-// Returns k_eff; T1 and A1 come back through s_red[0..1] (valid if k_eff > 0).
-__device__ inline int threshold_bin(const uint32_t* hq, int k, int* tmp, int* s_red) {
-  const int hb = NB1 - 1 - 2 * (int)threadIdx.x;
-  const int c_hi = (int)hq[hb];
-  const int c_lo = (int)hq[hb - 1];
-  int total;
-  const int incl = wg_scan_incl<256>(c_hi + c_lo, tmp, &total);
-  const int excl = incl - c_hi - c_lo;
-  const int keff = k < total ? k : total;
-  if (keff > 0) {
-    if (excl + c_hi >= keff && excl < keff) {
-      s_red[0] = hb;
-      s_red[1] = excl;
-    }
-    if (incl >= keff && excl + c_hi < keff) {
-      s_red[0] = hb - 1;
-      s_red[1] = excl + c_hi;
-    }
-  }
-  __syncthreads();
-  return keff;
-}
-
 __global__ __launch_bounds__(256) void k_idx_select(int T, int m, int64_t pos0,
                                                     const int64_t* __restrict__ qpos,
                                                     int64_t blk_cap, int C, bool cand_mode,
@@ -532,98 +531,14 @@ __global__ __launch_bounds__(256) void k_idx_select(int T, int m, int64_t pos0,
   if (threadIdx.x == 0) cnt[(int64_t)qi * n_tiles + tile] = total;
 }
 
-// Exact k-th score among LDS candidates: cs[0..M) holds scores, those in
-// bin T1 span [lo, hi], and `need` of them are still to be taken. Radix
-// refinement over (score - lo): a 256-bin histogram of the remaining range
-// per round, narrowed to the bin where the count from the top reaches need.
-// Returns tau; *take_eq = how many candidates equal to tau are taken. All
-// 256 threads call it; it ends with a barrier.
-__device__ inline int refine_tau(const int* cs, int M, int T1, int lo, int hi, int need,
-                                 uint32_t* bh, int* tmp, int* s_red, int* take_eq) {
-  int R = hi - lo;
-  while (R > 0) {
-    const int bits = 32 - __clz(R);
-    const int shift = bits > 8 ? bits - 8 : 0;
-    bh[threadIdx.x] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < M; i += 256) {
-      const int sv = cs[i];
-      if (score_bin512(sv) == T1 && sv >= lo && sv - lo <= R)
-        atomicAdd(&bh[(sv - lo) >> shift], 1u);
-    }
-    __syncthreads();
-    const int v = (int)bh[255 - threadIdx.x];
-    int tot;
-    const int inc = wg_scan_incl<256>(v, tmp, &tot);
-    if (inc >= need && inc - v < need) {
-      s_red[0] = 255 - (int)threadIdx.x;
-      s_red[1] = need - (inc - v);
-    }
-    __syncthreads();
-    const int beta = s_red[0];
-    need = s_red[1];
-    __syncthreads();
-    lo += beta << shift;
-    R = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
-  }
-  *take_eq = need;
-  return lo;
-}
-
-// Ordered emission of the selected candidates of cs/ce[0..M) (kept in index
-// order): thread j owns entries [8j, 8j + 8) of each 2048-entry round; one
-// scan of the packed (greater, equal) counts gives every entry's output
-// position: #greater before it + min(#equal before it, take_eq).
-// emit(pos, ce[i], cs[i]) for the keff selected ones.
-template <class Emit>
-__device__ inline void emit_ordered(const int* cs, const int* ce, int M, int tau, int take_eq,
-                                    int keff, int* tmp, Emit emit) {
-  int run_gt = 0, run_eq = 0;
-  for (int r0 = 0; r0 < M; r0 += 2048) {
-    const int i0 = r0 + 8 * (int)threadIdx.x;
-    int sv[8];
-    int gtc = 0, eqc = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sv[j] = i0 + j < M ? cs[i0 + j] : -1;
-      gtc += sv[j] > tau;
-      eqc += sv[j] == tau;
-    }
-    const int mine = (gtc << 16) | eqc;
-    int tot;
-    const int before = wg_scan_incl<256>(mine, tmp, &tot) - mine;
-    int gb = run_gt + (before >> 16), eb = run_eq + (before & 0xffff);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int pos = -1;
-      if (sv[j] > tau) {
-        pos = gb + min(eb, take_eq);
-        ++gb;
-      } else if (sv[j] == tau) {
-        if (eb < take_eq) pos = gb + eb;
-        ++eb;
-      }
-      if (pos >= 0 && pos < keff) emit(pos, ce[i0 + j], sv[j]);
-    }
-    run_gt += tot >> 16;
-    run_eq += tot & 0xffff;
-  }
-}
-
 // ------------------------------------------------------------------------
 // small selections, phase 2: one workgroup per query
 // ------------------------------------------------------------------------
 // When a query has at most PICK_MAX candidates (a small Reindex pool, or a
 // context of at most PICK_MAX entries) the per-tile select pass is not
-// needed: one workgroup per query loads the query's whole score row and
-// histogram (left by k_idx_scan) and finds the threshold bin; thread j holds
-// entries [PER j, PER j + PER) in registers. Up to PICK_LDS candidates at or
-// above the bin are compacted into LDS for refine_tau and emit_ordered; more
-// (heavy ties) are refined and emitted straight from the registers, so the
-// kernel needs 17 KB of LDS and several workgroups share a compute unit. It clears the histogram for the next call.
-// PER = entries per thread (PICK_MAX / 256 at most).
-constexpr int PICK_MAX = 8192;
-constexpr int PICK_LDS = 2048;  // candidates compacted into LDS (more stay in registers)
+// needed: one workgroup per query reads the query's whole score row and
+// histogram (left by k_idx_scan) and selects in registers (pick_select).
+// It clears the histogram for the next call. PER = entries per thread.
 template <int PER>
 __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
                                                   const int64_t* __restrict__ qpos,
@@ -633,13 +548,10 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
                                                   const int32_t* __restrict__ cand,
                                                   int32_t* __restrict__ out_idx,
                                                   int32_t* __restrict__ out_score) {
-  __shared__ int cs[PICK_LDS];
-  __shared__ int ce[PICK_LDS];
   __shared__ uint32_t bh[256];
   __shared__ int tmp[4];
   __shared__ int s_red[8];
   const int qi = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int N;  // candidates of the query: the pool, or its visible entries
   {
     const int b = qi / T;
@@ -647,163 +559,33 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
     nv = nv < blk_cap ? nv : blk_cap;
     N = cand ? C : (int)nv;
   }
-  const int32_t* sq = slab + (int64_t)qi * npad;
-  const int32_t* cq = cand ? cand + (int64_t)qi * C : nullptr;
   uint32_t* hq = hist + (int64_t)qi * NB1;
-  // this thread's PER scores (positions [PER j, PER j + PER)), issued before
-  // the histogram scan so that both loads overlap
-  const int p0 = PER * (int)threadIdx.x;
-  int sv[PER];
-  if (p0 + PER <= N) {
-#pragma unroll
-    for (int j = 0; j < PER; j += 4) {
-      const int4 v = *reinterpret_cast<const int4*>(sq + p0 + j);
-      sv[j] = v.x; sv[j + 1] = v.y; sv[j + 2] = v.z; sv[j + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) sv[j] = p0 + j < N ? sq[p0 + j] : -1;
-  }
-  const int keff = threshold_bin(hq, k, tmp, s_red);
-  // histogram consumed: clear it for the next call (thread j owns two bins)
-  hq[NB1 - 1 - 2 * (int)threadIdx.x] = 0u;
-  hq[NB1 - 2 - 2 * (int)threadIdx.x] = 0u;
+  const int32_t* cq = cand ? cand + (int64_t)qi * C : nullptr;
   int32_t* oi = out_idx + (int64_t)qi * k;
   int32_t* os = out_score ? out_score + (int64_t)qi * k : nullptr;
+  const int keff = pick_select<PER>(slab + (int64_t)qi * npad, hq, N, k,
+                                    SelShared{nullptr, nullptr, bh, tmp, s_red},
+                                    [&](int pos, int e, int v) {
+                                      oi[pos] = cq ? cq[e] : e;
+                                      if (os) os[pos] = v;
+                                    });
+  // histogram consumed (every read of it precedes the barriers inside the
+  // selection): clear it for the next call (thread j owns two bins)
+  hq[NB1 - 1 - 2 * (int)threadIdx.x] = 0u;
+  hq[NB1 - 2 - 2 * (int)threadIdx.x] = 0u;
   for (int i = keff + threadIdx.x; i < k; i += 256) {
     oi[i] = -1;
     if (os) os[i] = -1;
-  }
-  if (keff == 0) return;
-  const int T1 = s_red[0];
-  const int need = keff - s_red[1];
-  __syncthreads();
-  // the score range of bin T1, and the count of scores at or above it
-  int vmin = 0x7fffffff, vmax = -1, f = 0;
-  uint32_t in_mask = 0;  // bit j: sv[j] is at or above bin T1
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int bj = sv[j] >= 0 ? score_bin512(sv[j]) : -1;
-    if (bj >= T1) {
-      in_mask |= 1u << j;
-      ++f;
-    }
-    if (bj == T1) {
-      vmin = min(vmin, sv[j]);
-      vmax = max(vmax, sv[j]);
-    }
-  }
-  int M;
-  int at = wg_scan_incl<256>(f, tmp, &M) - f;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    vmin = min(vmin, __shfl_xor(vmin, off, 64));
-    vmax = max(vmax, __shfl_xor(vmax, off, 64));
-  }
-  if (lane == 0) {
-    s_red[wave] = vmin;
-    s_red[4 + wave] = vmax;
-  }
-  __syncthreads();
-  int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
-  const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
-  __syncthreads();
-  if (M <= PICK_LDS) {
-    // few candidates (the usual case): compacted into LDS in index order, so
-    // the refinement and the emission loop over them only
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if ((in_mask >> j) & 1u) {
-        cs[at] = sv[j];
-        ce[at] = p0 + j;
-        ++at;
-      }
-    }
-    __syncthreads();
-    int take_eq;
-    const int tau = refine_tau(cs, M, T1, lo, hi, need, bh, tmp, s_red, &take_eq);
-    emit_ordered(cs, ce, M, tau, take_eq, keff, tmp, [&](int pos, int e, int v) {
-      oi[pos] = cq ? cq[e] : e;
-      if (os) os[pos] = v;
-    });
-    return;
-  }
-  // many candidates (heavy ties): exact k-th score by the radix refinement of
-  // refine_tau, over the registers
-  int nd = need;
-  int R = hi - lo;
-  while (R > 0) {
-    const int bits = 32 - __clz(R);
-    const int shift = bits > 8 ? bits - 8 : 0;
-    bh[threadIdx.x] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int v = sv[j];
-      if (v >= 0 && score_bin512(v) == T1 && v >= lo && v - lo <= R)
-        atomicAdd(&bh[(v - lo) >> shift], 1u);
-    }
-    __syncthreads();
-    const int c = (int)bh[255 - threadIdx.x];
-    int tot;
-    const int inc = wg_scan_incl<256>(c, tmp, &tot);
-    if (inc >= nd && inc - c < nd) {
-      s_red[0] = 255 - (int)threadIdx.x;
-      s_red[1] = nd - (inc - c);
-    }
-    __syncthreads();
-    const int beta = s_red[0];
-    nd = s_red[1];
-    __syncthreads();
-    lo += beta << shift;
-    R = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
-  }
-  const int tau = lo, take_eq = nd;
-  // ordered emission: thread j's scores are entries [PER j, PER j + PER), so
-  // one scan of the packed (greater, equal) counts gives every output position
-  int gtc = 0, eqc = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    gtc += sv[j] > tau;
-    eqc += sv[j] == tau;
-  }
-  const int mine = (gtc << 16) | eqc;
-  int tot;
-  const int before = wg_scan_incl<256>(mine, tmp, &tot) - mine;
-  int gb = before >> 16, eb = before & 0xffff;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    int pos = -1;
-    if (sv[j] > tau) {
-      pos = gb + min(eb, take_eq);
-      ++gb;
-    } else if (sv[j] == tau) {
-      if (eb < take_eq) pos = gb + eb;
-      ++eb;
-    }
-    if (pos >= 0 && pos < keff) {
-      const int e = p0 + j;
-      oi[pos] = cq ? cq[e] : e;
-      if (os) os[pos] = sv[j];
-    }
   }
 }
 
 // ------------------------------------------------------------------------
 // split scan, phase 2b: one workgroup per query resolves the exact k-th score
-// among the candidates and writes the ascending index list
+// among the per-tile candidates and writes the ascending index list
+// (final_select); a group level writes each kept group entry by entry.
+// Dynamic LDS as final_select lays it out. The histogram of the query is
+// cleared for the next call.
 // ------------------------------------------------------------------------
-// Dynamic LDS: t_off[toff_n] ints (toff_n >= the tiles of either level), then
-// cap_lds (score, entry) pairs (2 cap_lds >= 4 toff_n, for the slow path's
-// per-tile arrays), then the speculative staging area. Many queries (prefill
-// chunks) get a compact budget so that several workgroups share a compute
-// unit. The histogram, the per-tile counts and the
-// first 2^spec_shift candidates of every tile are all loaded in one round (the
-// candidates speculatively, before their counts are known); only tiles with
-// more candidates than that need a second round. A query with more candidates
-// than cap_lds (massive ties) walks the per-tile lists in global memory
-// instead. The histogram of the query is cleared for the next call.
-constexpr int SPEC_SLOTS = 4096;  // speculative candidates staged per query (32 KiB)
 __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
                                                    const int64_t* __restrict__ qpos,
                                                    int64_t blk_cap,
@@ -814,324 +596,46 @@ __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
   __shared__ int tmp[4];
   __shared__ uint32_t bh[256];
   __shared__ int s_red[8];
-  __shared__ int w_gt[4], w_eq[4];
-  int* t_off = smem;                                  // [toff_n]
-  int* area = smem + toff_n;                          // [2 * cap_lds]
-  int2* spec = reinterpret_cast<int2*>(area + 2 * cap_lds);  // [spec_tiles << spec_shift]
   // queries of the entry selection first, then those of the group selection
   const bool lv1 = (int)blockIdx.x >= BT;
   const Level L = lv1 ? L1 : L0;
   const int qi = lv1 ? blockIdx.x - BT : blockIdx.x;
-  const int k = L.k, n_tiles = L.n_tiles, gs = L.gshift;
-  const int spec_tiles = L.spec_tiles, spec_shift = L.spec_shift;
-  const int64_t npad = L.npad;
-  const int2* cbuf = L.cbuf;
-  const int32_t* cnt = L.cnt;
-  uint32_t* hist = L.hist;
+  const int k = L.k, gs = L.gshift;
   int64_t nv;  // visible entries of the query (bounds the expanded groups)
   {
     const int b = qi / T;
     nv = (query_base(qpos, pos0, b) + (qi - b * T) + 1) / m;
     nv = nv < blk_cap ? nv : blk_cap;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int2* cq = cbuf + (int64_t)qi * npad;
-  uint32_t* hq = hist + (int64_t)qi * NB1;
-  const int32_t* cntq = cnt + (int64_t)qi * n_tiles;
-
-  // ---- one round of independent loads
-  const int hb = NB1 - 1 - 2 * (int)threadIdx.x;
-  const int c_hi = (int)hq[hb];
-  const int c_lo = (int)hq[hb - 1];
-  // loads first, LDS stores after: a load feeding an LDS store in the same
-  // loop iteration would make each iteration wait for its load
-  const int nspec = spec_tiles << spec_shift;
-  const int spt = 1 << spec_shift;
-  {
-    constexpr int SPT = SPEC_SLOTS / 256;  // speculative candidates per thread (max)
-    int2 r[SPT];
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      int i = threadIdx.x + 256 * u;
-      i = i < nspec ? i : 0;
-      r[u] = cq[(int64_t)(i >> spec_shift) * TILE + (i & (spt - 1))];
-    }
-    int cr[MAX_TILES / 256];
-#pragma unroll
-    for (int u = 0; u < MAX_TILES / 256; ++u) {
-      const int i = threadIdx.x + 256 * u;
-      cr[u] = i < n_tiles ? cntq[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const int i = threadIdx.x + 256 * u;
-      if (i < nspec) spec[i] = r[u];
-    }
-#pragma unroll
-    for (int u = 0; u < MAX_TILES / 256; ++u) {
-      const int i = threadIdx.x + 256 * u;
-      if (i < n_tiles) t_off[i] = cr[u];
-    }
-  }
-  // histogram consumed: clear it for the next call
-  hq[hb] = 0u;
-  hq[hb - 1] = 0u;
-
-  // ---- threshold bin (thread j owns bins 511-2j and 510-2j)
-  int total_valid;
-  const int incl = wg_scan_incl<256>(c_hi + c_lo, tmp, &total_valid);
-  const int excl = incl - c_hi - c_lo;
-  const int keff = k < total_valid ? k : total_valid;
-  if (keff > 0) {
-    if (excl + c_hi >= keff && excl < keff) {
-      s_red[0] = hb;
-      s_red[1] = excl;
-    }
-    if (incl >= keff && excl + c_hi < keff) {
-      s_red[0] = hb - 1;
-      s_red[1] = excl + c_hi;
-    }
-  }
-  __syncthreads();
-  const int T1 = s_red[0], A1 = s_red[1];
-
+  uint32_t* hq = L.hist + (int64_t)qi * NB1;
   int32_t* oi = L.out + ((int64_t)qi * k << gs);
   int32_t* os = L.out_score ? L.out_score + (int64_t)qi * k : nullptr;
   const int32_t* cqq = cand ? cand + (int64_t)qi * C : nullptr;
+  const FinalPlan P{L.n_tiles, k, L.spec_tiles, L.spec_shift, cap_lds, toff_n};
+  const int keff = final_select(
+      hq, L.cnt + (int64_t)qi * L.n_tiles, L.cbuf + (int64_t)qi * L.npad, P, smem, bh, tmp, s_red,
+      [&](int pos, int e, int sv) {
+        if (gs == 0) {
+          oi[pos] = cqq ? cqq[e] : e;
+          if (os) os[pos] = sv;
+        } else {
+          for (int r = 0; r < (1 << gs); ++r) {
+            const int64_t ent = ((int64_t)e << gs) + r;
+            oi[(pos << gs) + r] = ent < nv ? (int)ent : -1;
+          }
+        }
+      });
+  // histogram consumed: clear it for the next call
+  hq[NB1 - 1 - 2 * (int)threadIdx.x] = 0u;
+  hq[NB1 - 2 - 2 * (int)threadIdx.x] = 0u;
   for (int i = (keff << gs) + threadIdx.x; i < (k << gs); i += 256) oi[i] = -1;
   if (os)
     for (int i = keff + threadIdx.x; i < k; i += 256) os[i] = -1;
-  // selected item number pos: an entry id, or a group written out entry by
-  // entry (entries not visible yet as -1)
-  auto emit = [&](int pos, int e, int sv) {
-    if (gs == 0) {
-      oi[pos] = cqq ? cqq[e] : e;
-      if (os) os[pos] = sv;
-    } else {
-      for (int r = 0; r < (1 << gs); ++r) {
-        const int64_t ent = ((int64_t)e << gs) + r;
-        oi[(pos << gs) + r] = ent < nv ? (int)ent : -1;
-      }
-    }
-  };
-  if (keff == 0) return;
-
-  __syncthreads();
-  const int last_cnt = t_off[n_tiles - 1];
-  __syncthreads();
-  lds_excl_scan(t_off, n_tiles, tmp);
-  const int M = t_off[n_tiles - 1] + last_cnt;
-
-  int need = keff - A1;  // threshold-bin candidates still to take
-  if (M <= cap_lds) {
-    // ---- fast path: every candidate in LDS, index order kept. Two threads
-    // per tile copy its candidates (from the speculative stage, or from
-    // global memory past it) and track the score range of the threshold bin.
-    int* cs = area;
-    int* ce = area + cap_lds;
-    int vmin = 0x7fffffff, vmax = -1;
-    for (int tl = threadIdx.x >> 1; tl < n_tiles; tl += 128) {
-      const int base = t_off[tl];
-      const int c = (tl + 1 < n_tiles ? t_off[tl + 1] : M) - base;
-      for (int j = threadIdx.x & 1; j < c; j += 2) {
-        const int2 v = (tl < spec_tiles && j < spt) ? spec[(tl << spec_shift) + j]
-                                                     : cq[(int64_t)tl * TILE + j];
-        cs[base + j] = v.x;
-        ce[base + j] = v.y;
-        if (score_bin512(v.x) == T1) {
-          vmin = min(vmin, v.x);
-          vmax = max(vmax, v.x);
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      vmin = min(vmin, __shfl_xor(vmin, off, 64));
-      vmax = max(vmax, __shfl_xor(vmax, off, 64));
-    }
-    if (lane == 0) {
-      s_red[wave] = vmin;
-      s_red[4 + wave] = vmax;
-    }
-    __syncthreads();
-    const int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
-    const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
-    __syncthreads();
-    int take_eq;
-    const int tau = refine_tau(cs, M, T1, lo, hi, need, bh, tmp, s_red, &take_eq);
-    emit_ordered(cs, ce, M, tau, take_eq, keff, tmp, emit);
-    return;
-  }
-
-  // ---- slow path: per-tile lists in global memory (arrays alias the area)
-  int* t_cnt = area;
-  int* t_gt = area + toff_n;
-  int* t_eq = area + 2 * toff_n;
-  int* t_eqb = area + 3 * toff_n;
-  for (int i = threadIdx.x; i < n_tiles; i += 256) t_cnt[i] = cntq[i];
-  __syncthreads();
-  int vmin = 0x7fffffff, vmax = -1;
-  for (int tl = wave; tl < n_tiles; tl += 4) {
-    const int c = t_cnt[tl];
-    for (int j = lane; j < c; j += 64) {
-      const int sv = cq[(int64_t)tl * TILE + j].x;
-      if (score_bin512(sv) == T1) {
-        vmin = min(vmin, sv);
-        vmax = max(vmax, sv);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    vmin = min(vmin, __shfl_xor(vmin, off, 64));
-    vmax = max(vmax, __shfl_xor(vmax, off, 64));
-  }
-  if (lane == 0) {
-    s_red[wave] = vmin;
-    s_red[4 + wave] = vmax;
-  }
-  __syncthreads();
-  int lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
-  const int hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
-  __syncthreads();
-  int R = hi - lo;
-  while (R > 0) {
-    const int bits = 32 - __clz(R);
-    const int shift = bits > 8 ? bits - 8 : 0;
-    bh[threadIdx.x] = 0;
-    __syncthreads();
-    for (int tl = wave; tl < n_tiles; tl += 4) {
-      const int c = t_cnt[tl];
-      for (int j = lane; j < c; j += 64) {
-        const int sv = cq[(int64_t)tl * TILE + j].x;
-        if (score_bin512(sv) == T1 && sv >= lo && sv - lo <= R)
-          atomicAdd(&bh[(sv - lo) >> shift], 1u);
-      }
-    }
-    __syncthreads();
-    const int v = (int)bh[255 - threadIdx.x];
-    int tot;
-    const int inc = wg_scan_incl<256>(v, tmp, &tot);
-    if (inc >= need && inc - v < need) {
-      s_red[0] = 255 - (int)threadIdx.x;
-      s_red[1] = need - (inc - v);
-    }
-    __syncthreads();
-    const int beta = s_red[0];
-    need = s_red[1];
-    __syncthreads();
-    lo += beta << shift;
-    R = shift ? min(R - (beta << shift), (1 << shift) - 1) : 0;
-  }
-  const int tau = lo;
-  const int take_eq = need;
-  for (int tl = wave; tl < n_tiles; tl += 4) {
-    const int c = t_cnt[tl];
-    int gt = 0, eq = 0;
-    for (int j = lane; j < c; j += 64) {
-      const int sv = cq[(int64_t)tl * TILE + j].x;
-      gt += sv > tau;
-      eq += sv == tau;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      gt += __shfl_xor(gt, off, 64);
-      eq += __shfl_xor(eq, off, 64);
-    }
-    if (lane == 0) {
-      t_gt[tl] = gt;
-      t_eq[tl] = eq;
-      t_eqb[tl] = eq;
-    }
-  }
-  __syncthreads();
-  lds_excl_scan(t_eqb, n_tiles, tmp);
-  for (int tl = threadIdx.x; tl < n_tiles; tl += 256) {
-    int take = take_eq - t_eqb[tl];
-    take = take < 0 ? 0 : (take > t_eq[tl] ? t_eq[tl] : take);
-    t_gt[tl] += take;  // selected count of the tile
-  }
-  __syncthreads();
-  lds_excl_scan(t_gt, n_tiles, tmp);  // -> output offset of each tile
-  for (int tl = wave; tl < n_tiles; tl += 4) {
-    const int c = t_cnt[tl];
-    int eq_run = t_eqb[tl];
-    int out_run = t_gt[tl];
-    for (int j0 = 0; j0 < c; j0 += 64) {
-      const int j = j0 + lane;
-      int2 v = int2{-1, -1};
-      if (j < c) v = cq[(int64_t)tl * TILE + j];
-      const bool is_eq = j < c && v.x == tau;
-      const uint64_t meq = __ballot(is_eq);
-      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      const int eq_rank = eq_run + __popcll(meq & below);
-      const bool take = j < c && (v.x > tau || (is_eq && eq_rank < take_eq));
-      const uint64_t mt = __ballot(take);
-      if (take) {
-        const int pos = out_run + __popcll(mt & below);
-        if (pos < keff) {
-          emit(pos, v.y, v.x);
-        }
-      }
-      eq_run += __popcll(meq);
-      out_run += __popcll(mt);
-    }
-  }
 }
 
 // ------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------
-struct IdxLayout {
-  int n_tiles, g_tiles;  // entry tiles; group tiles (0 without a pool)
-  int64_t npad, gpad;
-  int64_t off_hist, off_ghist, off_cnt, off_slab, off_cbuf, off_gcnt, off_gslab, off_gcbuf, bytes;
-};
-
-static inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
-
-static IdxLayout idx_layout(int64_t BT, int64_t n_max, bool pool) {
-  IdxLayout L;
-  int64_t nt = (n_max + TILE - 1) / TILE;
-  L.n_tiles = (int)(nt < 1 ? 1 : nt);
-  L.npad = (int64_t)L.n_tiles * TILE;
-  L.g_tiles = pool ? (int)((L.npad / POOL_G + TILE - 1) / TILE) : 0;
-  L.gpad = (int64_t)L.g_tiles * TILE;
-  int64_t o = 0;
-  // header: depends on B*T only, kept zero between calls
-  L.off_hist = o; o = align_up(o + BT * NB1 * 4, 256);
-  L.off_ghist = o; o = align_up(o + BT * NB1 * 4, 256);
-  // body: rewritten by every call
-  L.off_cnt = o; o = align_up(o + BT * L.n_tiles * 4, 256);
-  L.off_slab = o; o = align_up(o + BT * L.npad * 4, 256);
-  L.off_cbuf = o; o = align_up(o + BT * L.npad * 8, 256);
-  L.off_gcnt = o; o = align_up(o + BT * L.g_tiles * 4, 256);
-  L.off_gslab = o; o = align_up(o + BT * L.gpad * 4, 256);
-  L.off_gcbuf = o; o = align_up(o + BT * L.gpad * 8, 256);
-  L.bytes = o;
-  return L;
-}
-
-// Candidates the final kernel keeps in LDS: about twice k (the entries above
-// the threshold bin plus that bin), at least `least` and enough for the
-// slow-path arrays (2 cap >= 4 toff_n), at most 8192 so that the kernel's LDS
-// stays within 104 KiB (larger k take the slow path, which reads the per-tile
-// lists from global memory).
-static int select_cap(int k, int toff_n, int least) {
-  int c = least;
-  while (c < 2 * k && c < 8192) c *= 2;
-  return c > 2 * toff_n ? c : 2 * toff_n;
-}
-
-// Speculative first-round candidates of the final pass: a staging area of
-// `slots` shared out evenly, a power of two per tile between 32 and TILE.
-static void spec_plan(int n_tiles, int slots, int* spec_tiles, int* spec_shift) {
-  int sh = 5;
-  while ((1 << (sh + 1)) <= TILE && ((int64_t)n_tiles << (sh + 1)) <= slots) ++sh;
-  *spec_shift = sh;
-  *spec_tiles = n_tiles < (slots >> sh) ? n_tiles : (slots >> sh);
-}
-
 // A launch of at least this many queries has workgroups to spare: its final
 // pass uses the compact LDS budget (2,048 candidates, as many speculative
 // slots), which lets four workgroups share a compute unit at k <= 1024.
@@ -1160,6 +664,7 @@ struct IdxArgs {
   const int64_t* pos = nullptr;  // per-sequence first positions (pos0 = their bound) or null
   int n_keep = 0;              // blockwise pool: groups kept (0 = no pool)
   int32_t* out_pool = nullptr;  // [B][T][POOL_G * n_keep]
+  bool lists = false;          // the workspace has the scan-side lists (csa_index_attn)
 };
 
 // Runs of at least PREFILL_MIN_T queries per sequence (prefill chunks) are
@@ -1197,7 +702,7 @@ static int idx_phase(const IdxArgs& a, int phase) {
   if (st != CSA_OK || a.B == 0 || a.T == 0) return st;
   const int BT = a.B * a.T;
   const bool pool = a.out_pool != nullptr;
-  IdxLayout L = idx_layout(BT, n_max, pool);
+  IdxLayout L = idx_layout(BT, n_max, pool, a.lists);
   if (!a.ws) return CSA_ERR_WORKSPACE;
   if (a.ws_bytes < L.bytes) return CSA_ERR_WORKSPACE;
   if (!csa_aligned(a.ws, 256)) return CSA_ERR_ALIGN;
@@ -1244,13 +749,20 @@ static int idx_phase(const IdxArgs& a, int phase) {
   } else if (phase == 0) {
     // small scans split each tile over 2 or 4 workgroups so that about 1024
     // workgroups (four per compute unit, all resident at once) stream the keys
-    const int64_t nwg = (int64_t)L.n_tiles * BT;
-    const int sub = nwg >= 1024 ? 1 : (nwg >= 512 ? 2 : 4);
+    const int sub = L.sub;
     const dim3 sgrid(L.n_tiles * sub, BT);
-#define CSA_LAUNCH_SCAN(DD, CC, SS, PP)                                                         \
-  hipLaunchKernelGGL((k_idx_scan<DD, CC, SS, PP>), sgrid, dim3(256), 0, a.stream, a.q_idx, a.w, \
-                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.pos, a.cand, C, L.npad, slab,  \
-                     hist, L.gpad, gslab, ghist)
+    int2* tinfo = reinterpret_cast<int2*>(ws + L.off_tinfo);
+    int2* comp = reinterpret_cast<int2*>(ws + L.off_comp);
+    const bool lists = a.lists && L.units > 0 && !a.cand && !pool;
+#define CSA_LAUNCH_SCAN1(DD, CC, SS, PP, LL)                                                     \
+  hipLaunchKernelGGL((k_idx_scan<DD, CC, SS, PP, LL>), sgrid, dim3(256), 0, a.stream, a.q_idx,  \
+                     a.w, a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.pos, a.cand, C, L.npad,    \
+                     slab, hist, L.gpad, gslab, ghist, tinfo, comp, L.lcap)
+#define CSA_LAUNCH_SCAN(DD, CC, SS, PP)                               \
+  do {                                                                \
+    if (!CC && !PP && lists) CSA_LAUNCH_SCAN1(DD, CC, SS, PP, true);  \
+    else CSA_LAUNCH_SCAN1(DD, CC, SS, PP, false);                     \
+  } while (0)
 #define CSA_LAUNCH_SCAN_S(DD, CC, PP)                  \
   do {                                                \
     if (sub == 1) CSA_LAUNCH_SCAN(DD, CC, 1, PP);     \
@@ -1272,6 +784,14 @@ static int idx_phase(const IdxArgs& a, int phase) {
     }
 #undef CSA_LAUNCH_SCAN_S
 #undef CSA_LAUNCH_SCAN
+#undef CSA_LAUNCH_SCAN1
+  } else if (phase == 2) {
+    // the per-tile select pass alone: an in-kernel selection resolves the
+    // top-k from its lists (csa_index_attn)
+    Level L0{slab, cbuf, cnt, hist, L.npad, L.n_tiles, a.k, 0, 0, 0, a.out_idx, a.out_score};
+    Level L1{};
+    hipLaunchKernelGGL(k_idx_select, dim3(L.n_tiles, BT), dim3(256), 0, a.stream, a.T, a.m,
+                       a.pos0, a.pos, a.blk_cap, C, a.cand != nullptr, L0, L1);
   } else if (phase == 1) {
     Level L0{slab, cbuf, cnt, hist, L.npad, L.n_tiles, a.k, 0, 0, 0, a.out_idx, a.out_score};
     Level L1{gslab, gcbuf, gcnt, ghist, L.gpad, L.g_tiles, a.n_keep, 3, 0, 0, a.out_pool,
@@ -1437,4 +957,90 @@ extern "C" int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream) 
                      reinterpret_cast<uint32_t*>(ws), n);
   CSA_TRY_LAUNCH();
   return CSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Indexer + top-k + sparse attention in one call (one CSA layer's decode
+// step). Few queries per sequence: the scan (which also leaves each unit's
+// short list of top-bin entries), then the attention kernel in which every
+// workgroup resolves its query's top-k for its own slots from those lists
+// or, with at most PICK_MAX candidates, from the whole score row (no select
+// or final pass, no id round trip through memory), then the merge. Runs of
+// queries: the separate index and attention launches.
+// ---------------------------------------------------------------------------
+extern "C" int64_t csa_index_attn_workspace(int B, int T, int64_t n_max, int k, int H, int d,
+                                            int W) {
+  if (B < 0 || T < 0 || n_max < 0 || k < 1 || H < 1 || d < 1 || W < 0) return -1;
+  const int64_t ib =
+      align_up(idx_layout((int64_t)B * T, n_max, false, n_max > PICK_MAX).bytes, 256);
+  const int64_t ns = (int64_t)k + W;
+  // (the fused plan's partials depend on the indexer shape only through n_max;
+  // Hi = 16 is the largest the indexer takes, so the size covers every Hi)
+  const int64_t ab = fused_attn_fits(T, ns)
+                         ? fused_attn_workspace(B, T, H, d, ns, fused_alg_bytes(n_max, 16, 128, k, W, H, d))
+                         : csa_attn_workspace(B, T, H, d, ns);
+  return ab < 0 ? -1 : ib + ab;
+}
+
+extern "C" int csa_index_attn(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                              int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                              const int64_t* pos, const int32_t* cand, int C, int k,
+                              const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                              const uint16_t* win, int Wcap, int W, int H, int d,
+                              float softmax_scale, int32_t* out_idx, int32_t* out_score,
+                              void* out, int out_dtype, float* lse, void* workspace,
+                              int64_t ws_bytes, int scale_fmt, hipStream_t stream) {
+  if (pos && !csa_aligned(pos, 8)) return CSA_ERR_ALIGN;
+  IdxArgs a{q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos0, cand, C, k, out_idx, out_score,
+            workspace, ws_bytes, stream};
+  a.pos = pos;
+  int64_t n_max = 0;
+  int st = idx_check(a, &n_max);
+  if (st != CSA_OK) return st;
+  if (B == 0 || T == 0) return CSA_OK;
+  const int BT = B * T;
+  // the scan's short lists serve queries with more than PICK_MAX candidates
+  // and no pool (smaller ones select from their whole score row)
+  a.lists = !cand && n_max > PICK_MAX;
+  const IdxLayout L = idx_layout(BT, n_max, false, a.lists);
+  const int64_t ib = align_up(L.bytes, 256);
+  const int64_t ns = (int64_t)k + W;
+  // in-kernel selection: from whole score rows (at most PICK_MAX candidates)
+  // or from the scan's short lists (when the layout could give every unit
+  // one); otherwise the separate passes
+  const bool fused = fused_attn_fits(T, ns) && (n_max <= PICK_MAX || (!cand && L.units > 0));
+  char* ws = reinterpret_cast<char*>(workspace);
+  FusedAttn f{q, codes, scales, blk_cap, k, win, Wcap, W, B, T, H, d, pos0, pos,
+              softmax_scale, out, out_dtype, lse, nullptr, 0, scale_fmt, stream,
+              0, reinterpret_cast<uint32_t*>(ws + L.off_hist),
+              reinterpret_cast<const int2*>(ws + L.off_tinfo),
+              reinterpret_cast<const int2*>(ws + L.off_comp),
+              reinterpret_cast<const int32_t*>(ws + L.off_slab), L.npad,
+              ListsPlan{L.units, __builtin_ctz(L.lcap > 0 ? L.lcap : 1)}, cand, cand ? C : 0, m,
+              out_idx, out_score, fused_alg_bytes(n_max, Hi, Di, k, W, H, d)};
+  // every argument is checked before anything is launched
+  st = fused_attn_check(f);
+  if (st != CSA_OK) return st;
+  const int64_t ab = fused ? fused_attn_workspace(B, T, H, d, ns, f.alg_bytes)
+                           : csa_attn_workspace(B, T, H, d, ns);
+  if (ab < 0) return CSA_ERR_SHAPE;
+  if (!workspace || ws_bytes < ib + ab) return CSA_ERR_WORKSPACE;
+  if (!csa_aligned(workspace, 256)) return CSA_ERR_ALIGN;
+  f.ws = ab > 0 ? ws + ib : nullptr;
+  f.ws_bytes = ws_bytes - ib;
+  st = idx_phase(a, 0);
+  if (st != CSA_OK) return st;
+  if (!fused) {
+    st = idx_phase(a, 1);
+    if (st != CSA_OK) return st;
+    if (pos)
+      return csa_sparse_attn_ragged(q, codes, scales, blk_cap, out_idx, k, win, Wcap, W, B, T, H, d,
+                                    pos, pos0, softmax_scale, out, out_dtype, lse, f.ws,
+                                    f.ws_bytes, scale_fmt, stream);
+    return csa_sparse_attn(q, codes, scales, blk_cap, out_idx, k, win, Wcap, W, B, T, H, d, pos0,
+                           softmax_scale, out, out_dtype, lse, f.ws, f.ws_bytes, scale_fmt,
+                           stream);
+  }
+  f.sel = n_max <= PICK_MAX ? 2 : 1;  // whole score rows, or the scan's lists
+  return fused_attn_launch(f);
 }

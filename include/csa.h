@@ -282,6 +282,39 @@ int csa_index_pool_select(const int8_t* q_idx, const int8_t* w, const int8_t* ke
                           int group, int n_keep, int32_t* out_pool,
                           void* workspace, int64_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * One CSA layer's index + attention step in a single call: csa_index_topk
+ * (no candidate pool, or a Reindex pool `cand`) followed by csa_sparse_attn
+ * over the selected entries plus the window, with the same results as those
+ * two calls (podcast cues 12 and 14: a Full or Reindex layer selects its
+ * top-k, then attends to it; "Frontier Architecture Decoding Notes (4)",
+ * section 1: selected compressed blocks plus the newest 128 tokens under one
+ * softmax). For decode (T < 16 queries per sequence, k + W <= 32768) the
+ * top-k is resolved inside the attention kernel: every workgroup selects for
+ * its own slots, so no separate final pass or id list round trip is needed.
+ * Arguments are those of csa_index_topk and csa_sparse_attn:
+ *   q_idx, w, keys, blk_cap, B, T, Hi, Di, m, cand, C, k, out_idx, out_score
+ *     as in csa_index_topk (keys and the FP4 cache share blk_cap);
+ *   q, codes, scales, win, Wcap, W, H, d, softmax_scale, out, out_dtype, lse,
+ *     scale_fmt as in csa_sparse_attn;
+ *   pos0: the queries' first position; or, with pos (int64 [B] DEVICE array,
+ *     8-byte aligned, may be NULL), the bound of the per-sequence positions
+ *     as in the *_ragged calls.
+ * out_idx is always written (ascending, -1 padded). Workspace:
+ * csa_index_attn_workspace(B, T, n_max, k, H, d, W) bytes, n_max as for
+ * csa_index_topk_workspace, 256-byte aligned; its head (the first part, laid
+ * out by B*T only) follows the csa_index_topk rules: zero before the first
+ * call and after a B*T change or a failed call, left zero by every
+ * successful call. Every argument is checked before the first launch. */
+int64_t csa_index_attn_workspace(int B, int T, int64_t n_max, int k, int H, int d, int W);
+int csa_index_attn(const int8_t* q_idx, const int8_t* w, const int8_t* keys, int64_t blk_cap,
+                   int B, int T, int Hi, int Di, int m, int64_t pos0, const int64_t* pos,
+                   const int32_t* cand, int C, int k,
+                   const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                   const uint16_t* win, int Wcap, int W, int H, int d, float softmax_scale,
+                   int32_t* out_idx, int32_t* out_score, void* out, int out_dtype, float* lse,
+                   void* workspace, int64_t ws_bytes, int scale_fmt, hipStream_t stream);
+
 /* Zero-fill a workspace with a kernel on `stream` (no hipMemset, so it may be
  * captured in a graph). bytes must be a multiple of 4 and ws 4-byte aligned. */
 int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);

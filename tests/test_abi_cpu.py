@@ -177,3 +177,26 @@ def test_prepare_keeps_marshalled_tensors_alive():
     del run
     gc.collect()
     assert ref() is None
+
+
+def test_index_attn_argument_errors(L):
+    """csa_index_attn checks the indexer and the attention arguments, then
+    the workspace, before launching anything."""
+    P = ctypes.c_void_p
+    fake = P(256)
+
+    def call(k=64, Di=64, d=512, H=64, W=128, ws=fake, ws_bytes=1 << 30, pos=None, out_dtype=0):
+        return L.csa_index_attn(fake, fake, fake, 1 << 16, 2, 1, 8, Di, 4, 4 * 1000, pos, None, 0,
+                                k, fake, fake, fake, fake, 256, W, H, d, ctypes.c_float(1.0),
+                                fake, None, fake, out_dtype, None, ws, ws_bytes, 0, None)
+    assert call(k=0) == -2
+    assert call(Di=48) == -2
+    assert call(d=96) == -2
+    assert call(H=65) == -2
+    assert call(out_dtype=9) == -5
+    assert call(pos=P(260)) == -7
+    assert call(ws=None) == -4
+    assert call(ws_bytes=1024) == -4
+    need = L.csa_index_attn_workspace(2, 1, 1000, 64, 64, 512, 128)
+    assert need > L.csa_index_topk_workspace(2, 1, 1000, 64, 0)
+    assert L.csa_index_attn_workspace(2, 1, 1000, 0, 64, 512, 128) == -1
