@@ -47,6 +47,57 @@ __device__ inline void pool8(int n, GateAt gate_at, RowAt row_at, double p[8]) {
   }
 }
 
+// Lane j of each aligned 4-lane quad receives quad lane J's value.
+template <int J>
+__device__ inline double quad_bcast(double v) {
+  constexpr int CTRL = J | (J << 2) | (J << 4) | (J << 6);  // quad_perm [J,J,J,J]
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+
+// pool8 for a full 4-token block, the same operations in the same order, with
+// the four gate exponentials and weight divisions spread over the lanes of
+// each quad (lane j of a quad takes token j) and broadcast back, and every row
+// load issued before the arithmetic. The quads of a block's lane group all hold
+// the same gates, so each quad computes the weights on its own.
+__device__ inline void pool4_quad(const float* __restrict__ g, const float* __restrict__ x,
+                                  int64_t ld, int lane, double p[8]) {
+  const float gl = g[lane & 3];
+  float4 a[4], c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = *reinterpret_cast<const float4*>(x + j * ld);
+    c[j] = *reinterpret_cast<const float4*>(x + j * ld + 4);
+  }
+  const double gd = (double)gl;
+  double gmax = fmax(quad_bcast<0>(gd), quad_bcast<1>(gd));
+  gmax = fmax(gmax, quad_bcast<2>(gd));
+  gmax = fmax(gmax, quad_bcast<3>(gd));
+  const double e = exp(gd - gmax);
+  double den = quad_bcast<0>(e);
+  den = den + quad_bcast<1>(e);
+  den = den + quad_bcast<2>(e);
+  den = den + quad_bcast<3>(e);
+  const double wl = e / den;
+  double w[4];
+  w[0] = quad_bcast<0>(wl);
+  w[1] = quad_bcast<1>(wl);
+  w[2] = quad_bcast<2>(wl);
+  w[3] = quad_bcast<3>(wl);
+  p[0] = w[0] * (double)a[0].x; p[1] = w[0] * (double)a[0].y;
+  p[2] = w[0] * (double)a[0].z; p[3] = w[0] * (double)a[0].w;
+  p[4] = w[0] * (double)c[0].x; p[5] = w[0] * (double)c[0].y;
+  p[6] = w[0] * (double)c[0].z; p[7] = w[0] * (double)c[0].w;
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    p[0] = p[0] + w[j] * (double)a[j].x; p[1] = p[1] + w[j] * (double)a[j].y;
+    p[2] = p[2] + w[j] * (double)a[j].z; p[3] = p[3] + w[j] * (double)a[j].w;
+    p[4] = p[4] + w[j] * (double)c[j].x; p[5] = p[5] + w[j] * (double)c[j].y;
+    p[6] = p[6] + w[j] * (double)c[j].z; p[7] = p[7] + w[j] * (double)c[j].w;
+  }
+}
+
 // MXFP4 (E8M0 per 32): the 4 lanes of a scale group call it together.
 // Returns the 8 packed codes; *sbyte = the scale byte (exponent + 127).
 __device__ inline uint32_t quantize8_e8m0(const double p[8], uint32_t* sbyte) {
@@ -135,34 +186,39 @@ __device__ inline void store_entry(const double p[8], int seg, int64_t row,
 }
 
 // One lane owns 8 consecutive channels of one block; D/8 lanes cover a block
-// row, so a wave holds 64/(D/8) blocks.
-template <int D, int FMT>
+// row, so a wave holds 64/(D/8) blocks. Grid: x over a sequence's blocks,
+// y over sequences. M4: m == 4, full blocks take pool4_quad (D/8 is a
+// multiple of 4, so quads never straddle blocks).
+template <int D, int FMT, bool M4>
 __global__ __launch_bounds__(256) void k_compress_quantize(
     const float* __restrict__ kv, int64_t kv_ld, const float* __restrict__ gate,
-    int64_t n_tok, int m, int64_t nblk, int64_t total, int64_t blk_first,
+    int64_t n_tok, int m, int64_t nblk, int64_t blk_first,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t blk_cap) {
   constexpr int LPB = D / 8;
   constexpr int BPW = 64 / LPB;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t gb = ((int64_t)blockIdx.x * 4 + wave) * BPW + lane / LPB;
-  if (gb >= total) return;  // whole 4-lane groups leave together
-  const int64_t b = gb / nblk;
-  const int64_t bi = gb - b * nblk;
+  const int64_t bi = ((int64_t)blockIdx.x * 4 + wave) * BPW + lane / LPB;
+  if (bi >= nblk) return;  // whole 4-lane groups leave together
+  const int64_t b = blockIdx.y;
   const int64_t j0 = bi * m;
   const int n = (int)((n_tok - j0) < m ? (n_tok - j0) : m);
   const int seg = lane % LPB;
   const float* g = gate + b * n_tok + j0;
   const float* x = kv + (b * n_tok + j0) * kv_ld + seg * 8;
   double p[8];
-  pool8(
-      n, [&](int j) { return g[j]; },
-      [&](int j, float4& a, float4& c) {
-        const float* xj = x + (int64_t)j * kv_ld;
-        a = *reinterpret_cast<const float4*>(xj);
-        c = *reinterpret_cast<const float4*>(xj + 4);
-      },
-      p);
+  if (M4 && n == 4) {
+    pool4_quad(g, x, kv_ld, lane, p);
+  } else {
+    pool8(
+        n, [&](int j) { return g[j]; },
+        [&](int j, float4& a, float4& c) {
+          const float* xj = x + (int64_t)j * kv_ld;
+          a = *reinterpret_cast<const float4*>(xj);
+          c = *reinterpret_cast<const float4*>(xj + 4);
+        },
+        p);
+  }
   store_entry<D, FMT>(p, seg, b * blk_cap + blk_first + bi, codes, scales);
 }
 
@@ -289,26 +345,41 @@ extern "C" int csa_compress_quantize(const float* kv, int64_t kv_ld, const float
   const int64_t blk_first = tok0 / m;
   const int64_t nblk = (n_tok + m - 1) / m;
   if (blk_first + nblk > blk_cap) return CSA_ERR_RANGE;
-  const int64_t total = (int64_t)B * nblk;
   const int bpwg = 4 * (64 / (d / 8));
-  const int64_t grid = (total + bpwg - 1) / bpwg;
+  const int64_t grid = (nblk + bpwg - 1) / bpwg;
   if (grid > 0x7fffffff) return CSA_ERR_SHAPE;
-#define CSA_LAUNCH_COMPRESS1(DD, FF)                                                          \
-  hipLaunchKernelGGL((k_compress_quantize<DD, FF>), dim3((unsigned)grid), dim3(256), 0, stream, \
-                     kv, kv_ld, gate, n_tok, m, nblk, total, blk_first, codes, scales, blk_cap)
+  const int scale_bytes = scale_fmt == CSA_SCALE_E4M3_16 ? d / 16 : d / 32;
+  // sequences go on grid y, at most 65535 per launch
+  for (int b0 = 0; b0 < B; b0 += 65535) {
+    const int nb = B - b0 < 65535 ? B - b0 : 65535;
+    const float* kv_b = kv + (int64_t)b0 * n_tok * kv_ld;
+    const float* gate_b = gate + (int64_t)b0 * n_tok;
+    uint8_t* codes_b = codes + (int64_t)b0 * blk_cap * (d / 2);
+    uint8_t* scales_b = scales + (int64_t)b0 * blk_cap * scale_bytes;
+#define CSA_LAUNCH_COMPRESS2(DD, FF, M4)                                                   \
+  hipLaunchKernelGGL((k_compress_quantize<DD, FF, M4>), dim3((unsigned)grid, (unsigned)nb), \
+                     dim3(256), 0, stream, kv_b, kv_ld, gate_b, n_tok, m, nblk, blk_first,  \
+                     codes_b, scales_b, blk_cap)
+#define CSA_LAUNCH_COMPRESS1(DD, FF)                \
+  do {                                              \
+    if (m == 4) CSA_LAUNCH_COMPRESS2(DD, FF, true); \
+    else CSA_LAUNCH_COMPRESS2(DD, FF, false);       \
+  } while (0)
 #define CSA_LAUNCH_COMPRESS(DD)                                         \
   if (scale_fmt == CSA_SCALE_E4M3_16) CSA_LAUNCH_COMPRESS1(DD, CSA_SCALE_E4M3_16); \
   else CSA_LAUNCH_COMPRESS1(DD, CSA_SCALE_E8M0_32)
-  switch (d) {
-    case 32: CSA_LAUNCH_COMPRESS(32); break;
-    case 64: CSA_LAUNCH_COMPRESS(64); break;
-    case 128: CSA_LAUNCH_COMPRESS(128); break;
-    case 256: CSA_LAUNCH_COMPRESS(256); break;
-    default: CSA_LAUNCH_COMPRESS(512); break;
-  }
+    switch (d) {
+      case 32: CSA_LAUNCH_COMPRESS(32); break;
+      case 64: CSA_LAUNCH_COMPRESS(64); break;
+      case 128: CSA_LAUNCH_COMPRESS(128); break;
+      case 256: CSA_LAUNCH_COMPRESS(256); break;
+      default: CSA_LAUNCH_COMPRESS(512); break;
+    }
 #undef CSA_LAUNCH_COMPRESS
 #undef CSA_LAUNCH_COMPRESS1
-  CSA_TRY_LAUNCH();
+#undef CSA_LAUNCH_COMPRESS2
+    CSA_TRY_LAUNCH();
+  }
   return CSA_OK;
 }
 
