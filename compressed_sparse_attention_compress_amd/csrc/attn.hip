@@ -564,15 +564,22 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       // P^T operands of the four 16-slot k-steps: element e of lane
       // (i + 32 gg) in k-step ks = 2 et + s is slot 32 et + 16 s + 8 (e / 4) +
       // 4 gg + e % 4, head i (logit registers 8 s .. 8 s + 7 of tile et)
-      v8h P[4];
+      // p goes into the product as two float16 terms, p = ph + pl with pl the
+      // float16 rounding of p - ph (exact in float32), so each weight carries
+      // about 22 significant bits: one float16 term alone moves up to 2^-11 of
+      // a weight between value rows, which for a query with a few slots of
+      // large, different values exceeds the output tolerance.
+      v8h P[4], Pl[4];
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
         // hardware exp2 (results below 2^-126 flush to 0, far under the
-        // float16 probabilities' resolution)
+        // weights' resolution)
         const float pv = none ? 0.f : __builtin_amdgcn_exp2f(x[r] - m_run);
+        const _Float16 ph = (_Float16)pv;
+        P[r >> 3][r & 7] = ph;
+        Pl[r >> 3][r & 7] = (_Float16)(pv - (float)ph);
         psum += pv;
-        P[r >> 3][r & 7] = (_Float16)pv;
       }
       l_run += psum;
       // O^T[channel][head] += V^T P^T over the 64 slots, for this wave's half
@@ -595,6 +602,7 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
           const v4h hi = lds_read_tr(vp + 8 * RS);
           const v8h A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, P[ks], O[ct], 0, 0, 0);
+          O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Pl[ks], O[ct], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }

@@ -4,8 +4,9 @@ benchmark uses, against the CPU oracle on sampled outputs.
 * decode_32k: 64 sequences x 32,768 tokens; every query checked.
 * decode_1m: 8 sequences x 1,048,576 tokens; every query checked.
 * prefill_128k: one 131,072-token sequence in 16 chunks of 8192 queries;
-  all cache bytes checked, and a sample of queries per chunk (first 32, last
-  32 and 32 seeded-random positions).
+  all cache bytes checked, and the top-k and output of the first and last 256
+  queries of every chunk plus 4096 seeded-random positions (about 12,000 of
+  the 131,072 queries), run through the oracle on a pool of host workers.
 * hca_reindex_1m: 16 sequences x 1,048,576 tokens; HCA layer (m=128, dense)
   and three CSA2 layers sharing one m=4 cache: a Full layer (top-4096 pool
   then its own top-512) and two Reindex layers rescoring the pool; every
@@ -23,6 +24,7 @@ import torch
 
 import compressed_sparse_attention_compress_amd as csa
 import oracle.csa_oracle as O
+from oracle.pool import HostArrays, query_job
 import synth
 from parity_util import REL_TOL, attn_excess_error, bf16_bits
 
@@ -108,7 +110,7 @@ def test_decode_workload(name):
     check_attn(q, codes, scales, idx, win, wl.W, wl.L - 1, out)
 
 
-def test_prefill_workload():
+def test_prefill_workload(oracle_pool):
     wl = synth.WORKLOADS["prefill_128k"]
     say("workload prefill_128k")
     cap = wl.n_blocks
@@ -116,31 +118,55 @@ def test_prefill_workload():
     scales = torch.empty(1, cap, wl.d // 32, device=DEV, dtype=torch.uint8)
     keys = synth.indexer_keys(wl, DEV)
     win = torch.zeros(1, wl.Wcap, wl.d, device=DEV, dtype=torch.bfloat16)
-    rng = np.random.default_rng(0)
     T = wl.chunk
-    for c in range(wl.L // T):
-        t0 = c * T
-        kv = synth.latent_chunk(wl, 0, c, DEV)[None].contiguous()
-        gate = synth.gate_chunk(wl, 0, c, DEV)[None].contiguous()
-        csa.compress_quantize(kv, gate, t0, wl.m, codes, scales)
-        pos = torch.arange(t0, t0 + T, device=DEV) % wl.Wcap
-        win[0, pos] = kv[0].to(torch.bfloat16)
-        q_idx, w = synth.indexer_queries(wl, DEV, layer=f"chunk{c}")
-        q = synth.queries(wl, DEV, layer=f"chunk{c}")
-        idx = torch.empty(1, T, wl.k, device=DEV, dtype=torch.int32)
-        out = torch.empty(1, T, wl.H, wl.d, device=DEV, dtype=torch.bfloat16)
-        csa.index_topk(q_idx, w, keys, wl.m, t0, wl.k, idx)
-        csa.sparse_attn(q, codes, scales, idx, win, wl.W, t0, 1.0, out)
-        torch.cuda.synchronize()
-        rc, rs = O.compress_quantize(kv[0].cpu().numpy(), gate[0].cpu().numpy(), wl.m)
-        assert np.array_equal(codes[0, t0 // 4:(t0 + T) // 4].cpu().numpy(), rc), c
-        assert np.array_equal(scales[0, t0 // 4:(t0 + T) // 4].cpu().numpy(), rs), c
-        ts = sorted(set(list(range(32)) + list(range(T - 32, T)) +
-                        list(rng.choice(T, 32, replace=False))))
-        rows = [(0, t) for t in ts]
-        say(f"  chunk {c}: checking {len(rows)} queries")
-        check_topk(q_idx, w, keys, wl.m, t0, wl.k, idx, rows=rows)
-        check_attn(q, codes, scales, idx, win, wl.W, t0, out, rows=rows)
+    nch = wl.L // T
+    rand = np.random.default_rng(0).choice(wl.L, 4096, replace=False)
+    jobs, got = [], []
+    with HostArrays() as host:
+        for c in range(nch):
+            t0 = c * T
+            kv = synth.latent_chunk(wl, 0, c, DEV)[None].contiguous()
+            gate = synth.gate_chunk(wl, 0, c, DEV)[None].contiguous()
+            csa.compress_quantize(kv, gate, t0, wl.m, codes, scales)
+            pos = torch.arange(t0, t0 + T, device=DEV) % wl.Wcap
+            win[0, pos] = kv[0].to(torch.bfloat16)
+            q_idx, w = synth.indexer_queries(wl, DEV, layer=f"chunk{c}")
+            q = synth.queries(wl, DEV, layer=f"chunk{c}")
+            idx = torch.empty(1, T, wl.k, device=DEV, dtype=torch.int32)
+            out = torch.empty(1, T, wl.H, wl.d, device=DEV, dtype=torch.bfloat16)
+            csa.index_topk(q_idx, w, keys, wl.m, t0, wl.k, idx)
+            csa.sparse_attn(q, codes, scales, idx, win, wl.W, t0, 1.0, out)
+            torch.cuda.synchronize()
+            rc, rs = O.compress_quantize(kv[0].cpu().numpy(), gate[0].cpu().numpy(), wl.m)
+            assert np.array_equal(codes[0, t0 // 4:(t0 + T) // 4].cpu().numpy(), rc), c
+            assert np.array_equal(scales[0, t0 // 4:(t0 + T) // 4].cpu().numpy(), rs), c
+            # first and last 256 queries of the chunk, and the chunk's share
+            # of 4096 seeded-random positions over the whole sequence
+            ts = sorted(set(range(256)) | set(range(T - 256, T)) |
+                        {int(t) - t0 for t in rand if t0 <= t < t0 + T})
+            sel = torch.tensor(ts, device=DEV)
+            wref = host.put(f"win{c}", bf16_bits(win[0]))
+            qi, wn = q_idx[0, sel].cpu().numpy(), w[0, sel].cpu().numpy()
+            qb = bf16_bits(q[0, sel])
+            for r, ti in enumerate(ts):
+                jobs.append(dict(b=0, q_idx=qi[r], w=wn[r], q=qb[r], win=wref, m=wl.m,
+                                 t=t0 + ti, k=wl.k, Wcap=wl.Wcap, W=wl.W, fmt="e8m0"))
+            got.append((c, ts, idx[0, sel].cpu().numpy(), out[0, sel].float().cpu().numpy()))
+            say(f"  chunk {c}: cache bytes exact; {len(ts)} queries sampled")
+        shared = dict(keys=host.put("keys", keys.cpu().numpy()),
+                      codes=host.put("codes", codes.cpu().numpy()),
+                      scales=host.put("scales", scales.cpu().numpy()))
+        say(f"  oracle on {len(jobs)} queries over {oracle_pool.n} workers")
+        res = oracle_pool.map(query_job, [dict(j, **shared) for j in jobs])
+    n = 0
+    for c, ts, gi, go in got:
+        ref = res[n:n + len(ts)]
+        n += len(ts)
+        for r, ti in enumerate(ts):
+            assert np.array_equal(gi[r], ref[r][0][0]), (c, ti)
+        ex, _ = attn_excess_error(go, np.stack([o for (_, o), _ in ref]), True)
+        say(f"  chunk {c}: top-k exact on {len(ts)} queries; attention excess / rms = {ex:.3e}")
+        assert ex <= REL_TOL, (c, ex)
 
 
 def test_hca_reindex_workload():
