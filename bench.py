@@ -13,7 +13,8 @@ and replays those, measured slower than eager launches on this path).
 Other workloads (--workload), each printing its own line:
   decode_32k      64 sequences at 32,768 tokens, top-512 (same step).
   prefill_128k    one 131,072-token sequence in 16 chunks of 8192 queries:
-                  per chunk compress + index + attention; one step = all 16.
+                  one compress launch over the prompt, then per chunk index +
+                  attention; one step = the compress and all 16 chunks.
   hca_reindex_1m  16 sequences at 1M tokens, one decode query each through
                   four layers: HCA (m=128, dense), a CSA Full layer (top-4096
                   pool, then its own top-512) and two Reindex layers scoring
@@ -259,43 +260,59 @@ def timed_runs(args, csa, steps):
 
 
 # --------------------------------------------------------------------------
+# cpu_baseline: the oracle over a pool of single-thread worker processes
+# --------------------------------------------------------------------------
+
+# oracle.pool.OraclePool, forked in main() before torch, the HIP library or
+# the GPU are touched (so its workers hold no GPU state); None: no baseline
+ORACLE_POOL = None
+
+
+def pool_run(fn, jobs, min_seconds):
+    return ORACLE_POOL.timed(fn, jobs, min_seconds)
+
+
+def pool_record(rate, unit, n_timed, wall, per_job, sample):
+    from oracle.pool import cpu_model
+    n = ORACLE_POOL.n
+    return dict(value=rate, unit=unit, cores=n, kind="oracle",
+                sample=f"{sample}; {n_timed} jobs over {n} worker processes of one thread each "
+                       f"(numpy fp64/int64), {per_job:.3f} s per job",
+                cpu_model=cpu_model(), seconds=round(wall, 3))
+
+
+# --------------------------------------------------------------------------
 # decode (decode_1m, decode_32k)
 # --------------------------------------------------------------------------
 
 def cpu_baseline_decode(s, wl, n_queries, min_seconds):
     """The oracle on the first n_queries queries of input set s (index + top-k
-    + attention each), one thread, repeated until min_seconds of oracle time
-    have passed; the first pass also checks the device results."""
+    + attention each) over the worker pool; the first pass is checked against
+    the device results."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import oracle.csa_oracle as O
-    keys = s["keys"].cpu().numpy()
-    q_idx, w = s["q_idx"].cpu().numpy(), s["w"].cpu().numpy()
-    qb, win = host_bits(s["q"]), host_bits(s["win"])
+    from oracle.pool import HostArrays, query_job
+    h = HostArrays()
+    try:
+        shared = dict(keys=h.put("keys", s["keys"][:n_queries].cpu().numpy()),
+                      codes=h.put("codes", s["codes"][:n_queries].cpu().numpy()),
+                      scales=h.put("scales", s["scales"][:n_queries].cpu().numpy()))
+        q_idx, w = s["q_idx"].cpu().numpy(), s["w"].cpu().numpy()
+        qb, win = host_bits(s["q"]), h.put("win", host_bits(s["win"])[:n_queries])
+        jobs = [dict(shared, b=b, q_idx=q_idx[b, 0], w=w[b, 0], q=qb[b, 0], win=win, m=wl.m,
+                     t=wl.L - 1, k=wl.k, Wcap=wl.Wcap, W=wl.W, fmt=FMT)
+                for b in range(n_queries)]
+        first, rate, n_timed, wall, per_job = pool_run(query_job, jobs, min_seconds)
+    finally:
+        h.close()
     gpu_idx = s["idx"].cpu().numpy()
     gpu_out = s["out"].cpu().float().numpy()
-    t_total, worst, idx_ok, done = 0.0, 0.0, True, 0
-    codes = [s["codes"][b].cpu().numpy() for b in range(n_queries)]
-    scales = [s["scales"][b].cpu().numpy() for b in range(n_queries)]
-    with threadpool_limits(limits=1):
-        while done == 0 or t_total < min_seconds:
-            for b in range(n_queries):
-                t0 = time.perf_counter()
-                ri, _ = O.index_topk(q_idx[b, 0], w[b, 0], keys[b], wl.m, wl.L - 1, wl.k)
-                ro, _ = O.sparse_attn(qb[b, 0], codes[b], scales[b], ri, win[b], wl.Wcap, wl.W,
-                                      wl.L - 1, 1.0, fmt=FMT)
-                t_total += time.perf_counter() - t0
-                if done < n_queries:
-                    idx_ok &= bool(np.array_equal(ri, gpu_idx[b, 0]))
-                    worst = max(worst, bf16_excess(gpu_out[b, 0], ro))
-                done += 1
+    idx_ok = all(bool(np.array_equal(ri, gpu_idx[b, 0])) for b, (ri, _) in enumerate(first))
+    worst = max(bf16_excess(gpu_out[b, 0], ro) for b, (_, ro) in enumerate(first))
     nv = wl.L // wl.m
-    return dict(value=done / t_total, unit="queries/s", cores=1, kind="oracle",
-                sample=f"{n_queries} of the {wl.B} decode queries of one step (full {nv:,}-entry "
-                       f"index scan + top-{wl.k} + attention each), run {done // n_queries} "
-                       "times over, numpy fp64/int64, 1 thread",
-                seconds=round(t_total, 3)), dict(topk_exact=idx_ok, attn_excess_over_rms=worst)
+    return pool_record(rate, "queries/s", n_timed, wall, per_job,
+                       f"{n_queries} of the {wl.B} decode queries of one step (full {nv:,}-entry "
+                       f"index scan + top-{wl.k} + attention each)"), \
+        dict(topk_exact=idx_ok, attn_excess_over_rms=worst)
 
 
 def run_decode(args, csa, synth, wl, dev):
@@ -350,7 +367,8 @@ def run_decode(args, csa, synth, wl, dev):
         torch.cuda.synchronize()
         cpu, parity = cpu_baseline_decode(sets[0], wl, min(args.cpu_queries, wl.B),
                                           args.cpu_seconds)
-        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
+        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['cores']} workers, "
+            f"{cpu['seconds']} s; parity {parity}")
 
     return {
         "metric": METRIC if wl.name == "decode_1m" else
@@ -419,20 +437,14 @@ def ragged_set(csa, synth, wl, dev, seed):
 
 def cpu_baseline_ragged(s, wl, n_queries, min_seconds):
     """The oracle on the first n_queries sequences of a ragged step (index +
-    top-k + attention at each sequence's own position), one thread, repeated
-    until min_seconds of oracle time have passed; the first pass also checks
-    the device results, and the entries the step's append completed against
-    the oracle's compression of those blocks' tokens."""
+    top-k + attention at each sequence's own position) over the worker pool;
+    the first pass is checked against the device results, and the entries the
+    step's append completed against the oracle's compression of those blocks'
+    tokens."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     import oracle.csa_oracle as O
     import synth
-    keys = s["keys"].cpu().numpy()
-    q_idx, w = s["q_idx"].cpu().numpy(), s["w"].cpu().numpy()
-    qb, win = host_bits(s["q"]), host_bits(s["win"])
-    gpu_idx = s["idx"].cpu().numpy()
-    gpu_out = s["out"].cpu().float().numpy()
     pos = s["pos_list"]
     ok = True
     for b, t in enumerate(pos):  # appended entries
@@ -445,28 +457,29 @@ def cpu_baseline_ragged(s, wl, n_queries, min_seconds):
             blk = t // wl.m
             ok &= bool(np.array_equal(s["codes"][b, blk].cpu().numpy(), rc[0]))
             ok &= bool(np.array_equal(s["scales"][b, blk].cpu().numpy(), rs[0]))
-    t_total, worst, done = 0.0, 0.0, 0
-    codes = [s["codes"][b].cpu().numpy() for b in range(n_queries)]
-    scales = [s["scales"][b].cpu().numpy() for b in range(n_queries)]
-    with threadpool_limits(limits=1):
-        while done == 0 or t_total < min_seconds:
-            for b in range(n_queries):
-                t = pos[b]
-                t0 = time.perf_counter()
-                ri, _ = O.index_topk(q_idx[b, 0], w[b, 0], keys[b], wl.m, t, wl.k)
-                ro, _ = O.sparse_attn(qb[b, 0], codes[b], scales[b], ri, win[b], wl.Wcap, wl.W,
-                                      t, 1.0, fmt=FMT)
-                t_total += time.perf_counter() - t0
-                if done < n_queries:
-                    ok &= bool(np.array_equal(ri, gpu_idx[b, 0]))
-                    worst = max(worst, bf16_excess(gpu_out[b, 0], ro))
-                done += 1
-    return dict(value=done / t_total, unit="queries/s", cores=1, kind="oracle",
-                sample=f"{n_queries} of the {wl.B} decode queries of one ragged step (index "
-                       f"scans of {pos[n_queries - 1] // wl.m:,}-{pos[0] // wl.m:,} entries + "
-                       f"top-{wl.k} + attention each), run {done // n_queries} times over, "
-                       "numpy fp64/int64, 1 thread",
-                seconds=round(t_total, 3)), dict(exact=ok, attn_excess_over_rms=worst)
+    from oracle.pool import HostArrays, query_job
+    h = HostArrays()
+    try:
+        shared = dict(keys=h.put("keys", s["keys"][:n_queries].cpu().numpy()),
+                      codes=h.put("codes", s["codes"][:n_queries].cpu().numpy()),
+                      scales=h.put("scales", s["scales"][:n_queries].cpu().numpy()))
+        q_idx, w = s["q_idx"].cpu().numpy(), s["w"].cpu().numpy()
+        qb, win = host_bits(s["q"]), h.put("win", host_bits(s["win"])[:n_queries])
+        jobs = [dict(shared, b=b, q_idx=q_idx[b, 0], w=w[b, 0], q=qb[b, 0], win=win, m=wl.m,
+                     t=pos[b], k=wl.k, Wcap=wl.Wcap, W=wl.W, fmt=FMT)
+                for b in range(n_queries)]
+        first, rate, n_timed, wall, per_job = pool_run(query_job, jobs, min_seconds)
+    finally:
+        h.close()
+    gpu_idx = s["idx"].cpu().numpy()
+    gpu_out = s["out"].cpu().float().numpy()
+    ok &= all(bool(np.array_equal(ri, gpu_idx[b, 0])) for b, (ri, _) in enumerate(first))
+    worst = max(bf16_excess(gpu_out[b, 0], ro) for b, (_, ro) in enumerate(first))
+    lo, hi = min(pos[:n_queries]) // wl.m, max(pos[:n_queries]) // wl.m
+    return pool_record(rate, "queries/s", n_timed, wall, per_job,
+                       f"{n_queries} of the {wl.B} decode queries of one ragged step (index "
+                       f"scans of {lo:,}-{hi:,} entries + top-{wl.k} + attention each)"), \
+        dict(exact=ok, attn_excess_over_rms=worst)
 
 
 def run_decode_ragged(args, csa, synth, wl, dev):
@@ -522,7 +535,8 @@ def run_decode_ragged(args, csa, synth, wl, dev):
         torch.cuda.synchronize()
         cpu, parity = cpu_baseline_ragged(sets[0], wl, min(args.cpu_queries, wl.B),
                                           args.cpu_seconds)
-        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
+        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['cores']} workers, "
+            f"{cpu['seconds']} s; parity {parity}")
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     return {
         "metric": "CSA ragged decode queries/sec (append + index + attention) at 590K-1M ctx, "
@@ -580,37 +594,31 @@ def prefill_work(wl):
 
 def cpu_baseline_prefill(wl, x, keys, codes, scales, c, n_queries, min_seconds):
     """The oracle on the last n_queries queries of chunk c (index + top-k +
-    attention each), one thread, repeated until min_seconds of oracle time
-    have passed; the first pass is checked against the device results."""
+    attention each) over the worker pool; the first pass is checked against
+    the device results."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import oracle.csa_oracle as O
     T = wl.chunk
-    kn = keys[0].cpu().numpy()
-    cn, sn = codes[0].cpu().numpy(), scales[0].cpu().numpy()
-    qi, wn = x["q_idx"][0].cpu().numpy(), x["w"][0].cpu().numpy()
-    qb, win = host_bits(x["q"])[0], host_bits(x["win"])[0]
+    from oracle.pool import HostArrays, query_job
+    h = HostArrays()
+    try:
+        shared = dict(keys=h.put("keys", keys[:1].cpu().numpy()),
+                      codes=h.put("codes", codes[:1].cpu().numpy()),
+                      scales=h.put("scales", scales[:1].cpu().numpy()))
+        qi, wn = x["q_idx"][0].cpu().numpy(), x["w"][0].cpu().numpy()
+        qb, win = host_bits(x["q"])[0], h.put("win", host_bits(x["win"])[0])
+        tis = list(range(T - n_queries, T))
+        jobs = [dict(shared, b=0, q_idx=qi[ti], w=wn[ti], q=qb[ti], win=win, m=wl.m,
+                     t=c * T + ti, k=wl.k, Wcap=wl.Wcap, W=wl.W, fmt=FMT) for ti in tis]
+        first, rate, n_timed, wall, per_job = pool_run(query_job, jobs, min_seconds)
+    finally:
+        h.close()
     gi = x["idx"][0].cpu().numpy()
     go = x["out"][0].cpu().float().numpy()
-    t_total, worst, ok, done = 0.0, 0.0, True, 0
-    with threadpool_limits(limits=1):
-        while done == 0 or t_total < min_seconds:
-            for ti in range(T - n_queries, T):
-                t = c * T + ti
-                t0 = time.perf_counter()
-                ri, _ = O.index_topk(qi[ti], wn[ti], kn, wl.m, t, wl.k)
-                ro, _ = O.sparse_attn(qb[ti], cn, sn, ri, win, wl.Wcap, wl.W, t, 1.0, fmt=FMT)
-                t_total += time.perf_counter() - t0
-                if done < n_queries:
-                    ok &= bool(np.array_equal(ri, gi[ti]))
-                    worst = max(worst, bf16_excess(go[ti], ro))
-                done += 1
-    return dict(value=done / t_total, unit="queries/s", cores=1, kind="oracle",
-                sample=f"last {n_queries} queries of the last {T}-query chunk (index over "
-                       f"{(c + 1) * T // wl.m:,} blocks + top-{wl.k} + attention each), run "
-                       f"{done // n_queries} times over, numpy fp64/int64, 1 thread",
-                seconds=round(t_total, 3)), \
+    ok = all(bool(np.array_equal(ri, gi[ti])) for ti, (ri, _) in zip(tis, first))
+    worst = max(bf16_excess(go[ti], ro) for ti, (_, ro) in zip(tis, first))
+    return pool_record(rate, "queries/s", n_timed, wall, per_job,
+                       f"last {n_queries} queries of the last {T}-query chunk (index over "
+                       f"{(c + 1) * T // wl.m:,} blocks + top-{wl.k} + attention each)"), \
         dict(topk_exact=ok, attn_excess_over_rms=worst)
 
 
@@ -622,12 +630,13 @@ def run_prefill(args, csa, synth, wl, dev):
     codes = torch.empty(1, wl.n_blocks, wl.d // 2, device=dev, dtype=torch.uint8)
     scales = torch.empty(1, wl.n_blocks, wl.d // SCALE_GROUP[FMT], device=dev, dtype=torch.uint8)
     keys = synth.indexer_keys(wl, dev)
+    # the prompt's latents and gate logits, [1][L][d] and [1][L]
+    kv = torch.cat([synth.latent_chunk(wl, 0, c, dev) for c in range(nch)])[None].contiguous()
+    gate = torch.cat([synth.gate_chunk(wl, 0, c, dev) for c in range(nch)])[None].contiguous()
     ch = []
     for c in range(nch):
         q_idx, w = synth.indexer_queries(wl, dev, layer=f"chunk{c}")
         ch.append(dict(
-            kv=synth.latent_chunk(wl, 0, c, dev)[None].contiguous(),
-            gate=synth.gate_chunk(wl, 0, c, dev)[None].contiguous(),
             q_idx=q_idx, w=w, q=synth.queries(wl, dev, layer=f"chunk{c}"),
             win=synth.window_ring(wl, (c + 1) * T - 1, dev),
             idx=torch.empty(1, T, wl.k, device=dev, dtype=torch.int32),
@@ -636,9 +645,8 @@ def run_prefill(args, csa, synth, wl, dev):
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s: {nch} chunks of {T} queries")
 
-    def compress(c):
-        x = ch[c]
-        csa.compress_quantize(x["kv"], x["gate"], c * T, wl.m, codes, scales, fmt=FMT)
+    def compress():
+        csa.compress_quantize(kv, gate, 0, wl.m, codes, scales, fmt=FMT)
 
     def index(c):
         x = ch[c]
@@ -650,8 +658,8 @@ def run_prefill(args, csa, synth, wl, dev):
                         fmt=FMT)
 
     def step():
+        compress()
         for c in range(nch):
-            compress(c)
             index(c)
             attend(c)
 
@@ -665,19 +673,23 @@ def run_prefill(args, csa, synth, wl, dev):
 
     # per-kernel device times (eager, events), one pass over the chunks
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nch)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nch)]
+    reps = 10
+    e_cmp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e_cmp[0].record(stream)
+    for _ in range(reps):
+        compress()
+    e_cmp[1].record(stream)
     for c in range(nch):
         ev[c][0].record(stream)
-        compress(c)
-        ev[c][1].record(stream)
         index(c)
-        ev[c][2].record(stream)
+        ev[c][1].record(stream)
         attend(c)
-        ev[c][3].record(stream)
+        ev[c][2].record(stream)
     torch.cuda.synchronize()
-    t_cmp = sum(ev[c][0].elapsed_time(ev[c][1]) for c in range(nch))
-    t_idx = sum(ev[c][1].elapsed_time(ev[c][2]) for c in range(nch))
-    t_att = sum(ev[c][2].elapsed_time(ev[c][3]) for c in range(nch))
+    t_cmp = e_cmp[0].elapsed_time(e_cmp[1]) / reps
+    t_idx = sum(ev[c][0].elapsed_time(ev[c][1]) for c in range(nch))
+    t_att = sum(ev[c][1].elapsed_time(ev[c][2]) for c in range(nch))
     att, ind = prefill_work(wl)
     att_tf = sum(att) / (t_att * 1e-3) / 1e12
     ind_tops = sum(ind) / (t_idx * 1e-3) / 1e12
@@ -690,7 +702,8 @@ def run_prefill(args, csa, synth, wl, dev):
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline_prefill(wl, ch[-1], keys, codes, scales, nch - 1,
                                            args.cpu_queries, args.cpu_seconds)
-        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
+        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['cores']} workers, "
+            f"{cpu['seconds']} s; parity {parity}")
 
     return {
         "metric": "CSA prefill tokens/sec at 128K ctx (16 chunks of 8192) + MFMA utilisation, "
@@ -712,9 +725,12 @@ def run_prefill(args, csa, synth, wl, dev):
         "indexer": {"bound": "mfma", "achieved": round(ind_tops, 1), "peak": INT8_PEAK_TOPS,
                     "unit": "TOP/s", "frac": round(ind_tops / INT8_PEAK_TOPS, 4),
                     "int8_ops_per_step": sum(ind)},
-        "compress": {"bound": "hbm", "achieved": round(cmp_gbs, 1), "peak": HBM_PEAK_GBS,
+        "compress": {"kernel": "k_compress_quantize (the prompt's 131,072 tokens, one launch)",
+                     "bound": "hbm", "achieved": round(cmp_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(cmp_gbs / HBM_PEAK_GBS, 4),
-                     "bytes_per_step": cmp_bytes},
+                     "traffic": measured_traffic("k_compress_quantize", wl.name),
+                     "avg_launch_us": round(t_cmp * 1e3, 2),
+                     "algorithmic_bytes_per_launch": cmp_bytes},
         "roofline": {
             "kernel": "k_attn (sparse attention, one workgroup per query)",
             "bound": "mfma",
@@ -765,64 +781,42 @@ def layers_set(csa, synth, wl, dev, seed, pool_len, n_reuse):
 
 
 def cpu_baseline_layers(s, wl, n_queries, n_groups, min_seconds):
-    """The oracle on the first n_queries sequences through all four layers,
-    one thread, repeated until min_seconds of oracle time have passed; the
-    first pass is checked against the device results. n_groups > 0: the Full
-    layer keeps a blockwise pool of n_groups 8-entry groups and attends its
-    own top-k; else its pool is its top-`pool` entries, rescored to top-k."""
+    """The oracle on the first n_queries sequences through all layers over the
+    worker pool; the first pass is checked against the device results.
+    n_groups > 0: the Full layer keeps a blockwise pool of n_groups 8-entry
+    groups and attends its own top-k; else its pool is its top-`pool`
+    entries, rescored to top-k."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import oracle.csa_oracle as O
     t = wl.L - 1
-    keys = s["keys"].cpu().numpy()
-    win, h_win = host_bits(s["win"]), host_bits(s["h_win"])
-    host = []
-    for b in range(n_queries):
-        host.append(dict(
-            cn=s["codes"][b].cpu().numpy(), sn=s["scales"][b].cpu().numpy(),
-            hc=s["h_codes"][b].cpu().numpy(), hs=s["h_scales"][b].cpu().numpy(),
-            hq=host_bits(s["h_q"])[b, 0],
-            qs={layer: (s[layer]["q_idx"][b, 0].cpu().numpy(), s[layer]["w"][b, 0].cpu().numpy(),
-                        host_bits(s[layer]["q"])[b, 0]) for layer in LAYERS},
-            rq=[host_bits(r["q"])[b, 0] for r in s["reuse"]]))
-    t_total, worst, ok, done = 0.0, 0.0, True, 0
-    with threadpool_limits(limits=1):
-        while done == 0 or t_total < min_seconds:
-            for b in range(n_queries):
-                h = host[b]
-                qs = h["qs"]
-                t0 = time.perf_counter()
-                ho, _ = O.hca_dense_attn(h["hq"], h["hc"], h["hs"], wl.m_hca, h_win[b], wl.Wcap,
-                                         wl.W, t, 1.0, fmt=FMT)
-                if n_groups:
-                    pool = O.block_pool(qs["full"][0], qs["full"][1], keys[b], wl.m, t, 8,
-                                        n_groups)
-                else:
-                    pool, _ = O.index_topk(qs["full"][0], qs["full"][1], keys[b], wl.m, t,
-                                           wl.pool)
-                outs = {}
-                for layer in LAYERS:
-                    qi, wi, qb = qs[layer]
-                    cand = None if (n_groups and layer == "full") else pool
-                    ri, _ = O.index_topk(qi, wi, keys[b], wl.m, t, wl.k, cand=cand)
-                    ro, _ = O.sparse_attn(qb, h["cn"], h["sn"], ri, win[b], wl.Wcap, wl.W, t,
-                                          1.0, fmt=FMT)
-                    outs[layer] = (ri, ro)
-                reuse_o = [O.sparse_attn(rq, h["cn"], h["sn"], outs["full"][0], win[b], wl.Wcap,
-                                         wl.W, t, 1.0, fmt=FMT)[0] for rq in h["rq"]]
-                t_total += time.perf_counter() - t0
-                if done < n_queries:
-                    ok &= bool(np.array_equal(pool, s["pool"][b, 0].cpu().numpy()))
-                    worst = max(worst, bf16_excess(s["h_out"][b, 0].cpu().float().numpy(), ho))
-                    for layer in LAYERS:
-                        ri, ro = outs[layer]
-                        ok &= bool(np.array_equal(ri, s[layer]["idx"][b, 0].cpu().numpy()))
-                        worst = max(worst, bf16_excess(s[layer]["out"][b, 0].cpu().float().numpy(),
-                                                       ro))
-                    for r, ro in zip(s["reuse"], reuse_o):
-                        worst = max(worst, bf16_excess(r["out"][b, 0].cpu().float().numpy(), ro))
-                done += 1
+    from oracle.pool import HostArrays, layers_job
+    h = HostArrays()
+    try:
+        shared = {name: h.put(name, s[name][:n_queries].cpu().numpy())
+                  for name in ("keys", "codes", "scales", "h_codes", "h_scales")}
+        shared["win"] = h.put("win", host_bits(s["win"])[:n_queries])
+        shared["h_win"] = h.put("h_win", host_bits(s["h_win"])[:n_queries])
+        jobs = []
+        for b in range(n_queries):
+            qs = {layer: (s[layer]["q_idx"][b, 0].cpu().numpy(),
+                          s[layer]["w"][b, 0].cpu().numpy(), host_bits(s[layer]["q"])[b, 0])
+                  for layer in LAYERS}
+            jobs.append(dict(shared, b=b, t=t, m=wl.m, k=wl.k, m_hca=wl.m_hca, pool=wl.pool,
+                             n_groups=n_groups, Wcap=wl.Wcap, W=wl.W, fmt=FMT,
+                             hq=host_bits(s["h_q"])[b, 0], qs=qs,
+                             rq=[host_bits(r["q"])[b, 0] for r in s["reuse"]]))
+        first, rate, n_timed, wall, per_job = pool_run(layers_job, jobs, min_seconds)
+    finally:
+        h.close()
+    ok, worst = True, 0.0
+    for b, (ho, pool, outs, reuse_o) in enumerate(first):
+        ok &= bool(np.array_equal(pool, s["pool"][b, 0].cpu().numpy()))
+        worst = max(worst, bf16_excess(s["h_out"][b, 0].cpu().float().numpy(), ho))
+        for layer in LAYERS:
+            ri, ro = outs[layer]
+            ok &= bool(np.array_equal(ri, s[layer]["idx"][b, 0].cpu().numpy()))
+            worst = max(worst, bf16_excess(s[layer]["out"][b, 0].cpu().float().numpy(), ro))
+        for r, ro in zip(s["reuse"], reuse_o):
+            worst = max(worst, bf16_excess(r["out"][b, 0].cpu().float().numpy(), ro))
     pool_txt = (f"top-{wl.k} + blockwise pool of {n_groups} 8-entry groups over "
                 f"{wl.L // wl.m:,} blocks, two top-{wl.k} rescorings of the pool"
                 if n_groups else
@@ -830,11 +824,10 @@ def cpu_baseline_layers(s, wl, n_queries, n_groups, min_seconds):
                 "rescorings of the pool")
     reuse_txt = (f", {len(s['reuse'])} Reuse layers attending the Full layer's top-{wl.k}"
                  if s["reuse"] else "")
-    return dict(value=done / t_total, unit="queries/s", cores=1, kind="oracle",
-                sample=f"{n_queries} of the {wl.B} sequences through all layers (HCA dense "
-                       f"over {wl.L // wl.m_hca:,} entries, {pool_txt} + attention{reuse_txt}), run "
-                       f"{done // n_queries} times over, numpy fp64/int64, 1 thread",
-                seconds=round(t_total, 3)), dict(topk_exact=ok, attn_excess_over_rms=worst)
+    return pool_record(rate, "queries/s", n_timed, wall, per_job,
+                       f"{n_queries} of the {wl.B} sequences through all layers (HCA dense "
+                       f"over {wl.L // wl.m_hca:,} entries, {pool_txt} + attention{reuse_txt})"), \
+        dict(topk_exact=ok, attn_excess_over_rms=worst)
 
 
 def run_layers(args, csa, synth, wl, dev):
@@ -943,9 +936,10 @@ def run_layers(args, csa, synth, wl, dev):
     if not args.no_cpu_baseline:
         eager[0]()
         torch.cuda.synchronize()
-        cpu, parity = cpu_baseline_layers(sets[0], wl, min(args.cpu_queries, 2), n_groups,
+        cpu, parity = cpu_baseline_layers(sets[0], wl, min(args.cpu_queries, wl.B), n_groups,
                                           args.cpu_seconds)
-        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['seconds']} s; parity {parity}")
+        log(f"cpu baseline {cpu['value']:.3f} queries/s over {cpu['cores']} workers, "
+            f"{cpu['seconds']} s; parity {parity}")
 
     return {
         "metric": ("CSA2 four-layer decode queries/sec (HCA + Full + 2 Reindex) at 1M ctx, "
@@ -1015,9 +1009,10 @@ def main():
                     help="groups kept by the blockwise pool (default: pool / 8)")
     ap.add_argument("--fmt", default="e8m0", choices=["e8m0", "e4m3"],
                     help="FP4 cache scales: E8M0 per 32 channels (MXFP4) or E4M3 per 16")
-    ap.add_argument("--cpu-queries", type=int, default=8)
+    ap.add_argument("--cpu-queries", type=int, default=16,
+                    help="queries (sequences for hca_reindex_1m) in the cpu_baseline sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="oracle time the cpu_baseline sample is repeated up to")
+                    help="wall time the cpu_baseline sample is repeated for over its workers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--python-launch", action="store_true",
                     help="time the Python wrappers instead of pre-marshalled calls")
@@ -1041,6 +1036,10 @@ def main():
         sys.exit(2)
     if args.steps < 1:
         ap.error("--steps must be at least 1")
+    global ORACLE_POOL
+    if not args.no_cpu_baseline:
+        from oracle.pool import OraclePool
+        ORACLE_POOL = OraclePool()
 
     import torch
 
@@ -1050,14 +1049,18 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
-    if args.workload == "prefill_128k":
-        rec = run_prefill(args, csa, synth, wl, dev)
-    elif args.workload == "hca_reindex_1m":
-        rec = run_layers(args, csa, synth, wl, dev)
-    elif args.workload == "decode_ragged_1m":
-        rec = run_decode_ragged(args, csa, synth, wl, dev)
-    else:
-        rec = run_decode(args, csa, synth, wl, dev)
+    try:
+        if args.workload == "prefill_128k":
+            rec = run_prefill(args, csa, synth, wl, dev)
+        elif args.workload == "hca_reindex_1m":
+            rec = run_layers(args, csa, synth, wl, dev)
+        elif args.workload == "decode_ragged_1m":
+            rec = run_decode_ragged(args, csa, synth, wl, dev)
+        else:
+            rec = run_decode(args, csa, synth, wl, dev)
+    finally:
+        if ORACLE_POOL is not None:
+            ORACLE_POOL.close()
     head = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"),
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
     print(json.dumps({**head, **rec}), flush=True)
