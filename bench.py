@@ -323,10 +323,17 @@ def run_decode(args, csa, synth, wl, dev):
     log(f"setup {time.time() - t_setup:.1f}s: {args.sets} input sets of {wl.name}")
     pos = wl.L - 1
 
+    # the step's first kernel alone: the key scan of csa_index_attn (with the
+    # per-unit short lists), or of csa_index_topk under --separate
     def scan(i):
         s = sets[i]
-        csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
-                       workspace=s["ws"])
+        if args.separate:
+            csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["idx"],
+                           workspace=s["ws"])
+        else:
+            csa.index_attn(s["q_idx"], s["w"], s["keys"], wl.m, pos, wl.k, s["q"], s["codes"],
+                           s["scales"], s["win"], wl.W, 1.0, s["idx"], s["out"],
+                           workspace=s["ws_fused"], fmt=FMT, scan_only=True)
 
     def step_fn(i):
         def f():
@@ -354,7 +361,8 @@ def run_decode(args, csa, synth, wl, dev):
 
     # dominant kernel: the indexer scan, timed with events on its launch stream
     # over back-to-back launches
-    scan_ms = back_to_back_ms(scan, len(sets), args.steps, [s["ws"] for s in sets])
+    scan_ms = back_to_back_ms(scan, len(sets), args.steps,
+                              [s["ws" if args.separate else "ws_fused"] for s in sets])
     scan_bytes = scan_bytes_per_query(wl) * wl.B
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     per_q = decode_bytes_per_query(wl)
@@ -391,7 +399,9 @@ def run_decode(args, csa, synth, wl, dev):
         "step_hbm": {"algorithmic_bytes_per_query": per_q["total"],
                      "GB/s": round(step_gbs, 1), "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "roofline": {
-            "kernel": "k_idx_scan (indexer key scan)",
+            "kernel": "k_idx_scan (indexer key scan)" if args.separate else
+                      "k_idx_scan (indexer key scan with per-unit short lists, the first kernel "
+                      "of csa_index_attn)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -499,17 +509,28 @@ def run_decode_ragged(args, csa, synth, wl, dev):
 
     def scan(i):
         s = sets[i]
-        csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
-                       workspace=s["ws"], pos_max=pos_max)
+        if args.separate:
+            csa.index_scan(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
+                           workspace=s["ws"], pos_max=pos_max)
+        else:
+            csa.index_attn(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["q"],
+                           s["codes"], s["scales"], s["win"], wl.W, 1.0, s["idx"], s["out"],
+                           workspace=s["ws_fused"], pos_max=pos_max, fmt=FMT, scan_only=True)
 
     def step_fn(i):
         def f():
             s = sets[i]
             append(i)
-            csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
-                           workspace=s["ws"], pos_max=pos_max)
-            csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W, s["pos"],
-                            1.0, s["out"], workspace=s["ws_attn"], pos_max=pos_max, fmt=FMT)
+            if args.separate:
+                csa.index_topk(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["idx"],
+                               workspace=s["ws"], pos_max=pos_max)
+                csa.sparse_attn(s["q"], s["codes"], s["scales"], s["idx"], s["win"], wl.W,
+                                s["pos"], 1.0, s["out"], workspace=s["ws_attn"],
+                                pos_max=pos_max, fmt=FMT)
+            else:
+                csa.index_attn(s["q_idx"], s["w"], s["keys"], wl.m, s["pos"], wl.k, s["q"],
+                               s["codes"], s["scales"], s["win"], wl.W, 1.0, s["idx"], s["out"],
+                               workspace=s["ws_fused"], pos_max=pos_max, fmt=FMT)
         return f
 
     eager = [step_fn(i) for i in range(len(sets))]
@@ -523,7 +544,8 @@ def run_decode_ragged(args, csa, synth, wl, dev):
     log(f"ragged step {ms_per_step * 1e3:.1f} us, {value:.0f} queries/s ({timing_name(args)})")
 
     # dominant kernel: the ragged indexer scan, timed with events on its stream
-    scan_ms = back_to_back_ms(scan, len(sets), args.steps, [s["ws"] for s in sets])
+    scan_ms = back_to_back_ms(scan, len(sets), args.steps,
+                              [s["ws" if args.separate else "ws_fused"] for s in sets])
     t_append = split_event_ms(append, None, len(sets), args.steps)
     pos = wl.positions()
     scan_bytes = sum((t + 1) // wl.m * wl.Di + wl.Hi * wl.Di + wl.Hi for t in pos)
@@ -558,7 +580,9 @@ def run_decode_ragged(args, csa, synth, wl, dev):
         },
         "append_us": round(t_append * 1e3, 2),
         "roofline": {
-            "kernel": "k_idx_scan (ragged indexer key scan)",
+            "kernel": "k_idx_scan (ragged indexer key scan" +
+                      (")" if args.separate else " with per-unit short lists, the first kernel "
+                       "of csa_index_attn)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -40,7 +40,7 @@ EXPORTED = [
     "csa_index_topk_ragged", "csa_index_scan_ragged", "csa_index_select_ragged",
     "csa_sparse_attn_ragged", "hca_dense_attn_ragged",
     "csa_workspace_clear", "csa_attn_workspace", "csa_sparse_attn", "hca_dense_attn",
-    "csa_sparse_attn_noalloc", "csa_index_attn_workspace", "csa_index_attn",
+    "csa_sparse_attn_noalloc", "csa_index_attn_workspace", "csa_index_attn", "csa_index_attn_scan",
 ]
 # bytes of the static device scratch of csa_sparse_attn_noalloc (CSA_NOALLOC_SCRATCH_MAX)
 NOALLOC_SCRATCH_MAX = 64 << 20
@@ -173,6 +173,8 @@ def lib():
             "csa_index_attn_workspace": (I64, [I, I, I64, I, I, I, I]),
             "csa_index_attn": (I, [P, P, P, I64, I, I, I, I, I, I64, P, P, I, I, P, P, P, P, I, I,
                                    I, I, F, P, P, P, I, P, P, I64, I, P]),
+            "csa_index_attn_scan": (I, [P, P, P, I64, I, I, I, I, I, I64, P, P, I, I, P, P, P, P,
+                                        I, I, I, I, F, P, P, P, I, P, P, I64, I, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -553,13 +555,14 @@ def index_attn_workspace(B, T, n_max, k, H, d, W) -> int:
 
 def index_attn(q_idx, w, keys, m, pos0, k, q, codes, scales, win, W, softmax_scale, out_idx, out,
                out_score=None, lse=None, cand=None, workspace=None, pos_max=None,
-               fmt: str = "e8m0"):
+               fmt: str = "e8m0", scan_only: bool = False):
     """Indexer top-k + sparse attention of one layer in one call; see
     csa_index_attn in include/csa.h. Same arguments as index_topk followed
     by those of sparse_attn (keys and the FP4 cache share blk_cap). pos0 may
     be an int64 [B] tensor of per-sequence positions bounded by pos_max.
     workspace: a Workspace (kept per B*T as for index_topk) or a raw uint8
-    tensor the caller keeps cleared."""
+    tensor the caller keeps cleared. scan_only: launch only the key scan
+    (csa_index_attn_scan), after which the workspace must be cleared."""
     _need(q_idx, torch.int8, "q_idx", 4)
     _need(w, torch.int8, "w", 3)
     _need(keys, torch.int8, "keys", 3)
@@ -590,8 +593,9 @@ def index_attn(q_idx, w, keys, m, pos0, k, q, codes, scales, win, W, softmax_sca
     ws = workspace.get(need, key=B * T) if isinstance(workspace, Workspace) else workspace
     ws_bytes = 0 if ws is None else ws.numel()
     _note_head(workspace, ws, B * T)
-    _check(lib().csa_index_attn(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di, m, pos0,
+    name = "csa_index_attn_scan" if scan_only else "csa_index_attn"
+    _check(getattr(lib(), name)(_ptr(q_idx), _ptr(w), _ptr(keys), blk_cap, B, T, Hi, Di, m, pos0,
                                 _ptr(pos), _ptr(cand), C, k, _ptr(q), _ptr(codes), _ptr(scales),
                                 _ptr(win), win.shape[1], W, H, d, float(softmax_scale),
                                 _ptr(out_idx), _ptr(out_score), _ptr(out), dt, _ptr(lse),
-                                _ptr(ws), ws_bytes, _fmt_code(fmt), _stream()), "csa_index_attn")
+                                _ptr(ws), ws_bytes, _fmt_code(fmt), _stream()), name)

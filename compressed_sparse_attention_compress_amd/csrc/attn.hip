@@ -256,7 +256,11 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         nv = nv < blk_cap ? nv : blk_cap;
         const csa_topk::SelShared sh{nullptr, nullptr, sel_bh, sel_tmp, sel_red};
         if constexpr (SEL == SEL_LISTS) {
-          keff = sel_ld.resolve(sa.slab + (int64_t)qi * sa.npad, (int)nv, k, sa.lp, sh, emit);
+          // a spilled selection compacts its candidates into the (still unused) stage
+          const int cap = ((STAGE_BYTES + LOGIT_BYTES) / 4 - 2 * sa.lp.units) / 2;
+          keff = sel_ld.resolve(sa.slab + (int64_t)qi * sa.npad, (int)nv, k, sa.lp, sh,
+                                sa.tinfo + (int64_t)qi * sa.lp.units,
+                                reinterpret_cast<int*>(s_raw), cap, emit);
         } else {
           const int N = cq ? sa.C : (int)nv;
           if (N <= csa_topk::PICK_MAX / 2)

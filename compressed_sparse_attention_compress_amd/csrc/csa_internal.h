@@ -58,6 +58,9 @@ __device__ inline int wave_scan_incl(int x) {
 }
 
 // Largest / smallest value over the 64 lanes of a wave, in every lane.
+// Sum over the wave (every lane gets it).
+__device__ inline int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_scan_incl(x), 63); }
+
 __device__ inline int wave_max(int x) {
   constexpr int lo = (int)0x80000000;
   x = max(x, dpp_move<0x111, 0xf>(x, lo));

@@ -982,14 +982,20 @@ extern "C" int64_t csa_index_attn_workspace(int B, int T, int64_t n_max, int k, 
   return ab < 0 ? -1 : ib + ab;
 }
 
-extern "C" int csa_index_attn(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
-                              int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
-                              const int64_t* pos, const int32_t* cand, int C, int k,
-                              const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                              const uint16_t* win, int Wcap, int W, int H, int d,
-                              float softmax_scale, int32_t* out_idx, int32_t* out_score,
-                              void* out, int out_dtype, float* lse, void* workspace,
-                              int64_t ws_bytes, int scale_fmt, hipStream_t stream) {
+#define CSA_INDEX_ATTN_PARAMS                                                                 \
+  const int8_t *q_idx, const int8_t *w, const int8_t *keys, int64_t blk_cap, int B, int T,     \
+      int Hi, int Di, int m, int64_t pos0, const int64_t *pos, const int32_t *cand, int C,     \
+      int k, const uint16_t *q, const uint8_t *codes, const uint8_t *scales,                   \
+      const uint16_t *win, int Wcap, int W, int H, int d, float softmax_scale,                 \
+      int32_t *out_idx, int32_t *out_score, void *out, int out_dtype, float *lse,              \
+      void *workspace, int64_t ws_bytes, int scale_fmt, hipStream_t stream
+#define CSA_INDEX_ATTN_ARGS                                                                  \
+  q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos0, pos, cand, C, k, q, codes, scales, win,     \
+      Wcap, W, H, d, softmax_scale, out_idx, out_score, out, out_dtype, lse, workspace,      \
+      ws_bytes, scale_fmt, stream
+
+// scan_only: every check, then only the first launch (the indexer scan)
+static int index_attn(CSA_INDEX_ATTN_PARAMS, bool scan_only) {
   if (pos && !csa_aligned(pos, 8)) return CSA_ERR_ALIGN;
   IdxArgs a{q_idx, w, keys, blk_cap, B, T, Hi, Di, m, pos0, cand, C, k, out_idx, out_score,
             workspace, ws_bytes, stream};
@@ -1016,7 +1022,9 @@ extern "C" int csa_index_attn(const int8_t* q_idx, const int8_t* w, const int8_t
               reinterpret_cast<const int2*>(ws + L.off_tinfo),
               reinterpret_cast<const int2*>(ws + L.off_comp),
               reinterpret_cast<const int32_t*>(ws + L.off_slab), L.npad,
-              ListsPlan{L.units, __builtin_ctz(L.lcap > 0 ? L.lcap : 1)}, cand, cand ? C : 0, m,
+              ListsPlan{L.units, __builtin_ctz(L.lcap > 0 ? L.lcap : 1),
+                        __builtin_ctz(TILE / L.sub)},
+              cand, cand ? C : 0, m,
               out_idx, out_score, fused_alg_bytes(n_max, Hi, Di, k, W, H, d)};
   // every argument is checked before anything is launched
   st = fused_attn_check(f);
@@ -1029,7 +1037,7 @@ extern "C" int csa_index_attn(const int8_t* q_idx, const int8_t* w, const int8_t
   f.ws = ab > 0 ? ws + ib : nullptr;
   f.ws_bytes = ws_bytes - ib;
   st = idx_phase(a, 0);
-  if (st != CSA_OK) return st;
+  if (st != CSA_OK || scan_only) return st;
   if (!fused) {
     st = idx_phase(a, 1);
     if (st != CSA_OK) return st;
@@ -1044,3 +1052,14 @@ extern "C" int csa_index_attn(const int8_t* q_idx, const int8_t* w, const int8_t
   f.sel = n_max <= PICK_MAX ? 2 : 1;  // whole score rows, or the scan's lists
   return fused_attn_launch(f);
 }
+
+extern "C" int csa_index_attn(CSA_INDEX_ATTN_PARAMS) {
+  return index_attn(CSA_INDEX_ATTN_ARGS, false);
+}
+
+extern "C" int csa_index_attn_scan(CSA_INDEX_ATTN_PARAMS) {
+  return index_attn(CSA_INDEX_ATTN_ARGS, true);
+}
+
+#undef CSA_INDEX_ATTN_PARAMS
+#undef CSA_INDEX_ATTN_ARGS

@@ -676,6 +676,7 @@ __device__ inline void row_walk_select(const int32_t* sq, int N, int keff, int T
 // ------------------------------------------------------------------------
 struct ListsPlan {
   int units, lshift;  // lcap = 2^lshift entries per unit; units * lcap <= SPEC_SLOTS, lcap >= LIST_MIN
+  int ushift;         // a unit covers entries [u << ushift, (u + 1) << ushift)
 };
 
 // lists_select in two steps, so that a kernel can issue these loads before
@@ -709,16 +710,140 @@ struct ListsLoad {
     ib = tinfo[ub];
   }
 
+  // A unit whose list stops above T1 (cut > T1) is read from the score row
+  // instead: the candidates (bin >= T1) of the listed units and of those
+  // rows are compacted into LDS in entry order (area: 2 * units ints, then
+  // scores and entries, cap each), then refined and emitted as in the final
+  // pass's compaction path. Returns false, having emitted nothing, when the
+  // candidates exceed cap.
+  template <class Emit>
+  __device__ inline bool spill_select(const int32_t* sq, int N, const int2* tinfo_q, int keff,
+                                      int T1, int need, ListsPlan P, int* area, int cap,
+                                      SelShared s, Emit emit) {
+    const int U = P.units;
+    int* u_off = area;         // per unit: candidate count, then its offset
+    int* u_base = area + U;    // per listed unit: rank of its first slot among listed candidates
+    int* cs = area + 2 * U;
+    int* ce = cs + cap;
+    __shared__ int s_sp[SPEC_SLOTS / LIST_MIN];  // the spilled units
+    __shared__ int s_nsp;
+    for (int u = threadIdx.x; u < U; u += 256) u_off[u] = 0;
+    if (threadIdx.x == 0) s_nsp = 0;
+    __syncthreads();
+    for (int u = threadIdx.x; u < U; u += 256)
+      if (tinfo_q[u].y > T1 && ((int64_t)u << P.ushift) < N) s_sp[atomicAdd(&s_nsp, 1)] = u;
+    // this thread's listed candidates: slots of units that did not spill
+    const int lmask = (1 << P.lshift) - 1;
+    bool q[SPT];
+    int ca = 0, cb = 0;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int i = i0 + u;
+      const bool in_a = (i >> P.lshift) == ua;
+      const int2 inf = in_a ? ia : ib;
+      q[u] = i < nslot && inf.y <= T1 && (i & lmask) < inf.x && score_bin512(r[u].x) >= T1;
+      ca += q[u] && in_a;
+      cb += q[u] && !in_a;
+    }
+    if (ca) atomicAdd(&u_off[ua], ca);
+    if (cb) atomicAdd(&u_off[ub], cb);
+    __syncthreads();
+    const int nsp = s_nsp;
+    // the spilled units' counts, from their score rows (8 entries a thread)
+    const int span = 1 << P.ushift;
+    for (int j = 0; j < nsp; ++j) {
+      const int u = s_sp[j];
+      const int64_t e0 = ((int64_t)u << P.ushift) + 8 * (int)threadIdx.x;
+      int c = 0;
+      if (8 * (int)threadIdx.x < span) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int v = e0 + jj < N ? sq[e0 + jj] : -1;
+          c += v >= 0 && score_bin512(v) >= T1;
+        }
+      }
+      c = wave_sum(c);
+      if ((threadIdx.x & 63) == 0 && c) atomicAdd(&u_off[u], c);
+    }
+    __syncthreads();
+    const int last_cnt = u_off[U - 1];
+    __syncthreads();
+    lds_excl_scan(u_off, U, s.tmp);
+    const int M = u_off[U - 1] + last_cnt;
+    if (M > cap) return false;
+    // ranks of the listed candidates: a scan over the threads (slots are in
+    // unit order), each unit's first slot recording where the unit starts
+    int tot;
+    int rank = wg_scan_incl<256>(ca + cb, s.tmp, &tot) - (ca + cb);
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int i = i0 + u;
+      if (i < nslot && (i & lmask) == 0) u_base[i >> P.lshift] = rank;
+      rank += q[u];
+    }
+    __syncthreads();
+    int vmin = 0x7fffffff, vmax = -1;
+    rank -= ca + cb;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      if (q[u]) {
+        const int un = (i0 + u) >> P.lshift;
+        const int at = u_off[un] + rank - u_base[un];
+        cs[at] = r[u].x;
+        ce[at] = r[u].y;
+        if (score_bin512(r[u].x) == T1) {
+          vmin = min(vmin, r[u].x);
+          vmax = max(vmax, r[u].x);
+        }
+        ++rank;
+      }
+    }
+    // the spilled units' candidates, in entry order
+    for (int j = 0; j < nsp; ++j) {
+      const int u = s_sp[j];
+      const int64_t e0 = ((int64_t)u << P.ushift) + 8 * (int)threadIdx.x;
+      int v[8];
+      int c = 0;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        v[jj] = (8 * (int)threadIdx.x < span && e0 + jj < N) ? sq[e0 + jj] : -1;
+        c += v[jj] >= 0 && score_bin512(v[jj]) >= T1;
+      }
+      int at = u_off[u] + wg_scan_incl<256>(c, s.tmp, &tot) - c;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (v[jj] >= 0 && score_bin512(v[jj]) >= T1) {
+          cs[at] = v[jj];
+          ce[at] = (int)(e0 + jj);
+          ++at;
+          if (score_bin512(v[jj]) == T1) {
+            vmin = min(vmin, v[jj]);
+            vmax = max(vmax, v[jj]);
+          }
+        }
+      }
+    }
+    int lo, hi;
+    bin_range(vmin, vmax, s.s_red, &lo, &hi);  // (its barrier orders the writes above)
+    int take_eq;
+    const int tau = refine_tau(cs, M, T1, lo, hi, need, s.bh, s.tmp, s.s_red, &take_eq);
+    emit_ordered(cs, ce, M, tau, take_eq, keff, s.tmp, emit);
+    return true;
+  }
+
+  // area/cap: LDS for the spill path (see spill_select); tinfo_q: the
+  // query's (count, cut) per unit
   template <class Emit>
   __device__ inline int resolve(const int32_t* sq, int N, int k, ListsPlan P, SelShared s,
-                                Emit emit) {
+                                const int2* tinfo_q, int* area, int cap, Emit emit) {
     const int keff = threshold_from_bins(c_hi, c_lo, k, s.tmp, s.s_red);
     if (keff == 0) return 0;
     const int T1 = s.s_red[0];
     const int need = keff - s.s_red[1];
     const bool spill = i0 < nslot && (ia.y > T1 || ib.y > T1);
     if (__syncthreads_or(spill ? 1 : 0)) {  // (also orders the s_red reads)
-      row_walk_select(sq, N, keff, T1, need, s, emit);
+      if (!spill_select(sq, N, tinfo_q, keff, T1, need, P, area, cap, s, emit))
+        row_walk_select(sq, N, keff, T1, need, s, emit);
       return keff;
     }
     int sv[SPT];

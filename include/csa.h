@@ -314,6 +314,21 @@ int csa_index_attn(const int8_t* q_idx, const int8_t* w, const int8_t* keys, int
                    const uint16_t* win, int Wcap, int W, int H, int d, float softmax_scale,
                    int32_t* out_idx, int32_t* out_score, void* out, int out_dtype, float* lse,
                    void* workspace, int64_t ws_bytes, int scale_fmt, hipStream_t stream);
+/* The first launch of csa_index_attn alone, so a caller can time the key scan
+ * by itself: identical arguments and checks, then only the indexer scan (the
+ * exact scores and histograms, and for queries with more than 8192 candidates
+ * and no pool the per-unit short lists the attention kernel selects from).
+ * out_idx, out_score, out and lse are not written. The scan adds into the
+ * workspace head, which only the rest of csa_index_attn returns to zero:
+ * clear it (csa_workspace_clear) before the workspace serves another call. */
+int csa_index_attn_scan(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
+                        int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
+                        const int64_t* pos, const int32_t* cand, int C, int k,
+                        const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                        const uint16_t* win, int Wcap, int W, int H, int d, float softmax_scale,
+                        int32_t* out_idx, int32_t* out_score, void* out, int out_dtype,
+                        float* lse, void* workspace, int64_t ws_bytes, int scale_fmt,
+                        hipStream_t stream);
 
 /* Zero-fill a workspace with a kernel on `stream` (no hipMemset, so it may be
  * captured in a graph). bytes must be a multiple of 4 and ws 4-byte aligned. */

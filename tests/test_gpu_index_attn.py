@@ -4,9 +4,11 @@ csa_index_topk + csa_sparse_attn and against the oracle: out_idx bit-exact,
 outputs within the attention bound of the separate calls (their split
 plans may differ) and of the oracle. Covers both
 in-kernel selections (per-tile candidate lists for long contexts, whole
-score rows for <= 8192 candidates), a Reindex pool, per-sequence positions,
+score rows for <= 8192 candidates; lists that miss part of the threshold
+bin, read from the score rows), a Reindex pool, per-sequence positions,
 tie storms (the global-walk path), clustered top-k (the compaction path),
-other head counts and widths, and batch invariance of the split plan."""
+other head counts and widths, batch invariance of the split plan, and the
+scan-only entry csa_index_attn_scan."""
 
 from __future__ import annotations
 
@@ -168,6 +170,19 @@ def test_index_attn_tie_storm_and_clusters():
     _compare(xc, 4, L - 1, 1024, 128, torch.bfloat16, oracle_seqs=(1,))
 
 
+@pytest.mark.parametrize("k", [512, 1024])
+def test_index_attn_dense_topk_spills(k):
+    """A top-k dense in a short context (12,000 entries in 24 units of 512):
+    most units hold more entries at or above the threshold bin than their
+    32-entry lists, so the selection reads those units' score rows."""
+    say("index_attn dense top-k", k)
+    L = 4 * 12000
+    x = _world(10, 2, L, 512, 64, 4, 8, 64)
+    _compare(x, 4, L - 1, k, 128, torch.bfloat16, oracle_seqs=(0, 1))
+    pos = torch.tensor([L - 1, 4 * 9000 + 3], device=DEV, dtype=torch.int64)
+    _compare(x, 4, pos, k, 128, torch.float32, pos_max=L - 1, oracle_seqs=(1,))
+
+
 @pytest.mark.parametrize("d,H", [(128, 8), (256, 20), (512, 40)])
 def test_index_attn_shapes(d, H):
     say("index_attn shapes", d, H)
@@ -201,6 +216,30 @@ def test_index_attn_workspace_reuse():
     for u, v in zip(a, d_):
         assert torch.equal(u, v)
     assert torch.equal(c[0][0], a[0][0]) and torch.equal(c[2][0], a[2][0])
+
+
+def test_index_attn_scan_only():
+    """csa_index_attn_scan launches the scan alone and writes no output; after
+    a workspace clear the full call gives what it gives on a fresh workspace."""
+    say("index_attn scan only")
+    L = 4 * 40000
+    x = _world(9, 2, L, 512, 64, 4, 8, 64)
+    ref = _fused(x, 4, L - 1, 1024, 128, torch.bfloat16)
+    ws = csa.Workspace(DEV)
+    B = 2
+    idx = torch.full((B, 1, 1024), -7, device=DEV, dtype=torch.int32)
+    out = torch.full(x["q"].shape, 9.0, device=DEV, dtype=torch.bfloat16)
+    for _ in range(2):
+        csa.index_attn(x["q_idx"], x["w"], x["keys"], 4, L - 1, 1024, x["q"], x["codes"],
+                       x["scales"], x["win"], 128, 1.0, idx, out, workspace=ws, scan_only=True)
+    torch.cuda.synchronize()
+    assert (idx == -7).all() and (out == 9.0).all()
+    assert ws.buf.any(), "the scan wrote nothing into the workspace"
+    csa.workspace_clear(ws.buf)
+    got = _fused(x, 4, L - 1, 1024, 128, torch.bfloat16, ws=ws)
+    torch.cuda.synchronize()
+    for u, v in zip(ref, got):
+        assert torch.equal(u, v)
 
 
 def test_batch_invariance_decode_and_hca():
