@@ -83,6 +83,13 @@ struct SelArgs {
   int C, m_idx;           // pool size; block size of the indexed cache
   int32_t* out_idx;       // [queries][k]
   int32_t* out_score;     // [queries][k] or null
+  const int2* tinfo2;     // [queries][units] (count, cut bin) of the wide lists (SEL_LISTS)
+  const int2* comp2;      // [queries][units][2 lcap] wide lists (SEL_LISTS)
+  const int8_t* q_idx;    // [queries][Hi][Di] indexer rows, w [queries][Hi] and keys
+  const int8_t* w;        // [B][blk_cap][Di]: a score of the whole-row walk is recomputed
+  const int8_t* keys;     // from them where the scan wrote no slab (slab_ok false)
+  int Hi, Di;
+  bool slab_ok;
 };
 
 
@@ -258,8 +265,13 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         if constexpr (SEL == SEL_LISTS) {
           // a spilled selection compacts its candidates into the (still unused) stage
           const int cap = ((STAGE_BYTES + LOGIT_BYTES) / 4 - 2 * sa.lp.units) / 2;
-          keff = sel_ld.resolve(sa.slab + (int64_t)qi * sa.npad, (int)nv, k, sa.lp, sh,
-                                sa.tinfo + (int64_t)qi * sa.lp.units,
+          const int64_t nu = sa.lp.units;
+          const csa_topk::ScoreSrc src{
+              sa.slab_ok ? sa.slab + (int64_t)qi * sa.npad : nullptr,
+              sa.keys + (int64_t)b * blk_cap * sa.Di, sa.q_idx + (int64_t)qi * sa.Hi * sa.Di,
+              sa.w + (int64_t)qi * sa.Hi, sa.Hi, sa.Di, reinterpret_cast<int*>(s_raw)};
+          keff = sel_ld.resolve(src, (int)nv, k, sa.lp, sh, sa.tinfo + qi * nu,
+                                sa.tinfo2 + qi * nu, sa.comp2 + ((qi * nu) << (sa.lp.lshift + 1)),
                                 reinterpret_cast<int*>(s_raw), cap, emit);
         } else {
           const int N = cq ? sa.C : (int)nv;
@@ -940,8 +952,9 @@ static AttnArgs fused_args(const FusedAttn& f) {
   a.pos = f.pos;
   a.scale_fmt = f.scale_fmt;
   a.sel = f.sel;
-  a.sa = SelArgs{f.hist, f.tinfo, f.comp, f.slab, f.npad, f.lp, f.cand, f.C, f.m_idx,
-                 f.out_idx, f.out_score};
+  a.sa = SelArgs{f.hist,    f.tinfo,   f.comp,  f.slab,  f.npad,  f.lp,   f.cand,
+                 f.C,       f.m_idx,   f.out_idx, f.out_score, f.tinfo2, f.comp2, f.q_idx,
+                 f.w,       f.keys,    f.Hi,    f.Di,    f.slab_ok};
   a.alg_bytes = f.alg_bytes;
   return a;
 }

@@ -57,30 +57,39 @@ __device__ inline int score_tile(const v4i (&A)[KS], const v4i (&Bk)[KS], const 
   return p;
 }
 
-// The scan unit's short list (k_idx_scan's LISTS tail): its cut bin, the
+// The scan unit's short lists (k_idx_scan's LISTS tail). Its cut bin is the
 // lowest bin whose suffix count (entries in it and above) is at most lcap
-// (NB1, an empty list, when the top bin alone holds more), then its entries
-// of the bins at or above the cut in entry order, and (count, cut). Kept out
-// of line: the scan's main loop runs at the register limit, and this code's
+// (NB1, an empty list, when the top bin alone holds more); the list holds its
+// entries of the bins at or above the cut in entry order, with (count, cut).
+// The wide list does the same for 2 lcap entries: a selection whose threshold
+// bin lies below a unit's cut reads that unit's candidates there. Kept out of
+// line: the scan's main loop runs at the register limit, and this code's
 // values must not stay live across it.
 __device__ __noinline__ void scan_unit_list(const uint32_t* lh, const int* ssc, int span,
                                             int64_t wg0, int64_t N, int2* lq, int2* info,
-                                            int lcap) {
+                                            int2* lq2, int2* info2, int lcap) {
   __shared__ int l_tmp[4];
-  __shared__ int l_cut[4];
+  __shared__ int l_cut[8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hb = NB1 - 1 - 2 * (int)threadIdx.x;
   const int c_hi = (int)lh[hb], c_lo = (int)lh[hb - 1];
   int tot;
   const int incl = wg_scan_incl<256>(c_hi + c_lo, l_tmp, &tot);
   const int excl = incl - c_hi - c_lo;
-  int cut = NB1;
+  int cut = NB1, cut2 = NB1;
   if (excl + c_hi <= lcap) cut = hb;
   if (incl <= lcap) cut = hb - 1;
+  if (excl + c_hi <= 2 * lcap) cut2 = hb;
+  if (incl <= 2 * lcap) cut2 = hb - 1;
   cut = wave_min(cut);
-  if (lane == 0) l_cut[wave] = cut;
+  cut2 = wave_min(cut2);
+  if (lane == 0) {
+    l_cut[wave] = cut;
+    l_cut[4 + wave] = cut2;
+  }
   __syncthreads();
   cut = min(min(l_cut[0], l_cut[1]), min(l_cut[2], l_cut[3]));
+  cut2 = min(min(l_cut[4], l_cut[5]), min(l_cut[6], l_cut[7]));
   // the listed entries in entry order: thread j takes [8 j, 8 j + 8)
   const int j0 = threadIdx.x * 8;
   int v[8];
@@ -89,14 +98,23 @@ __device__ __noinline__ void scan_unit_list(const uint32_t* lh, const int* ssc, 
   for (int j = 0; j < 8; ++j) {
     const bool in = j0 + j < span && wg0 + j0 + j < N;
     v[j] = in ? ssc[j0 + j] : -1;
-    f += v[j] >= 0 && score_bin512(v[j]) >= cut;
+    const int bn = v[j] >= 0 ? score_bin512(v[j]) : -1;
+    f += (bn >= cut ? 1 << 16 : 0) + (bn >= cut2 ? 1 : 0);
   }
   int total;
-  int at = wg_scan_incl<256>(f, l_tmp, &total) - f;
+  const int before = wg_scan_incl<256>(f, l_tmp, &total) - f;
+  int at = before >> 16, at2 = before & 0xffff;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (v[j] >= 0 && score_bin512(v[j]) >= cut) lq[at++] = int2{v[j], (int)(wg0 + j0 + j)};
-  if (threadIdx.x == 0) *info = int2{total, cut};
+  for (int j = 0; j < 8; ++j) {
+    const int bn = v[j] >= 0 ? score_bin512(v[j]) : -1;
+    const int2 ent = int2{v[j], (int)(wg0 + j0 + j)};
+    if (bn >= cut) lq[at++] = ent;
+    if (bn >= cut2) lq2[at2++] = ent;
+  }
+  if (threadIdx.x == 0) {
+    *info = int2{total >> 16, cut};
+    *info2 = int2{total & 0xffff, cut2};
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -121,7 +139,8 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int64_t* __restrict__ qpos, const int32_t* __restrict__ cand, int C, int64_t npad,
     int32_t* __restrict__ slab,
     uint32_t* __restrict__ hist, int64_t gpad, int32_t* __restrict__ gslab,
-    uint32_t* __restrict__ ghist, int2* __restrict__ tinfo, int2* __restrict__ comp, int lcap) {
+    uint32_t* __restrict__ ghist, int2* __restrict__ tinfo, int2* __restrict__ comp, int lcap,
+    int2* __restrict__ tinfo2, int2* __restrict__ comp2, int write_slab) {
   constexpr int KS = (DI + 63) / 64;
   constexpr int BATCH = 8;
   constexpr int SPAN = TILE / SUB;  // entries per workgroup (SUB workgroups per tile)
@@ -261,7 +280,7 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   // done (stores issued between loads would be waited on with them); entries
   // at or past N are never read, so whole 8-entry runs past it are not stored
   const int64_t e0 = wg0 + threadIdx.x * 8;
-  if (threadIdx.x * 8 < SPAN && e0 < N) {
+  if ((!LISTS || write_slab) && threadIdx.x * 8 < SPAN && e0 < N) {
     const int j0 = threadIdx.x * 8;
     int v[8];
 #pragma unroll
@@ -283,9 +302,11 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     if (lh[i]) atomicAdd(&hq[i], lh[i]);
     if (POOL && lhg[i]) atomicAdd(&ghist[(int64_t)qi * NB1 + i], lhg[i]);
   }
-  if constexpr (LISTS)
-    scan_unit_list(lh, ssc, SPAN, wg0, N, comp + ((int64_t)qi * gridDim.x + blockIdx.x) * lcap,
-                   tinfo + (int64_t)qi * gridDim.x + blockIdx.x, lcap);
+  if constexpr (LISTS) {
+    const int64_t unit = (int64_t)qi * gridDim.x + blockIdx.x;
+    scan_unit_list(lh, ssc, SPAN, wg0, N, comp + unit * lcap, tinfo + unit,
+                   comp2 + unit * 2 * lcap, tinfo2 + unit, lcap);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -665,6 +686,7 @@ struct IdxArgs {
   int n_keep = 0;              // blockwise pool: groups kept (0 = no pool)
   int32_t* out_pool = nullptr;  // [B][T][POOL_G * n_keep]
   bool lists = false;          // the workspace has the scan-side lists (csa_index_attn)
+  bool write_slab = true;      // false: a list scan whose scores only the lists carry on
 };
 
 // Runs of at least PREFILL_MIN_T queries per sequence (prefill chunks) are
@@ -753,11 +775,14 @@ static int idx_phase(const IdxArgs& a, int phase) {
     const dim3 sgrid(L.n_tiles * sub, BT);
     int2* tinfo = reinterpret_cast<int2*>(ws + L.off_tinfo);
     int2* comp = reinterpret_cast<int2*>(ws + L.off_comp);
+    int2* tinfo2 = reinterpret_cast<int2*>(ws + L.off_tinfo2);
+    int2* comp2 = reinterpret_cast<int2*>(ws + L.off_comp2);
     const bool lists = a.lists && L.units > 0 && !a.cand && !pool;
 #define CSA_LAUNCH_SCAN1(DD, CC, SS, PP, LL)                                                     \
   hipLaunchKernelGGL((k_idx_scan<DD, CC, SS, PP, LL>), sgrid, dim3(256), 0, a.stream, a.q_idx,  \
                      a.w, a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.pos, a.cand, C, L.npad,    \
-                     slab, hist, L.gpad, gslab, ghist, tinfo, comp, L.lcap)
+                     slab, hist, L.gpad, gslab, ghist, tinfo, comp, L.lcap, tinfo2, comp2,  \
+                     a.write_slab ? 1 : 0)
 #define CSA_LAUNCH_SCAN(DD, CC, SS, PP)                               \
   do {                                                                \
     if (!CC && !PP && lists) CSA_LAUNCH_SCAN1(DD, CC, SS, PP, true);  \
@@ -1026,6 +1051,17 @@ static int index_attn(CSA_INDEX_ATTN_PARAMS, bool scan_only) {
                         __builtin_ctz(TILE / L.sub)},
               cand, cand ? C : 0, m,
               out_idx, out_score, fused_alg_bytes(n_max, Hi, Di, k, W, H, d)};
+  // the fused list path keeps its scores in the lists (the whole-row walk of
+  // massive ties recomputes them from the keys), so its scan writes no slab
+  a.write_slab = !(fused && a.lists);
+  f.tinfo2 = reinterpret_cast<const int2*>(ws + L.off_tinfo2);
+  f.comp2 = reinterpret_cast<const int2*>(ws + L.off_comp2);
+  f.q_idx = q_idx;
+  f.w = w;
+  f.keys = keys;
+  f.Hi = Hi;
+  f.Di = Di;
+  f.slab_ok = a.write_slab;
   // every argument is checked before anything is launched
   st = fused_attn_check(f);
   if (st != CSA_OK) return st;

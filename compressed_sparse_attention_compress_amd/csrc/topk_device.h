@@ -583,22 +583,93 @@ __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, cons
 }
 
 // ------------------------------------------------------------------------
-// Exact selection by walking a query's whole score row sq[0..N) in global
-// memory (negative scores are holes), given its threshold bin T1 and the
-// `need` candidates of T1 still to take: the bin's score range, the radix
-// refinement of tau, then the ordered emission in rounds of 2048 entries.
-// The slow path of the list selection (a threshold bin the short lists do
-// not cover: massive ties, scores clustered in a few tiles).
+// Where a selection reads a query's scores: its row of the score slab, or,
+// where the scan wrote none (the list path of csa_index_attn), recomputed
+// from the keys as the scan computes them: the sum over the Hi heads of
+// w_h * max(0, q_h . key), in int32 (int8 products and their sums are exact,
+// so the order of the additions does not matter).
+// ------------------------------------------------------------------------
+template <int DI>
+__device__ inline int score_from_key(const int8_t* key, const int* q_lds, int Hi) {
+  int4 kv[DI / 16];
+#pragma unroll
+  for (int c = 0; c < DI / 16; ++c) kv[c] = reinterpret_cast<const int4*>(key)[c];
+  const int* wl = q_lds + Hi * (DI / 4);
+  int s = 0;
+  for (int h = 0; h < Hi; ++h) {
+    int d = 0;
+#pragma unroll
+    for (int c = 0; c < DI / 16; ++c) {
+      const int4 qv = *reinterpret_cast<const int4*>(q_lds + h * (DI / 4) + 4 * c);
+      d = __builtin_amdgcn_sdot4(qv.x, kv[c].x, d, false);
+      d = __builtin_amdgcn_sdot4(qv.y, kv[c].y, d, false);
+      d = __builtin_amdgcn_sdot4(qv.z, kv[c].z, d, false);
+      d = __builtin_amdgcn_sdot4(qv.w, kv[c].w, d, false);
+    }
+    s += wl[h] * max(d, 0);
+  }
+  return s;
+}
+
+struct ScoreSrc {
+  const int32_t* sq;   // the query's slab row, or null: recompute
+  const int8_t* keys;  // the sequence's keys [blk_cap][Di] (recompute)
+  const int8_t* q;     // the query's indexer rows [Hi][Di] (recompute)
+  const int8_t* w;     // its head weights [Hi] (recompute)
+  int Hi, Di;
+  int* q_lds;          // 16-byte aligned LDS: Hi * Di / 4 words of q, then Hi weights
+
+  // q and w into LDS (recompute only; every thread calls it; ends with a
+  // barrier when it stages)
+  __device__ inline void stage() const {
+    if (sq) return;
+    const int nq = Hi * Di / 4;
+    for (int i = threadIdx.x; i < nq; i += 256) q_lds[i] = reinterpret_cast<const int*>(q)[i];
+    if ((int)threadIdx.x < Hi) q_lds[nq + threadIdx.x] = (int)w[threadIdx.x];
+    __syncthreads();
+  }
+  // scores of entries e0 .. e0 + 7, -1 at and past N
+  __device__ inline void load8(int64_t e0, int64_t N, int (&v)[8]) const {
+    if (sq) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e0 + j < N ? sq[e0 + j] : -1;
+      return;
+    }
+    for (int j = 0; j < 8; ++j) {
+      const int64_t e = e0 + j;
+      int sc = -1;
+      if (e < N) {
+        const int8_t* key = keys + e * Di;
+        sc = Di == 32 ? score_from_key<32>(key, q_lds, Hi)
+                      : (Di == 64 ? score_from_key<64>(key, q_lds, Hi)
+                                  : score_from_key<128>(key, q_lds, Hi));
+      }
+      v[j] = sc;
+    }
+  }
+};
+
+// ------------------------------------------------------------------------
+// Exact selection by walking a query's whole score row (src: the slab row in
+// global memory, or the scores recomputed from the keys; negative scores are
+// holes), given its threshold bin T1 and the `need` candidates of T1 still to
+// take: the bin's score range, the radix refinement of tau, then the ordered
+// emission in rounds of 2048 entries. The slow path of the list selection (a
+// threshold bin that even the wide lists do not cover: massive ties).
 // ------------------------------------------------------------------------
 template <class Emit>
-__device__ inline void row_walk_select(const int32_t* sq, int N, int keff, int T1, int need,
+__device__ inline void row_walk_select(const ScoreSrc& src, int N, int keff, int T1, int need,
                                        SelShared s, Emit emit) {
   int vmin = 0x7fffffff, vmax = -1;
-  for (int i = threadIdx.x; i < N; i += 256) {
-    const int v = sq[i];
-    if (v >= 0 && score_bin512(v) == T1) {
-      vmin = min(vmin, v);
-      vmax = max(vmax, v);
+  for (int64_t b0 = 8 * (int64_t)threadIdx.x; b0 < N; b0 += 2048) {
+    int v[8];
+    src.load8(b0, N, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (v[j] >= 0 && score_bin512(v[j]) == T1) {
+        vmin = min(vmin, v[j]);
+        vmax = max(vmax, v[j]);
+      }
     }
   }
   int lo, hi;
@@ -609,10 +680,13 @@ __device__ inline void row_walk_select(const int32_t* sq, int N, int keff, int T
     const int shift = bits > 8 ? bits - 8 : 0;
     s.bh[threadIdx.x] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < N; i += 256) {
-      const int v = sq[i];
-      if (v >= 0 && score_bin512(v) == T1 && v >= lo && v - lo <= R)
-        atomicAdd(&s.bh[(v - lo) >> shift], 1u);
+    for (int64_t b0 = 8 * (int64_t)threadIdx.x; b0 < N; b0 += 2048) {
+      int v[8];
+      src.load8(b0, N, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (v[j] >= 0 && score_bin512(v[j]) == T1 && v[j] >= lo && v[j] - lo <= R)
+          atomicAdd(&s.bh[(v[j] - lo) >> shift], 1u);
     }
     __syncthreads();
     const int c = (int)s.bh[255 - threadIdx.x];
@@ -634,8 +708,7 @@ __device__ inline void row_walk_select(const int32_t* sq, int N, int keff, int T
   for (int r0 = 0; r0 < N; r0 += 2048) {
     const int b0 = r0 + 8 * (int)threadIdx.x;
     int sv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sv[j] = b0 + j < N ? sq[b0 + j] : -1;
+    src.load8(b0, N, sv);
     int gtc = 0, eqc = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -710,28 +783,37 @@ struct ListsLoad {
     ib = tinfo[ub];
   }
 
-  // A unit whose list stops above T1 (cut > T1) is read from the score row
-  // instead: the candidates (bin >= T1) of the listed units and of those
-  // rows are compacted into LDS in entry order (area: 2 * units ints, then
-  // scores and entries, cap each), then refined and emitted as in the final
-  // pass's compaction path. Returns false, having emitted nothing, when the
-  // candidates exceed cap.
+  // A unit whose list stops above T1 (cut > T1) takes its candidates from its
+  // wide list instead (2 lcap entries of its top bins); the candidates of
+  // all units (bin >= T1) are compacted into LDS in entry order (area: 2 *
+  // units ints, then scores and entries, cap each), then refined and emitted
+  // as in the final pass's compaction path. Returns false, having emitted
+  // nothing, when a wide list also stops above T1 or the candidates exceed
+  // cap.
   template <class Emit>
-  __device__ inline bool spill_select(const int32_t* sq, int N, const int2* tinfo_q, int keff,
-                                      int T1, int need, ListsPlan P, int* area, int cap,
-                                      SelShared s, Emit emit) {
+  __device__ inline bool spill_select(const int2* tinfo_q, const int2* tinfo2_q,
+                                      const int2* comp2_q, int keff, int T1, int need,
+                                      ListsPlan P, int* area, int cap, SelShared s, Emit emit) {
     const int U = P.units;
+    const int lcap2 = 2 << P.lshift;
     int* u_off = area;         // per unit: candidate count, then its offset
     int* u_base = area + U;    // per listed unit: rank of its first slot among listed candidates
     int* cs = area + 2 * U;
     int* ce = cs + cap;
     __shared__ int s_sp[SPEC_SLOTS / LIST_MIN];  // the spilled units
-    __shared__ int s_nsp;
+    __shared__ int s_nsp, s_deep;
     for (int u = threadIdx.x; u < U; u += 256) u_off[u] = 0;
-    if (threadIdx.x == 0) s_nsp = 0;
+    if (threadIdx.x == 0) {
+      s_nsp = 0;
+      s_deep = 0;
+    }
     __syncthreads();
-    for (int u = threadIdx.x; u < U; u += 256)
-      if (tinfo_q[u].y > T1 && ((int64_t)u << P.ushift) < N) s_sp[atomicAdd(&s_nsp, 1)] = u;
+    for (int u = threadIdx.x; u < U; u += 256) {
+      if (tinfo_q[u].y > T1) {
+        s_sp[atomicAdd(&s_nsp, 1)] = u;
+        if (tinfo2_q[u].y > T1) s_deep = 1;  // even the wide list misses part of bin T1
+      }
+    }
     // this thread's listed candidates: slots of units that did not spill
     const int lmask = (1 << P.lshift) - 1;
     bool q[SPT];
@@ -748,22 +830,17 @@ struct ListsLoad {
     if (ca) atomicAdd(&u_off[ua], ca);
     if (cb) atomicAdd(&u_off[ub], cb);
     __syncthreads();
+    if (s_deep) return false;
     const int nsp = s_nsp;
-    // the spilled units' counts, from their score rows (8 entries a thread)
-    const int span = 1 << P.ushift;
-    for (int j = 0; j < nsp; ++j) {
+    // the spilled units' counts, from their wide lists (a wave per unit)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int j = wave; j < nsp; j += 4) {
       const int u = s_sp[j];
-      const int64_t e0 = ((int64_t)u << P.ushift) + 8 * (int)threadIdx.x;
+      const int cnt2 = tinfo2_q[u].x;
       int c = 0;
-      if (8 * (int)threadIdx.x < span) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int v = e0 + jj < N ? sq[e0 + jj] : -1;
-          c += v >= 0 && score_bin512(v) >= T1;
-        }
-      }
+      for (int i = lane; i < cnt2; i += 64) c += score_bin512(comp2_q[u * lcap2 + i].x) >= T1;
       c = wave_sum(c);
-      if ((threadIdx.x & 63) == 0 && c) atomicAdd(&u_off[u], c);
+      if (lane == 0) u_off[u] = c;
     }
     __syncthreads();
     const int last_cnt = u_off[U - 1];
@@ -798,29 +875,27 @@ struct ListsLoad {
         ++rank;
       }
     }
-    // the spilled units' candidates, in entry order
-    for (int j = 0; j < nsp; ++j) {
+    // the spilled units' candidates from their wide lists (entry order), a
+    // wave per unit with a ballot for the ranks
+    for (int j = wave; j < nsp; j += 4) {
       const int u = s_sp[j];
-      const int64_t e0 = ((int64_t)u << P.ushift) + 8 * (int)threadIdx.x;
-      int v[8];
-      int c = 0;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        v[jj] = (8 * (int)threadIdx.x < span && e0 + jj < N) ? sq[e0 + jj] : -1;
-        c += v[jj] >= 0 && score_bin512(v[jj]) >= T1;
-      }
-      int at = u_off[u] + wg_scan_incl<256>(c, s.tmp, &tot) - c;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        if (v[jj] >= 0 && score_bin512(v[jj]) >= T1) {
-          cs[at] = v[jj];
-          ce[at] = (int)(e0 + jj);
-          ++at;
-          if (score_bin512(v[jj]) == T1) {
-            vmin = min(vmin, v[jj]);
-            vmax = max(vmax, v[jj]);
+      const int cnt2 = tinfo2_q[u].x;
+      int at = u_off[u];
+      for (int i0w = 0; i0w < cnt2; i0w += 64) {
+        const int i = i0w + lane;
+        const int2 ent = i < cnt2 ? comp2_q[u * lcap2 + i] : int2{-1, 0};
+        const bool take = i < cnt2 && score_bin512(ent.x) >= T1;
+        const uint64_t m = __ballot(take);
+        if (take) {
+          const int pos = at + __popcll(m & ((1ull << lane) - 1));
+          cs[pos] = ent.x;
+          ce[pos] = ent.y;
+          if (score_bin512(ent.x) == T1) {
+            vmin = min(vmin, ent.x);
+            vmax = max(vmax, ent.x);
           }
         }
+        at += __popcll(m);
       }
     }
     int lo, hi;
@@ -831,19 +906,24 @@ struct ListsLoad {
     return true;
   }
 
-  // area/cap: LDS for the spill path (see spill_select); tinfo_q: the
-  // query's (count, cut) per unit
+  // area/cap: LDS for the spill path (see spill_select); tinfo_q / tinfo2_q /
+  // comp2_q: the query's (count, cut) per unit and its wide lists; src: its
+  // scores for the whole-row walk (slab row, or recomputed from the keys)
   template <class Emit>
-  __device__ inline int resolve(const int32_t* sq, int N, int k, ListsPlan P, SelShared s,
-                                const int2* tinfo_q, int* area, int cap, Emit emit) {
+  __device__ inline int resolve(const ScoreSrc& src, int N, int k, ListsPlan P, SelShared s,
+                                const int2* tinfo_q, const int2* tinfo2_q, const int2* comp2_q,
+                                int* area, int cap, Emit emit) {
     const int keff = threshold_from_bins(c_hi, c_lo, k, s.tmp, s.s_red);
     if (keff == 0) return 0;
     const int T1 = s.s_red[0];
     const int need = keff - s.s_red[1];
     const bool spill = i0 < nslot && (ia.y > T1 || ib.y > T1);
     if (__syncthreads_or(spill ? 1 : 0)) {  // (also orders the s_red reads)
-      if (!spill_select(sq, N, tinfo_q, keff, T1, need, P, area, cap, s, emit))
-        row_walk_select(sq, N, keff, T1, need, s, emit);
+      if (!spill_select(tinfo_q, tinfo2_q, comp2_q, keff, T1, need, P, area, cap, s, emit)) {
+        __syncthreads();  // the spill path's LDS reads are done before the walk stages q
+        src.stage();
+        row_walk_select(src, N, keff, T1, need, s, emit);
+      }
       return keff;
     }
     int sv[SPT];
@@ -873,7 +953,7 @@ struct IdxLayout {
   // scan-side lists (csa_index_attn): per scan unit its (count, cut bin)
   // and its top entries [units][lcap] (score, entry); units = 0 without them
   int sub, units, lcap;
-  int64_t off_tinfo, off_comp, bytes;
+  int64_t off_tinfo, off_comp, off_tinfo2, off_comp2, bytes;  // (2: the wide lists, 2 lcap)
 };
 
 // Scan workgroups per 2048-entry tile: enough workgroups (about 1024, four
@@ -921,6 +1001,8 @@ inline IdxLayout idx_layout(int64_t BT, int64_t n_max, bool pool, bool lists = f
   }
   L.off_tinfo = o; o = align_up(o + BT * L.units * 8, 256);
   L.off_comp = o; o = align_up(o + BT * L.units * L.lcap * 8, 256);
+  L.off_tinfo2 = o; o = align_up(o + BT * L.units * 8, 256);
+  L.off_comp2 = o; o = align_up(o + BT * L.units * 2 * L.lcap * 8, 256);
   L.bytes = o;
   return L;
 }
@@ -958,6 +1040,11 @@ struct FusedAttn {
   int64_t npad; ListsPlan lp; const int32_t* cand; int C, m_idx;
   int32_t* out_idx; int32_t* out_score;
   int64_t alg_bytes;  // the query's algorithmic bytes (indexer + attention), for the split plan
+  // the wide lists, and what recomputes a score where the scan wrote no slab
+  const int2* tinfo2 = nullptr; const int2* comp2 = nullptr;
+  const int8_t* q_idx = nullptr; const int8_t* w = nullptr; const int8_t* keys = nullptr;
+  int Hi = 0, Di = 0;
+  bool slab_ok = true;
 };
 // Algorithmic HBM bytes of one query of the fused call: its indexer keys (or
 // pool rows), indexer query and weights, the selected entries, the window,
