@@ -17,11 +17,15 @@
 //    unconditionally and double-buffered). Runs of >= 16 queries per sequence
 //    (prefill chunks): k_idx_bscan, one workgroup per (group of 8-32
 //    consecutive queries, tile), so each key loaded feeds the whole group.
-//    Both write each score to a slab and add a 512-bin monotone histogram of
-//    the scores into a per-query global histogram.
+//    Both add a 512-bin monotone histogram of the scores into a per-query
+//    global histogram and (up to SLAB_SCAN_MAX entries) write each score to a
+//    slab.
 //  * k_idx_select (one workgroup per query and tile) reads the finished
 //    histogram, derives the threshold bin and keeps the tile's entries at or
-//    above it, in index order.
+//    above it, in index order. A batched scan over more entries keeps no
+//    slab: k_idx_thresh turns each histogram into a threshold score and a
+//    second k_idx_bscan pass rescores the keys and keeps each query's
+//    entries at or above it, per quarter tile, in index order.
 //  * k_idx_final (one workgroup per query) gathers those candidates into LDS,
 //    narrows the threshold to the exact k-th score by radix refinement and
 //    writes the ascending list.
@@ -36,6 +40,11 @@ namespace {
 
 using namespace csa_topk;
 constexpr int PREFILL_MIN_T = 16;
+// Batched scans over more entries than this keep no score slab: they score
+// every tile twice (histograms, then each query's candidates), since storing
+// and re-reading 4 B per (query, entry) costs more than the second scoring
+// pass. Smaller ones keep the slab (the one-workgroup pick reads it).
+constexpr int64_t SLAB_SCAN_MAX = PICK_MAX;
 
 // One 16-entry column tile: A = indexer queries (rows = heads), B = keys
 // (columns = entries). Lane (j + 16g) holds D[head 4g + r][entry j] in
@@ -321,19 +330,27 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
 // byte r of a packed word of int8 head weights, sign-extended
 __device__ inline int wbyte(uint32_t pk, int r) { return (int)(int8_t)(pk >> (8 * r)); }
 
-template <int DI, int HP>
-__global__ __launch_bounds__(256, DI <= 64 ? 4 : 1) void k_idx_bscan(
+// MODE: 0 scores to the slab and the histograms; 1 the histograms only; 2
+// (after k_idx_thresh) each query's candidates, its entries whose score
+// reaches its threshold score s1q (the first score of its threshold bin), as
+// (score, entry) in entry order, one list per wave's quarter of the tile at
+// cbuf[row][tile * TILE + wave * TILE / 4 ..] with its count in
+// cnt4[row][tile][wave] (k_idx_concat then joins the quarters), so that no
+// score row is written or read back.
+template <int DI, int HP, int MODE>
+__global__ __launch_bounds__(256, DI <= 64 ? (MODE == 2 || HP == 16 ? 3 : 4) : 1) void k_idx_bscan(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w,
     const int8_t* __restrict__ keys, int64_t blk_cap, int T, int Hi, int m, int64_t pos0,
     const int64_t* __restrict__ qpos, int64_t npad, int n_groups, int32_t* __restrict__ slab,
-    uint32_t* __restrict__ hist) {
+    uint32_t* __restrict__ hist, const int* __restrict__ s1q, int2* __restrict__ cbuf,
+    int32_t* __restrict__ cnt4, int n_tiles) {
   constexpr int KS = (DI + 63) / 64;
   constexpr int QPT = 16 / HP;
   constexpr int RT = 8 / KS;
   constexpr int QG = RT * QPT;
   constexpr int GPQ = HP / 4;  // lane groups per query in the score layout
   constexpr int BATCH = 4;     // column tiles per load round
-  __shared__ uint32_t lh[QG][NB1];
+  __shared__ uint32_t lh[MODE == 2 ? 1 : QG][NB1];
   const int tile = blockIdx.x;
   const int b = blockIdx.y / n_groups;
   const int t0 = (blockIdx.y - b * n_groups) * QG;  // first query (index within T)
@@ -341,7 +358,8 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 1) void k_idx_bscan(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
 
-  for (int i = threadIdx.x; i < QG * NB1; i += 256) (&lh[0][0])[i] = 0;
+  if (MODE != 2)
+    for (int i = threadIdx.x; i < QG * NB1; i += 256) (&lh[0][0])[i] = 0;
 
   // Query rows and head weights: unconditional loads with clamped indexes.
   // A row of a padding query or head keeps the clamped row: its product is
@@ -389,32 +407,45 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 1) void k_idx_bscan(
       wr[rt] = pk;
     }
   }
-  // the score lanes: lane group g holds query g / GPQ of each row tile; the
-  // first lane group of each query owns its scores
-  const bool owner = (g % GPQ) == 0;
-  // 32-bit per row tile: visible entries and the row offset from the group's
-  // first row, so that nothing 64-bit is kept (or recomputed) per score
-  int my_nv[RT];
-  int my_off[RT];
-  bool my_real[RT];  // padding queries of the last group store nothing
+  // The score lanes. Lane group g's MFMA rows are four heads of query g / GPQ
+  // of each row tile. The head sums go through a transpose: swapping 16-lane
+  // rows between the partial sums of two row tiles (then, for 16 heads, 32-lane
+  // halves between two such pairs) and adding leaves every lane a whole score,
+  // RJ of them, the j-th of row tile GPQ * j + g % GPQ's query g / GPQ. So
+  // lane group g owns the group's query row 4 j + lrow (lrow below) for each
+  // j, and the per-score work after the sums runs on every lane.
+  constexpr int RJ = RT / GPQ;
+  const int lrow = (g % GPQ) * QPT + g / GPQ;
+  // 32-bit per row: visible entries past this wave's first entry (negative
+  // when none), so that nothing 64-bit is kept (or recomputed) per score
+  const int64_t e_wave = (int64_t)tile * TILE + wave * (TILE / 4);
+  const int nv_w = (int)(e_wave < 0x7fffffff ? e_wave : 0x7fffffff);
+  int my_nv[RJ];
+  bool my_real[RJ];  // padding queries of the last group store nothing
+  int s1[RJ], run[RJ];  // emit: threshold score (above every score for padding
+                        // queries) and the running candidate count of the quarter
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int ti = t0 + rt * QPT + g / GPQ;
+  for (int j = 0; j < RJ; ++j) {
+    const int ti = t0 + 4 * j + lrow;
     int64_t nv = (base + ti + 1) / m;
     nv = nv < blk_cap ? nv : blk_cap;
-    my_real[rt] = ti < T;
-    my_nv[rt] = ti < T ? (int)nv : 0;
-    my_off[rt] = ((ti < T ? ti : T - 1) - t0) * (int)npad;
+    my_real[j] = ti < T;
+    my_nv[j] = ti < T ? (int)nv - nv_w : -1;
+    const int sv = MODE == 2 ? s1q[(int64_t)b * T + (ti < T ? ti : T - 1)] : 0;
+    s1[j] = ti < T ? sv : 0x7fffffff;
+    run[j] = 0;
   }
   const int t_last = (t0 + QG < T ? t0 + QG : T) - 1;
   int64_t n_end = (base + t_last + 1) / m;  // entries any query of the group can see
   n_end = n_end < blk_cap ? n_end : blk_cap;
   __syncthreads();
 
-  const int64_t e_wave = (int64_t)tile * TILE + wave * (TILE / 4);
-  // the group's first score row, from this wave's first entry on
-  int32_t* const slab_w = slab + ((int64_t)b * T + t0) * npad + e_wave;
-  const int nv_w = (int)(e_wave < 0x7fffffff ? e_wave : 0x7fffffff);
+  // this lane's first score row (slab, or candidate lists), from this wave's
+  // first entry on; row 4 j + lrow is 4 j rows further
+  int32_t* const slab_w =
+      MODE == 0 ? slab + ((int64_t)b * T + t0 + lrow) * npad + e_wave : nullptr;
+  int2* const cbuf_w = MODE == 2 ? cbuf + ((int64_t)b * T + t0 + lrow) * npad + e_wave : nullptr;
+  uint32_t* const lh_w = &lh[MODE == 2 ? 0 : lrow][0];
   const int8_t* kb = keys + (int64_t)b * blk_cap * DI;
   int coff[KS];
 #pragma unroll
@@ -434,15 +465,14 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 1) void k_idx_bscan(
     };
     // Per score the vector work is kept small (it, not the matrix cores,
     // bounds this kernel): 24-bit multiplies (an int8 weight times a ReLU'd
-    // product of at most DI x 2^14 fits), the cross-lane sum as a ds_swizzle
-    // (xor 16 within 32 lanes, no address register), 32-bit store offsets;
-    // e < npad always holds inside the tile.
+    // product of at most DI x 2^14 fits), the head sums as lane swaps, 32-bit
+    // store offsets; e < npad always holds inside the tile.
     auto consume = [&](int buf, int bt) {
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int el = (bt * BATCH + u) * 16 + i16;  // entry within the wave's range
         // the RT products of the column tile first (independent MFMAs), then
-        // their head sums and cross-lane reductions, then the stores
+        // their head sums, then the stores
         int p[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -455,17 +485,48 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 1) void k_idx_bscan(
                   __mul24(wbyte(wr[rt], 2), max(acc[2], 0)) +
                   __mul24(wbyte(wr[rt], 3), max(acc[3], 0));
         }
+        int sj[RJ];
+        if constexpr (GPQ == 1) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          if (GPQ >= 2) p[rt] += __builtin_amdgcn_ds_swizzle(p[rt], 0x401F);  // lane ^ 16
-          if (GPQ >= 4) p[rt] += __shfl_xor(p[rt], 32, 64);
+          for (int j = 0; j < RJ; ++j) sj[j] = p[j];
+        } else {
+          // rows 16-31 of p[2i] trade places with rows 0-15 of p[2i + 1] (and
+          // 48-63 with 32-47): the sum holds row tile 2i + (g & 1)
+          int h[RT / 2];
+#pragma unroll
+          for (int i = 0; i < RT / 2; ++i) {
+            const auto r = __builtin_amdgcn_permlane16_swap(p[2 * i], p[2 * i + 1], false, false);
+            h[i] = (int)r[0] + (int)r[1];
+          }
+          if constexpr (GPQ == 2) {
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) sj[j] = h[j];
+          } else {
+            // lanes 32-63 of h[2j] trade places with lanes 0-31 of h[2j + 1]:
+            // the sum holds row tile 4j + g
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+              const auto r = __builtin_amdgcn_permlane32_swap(h[2 * j], h[2 * j + 1], false, false);
+              sj[j] = (int)r[0] + (int)r[1];
+            }
+          }
         }
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          if (owner && my_real[rt]) {
-            const int sc = el < my_nv[rt] - nv_w ? p[rt] : -1;
-            slab_w[my_off[rt] + el] = sc;
-            if (sc >= 0) atomicAdd(&lh[rt * QPT + g / GPQ][score_bin512(sc)], 1u);
+        for (int j = 0; j < RJ; ++j) {
+          const int sc = el < my_nv[j] ? sj[j] : -1;
+          if constexpr (MODE == 2) {
+            // the row's candidates of this column tile (the threshold score
+            // is >= 0, so an invisible entry's -1 never passes), ranked
+            // within its 16 lanes by a ballot
+            const bool c = sc >= s1[j];
+            const uint32_t gb = (uint32_t)(__ballot(c) >> (16 * g)) & 0xffffu;
+            if (c)
+              cbuf_w[4 * j * (int)npad + run[j] + __popc(gb & ((1u << i16) - 1u))] =
+                  int2{sc, (int)(e_wave + el)};
+            run[j] += __popc(gb);
+          } else {
+            if (MODE == 0 && my_real[j]) slab_w[4 * j * (int)npad + el] = sc;
+            if (sc >= 0) atomicAdd(&lh_w[4 * j * NB1 + score_bin512(sc)], 1u);
           }
         }
       }
@@ -477,6 +538,14 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 1) void k_idx_bscan(
       consume(bt & 1, bt);
     }
   }
+  if constexpr (MODE == 2) {
+    // every real row's count of this quarter (zero where the wave saw nothing)
+#pragma unroll
+    for (int j = 0; j < RJ; ++j)
+      if (i16 == 0 && my_real[j])
+        cnt4[(((int64_t)b * T + t0 + 4 * j + lrow) * n_tiles + tile) * 4 + wave] = run[j];
+    return;
+  }
   // (slab entries past a query's visible range are never read)
   __syncthreads();
   for (int i = threadIdx.x; i < QG * NB1; i += 256) {
@@ -484,6 +553,58 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 1) void k_idx_bscan(
     const uint32_t c = (&lh[0][0])[i];
     if (c && t0 + ql < T) atomicAdd(&hist[((int64_t)b * T + t0 + ql) * NB1 + (i % NB1)], c);
   }
+}
+
+// Each query's threshold score for the candidate pass of k_idx_bscan: the
+// least score whose bin reaches the query's threshold bin (the bin where the
+// count from the top reaches min(k, visible entries)), found by bisection on
+// the monotone bin map, so that "score >= it" is exactly "bin >= threshold
+// bin"; INT_MAX (above every score) when the query sees no entry.
+__global__ __launch_bounds__(256) void k_idx_thresh(const uint32_t* __restrict__ hist, int k,
+                                                    int* __restrict__ s1q) {
+  __shared__ int tmp[4];
+  __shared__ int s_red[2];
+  const int qi = blockIdx.x;
+  const int keff = threshold_bin(hist + (int64_t)qi * NB1, k, tmp, s_red);
+  if (threadIdx.x != 0) return;
+  if (keff == 0) {
+    s1q[qi] = 0x7fffffff;
+    return;
+  }
+  const int T1 = s_red[0];
+  int lo = 0, hi = 0x7fffffff;  // bin(hi) >= T1 holds or hi is the sentinel
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (score_bin512(mid) >= T1) hi = mid;
+    else lo = mid + 1;
+  }
+  s1q[qi] = lo;
+}
+
+// Joins the four quarter lists of a (query, tile) that the candidate pass of
+// k_idx_bscan wrote into one list in entry order at the tile's start, with
+// its count, as k_idx_select would have left them for k_idx_final. The moved
+// quarters go through LDS, so every read precedes every write.
+__global__ __launch_bounds__(256) void k_idx_concat(int2* __restrict__ cbuf,
+                                                    const int32_t* __restrict__ cnt4,
+                                                    int32_t* __restrict__ cnt, int64_t npad,
+                                                    int n_tiles) {
+  constexpr int QL = TILE / 4;  // entries of a quarter
+  __shared__ int2 st[TILE];
+  const int tile = blockIdx.x, qi = blockIdx.y;
+  const int4 c = *reinterpret_cast<const int4*>(cnt4 + ((int64_t)qi * n_tiles + tile) * 4);
+  const int total = c.x + c.y + c.z + c.w;
+  if (threadIdx.x == 0) cnt[(int64_t)qi * n_tiles + tile] = total;
+  if (total == c.x) return;  // the first quarter's list is the whole list, in place
+  int2* base = cbuf + (int64_t)qi * npad + (int64_t)tile * TILE;
+  // wave q moves quarter q (q >= 1) behind the quarters before it
+  const int wq = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cw = wq == 1 ? c.y : (wq == 2 ? c.z : c.w);
+  const int pre = c.x + (wq >= 2 ? c.y : 0) + (wq >= 3 ? c.z : 0);
+  if (wq > 0)
+    for (int j = lane; j < cw; j += 64) st[pre + j] = base[wq * QL + j];
+  __syncthreads();
+  for (int j = c.x + (int)threadIdx.x; j < total; j += 256) base[j] = st[j];
 }
 
 // One selection of the select and final passes: over the entries themselves,
@@ -499,6 +620,7 @@ struct Level {
   int spec_tiles, spec_shift;
   int32_t* out;         // [BT][k << gshift]
   int32_t* out_score;   // [BT][k] or null (entries only)
+  int seg_shift = 11;   // the final pass's lists: cbuf[row][t << seg_shift], cnt[row][t]
 };
 
 // ------------------------------------------------------------------------
@@ -632,7 +754,7 @@ __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
   int32_t* oi = L.out + ((int64_t)qi * k << gs);
   int32_t* os = L.out_score ? L.out_score + (int64_t)qi * k : nullptr;
   const int32_t* cqq = cand ? cand + (int64_t)qi * C : nullptr;
-  const FinalPlan P{L.n_tiles, k, L.spec_tiles, L.spec_shift, cap_lds, toff_n};
+  const FinalPlan P{L.n_tiles, k, L.spec_tiles, L.spec_shift, cap_lds, toff_n, L.seg_shift};
   const int keff = final_select(
       hq, L.cnt + (int64_t)qi * L.n_tiles, L.cbuf + (int64_t)qi * L.npad, P, smem, bh, tmp, s_red,
       [&](int pos, int e, int sv) {
@@ -752,20 +874,52 @@ static int idx_phase(const IdxArgs& a, int phase) {
     CSA_TRY_LAUNCH();
     return CSA_OK;
   }
+  // a batched scan without the slab (SLAB_SCAN_MAX): the slab's space holds
+  // each query's threshold score [BT], then its per-quarter candidate counts
+  // [BT][n_tiles][4]
+  const bool rescan = batched_plan(a) && n_max > SLAB_SCAN_MAX;
+  int* s1q = slab;
+  int32_t* cnt4 = slab + align_up(BT, 64);
+  // the final pass takes the quarter lists as they are while their number
+  // fits its per-list registers (MAX_TILES); beyond that they are joined per
+  // tile first
+  const bool quarters = rescan && 4 * (int64_t)L.n_tiles <= MAX_TILES;
   if (phase == 0 && batched_plan(a)) {
     const int HP = a.Hi <= 4 ? 4 : (a.Hi <= 8 ? 8 : 16);
     const int KS = (a.Di + 63) / 64;
     const int QG = (8 / KS) * (16 / HP);
     const int n_groups = (a.T + QG - 1) / QG;
     const dim3 bgrid(L.n_tiles, a.B * n_groups);
-#define CSA_LAUNCH_BSCAN(DD, HH)                                                           \
-  hipLaunchKernelGGL((k_idx_bscan<DD, HH>), bgrid, dim3(256), 0, a.stream, a.q_idx, a.w,  \
-                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.pos, L.npad, n_groups, slab, hist)
-#define CSA_LAUNCH_BSCAN_H(DD) \
-  if (HP == 4) CSA_LAUNCH_BSCAN(DD, 4); else if (HP == 8) CSA_LAUNCH_BSCAN(DD, 8); else CSA_LAUNCH_BSCAN(DD, 16)
-    if (a.Di == 32) { CSA_LAUNCH_BSCAN_H(32); }
-    else if (a.Di == 64) { CSA_LAUNCH_BSCAN_H(64); }
-    else { CSA_LAUNCH_BSCAN_H(128); }
+#define CSA_LAUNCH_BSCAN(DD, HH, MM)                                                           \
+  hipLaunchKernelGGL((k_idx_bscan<DD, HH, MM>), bgrid, dim3(256), 0, a.stream, a.q_idx, a.w,  \
+                     a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.pos, L.npad, n_groups, slab,  \
+                     hist, s1q, cbuf, cnt4, L.n_tiles)
+#define CSA_LAUNCH_BSCAN_H(DD, MM)                                                  \
+  do {                                                                              \
+    if (HP == 4) CSA_LAUNCH_BSCAN(DD, 4, MM);                                       \
+    else if (HP == 8) CSA_LAUNCH_BSCAN(DD, 8, MM);                                  \
+    else CSA_LAUNCH_BSCAN(DD, 16, MM);                                              \
+  } while (0)
+#define CSA_LAUNCH_BSCAN_D(MM)                                                      \
+  do {                                                                              \
+    if (a.Di == 32) CSA_LAUNCH_BSCAN_H(32, MM);                                     \
+    else if (a.Di == 64) CSA_LAUNCH_BSCAN_H(64, MM);                                \
+    else CSA_LAUNCH_BSCAN_H(128, MM);                                               \
+  } while (0)
+    if (!rescan) {
+      CSA_LAUNCH_BSCAN_D(0);
+    } else {
+      // histograms; each query's threshold score; its candidates per wave
+      // quarter (joined per tile, as the select pass leaves them, only past
+      // MAX_TILES / 4 tiles)
+      CSA_LAUNCH_BSCAN_D(1);
+      hipLaunchKernelGGL(k_idx_thresh, dim3(BT), dim3(256), 0, a.stream, hist, a.k, s1q);
+      CSA_LAUNCH_BSCAN_D(2);
+      if (!quarters)
+        hipLaunchKernelGGL(k_idx_concat, dim3(L.n_tiles, BT), dim3(256), 0, a.stream, cbuf,
+                           cnt4, cnt, L.npad, L.n_tiles);
+    }
+#undef CSA_LAUNCH_BSCAN_D
 #undef CSA_LAUNCH_BSCAN_H
 #undef CSA_LAUNCH_BSCAN
   } else if (phase == 0) {
@@ -810,26 +964,25 @@ static int idx_phase(const IdxArgs& a, int phase) {
 #undef CSA_LAUNCH_SCAN_S
 #undef CSA_LAUNCH_SCAN
 #undef CSA_LAUNCH_SCAN1
-  } else if (phase == 2) {
-    // the per-tile select pass alone: an in-kernel selection resolves the
-    // top-k from its lists (csa_index_attn)
-    Level L0{slab, cbuf, cnt, hist, L.npad, L.n_tiles, a.k, 0, 0, 0, a.out_idx, a.out_score};
-    Level L1{};
-    hipLaunchKernelGGL(k_idx_select, dim3(L.n_tiles, BT), dim3(256), 0, a.stream, a.T, a.m,
-                       a.pos0, a.pos, a.blk_cap, C, a.cand != nullptr, L0, L1);
   } else if (phase == 1) {
     Level L0{slab, cbuf, cnt, hist, L.npad, L.n_tiles, a.k, 0, 0, 0, a.out_idx, a.out_score};
     Level L1{gslab, gcbuf, gcnt, ghist, L.gpad, L.g_tiles, a.n_keep, 3, 0, 0, a.out_pool,
              nullptr};
+    if (quarters) {  // the scan's quarter-tile lists and counts
+      L0.cnt = cnt4;
+      L0.n_tiles = 4 * L.n_tiles;
+      L0.seg_shift = __builtin_ctz(TILE / 4);
+    }
     const bool compact = BT >= FINAL_COMPACT_BT;
-    const int toff_n = ((L.n_tiles > L.g_tiles ? L.n_tiles : L.g_tiles) + 3) / 4 * 4;
+    const int toff_n = ((L0.n_tiles > L.g_tiles ? L0.n_tiles : L.g_tiles) + 3) / 4 * 4;
     const int cap_lds = select_cap(pool && a.n_keep > a.k ? a.n_keep : a.k, toff_n,
                                    compact ? 2048 : 4096);
     const int slots = compact && cap_lds < SPEC_SLOTS ? cap_lds : SPEC_SLOTS;
-    spec_plan(L.n_tiles, slots, &L0.spec_tiles, &L0.spec_shift);
+    spec_plan(L0.n_tiles, slots, &L0.spec_tiles, &L0.spec_shift, TILE >> (quarters ? 2 : 0));
     if (pool) spec_plan(L.g_tiles, slots, &L1.spec_tiles, &L1.spec_shift);
-    hipLaunchKernelGGL(k_idx_select, dim3(L.n_tiles + L.g_tiles, BT), dim3(256), 0, a.stream,
-                       a.T, a.m, a.pos0, a.pos, a.blk_cap, C, a.cand != nullptr, L0, L1);
+    if (!rescan)  // (the candidate pass of a rescan left the lists already)
+      hipLaunchKernelGGL(k_idx_select, dim3(L.n_tiles + L.g_tiles, BT), dim3(256), 0, a.stream,
+                         a.T, a.m, a.pos0, a.pos, a.blk_cap, C, a.cand != nullptr, L0, L1);
     const int spec_slots = (L0.spec_tiles << L0.spec_shift) >
                                    (pool ? (L1.spec_tiles << L1.spec_shift) : 0)
                                ? (L0.spec_tiles << L0.spec_shift)

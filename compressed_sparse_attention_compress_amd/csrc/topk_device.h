@@ -323,9 +323,11 @@ __device__ inline int pick_select(const int32_t* sq, const uint32_t* hq, int N, 
 }
 
 // ------------------------------------------------------------------------
-// Selection from the per-tile candidate lists the select pass leaves:
-// tile t of the query holds cnt[t] (score, entry) pairs at or above the
-// threshold bin, in entry order, at cq[t * TILE ...].
+// Selection from per-segment candidate lists (the select pass's per-tile
+// lists, or the batched scan's quarter-tile lists): segment t of the query
+// holds cnt[t] (score, entry) pairs at or above the threshold bin, in entry
+// order, at cq[t << seg_shift ...]; segments follow each other in entry
+// order, and "tile" below means a segment.
 //
 // One round of loads brings the histogram bins, the tile counts and the
 // first 2^spec_shift candidates of each of the first spec_tiles tiles
@@ -345,8 +347,11 @@ __device__ inline int pick_select(const int32_t* sq, const uint32_t* hq, int N, 
 // arrays), then the stage's scores and entries [spec_tiles << spec_shift]
 // ints each.
 // ------------------------------------------------------------------------
+// n_tiles candidate lists (segments), list t at cq[t << seg_shift] with its
+// count at cntq[t]: the select pass's per-tile lists (seg_shift = log2 TILE),
+// or the batched scan's quarter-tile lists (log2 TILE / 4)
 struct FinalPlan {
-  int n_tiles, k, spec_tiles, spec_shift, cap, toff_n;
+  int n_tiles, k, spec_tiles, spec_shift, cap, toff_n, seg_shift;
 };
 
 __host__ __device__ inline size_t final_lds_bytes(const FinalPlan& p) {
@@ -379,7 +384,7 @@ __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, cons
   for (int u = 0; u < SPT; u += 2) {  // pairs of slots: one 16-byte load each
     const int i = i0 + u < nspec ? i0 + u : 0;
     const int4 v = *reinterpret_cast<const int4*>(
-        cq + (int64_t)(i >> P.spec_shift) * TILE + (i & (spt - 1)));
+        cq + ((int64_t)(i >> P.spec_shift) << P.seg_shift) + (i & (spt - 1)));
     r[u] = int2{v.x, v.y};
     r[u + 1] = int2{v.z, v.w};
   }
@@ -457,7 +462,7 @@ __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, cons
           sv = sp_s[(tl << P.spec_shift) + j];
           ev = sp_e[(tl << P.spec_shift) + j];
         } else {
-          const int2 v = cq[(int64_t)tl * TILE + j];
+          const int2 v = cq[((int64_t)tl << P.seg_shift) + j];
           sv = v.x;
           ev = v.y;
         }
@@ -488,7 +493,7 @@ __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, cons
   for (int tl = wave; tl < n_tiles; tl += 4) {
     const int c = t_cnt[tl];
     for (int j = lane; j < c; j += 64) {
-      const int sv = cq[(int64_t)tl * TILE + j].x;
+      const int sv = cq[((int64_t)tl << P.seg_shift) + j].x;
       if (score_bin512(sv) == T1) {
         vmin = min(vmin, sv);
         vmax = max(vmax, sv);
@@ -506,7 +511,7 @@ __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, cons
     for (int tl = wave; tl < n_tiles; tl += 4) {
       const int c = t_cnt[tl];
       for (int j = lane; j < c; j += 64) {
-        const int sv = cq[(int64_t)tl * TILE + j].x;
+        const int sv = cq[((int64_t)tl << P.seg_shift) + j].x;
         if (score_bin512(sv) == T1 && sv >= lo && sv - lo <= R)
           atomicAdd(&bh[(sv - lo) >> shift], 1u);
       }
@@ -532,7 +537,7 @@ __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, cons
     const int c = t_cnt[tl];
     int gt = 0, eq = 0;
     for (int j = lane; j < c; j += 64) {
-      const int sv = cq[(int64_t)tl * TILE + j].x;
+      const int sv = cq[((int64_t)tl << P.seg_shift) + j].x;
       gt += sv > tau;
       eq += sv == tau;
     }
@@ -563,7 +568,7 @@ __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, cons
     for (int j0 = 0; j0 < c; j0 += 64) {
       const int j = j0 + lane;
       int2 v = int2{-1, -1};
-      if (j < c) v = cq[(int64_t)tl * TILE + j];
+      if (j < c) v = cq[((int64_t)tl << P.seg_shift) + j];
       const bool is_eq = j < c && v.x == tau;
       const uint64_t meq = __ballot(is_eq);
       const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -1018,11 +1023,12 @@ inline int select_cap(int k, int toff_n, int least) {
 }
 
 // Speculative first-round candidates: a stage of `slots` shared out evenly,
-// a power of two per tile between 8 and TILE (at least 8 so that every tile
-// of a context up to slots/8 tiles is staged and the direct path can apply).
-inline void spec_plan(int n_tiles, int slots, int* spec_tiles, int* spec_shift) {
+// a power of two per list between 8 and the list's capacity `seg` (at least 8
+// so that every list of a context up to slots/8 lists is staged and the
+// direct path can apply).
+inline void spec_plan(int n_tiles, int slots, int* spec_tiles, int* spec_shift, int seg = TILE) {
   int sh = 3;
-  while ((1 << (sh + 1)) <= TILE && ((int64_t)n_tiles << (sh + 1)) <= slots) ++sh;
+  while ((1 << (sh + 1)) <= seg && ((int64_t)n_tiles << (sh + 1)) <= slots) ++sh;
   *spec_shift = sh;
   *spec_tiles = n_tiles < (slots >> sh) ? n_tiles : (slots >> sh);
 }

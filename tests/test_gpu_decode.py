@@ -164,6 +164,10 @@ def test_index_ragged_prefill():
     say("index ragged prefill")
     _ragged_index_case(20, 8, 64, 4, [3000, 0, 4 * 1500 + 1], 6100, 40, 1600, seed=75)
     _ragged_index_case(33, 4, 32, 4, [100, 7000], 7000, 64, 1800, seed=76)
+    # over 8,192 entries (no score slab): one sequence at the start, one past
+    # the slab limit, one in the middle, with ragged tiles
+    _ragged_index_case(17, 8, 64, 4, [30, 4 * 11000 + 3, 4 * 5000], 4 * 11000 + 3, 300, 11050,
+                       seed=77, phases=True)
 
 
 # ------------------------------------------------------ ragged attention ----

@@ -170,6 +170,22 @@ def test_index_attn_tie_storm_and_clusters():
     _compare(xc, 4, L - 1, 1024, 128, torch.bfloat16, oracle_seqs=(1,))
 
 
+@pytest.mark.parametrize("Hi,Di", [(4, 32), (16, 64), (8, 128), (3, 64)])
+def test_index_attn_recomputed_scores(Hi, Di):
+    """A top-k packed into one 2048-entry unit (every key of the unit scores
+    high) overflows even the unit's wide list, so the selection walks the
+    whole score row, recomputing each score from the keys and the indexer
+    query (the list scan writes no score slab): exact against the separate
+    calls and the oracle for other indexer shapes."""
+    say("index_attn recomputed scores", Hi, Di)
+    B, L = 2, 4 * 30000
+    x = _world(11, B, L, 256, 20, 4, Hi, Di)
+    keys = x["keys"].clone()
+    keys[:, 4096:6144] = 7
+    qi = x["q_idx"].abs().to(torch.int8)
+    _compare(dict(x, keys=keys, q_idx=qi), 4, L - 1, 512, 128, torch.bfloat16, oracle_seqs=(0, 1))
+
+
 @pytest.mark.parametrize("k", [512, 1024])
 def test_index_attn_dense_topk_spills(k):
     """A top-k dense in a short context (12,000 entries in 24 units of 512):

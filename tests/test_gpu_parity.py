@@ -307,6 +307,29 @@ def test_index_prefill_edges():
     _index_case(1, 17, 8, 64, 1, 1000, 600, 1100, seed=21)
 
 
+@pytest.mark.parametrize("Hi,Di", [(4, 32), (8, 64), (16, 64), (2, 128), (5, 64), (16, 32),
+                                   (8, 128)])
+def test_index_prefill_rescan_shapes(Hi, Di):
+    """Query runs over more than 8,192 visible entries keep no score slab: the
+    batched scan runs twice (histograms, then each query's candidates per wave
+    quarter, joined per tile). 37 queries (a ragged last query group) over
+    10,037 entries (a ragged last tile), every query against the oracle."""
+    say("index prefill rescan", Hi, Di)
+    _index_case(2, 37, Hi, Di, 4, 4 * 10000 + 3, 200, 10040, seed=90)
+
+
+def test_index_prefill_rescan_edges():
+    say("index prefill rescan edges")
+    # scan and select as separate calls; k above a tile; k = 1
+    _index_case(1, 20, 8, 64, 4, 4 * 9000, 2500, 9100, seed=91, phases=True)
+    _index_case(1, 16, 8, 64, 4, 4 * 9000, 1, 9100, seed=92)
+    # every score tied; keys of one value (every entry a candidate of its tile)
+    _index_case(1, 18, 8, 64, 4, 4 * 8500, 700, 8600, seed=93, wzero=True)
+    _index_case(1, 24, 4, 32, 4, 4 * 8500, 300, 8600, seed=94, keyrange=1)
+    # a run whose first queries see fewer than 8,192 entries and its last more
+    _index_case(1, 400, 8, 64, 1, 8000, 64, 8500, seed=95, sample=60)
+
+
 def test_index_tiny_workload():
     """All 1024 queries of the tiny causal workload (Hi=4, Di=32, k=16)."""
     say("index tiny_causal")
