@@ -48,22 +48,29 @@ constexpr int64_t SLAB_SCAN_MAX = PICK_MAX;
 
 // One 16-entry column tile: A = indexer queries (rows = heads), B = keys
 // (columns = entries). Lane (j + 16g) holds D[head 4g + r][entry j] in
-// acc[r]; after the weighted ReLU and the sum over the four lane groups every
-// lane j + 16g returns the score of entry j.
+// acc[r] and returns its four heads' part of entry j's score: the weighted
+// ReLU as 24-bit multiplies (an int8 weight times a ReLU'd product of at most
+// DI x 2^14 fits).
 template <int KS>
-__device__ inline int score_tile(const v4i (&A)[KS], const v4i (&Bk)[KS], const int (&wr)[4]) {
+__device__ inline int score_part(const v4i (&A)[KS], const v4i (&Bk)[KS], const int (&wr)[4]) {
   v4i acc = {0, 0, 0, 0};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[ks], Bk[ks], acc, 0, 0, 0);
-  // 24-bit multiplies (an int8 weight times a ReLU'd product of at most
-  // DI x 2^14 fits), the sum over lane groups as a swizzle (xor 16 within 32
-  // lanes) and one permute (xor 32) whose address is fixed per lane
-  int p = __mul24(wr[0], max(acc[0], 0)) + __mul24(wr[1], max(acc[1], 0)) +
-          __mul24(wr[2], max(acc[2], 0)) + __mul24(wr[3], max(acc[3], 0));
-  p += __builtin_amdgcn_ds_swizzle(p, 0x401F);
-  p += __builtin_amdgcn_ds_bpermute((int)((threadIdx.x & 63) ^ 32) << 2, p);
-  return p;
+  return __mul24(wr[0], max(acc[0], 0)) + __mul24(wr[1], max(acc[1], 0)) +
+         __mul24(wr[2], max(acc[2], 0)) + __mul24(wr[3], max(acc[3], 0));
+}
+
+// The parts of four column tiles (p[u] in every lane group) summed over the
+// lane groups by a transpose: 16-lane rows of tiles 0/1 and 2/3 trade
+// places, then 32-lane halves of the two pairs, and the sums leave lane
+// (j + 16g) the whole score of tile g, entry j.
+__device__ inline int quad_scores(int p0, int p1, int p2, int p3) {
+  const auto a = __builtin_amdgcn_permlane16_swap(p0, p1, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(p2, p3, false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap((int)a[0] + (int)a[1], (int)c[0] + (int)c[1],
+                                                  false, false);
+  return (int)h[0] + (int)h[1];
 }
 
 // The scan unit's short lists (k_idx_scan's LISTS tail). Its cut bin is the
@@ -249,16 +256,19 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
       }
     };
     auto consume = [&](int buf, int bt, const v4i (&Aq)[KS]) {
-      int sc[BATCH];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int s = score_tile<KS>(Aq, Bk[buf][u], wr);
-        sc[u] = valid[buf][u] ? s : -1;
-      }
+      // an invalid entry's part is -2^28 in every lane group (validity does
+      // not depend on the group), so its sum is negative and stored as -1;
+      // a valid entry's parts are >= 0 and their sum is its score
       // lane (j + 16g) takes tile 4h+g, entry j
 #pragma unroll
       for (int h = 0; h < BATCH / 4; ++h) {
-        const int v = g == 0 ? sc[4 * h] : (g == 1 ? sc[4 * h + 1] : (g == 2 ? sc[4 * h + 2] : sc[4 * h + 3]));
+        int sc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int s = score_part<KS>(Aq, Bk[buf][4 * h + u], wr);
+          sc[u] = valid[buf][4 * h + u] ? s : -(1 << 28);
+        }
+        const int v = max(quad_scores(sc[0], sc[1], sc[2], sc[3]), -1);
         const int64_t e = tile_e(bt, 4 * h + g) + i16;
         if (e < N) {
           ssc[e - wg0] = v;
