@@ -523,11 +523,11 @@ __global__ __launch_bounds__(256, DI <= 64 ? (MODE == 2 || HP == 16 ? 3 : 4) : 1
         }
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-          const int sc = el < my_nv[j] ? sj[j] : -1;
           if constexpr (MODE == 2) {
             // the row's candidates of this column tile (the threshold score
             // is >= 0, so an invisible entry's -1 never passes), ranked
             // within its 16 lanes by a ballot
+            const int sc = el < my_nv[j] ? sj[j] : -1;
             const bool c = sc >= s1[j];
             const uint32_t gb = (uint32_t)(__ballot(c) >> (16 * g)) & 0xffffu;
             if (c)
@@ -535,8 +535,16 @@ __global__ __launch_bounds__(256, DI <= 64 ? (MODE == 2 || HP == 16 ? 3 : 4) : 1
                   int2{sc, (int)(e_wave + el)};
             run[j] += __popc(gb);
           } else {
-            if (MODE == 0 && my_real[j]) slab_w[4 * j * (int)npad + el] = sc;
-            if (sc >= 0) atomicAdd(&lh_w[4 * j * NB1 + score_bin512(sc)], 1u);
+            // An entry the row cannot see yet is counted in bin 0 (its score
+            // taken as 0) and taken out of it again after the loop, so no
+            // branch is needed; its slab value is never read (reads stop at
+            // the row's visible entries). Scores are >= 0, so the bin is
+            // max(float bits >> 19, 2031) - 2031 (score_bin512 without its
+            // test for s <= 0).
+            const int sc = el < my_nv[j] ? sj[j] : 0;
+            if (MODE == 0 && my_real[j]) slab_w[4 * j * (int)npad + el] = sj[j];
+            const uint32_t bk = max(__float_as_uint((float)(uint32_t)sc) >> 19, 2031u) - 2031u;
+            atomicAdd(&lh_w[4 * j * NB1 + (int)bk], 1u);
           }
         }
       }
@@ -546,6 +554,14 @@ __global__ __launch_bounds__(256, DI <= 64 ? (MODE == 2 || HP == 16 ? 3 : 4) : 1
     for (int bt = 0; bt < NBT; ++bt) {
       if (bt + 1 < NBT) issue((bt + 1) & 1, bt + 1);
       consume(bt & 1, bt);
+    }
+    if constexpr (MODE != 2) {
+      // the wave's TILE / 4 entries each row could not see, counted in bin 0
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) {
+        const int vis = my_nv[j] < 0 ? 0 : (my_nv[j] > TILE / 4 ? TILE / 4 : my_nv[j]);
+        if (i16 == 0 && vis < TILE / 4) atomicSub(&lh_w[4 * j * NB1], (uint32_t)(TILE / 4 - vis));
+      }
     }
   }
   if constexpr (MODE == 2) {
