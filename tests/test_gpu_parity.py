@@ -328,6 +328,9 @@ def test_index_prefill_rescan_edges():
     _index_case(1, 24, 4, 32, 4, 4 * 8500, 300, 8600, seed=94, keyrange=1)
     # a run whose first queries see fewer than 8,192 entries and its last more
     _index_case(1, 400, 8, 64, 1, 8000, 64, 8500, seed=95, sample=60)
+    # more than 2,048 quarter lists (over 1,048,576 entries): the quarters are
+    # joined per tile before the final pass
+    _index_case(1, 16, 8, 64, 4, 4 * 1050000, 64, 1050040, seed=96, sample=4)
 
 
 def test_index_tiny_workload():
