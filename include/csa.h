@@ -186,7 +186,8 @@ int csa_decode_append(const float* kv, int64_t kv_ld, const float* gate,
  * number of candidates a query can have: C when a pool is given, else
  * min(blk_cap, (pos0+T)/m). The size is about B*T*n_max*12 bytes (a score
  * and a candidate slot per entry), e.g. 3 GiB for an 8192-query chunk at
- * 32,768 visible blocks.
+ * 32,768 visible blocks (a run that keeps no scores uses the score part only
+ * for per-query thresholds and per-list counts).
  * ------------------------------------------------------------------------- */
 int64_t csa_index_topk_workspace(int B, int T, int64_t n_max, int k, int cand_given);
 
@@ -224,13 +225,18 @@ int csa_index_select_ragged(const int8_t* q_idx, const int8_t* w, const int8_t* 
                             int32_t* out_idx, int32_t* out_score,
                             void* workspace, int64_t ws_bytes, hipStream_t stream);
 
-/* The two launches csa_index_topk makes, exposed so a caller can place events
+/* The two phases csa_index_topk runs, exposed so a caller can place events
  * or other work between them: csa_index_topk == csa_index_scan followed by
- * csa_index_select with identical arguments. Scan computes every exact score
- * into the workspace (one key stream per query for T < 16 or a pool; for
- * runs of T >= 16 queries one key stream per group of 8-32 queries) plus a
- * per-query score histogram; select turns them into the sorted index list.
- * For a candidate pool of at most 4096 entries, select is one workgroup per
+ * csa_index_select with identical arguments (the workspace carries state from
+ * one to the other, so k and every other argument must match). Scan computes
+ * every exact score (one key stream per query for T < 16 or a pool; for runs
+ * of T >= 16 queries one key stream per group of 8-32 queries) and a
+ * per-query score histogram, and keeps the scores in the workspace; select
+ * turns them into the sorted index list. A run of T >= 16 queries over more
+ * than 8,192 entries keeps no scores: its scan scores the keys twice (the
+ * histograms, then each query's entries at or above its threshold bin as
+ * candidate lists) and its select is the final selection alone. For at most
+ * 8,192 candidates (a pool, or a short context), select is one workgroup per
  * query that reads the query's whole score row (one launch instead of two). */
 int csa_index_scan(const int8_t* q_idx, const int8_t* w, const int8_t* keys,
                    int64_t blk_cap, int B, int T, int Hi, int Di, int m, int64_t pos0,
