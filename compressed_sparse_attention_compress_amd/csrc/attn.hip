@@ -643,9 +643,44 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
   // a row outside float16's range anywhere in the workgroup makes the whole
   // output of the query NaN (a split's NaN partial carries into the merge)
   const bool bad = __syncthreads_or(out_of_range ? 1 : 0) != 0;
-  if (head >= H) return;
   const float inv = bad ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
   // output register r of tile ct: channel half (d/2) + 32 ct + 8 (r / 4) + 4 gg + r % 4
+  if (nsplit == 1 && out_dtype != CSA_F32) {
+    // bfloat16 output of a whole query through LDS (the stage is free now):
+    // each lane's 8-byte pieces sit 1 KB apart in the output (one head per
+    // lane), so they are written into a head-major copy first and then leave
+    // in 16-byte pieces, 1 KB contiguous per wave instruction
+    constexpr int OROW = D + 8;  // bfloat16 per LDS row (16 B past the row)
+    static_assert(NWV * 32 / 2 * OROW * 2 <= STAGE_BYTES + LOGIT_BYTES, "output rows fit");
+    __bf16* ol = reinterpret_cast<__bf16*>(s_raw);
+    typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+    const int hl = hg * 32 + i32;  // the lane's head within the workgroup
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = half * (D / 2) + 32 * ct + 8 * q4 + 4 * gg;
+        const v4bf v = {(__bf16)(O[ct][4 * q4] * inv), (__bf16)(O[ct][4 * q4 + 1] * inv),
+                        (__bf16)(O[ct][4 * q4 + 2] * inv), (__bf16)(O[ct][4 * q4 + 3] * inv)};
+        *reinterpret_cast<v4bf*>(ol + hl * OROW + c) = v;
+      }
+    __syncthreads();
+    constexpr int CPR = D / 8;               // 16-byte pieces per row
+    constexpr int PIECES = NWV * 16 * CPR;   // rows = NG * 32 heads
+    __bf16* ob = reinterpret_cast<__bf16*>(out) + (int64_t)qi * H * D;
+#pragma unroll
+    for (int i = threadIdx.x; i < PIECES; i += NT) {
+      const int row = i / CPR, cp = i % CPR;
+      if (row < H)
+        *reinterpret_cast<uint4*>(ob + (int64_t)row * D + 8 * cp) =
+            *reinterpret_cast<const uint4*>(ol + row * OROW + 8 * cp);
+    }
+    if (lse && head < H && half == 0 && gg == 0)
+      lse[(int64_t)qi * H + head] =
+          bad ? __builtin_nanf("") : (m_run + log2f(l_tot)) * 0.69314718055994531f;
+    return;
+  }
+  if (head >= H) return;
   if (nsplit == 1) {
     const int64_t base = ((int64_t)qi * H + head) * D + half * (D / 2) + 4 * gg;
 #pragma unroll
@@ -869,6 +904,7 @@ static void launch_attn(const AttnArgs& a, const AttnPlan& p, float* part_o, flo
                      a.sel != SEL_IDX ? a.sa.hist : nullptr)
     if (p.nsplit <= 8) CSA_LAUNCH_MERGE(8);
     else if (p.nsplit <= 16) CSA_LAUNCH_MERGE(16);
+    else if (p.nsplit <= 24) CSA_LAUNCH_MERGE(24);
     else CSA_LAUNCH_MERGE(MERGE_MAX);
 #undef CSA_LAUNCH_MERGE
   }
