@@ -203,6 +203,17 @@ def test_index_decode_edges():
     _index_case(2, 2, 8, 64, 4, 4 * 20000, 1000, 20000, seed=13, phases=True)
 
 
+def test_index_large_k_few_queries():
+    """A Full layer's candidate pool: few queries with k >= 2048 over up to
+    1,048,576 entries (the final pass's stage then holds few candidates per
+    list), ties, and k above the visible entries."""
+    say("index large k")
+    _index_case(3, 1, 8, 64, 4, 4 * 200000 - 1, 4096, 200000, seed=97)
+    _index_case(2, 2, 8, 64, 4, 4 * 150000, 2048, 150010, seed=98, keyrange=1)
+    _index_case(2, 1, 4, 32, 4, 4 * 9000, 10000, 9100, seed=99)
+    _index_case(2, 1, 8, 64, 4, 4 * 1048575, 4096, 1048576, seed=100, sample=2)
+
+
 def test_index_candidates():
     say("index candidates")
     _index_case(4, 1, 8, 64, 4, 4 * 10000 - 1, 128, 10000, seed=14, cand_C=4096)
