@@ -892,7 +892,7 @@ def run_layers(args, csa, synth, wl, dev):
         if n_groups and layer == "full":  # its top-k came with the pool
             csa.sparse_attn(x["q"], s["codes"], s["scales"], x["idx"], s["win"], wl.W, t, 1.0,
                             x["out"], workspace=s["ws_attn"], fmt=FMT)
-        elif args.fused_layers:  # top-k over the pool resolved inside the attention kernel
+        elif not args.separate_layers:  # top-k over the pool resolved in the attention kernel
             csa.index_attn(x["q_idx"], x["w"], s["keys"], wl.m, t, wl.k, x["q"], s["codes"],
                            s["scales"], s["win"], wl.W, 1.0, x["idx"], x["out"], cand=s["pool"],
                            workspace=s["ws_fused"], fmt=FMT)
@@ -993,7 +993,7 @@ def run_layers(args, csa, synth, wl, dev):
                    **({"pool_groups": n_groups} if n_groups else {}),
                    "top_k": wl.k, "window": wl.W,
                    "input_sets_rotated": n_sets, "timing": timing_name(args),
-                   "csa_layer_step": "csa_index_attn over the pool" if args.fused_layers else
+                   "csa_layer_step": "csa_index_attn over the pool" if not args.separate_layers else
                    "csa_index_topk + csa_sparse_attn"},
         "layers_us": {"hca": round(t_hca * 1e3, 2), "full_pool_topk": round(t_pool * 1e3, 2),
                       ("full_attn" if n_groups else "full_topk_attn"): round(t_full * 1e3, 2),
@@ -1053,9 +1053,9 @@ def main():
     ap.add_argument("--separate", action="store_true",
                     help="decode: time csa_index_topk + csa_sparse_attn as two calls instead of "
                          "the one-call csa_index_attn")
-    ap.add_argument("--fused-layers", action="store_true",
-                    help="hca_reindex_1m: run each CSA layer as one csa_index_attn call over "
-                         "the pool (measured slower there than the two calls)")
+    ap.add_argument("--separate-layers", action="store_true",
+                    help="hca_reindex_1m: run each CSA layer as csa_index_topk + csa_sparse_attn "
+                         "over the pool instead of one csa_index_attn call")
     ap.add_argument("--graph", action="store_true",
                     help="time HIP graph replays instead of eager launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

@@ -249,15 +249,17 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         __shared__ uint32_t sel_bh[256];
         __shared__ int sel_tmp[4];
         __shared__ int sel_red[8];
-        auto emit = [&](int pos, int e, int v) {
+        // emit_id takes the entry id itself (the whole-row pick loads a pool's
+        // ids with the scores); emit takes a candidate index
+        auto emit_id = [&](int pos, int id, int v) {
           if (pos >= ep0 && pos < ep1) {
-            int id = cq ? cq[e] : e;
             id = (id >= 0 && id < blk_cap) ? id : -1;
             s_blk[pos - ep0] = id;
             oi[pos] = id;
             if (os) os[pos] = v;
           }
         };
+        auto emit = [&](int pos, int e, int v) { emit_id(pos, cq ? cq[e] : e, v); };
         int keff;
         int64_t nv = (t + 1) / sa.m_idx;
         nv = nv < blk_cap ? nv : blk_cap;
@@ -277,10 +279,10 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
           const int N = cq ? sa.C : (int)nv;
           if (N <= csa_topk::PICK_MAX / 2)
             keff = csa_topk::pick_select<csa_topk::PICK_MAX / 512>(
-                sa.slab + (int64_t)qi * sa.npad, hq, N, k, sh, emit);
+                sa.slab + (int64_t)qi * sa.npad, cq, hq, N, k, sh, emit_id);
           else
             keff = csa_topk::pick_select<csa_topk::PICK_MAX / 256>(
-                sa.slab + (int64_t)qi * sa.npad, hq, N, k, sh, emit);
+                sa.slab + (int64_t)qi * sa.npad, cq, hq, N, k, sh, emit_id);
         }
         for (int64_t pos = (keff > ep0 ? keff : ep0) + threadIdx.x; pos < ep1; pos += NT) {
           s_blk[pos - ep0] = -1;

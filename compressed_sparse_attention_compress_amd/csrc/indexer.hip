@@ -180,7 +180,11 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
 
   // query rows and head weights: every load unconditional (indexes clamped
   // into the row, padding masked afterwards), so that all of them are in
-  // flight together instead of one round trip each
+  // flight together instead of one round trip each. A row past the last head
+  // holds a copy of that head's row: its products land in output rows whose
+  // weight is 0, so it needs no mask, and with DI a multiple of 64 nothing
+  // reads the q rows before the first products (a mask here made every wave
+  // wait for its q row before it sent most of its first batch of key loads).
   v4i A[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -188,7 +192,8 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     const int hr = i16 < Hi ? i16 : Hi - 1;
     const v4i v = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)qi * Hi + hr) * DI +
                                                 (c0 < DI ? c0 : 0));
-    A[ks] = (i16 < Hi && c0 < DI) ? v : v4i{0, 0, 0, 0};
+    if constexpr (DI % 64 == 0) A[ks] = v;
+    else A[ks] = c0 < DI ? v : v4i{0, 0, 0, 0};
   }
   int wr[4];
 #pragma unroll
@@ -285,13 +290,8 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
       // both batches together: the empty statement orders the key loads
       // before it (memory clobber) and the products after it (their query
       // operand takes a zero it yields)
-      int dep = 0;
-      asm volatile("" : "+v"(dep)::"memory");
-      v4i Aq[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Aq[ks] = A[ks];
-      Aq[0][0] += dep;
-      consume(bt & 1, bt, Aq);
+      asm volatile("" : "+v"(A[0])::"memory");
+      consume(bt & 1, bt, A);
     }
   }
   __syncthreads();
@@ -732,10 +732,10 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
   const int32_t* cq = cand ? cand + (int64_t)qi * C : nullptr;
   int32_t* oi = out_idx + (int64_t)qi * k;
   int32_t* os = out_score ? out_score + (int64_t)qi * k : nullptr;
-  const int keff = pick_select<PER>(slab + (int64_t)qi * npad, hq, N, k,
+  const int keff = pick_select<PER>(slab + (int64_t)qi * npad, cq, hq, N, k,
                                     SelShared{nullptr, nullptr, bh, tmp, s_red},
-                                    [&](int pos, int e, int v) {
-                                      oi[pos] = cq ? cq[e] : e;
+                                    [&](int pos, int id, int v) {
+                                      oi[pos] = id;
                                       if (os) os[pos] = v;
                                     });
   // histogram consumed (every read of it precedes the barriers inside the
@@ -1180,9 +1180,15 @@ extern "C" int64_t csa_index_attn_workspace(int B, int T, int64_t n_max, int k, 
   const int64_t ns = (int64_t)k + W;
   // (the fused plan's partials depend on the indexer shape only through n_max;
   // Hi = 16 is the largest the indexer takes, so the size covers every Hi)
-  const int64_t ab = fused_attn_fits(T, ns)
-                         ? fused_attn_workspace(B, T, H, d, ns, fused_alg_bytes(n_max, 16, 128, k, W, H, d))
-                         : csa_attn_workspace(B, T, H, d, ns);
+  // (a call with a candidate pool takes the uncapped plan: the larger of the two)
+  int64_t ab = csa_attn_workspace(B, T, H, d, ns);
+  if (fused_attn_fits(T, ns)) {
+    const int64_t capped =
+        fused_attn_workspace(B, T, H, d, ns, fused_alg_bytes(n_max, 16, 128, k, W, H, d));
+    const int64_t pooled = fused_attn_workspace(B, T, H, d, ns, 0);
+    ab = ab > capped ? ab : capped;
+    ab = ab > pooled ? ab : pooled;
+  }
   return ab < 0 ? -1 : ib + ab;
 }
 
@@ -1229,7 +1235,7 @@ static int index_attn(CSA_INDEX_ATTN_PARAMS, bool scan_only) {
               ListsPlan{L.units, __builtin_ctz(L.lcap > 0 ? L.lcap : 1),
                         __builtin_ctz(TILE / L.sub)},
               cand, cand ? C : 0, m,
-              out_idx, out_score, fused_alg_bytes(n_max, Hi, Di, k, W, H, d)};
+              out_idx, out_score, cand ? 0 : fused_alg_bytes(n_max, Hi, Di, k, W, H, d)};
   // the fused list path keeps its scores in the lists (the whole-row walk of
   // massive ties recomputes them from the keys), so its scan writes no slab
   a.write_slab = !(fused && a.lists);

@@ -292,22 +292,43 @@ __device__ inline void emit_regs(const int (&sv)[PER], int p0, int tau, int take
 // the histogram, the rest from refine_regs / emit_regs (no LDS staging: at
 // one or two waves per SIMD every LDS round trip of a loop is exposed).
 // emit(pos, row index, score) for the keff selected ones; returns keff. The
-// histogram is only read; SelShared's cs / ce are not used.
+// histogram is only read; SelShared's cs / ce are not used. With a candidate
+// pool `ids` (the row's entry ids), each thread loads its rows' ids with their
+// scores, and emit receives the id instead of the row index (no dependent load
+// per selected entry).
 // ------------------------------------------------------------------------
 template <int PER, class Emit>
-__device__ inline int pick_select(const int32_t* sq, const uint32_t* hq, int N, int k,
-                                  SelShared s, Emit emit) {
+__device__ inline int pick_select(const int32_t* sq, const int32_t* ids, const uint32_t* hq,
+                                  int N, int k, SelShared s, Emit emit) {
   const int p0 = PER * (int)threadIdx.x;
   int sv[PER];  // issued before the histogram scan so that both loads overlap
+  int cid[PER];
+  // (a pool row starts 16-byte aligned only when the pool length is a
+  // multiple of 4; otherwise its ids are loaded one by one)
+  const bool ids_vec = ids && ((reinterpret_cast<uintptr_t>(ids) & 15) == 0);
   if (p0 + PER <= N) {
 #pragma unroll
     for (int j = 0; j < PER; j += 4) {
       const int4 v = *reinterpret_cast<const int4*>(sq + p0 + j);
       sv[j] = v.x; sv[j + 1] = v.y; sv[j + 2] = v.z; sv[j + 3] = v.w;
     }
+    if (ids_vec) {
+#pragma unroll
+      for (int j = 0; j < PER; j += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(ids + p0 + j);
+        cid[j] = v.x; cid[j + 1] = v.y; cid[j + 2] = v.z; cid[j + 3] = v.w;
+      }
+    } else if (ids) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) cid[j] = ids[p0 + j];
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < PER; ++j) sv[j] = p0 + j < N ? sq[p0 + j] : -1;
+    if (ids) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) cid[j] = p0 + j < N ? ids[p0 + j] : -1;
+    }
   }
   const int keff = threshold_bin(hq, k, s.tmp, s.s_red);
   if (keff == 0) return 0;
@@ -317,7 +338,7 @@ __device__ inline int pick_select(const int32_t* sq, const uint32_t* hq, int N, 
   int take_eq;
   const int tau = refine_regs<PER>(sv, T1, need, s, &take_eq);
   emit_regs<PER>(sv, p0, tau, take_eq, keff, s.tmp, [&](int pos, int j, int v) {
-    emit(pos, p0 + j, v);
+    emit(pos, ids ? cid[j] : p0 + j, v);
   });
   return keff;
 }

@@ -141,6 +141,10 @@ def test_index_attn_reindex_pool():
                                      dtype=torch.int8),
               w=torch.randint(0, 4, x["w"].shape, generator=g, device=DEV, dtype=torch.int8))
     _compare(x2, 4, L - 1, 512, 128, torch.bfloat16, cand=pool, oracle_seqs=(1,))
+    # a pool length that is not a multiple of 4: every row after the first
+    # starts off a 16-byte boundary (its ids are then loaded one by one)
+    odd = pool[:, :, :4093].contiguous()
+    _compare(x2, 4, L - 1, 512, 128, torch.bfloat16, cand=odd, oracle_seqs=(2,))
 
 
 def test_index_attn_ragged_positions():
