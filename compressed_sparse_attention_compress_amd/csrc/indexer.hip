@@ -755,6 +755,7 @@ __global__ __launch_bounds__(256) void k_idx_pick(int T, int m, int64_t pos0,
 // Dynamic LDS as final_select lays it out. The histogram of the query is
 // cleared for the next call.
 // ------------------------------------------------------------------------
+template <bool FLAT>
 __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
                                                    const int64_t* __restrict__ qpos,
                                                    int64_t blk_cap,
@@ -781,7 +782,7 @@ __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
   int32_t* os = L.out_score ? L.out_score + (int64_t)qi * k : nullptr;
   const int32_t* cqq = cand ? cand + (int64_t)qi * C : nullptr;
   const FinalPlan P{L.n_tiles, k, L.spec_tiles, L.spec_shift, cap_lds, toff_n, L.seg_shift};
-  const int keff = final_select(
+  const int keff = final_select<FLAT>(
       hq, L.cnt + (int64_t)qi * L.n_tiles, L.cbuf + (int64_t)qi * L.npad, P, smem, bh, tmp, s_red,
       [&](int pos, int e, int sv) {
         if (gs == 0) {
@@ -810,8 +811,9 @@ __global__ __launch_bounds__(256) void k_idx_final(int T, int m, int64_t pos0,
 // slots), which lets four workgroups share a compute unit at k <= 1024.
 constexpr int FINAL_COMPACT_BT = 1024;
 
-// Raise k_idx_final's dynamic LDS limit once per device (to the largest
-// size asked so far), so calls inside a graph capture make no attribute call.
+// Raise the dynamic LDS limit of both k_idx_final variants once per device
+// (to the largest size asked so far), so calls inside a graph capture make no
+// attribute call.
 static bool final_lds_allow(size_t lds) {
   static std::mutex mu;
   static size_t allowed[64];
@@ -819,7 +821,9 @@ static bool final_lds_allow(size_t lds) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   std::lock_guard<std::mutex> lock(mu);
   if (allowed[dev] >= lds) return true;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_final),
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_final<true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
+      hipFuncSetAttribute(reinterpret_cast<const void*>(k_idx_final<false>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return false;
   allowed[dev] = lds;
@@ -1016,8 +1020,16 @@ static int idx_phase(const IdxArgs& a, int phase) {
     const size_t lds = (size_t)(toff_n + 2 * cap_lds) * sizeof(int) +
                        (size_t)spec_slots * sizeof(int2);
     if (lds > 65536 && !final_lds_allow(lds)) return CSA_ERR_HIP;
-    hipLaunchKernelGGL(k_idx_final, dim3(BT * (pool ? 2 : 1)), dim3(256), lds, a.stream, a.T,
-                       a.m, a.pos0, a.pos, a.blk_cap, a.cand, C, cap_lds, toff_n, BT, L0, L1);
+    // launches of few queries (a workgroup per compute unit) take the flat
+    // register path; compact ones keep the leaner kernel
+    if (compact)
+      hipLaunchKernelGGL(k_idx_final<false>, dim3(BT * (pool ? 2 : 1)), dim3(256), lds, a.stream,
+                         a.T, a.m, a.pos0, a.pos, a.blk_cap, a.cand, C, cap_lds, toff_n, BT, L0,
+                         L1);
+    else
+      hipLaunchKernelGGL(k_idx_final<true>, dim3(BT * (pool ? 2 : 1)), dim3(256), lds, a.stream,
+                         a.T, a.m, a.pos0, a.pos, a.blk_cap, a.cand, C, cap_lds, toff_n, BT, L0,
+                         L1);
   }
   CSA_TRY_LAUNCH();
   return CSA_OK;

@@ -30,6 +30,7 @@ constexpr int SPEC_SLOTS = 4096; // speculative candidates staged per query
 constexpr int FUSED_CAP = 4096;  // compaction slots of an in-kernel selection
 constexpr int LIST_CAP = 32;     // entries a scan unit lists (whole top bins)
 constexpr int LIST_MIN = 8;      // smallest list kept (more units: no lists)
+constexpr int FLAT_PER = 32;     // candidates per thread of the final pass's flat register path
 
 // LDS scratch of a selection: ints and counters the 256 threads share.
 struct SelShared {
@@ -379,7 +380,7 @@ __host__ __device__ inline size_t final_lds_bytes(const FinalPlan& p) {
   return (size_t)(p.toff_n + 2 * p.cap + 2 * (p.spec_tiles << p.spec_shift)) * sizeof(int);
 }
 
-template <class Emit>
+template <bool FLAT, class Emit>
 __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, const int2* cq,
                                    const FinalPlan& P, int* smem, uint32_t* bh, int* tmp,
                                    int* s_red, Emit emit) {
@@ -445,6 +446,60 @@ __device__ inline int final_select(const uint32_t* hq, const int32_t* cntq, cons
     emit_regs<SPT>(sv, i0, tau, take_eq, keff, tmp,
                    [&](int pos, int u, int v) { emit(pos, r[u].y, v); });
     return keff;
+  }
+
+  // ---- flat register path: with at most 256 lists and FLAT_PER * 256
+  // candidates, the list offsets come from one scan of the per-thread list
+  // counts, and thread j loads positions [FLAT_PER j, FLAT_PER j + FLAT_PER)
+  // of the concatenated lists (entry order) straight into registers; the
+  // refinement and the ordered emission then run as on the direct path (the
+  // LDS compaction, refinement and emission below cost about twice as much).
+  // Compiled only where asked (FLAT): its registers would cost the launches of
+  // many queries, which share a compute unit four workgroups at a time.
+  if (FLAT && n_tiles <= 256) {
+    const int c_me = (int)threadIdx.x < n_tiles ? cr[0] : 0;
+    int tot;
+    const int incl = wg_scan_incl<256>(c_me, tmp, &tot);
+    if (tot <= FLAT_PER * 256) {  // (uniform)
+      if ((int)threadIdx.x < n_tiles) t_off[threadIdx.x] = incl - c_me;
+      __syncthreads();
+      const int p0 = FLAT_PER * (int)threadIdx.x;
+      // the list holding position p0: the last one starting at or before it
+      int tl = 0;
+      if (p0 < tot) {
+        int lo = 0, hi = n_tiles - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (t_off[mid] <= p0) lo = mid;
+          else hi = mid - 1;
+        }
+        tl = lo;
+      }
+      int nxt = tl + 1 < n_tiles ? t_off[tl + 1] : tot;
+      int base = t_off[tl];
+      int2 v[FLAT_PER];
+#pragma unroll
+      for (int u = 0; u < FLAT_PER; ++u) {
+        const int p = p0 + u;
+        while (p < tot && p >= nxt) {  // (lists with no candidate are skipped)
+          ++tl;
+          base = nxt;
+          nxt = tl + 1 < n_tiles ? t_off[tl + 1] : tot;
+        }
+        const int pc = p < tot ? p : 0;
+        const int tc = p < tot ? tl : 0;
+        v[u] = cq[((int64_t)tc << P.seg_shift) + (p < tot ? pc - base : 0)];
+      }
+      int sv[FLAT_PER];
+#pragma unroll
+      for (int u = 0; u < FLAT_PER; ++u) sv[u] = p0 + u < tot ? v[u].x : -1;
+      const SelShared sh{nullptr, nullptr, bh, tmp, s_red};
+      int take_eq;
+      const int tau = refine_regs<FLAT_PER>(sv, T1, need, sh, &take_eq);
+      emit_regs<FLAT_PER>(sv, p0, tau, take_eq, keff, tmp,
+                          [&](int pos, int u, int val) { emit(pos, v[u].y, val); });
+      return keff;
+    }
   }
 
   // ---- per-tile offsets of the candidates; the stage goes to LDS as well

@@ -126,7 +126,7 @@ def test_compress_tiny_workload():
 # --------------------------------------------------------------- indexer ----
 
 def _index_case(B, T, Hi, Di, m, pos0, k, blk_cap, seed, cand_C=0, wzero=False, keyrange=8,
-                phases=False, sample=None):
+                phases=False, sample=None, hot_tiles=()):
     g = gen(seed, "idx", B, T, Hi, Di)
     q = torch.randint(-8, 8, (B, T, Hi, Di), generator=g, device=DEV, dtype=torch.int8)
     w = torch.randint(0, 4, (B, T, Hi), generator=g, device=DEV, dtype=torch.int8)
@@ -134,6 +134,10 @@ def _index_case(B, T, Hi, Di, m, pos0, k, blk_cap, seed, cand_C=0, wzero=False, 
         w.zero_()
     keys = torch.randint(-keyrange, keyrange, (B, blk_cap, Di), generator=g, device=DEV,
                          dtype=torch.int8)
+    for tl in hot_tiles:  # 2048-entry tiles of wide-range keys: the top-k clusters there
+        keys[:, tl * 2048:(tl + 1) * 2048] = torch.randint(
+            -100, 100, (B, min(2048, blk_cap - tl * 2048), Di), generator=g, device=DEV,
+            dtype=torch.int8)
     cand = None
     if cand_C:
         nv = min(blk_cap, (pos0 + T) // m)
@@ -212,6 +216,17 @@ def test_index_large_k_few_queries():
     _index_case(2, 2, 8, 64, 4, 4 * 150000, 2048, 150010, seed=98, keyrange=1)
     _index_case(2, 1, 4, 32, 4, 4 * 9000, 10000, 9100, seed=99)
     _index_case(2, 1, 8, 64, 4, 4 * 1048575, 4096, 1048576, seed=100, sample=2)
+
+
+def test_index_clustered_large_k():
+    """Few queries whose top-k clusters in a few tiles: those lists overflow
+    the final pass's stage, the rest are short or empty, so the candidates are
+    gathered per thread across empty lists (and past 8,192 candidates through
+    LDS or the global walk)."""
+    say("index clustered large k")
+    _index_case(2, 1, 8, 64, 4, 4 * 50000 - 1, 2000, 50000, seed=101, hot_tiles=(3, 17))
+    _index_case(2, 1, 8, 64, 4, 4 * 50000 - 1, 3500, 50000, seed=102, hot_tiles=(0, 1, 24))
+    _index_case(3, 1, 8, 64, 4, 4 * 120000 - 1, 7000, 120000, seed=103, hot_tiles=(5, 40, 58))
 
 
 def test_index_candidates():
