@@ -242,12 +242,27 @@ __global__ __launch_bounds__(256) void k_decode_append(
   const int64_t b = ((int64_t)blockIdx.x * 4 + wave) * BPW + lane / LPB;
   if (b >= B) return;  // whole sequences leave together
   const int64_t t = pos[b];
-  if (t < 0) return;
   const int seg = lane % LPB;
   const float* x = kv + b * kv_ld + seg * 8;
   const float4 xa = *reinterpret_cast<const float4*>(x);
   const float4 xc = *reinterpret_cast<const float4*>(x + 4);
   const float gt = gate[b];
+  // m = 4: the block's staged rows and gates are requested with the token, so
+  // they need not wait for the position (their addresses do not depend on it;
+  // the row this token overwrites is taken from registers below)
+  float* st = stage + b * m * D;
+  float4 pa[4], pc[4];
+  float pg[4];
+  if (m == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* sr = st + (int64_t)i * D + seg * 8;
+      pa[i] = *reinterpret_cast<const float4*>(sr);
+      pc[i] = *reinterpret_cast<const float4*>(sr + 4);
+      pg[i] = stage_gate[b * 4 + i];
+    }
+  }
+  if (t < 0) return;
 
   // bf16 ring row (round to nearest even)
   {
@@ -258,7 +273,6 @@ __global__ __launch_bounds__(256) void k_decode_append(
   }
   // staging row of the block being filled
   const int j = (int)(t % m);
-  float* st = stage + b * m * D;
   {
     float* sr = st + (int64_t)j * D + seg * 8;
     *reinterpret_cast<float4*>(sr) = xa;
@@ -270,6 +284,18 @@ __global__ __launch_bounds__(256) void k_decode_append(
   if (blk >= blk_cap) return;
   const float* sg = stage_gate + b * m;
   double p[8];
+  if (m == 4) {
+    // (j == 3 here: the token is the block's last row)
+    pool8(
+        4, [&](int i) { return i == 3 ? gt : pg[i]; },
+        [&](int i, float4& a, float4& c) {
+          a = i == 3 ? xa : pa[i];
+          c = i == 3 ? xc : pc[i];
+        },
+        p);
+    store_entry<D, FMT>(p, seg, b * blk_cap + blk, codes, scales);
+    return;
+  }
   pool8(
       m, [&](int i) { return i == j ? gt : sg[i]; },
       [&](int i, float4& a, float4& c) {
