@@ -249,8 +249,17 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
         __shared__ uint32_t sel_bh[256];
         __shared__ int sel_tmp[4];
         __shared__ int sel_red[8];
-        // emit_id takes the entry id itself (the whole-row pick loads a pool's
-        // ids with the scores); emit takes a candidate index
+        // emit takes a candidate index (the lists path); emit_id the entry id
+        // itself (the whole-row pick loads a pool's ids with the scores)
+        auto emit = [&](int pos, int e, int v) {
+          if (pos >= ep0 && pos < ep1) {
+            int id = cq ? cq[e] : e;
+            id = (id >= 0 && id < blk_cap) ? id : -1;
+            s_blk[pos - ep0] = id;
+            oi[pos] = id;
+            if (os) os[pos] = v;
+          }
+        };
         auto emit_id = [&](int pos, int id, int v) {
           if (pos >= ep0 && pos < ep1) {
             id = (id >= 0 && id < blk_cap) ? id : -1;
@@ -259,7 +268,6 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
             if (os) os[pos] = v;
           }
         };
-        auto emit = [&](int pos, int e, int v) { emit_id(pos, cq ? cq[e] : e, v); };
         int keff;
         int64_t nv = (t + 1) / sa.m_idx;
         nv = nv < blk_cap ? nv : blk_cap;
