@@ -200,3 +200,18 @@ def test_index_attn_argument_errors(L):
     need = L.csa_index_attn_workspace(2, 1, 1000, 64, 64, 512, 128)
     assert need > L.csa_index_topk_workspace(2, 1, 1000, 64, 0)
     assert L.csa_index_attn_workspace(2, 1, 1000, 0, 64, 512, 128) == -1
+
+
+def test_index_attn_workspace_covers_pool_plan(L):
+    """A call with a candidate pool takes the plain split plan (10 splits of 64
+    slots for 512 + 128 slots), not the byte-capped one, so the workspace size
+    (which does not know whether a pool is given) covers its partials: 16
+    queries x 10 splits x 64 heads x 512 channels x 4 B, on top of the index
+    part."""
+    B, n_pool, k, H, d, W = 16, 4096, 512, 64, 512, 128
+    partials = B * 10 * H * d * 4
+    ws = L.csa_index_attn_workspace(B, 1, n_pool, k, H, d, W)
+    assert ws >= partials + B * 10 * H * 8
+    assert ws >= L.csa_attn_workspace(B, 1, H, d, k + W)
+    # the capped plan of a long context without a pool is covered as well
+    assert L.csa_index_attn_workspace(8, 1, 262144, 1024, H, d, W) >= 8 * 18 * H * d * 4
