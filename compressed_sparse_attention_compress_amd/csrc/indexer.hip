@@ -75,57 +75,74 @@ __device__ inline int quad_scores(int p0, int p1, int p2, int p3) {
 
 // The scan unit's short lists (k_idx_scan's LISTS tail). Its cut bin is the
 // lowest bin whose suffix count (entries in it and above) is at most lcap
-// (NB1, an empty list, when the top bin alone holds more); the list holds its
-// entries of the bins at or above the cut in entry order, with (count, cut).
-// The wide list does the same for 2 lcap entries: a selection whose threshold
-// bin lies below a unit's cut reads that unit's candidates there. Kept out of
-// line: the scan's main loop runs at the register limit, and this code's
-// values must not stay live across it.
-__device__ __noinline__ void scan_unit_list(const uint32_t* lh, const int* ssc, int span,
-                                            int64_t wg0, int64_t N, int2* lq, int2* info,
-                                            int2* lq2, int2* info2, int lcap) {
-  __shared__ int l_tmp[4];
-  __shared__ int l_cut[8];
+// (NB1, an empty list, when no bin qualifies); the list holds its entries of
+// the bins at or above the cut in entry order, with (count, cut). The wide
+// list does the same for 2 lcap entries: a selection whose threshold bin lies
+// below a unit's cut reads that unit's candidates there. Every workgroup of
+// the scan runs this at the same time, at its end, so it is kept to two
+// barriers: one wave finds both cuts (8 bins per lane, a wave scan from the
+// top), and the entries' ranks come from wave scans plus the four wave totals.
+__device__ __attribute__((always_inline)) inline void scan_unit_list(
+    const uint32_t* lh, const int* ssc, int span, int64_t wg0, int64_t N, int2* lq, int2* info,
+    int2* lq2, int2* info2, int lcap) {
+  __shared__ int l_cut[2];
+  __shared__ int l_wtot[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hb = NB1 - 1 - 2 * (int)threadIdx.x;
-  const int c_hi = (int)lh[hb], c_lo = (int)lh[hb - 1];
-  int tot;
-  const int incl = wg_scan_incl<256>(c_hi + c_lo, l_tmp, &tot);
-  const int excl = incl - c_hi - c_lo;
-  int cut = NB1, cut2 = NB1;
-  if (excl + c_hi <= lcap) cut = hb;
-  if (incl <= lcap) cut = hb - 1;
-  if (excl + c_hi <= 2 * lcap) cut2 = hb;
-  if (incl <= 2 * lcap) cut2 = hb - 1;
-  cut = wave_min(cut);
-  cut2 = wave_min(cut2);
-  if (lane == 0) {
-    l_cut[wave] = cut;
-    l_cut[4 + wave] = cut2;
+  if (wave == 0) {
+    // lane l: bins NB1 - 1 - 8 l - u, u = 0..7 (from the top down)
+    int c[8];
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c[u] = (int)lh[NB1 - 1 - 8 * lane - u];
+      sum += c[u];
+    }
+    int run = wave_scan_incl(sum) - sum;  // entries in the bins above this lane's
+    int cut = NB1, cut2 = NB1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      run += c[u];  // entries in bin NB1 - 1 - 8 lane - u and above
+      const int bn = NB1 - 1 - 8 * lane - u;
+      if (run <= lcap) cut = bn;
+      if (run <= 2 * lcap) cut2 = bn;
+    }
+    cut = wave_min(cut);
+    cut2 = wave_min(cut2);
+    if (lane == 0) {
+      l_cut[0] = cut;
+      l_cut[1] = cut2;
+    }
   }
   __syncthreads();
-  cut = min(min(l_cut[0], l_cut[1]), min(l_cut[2], l_cut[3]));
-  cut2 = min(min(l_cut[4], l_cut[5]), min(l_cut[6], l_cut[7]));
+  const int cut = l_cut[0], cut2 = l_cut[1];
   // the listed entries in entry order: thread j takes [8 j, 8 j + 8)
   const int j0 = threadIdx.x * 8;
-  int v[8];
+  int v[8], bn[8];
   int f = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const bool in = j0 + j < span && wg0 + j0 + j < N;
     v[j] = in ? ssc[j0 + j] : -1;
-    const int bn = v[j] >= 0 ? score_bin512(v[j]) : -1;
-    f += (bn >= cut ? 1 << 16 : 0) + (bn >= cut2 ? 1 : 0);
+    bn[j] = v[j] >= 0 ? score_bin512(v[j]) : -1;
+    f += (bn[j] >= cut ? 1 << 16 : 0) + (bn[j] >= cut2 ? 1 : 0);
   }
-  int total;
-  const int before = wg_scan_incl<256>(f, l_tmp, &total) - f;
+  const int x = wave_scan_incl(f);
+  if (lane == 63) l_wtot[wave] = x;
+  __syncthreads();
+  int pre = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int t = l_wtot[w];
+    pre += w < wave ? t : 0;
+    total += t;
+  }
+  const int before = x - f + pre;
   int at = before >> 16, at2 = before & 0xffff;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int bn = v[j] >= 0 ? score_bin512(v[j]) : -1;
     const int2 ent = int2{v[j], (int)(wg0 + j0 + j)};
-    if (bn >= cut) lq[at++] = ent;
-    if (bn >= cut2) lq2[at2++] = ent;
+    if (bn[j] >= cut) lq[at++] = ent;
+    if (bn[j] >= cut2) lq2[at2++] = ent;
   }
   if (threadIdx.x == 0) {
     *info = int2{total >> 16, cut};
