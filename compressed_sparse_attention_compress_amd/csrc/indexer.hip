@@ -83,8 +83,8 @@ __device__ inline int quad_scores(int p0, int p1, int p2, int p3) {
 // barriers: one wave finds both cuts (8 bins per lane, a wave scan from the
 // top), and the entries' ranks come from wave scans plus the four wave totals.
 __device__ __attribute__((always_inline)) inline void scan_unit_list(
-    const uint32_t* lh, const int* ssc, int span, int64_t wg0, int64_t N, int2* lq, int2* info,
-    int2* lq2, int2* info2, int lcap) {
+    const uint32_t* lh, const int* ssc, const uint16_t* sbn, int span, int64_t wg0, int64_t N,
+    int2* lq, int2* info, int2* lq2, int2* info2, int lcap) {
   __shared__ int l_cut[2];
   __shared__ int l_wtot[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -115,16 +115,27 @@ __device__ __attribute__((always_inline)) inline void scan_unit_list(
   }
   __syncthreads();
   const int cut = l_cut[0], cut2 = l_cut[1];
-  // the listed entries in entry order: thread j takes [8 j, 8 j + 8)
+  // the listed entries in entry order: thread j takes [8 j, 8 j + 8) of the
+  // span (threads past it list nothing and read slot 0); entries at or past N
+  // are not listed. sbn holds each staged score's bin + 1 (0: no score), so
+  // "bin >= cut" is "sbn > cut", with both loads unconditional.
   const int j0 = threadIdx.x * 8;
-  int v[8], bn[8];
+  const int64_t rem64 = N - (wg0 + j0);
+  const int rem = j0 < span ? (rem64 < 0 ? 0 : (rem64 > 8 ? 8 : (int)rem64)) : 0;
+  const int jr = j0 < span ? j0 : 0;
+  const uint4 bw = *reinterpret_cast<const uint4*>(sbn + jr);
+  const int4 ra = *reinterpret_cast<const int4*>(ssc + jr);
+  const int4 rb = *reinterpret_cast<const int4*>(ssc + jr + 4);
+  const uint32_t bwd[4] = {bw.x, bw.y, bw.z, bw.w};
+  const int v[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+  bool l1[8], l2[8];
   int f = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const bool in = j0 + j < span && wg0 + j0 + j < N;
-    v[j] = in ? ssc[j0 + j] : -1;
-    bn[j] = v[j] >= 0 ? score_bin512(v[j]) : -1;
-    f += (bn[j] >= cut ? 1 << 16 : 0) + (bn[j] >= cut2 ? 1 : 0);
+    const int b1 = j < rem ? (int)((bwd[j >> 1] >> (16 * (j & 1))) & 0xffffu) : 0;
+    l1[j] = b1 > cut;
+    l2[j] = b1 > cut2;
+    f += (l1[j] ? 1 << 16 : 0) + (l2[j] ? 1 : 0);
   }
   const int x = wave_scan_incl(f);
   if (lane == 63) l_wtot[wave] = x;
@@ -138,11 +149,12 @@ __device__ __attribute__((always_inline)) inline void scan_unit_list(
   }
   const int before = x - f + pre;
   int at = before >> 16, at2 = before & 0xffff;
+  const int e0 = (int)(wg0 + j0);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int2 ent = int2{v[j], (int)(wg0 + j0 + j)};
-    if (bn[j] >= cut) lq[at++] = ent;
-    if (bn[j] >= cut2) lq2[at2++] = ent;
+    const int2 ent = int2{v[j], e0 + j};
+    if (l1[j]) lq[at++] = ent;
+    if (l2[j]) lq2[at2++] = ent;
   }
   if (threadIdx.x == 0) {
     *info = int2{total >> 16, cut};
@@ -180,6 +192,8 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   __shared__ uint32_t lh[NB1];
   __shared__ uint32_t lhg[POOL ? NB1 : 1];
   __shared__ __attribute__((aligned(16))) int ssc[SPAN];
+  // (LISTS) each staged score's histogram bin + 1, 0 where there is no score
+  __shared__ __attribute__((aligned(16))) uint16_t sbn[LISTS ? SPAN : 8];
   const int64_t wg0 = (int64_t)blockIdx.x * SPAN;  // first entry of the workgroup
   const int qi = blockIdx.y;
   const int b = qi / T;
@@ -239,7 +253,10 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   // block completes) every entry scores -1 and no key is read; otherwise the
   // loads below carry no condition, so they issue back to back
   if (wg0 < N && nv == 0) {
-    for (int j = threadIdx.x; j < SPAN; j += 256) ssc[j] = -1;
+    for (int j = threadIdx.x; j < SPAN; j += 256) {
+      ssc[j] = -1;
+      if (LISTS) sbn[j] = 0;
+    }
   } else if (wg0 < N) {
     // two register buffers: the keys of batch bt + 1 are in flight while
     // batch bt is in the matrix cores
@@ -294,7 +311,9 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
         const int64_t e = tile_e(bt, 4 * h + g) + i16;
         if (e < N) {
           ssc[e - wg0] = v;
-          if (v >= 0) atomicAdd(&lh[score_bin512(v)], 1u);
+          const int bv = score_bin512(v);
+          if (v >= 0) atomicAdd(&lh[bv], 1u);
+          if (LISTS) sbn[e - wg0] = (uint16_t)(v >= 0 ? bv + 1 : 0);
         }
       }
     };
@@ -340,7 +359,7 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
   }
   if constexpr (LISTS) {
     const int64_t unit = (int64_t)qi * gridDim.x + blockIdx.x;
-    scan_unit_list(lh, ssc, SPAN, wg0, N, comp + unit * lcap, tinfo + unit,
+    scan_unit_list(lh, ssc, sbn, SPAN, wg0, N, comp + unit * lcap, tinfo + unit,
                    comp2 + unit * 2 * lcap, tinfo2 + unit, lcap);
   }
 }
