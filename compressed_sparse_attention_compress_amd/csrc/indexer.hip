@@ -82,10 +82,15 @@ __device__ inline int quad_scores(int p0, int p1, int p2, int p3) {
 // the scan runs this at the same time, at its end, so it is kept to two
 // barriers: one wave finds both cuts (8 bins per lane, a wave scan from the
 // top), and the entries' ranks come from wave scans plus the four wave totals.
-__device__ __attribute__((always_inline)) inline void scan_unit_list(
+// Returns the lowest bin the unit must add into the query's histogram: the
+// bin of its kflush-th largest score (0 when it has fewer, or kflush <= 0).
+// The query's kflush-th largest score is at least every unit's, so its
+// threshold bin is at or above every unit's, and those bins stay exact; the
+// total still reaches kflush whenever some unit has kflush scores.
+__device__ __attribute__((always_inline)) inline int scan_unit_list(
     const uint32_t* lh, const int* ssc, const uint16_t* sbn, int span, int64_t wg0, int64_t N,
-    int2* lq, int2* info, int2* lq2, int2* info2, int lcap) {
-  __shared__ int l_cut[2];
+    int2* lq, int2* info, int2* lq2, int2* info2, int lcap, int kflush) {
+  __shared__ int l_cut[3];
   __shared__ int l_wtot[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
@@ -98,19 +103,22 @@ __device__ __attribute__((always_inline)) inline void scan_unit_list(
       sum += c[u];
     }
     int run = wave_scan_incl(sum) - sum;  // entries in the bins above this lane's
-    int cut = NB1, cut2 = NB1;
+    int cut = NB1, cut2 = NB1, kb = -1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       run += c[u];  // entries in bin NB1 - 1 - 8 lane - u and above
       const int bn = NB1 - 1 - 8 * lane - u;
       if (run <= lcap) cut = bn;
       if (run <= 2 * lcap) cut2 = bn;
+      if (run >= kflush && kb < 0) kb = bn;  // the highest bin reaching kflush
     }
     cut = wave_min(cut);
     cut2 = wave_min(cut2);
+    kb = wave_max(kb);
     if (lane == 0) {
       l_cut[0] = cut;
       l_cut[1] = cut2;
+      l_cut[2] = kflush > 0 && kb > 0 ? kb : 0;
     }
   }
   __syncthreads();
@@ -160,6 +168,7 @@ __device__ __attribute__((always_inline)) inline void scan_unit_list(
     *info = int2{total >> 16, cut};
     *info2 = int2{total & 0xffff, cut2};
   }
+  return l_cut[2];
 }
 
 // ------------------------------------------------------------------------
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     int32_t* __restrict__ slab,
     uint32_t* __restrict__ hist, int64_t gpad, int32_t* __restrict__ gslab,
     uint32_t* __restrict__ ghist, int2* __restrict__ tinfo, int2* __restrict__ comp, int lcap,
-    int2* __restrict__ tinfo2, int2* __restrict__ comp2, int write_slab) {
+    int2* __restrict__ tinfo2, int2* __restrict__ comp2, int write_slab, int kflush) {
   constexpr int KS = (DI + 63) / 64;
   constexpr int BATCH = 8;
   constexpr int SPAN = TILE / SUB;  // entries per workgroup (SUB workgroups per tile)
@@ -352,15 +361,19 @@ __global__ __launch_bounds__(256, DI <= 64 ? 4 : 2) void k_idx_scan(
     }
   }
   if (POOL) __syncthreads();
-  uint32_t* hq = hist + (int64_t)qi * NB1;
-  for (int i = threadIdx.x; i < NB1; i += 256) {
-    if (lh[i]) atomicAdd(&hq[i], lh[i]);
-    if (POOL && lhg[i]) atomicAdd(&ghist[(int64_t)qi * NB1 + i], lhg[i]);
-  }
+  // the lists (whose selection needs only the bins at or above the query's
+  // threshold bin) come first: their unit's kflush-th bin bounds the bins it
+  // adds into the query's histogram
+  int kcut = 0;
   if constexpr (LISTS) {
     const int64_t unit = (int64_t)qi * gridDim.x + blockIdx.x;
-    scan_unit_list(lh, ssc, sbn, SPAN, wg0, N, comp + unit * lcap, tinfo + unit,
-                   comp2 + unit * 2 * lcap, tinfo2 + unit, lcap);
+    kcut = scan_unit_list(lh, ssc, sbn, SPAN, wg0, N, comp + unit * lcap, tinfo + unit,
+                          comp2 + unit * 2 * lcap, tinfo2 + unit, lcap, kflush);
+  }
+  uint32_t* hq = hist + (int64_t)qi * NB1;
+  for (int i = threadIdx.x; i < NB1; i += 256) {
+    if (i >= kcut && lh[i]) atomicAdd(&hq[i], lh[i]);
+    if (POOL && lhg[i]) atomicAdd(&ghist[(int64_t)qi * NB1 + i], lhg[i]);
   }
 }
 
@@ -1002,7 +1015,7 @@ static int idx_phase(const IdxArgs& a, int phase) {
   hipLaunchKernelGGL((k_idx_scan<DD, CC, SS, PP, LL>), sgrid, dim3(256), 0, a.stream, a.q_idx,  \
                      a.w, a.keys, a.blk_cap, a.T, a.Hi, a.m, a.pos0, a.pos, a.cand, C, L.npad,    \
                      slab, hist, L.gpad, gslab, ghist, tinfo, comp, L.lcap, tinfo2, comp2,  \
-                     a.write_slab ? 1 : 0)
+                     a.write_slab ? 1 : 0, a.k)
 #define CSA_LAUNCH_SCAN(DD, CC, SS, PP)                               \
   do {                                                                \
     if (!CC && !PP && lists) CSA_LAUNCH_SCAN1(DD, CC, SS, PP, true);  \
