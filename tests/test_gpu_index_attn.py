@@ -219,6 +219,18 @@ def test_index_attn_small_k_and_early_positions():
     _compare(x, 4, pos, 64, 128, torch.float32, pos_max=4 * 3000 - 1, oracle_seqs=(0, 1))
 
 
+def test_index_attn_whole_tile_units_small_and_large_k():
+    """Whole-tile scan units (4 x 256 tiles: 1,024 scan workgroups, 2,048 entries
+    each): every unit adds into the query's histogram only its bins at or above
+    its own k-th largest score, which cuts deepest for a small k; a k above a
+    unit's size adds every bin."""
+    say("index_attn whole-tile units, k 64 / 3000")
+    L = 4 * 524288
+    x = _world(8, 4, L, 128, 16, 4, 8, 64, random_cache=True)
+    for k in (64, 3000):
+        _compare(x, 4, L - 1, k, 128, torch.bfloat16, oracle_seqs=(3,))
+
+
 def test_index_attn_workspace_reuse():
     """One Workspace over repeated calls and a change of B*T: every call
     leaves the head zero, so results repeat exactly."""
