@@ -569,11 +569,12 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
       // online-softmax rescale (128 accumulator values in AGPRs per lane),
       // skipped unless some head of the wave saw its max grow by more than
-      // one (log2 units), so the reference max lags by at most 1 and p stays
-      // at most 2 in fp16 (the branch is wave-uniform; heads whose max did
-      // not grow get alpha = 1). A lag of 1 left every measured attention
-      // error unchanged; lags of 2 and 4 raised the p.v error.
-      if (__ballot(cmax > m_run + 1.0f)) {
+      // four (log2 units), so the reference max lags by at most 4 and p stays
+      // at most 16 in fp16 (the branch is wave-uniform; heads whose max did
+      // not grow get alpha = 1). With p as two float16 terms the measured
+      // attention errors are the same for a lag of 1 and of 4 (with one term
+      // a lag of 2 or 4 had raised them).
+      if (__ballot(cmax > m_run + 4.0f)) {
         const float m_new = fmaxf(m_run, cmax);
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
