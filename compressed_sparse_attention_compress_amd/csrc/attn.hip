@@ -714,17 +714,18 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
       lse[(int64_t)qi * H + head] =
           bad ? __builtin_nanf("") : (m_run + log2f(l_tot)) * 0.69314718055994531f;
   } else {
-    // normalised partial output in float32, stored in register order
+    // the split's partial output sum p v (not divided by its l: the merge
+    // weights it by 2^(m - M) alone) in float32, stored in register order
     // [query][split][wave][column tile][r / 4][lane][4], so every store of a
-    // wave is 1 KB contiguous; m and l in float32
+    // wave is 1 KB contiguous; m and l in float32 (NaN for a row out of
+    // float16's range, which the merge carries into the query's output)
     float* pw = part_o + (((int64_t)qi * nsplit + split) * NWV + wave) * (CT * 1024) + lane * 4;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<float4*>(pw + (4 * ct + q4) * 256) =
-            float4{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
-                   O[ct][4 * q4 + 3] * inv};
+            float4{O[ct][4 * q4], O[ct][4 * q4 + 1], O[ct][4 * q4 + 2], O[ct][4 * q4 + 3]};
     if (half == 0 && gg == 0)
       part_ml[((int64_t)qi * nsplit + split) * H + head] =
           bad ? float2{__builtin_nanf(""), __builtin_nanf("")} : float2{m_run, l_tot};
@@ -733,8 +734,8 @@ __global__ __launch_bounds__(NG * 128) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 // Merge of the split partials, one workgroup per (query, 32-head group,
 // 32-channel tile), one thread per (register quad, lane) of that tile: weights
-// l_s * 2^(m_s - M) / L on the normalised partial outputs, summed in split
-// order. The partials are read in the register order the attention kernel
+// 2^(m_s - M) / L on the partial outputs (L = sum of l_s 2^(m_s - M)), summed
+// in split order. The partials are read in the register order the attention kernel
 // wrote them, 4 KB contiguous per split; thread (q4, lane) holds head lane %
 // 32 and channels 8 q4 + 4 (lane / 32) .. +3 of the tile. Every thread loads
 // its head's (max, sum) of all splits and its partials of all splits in one
@@ -793,8 +794,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const float f = (s >= nsplit || ml[s].x == -INFINITY) ? 0.f : ml[s].y * exp2f(ml[s].x - M);
-    L += f;
+    const float f = (s >= nsplit || ml[s].x == -INFINITY) ? 0.f : exp2f(ml[s].x - M);
+    L += ml[s].y * f;
     acc.x += po[s].x * f; acc.y += po[s].y * f;
     acc.z += po[s].z * f; acc.w += po[s].w * f;
   }

@@ -362,12 +362,12 @@ int csa_workspace_clear(void* ws, int64_t bytes, hipStream_t stream);
  * products as float16 (exact for values in float16's normal range: bfloat16
  * values of magnitude 2^-14 .. 65504, and entries while their scale byte lies
  * in [104, 140]; q values below 2^-14 keep float16's subnormal resolution of
- * 2^-24); q.k and p.v accumulate in float32, probabilities are float16
- * (taken against a running max that lags the true one by at most a factor
- * of 2, so they stay at most 2); when
- * the slots of a query are split over workgroups (few queries per sequence),
- * the normalised partial outputs are kept in float32 and merged in a fixed
- * order. Rows outside float16's range are not attended silently: a query
+ * 2^-24); q.k and p.v accumulate in float32, probabilities enter p.v as
+ * two float16 terms (about 22 significant bits), taken against a running
+ * max that lags the true one by at most a factor of 2^4, so they stay at
+ * most 16; when the slots of a query are split over workgroups (few queries
+ * per sequence), the partial outputs are kept in float32 and merged in a
+ * fixed order. Rows outside float16's range are not attended silently: a query
  * any of whose staged rows is an E8M0 entry with a scale byte above 140 (a
  * 32-channel group with amax >= 2^16, whose largest codes overflow float16),
  * or a window value of magnitude 2^16 or more or not finite, gets NaN in
