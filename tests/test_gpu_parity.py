@@ -465,6 +465,26 @@ def test_sparse_attn_decode(d, H):
         _check_attn(wd, idx, L - 1, W, out, lse)
 
 
+def test_sparse_attn_decode_sharp_softmax():
+    """Decode queries split 10 ways under a sharp softmax (scale 24): the
+    splits' maxima differ by tens of log2 units, so most splits' merge
+    weights 2^(m_s - M) are tiny or underflow, and the running-max rescale
+    fires within passes; float32 and bfloat16 outputs and lse against the
+    oracle."""
+    say("attn decode sharp softmax")
+    B, L, d, m, H, k, W = 2, 4 * 1500, 512, 4, 64, 512, 128
+    wd = _attn_world(B, L, d, m, 128, seed=48, H=H, T=1)
+    g = gen(49, "idx")
+    idx = torch.stack([torch.randperm(L // m, generator=g, device=DEV)[:k] for _ in range(B)])
+    idx = idx.reshape(B, 1, k).to(torch.int32).contiguous()
+    for od in (torch.float32, torch.bfloat16):
+        out = torch.empty(B, 1, H, d, device=DEV, dtype=od)
+        lse = torch.empty(B, 1, H, device=DEV, dtype=torch.float32)
+        csa.sparse_attn(wd["q"], wd["codes"], wd["scales"], idx, wd["win"], W, L - 1, 24.0,
+                        out, lse)
+        _check_attn(wd, idx, L - 1, W, out, lse, scale=24.0)
+
+
 def test_sparse_attn_prefill_block():
     """64 consecutive queries, 512 entries each (one workgroup per query)."""
     say("attn prefill block")
