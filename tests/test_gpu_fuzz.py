@@ -21,7 +21,7 @@ from parity_util import REL_TOL, attn_excess_error, bf16_bits, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 24
+N_CASES = 96
 
 
 def _case(rng):
